@@ -1,0 +1,568 @@
+/*
+ * fp4q_oracle.c -- plain CPU oracle for block-scaled FP4 (NVFP4 / MXFP4)
+ * activation quantization, the W4A4 GEMM with sparse residual compensation,
+ * its expert-grouped form, and the exact three-way MXFP4 error decomposition.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, calls or
+ * includes this file; only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark load it.  It shares no source with the HIP
+ * path: every codec here is written as its definition (nearest value out of an
+ * enumerated set, ties broken by the stated rule), not as the bit tricks the
+ * GPU kernels use.
+ *
+ * Sources (titles of the pages this follows):
+ *  - "QUADS: Stabilizing NVFP4 Reinforcement Learning for MoE via
+ *    QUantization-error Alignment across Dual Sides", abstract: NVFP4 joins
+ *    fine-grained scaling with native W4A4 FP4 GEMMs; activations are
+ *    re-quantized online and their error is amplified by the coarse E2M1 grid;
+ *    Residual Activation Compensation corrects high-error activation channels
+ *    while the W4A4 GEMM stays native.
+ *  - The German explainer of the same paper (gist.science), section 2.2 B:
+ *    a residual correction term Delta X_q on selected channels is added to
+ *    the quantized output; section 1: E2M1 has 8 levels per sign.
+ *  - "FourSight: Stable FP4 RL Post-Training via Sequence Filtering and Sparse
+ *    Channel Compensation", abstract: the top-variance activation channels are
+ *    kept in BF16 while the rest stays NVFP4.
+ *  - "Decomposing MXFP4 quantization error for LLM reinforcement learning",
+ *    abstract: the MXFP4 error splits exactly into three additive parts --
+ *    scale bias (power-of-two rounding of the scale), deadzone truncation
+ *    (small values zeroed) and grid noise (rounding to the 4-bit grid).
+ *
+ * The pages do not fix block sizes, scale encodings, rounding or packing; the
+ * readings used here (each stated where it is used) are:
+ *  - E2M1 magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}; round to nearest, ties to
+ *    the even mantissa bit; saturate at 6; sign bit = sign bit of the input.
+ *  - NVFP4: 16-element blocks along K, E4M3 (bias 7, max 448, no inf) block
+ *    scale from amax/6 divided by an FP32 tensor scale t = amax_tensor/2688.
+ *  - MXFP4: 32-element blocks, scale 2^e with the smallest e such that
+ *    6*2^e >= block amax (nothing clips), stored as E8M0 code e+127.
+ *  - Two codes per byte, even element in the low nibble.
+ *  - Residual R = bf16(x - deq(code)) on the chosen channels only.
+ *  - GEMM: Y = deq(Xq) * deq(Wq)^T + R[:,S] * deq(Wq)[:,S]^T, in FP64.
+ *
+ * Every FP32 step of the quantizer is one IEEE binary32 operation with
+ * round-to-nearest-even; build with -O2 -ffp-contract=off, no fast-math.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_NVFP4 0
+#define ORC_MXFP4 1
+
+/* ------------------------------------------------------------------------ */
+/* Number formats                                                            */
+/* ------------------------------------------------------------------------ */
+
+/* E2M1 magnitudes indexed by the 3 low bits of a code (sign is bit 3). */
+static const double E2M1_GRID[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+double orc_e2m1_value(uint8_t code) {
+    double m = E2M1_GRID[code & 7];
+    return (code & 8) ? -m : m;
+}
+
+/* Nearest E2M1 magnitude to |q|; on an exact tie the code whose mantissa bit
+ * (bit 0) is 0 wins.  Anything at or above the largest level 6 is nearest to
+ * 6 (saturation); it is decided first because for huge |q| the FP64
+ * distances below would no longer be exact.  Below 6 every distance is exact
+ * (a float and a grid value under 8 differ by at most ~30 significant bits,
+ * and a tiny float's distance to 0 is the float itself). */
+uint8_t orc_e2m1_encode_mag(float q) {
+    double a = fabs((double)q);
+    if (a >= 6.0) return 7;
+    int best = 0;
+    double best_d = fabs(a - E2M1_GRID[0]);
+    for (int c = 1; c < 8; ++c) {
+        double d = fabs(a - E2M1_GRID[c]);   /* exact: few significant bits */
+        if (d < best_d || (d == best_d && (c & 1) == 0 && (best & 1) == 1)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return (uint8_t)best;
+}
+
+/* E4M3 (FN variant): sign 1, exponent 4 (bias 7), mantissa 3.  Exponent
+ * field 0 is subnormal: m/8 * 2^-6.  Code 0x7F / 0xFF is NaN. */
+double orc_e4m3_value(uint8_t code) {
+    int e = (code >> 3) & 15, m = code & 7;
+    double v = (e == 0) ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + m / 8.0, e - 7);
+    return (code & 0x80) ? -v : v;
+}
+
+/* Nearest non-negative finite E4M3 value to v >= 0, ties to the even code
+ * (the code's lowest bit is the mantissa's lowest bit); anything above the
+ * largest finite value 448 lands on 448 (saturating). */
+uint8_t orc_e4m3_encode(float v) {
+    double a = (double)v;
+    if (a >= 448.0) return 0x7E;  /* at or beyond the largest finite value */
+    int best = 0;
+    double best_d = fabs(a - orc_e4m3_value(0));
+    for (int c = 1; c <= 0x7E; ++c) {
+        double d = fabs(a - orc_e4m3_value((uint8_t)c));
+        if (d < best_d || (d == best_d && (c & 1) == 0)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return (uint8_t)best;
+}
+
+double orc_e8m0_value(uint8_t code) { return ldexp(1.0, (int)code - 127); }
+
+float orc_bf16_value(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* BF16 nearest to a finite float, ties to even: the two candidates are the
+ * float truncated to 16 bits and the next BF16 away from zero. */
+uint16_t orc_bf16_from_f32(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    uint16_t lo = (uint16_t)(u >> 16);
+    if ((u & 0xFFFFu) == 0) return lo;
+    uint16_t hi = (uint16_t)(lo + 1);        /* next magnitude up, same sign */
+    double dl = fabs((double)f - (double)orc_bf16_value(lo));
+    double dh = fabs((double)orc_bf16_value(hi) - (double)f);
+    if (isinf(orc_bf16_value(hi))) dh = ldexp(1.0, 127 - 8);  /* half ulp of max */
+    if (dl < dh) return lo;
+    if (dh < dl) return hi;
+    return (lo & 1) ? hi : lo;
+}
+
+/* MXFP4 block exponent: the smallest integer e in [-127, 127] with
+ * 6 * 2^e >= amax (every element then fits the grid without clipping).
+ * An all-zero block gets e = -127. */
+int orc_mx_exponent(float amax) {
+    for (int e = -127; e <= 127; ++e)
+        if (6.0 * ldexp(1.0, e) >= (double)amax) return e;
+    return 127;
+}
+
+/* NVFP4 tensor scale from the tensor (or group) amax: t = A / 2688 with
+ * 2688 = 6 * 448, so the largest block maps its amax onto 6 * 448. */
+float orc_nv_tensor_scale(float amax) {
+    float t = amax / 2688.0f;
+    if (amax == 0.0f || t == 0.0f) t = 1.0f;
+    return t;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Quantizer                                                                 */
+/* ------------------------------------------------------------------------ */
+
+static float absf_bf16(uint16_t h) { return fabsf(orc_bf16_value(h)); }
+
+
+/*
+ * Quantize X (bf16 [rows, cols], row stride ldx) in row groups
+ * [off[g], off[g+1]) (off == NULL: a single group of all rows).
+ * Outputs: q [rows, cols/2], scales [rows, cols/blk],
+ * tensor_scale [num_groups] (NVFP4 only), resid bf16 [rows, n_chan] for the
+ * channels chan_idx[g*n_chan .. +n_chan) of each row's group.
+ * Returns 0, or -1 for a shape the formats do not allow.
+ */
+int orc_quantize(int fmt, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                 const int32_t* off, int32_t num_groups, const int32_t* chan_idx,
+                 int32_t n_chan, uint8_t* q, uint8_t* scales, float* tensor_scale,
+                 uint16_t* resid) {
+    const int blk = (fmt == ORC_NVFP4) ? 16 : 32;
+    if (fmt != ORC_NVFP4 && fmt != ORC_MXFP4) return -1;
+    if (cols % blk != 0 || num_groups < 1) return -1;
+    const int64_t nb = cols / blk;
+
+    for (int32_t g = 0; g < num_groups; ++g) {
+        int64_t r0 = off ? off[g] : 0, r1 = off ? off[g + 1] : rows;
+        const int32_t* S = chan_idx ? chan_idx + (int64_t)g * n_chan : NULL;
+        /* jmap[c] = position of channel c in the group's channel list, or -1 */
+        int32_t* jmap = (int32_t*)malloc(sizeof(int32_t) * (size_t)cols);
+        if (!jmap) return -1;
+        for (int64_t c = 0; c < cols; ++c) jmap[c] = -1;
+        for (int32_t j = 0; S && j < n_chan; ++j) jmap[S[j]] = j;
+
+        /* Tensor scale (NVFP4): amax over the group's rows. */
+        float t = 1.0f;
+        if (fmt == ORC_NVFP4) {
+            float A = 0.0f;
+            for (int64_t r = r0; r < r1; ++r)
+                for (int64_t c = 0; c < cols; ++c) {
+                    float a = absf_bf16(x[r * ldx + c]);
+                    if (a > A) A = a;
+                }
+            t = orc_nv_tensor_scale(A);
+            tensor_scale[g] = t;
+        }
+
+#pragma omp parallel for schedule(static)
+        for (int64_t r = r0; r < r1; ++r) {
+            for (int64_t b = 0; b < nb; ++b) {
+                const uint16_t* xb = x + r * ldx + b * blk;
+                float amax = 0.0f;
+                for (int k = 0; k < blk; ++k) {
+                    float a = absf_bf16(xb[k]);
+                    if (a > amax) amax = a;
+                }
+                /* Block scale. */
+                uint8_t sc;
+                float d;            /* the divisor that maps x onto the grid */
+                float sb = 0.0f;    /* NVFP4 decoded block scale */
+                int e = 0;          /* MXFP4 exponent */
+                if (fmt == ORC_NVFP4) {
+                    float v = (amax / 6.0f) / t;
+                    sc = orc_e4m3_encode(v);
+                    sb = (float)orc_e4m3_value(sc);
+                    d = sb * t;
+                } else {
+                    e = orc_mx_exponent(amax);
+                    sc = (uint8_t)(e + 127);
+                    d = (float)ldexp(1.0, e);
+                }
+                scales[r * nb + b] = sc;
+
+                for (int k = 0; k < blk; ++k) {
+                    uint16_t h = xb[k];
+                    float xv = orc_bf16_value(h);
+                    uint8_t mag;
+                    if (fmt == ORC_NVFP4)
+                        mag = (d == 0.0f) ? 0 : orc_e2m1_encode_mag(fabsf(xv) / d);
+                    else
+                        mag = orc_e2m1_encode_mag(fabsf(xv) * (float)ldexp(1.0, -e));
+                    uint8_t code = (uint8_t)(((h >> 15) << 3) | mag);
+                    int64_t kk = b * blk + k;
+                    uint8_t* byte = q + r * (cols / 2) + kk / 2;
+                    if ((kk & 1) == 0)
+                        *byte = (uint8_t)((*byte & 0xF0) | code);
+                    else
+                        *byte = (uint8_t)((*byte & 0x0F) | (code << 4));
+
+                    if (S && resid) {
+                        int32_t j = jmap[kk];
+                        if (j >= 0) {
+                            /* Dequantized value, one FP32 rounding per step. */
+                            float p;
+                            if (fmt == ORC_NVFP4)
+                                p = ((float)E2M1_GRID[mag] * sb) * t;
+                            else
+                                p = (float)E2M1_GRID[mag] * d;
+                            if (code & 8) p = -p;
+                            float rr = xv - p;
+                            resid[r * n_chan + j] = orc_bf16_from_f32(rr);
+                        }
+                    }
+                }
+            }
+        }
+        free(jmap);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Dequantization and the compensated W4A4 GEMM (FP64 definition)            */
+/* ------------------------------------------------------------------------ */
+
+/* Value of element k of row r of a packed FP4 matrix with its block scale
+ * and tensor scale: e2m1 * block scale * tensor scale. */
+static double deq(int fmt, const uint8_t* qm, const uint8_t* sm, double ts, int64_t K,
+                  int64_t r, int64_t k) {
+    const int blk = (fmt == ORC_NVFP4) ? 16 : 32;
+    uint8_t byte = qm[r * (K / 2) + k / 2];
+    uint8_t code = (k & 1) ? (byte >> 4) : (byte & 15);
+    uint8_t sc = sm[r * (K / blk) + k / blk];
+    double s = (fmt == ORC_NVFP4) ? orc_e4m3_value(sc) * ts : orc_e8m0_value(sc);
+    return orc_e2m1_value(code) * s;
+}
+
+/* One output element: y = sum_k A[m,k] B[n,k] + sum_j R[m,j] B[n,S_j], with
+ * yabs the same sum over absolute values of every term. */
+static void gemm_point(int fmt, int64_t K, const uint8_t* aq, const uint8_t* as, double ats,
+                       const uint8_t* bq, const uint8_t* bs, double bts, const int32_t* S,
+                       int32_t nS, const uint16_t* R, int64_t m, int64_t n, double* y,
+                       double* yabs) {
+    double acc = 0.0, aabs = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        double p = deq(fmt, aq, as, ats, K, m, k) * deq(fmt, bq, bs, bts, K, n, k);
+        acc += p;
+        aabs += fabs(p);
+    }
+    for (int32_t j = 0; j < nS; ++j) {
+        double p = (double)orc_bf16_value(R[m * nS + j]) * deq(fmt, bq, bs, bts, K, n, S[j]);
+        acc += p;
+        aabs += fabs(p);
+    }
+    *y = acc;
+    *yabs = aabs;
+}
+
+/* Dense GEMM at chosen points (pm[i], pn[i]).  A = activations [M, K]
+ * quantized, B = weights stored as W^T [N, K] quantized; tensor scales are
+ * host values (1 for MXFP4). */
+int orc_gemm_points(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* aq,
+                    const uint8_t* as, float ats, const uint8_t* bq, const uint8_t* bs,
+                    float bts, const int32_t* S, int32_t nS, const uint16_t* R,
+                    const int64_t* pm, const int64_t* pn, int64_t npts, double* y,
+                    double* yabs) {
+    (void)M;
+    (void)N;
+    double ta = (fmt == ORC_NVFP4) ? ats : 1.0, tb = (fmt == ORC_NVFP4) ? bts : 1.0;
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t i = 0; i < npts; ++i)
+        gemm_point(fmt, K, aq, as, ta, bq, bs, tb, S, nS, R, pm[i], pn[i], &y[i], &yabs[i]);
+    return 0;
+}
+
+/* Dense GEMM, every output: y, yabs [M, N] row-major. */
+int orc_gemm_full(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* aq,
+                  const uint8_t* as, float ats, const uint8_t* bq, const uint8_t* bs,
+                  float bts, const int32_t* S, int32_t nS, const uint16_t* R, double* y,
+                  double* yabs) {
+    double ta = (fmt == ORC_NVFP4) ? ats : 1.0, tb = (fmt == ORC_NVFP4) ? bts : 1.0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            gemm_point(fmt, K, aq, as, ta, bq, bs, tb, S, nS, R, m, n, &y[m * N + n],
+                       &yabs[m * N + n]);
+    return 0;
+}
+
+/* Expert-grouped GEMM at chosen points.  Row m belongs to the group g with
+ * off[g] <= m < off[g+1]; group g uses weight slice g (bq + g*N*K/2, ...),
+ * its own tensor scales ats[g], bts[g] and channel list S + g*nS.  The
+ * residual rows are indexed by the global row m. */
+int orc_grouped_gemm_points(int fmt, int64_t total_rows, int64_t N, int64_t K,
+                            const int32_t* off, int32_t G, const uint8_t* aq,
+                            const uint8_t* as, const float* ats, const uint8_t* bq,
+                            const uint8_t* bs, const float* bts, const int32_t* S, int32_t nS,
+                            const uint16_t* R, const int64_t* pm, const int64_t* pn,
+                            int64_t npts, double* y, double* yabs) {
+    const int blk = (fmt == ORC_NVFP4) ? 16 : 32;
+    (void)total_rows;
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t i = 0; i < npts; ++i) {
+        int64_t m = pm[i];
+        int32_t g = 0;
+        while (g < G && !(off[g] <= m && m < off[g + 1])) ++g;
+        if (g == G) {
+            y[i] = NAN;
+            yabs[i] = NAN;
+            continue;
+        }
+        double ta = (fmt == ORC_NVFP4) ? ats[g] : 1.0, tb = (fmt == ORC_NVFP4) ? bts[g] : 1.0;
+        gemm_point(fmt, K, aq, as, ta, bq + (int64_t)g * N * (K / 2),
+                   bs + (int64_t)g * N * (K / blk), tb, S ? S + (int64_t)g * nS : NULL, nS, R, m,
+                   pn[i], &y[i], &yabs[i]);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Exact three-way MXFP4 error decomposition                                 */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Per 32-block: s = 2^e is the scale the quantizer uses, s* = amax/6 the
+ * ideal (unrounded) scale.  Q_s is the MXFP4 quantizer; Q* rounds x/s* to the
+ * E2M1 grid with the same tie rule.  Per element:
+ *   total      = x - Q_s(x)
+ *   deadzone   = x              if Q_s(x) == 0, else 0
+ *   grid_noise = x - Q*(x)      if Q_s(x) != 0, else 0
+ *   scale_bias = Q*(x) - Q_s(x) if Q_s(x) != 0, else 0
+ * so total = scale_bias + deadzone + grid_noise for every element.  Values are
+ * produced multiplied by 6 (6x, g*amax, 6*g*2^e are all short dyadic numbers,
+ * so each difference is exact in FP64).
+ * Component order: 0 total, 1 scale_bias, 2 deadzone, 3 grid_noise.
+ */
+static void decompose_elem(float xv, float amax, int e, double c6[4], int* in_dz) {
+    double x6 = 6.0 * (double)xv;
+    double ax = fabs((double)xv);
+    double sgn = signbit(xv) ? -1.0 : 1.0;
+    /* Q_s: the quantizer's own E2M1 code (same rule as orc_quantize). */
+    uint8_t mag = orc_e2m1_encode_mag(fabsf(xv) * (float)ldexp(1.0, -e));
+    double qs6 = sgn * 6.0 * E2M1_GRID[mag] * ldexp(1.0, e);
+    /* Q*: nearest grid point to |x| / (amax/6) = 6|x|/amax, decided exactly by
+     * comparing distances scaled by amax: | 6|x| - g*amax |. */
+    int best = 0;
+    if (amax > 0.0f) {
+        double A = (double)amax;
+        double best_d = fabs(6.0 * ax - E2M1_GRID[0] * A);
+        for (int c = 1; c < 8; ++c) {
+            double d = fabs(6.0 * ax - E2M1_GRID[c] * A);
+            if (d < best_d || (d == best_d && (c & 1) == 0 && (best & 1) == 1)) {
+                best = c;
+                best_d = d;
+            }
+        }
+    }
+    double qstar6 = sgn * E2M1_GRID[best] * (double)amax;
+    c6[0] = x6 - qs6;
+    if (mag == 0) {
+        c6[1] = 0.0;
+        c6[2] = x6;
+        c6[3] = 0.0;
+        *in_dz = (xv != 0.0f);
+    } else {
+        c6[1] = qstar6 - qs6;
+        c6[2] = 0.0;
+        c6[3] = x6 - qstar6;
+        *in_dz = 0;
+    }
+}
+
+/* Per-element components (times 6), for small tensors: out[4][rows*cols]. */
+int orc_error_components(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                         double* out) {
+    if (cols % 32 != 0) return -1;
+    int64_t n = rows * cols;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < cols / 32; ++b) {
+            const uint16_t* xb = x + r * ldx + b * 32;
+            float amax = 0.0f;
+            for (int k = 0; k < 32; ++k)
+                if (absf_bf16(xb[k]) > amax) amax = absf_bf16(xb[k]);
+            int e = orc_mx_exponent(amax);
+            for (int k = 0; k < 32; ++k) {
+                double c6[4];
+                int dz;
+                decompose_elem(orc_bf16_value(xb[k]), amax, e, c6, &dz);
+                for (int c = 0; c < 4; ++c) out[c * n + r * cols + b * 32 + k] = c6[c];
+            }
+        }
+    return 0;
+}
+
+/* 320-bit two's complement fixed point, 5 little-endian 64-bit limbs,
+ * least significant bit worth 2^-136. */
+#define FIX_LIMBS 5
+#define FIX_LSB_EXP (-136)
+
+/* acc += v (v an FP64 multiple of 2^-136 whose magnitude is below 2^183). */
+static void fix_add(uint64_t acc[FIX_LIMBS], double v) {
+    if (v == 0.0) return;
+    int ex;
+    double fr = frexp(fabs(v), &ex);                 /* |v| = fr * 2^ex */
+    uint64_t mant = (uint64_t)ldexp(fr, 53);         /* 53-bit integer */
+    int shift = ex - 53 - FIX_LSB_EXP;               /* |v| = mant * 2^(shift-136) */
+    while (shift < 0) {                              /* drop trailing zero bits */
+        if (mant & 1) abort();                       /* not a multiple of 2^-136 */
+        mant >>= 1;
+        ++shift;
+    }
+    uint64_t mag[FIX_LIMBS] = {0};
+    int li = shift / 64, bo = shift % 64;
+    if (li >= FIX_LIMBS) abort();
+    mag[li] = mant << bo;
+    if (bo && li + 1 < FIX_LIMBS) mag[li + 1] = mant >> (64 - bo);
+    if (v < 0) {  /* negate: invert and add one */
+        unsigned __int128 c = 1;
+        for (int i = 0; i < FIX_LIMBS; ++i) {
+            c += (unsigned __int128)(~mag[i]);
+            mag[i] = (uint64_t)c;
+            c >>= 64;
+        }
+    }
+    unsigned __int128 c = 0;
+    for (int i = 0; i < FIX_LIMBS; ++i) {
+        c += (unsigned __int128)acc[i] + mag[i];
+        acc[i] = (uint64_t)c;
+        c >>= 64;
+    }
+}
+
+static void fix_add_fix(uint64_t acc[FIX_LIMBS], const uint64_t b[FIX_LIMBS]) {
+    unsigned __int128 c = 0;
+    for (int i = 0; i < FIX_LIMBS; ++i) {
+        c += (unsigned __int128)acc[i] + b[i];
+        acc[i] = (uint64_t)c;
+        c >>= 64;
+    }
+}
+
+/* Approximate value of the fixed-point number (for reporting). */
+static double fix_to_double(const uint64_t a[FIX_LIMBS]) {
+    uint64_t t[FIX_LIMBS];
+    memcpy(t, a, sizeof t);
+    int neg = (t[FIX_LIMBS - 1] >> 63) & 1;
+    if (neg) {
+        unsigned __int128 c = 1;
+        for (int i = 0; i < FIX_LIMBS; ++i) {
+            c += (unsigned __int128)(~t[i]);
+            t[i] = (uint64_t)c;
+            c >>= 64;
+        }
+    }
+    long double v = 0.0L;
+    for (int i = FIX_LIMBS - 1; i >= 0; --i) v = v * 18446744073709551616.0L + (long double)t[i];
+    v = ldexpl(v, FIX_LSB_EXP);
+    return (double)(neg ? -v : v);
+}
+
+typedef struct {
+    int64_t exact[4][5];  /* 6 * (sum of component), fixed point as above */
+    double sum[4];        /* sum of component (approximate) */
+    double sumsq[4];      /* sum of squared component (FP64) */
+    double cross_sb_gn;   /* sum of scale_bias * grid_noise (FP64) */
+    int64_t n_elems, n_deadzone, n_clipped;
+} orc_err_stats;
+
+int orc_error_decompose(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                        orc_err_stats* out) {
+    if (cols % 32 != 0) return -1;
+    memset(out, 0, sizeof *out);
+    /* Per-row partial results, combined afterwards in row order so that the
+     * FP64 sums do not depend on the number of threads. */
+    typedef struct {
+        uint64_t fix[4][FIX_LIMBS];
+        double sq[4], cross;
+        int64_t ndz, nclip;
+    } row_part;
+    row_part* parts = (row_part*)calloc((size_t)(rows > 0 ? rows : 1), sizeof(row_part));
+    if (!parts) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        row_part* p = &parts[r];
+        for (int64_t b = 0; b < cols / 32; ++b) {
+            const uint16_t* xb = x + r * ldx + b * 32;
+            float amax = 0.0f;
+            for (int k = 0; k < 32; ++k)
+                if (absf_bf16(xb[k]) > amax) amax = absf_bf16(xb[k]);
+            int e = orc_mx_exponent(amax);
+            for (int k = 0; k < 32; ++k) {
+                double c6[4];
+                int dz;
+                float xv = orc_bf16_value(xb[k]);
+                decompose_elem(xv, amax, e, c6, &dz);
+                p->ndz += dz;
+                if (fabs((double)xv) > 6.0 * ldexp(1.0, e)) ++p->nclip;
+                for (int c = 0; c < 4; ++c) {
+                    fix_add(p->fix[c], c6[c]);
+                    double cv = c6[c] / 6.0;
+                    p->sq[c] += cv * cv;
+                }
+                p->cross += (c6[1] / 6.0) * (c6[3] / 6.0);
+            }
+        }
+    }
+    uint64_t tot[4][FIX_LIMBS];
+    memset(tot, 0, sizeof tot);
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int c = 0; c < 4; ++c) {
+            fix_add_fix(tot[c], parts[r].fix[c]);
+            out->sumsq[c] += parts[r].sq[c];
+        }
+        out->cross_sb_gn += parts[r].cross;
+        out->n_deadzone += parts[r].ndz;
+        out->n_clipped += parts[r].nclip;
+    }
+    free(parts);
+    for (int c = 0; c < 4; ++c) {
+        for (int i = 0; i < FIX_LIMBS; ++i) out->exact[c][i] = (int64_t)tot[c][i];
+        out->sum[c] = fix_to_double(tot[c]) / 6.0;
+    }
+    out->n_elems = rows * cols;
+    return 0;
+}

@@ -1,0 +1,269 @@
+"""Python face of the CPU oracle (``fp4q_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the CPU
+baseline leg of the benchmark import this module; the product library never
+does.  It marshals numpy arrays into the plain C oracle and shares no code
+with the HIP path.
+
+Formats (readings of the pages, stated in ``fp4q_oracle.c``):
+  * NVFP4: 16-element blocks, E4M3 block scale, FP32 tensor scale.
+  * MXFP4: 32-element blocks, E8M0 power-of-two block scale.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+NVFP4 = 0
+MXFP4 = 1
+BLOCK = {NVFP4: 16, MXFP4: 32}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fp4q_oracle.c")
+_LIB = os.path.join(_HERE, "liborc_fp4q.so")
+CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared",
+          "-std=gnu11", "-Wall"]
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc into oracle/liborc_fp4q.so."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.run(["gcc", *CFLAGS, "-o", tmp, _SRC, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class ErrStats(ctypes.Structure):
+    _fields_ = [
+        ("exact", (ctypes.c_int64 * 5) * 4),
+        ("sum", ctypes.c_double * 4),
+        ("sumsq", ctypes.c_double * 4),
+        ("cross_sb_gn", ctypes.c_double),
+        ("n_elems", ctypes.c_int64),
+        ("n_deadzone", ctypes.c_int64),
+        ("n_clipped", ctypes.c_int64),
+    ]
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i64, i32, f32 = ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+        L.orc_e2m1_value.restype = ctypes.c_double
+        L.orc_e2m1_value.argtypes = [ctypes.c_uint8]
+        L.orc_e2m1_encode_mag.restype = ctypes.c_uint8
+        L.orc_e2m1_encode_mag.argtypes = [f32]
+        L.orc_e4m3_value.restype = ctypes.c_double
+        L.orc_e4m3_value.argtypes = [ctypes.c_uint8]
+        L.orc_e4m3_encode.restype = ctypes.c_uint8
+        L.orc_e4m3_encode.argtypes = [f32]
+        L.orc_e8m0_value.restype = ctypes.c_double
+        L.orc_e8m0_value.argtypes = [ctypes.c_uint8]
+        L.orc_bf16_value.restype = f32
+        L.orc_bf16_value.argtypes = [ctypes.c_uint16]
+        L.orc_bf16_from_f32.restype = ctypes.c_uint16
+        L.orc_bf16_from_f32.argtypes = [f32]
+        L.orc_mx_exponent.restype = ctypes.c_int
+        L.orc_mx_exponent.argtypes = [f32]
+        L.orc_nv_tensor_scale.restype = f32
+        L.orc_nv_tensor_scale.argtypes = [f32]
+        L.orc_quantize.restype = ctypes.c_int
+        L.orc_quantize.argtypes = [ctypes.c_int, P, i64, i64, i64, P, i32, P, i32, P, P, P, P]
+        L.orc_gemm_points.restype = ctypes.c_int
+        L.orc_gemm_points.argtypes = [ctypes.c_int, i64, i64, i64, P, P, f32, P, P, f32, P, i32,
+                                      P, P, P, i64, P, P]
+        L.orc_gemm_full.restype = ctypes.c_int
+        L.orc_gemm_full.argtypes = [ctypes.c_int, i64, i64, i64, P, P, f32, P, P, f32, P, i32,
+                                    P, P, P]
+        L.orc_grouped_gemm_points.restype = ctypes.c_int
+        L.orc_grouped_gemm_points.argtypes = [ctypes.c_int, i64, i64, i64, P, i32, P, P, P, P, P,
+                                              P, P, i32, P, P, P, i64, P, P]
+        L.orc_error_components.restype = ctypes.c_int
+        L.orc_error_components.argtypes = [P, i64, i64, i64, P]
+        L.orc_error_decompose.restype = ctypes.c_int
+        L.orc_error_decompose.argtypes = [P, i64, i64, i64, ctypes.POINTER(ErrStats)]
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+# ---- scalar codecs (exposed for the pins) --------------------------------
+
+def e2m1_value(code: int) -> float:
+    return lib().orc_e2m1_value(code)
+
+
+def e2m1_encode_mag(q: float) -> int:
+    return lib().orc_e2m1_encode_mag(q)
+
+
+def e4m3_value(code: int) -> float:
+    return lib().orc_e4m3_value(code)
+
+
+def e4m3_encode(v: float) -> int:
+    return lib().orc_e4m3_encode(v)
+
+
+def e8m0_value(code: int) -> float:
+    return lib().orc_e8m0_value(code)
+
+
+def bf16_value(h: int) -> float:
+    return lib().orc_bf16_value(h)
+
+
+def bf16_from_f32(f: float) -> int:
+    return lib().orc_bf16_from_f32(f)
+
+
+def mx_exponent(amax: float) -> int:
+    return lib().orc_mx_exponent(amax)
+
+
+def nv_tensor_scale(amax: float) -> float:
+    return lib().orc_nv_tensor_scale(amax)
+
+
+# ---- quantizer -----------------------------------------------------------
+
+def quantize(fmt: int, x: np.ndarray, offsets=None, chan_idx=None):
+    """x: uint16 bf16 bit patterns [rows, cols].  offsets: int32 [G+1] or None.
+    chan_idx: int32 [G, nS] (or [nS] for one group) or None.
+    Returns dict(q [rows, cols/2] u8, scales [rows, cols/blk] u8,
+    tscale [G] f32 (NVFP4) or None, resid [rows, nS] u16 or None)."""
+    x = _c(x, np.uint16)
+    rows, cols = x.shape
+    blk = BLOCK[fmt]
+    G = 1 if offsets is None else len(offsets) - 1
+    off = _c(offsets, np.int32)
+    if chan_idx is not None:
+        ci = _c(chan_idx, np.int32).reshape(G, -1)
+        nS = ci.shape[1]
+    else:
+        ci, nS = None, 0
+    q = np.zeros((rows, cols // 2), np.uint8)
+    sc = np.zeros((rows, cols // blk), np.uint8)
+    ts = np.zeros(G, np.float32) if fmt == NVFP4 else None
+    R = np.zeros((rows, nS), np.uint16) if nS else None
+    rc = lib().orc_quantize(fmt, _p(x), rows, cols, cols, _p(off), G, _p(ci), nS, _p(q), _p(sc),
+                            _p(ts), _p(R))
+    if rc != 0:
+        raise ValueError(f"oracle quantize rejected the shape (rc={rc})")
+    return {"q": q, "scales": sc, "tscale": ts, "resid": R}
+
+
+# ---- GEMM ----------------------------------------------------------------
+
+def gemm_points(fmt, aq, as_, ats, bq, bs, bts, chan_idx, resid, pm, pn):
+    """Y and Yabs at points (pm[i], pn[i]); A = [M, K/2] codes, B = W^T codes."""
+    aq, as_, bq, bs = (_c(a, np.uint8) for a in (aq, as_, bq, bs))
+    M, K2 = aq.shape
+    N = bq.shape[0]
+    ci = _c(chan_idx, np.int32)
+    nS = 0 if ci is None else ci.size
+    R = _c(resid, np.uint16)
+    pm, pn = _c(pm, np.int64), _c(pn, np.int64)
+    y = np.zeros(pm.size, np.float64)
+    ya = np.zeros(pm.size, np.float64)
+    lib().orc_gemm_points(fmt, M, N, 2 * K2, _p(aq), _p(as_), float(ats), _p(bq), _p(bs),
+                          float(bts), _p(ci), nS, _p(R), _p(pm), _p(pn), pm.size, _p(y), _p(ya))
+    return y, ya
+
+
+def gemm_full(fmt, aq, as_, ats, bq, bs, bts, chan_idx, resid):
+    aq, as_, bq, bs = (_c(a, np.uint8) for a in (aq, as_, bq, bs))
+    M, K2 = aq.shape
+    N = bq.shape[0]
+    ci = _c(chan_idx, np.int32)
+    nS = 0 if ci is None else ci.size
+    R = _c(resid, np.uint16)
+    y = np.zeros((M, N), np.float64)
+    ya = np.zeros((M, N), np.float64)
+    lib().orc_gemm_full(fmt, M, N, 2 * K2, _p(aq), _p(as_), float(ats), _p(bq), _p(bs),
+                        float(bts), _p(ci), nS, _p(R), _p(y), _p(ya))
+    return y, ya
+
+
+def grouped_gemm_points(fmt, offsets, aq, as_, ats, bq, bs, bts, chan_idx, resid, pm, pn):
+    """Grouped GEMM at points; bq [G, N, K/2], bs [G, N, K/blk], ats/bts [G],
+    chan_idx [G, nS], resid [rows, nS] indexed by global row."""
+    aq, as_, bq, bs = (_c(a, np.uint8) for a in (aq, as_, bq, bs))
+    off = _c(offsets, np.int32)
+    G = off.size - 1
+    rows, K2 = aq.shape
+    N = bq.shape[1]
+    ats = _c(ats if ats is not None else np.ones(G), np.float32)
+    bts = _c(bts if bts is not None else np.ones(G), np.float32)
+    ci = _c(chan_idx, np.int32)
+    nS = 0 if ci is None else ci.reshape(G, -1).shape[1]
+    R = _c(resid, np.uint16)
+    pm, pn = _c(pm, np.int64), _c(pn, np.int64)
+    y = np.zeros(pm.size, np.float64)
+    ya = np.zeros(pm.size, np.float64)
+    lib().orc_grouped_gemm_points(fmt, rows, N, 2 * K2, _p(off), G, _p(aq), _p(as_), _p(ats),
+                                  _p(bq), _p(bs), _p(bts), _p(ci), nS, _p(R), _p(pm), _p(pn),
+                                  pm.size, _p(y), _p(ya))
+    return y, ya
+
+
+# ---- error decomposition -------------------------------------------------
+
+COMPONENTS = ("total", "scale_bias", "deadzone", "grid_noise")
+
+
+def error_components6(x: np.ndarray) -> np.ndarray:
+    """Per-element components times 6: float64 [4, rows, cols]."""
+    x = _c(x, np.uint16)
+    rows, cols = x.shape
+    out = np.zeros((4, rows, cols), np.float64)
+    rc = lib().orc_error_components(_p(x), rows, cols, cols, _p(out))
+    if rc != 0:
+        raise ValueError("cols must be a multiple of 32")
+    return out
+
+
+def fixed_to_int(limbs) -> int:
+    """320-bit two's complement (5 little-endian int64 limbs) -> Python int."""
+    v = 0
+    for i, l in enumerate(limbs):
+        v |= (int(l) & 0xFFFFFFFFFFFFFFFF) << (64 * i)
+    if v >> 319:
+        v -= 1 << 320
+    return v
+
+
+def error_decompose(x: np.ndarray) -> dict:
+    x = _c(x, np.uint16)
+    rows, cols = x.shape
+    st = ErrStats()
+    rc = lib().orc_error_decompose(_p(x), rows, cols, cols, ctypes.byref(st))
+    if rc != 0:
+        raise ValueError("cols must be a multiple of 32")
+    return {
+        "exact": [[int(st.exact[c][i]) for i in range(5)] for c in range(4)],
+        "exact_int": [fixed_to_int(st.exact[c]) for c in range(4)],
+        "sum": [st.sum[c] for c in range(4)],
+        "sumsq": [st.sumsq[c] for c in range(4)],
+        "cross_sb_gn": st.cross_sb_gn,
+        "n_elems": st.n_elems,
+        "n_deadzone": st.n_deadzone,
+        "n_clipped": st.n_clipped,
+    }
