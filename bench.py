@@ -1,0 +1,349 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP4 W4A4 hot path on one MI355X.
+
+One step = one pass of the hot path over one batch of seeded synthetic
+input, inputs resident in HBM: online activation quantization (tensor amax,
+block scales, E2M1 codes, BF16 residual on the compensated channels) and the
+compensated W4A4 GEMM.  Weights are quantized once before timing (they are
+re-quantized only at weight sync).  Enough distinct weight and output copies
+rotate to defeat the 256 MB last-level cache on the memory-bound workloads.
+
+Default workload: dense decode NVFP4, X [64 x 2048], W [2048 x 11008],
+|S| = 64.  Prints ONE JSON line.  --workload selects another configuration
+(prefill_nvfp4, prefill_mxfp4, moe_nvfp4, tiny_nvfp4) for profiling.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "compensated W4A4 GEMM effective TFLOP/s + quantize GB/s, % of roofline"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "fp4": 10100.0}
+LLC_BYTES = 256 << 20
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="decode_nvfp4",
+                   choices=["decode_nvfp4", "prefill_nvfp4", "prefill_mxfp4", "moe_nvfp4",
+                            "tiny_nvfp4"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="target CPU time of the oracle baseline sample")
+    return p.parse_args()
+
+
+def src_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "fp4_w4a4_quantized_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, kernel_hash: str):
+    """HBM traffic per launch measured with rocprofv3 --pmc (FETCH_SIZE and
+    WRITE_SIZE, scaled by a copy-kernel calibration); used only if it was
+    taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+        ent = t.get(workload)
+        if ent and ent.get("src_hash") == kernel_hash:
+            return ent["bytes_per_launch"]
+    except (OSError, ValueError):
+        pass
+    return None
+
+
+class Timer:
+    """HIP events on a given stream."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+
+    def pair(self):
+        t = self.torch
+        return t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is "
+              "single-GPU by design and multi-GPU sharding is not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fp4_w4a4_quantized_amd as fq
+    from workloads import CONFIGS, dense_case, moe_case
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    name = args.workload
+    cfg = CONFIGS[name]
+    fmt = fq.NVFP4 if cfg["fmt"] == "nvfp4" else fq.MXFP4
+    blk = fq.BLOCK[fmt]
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+
+    t0 = time.time()
+    print(f"[bench] generating {name} inputs", file=sys.stderr, flush=True)
+    if name == "moe_nvfp4":
+        data = moe_case(**cfg)
+    else:
+        data = dense_case(**cfg)
+    print(f"[bench] inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    # ---- build the step ------------------------------------------------------
+    if name != "moe_nvfp4":
+        M, K, N = cfg["M"], cfg["K"], cfg["N"]
+        nS = int(data["chan_idx"].size)
+        x = up(data["x"])
+        chan = up(data["chan_idx"]) if nS else None
+        wq = fq.quantize(fmt, up(data["wt"]))  # offline weight quantization
+        torch.cuda.synchronize()
+        w_bytes = N * (K // 2) + N * (K // blk)
+        y_bytes = M * N * 4
+        n_rot = max(1, math.ceil(1.2 * LLC_BYTES / (w_bytes + y_bytes)))
+        n_rot = min(n_rot, 64)
+        wcopies = [wq] + [{k: (v.clone() if v is not None else None) for k, v in wq.items()}
+                          for _ in range(n_rot - 1)]
+        ys = [torch.empty((M, N), dtype=torch.float32, device=dev) for _ in range(n_rot)]
+        G = 1
+        qws = torch.empty(max(fq.quantize_workspace_bytes(fmt, M, K, 1), 16), dtype=torch.uint8,
+                          device=dev)
+        aq = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+        asc = torch.empty((M, K // blk), dtype=torch.uint8, device=dev)
+        ats = torch.empty(1, dtype=torch.float32, device=dev) if fmt == fq.NVFP4 else None
+        ar = torch.empty((M, nS), dtype=torch.int16, device=dev) if nS else None
+
+        def quant():
+            fq.quantize_into(fmt, x, None, 1, chan, nS, aq, asc, ats, ar, qws, stream)
+
+        def gemm(i):
+            w = wcopies[i % n_rot]
+            fq.gemm_into(fmt, M, N, K, aq, asc, ats, w["q"], w["scales"], w["tscale"], chan, nS,
+                         ar, ys[i % n_rot], 0, N, stream)
+
+        flops = 2.0 * M * N * K
+        gemm_bytes = (M * K // 2 + M * K // blk + M * nS * 2 + nS * 4 + w_bytes + y_bytes +
+                      (8 if fmt == fq.NVFP4 else 0))
+        quant_bytes = M * K * 2 + M * K // 2 + M * K // blk + M * nS * 2 + (4 if fmt == fq.NVFP4
+                                                                             else 0)
+        wl = {"workload": name, "format": cfg["fmt"], "M": M, "K": K, "N": N, "n_s": nS,
+              "weight_copies_rotated": n_rot}
+    else:
+        # MoE layer: gate_up then down, per-expert NVFP4, grouped GEMMs
+        off = up(data["offsets"])
+        G = int(data["offsets"].size - 1)
+        rows = int(data["offsets"][-1])
+        H, I2 = cfg["hidden"], 2 * cfg["inter"]
+        I = cfg["inter"]
+        nS = cfg["n_s"]
+        xg, xd = up(data["x_perm"]), up(data["h_perm"])
+        cg, cd = up(data["chan_gate_up"]), up(data["chan_down"])
+
+        def qexperts(wt):
+            qs = [fq.quantize(fmt, up(wt[e])) for e in range(G)]
+            return (torch.stack([q["q"] for q in qs]), torch.stack([q["scales"] for q in qs]),
+                    torch.cat([q["tscale"] for q in qs]))
+
+        wgu = qexperts(data["wt_gate_up"])
+        wdn = qexperts(data["wt_down"])
+        torch.cuda.synchronize()
+        n_rot = 1   # 128 experts' weights already exceed the last-level cache
+        bufs = {}
+        for tag, (r, k) in {"gu": (rows, H), "dn": (rows, I)}.items():
+            bufs[tag] = dict(
+                q=torch.empty((r, k // 2), dtype=torch.uint8, device=dev),
+                s=torch.empty((r, k // blk), dtype=torch.uint8, device=dev),
+                t=torch.empty(G, dtype=torch.float32, device=dev),
+                r=torch.empty((r, nS), dtype=torch.int16, device=dev),
+                ws=torch.empty(max(fq.quantize_workspace_bytes(fmt, r, k, G), 16),
+                               dtype=torch.uint8, device=dev))
+        ygu = torch.empty((rows, I2), dtype=torch.float32, device=dev)
+        ydn = torch.empty((rows, H), dtype=torch.float32, device=dev)
+
+        def quant():
+            for tag, xin, ch in (("gu", xg, cg), ("dn", xd, cd)):
+                b = bufs[tag]
+                fq.quantize_into(fmt, xin, off, G, ch, nS, b["q"], b["s"], b["t"], b["r"],
+                                 b["ws"], stream)
+
+        def gemm(i):
+            for tag, w, y, n, k, ch in (("gu", wgu, ygu, I2, H, cg), ("dn", wdn, ydn, H, I, cd)):
+                b = bufs[tag]
+                fq.grouped_gemm_into(fmt, rows, n, k, off, G, b["q"], b["s"], b["t"], w[0], w[1],
+                                     w[2], ch, nS, b["r"], y, 0, stream)
+
+        loads = data["loads"]
+        active = int((loads > 0).sum())
+        flops = 2.0 * rows * (H * I2 + I * H)
+        wb = active * (I2 * H // 2 + I2 * H // blk + H * I // 2 + H * I // blk)
+        gemm_bytes = (rows * (H + I) // 2 + rows * (H + I) // blk + 2 * rows * nS * 2 +
+                      2 * G * nS * 4 + wb + rows * (I2 + H) * 4 + 2 * (G + 1) * 4 + 4 * G * 4)
+        quant_bytes = rows * (H + I) * 2 + rows * (H + I) // 2 + rows * (H + I) // blk + \
+            2 * rows * nS * 2 + 2 * G * 4
+        M, K, N = rows, H, I2
+        wl = {"workload": name, "format": "nvfp4", "tokens": cfg["tokens"], "experts": G,
+              "top_k": cfg["top_k"], "hidden": H, "inter": I, "routed_rows": rows,
+              "n_s_per_expert": nS, "max_expert_rows": int(loads.max()),
+              "empty_experts": int((loads == 0).sum())}
+
+    def step(i):
+        quant()
+        gemm(i)
+
+    # ---- warmup + timed steps --------------------------------------------------
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    step_ms = ev0.elapsed_time(ev1) / args.steps
+    print(f"[bench] {args.steps} steps: {step_ms * 1e3:.2f} us/step (wall {wall:.3f}s)",
+          file=sys.stderr, flush=True)
+
+    # ---- per-kernel averages with HIP events on the launch stream -------------
+    def timed(fn, reps):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for i, (a, b) in enumerate(evs):
+            a.record(stream)
+            fn(i)
+            b.record(stream)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs) / reps * 1e-3  # seconds
+
+    reps = max(args.steps, 20)
+    quant(); gemm(0); torch.cuda.synchronize()
+    t_gemm = timed(gemm, reps)
+    t_quant = timed(lambda i: quant(), reps)
+    print(f"[bench] gemm {t_gemm * 1e6:.2f} us, quantize {t_quant * 1e6:.2f} us per launch",
+          file=sys.stderr, flush=True)
+
+    kh = src_hash()
+    if name in ("prefill_nvfp4", "prefill_mxfp4"):
+        mfma_dtype = "f16" if fmt == fq.NVFP4 else "fp4"
+        peak = MFMA_PEAK_TFLOPS[mfma_dtype]
+        ach = flops / t_gemm / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(ach / peak, 4), "traffic": load_traffic(name, kh),
+                "mfma_dtype": mfma_dtype}
+    else:
+        ach = gemm_bytes / t_gemm / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": load_traffic(name, kh),
+                "algorithmic_bytes": gemm_bytes}
+    quant_gbs = quant_bytes / t_quant / 1e9
+
+    # ---- CPU baseline: the oracle on this host --------------------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(name, cfg, data, fmt, args.cpu_seconds)
+
+    value = flops / (step_ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if fmt == fq.NVFP4 else "fp4",
+        "data": "synthetic (seeded; no dataset or trained weights)",
+        "config": wl,
+        "quantize_gbps": round(quant_gbs, 1),
+        "quantize_frac_hbm": round(quant_gbs / HBM_PEAK_GBS, 4),
+        "quantize_bytes": quant_bytes,
+        "gemm_us": round(t_gemm * 1e6, 3),
+        "quantize_us": round(t_quant * 1e6, 3),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernel_src_hash": kh,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(name, cfg, data, fmt, target_s):
+    """Time the oracle (as it is) on the host: quantize the activations, then
+    the FP64 GEMM on a bounded sample of outputs, scaled to TFLOP/s."""
+    import numpy as np
+
+    from oracle import oracle as orc
+
+    cores = int(os.environ.get("OMP_NUM_THREADS") or len(os.sched_getaffinity(0)))
+    if name == "moe_nvfp4":
+        x, chan, off = data["x_perm"], data["chan_gate_up"], data["offsets"]
+        K = cfg["hidden"]
+    else:
+        x, chan, off = data["x"], data["chan_idx"], None
+        K = cfg["K"]
+    t0 = time.perf_counter()
+    qa = orc.quantize(fmt, x, offsets=off, chan_idx=chan if chan.size else None)
+    t_q = time.perf_counter() - t0
+    # weights for the sample: the first rows of W^T (first expert for MoE)
+    wt = data["wt_gate_up"][0] if name == "moe_nvfp4" else data["wt"]
+    n_cols = min(wt.shape[0], 256)
+    qb = orc.quantize(fmt, wt[:n_cols])
+    M = x.shape[0] if off is None else int(off[1] - off[0])
+    ch0 = chan if off is None else chan[0]
+    if M == 0:
+        return None
+    # calibrate the sample size to about target_s seconds of oracle GEMM
+    rng = np.random.default_rng(0)
+    npts = 2048
+    ta = float(qa["tscale"][0]) if fmt == 0 else 1.0
+    tb = float(qb["tscale"][0]) if fmt == 0 else 1.0
+    R = qa["resid"][:M] if qa["resid"] is not None else None
+    while True:
+        pm, pn = rng.integers(0, M, npts), rng.integers(0, n_cols, npts)
+        t0 = time.perf_counter()
+        orc.gemm_points(fmt, qa["q"][:M], qa["scales"][:M], ta, qb["q"], qb["scales"], tb,
+                        ch0 if ch0.size else None, R, pm, pn)
+        t_g = time.perf_counter() - t0
+        if t_g > 0.2 * target_s or npts >= 1 << 24:
+            break
+        npts *= 4
+    sample_flops = 2.0 * npts * K
+    gflops_rate = sample_flops / t_g
+    return {"value": round(gflops_rate / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"oracle FP64 GEMM on {npts} sampled outputs of the {name} workload "
+                      f"(K={K}, {t_g:.1f}s) after oracle quantization of the full activation "
+                      f"tensor ({t_q:.2f}s)",
+            "quantize_s": round(t_q, 4)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,26 @@
+"""fp4q: block-scaled FP4 (NVFP4 / MXFP4) W4A4 linear layers with sparse
+residual compensation, for AMD Instinct MI355X (gfx950).
+
+The product is the C-ABI library ``libfp4q.so`` (include/fp4q.h); this
+package holds its HIP sources (``csrc/``), the build step (``build``) and a
+thin ctypes binding (``binding``).
+"""
+from .binding import (  # noqa: F401
+    BLOCK,
+    MXFP4,
+    NVFP4,
+    OUT_BF16,
+    OUT_F32,
+    Fp4qError,
+    error_decompose,
+    error_decompose_into,
+    error_decompose_workspace_bytes,
+    gemm,
+    gemm_into,
+    grouped_gemm,
+    grouped_gemm_into,
+    lib,
+    quantize,
+    quantize_into,
+    quantize_workspace_bytes,
+)

@@ -1,0 +1,211 @@
+"""ctypes binding of libfp4q (include/fp4q.h).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+libfp4q.so.  Tensors are torch tensors on the GPU (torch supplies device
+memory and the current HIP stream); each function has the name of the C
+entry point it calls, minus the ``fp4q_`` prefix.  The library must be built
+(``python -m fp4_w4a4_quantized_amd.build``); there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+NVFP4 = 0
+MXFP4 = 1
+OUT_F32 = 0
+OUT_BF16 = 1
+BLOCK = {NVFP4: 16, MXFP4: 32}
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp4q.so")
+_lib = None
+
+
+class Fp4qError(RuntimeError):
+    def __init__(self, fn, status, hip_error=0):
+        self.status = status
+        msg = f"{fn} failed: {lib().fp4q_status_str(status).decode()} ({status})"
+        if hip_error:
+            msg += f", hipError {hip_error}"
+        super().__init__(msg)
+
+
+class ErrStats(ctypes.Structure):
+    _fields_ = [
+        ("exact", (ctypes.c_int64 * 5) * 4),
+        ("sum", ctypes.c_double * 4),
+        ("sumsq", ctypes.c_double * 4),
+        ("cross_sb_gn", ctypes.c_double),
+        ("n_elems", ctypes.c_int64),
+        ("n_deadzone", ctypes.c_int64),
+        ("n_clipped", ctypes.c_int64),
+    ]
+
+
+ERR_STATS_BYTES = ctypes.sizeof(ErrStats)
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """Load libfp4q.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(f"{_LIB_PATH} is missing: build it with "
+                              "`python -m fp4_w4a4_quantized_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        P, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+        L.fp4q_status_str.restype = ctypes.c_char_p
+        L.fp4q_status_str.argtypes = [ctypes.c_int]
+        L.fp4q_last_hip_error.restype = ctypes.c_int
+        L.fp4q_last_hip_error.argtypes = []
+        L.fp4q_quantize_workspace_bytes.restype = sz
+        L.fp4q_quantize_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i32]
+        L.fp4q_quantize.restype = ctypes.c_int
+        L.fp4q_quantize.argtypes = [ctypes.c_int, P, i64, i64, i64, P, i32, P, i32, P, P, P, P, P,
+                                    sz, P]
+        L.fp4q_gemm.restype = ctypes.c_int
+        L.fp4q_gemm.argtypes = [ctypes.c_int, i64, i64, i64, P, P, P, P, P, P, P, i32, P, P,
+                                ctypes.c_int, i64, P]
+        L.fp4q_grouped_gemm.restype = ctypes.c_int
+        L.fp4q_grouped_gemm.argtypes = [ctypes.c_int, i64, i64, i64, P, i32, P, P, P, P, P, P, P,
+                                        i32, P, P, ctypes.c_int, P]
+        L.fp4q_error_decompose_workspace_bytes.restype = sz
+        L.fp4q_error_decompose_workspace_bytes.argtypes = [i64, i64]
+        L.fp4q_error_decompose.restype = ctypes.c_int
+        L.fp4q_error_decompose.argtypes = [ctypes.c_int, P, i64, i64, i64, P, P, sz, P]
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(fn, rc):
+    if rc != 0:
+        raise Fp4qError(fn, rc, lib().fp4q_last_hip_error() if rc == -4 else 0)
+
+
+# ---- raw entry points (same names and argument order as the C ABI) --------
+
+def quantize_workspace_bytes(fmt, rows, cols, num_groups=1) -> int:
+    return lib().fp4q_quantize_workspace_bytes(fmt, rows, cols, num_groups)
+
+
+def error_decompose_workspace_bytes(rows, cols) -> int:
+    return lib().fp4q_error_decompose_workspace_bytes(rows, cols)
+
+
+def quantize_into(fmt, x, group_offsets, num_groups, chan_idx, n_chan, q, scales, tensor_scale,
+                  resid, workspace, stream=None):
+    rows, cols = x.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().fp4q_quantize(fmt, _ptr(x), rows, cols, x.stride(0), _ptr(group_offsets),
+                             num_groups, _ptr(chan_idx), n_chan, _ptr(q), _ptr(scales),
+                             _ptr(tensor_scale), _ptr(resid), _ptr(workspace), ws_bytes,
+                             _stream(stream))
+    _check("fp4q_quantize", rc)
+
+
+def gemm_into(fmt, M, N, K, a_q, a_s, a_ts, b_q, b_s, b_ts, chan_idx, n_chan, resid, y,
+              y_dtype=OUT_F32, ldy=None, stream=None):
+    rc = lib().fp4q_gemm(fmt, M, N, K, _ptr(a_q), _ptr(a_s), _ptr(a_ts), _ptr(b_q), _ptr(b_s),
+                         _ptr(b_ts), _ptr(chan_idx), n_chan, _ptr(resid), _ptr(y), y_dtype,
+                         N if ldy is None else ldy, _stream(stream))
+    _check("fp4q_gemm", rc)
+
+
+def grouped_gemm_into(fmt, total_rows, N, K, group_offsets, num_groups, a_q, a_s, a_ts, b_q,
+                      b_s, b_ts, chan_idx, n_chan, resid, y, y_dtype=OUT_F32, stream=None):
+    rc = lib().fp4q_grouped_gemm(fmt, total_rows, N, K, _ptr(group_offsets), num_groups,
+                                 _ptr(a_q), _ptr(a_s), _ptr(a_ts), _ptr(b_q), _ptr(b_s),
+                                 _ptr(b_ts), _ptr(chan_idx), n_chan, _ptr(resid), _ptr(y),
+                                 y_dtype, _stream(stream))
+    _check("fp4q_grouped_gemm", rc)
+
+
+def error_decompose_into(fmt, x, out, workspace, stream=None):
+    rows, cols = x.shape
+    ws_bytes = workspace.numel() * workspace.element_size()
+    rc = lib().fp4q_error_decompose(fmt, _ptr(x), rows, cols, x.stride(0), _ptr(out),
+                                    _ptr(workspace), ws_bytes, _stream(stream))
+    _check("fp4q_error_decompose", rc)
+
+
+# ---- allocating conveniences ---------------------------------------------
+
+def quantize(fmt, x, group_offsets=None, chan_idx=None, stream=None):
+    """x: bf16 (or int16/uint16 bit patterns) [rows, cols] on the GPU.
+    group_offsets: int32 [G+1] on the GPU or None.  chan_idx: int32 [G, nS]
+    (or [nS]) on the GPU or None.  Returns dict(q, scales, tscale, resid)."""
+    dev = x.device
+    rows, cols = x.shape
+    blk = BLOCK[fmt]
+    G = 1 if group_offsets is None else group_offsets.numel() - 1
+    nS = 0 if chan_idx is None else chan_idx.numel() // G
+    q = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    sc = torch.empty((rows, cols // blk), dtype=torch.uint8, device=dev)
+    ts = torch.empty(G, dtype=torch.float32, device=dev) if fmt == NVFP4 else None
+    R = torch.empty((rows, nS), dtype=torch.int16, device=dev) if nS else None
+    wsb = quantize_workspace_bytes(fmt, rows, cols, G)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev) if wsb else None
+    quantize_into(fmt, x, group_offsets, G, chan_idx, nS, q, sc, ts, R, ws, stream)
+    return {"q": q, "scales": sc, "tscale": ts, "resid": R}
+
+
+def gemm(fmt, a, b, chan_idx=None, y_dtype=OUT_F32, stream=None):
+    """a, b: quantize() results (b from W^T [N, K]).  Returns Y [M, N]."""
+    M, K = a["q"].shape[0], a["q"].shape[1] * 2
+    N = b["q"].shape[0]
+    nS = 0 if chan_idx is None else chan_idx.numel()
+    y = torch.empty((M, N), dtype=torch.float32 if y_dtype == OUT_F32 else torch.bfloat16,
+                    device=a["q"].device)
+    gemm_into(fmt, M, N, K, a["q"], a["scales"], a["tscale"], b["q"], b["scales"], b["tscale"],
+              chan_idx, nS, a["resid"] if nS else None, y, y_dtype, N, stream)
+    return y
+
+
+def grouped_gemm(fmt, group_offsets, a, bq, bs, bts, chan_idx=None, y_dtype=OUT_F32,
+                 stream=None):
+    """a: grouped quantize() result; bq [G, N, K/2], bs [G, N, K/blk], bts [G]."""
+    total, K = a["q"].shape[0], a["q"].shape[1] * 2
+    G = group_offsets.numel() - 1
+    N = bq.shape[1]
+    nS = 0 if chan_idx is None else chan_idx.numel() // G
+    y = torch.empty((total, N), dtype=torch.float32 if y_dtype == OUT_F32 else torch.bfloat16,
+                    device=a["q"].device)
+    grouped_gemm_into(fmt, total, N, K, group_offsets, G, a["q"], a["scales"], a["tscale"], bq,
+                      bs, bts, chan_idx, nS, a["resid"] if nS else None, y, y_dtype, stream)
+    return y
+
+
+def error_decompose(fmt, x, stream=None):
+    """Returns a dict like the fp4q_err_stats_t struct (copied to the host)."""
+    rows, cols = x.shape
+    out = torch.zeros(ERR_STATS_BYTES, dtype=torch.uint8, device=x.device)
+    wsb = error_decompose_workspace_bytes(rows, cols)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=x.device)
+    error_decompose_into(fmt, x, out, ws, stream)
+    host = out.cpu().numpy().tobytes()
+    st = ErrStats.from_buffer_copy(host)
+    return {
+        "exact": [[int(st.exact[c][i]) for i in range(5)] for c in range(4)],
+        "sum": [st.sum[c] for c in range(4)],
+        "sumsq": [st.sumsq[c] for c in range(4)],
+        "cross_sb_gn": st.cross_sb_gn,
+        "n_elems": st.n_elems,
+        "n_deadzone": st.n_deadzone,
+        "n_clipped": st.n_clipped,
+    }

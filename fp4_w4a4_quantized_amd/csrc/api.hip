@@ -1,0 +1,167 @@
+// api.hip -- the C ABI of libfp4q (declared in include/fp4q.h): host-side
+// argument validation, workspace queries and kernel launches.  Every check
+// runs before the first HIP call, so invalid calls fail without touching
+// the device.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp4q_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+inline bool aligned(const void* p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+inline int blk_of(int fmt) { return fmt == FP4Q_NVFP4 ? 16 : 32; }
+
+inline bool fmt_ok(int fmt) { return fmt == FP4Q_NVFP4 || fmt == FP4Q_MXFP4; }
+
+// Clear any stale error state before a launch, so that check_launch() sees
+// only what this call's launches produced.
+inline void clear_error() { (void)hipGetLastError(); }
+
+// Report launch errors from the calls just made on this thread.
+inline int check_launch() {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return FP4Q_ERR_HIP;
+  }
+  return FP4Q_OK;
+}
+
+constexpr int MAX_GROUPS = 2048;  // grouped GEMM scans 8 groups per thread of 256
+
+}  // namespace
+
+extern "C" {
+
+const char* fp4q_status_str(int status) {
+  switch (status) {
+    case FP4Q_OK: return "ok";
+    case FP4Q_ERR_INVALID: return "invalid argument";
+    case FP4Q_ERR_UNSUPPORTED: return "unsupported shape";
+    case FP4Q_ERR_WORKSPACE: return "workspace missing or too small";
+    case FP4Q_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+int fp4q_last_hip_error(void) { return g_last_hip_error; }
+
+size_t fp4q_quantize_workspace_bytes(fp4q_format_t fmt, int64_t rows, int64_t cols,
+                                     int32_t num_groups) {
+  (void)rows;
+  (void)cols;
+  if (fmt != FP4Q_NVFP4) return 0;
+  return (size_t)(num_groups > 0 ? num_groups : 1) * sizeof(uint32_t);
+}
+
+int fp4q_quantize(fp4q_format_t fmt, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                  const int32_t* group_offsets, int32_t num_groups, const int32_t* chan_idx,
+                  int32_t n_chan, uint8_t* q, uint8_t* scales, float* tensor_scale,
+                  uint16_t* resid, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!fmt_ok(fmt)) return FP4Q_ERR_INVALID;
+  const int blk = blk_of(fmt);
+  if (rows < 0 || cols <= 0 || cols % blk != 0 || ldx < cols || ldx % 8 != 0)
+    return FP4Q_ERR_INVALID;
+  if (num_groups < 1 || (num_groups > 1 && !group_offsets)) return FP4Q_ERR_INVALID;
+  if (n_chan < 0 || n_chan > cols) return FP4Q_ERR_INVALID;
+  if ((n_chan > 0) != (chan_idx != nullptr) || (n_chan > 0) != (resid != nullptr))
+    return FP4Q_ERR_INVALID;
+  if (fmt == FP4Q_NVFP4 && !tensor_scale) return FP4Q_ERR_INVALID;
+  if (fmt == FP4Q_MXFP4 && tensor_scale) return FP4Q_ERR_INVALID;
+  if (rows > 0 && (!x || !q || !scales)) return FP4Q_ERR_INVALID;
+  if (rows > 0 && (!aligned(x, 16) || !aligned(q, 16))) return FP4Q_ERR_INVALID;
+  if (rows * (cols / blk) > (int64_t)INT32_MAX * 256) return FP4Q_ERR_UNSUPPORTED;
+  const size_t need = fp4q_quantize_workspace_bytes(fmt, rows, cols, num_groups);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 4)))
+    return FP4Q_ERR_WORKSPACE;
+  clear_error();
+  fp4q::launch_quantize(fmt, x, rows, cols, ldx, group_offsets, num_groups, chan_idx, n_chan, q,
+                        scales, tensor_scale, resid, workspace,
+                        static_cast<hipStream_t>(stream));
+  return check_launch();
+}
+
+static int validate_gemm_common(int fmt, int64_t N, int64_t K, const uint8_t* a_q,
+                                const uint8_t* a_s, const float* a_ts, const uint8_t* b_q,
+                                const uint8_t* b_s, const float* b_ts, const int32_t* chan_idx,
+                                int32_t n_chan, const uint16_t* resid, const void* y,
+                                int y_dtype, int64_t rows) {
+  if (!fmt_ok(fmt)) return FP4Q_ERR_INVALID;
+  if (y_dtype != FP4Q_OUT_F32 && y_dtype != FP4Q_OUT_BF16) return FP4Q_ERR_INVALID;
+  if (rows < 0 || N < 0 || K <= 0 || K % blk_of(fmt) != 0) return FP4Q_ERR_INVALID;
+  if (n_chan < 0 || n_chan > K) return FP4Q_ERR_INVALID;
+  if ((n_chan > 0) != (chan_idx != nullptr) || (n_chan > 0) != (resid != nullptr))
+    return FP4Q_ERR_INVALID;
+  if (fmt == FP4Q_NVFP4 && (!a_ts || !b_ts)) return FP4Q_ERR_INVALID;
+  if (fmt == FP4Q_MXFP4 && (a_ts || b_ts)) return FP4Q_ERR_INVALID;
+  if (rows > 0 && N > 0) {
+    if (!a_q || !a_s || !b_q || !b_s || !y) return FP4Q_ERR_INVALID;
+    if (!aligned(a_q, 16) || !aligned(b_q, 16) || !aligned(a_s, 8) || !aligned(b_s, 8))
+      return FP4Q_ERR_INVALID;
+  }
+  if (K % 128 != 0) return FP4Q_ERR_UNSUPPORTED;
+  return FP4Q_OK;
+}
+
+int fp4q_gemm(fp4q_format_t fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_q,
+              const uint8_t* a_s, const float* a_ts, const uint8_t* b_q, const uint8_t* b_s,
+              const float* b_ts, const int32_t* chan_idx, int32_t n_chan, const uint16_t* resid,
+              void* y, fp4q_dtype_t y_dtype, int64_t ldy, void* stream) {
+  int rc = validate_gemm_common(fmt, N, K, a_q, a_s, a_ts, b_q, b_s, b_ts, chan_idx, n_chan,
+                                resid, y, y_dtype, M);
+  if (rc != FP4Q_OK) return rc;
+  if (ldy < N) return FP4Q_ERR_INVALID;
+  if ((M + 127) / 128 > (int64_t)UINT32_MAX || (N + 31) / 32 > 65535) return FP4Q_ERR_UNSUPPORTED;
+  clear_error();
+  fp4q::launch_gemm(fmt, M, N, K, nullptr, 1, a_q, a_s, a_ts, b_q, b_s, b_ts, chan_idx, n_chan,
+                    resid, y, y_dtype == FP4Q_OUT_BF16, ldy, static_cast<hipStream_t>(stream));
+  return check_launch();
+}
+
+int fp4q_grouped_gemm(fp4q_format_t fmt, int64_t total_rows, int64_t N, int64_t K,
+                      const int32_t* group_offsets, int32_t num_groups, const uint8_t* a_q,
+                      const uint8_t* a_s, const float* a_ts, const uint8_t* b_q,
+                      const uint8_t* b_s, const float* b_ts, const int32_t* chan_idx,
+                      int32_t n_chan, const uint16_t* resid, void* y, fp4q_dtype_t y_dtype,
+                      void* stream) {
+  int rc = validate_gemm_common(fmt, N, K, a_q, a_s, a_ts, b_q, b_s, b_ts, chan_idx, n_chan,
+                                resid, y, y_dtype, total_rows);
+  if (rc != FP4Q_OK) return rc;
+  if (num_groups < 1 || !group_offsets) return FP4Q_ERR_INVALID;
+  if (num_groups > MAX_GROUPS) return FP4Q_ERR_UNSUPPORTED;
+  if ((N + 127) / 128 > 65535) return FP4Q_ERR_UNSUPPORTED;
+  clear_error();
+  fp4q::launch_gemm(fmt, total_rows, N, K, group_offsets, num_groups, a_q, a_s, a_ts, b_q, b_s,
+                    b_ts, chan_idx, n_chan, resid, y, y_dtype == FP4Q_OUT_BF16, N,
+                    static_cast<hipStream_t>(stream));
+  return check_launch();
+}
+
+size_t fp4q_error_decompose_workspace_bytes(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols <= 0) return 0;
+  return fp4q::decompose_workspace_bytes(rows, cols);
+}
+
+int fp4q_error_decompose(fp4q_format_t fmt, const uint16_t* x, int64_t rows, int64_t cols,
+                         int64_t ldx, fp4q_err_stats_t* out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (!fmt_ok(fmt)) return FP4Q_ERR_INVALID;
+  if (rows < 0 || cols <= 0 || cols % 32 != 0 || ldx < cols || ldx % 8 != 0)
+    return FP4Q_ERR_INVALID;
+  if (!out || !aligned(out, 8)) return FP4Q_ERR_INVALID;
+  if (rows > 0 && (!x || !aligned(x, 16))) return FP4Q_ERR_INVALID;
+  if (fmt != FP4Q_MXFP4) return FP4Q_ERR_UNSUPPORTED;
+  const size_t need = fp4q::decompose_workspace_bytes(rows, cols);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return FP4Q_ERR_WORKSPACE;
+  clear_error();
+  fp4q::launch_decompose(x, rows, cols, ldx, out, workspace, static_cast<hipStream_t>(stream));
+  return check_launch();
+}
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+// fp4q_device.h -- device-side number-format helpers for gfx950 kernels.
+//
+// E2M1 / E4M3 / E8M0 / BF16 encode and decode as used by the quantizer and
+// the GEMM prologues.  These are branch-light integer and compare forms
+// (threshold tables, exponent-field arithmetic), written for VALU
+// throughput; their results are defined by the format rules stated in
+// include/fp4q.h.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4q {
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// Nearest-even float -> bf16 (inputs finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// E2M1 magnitude code of a >= 0 by its decision thresholds (the midpoints of
+// the grid 0, .5, 1, 1.5, 2, 3, 4, 6): at a midpoint the even mantissa code
+// wins, so 0.25, 1.25, 2.5, 5 round down and 0.75, 1.75, 3.5 round up.
+__device__ __forceinline__ uint32_t e2m1_mag_code(float a) {
+  return (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+         (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+         (uint32_t)(a > 5.0f);
+}
+
+// E2M1 magnitude of a code's 3 low bits, as float.
+__device__ __forceinline__ float e2m1_mag_value(uint32_t c) {
+  // c = (exp << 1) | mant; exp 0 -> 0.5 * mant, else 2^(exp-1) * (1 + mant/2)
+  uint32_t e = (c >> 1) & 3u, m = c & 1u;
+  float v = e ? __uint_as_float((126u + e) << 23 | (m << 22)) : 0.5f * (float)m;
+  return v;
+}
+
+// E4M3 (FN) value of a non-negative code: the code's 7 low bits placed at
+// the top of an FP32 exponent/mantissa field give 2^-120 times the value, for
+// normal and subnormal codes alike.
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  return __uint_as_float((c & 0x7Fu) << 20) * 0x1p120f;
+}
+
+// Nearest-even E4M3 code of v >= 0, saturating at 448 (0x7E).
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+  if (v >= 448.0f) return 0x7Eu;
+  if (v < 0x1p-6f) {
+    // subnormal range: multiples of 2^-9; rintf rounds half to even
+    return (uint32_t)rintf(v * 512.0f);
+  }
+  uint32_t u = __float_as_uint(v);
+  u += 0x7FFFFu + ((u >> 20) & 1u);  // round mantissa to 3 bits, ties to even
+  return (u >> 20) - (120u << 3);     // rebias exponent 127 -> 7
+}
+
+// MXFP4 block exponent: smallest e in [-127, 127] with 6 * 2^e >= amax.
+// amax = f * 2^E, f in [1, 2): e = E - 2 when f <= 1.5, else E - 1.
+__device__ __forceinline__ int mx_exponent(float amax) {
+  uint32_t u = __float_as_uint(amax);
+  int ef = (int)(u >> 23);
+  if (ef == 0) return -127;  // zero or subnormal amax: 6 * 2^-127 covers it
+  int E = ef - 127;
+  int e = ((u & 0x7FFFFFu) <= 0x400000u) ? E - 2 : E - 1;
+  return e < -127 ? -127 : e;
+}
+
+// 2^e as float for e in [-127, 127] (2^-127 is an FP32 subnormal).
+__device__ __forceinline__ float exp2i(int e) {
+  return e >= -126 ? __uint_as_float((uint32_t)(e + 127) << 23) : __uint_as_float(0x00400000u);
+}
+
+// NVFP4 tensor scale from the tensor amax.
+__device__ __forceinline__ float nv_tensor_scale(float amax) {
+  float t = amax / 2688.0f;
+  return (amax == 0.0f || t == 0.0f) ? 1.0f : t;
+}
+
+}  // namespace fp4q

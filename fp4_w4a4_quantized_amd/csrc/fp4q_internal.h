@@ -1,0 +1,27 @@
+// fp4q_internal.h -- declarations shared by the library's translation units.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/fp4q.h"
+
+namespace fp4q {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+int launch_quantize(int fmt, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                    const int32_t* off, int G, const int32_t* chan, int nS, uint8_t* q,
+                    uint8_t* scales, float* tscale, uint16_t* resid, void* ws,
+                    hipStream_t stream);
+
+int launch_gemm(int fmt, int64_t M, int64_t N, int64_t K, const int32_t* off, int G,
+                const uint8_t* aq, const uint8_t* as, const float* ats, const uint8_t* bq,
+                const uint8_t* bs, const float* bts, const int32_t* chan, int nS,
+                const uint16_t* resid, void* y, int y_bf16, int64_t ldy, hipStream_t stream);
+
+size_t decompose_workspace_bytes(int64_t rows, int64_t cols);
+int launch_decompose(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                     fp4q_err_stats_t* out, void* ws, hipStream_t stream);
+
+}  // namespace fp4q

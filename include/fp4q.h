@@ -1,0 +1,199 @@
+/*
+ * fp4q.h -- C ABI of libfp4q: block-scaled FP4 (NVFP4 / MXFP4) activation
+ * quantization, the W4A4 GEMM with fused sparse residual compensation, its
+ * expert-grouped (MoE) form, and the exact three-way MXFP4 error
+ * decomposition, on AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow these pages:
+ *  - "QUADS: Stabilizing NVFP4 Reinforcement Learning for MoE via
+ *    QUantization-error Alignment across Dual Sides", abstract: NVFP4 combines
+ *    fine-grained scaling with native W4A4 FP4 GEMMs; activations are
+ *    re-quantized online every forward pass; Residual Activation
+ *    Compensation corrects high-error activation channels while keeping the
+ *    W4A4 GEMM native; weights share one quantize-dequantize path.
+ *  - its German explainer (gist.science), section 2.2 B: a residual term on
+ *    selected channels is added to the quantized output.
+ *  - "FourSight: Stable FP4 RL Post-Training via Sequence Filtering and Sparse
+ *    Channel Compensation", abstract: a few top-variance activation channels
+ *    are kept in BF16 inside an otherwise NVFP4 GEMM.
+ *  - "Decomposing MXFP4 quantization error for LLM reinforcement learning",
+ *    abstract: MXFP4 error = scale bias + deadzone truncation + grid noise,
+ *    exactly.
+ *
+ * Formats (the pages name them; block sizes and encodings are the reading
+ * this library implements):
+ *  - element: E2M1, magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}, sign in bit 3;
+ *    round to nearest, ties to the even mantissa bit, saturating at 6; the
+ *    sign bit is the input's sign bit (so -0 gives code 0x8).
+ *  - NVFP4: 16-element blocks along the contiguous dimension; block scale
+ *    E4M3 (bias 7, largest 448, satfinite, nearest-even) of
+ *    (block_amax / 6) / t, where t = tensor_amax / 2688 (FP32; t = 1 when
+ *    the amax is 0); element = e2m1(x / (scale * t)).
+ *  - MXFP4: 32-element blocks; scale 2^e with the smallest e in [-127, 127]
+ *    such that 6 * 2^e >= block_amax, stored as E8M0 code e + 127;
+ *    element = e2m1(x * 2^-e).  No tensor scale.
+ *  - packing: two codes per byte, even element in the low nibble.
+ *
+ * Conventions for every entry point:
+ *  - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    allocates nothing and keeps no state beyond a thread-local last error.
+ *  - Every call is asynchronous on the caller's HIP stream (passed as void*,
+ *    NULL = default stream); results are ready when that stream is.
+ *  - Layouts are row-major with the FP4 blocks along the contiguous (K)
+ *    dimension.  Weights are passed transposed, W^T [N, K].
+ *  - Arguments are validated on the host before any HIP call; device-side
+ *    contents are preconditions and are NOT checked (doing so would need a
+ *    synchronisation): channel lists ascending, unique and < K; group
+ *    offsets non-decreasing with offsets[0] = 0 and offsets[G] = rows;
+ *    inputs finite; dequantized products within FP32 range.
+ *  - No C++ exception crosses the ABI.
+ */
+#ifndef FP4Q_H
+#define FP4Q_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FP4Q_NVFP4 = 0, FP4Q_MXFP4 = 1 } fp4q_format_t;
+typedef enum { FP4Q_OUT_F32 = 0, FP4Q_OUT_BF16 = 1 } fp4q_dtype_t;
+
+/* Status codes. */
+#define FP4Q_OK 0
+#define FP4Q_ERR_INVALID (-1)     /* null pointer with non-zero size, bad enum, bad shape or stride, misaligned pointer */
+#define FP4Q_ERR_UNSUPPORTED (-2) /* a valid shape the kernels do not take (e.g. K not a multiple of 128 in a GEMM) */
+#define FP4Q_ERR_WORKSPACE (-3)   /* workspace missing or smaller than the *_workspace_bytes query */
+#define FP4Q_ERR_HIP (-4)         /* a HIP call failed; fp4q_last_hip_error() returns its hipError_t */
+
+/* Message for a status code (static storage). */
+const char* fp4q_status_str(int status);
+
+/* hipError_t of the last FP4Q_ERR_HIP on the calling thread (0 if none). */
+int fp4q_last_hip_error(void);
+
+/* ------------------------------------------------------------------------
+ * Activation (or weight) quantization.  QUADS abstract: activations are
+ * quantized online each forward pass (weights go through the same path once
+ * per weight sync, with n_chan = 0); QUADS explainer section 2.2 B /
+ * FourSight abstract: the residual of the selected channels is kept.
+ *
+ *   x             bf16 [rows, cols], row stride ldx elements (ldx >= cols,
+ *                 ldx % 8 == 0, x 16-byte aligned)
+ *   group_offsets device int32 [num_groups + 1] row ranges, one quantization
+ *                 group each (own tensor scale and channel list); NULL with
+ *                 num_groups == 1 means one group of all rows
+ *   chan_idx      device int32 [num_groups, n_chan]: channels (columns) whose
+ *                 residual is emitted, ascending per group; NULL iff n_chan == 0
+ *   q             out u8 [rows, cols/2] packed codes (16-byte aligned)
+ *   scales        out u8 [rows, cols/blk] block scale codes (blk 16 / 32)
+ *   tensor_scale  out f32 [num_groups] (NVFP4; must be NULL for MXFP4);
+ *                 empty groups get 1.0
+ *   resid         out bf16 [rows, n_chan]: bf16_rne(x - deq(code)) at
+ *                 column chan_idx[g][j]; deq = (e2m1 * scale) * t in FP32
+ *                 (NVFP4) or e2m1 * 2^e (MXFP4); NULL iff n_chan == 0
+ *   workspace     device scratch of fp4q_quantize_workspace_bytes() bytes
+ *                 (NVFP4 only; may be NULL when that is 0); contents need
+ *                 no initialisation and are left undefined
+ *
+ * cols must be a multiple of the block size; 0 <= n_chan <= cols.
+ * ------------------------------------------------------------------------ */
+size_t fp4q_quantize_workspace_bytes(fp4q_format_t fmt, int64_t rows, int64_t cols,
+                                     int32_t num_groups);
+
+int fp4q_quantize(fp4q_format_t fmt, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                  const int32_t* group_offsets, int32_t num_groups, const int32_t* chan_idx,
+                  int32_t n_chan, uint8_t* q, uint8_t* scales, float* tensor_scale,
+                  uint16_t* resid, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Compensated W4A4 GEMM.  QUADS abstract (native W4A4 FP4 GEMM plus
+ * Residual Activation Compensation on high-error channels), explainer
+ * section 2.2 B (residual term added to the quantized output), FourSight
+ * abstract (sparse BF16 channels spliced into the NVFP4 GEMM):
+ *
+ *   Y[m, n] = sum_k A[m, k] * B[n, k] + sum_j R[m, j] * B[n, S_j]
+ *
+ * with A = deq(a_q, a_s, a_ts) [M, K], B = deq(b_q, b_s, b_ts) [N, K]
+ * (weights as W^T) and S = chan_idx.  Accumulation is FP32 (MFMA); the
+ * result equals the exact sum within (K + n_chan) * 2^-23 * sum|terms|.
+ *
+ *   a_q, a_s   u8 [M, K/2], [M, K/blk] (16-byte aligned)
+ *   a_ts       device f32 [1] tensor scale (NVFP4), NULL for MXFP4
+ *   b_q, b_s   u8 [N, K/2], [N, K/blk] (16-byte aligned)
+ *   b_ts       device f32 [1] (NVFP4), NULL for MXFP4
+ *   chan_idx   device int32 [n_chan] ascending, < K; resid bf16 [M, n_chan]
+ *              (both NULL iff n_chan == 0)
+ *   y          out [M, ldy] f32 or bf16 (nearest-even), ldy >= N
+ *
+ * K must be a multiple of 128 (FP4Q_ERR_UNSUPPORTED otherwise).
+ * ------------------------------------------------------------------------ */
+int fp4q_gemm(fp4q_format_t fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_q,
+              const uint8_t* a_s, const float* a_ts, const uint8_t* b_q, const uint8_t* b_s,
+              const float* b_ts, const int32_t* chan_idx, int32_t n_chan, const uint16_t* resid,
+              void* y, fp4q_dtype_t y_dtype, int64_t ldy, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Expert-grouped compensated GEMM (MoE layer; QUADS abstract: NVFP4 rollout
+ * for Mixture-of-Experts).  Rows [off[g], off[g+1]) of the permuted
+ * activations use expert g's weights, tensor scales and channel list:
+ *
+ *   group_offsets  device int32 [G + 1]
+ *   a_q, a_s       [total_rows, K/2], [total_rows, K/blk]
+ *   a_ts           device f32 [G] (NVFP4), NULL for MXFP4
+ *   b_q, b_s       [G, N, K/2], [G, N, K/blk]
+ *   b_ts           device f32 [G] (NVFP4), NULL for MXFP4
+ *   chan_idx       device int32 [G, n_chan]; resid bf16 [total_rows, n_chan]
+ *   y              out [total_rows, N] (row stride N)
+ *
+ * Empty groups produce nothing.  K must be a multiple of 128.
+ * ------------------------------------------------------------------------ */
+int fp4q_grouped_gemm(fp4q_format_t fmt, int64_t total_rows, int64_t N, int64_t K,
+                      const int32_t* group_offsets, int32_t num_groups, const uint8_t* a_q,
+                      const uint8_t* a_s, const float* a_ts, const uint8_t* b_q,
+                      const uint8_t* b_s, const float* b_ts, const int32_t* chan_idx,
+                      int32_t n_chan, const uint16_t* resid, void* y, fp4q_dtype_t y_dtype,
+                      void* stream);
+
+/* ------------------------------------------------------------------------
+ * Exact three-way MXFP4 error decomposition ("Decomposing MXFP4
+ * quantization error ...", abstract).  Per 32-block with actual scale
+ * s = 2^e and ideal scale s* = amax/6, per element x:
+ *   total      = x - Q_s(x)
+ *   deadzone   = x               where Q_s(x) = 0, else 0
+ *   grid_noise = x - Q*(x)       where Q_s(x) != 0, else 0
+ *   scale_bias = Q*(x) - Q_s(x)  where Q_s(x) != 0, else 0
+ * Q_s is the MXFP4 quantizer, Q* the same E2M1 rounding with s*.  So
+ * total = scale_bias + deadzone + grid_noise element by element, and the
+ * exact integer sums below satisfy the identity bit for bit.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+    /* 6 * (sum of component c) as a 320-bit two's complement integer in units
+     * of 2^-136, 5 little-endian 64-bit limbs; c = 0 total, 1 scale_bias,
+     * 2 deadzone, 3 grid_noise */
+    int64_t exact[4][5];
+    double sum[4];       /* the same sums as doubles (approximate) */
+    double sumsq[4];     /* FP64 sums of squared components */
+    double cross_sb_gn;  /* FP64 sum of scale_bias * grid_noise */
+    int64_t n_elems;     /* rows * cols */
+    int64_t n_deadzone;  /* non-zero inputs quantized to zero */
+    int64_t n_clipped;   /* |x| > 6 * 2^e (0 under the scale rule) */
+} fp4q_err_stats_t;
+
+/*   fmt        must be FP4Q_MXFP4 (NVFP4 gives FP4Q_ERR_UNSUPPORTED)
+ *   x          bf16 [rows, cols], ldx as for fp4q_quantize; cols % 32 == 0
+ *   out        DEVICE pointer to one fp4q_err_stats_t (8-byte aligned)
+ *   workspace  device scratch of fp4q_error_decompose_workspace_bytes() */
+size_t fp4q_error_decompose_workspace_bytes(int64_t rows, int64_t cols);
+
+int fp4q_error_decompose(fp4q_format_t fmt, const uint16_t* x, int64_t rows, int64_t cols,
+                         int64_t ldx, fp4q_err_stats_t* out, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4Q_H */

@@ -1,0 +1,112 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/fp4q.h declares, and rejects invalid arguments on the host before any
+HIP call (status codes as documented in the header)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp4q.h")
+
+INVALID, UNSUPPORTED, WORKSPACE = -1, -2, -3
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp4q_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from fp4_w4a4_quantized_amd import binding
+    return binding.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert {"fp4q_quantize", "fp4q_gemm", "fp4q_grouped_gemm", "fp4q_error_decompose"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    assert L.fp4q_status_str(0) == b"ok"
+    assert L.fp4q_status_str(-4) == b"HIP error"
+    assert L.fp4q_status_str(12345) == b"unknown status"
+    assert L.fp4q_last_hip_error() == 0
+
+
+def test_workspace_queries(L):
+    assert L.fp4q_quantize_workspace_bytes(0, 100, 64, 5) == 20
+    assert L.fp4q_quantize_workspace_bytes(1, 100, 64, 5) == 0
+    assert L.fp4q_error_decompose_workspace_bytes(8192, 4096) >= 256
+
+
+# Fake, never-dereferenced device addresses: validation fails before use.
+A = ctypes.c_void_p(0x10000)
+B = ctypes.c_void_p(0x20000)
+
+
+def q(L, fmt=0, x=A, rows=4, cols=64, ldx=64, off=None, G=1, chan=None, nS=0, qq=B, sc=B,
+      ts=B, R=None, ws=A, wsb=64):
+    return L.fp4q_quantize(fmt, x, rows, cols, ldx, off, G, chan, nS, qq, sc, ts, R, ws, wsb, None)
+
+
+def test_quantize_rejects(L):
+    assert q(L, fmt=7) == INVALID
+    assert q(L, cols=40) == INVALID              # not a multiple of 16
+    assert q(L, fmt=1, ts=None, cols=48) == INVALID   # MXFP4 needs cols % 32
+    assert q(L, ldx=32) == INVALID               # ldx < cols
+    assert q(L, ldx=68) == INVALID               # ldx % 8
+    assert q(L, rows=-1) == INVALID
+    assert q(L, G=0) == INVALID
+    assert q(L, G=3, off=None) == INVALID
+    assert q(L, nS=2, chan=None, R=B) == INVALID
+    assert q(L, nS=2, chan=A, R=None) == INVALID
+    assert q(L, nS=65, chan=A, R=B) == INVALID   # more channels than columns
+    assert q(L, ts=None) == INVALID              # NVFP4 needs the tensor scale
+    assert q(L, fmt=1) == INVALID                # MXFP4 takes none
+    assert q(L, x=None) == INVALID
+    assert q(L, x=ctypes.c_void_p(0x10008)) == INVALID   # misaligned
+    assert q(L, ws=None) == WORKSPACE
+    assert q(L, wsb=2) == WORKSPACE
+
+
+def g(L, fmt=0, M=4, N=8, K=256, aq=A, as_=A, ats=B, bq=B, bs=B, bts=B, chan=None, nS=0, R=None,
+      y=A, dt=0, ldy=8):
+    return L.fp4q_gemm(fmt, M, N, K, aq, as_, ats, bq, bs, bts, chan, nS, R, y, dt, ldy, None)
+
+
+def test_gemm_rejects(L):
+    assert g(L, fmt=2) == INVALID
+    assert g(L, dt=5) == INVALID
+    assert g(L, K=40) == INVALID
+    assert g(L, K=144) == UNSUPPORTED            # valid NVFP4 K, not a multiple of 128
+    assert g(L, ldy=4) == INVALID
+    assert g(L, ats=None) == INVALID
+    assert g(L, fmt=1) == INVALID                # MXFP4 with tensor scales
+    assert g(L, nS=3, chan=A, R=None) == INVALID
+    assert g(L, nS=300, chan=A, R=B) == INVALID
+    assert g(L, aq=ctypes.c_void_p(0x10004)) == INVALID
+    assert g(L, y=None) == INVALID
+
+
+def test_grouped_gemm_rejects(L):
+    f = L.fp4q_grouped_gemm
+    assert f(0, 10, 8, 256, None, 2, A, A, B, B, B, B, None, 0, None, A, 0, None) == INVALID
+    assert f(0, 10, 8, 256, A, 0, A, A, B, B, B, B, None, 0, None, A, 0, None) == INVALID
+    assert f(0, 10, 8, 256, A, 5000, A, A, B, B, B, B, None, 0, None, A, 0, None) == UNSUPPORTED
+    # MXFP4 takes no tensor scales
+    assert f(1, 10, 8, 256, A, 2, A, A, B, B, B, None, None, 0, None, A, 0, None) == INVALID
+
+
+def test_error_decompose_rejects(L):
+    f = L.fp4q_error_decompose
+    assert f(1, A, 4, 48, 48, B, A, 1 << 20, None) == INVALID     # cols % 32
+    assert f(1, A, 4, 64, 64, None, A, 1 << 20, None) == INVALID  # no output
+    assert f(0, A, 4, 64, 64, B, A, 1 << 20, None) == UNSUPPORTED  # NVFP4 split is not offered
+    assert f(1, A, 4, 64, 64, B, None, 0, None) == WORKSPACE
+    assert f(1, A, 4, 64, 64, B, A, 8, None) == WORKSPACE

@@ -1,0 +1,110 @@
+"""GPU parity of fp4q_quantize against the oracle: codes, block scales,
+tensor scales and residuals bit for bit, at the workload shapes (full
+tensors), ragged shapes and the degenerate cases."""
+import numpy as np
+import pytest
+import torch
+
+import fp4_w4a4_quantized_amd as fq
+from gpu_helpers import workload, assert_quant_equal, need_gpu, say, to_dev
+from workloads import CONFIGS, bf16_bits, dense_case, moe_case
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(orc, fmt, x, chan=None, offsets=None):
+    dev = need_gpu()
+    ref = orc.quantize(fmt, x, offsets=offsets, chan_idx=chan)
+    got = fq.quantize(fmt, to_dev(x), group_offsets=None if offsets is None else to_dev(offsets),
+                      chan_idx=None if chan is None else to_dev(np.ascontiguousarray(chan)))
+    torch.cuda.synchronize(dev)
+    assert_quant_equal(got, ref, fmt)
+
+
+@pytest.mark.parametrize("name", ["tiny_nvfp4", "decode_nvfp4", "prefill_nvfp4", "prefill_mxfp4"])
+def test_workload_activations(orc, name):
+    cfg = CONFIGS[name]
+    say(f"quantize activations {name}")
+    d = dense_case(**{**cfg, "N": 8})   # weights are not needed here
+    _run(orc, 0 if cfg["fmt"] == "nvfp4" else 1, d["x"], d["chan_idx"])
+
+
+@pytest.mark.parametrize("name", ["tiny_nvfp4", "decode_nvfp4"])
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_workload_weights(orc, name, fmt):
+    say(f"quantize weights {name} fmt {fmt}")
+    d = workload(name)
+    _run(orc, fmt, d["wt"])
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("rows,cols,nS", [(1, 256, 3), (37, 96 * 2, 11), (100, 64, 64),
+                                          (300, 512, 0), (5, 2048, 2048)])
+def test_ragged_and_channel_counts(orc, fmt, rows, cols, nS):
+    if fmt == 1 and cols % 32:
+        pytest.skip("MXFP4 needs cols % 32")
+    say(f"quantize ragged fmt {fmt} {rows}x{cols} nS {nS}")
+    d = dense_case(rows, cols, 8, n_out=max(1, cols // 100), seed=rows * 7 + cols)
+    chan = np.sort(np.random.default_rng(rows).choice(cols, nS, replace=False)).astype(np.int32)
+    _run(orc, fmt, d["x"], chan if nS else None)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_special_values(orc, fmt):
+    say(f"quantize special values fmt {fmt}")
+    rng = np.random.default_rng(5)
+    x = bf16_bits(rng.standard_normal((16, 256)).astype(np.float32))
+    x[0] = 0                        # all-zero row
+    x[1, :32] = 0x8000              # -0.0
+    x[2, :] = np.arange(256, dtype=np.uint16) + 1          # positive subnormals
+    x[3, :] = (np.arange(256, dtype=np.uint16) + 1) | 0x8000
+    x[4, :16] = 0x7F7F              # largest finite bf16
+    x[4, 16:32] = 0xFF7F
+    x[5, :] = bf16_bits(np.full(256, 1e-30, np.float32))
+    x[6, ::2] = bf16_bits(np.float32(2.5))                 # exact ties
+    x[7, :] = bf16_bits(np.linspace(-7, 7, 256).astype(np.float32))
+    chan = np.arange(0, 256, 9, dtype=np.int32)
+    _run(orc, fmt, x, chan)
+    # tiny-magnitude tensor (tensor scale far below one)
+    _run(orc, fmt, x[2:4].copy(), chan)
+
+
+def test_ldx_larger_than_cols(orc):
+    need_gpu()
+    say("quantize with row stride > cols")
+    d = dense_case(20, 320, 8, seed=9)
+    ref = orc.quantize(0, d["x"][:, :256].copy(), chan_idx=np.array([1, 255], np.int32))
+    xt = to_dev(d["x"])[:, :256]    # a strided view: ldx = 320
+    got = fq.quantize(0, xt, chan_idx=to_dev(np.array([1, 255], np.int32)))
+    torch.cuda.synchronize()
+    assert_quant_equal(got, ref, 0)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_grouped_small(orc, fmt):
+    say(f"quantize grouped small fmt {fmt}")
+    x = dense_case(90, 256, 8, n_out=3, seed=41)["x"]
+    off = np.array([0, 0, 13, 13, 14, 60, 90, 90], np.int32)   # empty and 1-row groups
+    G = off.size - 1
+    rng = np.random.default_rng(2)
+    chan = np.sort(np.stack([rng.choice(256, 7, replace=False) for _ in range(G)]), 1)
+    _run(orc, fmt, x, chan.astype(np.int32), off)
+
+
+def test_grouped_moe_workload(orc):
+    """MoE layer at full size: 32768 routed rows x 2048, 128 experts with
+    per-expert tensor scales and 32 channels each (and the down input)."""
+    say("quantize grouped MoE workload")
+    m = moe_case(**CONFIGS["moe_nvfp4"], with_weights=False)
+    _run(orc, 0, m["x_perm"], m["chan_gate_up"], m["offsets"])
+    _run(orc, 0, m["h_perm"], m["chan_down"], m["offsets"])
+
+
+def test_deterministic(orc):
+    dev = need_gpu()
+    d = dense_case(64, 2048, 8, n_out=20, seed=2)
+    x = to_dev(d["x"])
+    a = fq.quantize(0, x, chan_idx=to_dev(d["chan_idx"]) if d["chan_idx"].size else None)
+    b = fq.quantize(0, x)
+    torch.cuda.synchronize(dev)
+    assert torch.equal(a["q"], b["q"]) and torch.equal(a["scales"], b["scales"])
