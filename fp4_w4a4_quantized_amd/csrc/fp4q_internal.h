@@ -20,6 +20,12 @@ int launch_gemm(int fmt, int64_t M, int64_t N, int64_t K, const int32_t* off, in
                 const uint8_t* bs, const float* bts, const int32_t* chan, int nS,
                 const uint16_t* resid, void* y, int y_bf16, int64_t ldy, hipStream_t stream);
 
+bool big_gemm_eligible(int64_t M, int64_t N, int64_t K, int nS);
+int launch_gemm_big(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* aq,
+                    const uint8_t* as, const float* ats, const uint8_t* bq, const uint8_t* bs,
+                    const float* bts, const int32_t* chan, int nS, const uint16_t* resid,
+                    void* y, int y_bf16, int64_t ldy, hipStream_t stream);
+
 size_t decompose_workspace_bytes(int64_t rows, int64_t cols);
 int launch_decompose(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                      fp4q_err_stats_t* out, void* ws, hipStream_t stream);

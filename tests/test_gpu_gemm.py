@@ -92,6 +92,23 @@ def test_ragged(orc, fmt, M, N, K, nS):
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("M,N,K,nS", [(300, 520, 512, 100), (256, 256, 256, 0), (513, 300, 768, 128),
+                                      (260, 270, 256, 129), (1024, 768, 1024, 16)])
+def test_large_tiles_ragged(orc, fmt, M, N, K, nS):
+    """Shapes that take the 256x256-tile pipelined kernel (M, N >= 256,
+    K % 256 == 0, |S| <= 128), with ragged edges, and the fallback past it."""
+    need_gpu()
+    say(f"gemm large-tile fmt {fmt} M{M} N{N} K{K} nS{nS}")
+    d = dense_case(M, K, N, n_out=max(1, K // 100), seed=M + 7 * N + K + nS)
+    chan = np.sort(np.random.default_rng(N).choice(K, nS, replace=False)).astype(np.int32)
+    chan = chan if nS else None
+    qa, qb = _prep(orc, fmt, d, chan)
+    y = to_host(_gpu_gemm(fmt, qa, qb, chan))
+    yo, ya = _oracle_full(orc, fmt, qa, qb, chan)
+    assert_gemm_close(y, yo, ya)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
 def test_bf16_output_and_ldy(orc, fmt):
     need_gpu()
     say(f"gemm bf16 out + ldy fmt {fmt}")
