@@ -8,6 +8,10 @@ compensated W4A4 GEMM.  Weights are quantized once before timing (they are
 re-quantized only at weight sync).  Enough distinct weight and output copies
 rotate to defeat the 256 MB last-level cache on the memory-bound workloads.
 
+The timed steps run as one captured HIP graph (host launch cost out of the
+measurement); per-kernel times come from HIP events around a graph of
+repeated launches of that kernel on the same stream.
+
 Default workload: dense decode NVFP4, X [64 x 2048], W [2048 x 11008],
 |S| = 64.  Prints ONE JSON line.  --workload selects another configuration
 (prefill_nvfp4, prefill_mxfp4, moe_nvfp4, tiny_nvfp4) for profiling.
@@ -70,17 +74,6 @@ def load_traffic(workload: str, kernel_hash: str):
     return None
 
 
-class Timer:
-    """HIP events on a given stream."""
-
-    def __init__(self, torch, stream):
-        self.torch, self.stream = torch, stream
-
-    def pair(self):
-        t = self.torch
-        return t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
-
-
 def main():
     args = parse()
     if args.gpus != 1:
@@ -96,7 +89,11 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     dev = torch.device("cuda:0")
-    stream = torch.cuda.current_stream(dev)
+    # an explicit stream (default priority) for all work and for the timing
+    # events.  Library calls take the current stream (no explicit argument):
+    # under graph capture that is the capture stream.
+    stream = torch.cuda.Stream(dev)
+    torch.cuda.set_stream(stream)
     name = args.workload
     cfg = CONFIGS[name]
     fmt = fq.NVFP4 if cfg["fmt"] == "nvfp4" else fq.MXFP4
@@ -138,12 +135,12 @@ def main():
         ar = torch.empty((M, nS), dtype=torch.int16, device=dev) if nS else None
 
         def quant():
-            fq.quantize_into(fmt, x, None, 1, chan, nS, aq, asc, ats, ar, qws, stream)
+            fq.quantize_into(fmt, x, None, 1, chan, nS, aq, asc, ats, ar, qws)
 
         def gemm(i):
             w = wcopies[i % n_rot]
             fq.gemm_into(fmt, M, N, K, aq, asc, ats, w["q"], w["scales"], w["tscale"], chan, nS,
-                         ar, ys[i % n_rot], 0, N, stream)
+                         ar, ys[i % n_rot], 0, N)
 
         flops = 2.0 * M * N * K
         gemm_bytes = (M * K // 2 + M * K // blk + M * nS * 2 + nS * 4 + w_bytes + y_bytes +
@@ -188,13 +185,13 @@ def main():
             for tag, xin, ch in (("gu", xg, cg), ("dn", xd, cd)):
                 b = bufs[tag]
                 fq.quantize_into(fmt, xin, off, G, ch, nS, b["q"], b["s"], b["t"], b["r"],
-                                 b["ws"], stream)
+                                 b["ws"])
 
         def gemm(i):
             for tag, w, y, n, k, ch in (("gu", wgu, ygu, I2, H, cg), ("dn", wdn, ydn, H, I, cd)):
                 b = bufs[tag]
                 fq.grouped_gemm_into(fmt, rows, n, k, off, G, b["q"], b["s"], b["t"], w[0], w[1],
-                                     w[2], ch, nS, b["r"], y, 0, stream)
+                                     w[2], ch, nS, b["r"], y, 0)
 
         loads = data["loads"]
         active = int((loads > 0).sum())
@@ -214,35 +211,49 @@ def main():
         quant()
         gemm(i)
 
-    # ---- warmup + timed steps --------------------------------------------------
+    # ---- warmup (eager), then the K timed steps as one HIP graph ----------------
+    # Launching each kernel from Python costs more host time than the decode
+    # kernels take on the GPU, so the timed steps are captured once and
+    # replayed: the GPU then runs them back to back, as a serving loop does.
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+
+    def capture(fn, n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                fn(i)
+        torch.cuda.synchronize()
+        g.replay()  # untimed first replay
+        torch.cuda.synchronize()
+        return g
+
+    g_steps = capture(step, args.steps)
     t_start = time.perf_counter()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record(stream)
-    for i in range(args.steps):
-        step(i)
+    g_steps.replay()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     step_ms = ev0.elapsed_time(ev1) / args.steps
     print(f"[bench] {args.steps} steps: {step_ms * 1e3:.2f} us/step (wall {wall:.3f}s)",
           file=sys.stderr, flush=True)
+    del g_steps
 
-    # ---- per-kernel averages with HIP events on the launch stream -------------
+    # ---- per-kernel averages: HIP events on the launch stream around a graph of
+    # `reps` launches of one kernel sequence
     def timed(fn, reps):
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(reps)]
-        for i, (a, b) in enumerate(evs):
-            a.record(stream)
-            fn(i)
-            b.record(stream)
+        g = capture(fn, reps)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.replay()
+        b.record(stream)
         torch.cuda.synchronize()
-        return sum(a.elapsed_time(b) for a, b in evs) / reps * 1e-3  # seconds
+        return a.elapsed_time(b) / reps * 1e-3  # seconds
 
     reps = max(args.steps, 20)
-    quant(); gemm(0); torch.cuda.synchronize()
     t_gemm = timed(gemm, reps)
     t_quant = timed(lambda i: quant(), reps)
     print(f"[bench] gemm {t_gemm * 1e6:.2f} us, quantize {t_quant * 1e6:.2f} us per launch",

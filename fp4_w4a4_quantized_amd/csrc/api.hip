@@ -56,8 +56,7 @@ size_t fp4q_quantize_workspace_bytes(fp4q_format_t fmt, int64_t rows, int64_t co
                                      int32_t num_groups) {
   (void)rows;
   (void)cols;
-  if (fmt != FP4Q_NVFP4) return 0;
-  return (size_t)(num_groups > 0 ? num_groups : 1) * sizeof(uint32_t);
+  return fp4q::quantize_workspace_bytes(fmt, num_groups > 0 ? num_groups : 1);
 }
 
 int fp4q_quantize(fp4q_format_t fmt, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
@@ -76,7 +75,7 @@ int fp4q_quantize(fp4q_format_t fmt, const uint16_t* x, int64_t rows, int64_t co
   if (fmt == FP4Q_MXFP4 && tensor_scale) return FP4Q_ERR_INVALID;
   if (rows > 0 && (!x || !q || !scales)) return FP4Q_ERR_INVALID;
   if (rows > 0 && (!aligned(x, 16) || !aligned(q, 16))) return FP4Q_ERR_INVALID;
-  if (rows * (cols / blk) > (int64_t)INT32_MAX * 256) return FP4Q_ERR_UNSUPPORTED;
+  if (rows * (cols / 8) >= ((int64_t)1 << 31)) return FP4Q_ERR_UNSUPPORTED;  // 32-bit chunk index
   const size_t need = fp4q_quantize_workspace_bytes(fmt, rows, cols, num_groups);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 4)))
     return FP4Q_ERR_WORKSPACE;

@@ -386,6 +386,9 @@ int launch_gemm(int fmt, int64_t M, int64_t N, int64_t K, const int32_t* off, in
     unsigned mt = (unsigned)((M + BM - 1) / BM + G);  // each group adds at most one partial tile
     if (fmt == FP4Q_NVFP4) launch_one<FP4Q_NVFP4, BM, 128, true>(a, mt, stream);
     else launch_one<FP4Q_MXFP4, BM, 128, true>(a, mt, stream);
+  } else if (skinny_gemm_eligible(M, N, K, nS, resid)) {
+    launch_gemm_skinny(fmt, M, N, K, aq, as, ats, bq, bs, bts, chan, nS, resid, y, y_bf16, ldy,
+                       stream);
   } else if (big_gemm_eligible(M, N, K, nS)) {
     launch_gemm_big(fmt, M, N, K, aq, as, ats, bq, bs, bts, chan, nS, resid, y, y_bf16, ldy,
                     stream);

@@ -1,0 +1,376 @@
+// gemm_skinny.hip -- the decode-shaped (few activation rows) compensated
+// W4A4 GEMM for gfx950.
+//
+// Same operation as gemm.hip (QUADS abstract: native W4A4 GEMM plus Residual
+// Activation Compensation; explainer section 2.2 B; FourSight abstract:
+// selected channels effectively BF16, with a separate decode datapath):
+//   Y[m,n] = sum_k A[m,k] B[n,k] + sum_j R[m,j] B[n,S_j],   M <= 64.
+// With at most 64 activation rows the cost is streaming the weights, so:
+//  * a workgroup of 8 waves owns 48 output columns (3 groups of 16) and all
+//    64 rows; the grid is about one workgroup per CU;
+//  * the waves split K: wave w takes the 128-wide K steps w, w + 8, w + 16,
+//    ... with two steps in flight.  Each lane loads its weight bytes and its
+//    activation fragments (which stay in L2: every workgroup reads them)
+//    straight into registers; the scale bytes of a step come with one
+//    coalesced load per operand and are redistributed through a
+//    wave-private LDS slot -- the main path has no barrier and waits only
+//    for its own data (load issue, not bandwidth, bounds this shape, so the
+//    load instruction count is kept low);
+//  * NVFP4 decodes both operands in registers (v_cvt_scalef32_pk_f16_fp4,
+//    then one v_pk_mul_f16 by the E4M3 block scale: exact in f16) for
+//    v_mfma_f32_16x16x32_f16; MXFP4 feeds the packed codes and E8M0 scales
+//    to v_mfma_scale_f32_16x16x128_f8f6f4 directly;
+//  * the compensation weights B[n, S_j] are taken from the weight registers
+//    of the wave whose K step holds channel S_j (decoded to bf16, exact) and
+//    written to LDS; R[:, S] is staged in LDS at the start (16-byte loads).
+//    After the eight K-partial sums meet in LDS, waves 0-3 (16 rows each)
+//    add R B_S with v_mfma_f32_16x16x16_bf16 and store
+//    y = tw * (tx * main + comp).
+// Rows past M use clamped (real) rows: a row of A only reaches the same row
+// of the product, and those rows are not stored.  Columns past N likewise.
+#include "fp4q_device.h"
+#include "fp4q_internal.h"
+
+namespace fp4q {
+
+typedef float v4f32s __attribute__((ext_vector_type(4)));
+typedef int i32x8s __attribute__((ext_vector_type(8)));
+typedef _Float16 h8s __attribute__((ext_vector_type(8)));
+typedef _Float16 h2s __attribute__((ext_vector_type(2)));
+typedef short s4s __attribute__((ext_vector_type(4)));
+
+constexpr int SK_COLS = 48;            // output columns per workgroup
+constexpr int SK_CG = 3;               // 16-column groups
+constexpr int SK_M = 64;               // activation rows handled
+constexpr int SK_WAVES = 8;
+constexpr int SK_T = 64 * SK_WAVES;
+constexpr int SK_MAXS = 64;            // compensation channels
+constexpr int SK_SRS = SK_MAXS + 4;    // LDS row stride (bf16) of R and B_S
+
+struct SkinnyArgs {
+  int64_t M, N, K;
+  const uint8_t* aq;
+  const uint8_t* as;
+  const float* ats;
+  const uint8_t* bq;
+  const uint8_t* bs;
+  const float* bts;
+  const int32_t* chan;
+  int nS;
+  const uint16_t* resid;
+  void* y;
+  int y_bf16;
+  int64_t ldy;
+};
+
+__device__ __forceinline__ h8s sk_decode8(uint32_t w, h2s s) {
+  h2s p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s;
+  h2s p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s;
+  h2s p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s;
+  h2s p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s;
+  h8s r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+__device__ __forceinline__ h2s sk_scale2(uint32_t code) {
+  _Float16 v = (_Float16)e4m3_value(code & 0xFFu);
+  return h2s{v, v};
+}
+
+// Registers of one K step for one wave.  Lane (lr = lane % 16, q = lane / 16)
+// holds:
+//   x[a]  16 bytes of activation row 16a + lr, elements 32q .. 32q+31 of the
+//         step; w[g] the same bytes of weight row col0 + 16g + lr
+//   xsc   the step's scale bytes of activation row `lane` (8 NVFP4 blocks or
+//         4 MXFP4 blocks), wsc those of weight row col0 + lane (lane < 48);
+//         loaded with one coalesced load per operand and redistributed
+//         through a wave-private LDS slot
+struct Step {
+  u32x4 x[4];
+  u32x4 w[SK_CG];
+  u32x2 xsc, wsc;
+};
+
+template <int FMT>
+__device__ __forceinline__ void load_step(const SkinnyArgs& p, int kt, int lane, int64_t col0,
+                                          Step& s) {
+  constexpr int BLK = (FMT == FP4Q_NVFP4) ? 16 : 32;
+  const int64_t K2 = p.K >> 1, KS = p.K / BLK;
+  const int q = lane >> 4, lr = lane & 15;
+#pragma unroll
+  for (int g = 0; g < SK_CG; ++g) {
+    int64_t row = col0 + 16 * g + lr;
+    row = row < p.N ? row : p.N - 1;
+    s.w[g] = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(p.bq + row * K2 + (int64_t)kt * 64 + q * 16));
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    int64_t row = 16 * a + lr;
+    row = row < p.M ? row : p.M - 1;
+    s.x[a] = *reinterpret_cast<const u32x4*>(p.aq + row * K2 + (int64_t)kt * 64 + q * 16);
+  }
+  int64_t wrow = col0 + (lane < SK_COLS ? lane : SK_COLS - 1);
+  wrow = wrow < p.N ? wrow : p.N - 1;
+  const int64_t xrow = lane < p.M ? lane : p.M - 1;
+  if (FMT == FP4Q_NVFP4) {
+    s.wsc = *reinterpret_cast<const u32x2*>(p.bs + wrow * KS + (int64_t)kt * 8);
+    s.xsc = *reinterpret_cast<const u32x2*>(p.as + xrow * KS + (int64_t)kt * 8);
+  } else {
+    s.wsc = u32x2{*reinterpret_cast<const uint32_t*>(p.bs + wrow * KS + (int64_t)kt * 4), 0u};
+    s.xsc = u32x2{*reinterpret_cast<const uint32_t*>(p.as + xrow * KS + (int64_t)kt * 4), 0u};
+  }
+}
+
+// Element e (0..31) of a lane's 16 packed bytes: its 4-bit code.
+__device__ __forceinline__ uint32_t nibble_of(u32x4 v, int e) {
+  const int d = e >> 3;  // wave-uniform
+  const uint32_t word = d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w;
+  return (word >> (4 * (e & 7))) & 15u;
+}
+
+// Bytes of one wave-private scale slot: weight rows then activation rows.
+template <int FMT> struct SlotLayout {
+  static constexpr int PER_ROW = (FMT == FP4Q_NVFP4) ? 8 : 4;  // scale bytes per row per step
+  static constexpr int X_OFF = SK_COLS * PER_ROW;
+  static constexpr int BYTES = X_OFF + SK_M * PER_ROW;
+};
+
+// Multiply one K step into the accumulators; take the compensation weights
+// of the channels that fall in it.
+template <int FMT>
+__device__ __forceinline__ void process_step(const Step& st, int kt, uint8_t* slot, int lane,
+                                             int my_ch, int nS, uint16_t* sB,
+                                             v4f32s (&acc)[4][SK_CG]) {
+  using L = SlotLayout<FMT>;
+  const int q = lane >> 4, lr = lane & 15;
+  // redistribute the scale bytes: lane (lr, q) needs those of its rows for
+  // elements 32q .. 32q+31 (NVFP4: blocks 2q, 2q+1; MXFP4: block q)
+  if (FMT == FP4Q_NVFP4) {
+    if (lane < SK_COLS) *reinterpret_cast<u32x2*>(slot + lane * 8) = st.wsc;
+    *reinterpret_cast<u32x2*>(slot + L::X_OFF + lane * 8) = st.xsc;
+  } else {
+    if (lane < SK_COLS) *reinterpret_cast<uint32_t*>(slot + lane * 4) = st.wsc.x;
+    *reinterpret_cast<uint32_t*>(slot + L::X_OFF + lane * 4) = st.xsc.x;
+  }
+  uint32_t ws[SK_CG], xs[4];
+#pragma unroll
+  for (int g = 0; g < SK_CG; ++g)
+    ws[g] = (FMT == FP4Q_NVFP4)
+                ? (uint32_t)*reinterpret_cast<const uint16_t*>(slot + (16 * g + lr) * 8 + 2 * q)
+                : (uint32_t)slot[(16 * g + lr) * 4 + q];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+    xs[a] = (FMT == FP4Q_NVFP4)
+                ? (uint32_t)*reinterpret_cast<const uint16_t*>(slot + L::X_OFF + (16 * a + lr) * 8 + 2 * q)
+                : (uint32_t)slot[L::X_OFF + (16 * a + lr) * 4 + q];
+
+  if (FMT == FP4Q_NVFP4) {
+    // sub-step s: lane (lr, q) holds elements 32q + 8s .. +7 of the step
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      h8s db[SK_CG];
+#pragma unroll
+      for (int g = 0; g < SK_CG; ++g) db[g] = sk_decode8(st.w[g][s], sk_scale2(ws[g] >> (8 * (s >> 1))));
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const h8s da = sk_decode8(st.x[a][s], sk_scale2(xs[a] >> (8 * (s >> 1))));
+#pragma unroll
+        for (int g = 0; g < SK_CG; ++g)
+          acc[a][g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(da, db[g], acc[a][g], 0, 0, 0);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const u32x4 xa = st.x[a];
+      const i32x8s av = {(int)xa.x, (int)xa.y, (int)xa.z, (int)xa.w, 0, 0, 0, 0};
+#pragma unroll
+      for (int g = 0; g < SK_CG; ++g) {
+        const u32x4 wb = st.w[g];
+        const i32x8s bv = {(int)wb.x, (int)wb.y, (int)wb.z, (int)wb.w, 0, 0, 0, 0};
+        acc[a][g] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[a][g], 4, 4, 0,
+                                                                     (int)xs[a], 0, (int)ws[g]);
+      }
+    }
+  }
+  // compensation weights of the channels in this step (S ascending: a run
+  // of the lanes of my_ch); the lanes of group q_t hold the byte
+  if (nS > 0) {
+    uint64_t m = __ballot(my_ch >= 0 && (my_ch >> 7) == kt);
+    while (m) {
+      const int j = __builtin_ctzll(m);
+      m &= m - 1;
+      const int ch = __builtin_amdgcn_readlane(my_ch, j);
+      const int pos = ch & 127, qt = pos >> 5, e = pos & 31;
+      if (q == qt) {
+#pragma unroll
+        for (int g = 0; g < SK_CG; ++g) {
+          const uint32_t code = nibble_of(st.w[g], e);
+          float sv;
+          if (FMT == FP4Q_NVFP4) {
+            sv = e4m3_value(ws[g] >> (8 * (e >> 4)));
+          } else {
+            const uint32_t c8 = ws[g] & 0xFFu;
+            sv = c8 ? __uint_as_float(c8 << 23) : __uint_as_float(0x00400000u);
+          }
+          const float v = e2m1_mag_value(code) * sv;  // exact, and exact in bf16
+          sB[(16 * g + lr) * SK_SRS + j] = (uint16_t)((__float_as_uint(v) >> 16) | ((code & 8u) << 12));
+        }
+      }
+    }
+  }
+}
+
+template <int FMT>
+__global__ void __launch_bounds__(SK_T, 1) k_gemm_skinny(SkinnyArgs p) {
+  using L = SlotLayout<FMT>;
+  __shared__ __attribute__((aligned(16))) v4f32s red[SK_WAVES * 4 * SK_CG * 64];   // 96 KB
+  __shared__ __attribute__((aligned(16))) uint8_t sScale[SK_WAVES * 2 * L::BYTES];  // 2 slots per wave
+  __shared__ __attribute__((aligned(16))) uint16_t sR[SK_M * SK_SRS];              // R[m][j]
+  __shared__ __attribute__((aligned(16))) uint16_t sB[SK_COLS * SK_SRS];           // B_S[n][j]
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int q = lane >> 4, lr = lane & 15;
+  const int64_t col0 = (int64_t)blockIdx.x * SK_COLS;
+  const int nk = (int)(p.K / 128);
+  const int nS = p.nS;
+
+  // ---- prologue.  No barrier: everything here is per wave, and the
+  // residual rows (held in registers through the main loop) reach LDS just
+  // before the reduction barrier.  Every load is unconditional (clamped
+  // indices, or a valid stand-in address when there are no channels) so the
+  // compiler can count the loads in flight and wait only for the data used.
+  float tx = 1.0f, tw = 1.0f;
+  if (FMT == FP4Q_NVFP4) {
+    tx = *p.ats;
+    tw = *p.bts;
+  }
+  // lane j holds channel S_j (valid for j < nS); issued first, so waiting
+  // for it never waits for the operand stream
+  const int my_ch_raw = *(nS > 0 ? p.chan + (lane < nS ? lane : nS - 1)
+                                 : reinterpret_cast<const int32_t*>(p.aq));
+  Step s0, s1;
+  load_step<FMT>(p, wave < nk ? wave : nk - 1, lane, col0, s0);
+  load_step<FMT>(p, wave + SK_WAVES < nk ? wave + SK_WAVES : nk - 1, lane, col0, s1);
+  // R [M][nS] bf16, contiguous, 16-byte aligned, M nS a multiple of 8:
+  // elements 8t .. 8t+7 of the (at most 4096)
+  const int rtot = (int)p.M * nS, e0 = 8 * t;
+  const u32x4 rv = *reinterpret_cast<const u32x4*>(
+      nS > 0 ? p.resid + (e0 < rtot ? e0 : rtot - 8) : reinterpret_cast<const uint16_t*>(p.aq));
+
+  v4f32s acc[4][SK_CG];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int g = 0; g < SK_CG; ++g) acc[a][g] = v4f32s{0.f, 0.f, 0.f, 0.f};
+
+  // ---- K steps wave, wave + 8, wave + 16, ...: two steps in flight
+  uint8_t* slot0 = sScale + (wave * 2 + 0) * L::BYTES;
+  uint8_t* slot1 = sScale + (wave * 2 + 1) * L::BYTES;
+  const int my_ch = (nS > 0 && lane < nS) ? my_ch_raw : -1;
+  if (nk <= 2 * SK_WAVES) {
+    // K <= 2048: both steps are already in flight
+    if (wave < nk) process_step<FMT>(s0, wave, slot0, lane, my_ch, nS, sB, acc);
+    if (wave + SK_WAVES < nk) process_step<FMT>(s1, wave + SK_WAVES, slot1, lane, my_ch, nS, sB, acc);
+  } else {
+    for (int kt = wave; kt < nk; kt += 2 * SK_WAVES) {
+      process_step<FMT>(s0, kt, slot0, lane, my_ch, nS, sB, acc);
+      if (kt + 2 * SK_WAVES < nk) load_step<FMT>(p, kt + 2 * SK_WAVES, lane, col0, s0);
+      if (kt + SK_WAVES < nk) {
+        process_step<FMT>(s1, kt + SK_WAVES, slot1, lane, my_ch, nS, sB, acc);
+        if (kt + 3 * SK_WAVES < nk) load_step<FMT>(p, kt + 3 * SK_WAVES, lane, col0, s1);
+      }
+    }
+  }
+
+  // (keep the staging below the main loop: it waits for the residual load,
+  // the last one issued)
+  asm volatile("" ::: "memory");
+  if (nS > 0 && e0 < rtot) {
+    const uint32_t w4[4] = {rv.x, rv.y, rv.z, rv.w};
+    int row = e0 / nS, j = e0 - row * nS;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      sR[row * SK_SRS + j] = (uint16_t)(w4[k >> 1] >> (16 * (k & 1)));
+      if (++j == nS) { j = 0; ++row; }
+    }
+  }
+
+  // ---- K-partial sums meet in LDS; wave a (< 4) then owns rows 16a .. 16a+15
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int g = 0; g < SK_CG; ++g) red[((wave * 4 + a) * SK_CG + g) * 64 + lane] = acc[a][g];
+  __syncthreads();
+  if (wave >= 4) return;
+  v4f32s out[SK_CG];
+#pragma unroll
+  for (int g = 0; g < SK_CG; ++g) {
+    out[g] = red[((0 * 4 + wave) * SK_CG + g) * 64 + lane];
+#pragma unroll
+    for (int w2 = 1; w2 < SK_WAVES; ++w2) out[g] += red[((w2 * 4 + wave) * SK_CG + g) * 64 + lane];
+  }
+
+  // ---- compensation: y = tw * (tx * main + comp).  Entries j >= nS of
+  // both operands are masked to zero (the LDS there is not written).
+  if (FMT == FP4Q_NVFP4) {
+#pragma unroll
+    for (int g = 0; g < SK_CG; ++g) out[g] *= tx;
+  }
+  for (int j0 = 0; j0 < nS; j0 += 16) {
+    const int jq = j0 + 4 * q;
+    const u32x2 m2 = u32x2{(jq + 0 < nS ? 0xFFFFu : 0u) | (jq + 1 < nS ? 0xFFFF0000u : 0u),
+                           (jq + 2 < nS ? 0xFFFFu : 0u) | (jq + 3 < nS ? 0xFFFF0000u : 0u)};
+    // A: R[16 wave + lr][jq .. jq+3]; B: B_S[16 g + lr][jq .. jq+3]
+    const s4s ra = __builtin_bit_cast(
+        s4s, *reinterpret_cast<const u32x2*>(sR + (16 * wave + lr) * SK_SRS + jq) & m2);
+#pragma unroll
+    for (int g = 0; g < SK_CG; ++g) {
+      const s4s rb = __builtin_bit_cast(
+          s4s, *reinterpret_cast<const u32x2*>(sB + (16 * g + lr) * SK_SRS + jq) & m2);
+      out[g] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ra, rb, out[g], 0, 0, 0);
+    }
+  }
+
+  // ---- store: lane holds rows 16 wave + 4q + e, column col0 + 16g + lr
+#pragma unroll
+  for (int g = 0; g < SK_CG; ++g) {
+    const int64_t col = col0 + 16 * g + lr;
+    if (col >= p.N) continue;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t row = 16 * wave + 4 * q + e;
+      if (row >= p.M) continue;
+      const float v = out[g][e] * tw;
+      if (p.y_bf16)
+        reinterpret_cast<uint16_t*>(p.y)[row * p.ldy + col] = (uint16_t)f32_to_bf16_rne(v);
+      else
+        reinterpret_cast<float*>(p.y)[row * p.ldy + col] = v;
+    }
+  }
+}
+
+bool skinny_gemm_eligible(int64_t M, int64_t N, int64_t K, int nS, const void* resid) {
+  // the residual rows are read as 16-byte pieces of 8 entries
+  const bool resid_ok =
+      nS == 0 || ((reinterpret_cast<uintptr_t>(resid) & 15) == 0 && (M * nS) % 8 == 0);
+  return M >= 1 && M <= SK_M && N >= 1 && K % 128 == 0 && nS <= SK_MAXS && resid_ok;
+}
+
+int launch_gemm_skinny(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* aq,
+                       const uint8_t* as, const float* ats, const uint8_t* bq, const uint8_t* bs,
+                       const float* bts, const int32_t* chan, int nS, const uint16_t* resid,
+                       void* y, int y_bf16, int64_t ldy, hipStream_t stream) {
+  SkinnyArgs a{M, N, K, aq, as, ats, bq, bs, bts, chan, nS, resid, y, y_bf16, ldy};
+  dim3 grid((unsigned)((N + SK_COLS - 1) / SK_COLS));
+  if (fmt == FP4Q_NVFP4)
+    hipLaunchKernelGGL(k_gemm_skinny<FP4Q_NVFP4>, grid, dim3(SK_T), 0, stream, a);
+  else
+    hipLaunchKernelGGL(k_gemm_skinny<FP4Q_MXFP4>, grid, dim3(SK_T), 0, stream, a);
+  return 0;
+}
+
+}  // namespace fp4q

@@ -5,18 +5,42 @@
 // suffer the coarse E2M1 grid; the explainer's section 2.2 B and the
 // FourSight abstract keep a residual for a few selected channels.
 //
-// NVFP4 needs the tensor (or per-expert group) amax before any block scale,
-// so it runs in two streaming passes: k_group_amax (atomic max of the FP32
-// bit pattern, exact and order-free for non-negative values) and
-// k_quantize.  MXFP4 is a single pass.  One thread owns one scale block:
-// it loads the block with 16-byte vector loads, computes the block amax, the
-// scale code, the E2M1 codes (nearest-even by threshold compares), packs two
-// codes per byte and stores them with one vector store, and writes the BF16
-// residual for the selected channels that fall in its block.
+// Work unit: one lane owns one 16-byte chunk (8 BF16 elements), so a wave's
+// loads and code stores are fully contiguous.  A scale block is 2 (NVFP4) or
+// 4 (MXFP4) neighbouring lanes; they combine their maxima with DPP lane moves
+// and compute the scale redundantly; the block's first lane stores the scale
+// byte.  Element quotients use a per-block reciprocal with exact FMA
+// corrections (bit-identical to IEEE division); E2M1 rounding and packing use
+// the hardware FP4 conversion.  Each lane writes its 8 codes with one 32-bit
+// store.  The residual
+// channels of a chunk come from a per-workgroup table in LDS (first channel
+// index and an 8-bit mask per column chunk), built once from the channel
+// list.
+//
+// NVFP4 needs the tensor (or per-expert group) amax before any block scale:
+//  * small dense tensors (the decode regime): one launch; every workgroup
+//    first reduces the whole tensor's amax itself (it sits in L2), then
+//    quantizes its chunks -- no second launch and no workspace;
+//  * large dense tensors: a partial-amax pass writes one maximum per
+//    workgroup to the workspace; each quantize workgroup reduces those
+//    first;
+//  * expert groups: atomic max of the FP32 bit pattern per group (exact and
+//    order-free for non-negative values) after a fill kernel clears the
+//    words.
+// MXFP4 is a single pass.
 #include "fp4q_device.h"
 #include "fp4q_internal.h"
 
 namespace fp4q {
+
+constexpr int QT = 256;              // threads per workgroup, general path
+constexpr int QU = 4;                // chunks per thread, general path
+constexpr int FT = 1024;             // threads per workgroup, fused small path
+constexpr int64_t FUSED_MAX_CHUNKS = 32 * FT;  // small-tensor path up to 256K elements
+constexpr bool SMALL_FUSED = true;   // small tensors: one launch (else two short passes)
+constexpr int AMAX_PARTS = 1024;     // partial maxima of the dense large path
+constexpr int AMAX_BATCH = 16;       // loads in flight per thread in amax scans
+constexpr int TAB_MAX = 2048;        // column chunks covered by the LDS channel table
 
 // Group of a row: the g with off[g] <= row < off[g+1] (binary search).
 __device__ __forceinline__ int group_of_row(const int32_t* __restrict__ off, int G, int64_t row) {
@@ -27,6 +51,77 @@ __device__ __forceinline__ int group_of_row(const int32_t* __restrict__ off, int
   }
   return lo;
 }
+
+// Largest BF16 magnitude pattern of 8 packed elements.
+__device__ __forceinline__ uint32_t absmax8(u32x4 v) {
+  uint32_t m = max(v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu);
+  m = max(m, max(v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu));
+  m = max(m, max(v.z & 0x7FFFu, (v.z >> 16) & 0x7FFFu));
+  return max(m, max(v.w & 0x7FFFu, (v.w >> 16) & 0x7FFFu));
+}
+
+// Row and column chunk of flat chunk index c (< 2^31): quotient estimated in
+// FP64 (exact operands, error far below one) and corrected by one step.
+struct ChunkGrid {
+  const uint16_t* x;
+  uint32_t cpr;      // 16-byte chunks per row
+  int64_t ldx;       // row stride in elements
+  double rcp;        // 1 / cpr
+  bool contig;       // ldx == cols: chunk c sits at x + 8c
+};
+
+__device__ __forceinline__ void chunk_rc(const ChunkGrid& gr, uint32_t c, uint32_t& r, uint32_t& cc) {
+  uint32_t q = (uint32_t)((double)c * gr.rcp);
+  int32_t rem = (int32_t)(c - q * gr.cpr);
+  if (rem < 0) { --q; rem += (int32_t)gr.cpr; }
+  else if (rem >= (int32_t)gr.cpr) { ++q; rem -= (int32_t)gr.cpr; }
+  r = q;
+  cc = (uint32_t)rem;
+}
+
+__device__ __forceinline__ u32x4 load_chunk(const ChunkGrid& gr, uint32_t c) {
+  const uint16_t* p;
+  if (gr.contig) {
+    p = gr.x + (int64_t)c * 8;
+  } else {
+    uint32_t r, cc;
+    chunk_rc(gr, c, r, cc);
+    p = gr.x + (int64_t)r * gr.ldx + (int64_t)cc * 8;
+  }
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+// Max |x| (BF16 magnitude pattern) over the chunks first, first + stride, ...
+// below `end`, AMAX_BATCH independent loads in flight per thread.
+__device__ __forceinline__ uint32_t strided_amax(const ChunkGrid& gr, uint32_t first, uint32_t end,
+                                                 uint32_t stride) {
+  uint32_t m = 0;
+  int64_t i = first;
+  for (; i + (int64_t)(AMAX_BATCH - 1) * stride < end; i += (int64_t)AMAX_BATCH * stride) {
+    u32x4 v[AMAX_BATCH];
+#pragma unroll
+    for (int u = 0; u < AMAX_BATCH; ++u) v[u] = load_chunk(gr, (uint32_t)(i + u * stride));
+#pragma unroll
+    for (int u = 0; u < AMAX_BATCH; ++u) m = max(m, absmax8(v[u]));
+  }
+  for (; i < end; i += stride) m = max(m, absmax8(load_chunk(gr, (uint32_t)i)));
+  return m;
+}
+
+// Reduce a per-thread maximum across the workgroup; every thread gets it.
+template <int NT>
+__device__ __forceinline__ uint32_t wg_max(uint32_t m, uint32_t* red) {
+  for (int s = 32; s > 0; s >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, s));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) m = max(m, red[i]);
+  __syncthreads();
+  return m;
+}
+
+// ---- NVFP4 tensor amax passes ---------------------------------------------
 
 // Clear the amax words and pre-set every tensor scale to 1 (empty groups
 // keep it).  A fill kernel rather than a memset so the sequence can be
@@ -39,184 +134,320 @@ __global__ void k_quant_init(uint32_t* __restrict__ amax_bits, float* __restrict
   }
 }
 
-// Per-group amax.  Each workgroup owns a run of ROWS_PER_WG rows; waves take
-// rows in turn, lanes stride along the row in 8-element (16-byte) chunks.
-// When the whole run lies in one group (always when G == 1) the workgroup
-// reduces in LDS and issues one atomic; otherwise each row issues its own.
+// Per-group amax.  Each workgroup owns a run of rows.  When the run lies in
+// one group the workgroup scans it as one flat range and issues one atomic;
+// otherwise each wave takes rows in turn and issues one atomic per row.
 constexpr int AMAX_ROWS_PER_WG = 16;
 
-__global__ void __launch_bounds__(256) k_group_amax(const uint16_t* __restrict__ x, int64_t rows,
-                                                    int64_t cols, int64_t ldx,
-                                                    const int32_t* __restrict__ off, int G,
-                                                    uint32_t* __restrict__ amax_bits) {
-  __shared__ uint32_t red[4];
+__global__ void __launch_bounds__(QT) k_group_amax(ChunkGrid gr, int64_t rows,
+                                                   const int32_t* __restrict__ off, int G,
+                                                   uint32_t* __restrict__ amax_bits) {
+  __shared__ uint32_t red[QT / 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t r0 = (int64_t)blockIdx.x * AMAX_ROWS_PER_WG;
   const int64_t r1 = r0 + AMAX_ROWS_PER_WG < rows ? r0 + AMAX_ROWS_PER_WG : rows;
-  const int g0 = (G > 1) ? group_of_row(off, G, r0) : 0;
-  const int g1 = (G > 1) ? group_of_row(off, G, r1 - 1) : 0;
-  const bool one_group = (g0 == g1);
-  uint32_t wmax = 0;
-  const int64_t nchunk = cols >> 3;
-  for (int64_t r = r0 + wave; r < r1; r += 4) {
-    const u32x4* xr = reinterpret_cast<const u32x4*>(x + r * ldx);
-    uint32_t m = 0;
-    for (int64_t c = lane; c < nchunk; c += 64) {
-      u32x4 v = __builtin_nontemporal_load(xr + c);
-      // |bf16| patterns compare like the values (finite inputs)
-      m = max(m, max(v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu));
-      m = max(m, max(v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu));
-      m = max(m, max(v.z & 0x7FFFu, (v.z >> 16) & 0x7FFFu));
-      m = max(m, max(v.w & 0x7FFFu, (v.w >> 16) & 0x7FFFu));
-    }
-    for (int s = 32; s > 0; s >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, s));
-    if (one_group) {
-      wmax = max(wmax, m);
-    } else if (lane == 0) {
-      atomicMax(&amax_bits[group_of_row(off, G, r)], m << 16);
-    }
+  const int g0 = group_of_row(off, G, r0);
+  const int g1 = group_of_row(off, G, r1 - 1);
+  const uint32_t cpr = gr.cpr;
+  if (g0 == g1) {
+    uint32_t m = strided_amax(gr, (uint32_t)(r0 * cpr) + threadIdx.x, (uint32_t)(r1 * cpr), QT);
+    m = wg_max<QT>(m, red);
+    if (threadIdx.x == 0 && m) atomicMax(&amax_bits[g0], m << 16);
+    return;
   }
-  if (one_group) {
-    if (lane == 0) red[wave] = wmax;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      uint32_t m = max(max(red[0], red[1]), max(red[2], red[3]));
-      if (m) atomicMax(&amax_bits[g0], m << 16);
+  for (int64_t r = r0 + wave; r < r1; r += QT / 64) {
+    uint32_t m = strided_amax(gr, (uint32_t)(r * cpr) + lane, (uint32_t)((r + 1) * cpr), 64);
+    for (int s = 32; s > 0; s >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, s));
+    if (lane == 0 && m) atomicMax(&amax_bits[group_of_row(off, G, r)], m << 16);
+  }
+}
+
+// Dense, large: one partial maximum per workgroup.
+__global__ void __launch_bounds__(QT) k_amax_partial(ChunkGrid gr, uint32_t total,
+                                                     uint32_t* __restrict__ part) {
+  __shared__ uint32_t red[QT / 64];
+  uint32_t m = strided_amax(gr, blockIdx.x * QT + threadIdx.x, total, gridDim.x * QT);
+  m = wg_max<QT>(m, red);
+  if (threadIdx.x == 0) part[blockIdx.x] = m;
+}
+
+// ---- residual channel table --------------------------------------------------
+
+// Entry for column chunk cc (columns 8cc .. 8cc+7): bits 0-7 mark the
+// selected columns, bits 8-31 hold the index j of the first of them in S.
+__device__ __forceinline__ void build_chan_table(const int32_t* __restrict__ S, int nS,
+                                                 int64_t cpr, uint32_t* tab, int nt) {
+  for (int i = threadIdx.x; i < cpr; i += nt) tab[i] = 0u;
+  __syncthreads();
+  for (int j = threadIdx.x; j < nS; j += nt) {
+    const int c = S[j], cc = c >> 3;
+    uint32_t v = 1u << (c & 7);
+    if (j == 0 || (S[j - 1] >> 3) != cc) v |= (uint32_t)j << 8;
+    atomicOr(&tab[cc], v);
+  }
+  __syncthreads();
+}
+
+// The same entry found by binary search in S (table too small, or a chunk
+// of another group than the one the table was built for).
+__device__ __forceinline__ uint32_t chan_entry_search(const int32_t* __restrict__ S, int nS,
+                                                      int64_t cc) {
+  const int c0 = (int)(cc * 8);
+  int lo = 0, hi = nS;  // first j with S[j] >= c0
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (S[mid] < c0) lo = mid + 1; else hi = mid;
+  }
+  uint32_t mask = 0;
+  for (int j = lo; j < nS && j < lo + 8; ++j) {
+    const int c = S[j];
+    if (c >= c0 + 8) break;
+    mask |= 1u << (c - c0);
+  }
+  return mask | ((uint32_t)lo << 8);
+}
+
+// ---- one chunk ---------------------------------------------------------------
+
+// x / d rounded to nearest FP32, for the quotients the quantizer forms
+// (|x| <= about 7 d).  With y = RN(1/d), q0 = RN(a y), a = |x|, is within two
+// ulps of a/d; one FMA correction brings it within one ulp, and a second
+// yields the correctly rounded quotient by Markstein's theorem (the residual
+// a - q d is exact when nothing underflows).  The sign is x's sign bit: the
+// corrections would turn -0 into +0.  Valid for d >= 2^-96; smaller divisors
+// take the IEEE division instruction sequence.
+__device__ __forceinline__ float div_rn(float x, float d, float y) {
+  const float a = fabsf(x);
+  float q = a * y;
+  float r = __builtin_fmaf(-q, d, a);
+  q = __builtin_fmaf(r, y, q);
+  r = __builtin_fmaf(-q, d, a);
+  q = __builtin_fmaf(r, y, q);
+  return __uint_as_float(__float_as_uint(q) | (__float_as_uint(x) & 0x80000000u));
+}
+
+// E2M1 codes of 8 FP32 values, packed two per byte (even element in the low
+// nibble), by gfx950's v_cvt_scalef32_pk_fp4_f32 with scale 1: nearest-even
+// on the E2M1 grid, saturating at 6, sign kept (also for -0 and values that
+// round to zero) -- the same decisions as the threshold rule of the grid.
+__device__ __forceinline__ uint32_t e2m1_pack8(const float (&v)[8]) {
+  uint32_t p = 0;
+  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[0], v[1], 1.0f, 0);
+  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[2], v[3], 1.0f, 1);
+  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[4], v[5], 1.0f, 2);
+  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[6], v[7], 1.0f, 3);
+  return p;
+}
+
+// Quantize chunk cc of row `row` held in v.  All lanes of the wave call this
+// (the block max moves between lanes); `active` gates the stores.
+template <int FMT>
+__device__ __forceinline__ void quantize_chunk(u32x4 v, bool active, int64_t row, int64_t cc,
+                                               int64_t cols, float t, uint32_t chan_ent, int nS,
+                                               uint8_t* __restrict__ q, uint8_t* __restrict__ scales,
+                                               uint16_t* __restrict__ resid) {
+  constexpr int CPB = (FMT == FP4Q_NVFP4) ? 2 : 4;  // chunks per scale block
+  // block max over the 2 or 4 lanes of the block: DPP quad permutations
+  // [1,0,3,2] (lane ^ 1) and [2,3,0,1] (lane ^ 2)
+  uint32_t am = absmax8(v);
+  am = max(am, (uint32_t)__builtin_amdgcn_mov_dpp((int)am, 0xB1, 0xF, 0xF, false));
+  if (CPB == 4) am = max(am, (uint32_t)__builtin_amdgcn_mov_dpp((int)am, 0x4E, 0xF, 0xF, false));
+  const float amax = bf16_to_f32(am);
+
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float xs[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) xs[k] = __uint_as_float((k & 1) ? (w[k >> 1] & 0xFFFF0000u) : (w[k >> 1] << 16));
+
+  float d, sb = 0.0f, qv[8];
+  uint32_t sc;
+  if (FMT == FP4Q_NVFP4) {
+    const float vs = (amax / 6.0f) / t;
+    sc = e4m3_encode(vs);
+    sb = e4m3_value(sc);
+    d = sb * t;
+    if (d >= 0x1p-96f) {
+      const float y = 1.0f / d;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) qv[k] = div_rn(xs[k], d, y);
+    } else if (d > 0.0f) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) qv[k] = xs[k] / d;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) qv[k] = xs[k] * 0.0f;  // signed zero: magnitude code 0
+    }
+  } else {
+    const int e = mx_exponent(amax);
+    sc = (uint32_t)(e + 127);
+    d = exp2i(e);
+    const float inv_pow2 = exp2i(-e);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) qv[k] = xs[k] * inv_pow2;  // exact
+  }
+  if (!active) return;
+  if ((cc & (CPB - 1)) == 0) scales[row * (cols / (8 * CPB)) + cc / CPB] = (uint8_t)sc;
+
+  const uint32_t packed = e2m1_pack8(qv);
+  *reinterpret_cast<uint32_t*>(q + row * (cols >> 1) + 4 * cc) = packed;
+
+  // residual on the selected channels of this chunk
+  uint32_t mask = chan_ent & 0xFFu;
+  if (nS > 0 && mask) {
+    int j = (int)(chan_ent >> 8);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (mask & (1u << k)) {
+        const uint32_t code = (packed >> (4 * k)) & 15u;
+        float p;
+        if (FMT == FP4Q_NVFP4)
+          p = (e2m1_mag_value(code) * sb) * t;  // first product exact
+        else
+          p = e2m1_mag_value(code) * d;         // exact
+        if (code & 8u) p = -p;
+        resid[row * nS + j] = (uint16_t)f32_to_bf16_rne(xs[k] - p);
+        ++j;
+      }
     }
   }
 }
 
-// One thread per scale block of BLK elements (16 NVFP4, 32 MXFP4).
-template <int FMT>
-__global__ void __launch_bounds__(256) k_quantize(
-    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
-    const int32_t* __restrict__ off, int G, const int32_t* __restrict__ chan, int nS,
-    uint8_t* __restrict__ q, uint8_t* __restrict__ scales, float* __restrict__ tscale,
-    uint16_t* __restrict__ resid, const uint32_t* __restrict__ amax_bits) {
-  constexpr int BLK = (FMT == FP4Q_NVFP4) ? 16 : 32;
-  constexpr int NV = BLK / 8;  // 16-byte vectors per block
-  const int64_t nb = cols / BLK;
-  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (id >= rows * nb) return;
-  const int64_t row = id / nb, b = id - row * nb;
-  const int g = (G > 1) ? group_of_row(off, G, row) : 0;
+// ---- the quantize kernel -------------------------------------------------------
 
-  // load the block
-  uint32_t w[BLK / 2];
-  const u32x4* src = reinterpret_cast<const u32x4*>(x + row * ldx + b * BLK);
-#pragma unroll
-  for (int v = 0; v < NV; ++v) {
-    u32x4 t = __builtin_nontemporal_load(src + v);
-    w[4 * v + 0] = t.x; w[4 * v + 1] = t.y; w[4 * v + 2] = t.z; w[4 * v + 3] = t.w;
-  }
-  uint32_t am = 0;
-#pragma unroll
-  for (int i = 0; i < BLK / 2; ++i) am = max(am, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
-  const float amax = bf16_to_f32(am);
+// How NVFP4 finds its tensor scale.
+enum { AMAX_NONE = 0, AMAX_GROUP_WORDS = 1, AMAX_PARTIALS = 2, AMAX_FUSED = 3 };
 
-  // block scale
-  float t = 1.0f, d, sb = 0.0f, inv_pow2 = 1.0f;
-  uint32_t sc;
-  if (FMT == FP4Q_NVFP4) {
-    t = nv_tensor_scale(__uint_as_float(amax_bits[g]));
-    float v = (amax / 6.0f) / t;
-    sc = e4m3_encode(v);
-    sb = e4m3_value(sc);
-    d = sb * t;
-    if (row == (G > 1 ? (int64_t)off[g] : 0) && b == 0) tscale[g] = t;
-  } else {
-    int e = mx_exponent(amax);
-    sc = (uint32_t)(e + 127);
-    d = exp2i(e);
-    inv_pow2 = exp2i(-e);
-  }
-  scales[row * nb + b] = (uint8_t)sc;
+template <int FMT, int MODE, int NT, int U>
+__global__ void __launch_bounds__(NT) k_quantize(
+    ChunkGrid gr, int64_t rows, int64_t cols, const int32_t* __restrict__ off, int G,
+    const int32_t* __restrict__ chan, int nS, uint8_t* __restrict__ q,
+    uint8_t* __restrict__ scales, float* __restrict__ tscale, uint16_t* __restrict__ resid,
+    const uint32_t* __restrict__ amax_words, int nparts) {
+  __shared__ uint32_t red[NT / 64];
+  __shared__ uint32_t tab[TAB_MAX];
+  const uint32_t cpr = gr.cpr, total = (uint32_t)(rows * cpr);
+  const uint32_t base = blockIdx.x * (uint32_t)(NT * U);
+  const bool grouped = (G > 1);
 
-  // element codes, packed two per byte (even element in the low nibble)
-  uint32_t packed[BLK / 8];
+  // this thread's chunks go out first (a clamped in-range address past the
+  // end, so no branch separates the loads)
+  u32x4 v[U];
 #pragma unroll
-  for (int i = 0; i < BLK / 8; ++i) packed[i] = 0;
-#pragma unroll
-  for (int k = 0; k < BLK; ++k) {
-    uint32_t h = (w[k >> 1] >> ((k & 1) * 16)) & 0xFFFFu;
-    float a = bf16_to_f32(h & 0x7FFFu);
-    uint32_t mag;
-    if (FMT == FP4Q_NVFP4)
-      mag = (d == 0.0f) ? 0u : e2m1_mag_code(a / d);
-    else
-      mag = e2m1_mag_code(a * inv_pow2);
-    uint32_t code = ((h >> 15) << 3) | mag;
-    packed[k >> 3] |= code << ((k & 7) * 4);
-  }
-  uint8_t* qdst = q + row * (cols >> 1) + b * (BLK / 2);
-  if (BLK == 16) {
-    *reinterpret_cast<u32x2*>(qdst) = u32x2{packed[0], packed[1]};
-  } else {
-    *reinterpret_cast<u32x4*>(qdst) = u32x4{packed[0], packed[1], packed[2], packed[3]};
+  for (int u = 0; u < U; ++u) {
+    const uint32_t c = base + u * NT + threadIdx.x;
+    v[u] = load_chunk(gr, c < total ? c : total - 1);
   }
 
-  // residual on the selected channels of this block
-  if (nS > 0) {
-    const int32_t* S = chan + (int64_t)g * nS;
-    const int c0 = (int)(b * BLK);
-    int lo = 0, hi = nS;  // first j with S[j] >= c0
-    while (lo < hi) {
-      int mid = (lo + hi) >> 1;
-      if (S[mid] < c0) lo = mid + 1; else hi = mid;
+  // tensor scale of the dense paths (one group)
+  float tdense = 1.0f;
+  if (MODE == AMAX_PARTIALS) {
+    uint32_t m = 0;
+    for (int i = threadIdx.x; i < nparts; i += NT) m = max(m, amax_words[i]);
+    tdense = nv_tensor_scale(bf16_to_f32(wg_max<NT>(m, red)));
+  } else if (MODE == AMAX_FUSED) {
+    // the whole (small) tensor, read by every workgroup from L2
+    const uint32_t m = strided_amax(gr, threadIdx.x, total, NT);
+    tdense = nv_tensor_scale(bf16_to_f32(wg_max<NT>(m, red)));
+  }
+  if ((MODE == AMAX_PARTIALS || MODE == AMAX_FUSED) && blockIdx.x == 0 && threadIdx.x == 0)
+    tscale[0] = tdense;
+
+  // group of the workgroup's first row; its channel table
+  uint32_t row_first, cc_first;
+  chunk_rc(gr, base, row_first, cc_first);
+  const int gA = grouped ? group_of_row(off, G, row_first) : 0;
+  const int64_t gA_end = grouped ? (int64_t)off[gA + 1] : rows;
+  const bool use_tab = nS > 0 && cpr <= TAB_MAX;
+  if (use_tab) build_chan_table(chan + (int64_t)gA * nS, nS, cpr, tab, NT);
+
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t c = base + u * NT + threadIdx.x;
+    const bool active = c < total;
+    uint32_t row, cc;
+    chunk_rc(gr, active ? c : 0u, row, cc);
+    int g = gA;
+    if (grouped && active && row >= gA_end) g = group_of_row(off, G, row);
+    float t = tdense;
+    if (MODE == AMAX_GROUP_WORDS) {
+      t = nv_tensor_scale(__uint_as_float(amax_words[g]));
+      if (active && cc == 0 && row == (uint32_t)off[g]) tscale[g] = t;
     }
-    int j = lo;
-    int cn = (j < nS) ? S[j] : 0x7FFFFFFF;
-    if (cn < c0 + BLK) {
-#pragma unroll
-      for (int k = 0; k < BLK; ++k) {
-        if (c0 + k == cn) {
-          uint32_t h = (w[k >> 1] >> ((k & 1) * 16)) & 0xFFFFu;
-          float xv = bf16_to_f32(h);
-          uint32_t code = (packed[k >> 3] >> ((k & 7) * 4)) & 15u;
-          float p;
-          if (FMT == FP4Q_NVFP4) {
-            p = e2m1_mag_value(code) * sb;  // exact
-            p = p * t;
-          } else {
-            p = e2m1_mag_value(code) * d;   // exact
-          }
-          if (code & 8u) p = -p;
-          float r = xv - p;
-          resid[row * nS + j] = (uint16_t)f32_to_bf16_rne(r);
-          ++j;
-          cn = (j < nS) ? S[j] : 0x7FFFFFFF;
-        }
-      }
-    }
+    uint32_t ent = 0;
+    if (nS > 0 && active)
+      ent = (use_tab && g == gA) ? tab[cc] : chan_entry_search(chan + (int64_t)g * nS, nS, cc);
+    quantize_chunk<FMT>(v[u], active, row, cc, cols, t, ent, nS, q, scales, resid);
   }
+}
+
+template <int FMT, int MODE, int NT, int U>
+static void launch_q(const ChunkGrid& gr, int64_t rows, int64_t cols, hipStream_t stream,
+                     const int32_t* off, int G, const int32_t* chan, int nS, uint8_t* q,
+                     uint8_t* scales, float* tscale, uint16_t* resid, const uint32_t* words,
+                     int nparts) {
+  const int64_t per = (int64_t)NT * U, total = rows * (int64_t)gr.cpr;
+  dim3 grid((unsigned)((total + per - 1) / per));
+  hipLaunchKernelGGL((k_quantize<FMT, MODE, NT, U>), grid, dim3(NT), 0, stream, gr, rows, cols, off,
+                     G, chan, nS, q, scales, tscale, resid, words, nparts);
 }
 
 int launch_quantize(int fmt, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                     const int32_t* off, int G, const int32_t* chan, int nS, uint8_t* q,
                     uint8_t* scales, float* tscale, uint16_t* resid, void* ws,
                     hipStream_t stream) {
-  const int64_t blk = (fmt == FP4Q_NVFP4) ? 16 : 32;
-  const int64_t nthreads = rows * (cols / blk);
-  uint32_t* amax_bits = static_cast<uint32_t*>(ws);
-  if (fmt == FP4Q_NVFP4) {
-    hipLaunchKernelGGL(k_quant_init, dim3((G + 255) / 256), dim3(256), 0, stream, amax_bits,
-                       tscale, G);
+  const int64_t chunks = rows * (cols >> 3);
+  const ChunkGrid gr{x, (uint32_t)(cols >> 3), ldx, 1.0 / (double)(cols >> 3), ldx == cols};
+  uint32_t* words = static_cast<uint32_t*>(ws);
+  const bool grouped = (off != nullptr && G > 1);
+  const int Gk = grouped ? G : 1;
+  if (fmt == FP4Q_MXFP4) {
+    if (chunks > 0)
+      launch_q<FP4Q_MXFP4, AMAX_NONE, QT, QU>(gr, rows, cols, stream, off, Gk, chan, nS, q, scales,
+                                               tscale, resid, words, 0);
+    return 0;
+  }
+  if (grouped) {
+    hipLaunchKernelGGL(k_quant_init, dim3((G + QT - 1) / QT), dim3(QT), 0, stream, words, tscale, G);
     if (rows > 0) {
       const int64_t nwg = (rows + AMAX_ROWS_PER_WG - 1) / AMAX_ROWS_PER_WG;
-      hipLaunchKernelGGL(k_group_amax, dim3((unsigned)nwg), dim3(256), 0, stream, x, rows, cols,
-                         ldx, off, G, amax_bits);
+      hipLaunchKernelGGL(k_group_amax, dim3((unsigned)nwg), dim3(QT), 0, stream, gr, rows, off, G,
+                         words);
+      launch_q<FP4Q_NVFP4, AMAX_GROUP_WORDS, QT, QU>(gr, rows, cols, stream, off, G, chan, nS, q,
+                                                      scales, tscale, resid, words, 0);
     }
+    return 0;
   }
-  if (nthreads > 0) {
-    dim3 grid((unsigned)((nthreads + 255) / 256));
-    if (fmt == FP4Q_NVFP4)
-      hipLaunchKernelGGL(k_quantize<FP4Q_NVFP4>, grid, dim3(256), 0, stream, x, rows, cols, ldx,
-                         off, G, chan, nS, q, scales, tscale, resid, amax_bits);
-    else
-      hipLaunchKernelGGL(k_quantize<FP4Q_MXFP4>, grid, dim3(256), 0, stream, x, rows, cols, ldx,
-                         off, G, chan, nS, q, scales, tscale, resid, amax_bits);
+  if (rows == 0) {  // empty tensor: tensor scale 1
+    hipLaunchKernelGGL(k_quant_init, dim3(1), dim3(QT), 0, stream, words, tscale, 1);
+    return 0;
   }
+  if (chunks <= FUSED_MAX_CHUNKS) {
+    if (SMALL_FUSED) {
+      launch_q<FP4Q_NVFP4, AMAX_FUSED, FT, 1>(gr, rows, cols, stream, off, 1, chan, nS, q, scales,
+                                              tscale, resid, words, 0);
+    } else {
+      // two short passes spread over many workgroups
+      const int64_t parts = (chunks + QT - 1) / QT;
+      hipLaunchKernelGGL(k_amax_partial, dim3((unsigned)parts), dim3(QT), 0, stream, gr,
+                         (uint32_t)chunks, words);
+      launch_q<FP4Q_NVFP4, AMAX_PARTIALS, QT, 1>(gr, rows, cols, stream, off, 1, chan, nS, q,
+                                                  scales, tscale, resid, words, (int)parts);
+    }
+    return 0;
+  }
+  int64_t parts = (chunks + (int64_t)QT * AMAX_BATCH - 1) / ((int64_t)QT * AMAX_BATCH);
+  parts = parts < AMAX_PARTS ? parts : AMAX_PARTS;
+  hipLaunchKernelGGL(k_amax_partial, dim3((unsigned)parts), dim3(QT), 0, stream, gr,
+                     (uint32_t)chunks, words);
+  launch_q<FP4Q_NVFP4, AMAX_PARTIALS, QT, QU>(gr, rows, cols, stream, off, 1, chan, nS, q, scales,
+                                               tscale, resid, words, (int)parts);
   return 0;
+}
+
+size_t quantize_workspace_bytes(int fmt, int G) {
+  if (fmt != FP4Q_NVFP4) return 0;
+  const int n = G > AMAX_PARTS ? G : AMAX_PARTS;
+  return (size_t)n * sizeof(uint32_t);
 }
 
 }  // namespace fp4q

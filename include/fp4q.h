@@ -99,6 +99,8 @@ int fp4q_last_hip_error(void);
  *                 no initialisation and are left undefined
  *
  * cols must be a multiple of the block size; 0 <= n_chan <= cols.
+ * rows * cols / 8 must be below 2^31 (FP4Q_ERR_UNSUPPORTED otherwise: 32 GiB
+ * of BF16 per call).
  * ------------------------------------------------------------------------ */
 size_t fp4q_quantize_workspace_bytes(fp4q_format_t fmt, int64_t rows, int64_t cols,
                                      int32_t num_groups);

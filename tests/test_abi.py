@@ -40,7 +40,8 @@ def test_status_strings(L):
 
 
 def test_workspace_queries(L):
-    assert L.fp4q_quantize_workspace_bytes(0, 100, 64, 5) == 20
+    assert L.fp4q_quantize_workspace_bytes(0, 100, 64, 5) >= 20
+    assert L.fp4q_quantize_workspace_bytes(0, 100, 64, 3000) >= 12000
     assert L.fp4q_quantize_workspace_bytes(1, 100, 64, 5) == 0
     assert L.fp4q_error_decompose_workspace_bytes(8192, 4096) >= 256
 
@@ -73,6 +74,7 @@ def test_quantize_rejects(L):
     assert q(L, x=ctypes.c_void_p(0x10008)) == INVALID   # misaligned
     assert q(L, ws=None) == WORKSPACE
     assert q(L, wsb=2) == WORKSPACE
+    assert q(L, rows=1 << 28) == UNSUPPORTED     # 2^31 chunks of 8 elements
 
 
 def g(L, fmt=0, M=4, N=8, K=256, aq=A, as_=A, ats=B, bq=B, bs=B, bts=B, chan=None, nS=0, R=None,

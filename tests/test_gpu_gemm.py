@@ -78,7 +78,8 @@ def test_prefill_sampled(orc, name):
 @pytest.mark.parametrize("fmt", [0, 1])
 @pytest.mark.parametrize("M,N,K,nS", [(1, 1, 128, 0), (33, 17, 256, 5), (130, 200, 384, 37),
                                       (64, 96, 768, 32), (257, 129, 512, 128),
-                                      (70, 300, 128, 128)])
+                                      (70, 300, 128, 128), (64, 100, 2048, 64),
+                                      (1, 47, 1920, 63), (48, 49, 640, 64), (5, 50, 2048, 65)])
 def test_ragged(orc, fmt, M, N, K, nS):
     need_gpu()
     say(f"gemm ragged fmt {fmt} M{M} N{N} K{K} nS{nS}")

@@ -39,7 +39,8 @@ def test_workload_weights(orc, name, fmt):
 
 @pytest.mark.parametrize("fmt", [0, 1])
 @pytest.mark.parametrize("rows,cols,nS", [(1, 256, 3), (37, 96 * 2, 11), (100, 64, 64),
-                                          (300, 512, 0), (5, 2048, 2048)])
+                                          (300, 512, 0), (5, 2048, 2048), (3, 17408, 40),
+                                          (600, 512, 37), (64, 4096, 64), (129, 2048, 64)])
 def test_ragged_and_channel_counts(orc, fmt, rows, cols, nS):
     if fmt == 1 and cols % 32:
         pytest.skip("MXFP4 needs cols % 32")
@@ -63,21 +64,28 @@ def test_special_values(orc, fmt):
     x[5, :] = bf16_bits(np.full(256, 1e-30, np.float32))
     x[6, ::2] = bf16_bits(np.float32(2.5))                 # exact ties
     x[7, :] = bf16_bits(np.linspace(-7, 7, 256).astype(np.float32))
+    x[8, ::3] = 0x8000              # -0.0 inside blocks with a nonzero maximum
+    x[9, 1::2] = 0x8000
     chan = np.arange(0, 256, 9, dtype=np.int32)
     _run(orc, fmt, x, chan)
     # tiny-magnitude tensor (tensor scale far below one)
     _run(orc, fmt, x[2:4].copy(), chan)
 
 
-def test_ldx_larger_than_cols(orc):
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("rows", [20, 600])
+def test_ldx_larger_than_cols(orc, fmt, rows):
+    """Row stride 640 over 512 used columns: the single-launch small-tensor
+    path (20 rows) and the two-pass path (600 rows)."""
     need_gpu()
-    say("quantize with row stride > cols")
-    d = dense_case(20, 320, 8, seed=9)
-    ref = orc.quantize(0, d["x"][:, :256].copy(), chan_idx=np.array([1, 255], np.int32))
-    xt = to_dev(d["x"])[:, :256]    # a strided view: ldx = 320
-    got = fq.quantize(0, xt, chan_idx=to_dev(np.array([1, 255], np.int32)))
+    say(f"quantize with row stride > cols, fmt {fmt}, {rows} rows")
+    d = dense_case(rows, 640, 8, seed=9 + rows)
+    chan = np.array([1, 255, 256, 511], np.int32)
+    ref = orc.quantize(fmt, d["x"][:, :512].copy(), chan_idx=chan)
+    xt = to_dev(d["x"])[:, :512]    # a strided view: ldx = 640
+    got = fq.quantize(fmt, xt, chan_idx=to_dev(chan))
     torch.cuda.synchronize()
-    assert_quant_equal(got, ref, 0)
+    assert_quant_equal(got, ref, fmt)
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
@@ -88,6 +96,18 @@ def test_grouped_small(orc, fmt):
     G = off.size - 1
     rng = np.random.default_rng(2)
     chan = np.sort(np.stack([rng.choice(256, 7, replace=False) for _ in range(G)]), 1)
+    _run(orc, fmt, x, chan.astype(np.int32), off)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_grouped_wide_rows(orc, fmt):
+    """Rows wider than the workgroup's LDS channel table (17408 columns)."""
+    say(f"quantize grouped wide rows fmt {fmt}")
+    x = dense_case(40, 17408, 8, n_out=30, seed=43)["x"]
+    off = np.array([0, 10, 10, 11, 40], np.int32)
+    G = off.size - 1
+    rng = np.random.default_rng(8)
+    chan = np.sort(np.stack([rng.choice(17408, 5, replace=False) for _ in range(G)]), 1)
     _run(orc, fmt, x, chan.astype(np.int32), off)
 
 
