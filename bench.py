@@ -46,7 +46,24 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle baseline sample")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run only a device-to-device copy of 256 MiB, 5 times (the known-size "
+                        "reference for the FETCH_SIZE / WRITE_SIZE counter scale)")
     return p.parse_args()
+
+
+def copy_calibration():
+    """A plain copy kernel of known size: 256 MiB read and 256 MiB written per
+    launch.  Run under rocprofv3 --pmc, its FETCH_SIZE and WRITE_SIZE give the
+    factor that turns those counters into HBM bytes."""
+    import torch
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}), flush=True)
 
 
 def src_hash() -> str:
@@ -76,6 +93,9 @@ def load_traffic(workload: str, kernel_hash: str):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is "
               "single-GPU by design and multi-GPU sharding is not built.", file=sys.stderr)
