@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--workload", default="decode_nvfp4",
                    choices=["decode_nvfp4", "prefill_nvfp4", "prefill_mxfp4", "moe_nvfp4",
                             "tiny_nvfp4"])
+    p.add_argument("--layout", choices=("tiled", "rowmajor"), default="tiled",
+                   help="packed operand layout of the dense workloads (MoE is row-major)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle baseline sample")
@@ -137,30 +139,32 @@ def main():
         nS = int(data["chan_idx"].size)
         x = up(data["x"])
         chan = up(data["chan_idx"]) if nS else None
-        wq = fq.quantize(fmt, up(data["wt"]))  # offline weight quantization
+        layout = fq.TILED if args.layout == "tiled" else fq.ROWMAJOR
+        wq = fq.quantize(fmt, up(data["wt"]), layout=layout)  # offline weight quantization
         torch.cuda.synchronize()
         w_bytes = N * (K // 2) + N * (K // blk)
         y_bytes = M * N * 4
         n_rot = max(1, math.ceil(1.2 * LLC_BYTES / (w_bytes + y_bytes)))
         n_rot = min(n_rot, 64)
-        wcopies = [wq] + [{k: (v.clone() if v is not None else None) for k, v in wq.items()}
-                          for _ in range(n_rot - 1)]
+        wcopies = [wq] + [{k: (v.clone() if isinstance(v, torch.Tensor) else v)
+                           for k, v in wq.items()} for _ in range(n_rot - 1)]
         ys = [torch.empty((M, N), dtype=torch.float32, device=dev) for _ in range(n_rot)]
         G = 1
         qws = torch.empty(max(fq.quantize_workspace_bytes(fmt, M, K, 1), 16), dtype=torch.uint8,
                           device=dev)
-        aq = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
-        asc = torch.empty((M, K // blk), dtype=torch.uint8, device=dev)
+        cb, sb = fq.packed_bytes(fmt, layout, M, K)
+        aq = torch.empty(cb, dtype=torch.uint8, device=dev)
+        asc = torch.empty(sb, dtype=torch.uint8, device=dev)
         ats = torch.empty(1, dtype=torch.float32, device=dev) if fmt == fq.NVFP4 else None
         ar = torch.empty((M, nS), dtype=torch.int16, device=dev) if nS else None
 
         def quant():
-            fq.quantize_into(fmt, x, None, 1, chan, nS, aq, asc, ats, ar, qws)
+            fq.quantize_into(fmt, layout, x, None, 1, chan, nS, aq, asc, ats, ar, qws)
 
         def gemm(i):
             w = wcopies[i % n_rot]
-            fq.gemm_into(fmt, M, N, K, aq, asc, ats, w["q"], w["scales"], w["tscale"], chan, nS,
-                         ar, ys[i % n_rot], 0, N)
+            fq.gemm_into(fmt, layout, M, N, K, aq, asc, ats, w["q"], w["scales"], w["tscale"],
+                         chan, nS, ar, ys[i % n_rot], 0, N)
 
         flops = 2.0 * M * N * K
         gemm_bytes = (M * K // 2 + M * K // blk + M * nS * 2 + nS * 4 + w_bytes + y_bytes +
@@ -168,7 +172,7 @@ def main():
         quant_bytes = M * K * 2 + M * K // 2 + M * K // blk + M * nS * 2 + (4 if fmt == fq.NVFP4
                                                                              else 0)
         wl = {"workload": name, "format": cfg["fmt"], "M": M, "K": K, "N": N, "n_s": nS,
-              "weight_copies_rotated": n_rot}
+              "layout": args.layout, "weight_copies_rotated": n_rot}
     else:
         # MoE layer: gate_up then down, per-expert NVFP4, grouped GEMMs
         off = up(data["offsets"])
@@ -204,7 +208,7 @@ def main():
         def quant():
             for tag, xin, ch in (("gu", xg, cg), ("dn", xd, cd)):
                 b = bufs[tag]
-                fq.quantize_into(fmt, xin, off, G, ch, nS, b["q"], b["s"], b["t"], b["r"],
+                fq.quantize_into(fmt, fq.ROWMAJOR, xin, off, G, ch, nS, b["q"], b["s"], b["t"], b["r"],
                                  b["ws"])
 
         def gemm(i):

@@ -11,6 +11,8 @@ from .binding import (  # noqa: F401
     NVFP4,
     OUT_BF16,
     OUT_F32,
+    ROWMAJOR,
+    TILED,
     Fp4qError,
     error_decompose,
     error_decompose_into,
@@ -20,6 +22,7 @@ from .binding import (  # noqa: F401
     grouped_gemm,
     grouped_gemm_into,
     lib,
+    packed_bytes,
     quantize,
     quantize_into,
     quantize_workspace_bytes,

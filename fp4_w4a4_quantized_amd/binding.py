@@ -17,6 +17,8 @@ NVFP4 = 0
 MXFP4 = 1
 OUT_F32 = 0
 OUT_BF16 = 1
+ROWMAJOR = 0
+TILED = 1
 BLOCK = {NVFP4: 16, MXFP4: 32}
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp4q.so")
@@ -64,14 +66,17 @@ def lib():
         L.fp4q_status_str.argtypes = [ctypes.c_int]
         L.fp4q_last_hip_error.restype = ctypes.c_int
         L.fp4q_last_hip_error.argtypes = []
+        L.fp4q_packed_bytes.restype = ctypes.c_int
+        L.fp4q_packed_bytes.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64,
+                                        ctypes.POINTER(sz), ctypes.POINTER(sz)]
         L.fp4q_quantize_workspace_bytes.restype = sz
         L.fp4q_quantize_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i32]
         L.fp4q_quantize.restype = ctypes.c_int
-        L.fp4q_quantize.argtypes = [ctypes.c_int, P, i64, i64, i64, P, i32, P, i32, P, P, P, P, P,
-                                    sz, P]
+        L.fp4q_quantize.argtypes = [ctypes.c_int, ctypes.c_int, P, i64, i64, i64, P, i32, P, i32,
+                                    P, P, P, P, P, sz, P]
         L.fp4q_gemm.restype = ctypes.c_int
-        L.fp4q_gemm.argtypes = [ctypes.c_int, i64, i64, i64, P, P, P, P, P, P, P, i32, P, P,
-                                ctypes.c_int, i64, P]
+        L.fp4q_gemm.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, P, P, P, P, P, P, P,
+                                i32, P, P, ctypes.c_int, i64, P]
         L.fp4q_grouped_gemm.restype = ctypes.c_int
         L.fp4q_grouped_gemm.argtypes = [ctypes.c_int, i64, i64, i64, P, i32, P, P, P, P, P, P, P,
                                         i32, P, P, ctypes.c_int, P]
@@ -100,6 +105,14 @@ def _check(fn, rc):
 
 # ---- raw entry points (same names and argument order as the C ABI) --------
 
+def packed_bytes(fmt, layout, rows, cols):
+    """(code_bytes, scale_bytes) of one packed operand."""
+    cb, sb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check("fp4q_packed_bytes",
+           lib().fp4q_packed_bytes(fmt, layout, rows, cols, ctypes.byref(cb), ctypes.byref(sb)))
+    return cb.value, sb.value
+
+
 def quantize_workspace_bytes(fmt, rows, cols, num_groups=1) -> int:
     return lib().fp4q_quantize_workspace_bytes(fmt, rows, cols, num_groups)
 
@@ -108,20 +121,20 @@ def error_decompose_workspace_bytes(rows, cols) -> int:
     return lib().fp4q_error_decompose_workspace_bytes(rows, cols)
 
 
-def quantize_into(fmt, x, group_offsets, num_groups, chan_idx, n_chan, q, scales, tensor_scale,
-                  resid, workspace, stream=None):
+def quantize_into(fmt, layout, x, group_offsets, num_groups, chan_idx, n_chan, q, scales,
+                  tensor_scale, resid, workspace, stream=None):
     rows, cols = x.shape
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = lib().fp4q_quantize(fmt, _ptr(x), rows, cols, x.stride(0), _ptr(group_offsets),
+    rc = lib().fp4q_quantize(fmt, layout, _ptr(x), rows, cols, x.stride(0), _ptr(group_offsets),
                              num_groups, _ptr(chan_idx), n_chan, _ptr(q), _ptr(scales),
                              _ptr(tensor_scale), _ptr(resid), _ptr(workspace), ws_bytes,
                              _stream(stream))
     _check("fp4q_quantize", rc)
 
 
-def gemm_into(fmt, M, N, K, a_q, a_s, a_ts, b_q, b_s, b_ts, chan_idx, n_chan, resid, y,
+def gemm_into(fmt, layout, M, N, K, a_q, a_s, a_ts, b_q, b_s, b_ts, chan_idx, n_chan, resid, y,
               y_dtype=OUT_F32, ldy=None, stream=None):
-    rc = lib().fp4q_gemm(fmt, M, N, K, _ptr(a_q), _ptr(a_s), _ptr(a_ts), _ptr(b_q), _ptr(b_s),
+    rc = lib().fp4q_gemm(fmt, layout, M, N, K, _ptr(a_q), _ptr(a_s), _ptr(a_ts), _ptr(b_q), _ptr(b_s),
                          _ptr(b_ts), _ptr(chan_idx), n_chan, _ptr(resid), _ptr(y), y_dtype,
                          N if ldy is None else ldy, _stream(stream))
     _check("fp4q_gemm", rc)
@@ -146,33 +159,52 @@ def error_decompose_into(fmt, x, out, workspace, stream=None):
 
 # ---- allocating conveniences ---------------------------------------------
 
-def quantize(fmt, x, group_offsets=None, chan_idx=None, stream=None):
+def quantize(fmt, x, group_offsets=None, chan_idx=None, layout=ROWMAJOR, stream=None):
     """x: bf16 (or int16/uint16 bit patterns) [rows, cols] on the GPU.
     group_offsets: int32 [G+1] on the GPU or None.  chan_idx: int32 [G, nS]
-    (or [nS]) on the GPU or None.  Returns dict(q, scales, tscale, resid)."""
+    (or [nS]) on the GPU or None.  Returns dict(q, scales, tscale, resid,
+    layout, rows, cols); q and scales are [rows, cols/2] and [rows, cols/blk]
+    when row-major, flat byte buffers of packed_bytes() when tiled."""
     dev = x.device
     rows, cols = x.shape
     blk = BLOCK[fmt]
     G = 1 if group_offsets is None else group_offsets.numel() - 1
     nS = 0 if chan_idx is None else chan_idx.numel() // G
-    q = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
-    sc = torch.empty((rows, cols // blk), dtype=torch.uint8, device=dev)
+    if layout == ROWMAJOR:
+        q = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+        sc = torch.empty((rows, cols // blk), dtype=torch.uint8, device=dev)
+    else:
+        cb, sb = packed_bytes(fmt, layout, rows, cols)
+        q = torch.empty(cb, dtype=torch.uint8, device=dev)
+        sc = torch.empty(sb, dtype=torch.uint8, device=dev)
     ts = torch.empty(G, dtype=torch.float32, device=dev) if fmt == NVFP4 else None
     R = torch.empty((rows, nS), dtype=torch.int16, device=dev) if nS else None
     wsb = quantize_workspace_bytes(fmt, rows, cols, G)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev) if wsb else None
-    quantize_into(fmt, x, group_offsets, G, chan_idx, nS, q, sc, ts, R, ws, stream)
-    return {"q": q, "scales": sc, "tscale": ts, "resid": R}
+    quantize_into(fmt, layout, x, group_offsets, G, chan_idx, nS, q, sc, ts, R, ws, stream)
+    return {"q": q, "scales": sc, "tscale": ts, "resid": R, "layout": layout, "rows": rows,
+            "cols": cols}
+
+
+def _shape(t):
+    """(rows, cols, layout) of a quantize() result (or a row-major dict of
+    q [rows, cols/2] and scales without those keys)."""
+    if "rows" in t:
+        return t["rows"], t["cols"], t["layout"]
+    return t["q"].shape[0], t["q"].shape[1] * 2, ROWMAJOR
 
 
 def gemm(fmt, a, b, chan_idx=None, y_dtype=OUT_F32, stream=None):
-    """a, b: quantize() results (b from W^T [N, K]).  Returns Y [M, N]."""
-    M, K = a["q"].shape[0], a["q"].shape[1] * 2
-    N = b["q"].shape[0]
+    """a, b: quantize() results in one layout (b from W^T [N, K]).
+    Returns Y [M, N]."""
+    M, K, layout = _shape(a)
+    N, Kb, layout_b = _shape(b)
+    if Kb != K or layout_b != layout:
+        raise ValueError("operands differ in K or layout")
     nS = 0 if chan_idx is None else chan_idx.numel()
     y = torch.empty((M, N), dtype=torch.float32 if y_dtype == OUT_F32 else torch.bfloat16,
                     device=a["q"].device)
-    gemm_into(fmt, M, N, K, a["q"], a["scales"], a["tscale"], b["q"], b["scales"], b["tscale"],
+    gemm_into(fmt, layout, M, N, K, a["q"], a["scales"], a["tscale"], b["q"], b["scales"], b["tscale"],
               chan_idx, nS, a["resid"] if nS else None, y, y_dtype, N, stream)
     return y
 

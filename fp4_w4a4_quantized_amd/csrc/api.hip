@@ -19,6 +19,10 @@ inline int blk_of(int fmt) { return fmt == FP4Q_NVFP4 ? 16 : 32; }
 
 inline bool fmt_ok(int fmt) { return fmt == FP4Q_NVFP4 || fmt == FP4Q_MXFP4; }
 
+inline bool layout_ok(int layout) {
+  return layout == FP4Q_LAYOUT_ROWMAJOR || layout == FP4Q_LAYOUT_TILED;
+}
+
 // Clear any stale error state before a launch, so that check_launch() sees
 // only what this call's launches produced.
 inline void clear_error() { (void)hipGetLastError(); }
@@ -52,6 +56,22 @@ const char* fp4q_status_str(int status) {
 
 int fp4q_last_hip_error(void) { return g_last_hip_error; }
 
+int fp4q_packed_bytes(fp4q_format_t fmt, fp4q_layout_t layout, int64_t rows, int64_t cols,
+                      size_t* code_bytes, size_t* scale_bytes) {
+  if (!fmt_ok(fmt) || !layout_ok(layout) || rows < 0 || cols <= 0) return FP4Q_ERR_INVALID;
+  const int blk = blk_of(fmt);
+  if (cols % blk != 0) return FP4Q_ERR_INVALID;
+  int64_t rc = rows, rs = rows;
+  if (layout == FP4Q_LAYOUT_TILED) {
+    if (cols % 128 != 0) return FP4Q_ERR_INVALID;
+    rc = (rows + 15) / 16 * 16;
+    rs = (rows + 63) / 64 * 64;
+  }
+  if (code_bytes) *code_bytes = (size_t)(rc * (cols / 2));
+  if (scale_bytes) *scale_bytes = (size_t)(rs * (cols / blk));
+  return FP4Q_OK;
+}
+
 size_t fp4q_quantize_workspace_bytes(fp4q_format_t fmt, int64_t rows, int64_t cols,
                                      int32_t num_groups) {
   (void)rows;
@@ -59,14 +79,16 @@ size_t fp4q_quantize_workspace_bytes(fp4q_format_t fmt, int64_t rows, int64_t co
   return fp4q::quantize_workspace_bytes(fmt, num_groups > 0 ? num_groups : 1);
 }
 
-int fp4q_quantize(fp4q_format_t fmt, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
-                  const int32_t* group_offsets, int32_t num_groups, const int32_t* chan_idx,
-                  int32_t n_chan, uint8_t* q, uint8_t* scales, float* tensor_scale,
-                  uint16_t* resid, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!fmt_ok(fmt)) return FP4Q_ERR_INVALID;
+int fp4q_quantize(fp4q_format_t fmt, fp4q_layout_t layout, const uint16_t* x, int64_t rows,
+                  int64_t cols, int64_t ldx, const int32_t* group_offsets, int32_t num_groups,
+                  const int32_t* chan_idx, int32_t n_chan, uint8_t* q, uint8_t* scales,
+                  float* tensor_scale, uint16_t* resid, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  if (!fmt_ok(fmt) || !layout_ok(layout)) return FP4Q_ERR_INVALID;
   const int blk = blk_of(fmt);
   if (rows < 0 || cols <= 0 || cols % blk != 0 || ldx < cols || ldx % 8 != 0)
     return FP4Q_ERR_INVALID;
+  if (layout == FP4Q_LAYOUT_TILED && cols % 128 != 0) return FP4Q_ERR_INVALID;
   if (num_groups < 1 || (num_groups > 1 && !group_offsets)) return FP4Q_ERR_INVALID;
   if (n_chan < 0 || n_chan > cols) return FP4Q_ERR_INVALID;
   if ((n_chan > 0) != (chan_idx != nullptr) || (n_chan > 0) != (resid != nullptr))
@@ -74,14 +96,15 @@ int fp4q_quantize(fp4q_format_t fmt, const uint16_t* x, int64_t rows, int64_t co
   if (fmt == FP4Q_NVFP4 && !tensor_scale) return FP4Q_ERR_INVALID;
   if (fmt == FP4Q_MXFP4 && tensor_scale) return FP4Q_ERR_INVALID;
   if (rows > 0 && (!x || !q || !scales)) return FP4Q_ERR_INVALID;
-  if (rows > 0 && (!aligned(x, 16) || !aligned(q, 16))) return FP4Q_ERR_INVALID;
+  if (rows > 0 && (!aligned(x, 16) || !aligned(q, 16) || !aligned(scales, 4)))
+    return FP4Q_ERR_INVALID;
   if (rows * (cols / 8) >= ((int64_t)1 << 31)) return FP4Q_ERR_UNSUPPORTED;  // 32-bit chunk index
   const size_t need = fp4q_quantize_workspace_bytes(fmt, rows, cols, num_groups);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 4)))
     return FP4Q_ERR_WORKSPACE;
   clear_error();
-  fp4q::launch_quantize(fmt, x, rows, cols, ldx, group_offsets, num_groups, chan_idx, n_chan, q,
-                        scales, tensor_scale, resid, workspace,
+  fp4q::launch_quantize(fmt, layout == FP4Q_LAYOUT_TILED, x, rows, cols, ldx, group_offsets,
+                        num_groups, chan_idx, n_chan, q, scales, tensor_scale, resid, workspace,
                         static_cast<hipStream_t>(stream));
   return check_launch();
 }
@@ -108,18 +131,20 @@ static int validate_gemm_common(int fmt, int64_t N, int64_t K, const uint8_t* a_
   return FP4Q_OK;
 }
 
-int fp4q_gemm(fp4q_format_t fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_q,
-              const uint8_t* a_s, const float* a_ts, const uint8_t* b_q, const uint8_t* b_s,
-              const float* b_ts, const int32_t* chan_idx, int32_t n_chan, const uint16_t* resid,
-              void* y, fp4q_dtype_t y_dtype, int64_t ldy, void* stream) {
+int fp4q_gemm(fp4q_format_t fmt, fp4q_layout_t layout, int64_t M, int64_t N, int64_t K,
+              const uint8_t* a_q, const uint8_t* a_s, const float* a_ts, const uint8_t* b_q,
+              const uint8_t* b_s, const float* b_ts, const int32_t* chan_idx, int32_t n_chan,
+              const uint16_t* resid, void* y, fp4q_dtype_t y_dtype, int64_t ldy, void* stream) {
+  if (!layout_ok(layout)) return FP4Q_ERR_INVALID;
   int rc = validate_gemm_common(fmt, N, K, a_q, a_s, a_ts, b_q, b_s, b_ts, chan_idx, n_chan,
                                 resid, y, y_dtype, M);
   if (rc != FP4Q_OK) return rc;
   if (ldy < N) return FP4Q_ERR_INVALID;
   if ((M + 127) / 128 > (int64_t)UINT32_MAX || (N + 31) / 32 > 65535) return FP4Q_ERR_UNSUPPORTED;
   clear_error();
-  fp4q::launch_gemm(fmt, M, N, K, nullptr, 1, a_q, a_s, a_ts, b_q, b_s, b_ts, chan_idx, n_chan,
-                    resid, y, y_dtype == FP4Q_OUT_BF16, ldy, static_cast<hipStream_t>(stream));
+  fp4q::launch_gemm(fmt, layout == FP4Q_LAYOUT_TILED, M, N, K, nullptr, 1, a_q, a_s, a_ts, b_q,
+                    b_s, b_ts, chan_idx, n_chan, resid, y, y_dtype == FP4Q_OUT_BF16, ldy,
+                    static_cast<hipStream_t>(stream));
   return check_launch();
 }
 
@@ -136,8 +161,8 @@ int fp4q_grouped_gemm(fp4q_format_t fmt, int64_t total_rows, int64_t N, int64_t 
   if (num_groups > MAX_GROUPS) return FP4Q_ERR_UNSUPPORTED;
   if ((N + 127) / 128 > 65535) return FP4Q_ERR_UNSUPPORTED;
   clear_error();
-  fp4q::launch_gemm(fmt, total_rows, N, K, group_offsets, num_groups, a_q, a_s, a_ts, b_q, b_s,
-                    b_ts, chan_idx, n_chan, resid, y, y_dtype == FP4Q_OUT_BF16, N,
+  fp4q::launch_gemm(fmt, false, total_rows, N, K, group_offsets, num_groups, a_q, a_s, a_ts, b_q,
+                    b_s, b_ts, chan_idx, n_chan, resid, y, y_dtype == FP4Q_OUT_BF16, N,
                     static_cast<hipStream_t>(stream));
   return check_launch();
 }

@@ -78,4 +78,31 @@ __device__ __forceinline__ float nv_tensor_scale(float amax) {
   return (amax == 0.0f || t == 0.0f) ? 1.0f : t;
 }
 
+// Byte offsets of packed FP4 operands in the two layouts (include/fp4q.h
+// defines them).  Row-major: codes [rows][K/2], scales [rows][K/blk].
+// Tiled (K % 128 == 0): codes in 1 KB blocks, one per (16-row group,
+// 128-column step), the 16 bytes of row r and step-byte chunk c at
+// (c*16 + r)*16 inside the block; scales in blocks per (64-row group, step)
+// of 64 rows x (128/blk) bytes, NVFP4 as two dword planes [d][row], MXFP4 as
+// one dword per row.  One wave's 16-byte loads of 16 rows x 64 bytes, and
+// its dword loads of 64 rows' scales, are then single contiguous spans.
+__device__ __forceinline__ int64_t code_off(bool tiled, int64_t row, int64_t byte_col, int64_t K) {
+  if (!tiled) return row * (K >> 1) + byte_col;
+  const int b64 = (int)(byte_col & 63);
+  return (((row >> 4) * (K >> 7) + (byte_col >> 6)) << 10) +
+         ((((b64 >> 4) << 4) + (row & 15)) << 4) + (b64 & 15);
+}
+
+// FMT: 0 NVFP4 (16-element blocks), 1 MXFP4 (32).
+template <int FMT>
+__device__ __forceinline__ int64_t scale_off(bool tiled, int64_t row, int64_t blk, int64_t K) {
+  constexpr int BLK = (FMT == 0) ? 16 : 32;
+  constexpr int SPS = 128 / BLK;  // scale bytes per row per 128-column step
+  if (!tiled) return row * (K / BLK) + blk;
+  const int e = (int)(blk % SPS);
+  const int64_t base = ((row >> 6) * (K >> 7) + blk / SPS) * (SPS * 64);
+  if (FMT == 0) return base + (((e >> 2) * 64 + (row & 63)) << 2) + (e & 3);
+  return base + ((row & 63) << 2) + e;
+}
+
 }  // namespace fp4q

@@ -10,26 +10,26 @@ namespace fp4q {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-int launch_quantize(int fmt, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+int launch_quantize(int fmt, bool tiled, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                     const int32_t* off, int G, const int32_t* chan, int nS, uint8_t* q,
                     uint8_t* scales, float* tscale, uint16_t* resid, void* ws,
                     hipStream_t stream);
 
 size_t quantize_workspace_bytes(int fmt, int G);
 
-int launch_gemm(int fmt, int64_t M, int64_t N, int64_t K, const int32_t* off, int G,
+int launch_gemm(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const int32_t* off, int G,
                 const uint8_t* aq, const uint8_t* as, const float* ats, const uint8_t* bq,
                 const uint8_t* bs, const float* bts, const int32_t* chan, int nS,
                 const uint16_t* resid, void* y, int y_bf16, int64_t ldy, hipStream_t stream);
 
-bool big_gemm_eligible(int64_t M, int64_t N, int64_t K, int nS);
-int launch_gemm_big(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* aq,
+bool big_gemm_eligible(int64_t M, int64_t N, int64_t K, int nS, const void* resid);
+int launch_gemm_big(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const uint8_t* aq,
                     const uint8_t* as, const float* ats, const uint8_t* bq, const uint8_t* bs,
                     const float* bts, const int32_t* chan, int nS, const uint16_t* resid,
                     void* y, int y_bf16, int64_t ldy, hipStream_t stream);
 
 bool skinny_gemm_eligible(int64_t M, int64_t N, int64_t K, int nS, const void* resid);
-int launch_gemm_skinny(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* aq,
+int launch_gemm_skinny(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const uint8_t* aq,
                        const uint8_t* as, const float* ats, const uint8_t* bq, const uint8_t* bs,
                        const float* bts, const int32_t* chan, int nS, const uint16_t* resid,
                        void* y, int y_bf16, int64_t ldy, hipStream_t stream);

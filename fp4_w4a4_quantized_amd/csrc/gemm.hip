@@ -57,6 +57,7 @@ struct GemmArgs {
   void* y;
   int y_bf16;
   int64_t ldy;
+  bool tiled;  // packed operands in the tiled layout (never for the grouped form)
 };
 
 constexpr int LDS_ROW = 80;  // bytes per staged row: 64 data + 16 pad
@@ -78,11 +79,11 @@ __device__ __forceinline__ f16x8 decode_nv8(uint32_t w, f16x2 s) {
 template <int FMT>
 __device__ __forceinline__ uint32_t wdeq_bf16(const uint8_t* __restrict__ bq,
                                               const uint8_t* __restrict__ bs, int64_t K,
-                                              int64_t n, int c) {
+                                              bool tiled, int64_t n, int c) {
   constexpr int BLK = (FMT == FP4Q_NVFP4) ? 16 : 32;
-  uint32_t byte = bq[n * (K >> 1) + (c >> 1)];
+  uint32_t byte = bq[code_off(tiled, n, c >> 1, K)];
   uint32_t code = (c & 1) ? (byte >> 4) : (byte & 15u);
-  uint32_t sc = bs[n * (K / BLK) + c / BLK];
+  uint32_t sc = bs[scale_off<FMT>(tiled, n, c / BLK, K)];
   float s = (FMT == FP4Q_NVFP4) ? e4m3_value(sc)
                                 : (sc ? __uint_as_float(sc << 23) : __uint_as_float(0x00400000u));
   float v = e2m1_mag_value(code) * s;
@@ -106,6 +107,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs p) {
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t K = p.K, N = p.N;
   const int64_t K2 = K >> 1, KS = K / BLK;
+  const bool tiled = GROUPED ? false : p.tiled;
 
   // ---- which rows / group this workgroup owns
   int g = 0;
@@ -171,7 +173,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs p) {
       int64_t gr = row_begin + r;
       u32x4 v = {0u, 0u, 0u, 0u};
       if (c < BM * 4 && gr < row_end)
-        v = *reinterpret_cast<const u32x4*>(aq + gr * K2 + (int64_t)kt * 64 + ch * 16);
+        v = *reinterpret_cast<const u32x4*>(aq + code_off(tiled, gr, (int64_t)kt * 64 + ch * 16, K));
       ra[i] = v;
     }
 #pragma unroll
@@ -181,26 +183,27 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs p) {
       int64_t gc = col0 + r;
       u32x4 v = {0u, 0u, 0u, 0u};
       if (c < BN * 4 && gc < N)
-        v = *reinterpret_cast<const u32x4*>(bq + gc * K2 + (int64_t)kt * 64 + ch * 16);
+        v = *reinterpret_cast<const u32x4*>(bq + code_off(tiled, gc, (int64_t)kt * 64 + ch * 16, K));
       rb[i] = v;
     }
+    // scale dwords: bytes [0,4) and (NVFP4) [4,8) of the row's step; in the
+    // tiled layout the two NVFP4 dwords sit in separate planes
     rsc[0] = rsc[1] = 0u;
     const uint8_t* src = nullptr;
+    int64_t srow = 0;
     if (t < BM) {
-      int64_t gr = row_begin + t;
-      if (gr < row_end) src = as + gr * KS + (int64_t)kt * SPR;
+      srow = row_begin + t;
+      if (srow < row_end) src = as;
     } else if (t < BM + BN) {
-      int64_t gc = col0 + (t - BM);
-      if (gc < N) src = bs + gc * KS + (int64_t)kt * SPR;
+      srow = col0 + (t - BM);
+      if (srow < N) src = bs;
     }
     if (src) {
-      if (SPR == 8) {
-        u32x2 v = *reinterpret_cast<const u32x2*>(src);
-        rsc[0] = v.x;
-        rsc[1] = v.y;
-      } else {
-        rsc[0] = *reinterpret_cast<const uint32_t*>(src);
-      }
+      rsc[0] = *reinterpret_cast<const uint32_t*>(
+          src + scale_off<FMT>(tiled, srow, (int64_t)kt * SPR, K));
+      if (SPR == 8)
+        rsc[1] = *reinterpret_cast<const uint32_t*>(
+            src + scale_off<FMT>(tiled, srow, (int64_t)kt * SPR + 4, K));
     }
   };
   auto sstore = [&](int buf) {
@@ -334,7 +337,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs p) {
         uint32_t h[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          h[e] = (gc < N && ch[e] >= 0) ? wdeq_bf16<FMT>(bq, bs, K, gc, ch[e]) : 0u;
+          h[e] = (gc < N && ch[e] >= 0) ? wdeq_bf16<FMT>(bq, bs, K, tiled, gc, ch[e]) : 0u;
         u32x4 pk = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
                     h[6] | (h[7] << 16)};
         rb8[j] = __builtin_bit_cast(bf16x8, pk);
@@ -374,11 +377,11 @@ static void launch_one(const GemmArgs& a, unsigned mtiles, hipStream_t stream) {
   hipLaunchKernelGGL((k_gemm<FMT, BM, BN, GROUPED>), grid, dim3(256), 0, stream, a);
 }
 
-int launch_gemm(int fmt, int64_t M, int64_t N, int64_t K, const int32_t* off, int G,
+int launch_gemm(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const int32_t* off, int G,
                 const uint8_t* aq, const uint8_t* as, const float* ats, const uint8_t* bq,
                 const uint8_t* bs, const float* bts, const int32_t* chan, int nS,
                 const uint16_t* resid, void* y, int y_bf16, int64_t ldy, hipStream_t stream) {
-  GemmArgs a{M, N, K, off, G, aq, as, ats, bq, bs, bts, chan, nS, resid, y, y_bf16, ldy};
+  GemmArgs a{M, N, K, off, G, aq, as, ats, bq, bs, bts, chan, nS, resid, y, y_bf16, ldy, tiled};
   if (M == 0 || N == 0) return 0;
   const bool grouped = (off != nullptr);
   if (grouped) {
@@ -387,10 +390,10 @@ int launch_gemm(int fmt, int64_t M, int64_t N, int64_t K, const int32_t* off, in
     if (fmt == FP4Q_NVFP4) launch_one<FP4Q_NVFP4, BM, 128, true>(a, mt, stream);
     else launch_one<FP4Q_MXFP4, BM, 128, true>(a, mt, stream);
   } else if (skinny_gemm_eligible(M, N, K, nS, resid)) {
-    launch_gemm_skinny(fmt, M, N, K, aq, as, ats, bq, bs, bts, chan, nS, resid, y, y_bf16, ldy,
+    launch_gemm_skinny(fmt, tiled, M, N, K, aq, as, ats, bq, bs, bts, chan, nS, resid, y, y_bf16, ldy,
                        stream);
-  } else if (big_gemm_eligible(M, N, K, nS)) {
-    launch_gemm_big(fmt, M, N, K, aq, as, ats, bq, bs, bts, chan, nS, resid, y, y_bf16, ldy,
+  } else if (big_gemm_eligible(M, N, K, nS, resid)) {
+    launch_gemm_big(fmt, tiled, M, N, K, aq, as, ats, bq, bs, bts, chan, nS, resid, y, y_bf16, ldy,
                     stream);
   } else if (M <= 64) {
     unsigned mt = (unsigned)((M + 63) / 64);

@@ -93,11 +93,48 @@ struct Step {
   u32x2 xsc, wsc;
 };
 
-template <int FMT>
+// Row-major operands: each lane computes its row addresses.  Tiled operands
+// (TL): a fragment load of 16 rows x 64 bytes is one 1 KB block, lane l at
+// byte 16 l, so only the block index (wave-uniform: the 16-row group,
+// clamped to the last padded group) varies; `wso` is the lane's weight-row
+// scale offset within a step (computed once per workgroup).
+template <int FMT, bool TL>
 __device__ __forceinline__ void load_step(const SkinnyArgs& p, int kt, int lane, int64_t col0,
-                                          Step& s) {
-  constexpr int BLK = (FMT == FP4Q_NVFP4) ? 16 : 32;
-  const int64_t K2 = p.K >> 1, KS = p.K / BLK;
+                                          int64_t wso, Step& s) {
+  constexpr int SPS = (FMT == FP4Q_NVFP4) ? 8 : 4;  // scale bytes per row per step
+  const int64_t K = p.K;
+  if (TL) {
+    const int64_t KB = K >> 7;
+    const int64_t gN = ((p.N + 15) >> 4) - 1, gM = ((p.M + 15) >> 4) - 1;
+#pragma unroll
+    for (int g = 0; g < SK_CG; ++g) {
+      int64_t grp = (col0 >> 4) + g;
+      grp = grp < gN ? grp : gN;
+      s.w[g] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(p.bq + ((grp * KB + kt) << 10) + lane * 16));
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int64_t grp = a < gM ? a : gM;
+      s.x[a] = *reinterpret_cast<const u32x4*>(p.aq + ((grp * KB + kt) << 10) + lane * 16);
+    }
+    // activation rows 0..63 are the first 64-row scale group
+    const int64_t st = (int64_t)kt * (SPS * 64);
+    const uint8_t* ws = p.bs + wso + st;
+    const uint8_t* xs = p.as + st + lane * 4;
+    if (FMT == FP4Q_NVFP4) {
+      // the two scale dwords of a step sit in planes 256 bytes apart
+      s.wsc = u32x2{*reinterpret_cast<const uint32_t*>(ws),
+                    *reinterpret_cast<const uint32_t*>(ws + 256)};
+      s.xsc = u32x2{*reinterpret_cast<const uint32_t*>(xs),
+                    *reinterpret_cast<const uint32_t*>(xs + 256)};
+    } else {
+      s.wsc = u32x2{*reinterpret_cast<const uint32_t*>(ws), 0u};
+      s.xsc = u32x2{*reinterpret_cast<const uint32_t*>(xs), 0u};
+    }
+    return;
+  }
+  const int64_t K2 = K >> 1, KS = K / (FMT == FP4Q_NVFP4 ? 16 : 32);
   const int q = lane >> 4, lr = lane & 15;
 #pragma unroll
   for (int g = 0; g < SK_CG; ++g) {
@@ -224,7 +261,7 @@ __device__ __forceinline__ void process_step(const Step& st, int kt, uint8_t* sl
   }
 }
 
-template <int FMT>
+template <int FMT, bool TL>
 __global__ void __launch_bounds__(SK_T, 1) k_gemm_skinny(SkinnyArgs p) {
   using L = SlotLayout<FMT>;
   __shared__ __attribute__((aligned(16))) v4f32s red[SK_WAVES * 4 * SK_CG * 64];   // 96 KB
@@ -252,9 +289,19 @@ __global__ void __launch_bounds__(SK_T, 1) k_gemm_skinny(SkinnyArgs p) {
   // for it never waits for the operand stream
   const int my_ch_raw = *(nS > 0 ? p.chan + (lane < nS ? lane : nS - 1)
                                  : reinterpret_cast<const int32_t*>(p.aq));
+  // tiled layout: this lane's weight-row scale offset within a step (rows
+  // exist up to the 64-row padding)
+  int64_t wso = 0;
+  if (TL) {
+    constexpr int SPS = (FMT == FP4Q_NVFP4) ? 8 : 4;
+    int64_t wrow = col0 + (lane < SK_COLS ? lane : SK_COLS - 1);
+    const int64_t wlast = ((p.N + 63) & ~(int64_t)63) - 1;
+    wrow = wrow < wlast ? wrow : wlast;
+    wso = (wrow >> 6) * (p.K >> 7) * (SPS * 64) + (wrow & 63) * 4;
+  }
   Step s0, s1;
-  load_step<FMT>(p, wave < nk ? wave : nk - 1, lane, col0, s0);
-  load_step<FMT>(p, wave + SK_WAVES < nk ? wave + SK_WAVES : nk - 1, lane, col0, s1);
+  load_step<FMT, TL>(p, wave < nk ? wave : nk - 1, lane, col0, wso, s0);
+  load_step<FMT, TL>(p, wave + SK_WAVES < nk ? wave + SK_WAVES : nk - 1, lane, col0, wso, s1);
   // R [M][nS] bf16, contiguous, 16-byte aligned, M nS a multiple of 8:
   // elements 8t .. 8t+7 of the (at most 4096)
   const int rtot = (int)p.M * nS, e0 = 8 * t;
@@ -278,10 +325,10 @@ __global__ void __launch_bounds__(SK_T, 1) k_gemm_skinny(SkinnyArgs p) {
   } else {
     for (int kt = wave; kt < nk; kt += 2 * SK_WAVES) {
       process_step<FMT>(s0, kt, slot0, lane, my_ch, nS, sB, acc);
-      if (kt + 2 * SK_WAVES < nk) load_step<FMT>(p, kt + 2 * SK_WAVES, lane, col0, s0);
+      if (kt + 2 * SK_WAVES < nk) load_step<FMT, TL>(p, kt + 2 * SK_WAVES, lane, col0, wso, s0);
       if (kt + SK_WAVES < nk) {
         process_step<FMT>(s1, kt + SK_WAVES, slot1, lane, my_ch, nS, sB, acc);
-        if (kt + 3 * SK_WAVES < nk) load_step<FMT>(p, kt + 3 * SK_WAVES, lane, col0, s1);
+        if (kt + 3 * SK_WAVES < nk) load_step<FMT, TL>(p, kt + 3 * SK_WAVES, lane, col0, wso, s1);
       }
     }
   }
@@ -360,16 +407,20 @@ bool skinny_gemm_eligible(int64_t M, int64_t N, int64_t K, int nS, const void* r
   return M >= 1 && M <= SK_M && N >= 1 && K % 128 == 0 && nS <= SK_MAXS && resid_ok;
 }
 
-int launch_gemm_skinny(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* aq,
+int launch_gemm_skinny(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const uint8_t* aq,
                        const uint8_t* as, const float* ats, const uint8_t* bq, const uint8_t* bs,
                        const float* bts, const int32_t* chan, int nS, const uint16_t* resid,
                        void* y, int y_bf16, int64_t ldy, hipStream_t stream) {
   SkinnyArgs a{M, N, K, aq, as, ats, bq, bs, bts, chan, nS, resid, y, y_bf16, ldy};
   dim3 grid((unsigned)((N + SK_COLS - 1) / SK_COLS));
-  if (fmt == FP4Q_NVFP4)
-    hipLaunchKernelGGL(k_gemm_skinny<FP4Q_NVFP4>, grid, dim3(SK_T), 0, stream, a);
+  if (fmt == FP4Q_NVFP4 && tiled)
+    hipLaunchKernelGGL((k_gemm_skinny<FP4Q_NVFP4, true>), grid, dim3(SK_T), 0, stream, a);
+  else if (fmt == FP4Q_NVFP4)
+    hipLaunchKernelGGL((k_gemm_skinny<FP4Q_NVFP4, false>), grid, dim3(SK_T), 0, stream, a);
+  else if (tiled)
+    hipLaunchKernelGGL((k_gemm_skinny<FP4Q_MXFP4, true>), grid, dim3(SK_T), 0, stream, a);
   else
-    hipLaunchKernelGGL(k_gemm_skinny<FP4Q_MXFP4>, grid, dim3(SK_T), 0, stream, a);
+    hipLaunchKernelGGL((k_gemm_skinny<FP4Q_MXFP4, false>), grid, dim3(SK_T), 0, stream, a);
   return 0;
 }
 

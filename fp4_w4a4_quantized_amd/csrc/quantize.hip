@@ -242,8 +242,9 @@ __device__ __forceinline__ uint32_t e2m1_pack8(const float (&v)[8]) {
 // Quantize chunk cc of row `row` held in v.  All lanes of the wave call this
 // (the block max moves between lanes); `active` gates the stores.
 template <int FMT>
-__device__ __forceinline__ void quantize_chunk(u32x4 v, bool active, int64_t row, int64_t cc,
-                                               int64_t cols, float t, uint32_t chan_ent, int nS,
+__device__ __forceinline__ void quantize_chunk(u32x4 v, bool active, bool tiled, int64_t row,
+                                               int64_t cc, int64_t cols, float t,
+                                               uint32_t chan_ent, int nS,
                                                uint8_t* __restrict__ q, uint8_t* __restrict__ scales,
                                                uint16_t* __restrict__ resid) {
   constexpr int CPB = (FMT == FP4Q_NVFP4) ? 2 : 4;  // chunks per scale block
@@ -286,10 +287,10 @@ __device__ __forceinline__ void quantize_chunk(u32x4 v, bool active, int64_t row
     for (int k = 0; k < 8; ++k) qv[k] = xs[k] * inv_pow2;  // exact
   }
   if (!active) return;
-  if ((cc & (CPB - 1)) == 0) scales[row * (cols / (8 * CPB)) + cc / CPB] = (uint8_t)sc;
+  if ((cc & (CPB - 1)) == 0) scales[scale_off<FMT>(tiled, row, cc / CPB, cols)] = (uint8_t)sc;
 
   const uint32_t packed = e2m1_pack8(qv);
-  *reinterpret_cast<uint32_t*>(q + row * (cols >> 1) + 4 * cc) = packed;
+  *reinterpret_cast<uint32_t*>(q + code_off(tiled, row, 4 * cc, cols)) = packed;
 
   // residual on the selected channels of this chunk
   uint32_t mask = chan_ent & 0xFFu;
@@ -319,7 +320,7 @@ enum { AMAX_NONE = 0, AMAX_GROUP_WORDS = 1, AMAX_PARTIALS = 2, AMAX_FUSED = 3 };
 
 template <int FMT, int MODE, int NT, int U>
 __global__ void __launch_bounds__(NT) k_quantize(
-    ChunkGrid gr, int64_t rows, int64_t cols, const int32_t* __restrict__ off, int G,
+    ChunkGrid gr, int64_t rows, int64_t cols, bool tiled, const int32_t* __restrict__ off, int G,
     const int32_t* __restrict__ chan, int nS, uint8_t* __restrict__ q,
     uint8_t* __restrict__ scales, float* __restrict__ tscale, uint16_t* __restrict__ resid,
     const uint32_t* __restrict__ amax_words, int nparts) {
@@ -376,22 +377,23 @@ __global__ void __launch_bounds__(NT) k_quantize(
     uint32_t ent = 0;
     if (nS > 0 && active)
       ent = (use_tab && g == gA) ? tab[cc] : chan_entry_search(chan + (int64_t)g * nS, nS, cc);
-    quantize_chunk<FMT>(v[u], active, row, cc, cols, t, ent, nS, q, scales, resid);
+    quantize_chunk<FMT>(v[u], active, tiled, row, cc, cols, t, ent, nS, q, scales, resid);
   }
 }
 
 template <int FMT, int MODE, int NT, int U>
-static void launch_q(const ChunkGrid& gr, int64_t rows, int64_t cols, hipStream_t stream,
+static void launch_q(const ChunkGrid& gr, int64_t rows, int64_t cols, bool tiled,
+                     hipStream_t stream,
                      const int32_t* off, int G, const int32_t* chan, int nS, uint8_t* q,
                      uint8_t* scales, float* tscale, uint16_t* resid, const uint32_t* words,
                      int nparts) {
   const int64_t per = (int64_t)NT * U, total = rows * (int64_t)gr.cpr;
   dim3 grid((unsigned)((total + per - 1) / per));
-  hipLaunchKernelGGL((k_quantize<FMT, MODE, NT, U>), grid, dim3(NT), 0, stream, gr, rows, cols, off,
-                     G, chan, nS, q, scales, tscale, resid, words, nparts);
+  hipLaunchKernelGGL((k_quantize<FMT, MODE, NT, U>), grid, dim3(NT), 0, stream, gr, rows, cols,
+                     tiled, off, G, chan, nS, q, scales, tscale, resid, words, nparts);
 }
 
-int launch_quantize(int fmt, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+int launch_quantize(int fmt, bool tiled, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                     const int32_t* off, int G, const int32_t* chan, int nS, uint8_t* q,
                     uint8_t* scales, float* tscale, uint16_t* resid, void* ws,
                     hipStream_t stream) {
@@ -402,7 +404,7 @@ int launch_quantize(int fmt, const uint16_t* x, int64_t rows, int64_t cols, int6
   const int Gk = grouped ? G : 1;
   if (fmt == FP4Q_MXFP4) {
     if (chunks > 0)
-      launch_q<FP4Q_MXFP4, AMAX_NONE, QT, QU>(gr, rows, cols, stream, off, Gk, chan, nS, q, scales,
+      launch_q<FP4Q_MXFP4, AMAX_NONE, QT, QU>(gr, rows, cols, tiled, stream, off, Gk, chan, nS, q, scales,
                                                tscale, resid, words, 0);
     return 0;
   }
@@ -412,7 +414,7 @@ int launch_quantize(int fmt, const uint16_t* x, int64_t rows, int64_t cols, int6
       const int64_t nwg = (rows + AMAX_ROWS_PER_WG - 1) / AMAX_ROWS_PER_WG;
       hipLaunchKernelGGL(k_group_amax, dim3((unsigned)nwg), dim3(QT), 0, stream, gr, rows, off, G,
                          words);
-      launch_q<FP4Q_NVFP4, AMAX_GROUP_WORDS, QT, QU>(gr, rows, cols, stream, off, G, chan, nS, q,
+      launch_q<FP4Q_NVFP4, AMAX_GROUP_WORDS, QT, QU>(gr, rows, cols, tiled, stream, off, G, chan, nS, q,
                                                       scales, tscale, resid, words, 0);
     }
     return 0;
@@ -423,14 +425,14 @@ int launch_quantize(int fmt, const uint16_t* x, int64_t rows, int64_t cols, int6
   }
   if (chunks <= FUSED_MAX_CHUNKS) {
     if (SMALL_FUSED) {
-      launch_q<FP4Q_NVFP4, AMAX_FUSED, FT, 1>(gr, rows, cols, stream, off, 1, chan, nS, q, scales,
+      launch_q<FP4Q_NVFP4, AMAX_FUSED, FT, 1>(gr, rows, cols, tiled, stream, off, 1, chan, nS, q, scales,
                                               tscale, resid, words, 0);
     } else {
       // two short passes spread over many workgroups
       const int64_t parts = (chunks + QT - 1) / QT;
       hipLaunchKernelGGL(k_amax_partial, dim3((unsigned)parts), dim3(QT), 0, stream, gr,
                          (uint32_t)chunks, words);
-      launch_q<FP4Q_NVFP4, AMAX_PARTIALS, QT, 1>(gr, rows, cols, stream, off, 1, chan, nS, q,
+      launch_q<FP4Q_NVFP4, AMAX_PARTIALS, QT, 1>(gr, rows, cols, tiled, stream, off, 1, chan, nS, q,
                                                   scales, tscale, resid, words, (int)parts);
     }
     return 0;
@@ -439,7 +441,7 @@ int launch_quantize(int fmt, const uint16_t* x, int64_t rows, int64_t cols, int6
   parts = parts < AMAX_PARTS ? parts : AMAX_PARTS;
   hipLaunchKernelGGL(k_amax_partial, dim3((unsigned)parts), dim3(QT), 0, stream, gr,
                      (uint32_t)chunks, words);
-  launch_q<FP4Q_NVFP4, AMAX_PARTIALS, QT, QU>(gr, rows, cols, stream, off, 1, chan, nS, q, scales,
+  launch_q<FP4Q_NVFP4, AMAX_PARTIALS, QT, QU>(gr, rows, cols, tiled, stream, off, 1, chan, nS, q, scales,
                                                tscale, resid, words, (int)parts);
   return 0;
 }

@@ -34,13 +34,29 @@
  *    element = e2m1(x * 2^-e).  No tensor scale.
  *  - packing: two codes per byte, even element in the low nibble.
  *
+ * Packed operand layouts (codes and block scales; chosen per call):
+ *  - FP4Q_LAYOUT_ROWMAJOR: codes u8 [rows, cols/2], scales u8 [rows, cols/blk].
+ *  - FP4Q_LAYOUT_TILED (cols % 128 == 0): the GEMM's native layout.  Codes
+ *    are 1 KB blocks, one per (16-row group G, 128-column step k), block
+ *    (G, k) at byte (G * cols/128 + k) * 1024; inside it the 16 bytes of row
+ *    16G + r, step bytes [16c, 16c + 16) (c = 0..3), sit at (c*16 + r)*16.
+ *    Scales are blocks per (64-row group H, step k) at
+ *    (H * cols/128 + k) * (64 * 128/blk): NVFP4 (512 bytes) holds scale byte
+ *    8k + 4d + e of row 64H + r at (d*64 + r)*4 + e; MXFP4 (256 bytes) holds
+ *    byte 4k + e of row 64H + r at r*4 + e.  Rows are padded up to a
+ *    multiple of 16 (codes) and 64 (scales); fp4q_packed_bytes() gives the
+ *    sizes.  A GEMM load of 16 rows x 64 bytes, or of 64 rows' scales, is
+ *    then one contiguous span: on MI355X that streams operand tiles about
+ *    2.7x faster than rows 2 KB apart.  The contents of padding rows are
+ *    never used in a result.
+ *
  * Conventions for every entry point:
  *  - Tensor pointers are DEVICE pointers owned by the caller.  The library
  *    allocates nothing and keeps no state beyond a thread-local last error.
  *  - Every call is asynchronous on the caller's HIP stream (passed as void*,
  *    NULL = default stream); results are ready when that stream is.
- *  - Layouts are row-major with the FP4 blocks along the contiguous (K)
- *    dimension.  Weights are passed transposed, W^T [N, K].
+ *  - Unpacked tensors are row-major; FP4 blocks run along the contiguous
+ *    (K) dimension.  Weights are passed transposed, W^T [N, K].
  *  - Arguments are validated on the host before any HIP call; device-side
  *    contents are preconditions and are NOT checked (doing so would need a
  *    synchronisation): channel lists ascending, unique and < K; group
@@ -60,6 +76,7 @@ extern "C" {
 
 typedef enum { FP4Q_NVFP4 = 0, FP4Q_MXFP4 = 1 } fp4q_format_t;
 typedef enum { FP4Q_OUT_F32 = 0, FP4Q_OUT_BF16 = 1 } fp4q_dtype_t;
+typedef enum { FP4Q_LAYOUT_ROWMAJOR = 0, FP4Q_LAYOUT_TILED = 1 } fp4q_layout_t;
 
 /* Status codes. */
 #define FP4Q_OK 0
@@ -74,6 +91,13 @@ const char* fp4q_status_str(int status);
 /* hipError_t of the last FP4Q_ERR_HIP on the calling thread (0 if none). */
 int fp4q_last_hip_error(void);
 
+/* Bytes of the packed codes and block scales of a [rows, cols] tensor in a
+ * layout (rows padded as the tiled layout requires).  Returns FP4Q_OK, or
+ * FP4Q_ERR_INVALID for a bad enum, negative rows, cols not a multiple of the
+ * block size, or a tiled layout with cols % 128 != 0. */
+int fp4q_packed_bytes(fp4q_format_t fmt, fp4q_layout_t layout, int64_t rows, int64_t cols,
+                      size_t* code_bytes, size_t* scale_bytes);
+
 /* ------------------------------------------------------------------------
  * Activation (or weight) quantization.  QUADS abstract: activations are
  * quantized online each forward pass (weights go through the same path once
@@ -87,8 +111,12 @@ int fp4q_last_hip_error(void);
  *                 num_groups == 1 means one group of all rows
  *   chan_idx      device int32 [num_groups, n_chan]: channels (columns) whose
  *                 residual is emitted, ascending per group; NULL iff n_chan == 0
- *   q             out u8 [rows, cols/2] packed codes (16-byte aligned)
- *   scales        out u8 [rows, cols/blk] block scale codes (blk 16 / 32)
+ *   layout        layout of q and scales (see above); FP4Q_LAYOUT_TILED needs
+ *                 cols % 128 == 0 and buffers of fp4q_packed_bytes()
+ *   q             out packed codes (16-byte aligned), u8 [rows, cols/2]
+ *                 when row-major
+ *   scales        out block scale codes (blk 16 / 32; 4-byte aligned),
+ *                 u8 [rows, cols/blk] when row-major
  *   tensor_scale  out f32 [num_groups] (NVFP4; must be NULL for MXFP4);
  *                 empty groups get 1.0
  *   resid         out bf16 [rows, n_chan]: bf16_rne(x - deq(code)) at
@@ -105,10 +133,11 @@ int fp4q_last_hip_error(void);
 size_t fp4q_quantize_workspace_bytes(fp4q_format_t fmt, int64_t rows, int64_t cols,
                                      int32_t num_groups);
 
-int fp4q_quantize(fp4q_format_t fmt, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
-                  const int32_t* group_offsets, int32_t num_groups, const int32_t* chan_idx,
-                  int32_t n_chan, uint8_t* q, uint8_t* scales, float* tensor_scale,
-                  uint16_t* resid, void* workspace, size_t workspace_bytes, void* stream);
+int fp4q_quantize(fp4q_format_t fmt, fp4q_layout_t layout, const uint16_t* x, int64_t rows,
+                  int64_t cols, int64_t ldx, const int32_t* group_offsets, int32_t num_groups,
+                  const int32_t* chan_idx, int32_t n_chan, uint8_t* q, uint8_t* scales,
+                  float* tensor_scale, uint16_t* resid, void* workspace, size_t workspace_bytes,
+                  void* stream);
 
 /* ------------------------------------------------------------------------
  * Compensated W4A4 GEMM.  QUADS abstract (native W4A4 FP4 GEMM plus
@@ -122,9 +151,11 @@ int fp4q_quantize(fp4q_format_t fmt, const uint16_t* x, int64_t rows, int64_t co
  * (weights as W^T) and S = chan_idx.  Accumulation is FP32 (MFMA); the
  * result equals the exact sum within (K + n_chan) * 2^-23 * sum|terms|.
  *
- *   a_q, a_s   u8 [M, K/2], [M, K/blk] (16-byte aligned)
+ *   layout     layout of both operands' codes and scales (see above)
+ *   a_q, a_s   packed activations and scales, [M, K/2], [M, K/blk] when
+ *              row-major (codes 16-byte, scales 8-byte aligned)
  *   a_ts       device f32 [1] tensor scale (NVFP4), NULL for MXFP4
- *   b_q, b_s   u8 [N, K/2], [N, K/blk] (16-byte aligned)
+ *   b_q, b_s   packed W^T, [N, K/2], [N, K/blk] when row-major (same alignment)
  *   b_ts       device f32 [1] (NVFP4), NULL for MXFP4
  *   chan_idx   device int32 [n_chan] ascending, < K; resid bf16 [M, n_chan]
  *              (both NULL iff n_chan == 0)
@@ -132,10 +163,10 @@ int fp4q_quantize(fp4q_format_t fmt, const uint16_t* x, int64_t rows, int64_t co
  *
  * K must be a multiple of 128 (FP4Q_ERR_UNSUPPORTED otherwise).
  * ------------------------------------------------------------------------ */
-int fp4q_gemm(fp4q_format_t fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_q,
-              const uint8_t* a_s, const float* a_ts, const uint8_t* b_q, const uint8_t* b_s,
-              const float* b_ts, const int32_t* chan_idx, int32_t n_chan, const uint16_t* resid,
-              void* y, fp4q_dtype_t y_dtype, int64_t ldy, void* stream);
+int fp4q_gemm(fp4q_format_t fmt, fp4q_layout_t layout, int64_t M, int64_t N, int64_t K,
+              const uint8_t* a_q, const uint8_t* a_s, const float* a_ts, const uint8_t* b_q,
+              const uint8_t* b_s, const float* b_ts, const int32_t* chan_idx, int32_t n_chan,
+              const uint16_t* resid, void* y, fp4q_dtype_t y_dtype, int64_t ldy, void* stream);
 
 /* ------------------------------------------------------------------------
  * Expert-grouped compensated GEMM (MoE layer; QUADS abstract: NVFP4 rollout
@@ -143,7 +174,7 @@ int fp4q_gemm(fp4q_format_t fmt, int64_t M, int64_t N, int64_t K, const uint8_t*
  * activations use expert g's weights, tensor scales and channel list:
  *
  *   group_offsets  device int32 [G + 1]
- *   a_q, a_s       [total_rows, K/2], [total_rows, K/blk]
+ *   a_q, a_s       [total_rows, K/2], [total_rows, K/blk] (row-major)
  *   a_ts           device f32 [G] (NVFP4), NULL for MXFP4
  *   b_q, b_s       [G, N, K/2], [G, N, K/blk]
  *   b_ts           device f32 [G] (NVFP4), NULL for MXFP4

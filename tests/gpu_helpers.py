@@ -36,9 +36,71 @@ def to_host(t) -> np.ndarray:
     return a
 
 
+# ---- the tiled packed layout, written from its definition in include/fp4q.h:
+# codes in 1 KB blocks per (16-row group, 128-column step), the 16 bytes of
+# row r and step chunk c at (c*16 + r)*16; scales in blocks per (64-row
+# group, step), NVFP4 byte 4d + e of a row's step at (d*64 + r)*4 + e,
+# MXFP4 byte e at r*4 + e.  Rows are padded to 16 (codes) and 64 (scales).
+
+def _pad_rows(a: np.ndarray, mult: int) -> np.ndarray:
+    rows = a.shape[0]
+    rp = -(-rows // mult) * mult
+    out = np.zeros((rp,) + a.shape[1:], a.dtype)
+    out[:rows] = a
+    return out
+
+
+def tile_codes(q: np.ndarray) -> np.ndarray:
+    """Row-major codes [rows, K/2] -> tiled byte buffer."""
+    rows, kh = q.shape
+    assert kh % 64 == 0
+    p = _pad_rows(q, 16)
+    t = p.reshape(p.shape[0] // 16, 16, kh // 64, 4, 16)      # [G, r, k, c, byte]
+    return np.ascontiguousarray(t.transpose(0, 2, 3, 1, 4)).reshape(-1)
+
+
+def untile_codes(buf: np.ndarray, rows: int, K: int) -> np.ndarray:
+    rp = -(-rows // 16) * 16
+    t = buf[:rp * K // 2].reshape(rp // 16, K // 128, 4, 16, 16)  # [G, k, c, r, byte]
+    return np.ascontiguousarray(t.transpose(0, 3, 1, 2, 4)).reshape(rp, K // 2)[:rows]
+
+
+def tile_scales(s: np.ndarray, fmt: int) -> np.ndarray:
+    """Row-major block scales [rows, K/blk] -> tiled byte buffer."""
+    rows, ks = s.shape
+    p = _pad_rows(s, 64)
+    H = p.shape[0] // 64
+    if fmt == 0:
+        t = p.reshape(H, 64, ks // 8, 2, 4).transpose(0, 2, 3, 1, 4)   # [H, k, d, r, e]
+    else:
+        t = p.reshape(H, 64, ks // 4, 4).transpose(0, 2, 1, 3)         # [H, k, r, e]
+    return np.ascontiguousarray(t).reshape(-1)
+
+
+def untile_scales(buf: np.ndarray, rows: int, K: int, fmt: int) -> np.ndarray:
+    rp = -(-rows // 64) * 64
+    H = rp // 64
+    if fmt == 0:
+        t = buf[:rp * K // 16].reshape(H, K // 128, 2, 64, 4).transpose(0, 3, 1, 2, 4)
+        return np.ascontiguousarray(t).reshape(rp, K // 16)[:rows]
+    t = buf[:rp * K // 32].reshape(H, K // 128, 64, 4).transpose(0, 2, 1, 3)
+    return np.ascontiguousarray(t).reshape(rp, K // 32)[:rows]
+
+
+def host_packed(gpu: dict, fmt: int):
+    """(codes, scales) of a quantize() result as row-major host arrays."""
+    q, s = to_host(gpu["q"]), to_host(gpu["scales"])
+    if gpu.get("layout", 0) == 1:
+        rows, K = gpu["rows"], gpu["cols"]
+        return untile_codes(q, rows, K), untile_scales(s, rows, K, fmt)
+    return q, s
+
+
 def assert_quant_equal(gpu: dict, ref: dict, fmt: int):
-    for k in ("q", "scales"):
-        g, r = to_host(gpu[k]), ref[k]
+    hq, hs = host_packed(gpu, fmt)
+    for k, g in (("q", hq), ("scales", hs)):
+        r = ref[k]
+        assert g.shape == r.shape, (k, g.shape, r.shape)
         bad = np.argwhere(g != r)
         assert bad.size == 0, f"{k}: {len(bad)} mismatches, first {bad[:3].tolist()}"
     if fmt == 0:
@@ -65,11 +127,17 @@ def oracle_quant(orc, fmt, x, chan=None, offsets=None):
     return orc.quantize(fmt, x, offsets=offsets, chan_idx=chan)
 
 
-def dev_quant(ref: dict, device="cuda:0"):
-    """Upload an oracle-quantized tensor set for the GEMM."""
-    out = {"q": to_dev(ref["q"], device), "scales": to_dev(ref["scales"], device),
+def dev_quant(ref: dict, device="cuda:0", layout=0, fmt=None):
+    """Upload an oracle-quantized tensor set for the GEMM (tiled on the host
+    when layout == 1; fmt is then needed for the scale arrangement)."""
+    q, s = ref["q"], ref["scales"]
+    rows, K = q.shape[0], q.shape[1] * 2
+    if layout == 1:
+        q, s = tile_codes(q), tile_scales(s, fmt)
+    out = {"q": to_dev(q, device), "scales": to_dev(s, device),
            "tscale": None if ref["tscale"] is None else to_dev(ref["tscale"], device),
-           "resid": None if ref["resid"] is None else to_dev(ref["resid"], device)}
+           "resid": None if ref["resid"] is None else to_dev(ref["resid"], device),
+           "layout": layout, "rows": rows, "cols": K}
     return out
 
 

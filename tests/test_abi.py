@@ -52,8 +52,9 @@ B = ctypes.c_void_p(0x20000)
 
 
 def q(L, fmt=0, x=A, rows=4, cols=64, ldx=64, off=None, G=1, chan=None, nS=0, qq=B, sc=B,
-      ts=B, R=None, ws=A, wsb=64):
-    return L.fp4q_quantize(fmt, x, rows, cols, ldx, off, G, chan, nS, qq, sc, ts, R, ws, wsb, None)
+      ts=B, R=None, ws=A, wsb=64, layout=0):
+    return L.fp4q_quantize(fmt, layout, x, rows, cols, ldx, off, G, chan, nS, qq, sc, ts, R, ws,
+                           wsb, None)
 
 
 def test_quantize_rejects(L):
@@ -75,11 +76,16 @@ def test_quantize_rejects(L):
     assert q(L, ws=None) == WORKSPACE
     assert q(L, wsb=2) == WORKSPACE
     assert q(L, rows=1 << 28) == UNSUPPORTED     # 2^31 chunks of 8 elements
+    assert q(L, layout=2) == INVALID
+    assert q(L, layout=1, cols=64) == INVALID    # tiled needs cols % 128
+    assert q(L, layout=1, cols=128, ldx=128, sc=ctypes.c_void_p(0x20002)) == INVALID
+    assert q(L, sc=ctypes.c_void_p(0x20002)) == INVALID  # scales 4-byte aligned
 
 
 def g(L, fmt=0, M=4, N=8, K=256, aq=A, as_=A, ats=B, bq=B, bs=B, bts=B, chan=None, nS=0, R=None,
-      y=A, dt=0, ldy=8):
-    return L.fp4q_gemm(fmt, M, N, K, aq, as_, ats, bq, bs, bts, chan, nS, R, y, dt, ldy, None)
+      y=A, dt=0, ldy=8, layout=0):
+    return L.fp4q_gemm(fmt, layout, M, N, K, aq, as_, ats, bq, bs, bts, chan, nS, R, y, dt, ldy,
+                       None)
 
 
 def test_gemm_rejects(L):
@@ -94,6 +100,30 @@ def test_gemm_rejects(L):
     assert g(L, nS=300, chan=A, R=B) == INVALID
     assert g(L, aq=ctypes.c_void_p(0x10004)) == INVALID
     assert g(L, y=None) == INVALID
+    assert g(L, layout=5) == INVALID
+    assert g(L, layout=1, K=144) == UNSUPPORTED
+
+
+def _packed(L, fmt, layout, rows, cols):
+    cb, sb = ctypes.c_size_t(7), ctypes.c_size_t(7)
+    rc = L.fp4q_packed_bytes(fmt, layout, rows, cols, ctypes.byref(cb), ctypes.byref(sb))
+    return rc, cb.value, sb.value
+
+
+def test_packed_bytes(L):
+    # row-major: exact sizes
+    assert _packed(L, 0, 0, 5, 64) == (0, 160, 20)
+    assert _packed(L, 1, 0, 5, 64) == (0, 160, 10)
+    # tiled: codes padded to 16 rows, scales to 64 rows
+    assert _packed(L, 0, 1, 5, 256) == (0, 16 * 128, 64 * 16)
+    assert _packed(L, 1, 1, 5, 256) == (0, 16 * 128, 64 * 8)
+    assert _packed(L, 0, 1, 64, 128) == (0, 64 * 64, 64 * 8)
+    assert _packed(L, 0, 1, 65, 128) == (0, 80 * 64, 128 * 8)
+    assert _packed(L, 0, 1, 0, 128) == (0, 0, 0)
+    assert _packed(L, 0, 1, 5, 64)[0] == INVALID     # tiled needs cols % 128
+    assert _packed(L, 1, 0, 5, 48)[0] == INVALID     # MXFP4 needs cols % 32
+    assert _packed(L, 0, 3, 5, 128)[0] == INVALID
+    assert _packed(L, 0, 0, -1, 128)[0] == INVALID
 
 
 def test_grouped_gemm_rejects(L):

@@ -19,8 +19,8 @@ def _prep(orc, fmt, d, chan):
     return qa, qb
 
 
-def _gpu_gemm(fmt, qa, qb, chan, y_dtype=0):
-    a, b = dev_quant(qa), dev_quant(qb)
+def _gpu_gemm(fmt, qa, qb, chan, y_dtype=0, layout=fq.ROWMAJOR):
+    a, b = dev_quant(qa, layout=layout, fmt=fmt), dev_quant(qb, layout=layout, fmt=fmt)
     y = fq.gemm(fmt, a, b, chan_idx=None if chan is None else to_dev(chan), y_dtype=y_dtype)
     torch.cuda.synchronize()
     return y
@@ -40,32 +40,42 @@ def _oracle_points(orc, fmt, qa, qb, chan, pm, pn):
                            qa["resid"], pm, pn)
 
 
+_PREP = {}
+
+
+def _prep_cached(orc, fmt, name):
+    """Oracle quantization of a named workload, shared by the layout variants."""
+    key = (name, fmt)
+    if key not in _PREP:
+        d = workload(name)
+        _PREP[key] = (d["chan_idx"],) + _prep(orc, fmt, d, d["chan_idx"])
+    return _PREP[key]
+
+
+@pytest.mark.parametrize("layout", [fq.ROWMAJOR, fq.TILED])
 @pytest.mark.parametrize("name,fmt", [("tiny_nvfp4", 0), ("tiny_nvfp4", 1),
                                       ("decode_nvfp4", 0), ("decode_nvfp4", 1)])
-def test_workload_all_outputs(orc, name, fmt):
+def test_workload_all_outputs(orc, name, fmt, layout):
     need_gpu()
-    say(f"gemm all outputs {name} fmt {fmt}")
-    d = workload(name)
-    chan = d["chan_idx"]
-    qa, qb = _prep(orc, fmt, d, chan)
-    y = to_host(_gpu_gemm(fmt, qa, qb, chan))
+    say(f"gemm all outputs {name} fmt {fmt} layout {layout}")
+    chan, qa, qb = _prep_cached(orc, fmt, name)
+    y = to_host(_gpu_gemm(fmt, qa, qb, chan, layout=layout))
     yo, ya = _oracle_full(orc, fmt, qa, qb, chan)
     r = assert_gemm_close(y, yo, ya)
     say(f"  worst |dY|/Yabs = {r:.3e}")
 
 
+@pytest.mark.parametrize("layout", [fq.ROWMAJOR, fq.TILED])
 @pytest.mark.parametrize("name", ["prefill_nvfp4", "prefill_mxfp4"])
-def test_prefill_sampled(orc, name):
+def test_prefill_sampled(orc, name, layout):
     """Full prefill shape (8192 x 4096 x 14336) in the benchmark's launch
     configuration; 40000 sampled outputs plus two full rows and columns."""
     need_gpu()
-    say(f"gemm sampled {name}")
+    say(f"gemm sampled {name} layout {layout}")
     cfg = CONFIGS[name]
     fmt = 0 if cfg["fmt"] == "nvfp4" else 1
-    d = workload(name)
-    chan = d["chan_idx"]
-    qa, qb = _prep(orc, fmt, d, chan)
-    y = to_host(_gpu_gemm(fmt, qa, qb, chan))
+    chan, qa, qb = _prep_cached(orc, fmt, name)
+    y = to_host(_gpu_gemm(fmt, qa, qb, chan, layout=layout))
     M, N = y.shape
     rng = np.random.default_rng(123)
     pm = np.concatenate([rng.integers(0, M, 40000), np.full(N, M - 1), np.arange(M)])
@@ -87,9 +97,10 @@ def test_ragged(orc, fmt, M, N, K, nS):
     chan = np.sort(np.random.default_rng(M).choice(K, nS, replace=False)).astype(np.int32)
     chan = chan if nS else None
     qa, qb = _prep(orc, fmt, d, chan)
-    y = to_host(_gpu_gemm(fmt, qa, qb, chan))
     yo, ya = _oracle_full(orc, fmt, qa, qb, chan)
-    assert_gemm_close(y, yo, ya)
+    for layout in (fq.ROWMAJOR, fq.TILED):
+        y = to_host(_gpu_gemm(fmt, qa, qb, chan, layout=layout))
+        assert_gemm_close(y, yo, ya)
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
@@ -104,9 +115,10 @@ def test_large_tiles_ragged(orc, fmt, M, N, K, nS):
     chan = np.sort(np.random.default_rng(N).choice(K, nS, replace=False)).astype(np.int32)
     chan = chan if nS else None
     qa, qb = _prep(orc, fmt, d, chan)
-    y = to_host(_gpu_gemm(fmt, qa, qb, chan))
     yo, ya = _oracle_full(orc, fmt, qa, qb, chan)
-    assert_gemm_close(y, yo, ya)
+    for layout in (fq.ROWMAJOR, fq.TILED):
+        y = to_host(_gpu_gemm(fmt, qa, qb, chan, layout=layout))
+        assert_gemm_close(y, yo, ya)
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
@@ -118,8 +130,8 @@ def test_bf16_output_and_ldy(orc, fmt):
     qa, qb = _prep(orc, fmt, d, chan)
     a, b = dev_quant(qa), dev_quant(qb)
     ybig = torch.full((96, 128), 7.0, dtype=torch.float32, device="cuda:0")
-    fq.gemm_into(fmt, 96, 80, 256, a["q"], a["scales"], a["tscale"], b["q"], b["scales"],
-                 b["tscale"], to_dev(chan), 4, a["resid"], ybig, 0, 128)
+    fq.gemm_into(fmt, fq.ROWMAJOR, 96, 80, 256, a["q"], a["scales"], a["tscale"], b["q"],
+                 b["scales"], b["tscale"], to_dev(chan), 4, a["resid"], ybig, 0, 128)
     yb = fq.gemm(fmt, a, b, chan_idx=to_dev(chan), y_dtype=1)
     torch.cuda.synchronize()
     yo, ya = _oracle_full(orc, fmt, qa, qb, chan)
@@ -141,16 +153,17 @@ def test_deterministic(orc):
     assert torch.equal(y1, y2)
 
 
-def test_end_to_end_gpu_quantize_then_gemm(orc):
+@pytest.mark.parametrize("layout", [fq.ROWMAJOR, fq.TILED])
+def test_end_to_end_gpu_quantize_then_gemm(orc, layout):
     """GPU quantize feeding the GPU GEMM, against oracle quantize + oracle GEMM."""
     need_gpu()
-    say("end-to-end decode workload on the GPU path")
+    say(f"end-to-end decode workload on the GPU path, layout {layout}")
     d = workload("decode_nvfp4")
     chan = d["chan_idx"]
-    a = fq.quantize(0, to_dev(d["x"]), chan_idx=to_dev(chan))
-    b = fq.quantize(0, to_dev(d["wt"]))
+    a = fq.quantize(0, to_dev(d["x"]), chan_idx=to_dev(chan), layout=layout)
+    b = fq.quantize(0, to_dev(d["wt"]), layout=layout)
     y = to_host(fq.gemm(0, a, b, chan_idx=to_dev(chan)))
-    qa, qb = _prep(orc, 0, d, chan)
+    _, qa, qb = _prep_cached(orc, 0, "decode_nvfp4")
     rng = np.random.default_rng(4)
     pm, pn = rng.integers(0, 64, 20000), rng.integers(0, y.shape[1], 20000)
     yo, ya = _oracle_points(orc, 0, qa, qb, chan, pm, pn)

@@ -16,11 +16,11 @@ from workloads import dense_case
 pytestmark = pytest.mark.gpu
 
 
-def _bufs(fmt, rows, K, nS, G, dev):
-    blk = fq.BLOCK[fmt]
+def _bufs(fmt, rows, K, nS, G, dev, layout=fq.ROWMAJOR):
+    cb, sb = fq.packed_bytes(fmt, layout, rows, K)
     return dict(
-        q=torch.empty((rows, K // 2), dtype=torch.uint8, device=dev),
-        s=torch.empty((rows, K // blk), dtype=torch.uint8, device=dev),
+        q=torch.empty(cb, dtype=torch.uint8, device=dev),
+        s=torch.empty(sb, dtype=torch.uint8, device=dev),
         t=torch.empty(G, dtype=torch.float32, device=dev) if fmt == fq.NVFP4 else None,
         r=torch.empty((rows, nS), dtype=torch.int16, device=dev) if nS else None,
         ws=torch.empty(max(fq.quantize_workspace_bytes(fmt, rows, K, G), 16), dtype=torch.uint8,
@@ -48,22 +48,24 @@ def _check_replays(run, outputs, scramble):
         torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("layout", [fq.ROWMAJOR, fq.TILED])
 @pytest.mark.parametrize("fmt", [0, 1])
-def test_graph_decode_step(fmt):
+def test_graph_decode_step(fmt, layout):
     dev = need_gpu()
-    say(f"graph replay: decode quantize + gemm, fmt {fmt}")
+    say(f"graph replay: decode quantize + gemm, fmt {fmt} layout {layout}")
     d = workload("decode_nvfp4")
     M, K = d["x"].shape
     N = d["wt"].shape[0]
     nS = d["chan_idx"].size
     x, chan = to_dev(d["x"]), to_dev(d["chan_idx"])
-    w = fq.quantize(fmt, to_dev(d["wt"]))
-    b = _bufs(fmt, M, K, nS, 1, dev)
+    w = fq.quantize(fmt, to_dev(d["wt"]), layout=layout)
+    b = _bufs(fmt, M, K, nS, 1, dev, layout)
     y = torch.empty((M, N), dtype=torch.float32, device=dev)
 
     def run():
-        fq.quantize_into(fmt, x, None, 1, chan, nS, b["q"], b["s"], b["t"], b["r"], b["ws"])
-        fq.gemm_into(fmt, M, N, K, b["q"], b["s"], b["t"], w["q"], w["scales"], w["tscale"], chan,
+        fq.quantize_into(fmt, layout, x, None, 1, chan, nS, b["q"], b["s"], b["t"], b["r"],
+                         b["ws"])
+        fq.gemm_into(fmt, layout, M, N, K, b["q"], b["s"], b["t"], w["q"], w["scales"], w["tscale"], chan,
                      nS, b["r"], y, 0, N)
 
     def outputs():
@@ -97,7 +99,8 @@ def test_graph_grouped_layer():
     y = torch.empty((rows, N), dtype=torch.float32, device=dev)
 
     def run():
-        fq.quantize_into(fmt, x, off, G, chan, nS, b["q"], b["s"], b["t"], b["r"], b["ws"])
+        fq.quantize_into(fmt, fq.ROWMAJOR, x, off, G, chan, nS, b["q"], b["s"], b["t"], b["r"],
+                         b["ws"])
         fq.grouped_gemm_into(fmt, rows, N, K, off, G, b["q"], b["s"], b["t"], bq, bs, bt, chan, nS,
                              b["r"], y, 0)
 

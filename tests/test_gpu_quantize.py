@@ -6,35 +6,46 @@ import pytest
 import torch
 
 import fp4_w4a4_quantized_amd as fq
-from gpu_helpers import workload, assert_quant_equal, need_gpu, say, to_dev
+from gpu_helpers import workload, assert_quant_equal, need_gpu, say, to_dev, to_host
 from workloads import CONFIGS, bf16_bits, dense_case, moe_case
 
 pytestmark = pytest.mark.gpu
 
 
-def _run(orc, fmt, x, chan=None, offsets=None):
+_REF = {}
+
+
+def _run(orc, fmt, x, chan=None, offsets=None, layout=fq.ROWMAJOR, key=None):
     dev = need_gpu()
-    ref = orc.quantize(fmt, x, offsets=offsets, chan_idx=chan)
+    if key is None or key not in _REF:
+        ref = orc.quantize(fmt, x, offsets=offsets, chan_idx=chan)
+        if key is not None:
+            _REF[key] = ref
+    ref = _REF[key] if key is not None else ref
     got = fq.quantize(fmt, to_dev(x), group_offsets=None if offsets is None else to_dev(offsets),
-                      chan_idx=None if chan is None else to_dev(np.ascontiguousarray(chan)))
+                      chan_idx=None if chan is None else to_dev(np.ascontiguousarray(chan)),
+                      layout=layout)
     torch.cuda.synchronize(dev)
     assert_quant_equal(got, ref, fmt)
 
 
+@pytest.mark.parametrize("layout", [fq.ROWMAJOR, fq.TILED])
 @pytest.mark.parametrize("name", ["tiny_nvfp4", "decode_nvfp4", "prefill_nvfp4", "prefill_mxfp4"])
-def test_workload_activations(orc, name):
+def test_workload_activations(orc, name, layout):
     cfg = CONFIGS[name]
-    say(f"quantize activations {name}")
+    say(f"quantize activations {name} layout {layout}")
     d = dense_case(**{**cfg, "N": 8})   # weights are not needed here
-    _run(orc, 0 if cfg["fmt"] == "nvfp4" else 1, d["x"], d["chan_idx"])
+    _run(orc, 0 if cfg["fmt"] == "nvfp4" else 1, d["x"], d["chan_idx"], layout=layout,
+         key=("act", name))
 
 
+@pytest.mark.parametrize("layout", [fq.ROWMAJOR, fq.TILED])
 @pytest.mark.parametrize("name", ["tiny_nvfp4", "decode_nvfp4"])
 @pytest.mark.parametrize("fmt", [0, 1])
-def test_workload_weights(orc, name, fmt):
-    say(f"quantize weights {name} fmt {fmt}")
+def test_workload_weights(orc, name, fmt, layout):
+    say(f"quantize weights {name} fmt {fmt} layout {layout}")
     d = workload(name)
-    _run(orc, fmt, d["wt"])
+    _run(orc, fmt, d["wt"], layout=layout, key=("w", name, fmt))
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
@@ -48,6 +59,36 @@ def test_ragged_and_channel_counts(orc, fmt, rows, cols, nS):
     d = dense_case(rows, cols, 8, n_out=max(1, cols // 100), seed=rows * 7 + cols)
     chan = np.sort(np.random.default_rng(rows).choice(cols, nS, replace=False)).astype(np.int32)
     _run(orc, fmt, d["x"], chan if nS else None)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("rows,cols,nS", [(1, 128, 3), (17, 384, 11), (63, 256, 0),
+                                          (65, 1024, 64), (3, 17408, 40), (600, 512, 37),
+                                          (129, 2048, 64)])
+def test_tiled_ragged(orc, fmt, rows, cols, nS):
+    """Tiled packed layout: row counts off the 16- and 64-row padding, and
+    nothing written past fp4q_packed_bytes()."""
+    dev = need_gpu()
+    say(f"quantize tiled fmt {fmt} {rows}x{cols} nS {nS}")
+    d = dense_case(rows, cols, 8, n_out=max(1, cols // 100), seed=rows * 5 + cols)
+    chan = np.sort(np.random.default_rng(rows).choice(cols, nS, replace=False)).astype(np.int32)
+    ref = orc.quantize(fmt, d["x"], chan_idx=chan if nS else None)
+    cb, sb = fq.packed_bytes(fmt, fq.TILED, rows, cols)
+    tail = 512
+    q = torch.full((cb + tail,), 0xA5, dtype=torch.uint8, device=dev)
+    sc = torch.full((sb + tail,), 0x5A, dtype=torch.uint8, device=dev)
+    ts = torch.empty(1, dtype=torch.float32, device=dev) if fmt == 0 else None
+    R = torch.empty((rows, nS), dtype=torch.int16, device=dev) if nS else None
+    wsb = fq.quantize_workspace_bytes(fmt, rows, cols, 1)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    fq.quantize_into(fmt, fq.TILED, to_dev(d["x"]), None, 1, to_dev(chan) if nS else None, nS,
+                     q, sc, ts, R, ws)
+    torch.cuda.synchronize(dev)
+    qh, sh = to_host(q), to_host(sc)
+    assert np.all(qh[cb:] == 0xA5) and np.all(sh[sb:] == 0x5A), "write past the packed size"
+    got = {"q": q[:cb], "scales": sc[:sb], "tscale": ts, "resid": R, "layout": fq.TILED,
+           "rows": rows, "cols": cols}
+    assert_quant_equal(got, ref, fmt)
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
