@@ -45,6 +45,8 @@ def parse():
                             "tiny_nvfp4"])
     p.add_argument("--layout", choices=("tiled", "rowmajor"), default="tiled",
                    help="packed operand layout of the dense workloads (MoE is row-major)")
+    p.add_argument("--out-dtype", choices=("f32", "bf16"), default="f32",
+                   help="GEMM output type of the dense workloads")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle baseline sample")
@@ -143,12 +145,16 @@ def main():
         wq = fq.quantize(fmt, up(data["wt"]), layout=layout)  # offline weight quantization
         torch.cuda.synchronize()
         w_bytes = N * (K // 2) + N * (K // blk)
-        y_bytes = M * N * 4
+        y_bytes = M * N * (2 if args.out_dtype == "bf16" else 4)
         n_rot = max(1, math.ceil(1.2 * LLC_BYTES / (w_bytes + y_bytes)))
         n_rot = min(n_rot, 64)
         wcopies = [wq] + [{k: (v.clone() if isinstance(v, torch.Tensor) else v)
                            for k, v in wq.items()} for _ in range(n_rot - 1)]
-        ys = [torch.empty((M, N), dtype=torch.float32, device=dev) for _ in range(n_rot)]
+        ydt = fq.OUT_BF16 if args.out_dtype == "bf16" else fq.OUT_F32
+        ys = [torch.empty((M, N), dtype=torch.bfloat16 if ydt == fq.OUT_BF16 else torch.float32,
+                          device=dev) for _ in range(n_rot)]
+        gwsb = fq.gemm_workspace_bytes(fmt, layout, M, N, K, nS)
+        gws = torch.empty(gwsb, dtype=torch.uint8, device=dev) if gwsb else None
         G = 1
         qws = torch.empty(max(fq.quantize_workspace_bytes(fmt, M, K, 1), 16), dtype=torch.uint8,
                           device=dev)
@@ -164,7 +170,7 @@ def main():
         def gemm(i):
             w = wcopies[i % n_rot]
             fq.gemm_into(fmt, layout, M, N, K, aq, asc, ats, w["q"], w["scales"], w["tscale"],
-                         chan, nS, ar, ys[i % n_rot], 0, N)
+                         chan, nS, ar, ys[i % n_rot], ydt, N, gws)
 
         flops = 2.0 * M * N * K
         gemm_bytes = (M * K // 2 + M * K // blk + M * nS * 2 + nS * 4 + w_bytes + y_bytes +
@@ -172,7 +178,7 @@ def main():
         quant_bytes = M * K * 2 + M * K // 2 + M * K // blk + M * nS * 2 + (4 if fmt == fq.NVFP4
                                                                              else 0)
         wl = {"workload": name, "format": cfg["fmt"], "M": M, "K": K, "N": N, "n_s": nS,
-              "layout": args.layout, "weight_copies_rotated": n_rot}
+              "layout": args.layout, "out_dtype": args.out_dtype, "weight_copies_rotated": n_rot}
     else:
         # MoE layer: gate_up then down, per-expert NVFP4, grouped GEMMs
         off = up(data["offsets"])

@@ -19,6 +19,7 @@ from .binding import (  # noqa: F401
     error_decompose_workspace_bytes,
     gemm,
     gemm_into,
+    gemm_workspace_bytes,
     grouped_gemm,
     grouped_gemm_into,
     lib,

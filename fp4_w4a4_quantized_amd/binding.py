@@ -74,9 +74,11 @@ def lib():
         L.fp4q_quantize.restype = ctypes.c_int
         L.fp4q_quantize.argtypes = [ctypes.c_int, ctypes.c_int, P, i64, i64, i64, P, i32, P, i32,
                                     P, P, P, P, P, sz, P]
+        L.fp4q_gemm_workspace_bytes.restype = sz
+        L.fp4q_gemm_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, i32]
         L.fp4q_gemm.restype = ctypes.c_int
         L.fp4q_gemm.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, P, P, P, P, P, P, P,
-                                i32, P, P, ctypes.c_int, i64, P]
+                                i32, P, P, ctypes.c_int, i64, P, sz, P]
         L.fp4q_grouped_gemm.restype = ctypes.c_int
         L.fp4q_grouped_gemm.argtypes = [ctypes.c_int, i64, i64, i64, P, i32, P, P, P, P, P, P, P,
                                         i32, P, P, ctypes.c_int, P]
@@ -117,6 +119,10 @@ def quantize_workspace_bytes(fmt, rows, cols, num_groups=1) -> int:
     return lib().fp4q_quantize_workspace_bytes(fmt, rows, cols, num_groups)
 
 
+def gemm_workspace_bytes(fmt, layout, M, N, K, n_chan) -> int:
+    return lib().fp4q_gemm_workspace_bytes(fmt, layout, M, N, K, n_chan)
+
+
 def error_decompose_workspace_bytes(rows, cols) -> int:
     return lib().fp4q_error_decompose_workspace_bytes(rows, cols)
 
@@ -133,10 +139,11 @@ def quantize_into(fmt, layout, x, group_offsets, num_groups, chan_idx, n_chan, q
 
 
 def gemm_into(fmt, layout, M, N, K, a_q, a_s, a_ts, b_q, b_s, b_ts, chan_idx, n_chan, resid, y,
-              y_dtype=OUT_F32, ldy=None, stream=None):
+              y_dtype=OUT_F32, ldy=None, workspace=None, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = lib().fp4q_gemm(fmt, layout, M, N, K, _ptr(a_q), _ptr(a_s), _ptr(a_ts), _ptr(b_q), _ptr(b_s),
                          _ptr(b_ts), _ptr(chan_idx), n_chan, _ptr(resid), _ptr(y), y_dtype,
-                         N if ldy is None else ldy, _stream(stream))
+                         N if ldy is None else ldy, _ptr(workspace), ws_bytes, _stream(stream))
     _check("fp4q_gemm", rc)
 
 
@@ -202,10 +209,13 @@ def gemm(fmt, a, b, chan_idx=None, y_dtype=OUT_F32, stream=None):
     if Kb != K or layout_b != layout:
         raise ValueError("operands differ in K or layout")
     nS = 0 if chan_idx is None else chan_idx.numel()
+    dev = a["q"].device
     y = torch.empty((M, N), dtype=torch.float32 if y_dtype == OUT_F32 else torch.bfloat16,
-                    device=a["q"].device)
-    gemm_into(fmt, layout, M, N, K, a["q"], a["scales"], a["tscale"], b["q"], b["scales"], b["tscale"],
-              chan_idx, nS, a["resid"] if nS else None, y, y_dtype, N, stream)
+                    device=dev)
+    wsb = gemm_workspace_bytes(fmt, layout, M, N, K, nS)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
+    gemm_into(fmt, layout, M, N, K, a["q"], a["scales"], a["tscale"], b["q"], b["scales"],
+              b["tscale"], chan_idx, nS, a["resid"] if nS else None, y, y_dtype, N, ws, stream)
     return y
 
 

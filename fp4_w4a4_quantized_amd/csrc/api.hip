@@ -120,6 +120,7 @@ static int validate_gemm_common(int fmt, int64_t N, int64_t K, const uint8_t* a_
   if (n_chan < 0 || n_chan > K) return FP4Q_ERR_INVALID;
   if ((n_chan > 0) != (chan_idx != nullptr) || (n_chan > 0) != (resid != nullptr))
     return FP4Q_ERR_INVALID;
+  if (n_chan > 0 && !aligned(resid, 16)) return FP4Q_ERR_INVALID;
   if (fmt == FP4Q_NVFP4 && (!a_ts || !b_ts)) return FP4Q_ERR_INVALID;
   if (fmt == FP4Q_MXFP4 && (a_ts || b_ts)) return FP4Q_ERR_INVALID;
   if (rows > 0 && N > 0) {
@@ -131,20 +132,32 @@ static int validate_gemm_common(int fmt, int64_t N, int64_t K, const uint8_t* a_
   return FP4Q_OK;
 }
 
+size_t fp4q_gemm_workspace_bytes(fp4q_format_t fmt, fp4q_layout_t layout, int64_t M, int64_t N,
+                                 int64_t K, int32_t n_chan) {
+  (void)fmt;
+  (void)layout;
+  if (M <= 0 || N <= 0 || K <= 0 || n_chan <= 0) return 0;
+  return fp4q::gemm_workspace_bytes(M, N, K, n_chan);
+}
+
 int fp4q_gemm(fp4q_format_t fmt, fp4q_layout_t layout, int64_t M, int64_t N, int64_t K,
               const uint8_t* a_q, const uint8_t* a_s, const float* a_ts, const uint8_t* b_q,
               const uint8_t* b_s, const float* b_ts, const int32_t* chan_idx, int32_t n_chan,
-              const uint16_t* resid, void* y, fp4q_dtype_t y_dtype, int64_t ldy, void* stream) {
+              const uint16_t* resid, void* y, fp4q_dtype_t y_dtype, int64_t ldy, void* workspace,
+              size_t workspace_bytes, void* stream) {
   if (!layout_ok(layout)) return FP4Q_ERR_INVALID;
   int rc = validate_gemm_common(fmt, N, K, a_q, a_s, a_ts, b_q, b_s, b_ts, chan_idx, n_chan,
                                 resid, y, y_dtype, M);
   if (rc != FP4Q_OK) return rc;
   if (ldy < N) return FP4Q_ERR_INVALID;
   if ((M + 127) / 128 > (int64_t)UINT32_MAX || (N + 31) / 32 > 65535) return FP4Q_ERR_UNSUPPORTED;
+  const size_t need = fp4q_gemm_workspace_bytes(fmt, layout, M, N, K, n_chan);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
+    return FP4Q_ERR_WORKSPACE;
   clear_error();
   fp4q::launch_gemm(fmt, layout == FP4Q_LAYOUT_TILED, M, N, K, nullptr, 1, a_q, a_s, a_ts, b_q,
                     b_s, b_ts, chan_idx, n_chan, resid, y, y_dtype == FP4Q_OUT_BF16, ldy,
-                    static_cast<hipStream_t>(stream));
+                    workspace, static_cast<hipStream_t>(stream));
   return check_launch();
 }
 
@@ -162,7 +175,7 @@ int fp4q_grouped_gemm(fp4q_format_t fmt, int64_t total_rows, int64_t N, int64_t 
   if ((N + 127) / 128 > 65535) return FP4Q_ERR_UNSUPPORTED;
   clear_error();
   fp4q::launch_gemm(fmt, false, total_rows, N, K, group_offsets, num_groups, a_q, a_s, a_ts, b_q,
-                    b_s, b_ts, chan_idx, n_chan, resid, y, y_dtype == FP4Q_OUT_BF16, N,
+                    b_s, b_ts, chan_idx, n_chan, resid, y, y_dtype == FP4Q_OUT_BF16, N, nullptr,
                     static_cast<hipStream_t>(stream));
   return check_launch();
 }

@@ -17,18 +17,26 @@ int launch_quantize(int fmt, bool tiled, const uint16_t* x, int64_t rows, int64_
 
 size_t quantize_workspace_bytes(int fmt, int G);
 
+// Dense GEMM kernel choice (a function of the shape only, so that the
+// workspace query and the launch agree).
+enum GemmPath { PATH_GENERIC = 0, PATH_SKINNY = 1, PATH_BIG = 2 };
+GemmPath gemm_path(int64_t M, int64_t N, int64_t K, int nS);
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int nS);
+
 int launch_gemm(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const int32_t* off, int G,
                 const uint8_t* aq, const uint8_t* as, const float* ats, const uint8_t* bq,
                 const uint8_t* bs, const float* bts, const int32_t* chan, int nS,
-                const uint16_t* resid, void* y, int y_bf16, int64_t ldy, hipStream_t stream);
+                const uint16_t* resid, void* y, int y_bf16, int64_t ldy, void* ws,
+                hipStream_t stream);
 
-bool big_gemm_eligible(int64_t M, int64_t N, int64_t K, int nS, const void* resid);
+bool big_gemm_eligible(int64_t M, int64_t N, int64_t K, int nS);
+size_t big_gemm_workspace_bytes(int64_t N, int nS);
 int launch_gemm_big(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const uint8_t* aq,
                     const uint8_t* as, const float* ats, const uint8_t* bq, const uint8_t* bs,
                     const float* bts, const int32_t* chan, int nS, const uint16_t* resid,
-                    void* y, int y_bf16, int64_t ldy, hipStream_t stream);
+                    void* y, int y_bf16, int64_t ldy, void* ws, hipStream_t stream);
 
-bool skinny_gemm_eligible(int64_t M, int64_t N, int64_t K, int nS, const void* resid);
+bool skinny_gemm_eligible(int64_t M, int64_t N, int64_t K, int nS);
 int launch_gemm_skinny(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const uint8_t* aq,
                        const uint8_t* as, const float* ats, const uint8_t* bq, const uint8_t* bs,
                        const float* bts, const int32_t* chan, int nS, const uint16_t* resid,

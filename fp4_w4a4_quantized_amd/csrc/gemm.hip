@@ -377,32 +377,49 @@ static void launch_one(const GemmArgs& a, unsigned mtiles, hipStream_t stream) {
   hipLaunchKernelGGL((k_gemm<FMT, BM, BN, GROUPED>), grid, dim3(256), 0, stream, a);
 }
 
+GemmPath gemm_path(int64_t M, int64_t N, int64_t K, int nS) {
+  if (skinny_gemm_eligible(M, N, K, nS)) return PATH_SKINNY;
+  if (big_gemm_eligible(M, N, K, nS)) return PATH_BIG;
+  return PATH_GENERIC;
+}
+
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int nS) {
+  return gemm_path(M, N, K, nS) == PATH_BIG ? big_gemm_workspace_bytes(N, nS) : 0;
+}
+
 int launch_gemm(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const int32_t* off, int G,
                 const uint8_t* aq, const uint8_t* as, const float* ats, const uint8_t* bq,
                 const uint8_t* bs, const float* bts, const int32_t* chan, int nS,
-                const uint16_t* resid, void* y, int y_bf16, int64_t ldy, hipStream_t stream) {
+                const uint16_t* resid, void* y, int y_bf16, int64_t ldy, void* ws,
+                hipStream_t stream) {
   GemmArgs a{M, N, K, off, G, aq, as, ats, bq, bs, bts, chan, nS, resid, y, y_bf16, ldy, tiled};
   if (M == 0 || N == 0) return 0;
-  const bool grouped = (off != nullptr);
-  if (grouped) {
+  if (off != nullptr) {
     constexpr int BM = 64;
     unsigned mt = (unsigned)((M + BM - 1) / BM + G);  // each group adds at most one partial tile
     if (fmt == FP4Q_NVFP4) launch_one<FP4Q_NVFP4, BM, 128, true>(a, mt, stream);
     else launch_one<FP4Q_MXFP4, BM, 128, true>(a, mt, stream);
-  } else if (skinny_gemm_eligible(M, N, K, nS, resid)) {
-    launch_gemm_skinny(fmt, tiled, M, N, K, aq, as, ats, bq, bs, bts, chan, nS, resid, y, y_bf16, ldy,
-                       stream);
-  } else if (big_gemm_eligible(M, N, K, nS, resid)) {
-    launch_gemm_big(fmt, tiled, M, N, K, aq, as, ats, bq, bs, bts, chan, nS, resid, y, y_bf16, ldy,
-                    stream);
-  } else if (M <= 64) {
-    unsigned mt = (unsigned)((M + 63) / 64);
-    if (fmt == FP4Q_NVFP4) launch_one<FP4Q_NVFP4, 64, 32, false>(a, mt, stream);
-    else launch_one<FP4Q_MXFP4, 64, 32, false>(a, mt, stream);
-  } else {
-    unsigned mt = (unsigned)((M + 127) / 128);
-    if (fmt == FP4Q_NVFP4) launch_one<FP4Q_NVFP4, 128, 128, false>(a, mt, stream);
-    else launch_one<FP4Q_MXFP4, 128, 128, false>(a, mt, stream);
+    return 0;
+  }
+  switch (gemm_path(M, N, K, nS)) {
+    case PATH_SKINNY:
+      launch_gemm_skinny(fmt, tiled, M, N, K, aq, as, ats, bq, bs, bts, chan, nS, resid, y, y_bf16,
+                         ldy, stream);
+      break;
+    case PATH_BIG:
+      launch_gemm_big(fmt, tiled, M, N, K, aq, as, ats, bq, bs, bts, chan, nS, resid, y, y_bf16,
+                      ldy, ws, stream);
+      break;
+    default:
+      if (M <= 64) {
+        unsigned mt = (unsigned)((M + 63) / 64);
+        if (fmt == FP4Q_NVFP4) launch_one<FP4Q_NVFP4, 64, 32, false>(a, mt, stream);
+        else launch_one<FP4Q_MXFP4, 64, 32, false>(a, mt, stream);
+      } else {
+        unsigned mt = (unsigned)((M + 127) / 128);
+        if (fmt == FP4Q_NVFP4) launch_one<FP4Q_NVFP4, 128, 128, false>(a, mt, stream);
+        else launch_one<FP4Q_MXFP4, 128, 128, false>(a, mt, stream);
+      }
   }
   return 0;
 }

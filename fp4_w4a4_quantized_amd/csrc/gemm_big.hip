@@ -5,39 +5,38 @@
 // selected channels effectively BF16):
 //   Y[m,n] = sum_k A[m,k] B[n,k] + sum_j R[m,j] B[n,S_j]
 // for M, N >= 256.  Design:
-//  * 256 x 256 output tile per workgroup; the waves split it WM x 2, each
-//    owning (256/WM) x 128 outputs as FI x 8 tiles of 16x16 MFMAs.  The wave
-//    count is a template parameter (measured: two waves per SIMD with
-//    64 x 128 wave tiles keep the FP4 MFMA pipe busier than one wave per
-//    SIMD with 128 x 128).
-//  * K advances 128 per stage.  Packed FP4 tiles and block scales go from
-//    HBM straight into LDS with global_load_lds (no register staging); three
-//    LDS stages rotate.  With fragment double buffering a wave reads the
-//    next stage's operand fragments into registers while its MFMAs work on
-//    the current stage; otherwise it reads the current stage after the
-//    barrier and a second wave on the SIMD covers the wait.  One barrier
-//    per stage is the only synchronisation on the main path.
-//  * LDS layout per 16-row group and stage: 16-byte slot (chunk c, row r) at
-//    c*16 + r, one global_load_lds_dwordx4 per group, and the MFMA operand
-//    read of a wave is 64 consecutive slots (no bank conflicts).
-//  * MXFP4: v_mfma_scale_f32_16x16x128_f8f6f4; a lane's 32 K-values are one
+//  * 256 x 256 output tile per workgroup of 8 waves (two per SIMD); wave
+//    (wm, wn) owns rows 64 wm .. 64 wm + 63 and columns 128 wn .. +127 as
+//    2 x 4 blocks of 32 x 32.  The 32x32 MFMA shapes are used throughout:
+//    measured on MI355X, v_mfma_scale_f32_32x32x64_f8f6f4 keeps the matrix
+//    pipe about 97% busy even from one wave per SIMD, where the 16x16x128
+//    form reaches about 70%, and the LDS fragment reads that run beside it
+//    are slowed less.
+//  * The K loop is a sequence of stages that all look alike to the
+//    pipeline: first K/128 FP4 stages (packed codes of A and B plus block
+//    scales), then ceil(|S|/32) compensation stages (32 channels of the
+//    residual R and of the gathered compensation weights B_S, both BF16).
+//    Stages go from memory straight into LDS with global_load_lds (no
+//    register staging); three LDS buffers rotate, two stages are in flight
+//    and one barrier per stage is the only synchronisation.
+//  * LDS layout per 16-row group and stage: 16-byte slot (chunk c, row r)
+//    at (16c + r) * 16 -- the tiled operand layout itself, and for BF16
+//    stages the same arrangement of 8-channel pieces.  A 32x32 fragment read
+//    (rows 32i + (l & 31), chunk 2h + (l >> 5)) is then two contiguous
+//    512-byte halves, free of bank conflicts, for all three stage kinds.
+//  * MXFP4: v_mfma_scale_f32_32x32x64_f8f6f4; a lane's 32 K-values are one
 //    MX block and its E8M0 code comes from LDS.  NVFP4: E4M3 scales on 16
 //    elements and 6-bit products do not fit the FP4/FP8 MFMAs exactly, so
 //    each lane decodes its codes to f16 (v_cvt_scalef32_pk_f16_fp4, then
 //    v_pk_mul_f16 by the block scale, both exact) for
-//    v_mfma_f32_16x16x32_f16.
-//  * Compensation: the selected channels are sorted, so each stage holds a
-//    run of them.  A per-stage table (count, first index, and the LDS
-//    offsets of up to 4 channels) is built once per tile.  While a B stage
-//    sits in LDS, each thread (one column of the tile) reads the code and
-//    scale bytes of the stage's channels before the stage's MFMAs and
-//    decodes them to bf16 (e2m1 * block scale, exact) after, into a
-//    16-channel staging buffer (double buffered).  Each complete group of 16
-//    channels is multiplied at once with v_mfma_f32_16x16x16_bf16 against R
-//    (bf16), which global_load_lds brings into LDS well ahead of use.  MXFP4
-//    accumulates it directly; NVFP4 scales R by 1/t_x, split into a high and
-//    a low bf16 part, so that the final y = (t_x t_w) * acc equals
-//    t_w (t_x main + comp) and only MFMAs touch the accumulators.
+//    v_mfma_f32_32x32x16_f16.  The tensor scales are applied as
+//    y = t_w (t_x main + comp).
+//  * Compensation: B_S[n, j] = e2m1(B[n, S_j]) * blockscale (exact in
+//    BF16, tensor scale excluded) is gathered once per call by a small
+//    kernel into a tiled BF16 workspace, so the GEMM streams R and B_S like
+//    any other operand and multiplies them with v_mfma_f32_32x32x16_bf16.
+//  * Epilogue: each wave stages 32 x 64 pieces of its tile through LDS and
+//    writes full 16-byte vectors.
 //  * Workgroup ids are remapped so that the workgroups resident on one XCD
 //    (ids congruent mod 8) share a compact block of tiles in L2.
 // Rows past M / columns past N load a clamped valid row and are not stored.
@@ -47,22 +46,21 @@
 namespace fp4q {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef float v4f32 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x8b __attribute__((ext_vector_type(8)));
 typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2b __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8b __attribute__((ext_vector_type(8)));
+typedef float f32x4b __attribute__((ext_vector_type(4)));
 
 constexpr int GB_TILE = 256;             // rows (M) and columns (N) per workgroup
+constexpr int GB_W = 8;                  // waves per workgroup
+constexpr int GB_T = 64 * GB_W;
 constexpr int GB_GRP = 1024;             // bytes per 16-row group per stage
 constexpr int GB_DATA = 16 * GB_GRP;     // 16 KB per operand per stage
-constexpr int GB_CG = 16;                // channels per compensation group
-constexpr int GB_COMP = GB_CG * GB_TILE; // bf16 entries per staging buffer (8 KB)
-constexpr int GB_MAX_NS = 1024;          // channel list held in LDS
-constexpr int GB_MAX_NK = 256;           // stages covered by the channel table (K <= 32768)
-constexpr int GB_XB = 4;                 // channels per stage handled in the MFMA shadow
+constexpr int GB_CS = 32;                // channels per compensation stage
 constexpr int GB_GROUP_M = 4;            // tile rows per L2 group
+constexpr int GB_EP_STRIDE = 68;         // epilogue LDS row stride (floats)
 
 struct BigArgs {
   int64_t M, N, K;
@@ -72,30 +70,22 @@ struct BigArgs {
   const uint8_t* bq;
   const uint8_t* bs;
   const float* bts;
-  const int32_t* chan;
   int nS;
   const uint16_t* resid;
+  const uint8_t* bsel;  // gathered B_S, tiled BF16 (see k_gather_bsel)
   void* y;
   int y_bf16;
   int64_t ldy;
   int mt, nt;  // tile counts
+  int nk, nc;  // FP4 stages, compensation stages
 };
 
-// Wave layout: W waves as WM x 2; wave tile (256 / WM) x 128 = FI x FJ
-// fragments of 16 x 16.
-template <int W>
-struct WaveLayout {
-  static constexpr int T = 64 * W;
-  static constexpr int WM = W / 2;
-  static constexpr int FI = GB_TILE / WM / 16;
-  static constexpr int FJ = 8;
-  static constexpr int GPW = 16 / W;  // 16-row data groups per operand a wave loads per stage
-};
-
-// Byte offsets inside one LDS stage, and the direct-to-LDS loads a wave
-// issues per stage (data, then scales: NVFP4 16 dword instructions per
-// stage, MXFP4 8, spread over the waves).
-template <int FMT, int W>
+// Byte offsets inside one LDS stage and the direct-to-LDS loads a wave
+// issues per stage: 2 data groups per operand, then scales (NVFP4 16 dword
+// instructions per stage, MXFP4 8, spread over the waves).  Compensation
+// stages issue the same count (their scale-slot loads are placeholders), so
+// one vmcnt figure serves every stage.
+template <int FMT>
 struct StageLayout {
   static constexpr int SC = (FMT == FP4Q_NVFP4) ? 2048 : 1024;  // scale bytes per operand
   static constexpr int A = 0;
@@ -104,7 +94,8 @@ struct StageLayout {
   static constexpr int SB = 2 * GB_DATA + SC;
   static constexpr int BYTES = 2 * GB_DATA + 2 * SC;
   static constexpr int SCALE_INSTR = (FMT == FP4Q_NVFP4) ? 16 : 8;
-  static constexpr int LOADS = 2 * WaveLayout<W>::GPW + SCALE_INSTR / W;
+  static constexpr int SPW = SCALE_INSTR / GB_W;
+  static constexpr int LOADS = 4 + SPW;
 };
 
 // Direct-to-LDS loads (global_load_lds): lane l's bytes land at the
@@ -148,40 +139,64 @@ __device__ __forceinline__ h16x2 e4m3_h2(uint32_t code) {
 // arrives, and direct-to-LDS loads are waited for with explicit vmcnt
 // counts.  The lgkmcnt wait is the builtin (simm16 0xC07F: lgkmcnt 0,
 // vmcnt and expcnt unconstrained) so that the compiler's wait counting
-// knows the LDS reads issued before it are complete and does not wait for
-// later ones in their place.  The empty asm statements keep the compiler
-// from moving memory operations across the barrier.
+// knows the LDS reads issued before it are complete.  The scheduling
+// barriers keep the compiler from moving any instruction across, so each
+// stage's LDS reads and MFMAs stay in their own interval.
 __device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0xC07F);
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
-// Issue the direct-to-LDS loads of one K stage (this wave's share).
-// Data: 16 instructions per operand, one per 16-row group g: lane l loads
-// row 16g + l%16, 16-byte chunk l/16.  Scales: NVFP4 two dwords per row
-// stored [d][row]; MXFP4 one dword per row stored [row]; scale instruction
-// n covers operand A (first half of n) or B, 64-row chunk n % 4, and for
-// NVFP4 dword (n / 4) % 2.  This LDS arrangement is the tiled operand
+// Issue the direct-to-LDS loads of stage s (this wave's share).
+// FP4 stage: 16 instructions per operand, one per 16-row group g: lane l
+// loads row 16g + l%16, 16-byte chunk l/16.  Scales: NVFP4 two dwords per
+// row stored [d][row]; MXFP4 one dword per row stored [row]; scale
+// instruction n covers operand A (first half of n) or B, 64-row chunk n % 4,
+// and for NVFP4 dword (n / 4) % 2.  This LDS arrangement is the tiled operand
 // layout itself, so with TL each instruction reads one contiguous span (1 KB
 // of codes or 256 bytes of scales); row-major operands are gathered from
 // rows K/2 bytes apart.
-template <int FMT, int W, bool TL>
-__device__ __forceinline__ void issue_stage(const BigArgs& p, int kt, int wave, int lane,
+// Compensation stage cs: per 16-row group, R rows (channels 32cs + 8(l/16)
+// .. +7 of row 16g + l%16; a piece past |S| is re-read from the last valid
+// one and meets zero weights) and the matching 1 KB block of B_S.
+template <int FMT, bool TL>
+__device__ __forceinline__ void issue_stage(const BigArgs& p, int s, int wave, int lane,
                                             int64_t r0, int64_t c0, uint8_t* st) {
-  using SL = StageLayout<FMT, W>;
-  constexpr int GPW = WaveLayout<W>::GPW;
-  constexpr int SPW = SL::SCALE_INSTR / W;
+  using SL = StageLayout<FMT>;
   constexpr int SPS = (FMT == FP4Q_NVFP4) ? 8 : 4;  // scale bytes per row per step
+  if (s >= p.nk) {
+    const int cs = s - p.nk;
+    const int64_t gN = ((p.N + 15) >> 4) - 1;
+    int ch = GB_CS * cs + 8 * (lane >> 4);
+    ch = ch < p.nS - 8 ? ch : p.nS - 8;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int g = wave * 2 + i;
+      int64_t row = r0 + 16 * g + (lane & 15);
+      row = row < p.M ? row : p.M - 1;
+      int64_t gb = (c0 >> 4) + g;
+      gb = gb < gN ? gb : gN;
+      lds_load16(p.resid + row * p.nS + ch, st + SL::A + g * GB_GRP);
+      lds_load16(p.bsel + ((gb * p.nc + cs) << 10) + lane * 16, st + SL::B + g * GB_GRP);
+    }
+#pragma unroll
+    for (int i = 0; i < SL::SPW; ++i)  // placeholders keeping the per-stage load count
+      lds_load4(p.resid, st + SL::SA + (wave * SL::SPW + i) * 256);
+    return;
+  }
+  const int kt = s;
   if (TL) {
     // block indices are wave-uniform (16- or 64-row group, clamped to the
     // last padded group); lane l reads bytes [16 l, 16 l + 16) or [4 l, 4 l + 4)
     const int64_t KB = p.K >> 7;
     const int64_t gM = ((p.M + 15) >> 4) - 1, gN = ((p.N + 15) >> 4) - 1;
 #pragma unroll
-    for (int i = 0; i < GPW; ++i) {
-      const int g = wave * GPW + i;
+    for (int i = 0; i < 2; ++i) {
+      const int g = wave * 2 + i;
       int64_t ga = (r0 >> 4) + g, gb = (c0 >> 4) + g;
       ga = ga < gM ? ga : gM;
       gb = gb < gN ? gb : gN;
@@ -190,8 +205,8 @@ __device__ __forceinline__ void issue_stage(const BigArgs& p, int kt, int wave, 
     }
     const int64_t hM = ((p.M + 63) >> 6) - 1, hN = ((p.N + 63) >> 6) - 1;
 #pragma unroll
-    for (int i = 0; i < SPW; ++i) {
-      const int n = wave * SPW + i;
+    for (int i = 0; i < SL::SPW; ++i) {
+      const int n = wave * SL::SPW + i;
       const int c = n & 3;
       const bool isb = n >= SL::SCALE_INSTR / 2;
       int64_t h = ((isb ? c0 : r0) >> 6) + c;
@@ -211,8 +226,8 @@ __device__ __forceinline__ void issue_stage(const BigArgs& p, int kt, int wave, 
   const int64_t K2 = p.K >> 1, KS = p.K / (FMT == FP4Q_NVFP4 ? 16 : 32);
   const int64_t off = (int64_t)kt * 64 + (lane >> 4) * 16;
 #pragma unroll
-  for (int i = 0; i < GPW; ++i) {
-    const int g = wave * GPW + i;
+  for (int i = 0; i < 2; ++i) {
+    const int g = wave * 2 + i;
     int64_t ra = r0 + 16 * g + (lane & 15), rb = c0 + 16 * g + (lane & 15);
     ra = ra < p.M ? ra : p.M - 1;
     rb = rb < p.N ? rb : p.N - 1;
@@ -220,8 +235,8 @@ __device__ __forceinline__ void issue_stage(const BigArgs& p, int kt, int wave, 
     lds_load16(p.bq + rb * K2 + off, st + SL::B + g * GB_GRP);
   }
 #pragma unroll
-  for (int i = 0; i < SPW; ++i) {
-    const int n = wave * SPW + i;
+  for (int i = 0; i < SL::SPW; ++i) {
+    const int n = wave * SL::SPW + i;
     const int c = n & 3;
     const bool isb = n >= SL::SCALE_INSTR / 2;
     int64_t row = (isb ? c0 : r0) + 64 * c + lane;
@@ -238,194 +253,131 @@ __device__ __forceinline__ void issue_stage(const BigArgs& p, int kt, int wave, 
   }
 }
 
-// One stage's operands for one wave, in registers.  Lane (lr, q) holds for
-// row fragment i (rows wm*16*FI + 16i + lr) and column fragment j (columns
-// wn*128 + 16j + lr) the 16 bytes of K chunk q (elements 32q .. 32q+31) and
-// the scale word holding the scales of those 32 elements (MXFP4: byte q;
-// NVFP4: bytes 2(q%2) and 2(q%2)+1 of dword q/2 -- blocks 2q and 2q+1).  The
-// words are kept raw and shifted where they are used, so reading the next
-// stage never forces a wait before the current stage's MFMAs.
-template <int FI, int FJ>
+// One stage's operands for one wave, in registers.  Lane l holds, for row
+// block i (rows 64 wm + 32 i + (l & 31)) and column block j (columns
+// 128 wn + 32 j + (l & 31)), K half h: the 16 bytes of chunk 2h + (l >> 5)
+// (FP4: 32 codes, elements 64h + 32(l >> 5) .. +31 of the stage; BF16: 8
+// channels).  Scales: MXFP4 the row's dword (byte 2h + (l >> 5) is the
+// block of that chunk); NVFP4 the row's dword h (bytes 2(l >> 5) and
+// 2(l >> 5) + 1 scale the chunk's two 16-element blocks).  The words are
+// kept raw and shifted where they are used.
 struct Frag {
-  u32x4 a[FI];
-  u32x4 b[FJ];
-  uint32_t sa[FI];
-  uint32_t sb[FJ];
+  u32x4 a[2][2];
+  u32x4 b[4][2];
+  uint32_t sa[2][2];
+  uint32_t sb[4][2];
 };
 
-template <int FMT, int W, int FI, int FJ>
-__device__ __forceinline__ void read_frags(const uint8_t* st, int wm, int wn, int lane,
-                                           Frag<FI, FJ>& f) {
-  using SL = StageLayout<FMT, W>;
-  const int q = lane >> 4, lr = lane & 15;
+template <int FMT, bool SCALES>
+__device__ __forceinline__ void read_frags(const uint8_t* st, int wm, int wn, int lane, Frag& f) {
+  using SL = StageLayout<FMT>;
+  const uint32_t l32 =
+      (uint32_t)((((lane >> 4) & 1) * GB_GRP) + ((lane >> 5) * 16 + (lane & 15)) * 16);
 #pragma unroll
-  for (int i = 0; i < FI; ++i) {
-    f.a[i] = *reinterpret_cast<const u32x4*>(st + SL::A + (wm * FI + i) * GB_GRP + lane * 16);
-    const int row = wm * 16 * FI + i * 16 + lr;
-    f.sa[i] = (FMT == FP4Q_MXFP4)
-                  ? *reinterpret_cast<const uint32_t*>(st + SL::SA + row * 4)
-                  : *reinterpret_cast<const uint32_t*>(st + SL::SA + ((q >> 1) * 256 + row) * 4);
-  }
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-  for (int j = 0; j < FJ; ++j) {
-    f.b[j] = *reinterpret_cast<const u32x4*>(st + SL::B + (wn * FJ + j) * GB_GRP + lane * 16);
-    const int col = wn * 16 * FJ + j * 16 + lr;
-    f.sb[j] = (FMT == FP4Q_MXFP4)
-                  ? *reinterpret_cast<const uint32_t*>(st + SL::SB + col * 4)
-                  : *reinterpret_cast<const uint32_t*>(st + SL::SB + ((q >> 1) * 256 + col) * 4);
-  }
-}
-
-// Multiply one stage held in registers into the FI x FJ accumulator tiles.
-template <int FMT, int FI, int FJ>
-__device__ __forceinline__ void compute_frags(v4f32 (&acc)[FI][FJ], const Frag<FI, FJ>& f,
-                                              int lane) {
-  const int q = lane >> 4;
-  if (FMT == FP4Q_MXFP4) {
-    int sa[FI];
+    for (int h = 0; h < 2; ++h)
+      f.a[i][h] = *reinterpret_cast<const u32x4*>(st + SL::A + (wm * 4 + 2 * i) * GB_GRP + l32 +
+                                                  h * 512);
 #pragma unroll
-    for (int i = 0; i < FI; ++i) sa[i] = (int)(f.sa[i] >> (8 * q));
+  for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int j = 0; j < FJ; ++j) {
-      const i32x8b bv = {(int)f.b[j].x, (int)f.b[j].y, (int)f.b[j].z, (int)f.b[j].w, 0, 0, 0, 0};
-      const int sb = (int)(f.sb[j] >> (8 * q));
+    for (int h = 0; h < 2; ++h)
+      f.b[j][h] = *reinterpret_cast<const u32x4*>(st + SL::B + (wn * 8 + 2 * j) * GB_GRP + l32 +
+                                                  h * 512);
+  if (!SCALES) return;
 #pragma unroll
-      for (int i = 0; i < FI; ++i) {
-        const i32x8b av = {(int)f.a[i].x, (int)f.a[i].y, (int)f.a[i].z, (int)f.a[i].w, 0, 0, 0, 0};
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[i][j], 4, 4, 0,
-                                                                     sa[i], 0, sb);
-      }
-    }
-  } else {
-    const int sh = 16 * (q & 1);
-    // sub-step s: lane q holds elements 32q + 8s .. +7 (block 2q + s/2)
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      h16x8 da[FI];
-#pragma unroll
-      for (int i = 0; i < FI; ++i)
-        da[i] = nv_decode8(f.a[i][s], e4m3_h2(f.sa[i] >> (sh + 8 * (s >> 1))));
-#pragma unroll
-      for (int j = 0; j < FJ; ++j) {
-        const h16x8 db = nv_decode8(f.b[j][s], e4m3_h2(f.sb[j] >> (sh + 8 * (s >> 1))));
-#pragma unroll
-        for (int i = 0; i < FI; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(da[i], db, acc[i][j], 0, 0, 0);
-      }
-    }
-  }
-}
-
-// Per-channel LDS offsets inside a stage for channel position k = S_j % 128:
-// bits 0-9 the code byte's offset less the column part, bit 10 the nibble
-// (odd k: high nibble), bits 11-21 the scale byte's offset less the column
-// part.  Column t adds (t/16)*1024 + (t%16)*16 to the code offset (group,
-// slot row) and 4t to the scale offset.
-template <int FMT>
-__device__ __forceinline__ uint32_t chan_desc(int k) {
-  const int bi = k >> 1;
-  const uint32_t cpart = (uint32_t)((bi >> 4) * 256 + (bi & 15));
-  uint32_t spart;
-  if (FMT == FP4Q_NVFP4) {
-    const int blkk = k >> 4;  // 0..7: dword blkk/4, byte blkk%4
-    spart = (uint32_t)((blkk >> 2) * 1024 + (blkk & 3));
-  } else {
-    spart = (uint32_t)(k >> 5);
-  }
-  return cpart | ((uint32_t)(k & 1) << 10) | (spart << 11);
-}
-
-// bf16 bits of the B value (e2m1 code * block scale, exact) for a code byte,
-// the channel's nibble and the scale byte.
-template <int FMT>
-__device__ __forceinline__ uint16_t comp_bits(uint32_t cbyte, uint32_t desc, uint32_t sbyte) {
-  const uint32_t code = ((desc >> 10) & 1u) ? (cbyte >> 4) : (cbyte & 15u);
-  float sc;
-  if (FMT == FP4Q_NVFP4)
-    sc = e4m3_value(sbyte);
-  else
-    sc = sbyte ? __uint_as_float(sbyte << 23) : __uint_as_float(0x00400000u);
-  const float v = e2m1_mag_value(code) * sc;
-  return (uint16_t)((__float_as_uint(v) >> 16) | ((code & 8u) << 12));
-}
-
-// Bring R[rows, channels of group g] into an LDS staging buffer laid out
-// [row][16 channels]: 8 instructions of 32 rows, two lanes per row.
-template <int W>
-__device__ __forceinline__ void issue_resid(const BigArgs& p, int64_t r0, int wave, int lane,
-                                            int g, uint16_t* rbuf) {
-  constexpr int RPW = 8 / W;
-#pragma unroll
-  for (int i = 0; i < RPW; ++i) {
-    const int n = wave * RPW + i;
-    int64_t row = r0 + 32 * n + (lane >> 1);
-    row = row < p.M ? row : p.M - 1;
-    lds_load16(p.resid + row * p.nS + g * GB_CG + 8 * (lane & 1), rbuf + 32 * n * GB_CG);
-  }
-}
-
-// acc += R_group x Wdeq_group, with R scaled by 1/t_x for NVFP4 (so that the
-// final y = (t_x t_w) * acc equals t_w (t_x main + comp)).  The scaled R
-// goes into the bf16 MFMA as a high and a low bf16 part (h = bf16(r),
-// l = bf16(r - h): relative error about 2^-17 over the whole FP32 range),
-// so the accumulators are only ever touched by MFMAs.  A operand: lane takes
-// row lr of each 16-row fragment, channels 4q .. 4q+3.
-template <int FMT, int FI, int FJ>
-__device__ __forceinline__ void flush_group(v4f32 (&acc)[FI][FJ], const uint16_t* comp,
-                                            const uint16_t* rbuf, float inv_tx, int wm, int wn,
-                                            int lane) {
-  const int q = lane >> 4, lr = lane & 15;
-  s16x4 ra[FI], rl[FI];
-#pragma unroll
-  for (int i = 0; i < FI; ++i) {
-    const u32x2b w =
-        *reinterpret_cast<const u32x2b*>(rbuf + (wm * 16 * FI + i * 16 + lr) * GB_CG + 4 * q);
+  for (int i = 0; i < 2; ++i) {
+    const int row = wm * 64 + 32 * i + (lane & 31);
     if (FMT == FP4Q_MXFP4) {
-      ra[i] = __builtin_bit_cast(s16x4, w);
+      f.sa[i][0] = *reinterpret_cast<const uint32_t*>(st + SL::SA + row * 4);
     } else {
-      uint32_t hi[2], lo[2];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t wh = h ? w.y : w.x;
-        const float r0 = __uint_as_float(wh << 16) * inv_tx;
-        const float r1 = __uint_as_float(wh & 0xFFFF0000u) * inv_tx;
-        const uint32_t h0 = f32_to_bf16_rne(r0), h1 = f32_to_bf16_rne(r1);
-        const uint32_t l0 = f32_to_bf16_rne(r0 - __uint_as_float(h0 << 16));
-        const uint32_t l1 = f32_to_bf16_rne(r1 - __uint_as_float(h1 << 16));
-        hi[h] = h0 | (h1 << 16);
-        lo[h] = l0 | (l1 << 16);
-      }
-      ra[i] = __builtin_bit_cast(s16x4, u32x2b{hi[0], hi[1]});
-      rl[i] = __builtin_bit_cast(s16x4, u32x2b{lo[0], lo[1]});
+      for (int h = 0; h < 2; ++h)
+        f.sa[i][h] = *reinterpret_cast<const uint32_t*>(st + SL::SA + (h * 256 + row) * 4);
     }
   }
 #pragma unroll
-  for (int j = 0; j < FJ; ++j) {
-    const s16x4 rb = __builtin_bit_cast(
-        s16x4, *reinterpret_cast<const u32x2b*>(comp + (q * 256 + wn * 16 * FJ + j * 16 + lr) * 4));
+  for (int j = 0; j < 4; ++j) {
+    const int col = wn * 128 + 32 * j + (lane & 31);
+    if (FMT == FP4Q_MXFP4) {
+      f.sb[j][0] = *reinterpret_cast<const uint32_t*>(st + SL::SB + col * 4);
+    } else {
 #pragma unroll
-    for (int i = 0; i < FI; ++i) {
-      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ra[i], rb, acc[i][j], 0, 0, 0);
-      if (FMT == FP4Q_NVFP4)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(rl[i], rb, acc[i][j], 0, 0, 0);
+      for (int h = 0; h < 2; ++h)
+        f.sb[j][h] = *reinterpret_cast<const uint32_t*>(st + SL::SB + (h * 256 + col) * 4);
     }
   }
 }
 
-// W waves; DB: the next stage's fragments are read into a second register
-// set during the current stage's MFMAs (three stages in flight), else the
-// current stage is read after its barrier (two in flight).
-template <int FMT, int W, bool DB, bool TL>
-__global__ void __launch_bounds__(WaveLayout<W>::T, 1) k_gemm_big(BigArgs args) {
-  using SL = StageLayout<FMT, W>;
-  using WL = WaveLayout<W>;
-  constexpr int FI = WL::FI, FJ = WL::FJ, NT = WL::T;
+// One FP4 stage into the 2 x 4 accumulator blocks.
+template <int FMT>
+__device__ __forceinline__ void compute_fp4(f32x16 (&acc)[2][4], const Frag& f, int lane) {
+  const int hi = lane >> 5;
+  if (FMT == FP4Q_MXFP4) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      int sa[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) sa[i] = (int)(f.sa[i][0] >> (8 * (2 * h + hi)));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 bb = f.b[j][h];
+        const i32x8b bv = {(int)bb.x, (int)bb.y, (int)bb.z, (int)bb.w, 0, 0, 0, 0};
+        const int sb = (int)(f.sb[j][0] >> (8 * (2 * h + hi)));
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const u32x4 aa = f.a[i][h];
+          const i32x8b av = {(int)aa.x, (int)aa.y, (int)aa.z, (int)aa.w, 0, 0, 0, 0};
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[i][j], 4, 4, 0,
+                                                                      sa[i], 0, sb);
+        }
+      }
+    }
+  } else {
+    // sub-step (h, s): lane feeds elements 64h + 32hi + 8s .. +7 (block
+    // 4h + 2hi + s/2) as K positions 8hi .. 8hi+7 of a 16-deep MFMA step; A
+    // and B use the same K permutation, so the sum is unchanged
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int sh = 16 * hi + 8 * (s >> 1);
+        h16x8 da[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) da[i] = nv_decode8(f.a[i][h][s], e4m3_h2(f.sa[i][h] >> sh));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const h16x8 db = nv_decode8(f.b[j][h][s], e4m3_h2(f.sb[j][h] >> sh));
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(da[i], db, acc[i][j], 0, 0, 0);
+        }
+      }
+  }
+}
+
+// One compensation stage: 32 channels of R x B_S^T, BF16 products (exact)
+// accumulated in FP32.
+__device__ __forceinline__ void compute_comp(f32x16 (&acc)[2][4], const Frag& f) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8b bv = __builtin_bit_cast(bf16x8b, f.b[j][h]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8b, f.a[i][h]),
+                                                            bv, acc[i][j], 0, 0, 0);
+    }
+}
+
+template <int FMT, bool TL>
+__global__ void __launch_bounds__(GB_T, 1) k_gemm_big(BigArgs args) {
+  using SL = StageLayout<FMT>;
+  constexpr int L = SL::LOADS;
   __shared__ __attribute__((aligned(16))) uint8_t sStage[3 * SL::BYTES];
-  __shared__ __attribute__((aligned(16))) uint16_t sComp[2][GB_COMP];
-  __shared__ __attribute__((aligned(16))) uint16_t sR[2][GB_COMP];
-  __shared__ int sS[GB_MAX_NS];
-  // per stage: count, first channel index, descriptors of up to GB_XB channels
-  __shared__ __attribute__((aligned(16))) int sRow[GB_MAX_NK][8];
+  static_assert(GB_W * 32 * GB_EP_STRIDE * 4 <= 3 * SL::BYTES, "epilogue staging");
 
   const BigArgs& p = args;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -442,260 +394,219 @@ __global__ void __launch_bounds__(WaveLayout<W>::T, 1) k_gemm_big(BigArgs args) 
   const int pid_n = (tile % gsize) / gm;
   const int64_t r0 = (int64_t)pid_m * GB_TILE, c0 = (int64_t)pid_n * GB_TILE;
 
-  const int nS = p.nS;
-  const int nk = (int)(p.K / 128);
-  constexpr int L = SL::LOADS;
-  float tx = 1.0f, tw = 1.0f, inv_tx = 1.0f;
+  const int nk = p.nk, ns = p.nk + p.nc;
+  float tx = 1.0f, tw = 1.0f;
   if (FMT == FP4Q_NVFP4) {
     tx = *p.ats;
     tw = *p.bts;
-    inv_tx = 1.0f / tx;
   }
-  auto stage = [&](int kt) __attribute__((always_inline)) { return sStage + (kt % 3) * SL::BYTES; };
-  auto uni = [](int v) __attribute__((always_inline)) { return __builtin_amdgcn_readfirstlane(v); };
+  auto stage = [&](int s) __attribute__((always_inline)) { return sStage + (s % 3) * SL::BYTES; };
 
-  // ---- prologue, before any stage is in flight (the fences of these
-  // barriers then cost nothing): channel list, zeroed staging buffers, the
-  // per-stage channel table
-  if (nS > 0) {
-    for (int j = t; j < nS; j += NT) sS[j] = p.chan[j];
-    for (int i = t; i < 2 * GB_COMP / 8; i += NT)
-      reinterpret_cast<u32x4*>(&sComp[0][0])[i] = u32x4{0u, 0u, 0u, 0u};
-    __syncthreads();
-    for (int kt = t; kt < nk; kt += NT) {
-      // first channel at or past 128 kt, and at or past 128 (kt + 1)
-      int lo = 0, hi = nS;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (sS[mid] < 128 * kt) lo = mid + 1; else hi = mid;
-      }
-      int lo2 = lo, hi2 = nS;
-      while (lo2 < hi2) {
-        const int mid = (lo2 + hi2) >> 1;
-        if (sS[mid] < 128 * kt + 128) lo2 = mid + 1; else hi2 = mid;
-      }
-      uint32_t d[GB_XB];
+  issue_stage<FMT, TL>(p, 0, wave, lane, r0, c0, stage(0));
+  if (ns > 1) issue_stage<FMT, TL>(p, 1, wave, lane, r0, c0, stage(1));
+
+  f32x16 acc[2][4];
 #pragma unroll
-      for (int c = 0; c < GB_XB; ++c) d[c] = (lo + c < lo2) ? chan_desc<FMT>(sS[lo + c] & 127) : 0u;
-      *reinterpret_cast<u32x4*>(&sRow[kt][0]) = u32x4{(uint32_t)(lo2 - lo), (uint32_t)lo, d[0], d[1]};
-      *reinterpret_cast<u32x4*>(&sRow[kt][4]) = u32x4{d[2], d[3], 0u, 0u};
-    }
-  }
-  asm volatile("" ::: "memory");
-  if (nS > 0) issue_resid<W>(p, r0, wave, lane, 0, sR[0]);
-  issue_stage<FMT, W, TL>(p, 0, wave, lane, r0, c0, stage(0));
-  if (nk > 1) issue_stage<FMT, W, TL>(p, 1, wave, lane, r0, c0, stage(1));
-  if (DB && nk > 2) issue_stage<FMT, W, TL>(p, 2, wave, lane, r0, c0, stage(2));
-
-  v4f32 acc[FI][FJ];
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-  for (int i = 0; i < FI; ++i)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int j = 0; j < FJ; ++j) acc[i][j] = v4f32{0.f, 0.f, 0.f, 0.f};
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  // Compensation bookkeeping is identical in every lane; readfirstlane keeps
-  // it in scalar registers so the branches around the barriers below are
-  // uniform branches the compiler can see as such.
-  int jx = 0;        // channels extracted so far
-  int gf = 0;        // compensation groups flushed so far
-  int r_iter = -4;   // step that issued the residual loads of group gf
-
-  // Flush group gf.  Its residual loads are older than the stage awaited at
-  // the top of step r_iter + 3, so from then on they have landed; earlier,
-  // wait for them explicitly.  Then prefetch the next group's residual into
-  // the buffer just freed.
-  auto flush = [&](int kt) __attribute__((always_inline)) {
-    if (kt < r_iter + 3) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // Stage s: wait for its loads, barrier (it landed everywhere; the buffer
+  // of stage s-1 is free), issue stage s+2, then read and multiply stage s.
+  // The second wave on the SIMD covers this wave's LDS read latency.  The
+  // FP4 and the compensation stages run as two loops (one loop with both
+  // bodies makes the register allocator spill).
+  auto pipe = [&](int s) __attribute__((always_inline)) {
+    if (s + 1 < ns)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
-    flush_group<FMT, FI, FJ>(acc, sComp[gf & 1], sR[gf & 1], inv_tx, wm, wn, lane);
-    gf = uni(gf + 1);
-    if (gf * GB_CG < nS) {
-      lds_barrier();  // every wave is done with the buffer about to be refilled
-      issue_resid<W>(p, r0, wave, lane, gf, sR[gf & 1]);
-      r_iter = kt;
-    }
+    if (s + 2 < ns) issue_stage<FMT, TL>(p, s + 2, wave, lane, r0, c0, stage(s + 2));
   };
-
-  // Channel extraction of stage kx in two halves around the MFMAs: the
-  // first reads the table row and the code and scale bytes of up to GB_XB
-  // channels (thread t < 256 = column t); the second decodes, writes the
-  // staging buffers, extracts any further channels of the stage and
-  // flushes groups as they complete.
-  struct Pending {
-    int cnt, jbase;
-    uint32_t desc[GB_XB], cb[GB_XB], sb[GB_XB];
-  };
-  const int tcol = t & 255;
-  const uint32_t toff_c = (uint32_t)(SL::B + (tcol >> 4) * GB_GRP + (tcol & 15) * 16);
-  const uint32_t toff_s = (uint32_t)(SL::SB + tcol * 4);
-  auto extract_begin = [&](int kx, Pending& pd) __attribute__((always_inline)) {
-    const u32x4 r0v = *reinterpret_cast<const u32x4*>(&sRow[kx][0]);
-    const u32x4 r1v = *reinterpret_cast<const u32x4*>(&sRow[kx][4]);
-    pd.cnt = uni((int)r0v.x);
-    pd.jbase = uni((int)r0v.y);
-    const uint32_t d[GB_XB] = {r0v.z, r0v.w, r1v.x, r1v.y};
-    const uint8_t* st = stage(kx);
+  for (int s = 0; s < nk; ++s) {
+    pipe(s);
+    Frag f;
+    read_frags<FMT, true>(stage(s), wm, wn, lane, f);
+    compute_fp4<FMT>(acc, f, lane);
+  }
+  if (FMT == FP4Q_NVFP4) {
+    // y = t_w (t_x main + comp): scale the main sum once, before R B_S
 #pragma unroll
-    for (int c = 0; c < GB_XB; ++c) {
-      pd.desc[c] = (uint32_t)uni((int)d[c]);
-      pd.cb[c] = st[toff_c + (pd.desc[c] & 1023u)];
-      pd.sb[c] = st[toff_s + (pd.desc[c] >> 11)];
-    }
-  };
-  auto extract_end = [&](int kx, const Pending& pd, int kstep) __attribute__((always_inline)) {
-    const int jend = pd.jbase + pd.cnt;
-    for (int c = 0; jx < jend; ++c, jx = uni(jx + 1)) {
-      const int g = jx / GB_CG;
-      if (g >= gf + 2) flush(kstep);  // both staging buffers hold unflushed groups
-      uint32_t desc, cb, sb;
-      if (c < GB_XB) {
-        desc = c == 0 ? pd.desc[0] : c == 1 ? pd.desc[1] : c == 2 ? pd.desc[2] : pd.desc[3];
-        cb = c == 0 ? pd.cb[0] : c == 1 ? pd.cb[1] : c == 2 ? pd.cb[2] : pd.cb[3];
-        sb = c == 0 ? pd.sb[0] : c == 1 ? pd.sb[1] : c == 2 ? pd.sb[2] : pd.sb[3];
-      } else {  // more channels in this stage than the table row holds
-        desc = (uint32_t)uni((int)chan_desc<FMT>(uni(sS[jx]) & 127));
-        cb = stage(kx)[toff_c + (desc & 1023u)];
-        sb = stage(kx)[toff_s + (desc >> 11)];
-      }
-      if (t < 256) {
-        const int jj = jx % GB_CG;
-        sComp[g & 1][((jj >> 2) * 256 + tcol) * 4 + (jj & 3)] = comp_bits<FMT>(cb, desc, sb);
-      }
-    }
-    if (gf * GB_CG + GB_CG <= jx) flush(kstep);  // the oldest group is complete
-  };
-
-  if (DB) {
-    // three stages in flight, fragments double-buffered in registers
-    Frag<FI, FJ> f0, f1;
-    Pending pd;
-    if (nk > 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * L) : "memory");
-    else if (nk > 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L) : "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    lds_barrier();
-    read_frags<FMT, W>(stage(0), wm, wn, lane, f0);
-    if (nS > 0) {
-      extract_begin(0, pd);
-      extract_end(0, pd, -1);
-    }
-    // stage kt's fragments are in `cur`; stage kt+1 is read into `nxt` and
-    // its channels extracted; stage kt+3 goes into the LDS stage kt used
-    auto step = [&](int kt, Frag<FI, FJ>& cur, Frag<FI, FJ>& nxt) __attribute__((always_inline)) {
-      if (kt + 1 < nk) {
-        if (kt + 2 < nk)
-          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L) : "memory");
-        else
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      }
-      lds_barrier();  // stage kt+1 landed everywhere; stage kt's LDS is free
-      if (kt + 3 < nk) issue_stage<FMT, W, TL>(p, kt + 3, wave, lane, r0, c0, stage(kt));
-      if (kt + 1 < nk) read_frags<FMT, W>(stage(kt + 1), wm, wn, lane, nxt);
-      const bool ex = nS > 0 && kt + 1 < nk;
-      if (ex) extract_begin(kt + 1, pd);
-      compute_frags<FMT, FI, FJ>(acc, cur, lane);
-      if (ex) extract_end(kt + 1, pd, kt);
-    };
-    for (int kt = 0; kt < nk; kt += 2) {
-      step(kt, f0, f1);
-      if (kt + 1 >= nk) break;
-      step(kt + 1, f1, f0);
-    }
-  } else {
-    // two stages in flight; the current stage is read after its barrier
-    Pending pd;
-    auto step = [&](int kt) __attribute__((always_inline)) {
-      if (kt + 1 < nk)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L) : "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      lds_barrier();  // stage kt landed everywhere; stage kt-1's LDS is free
-      if (kt + 2 < nk) issue_stage<FMT, W, TL>(p, kt + 2, wave, lane, r0, c0, stage(kt + 2));
-      Frag<FI, FJ> f;
-      read_frags<FMT, W>(stage(kt), wm, wn, lane, f);
-      if (nS > 0) extract_begin(kt, pd);
-      compute_frags<FMT, FI, FJ>(acc, f, lane);
-      if (nS > 0) extract_end(kt, pd, kt);
-    };
-    for (int kt = 0; kt < nk; ++kt) step(kt);
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] *= tx;
+  }
+  for (int s = nk; s < ns; ++s) {
+    pipe(s);
+    Frag f;
+    read_frags<FMT, false>(stage(s), wm, wn, lane, f);
+    compute_comp(acc, f);
   }
 
-  // remaining compensation groups (every channel is < K, so all extracted)
-  while (gf * GB_CG < nS) flush(nk);
-
-  // ---- epilogue: y = (t_x t_w) * acc; lane holds column lr, rows 4q..4q+3
-  // of each 16x16 tile
-  const float ys = (FMT == FP4Q_NVFP4) ? tx * tw : 1.0f;
-  const int q = lane >> 4, lr = lane & 15;
+  // ---- epilogue.  acc[i][j][e] is row 64 wm + 32 i + 8 (e / 4) + 4 (l / 32)
+  // + e % 4, column 128 wn + 32 j + l % 32.
+  const int hi = lane >> 5, l31 = lane & 31;
+  const int64_t rw = r0 + wm * 64, cw = c0 + wn * 128;
   const bool interior = (r0 + GB_TILE <= p.M) && (c0 + GB_TILE <= p.N);
-  const int64_t rw = r0 + wm * 16 * FI + 4 * q, cw = c0 + wn * 16 * FJ + lr;
-  if (!p.y_bf16) {
-    float* y = reinterpret_cast<float*>(p.y);
-    if (interior) {
+  const bool vec = interior && (p.ldy % 8) == 0 && (reinterpret_cast<uintptr_t>(p.y) & 15) == 0;
+  if (vec) {
+    // Each wave stages 32 x 64 pieces (two blocks) in its own LDS region and
+    // writes 16-byte vectors: rows of 256 bytes (FP32) or 128 bytes (BF16).
+    lds_barrier();  // every wave is done with the last stage
+    float* ep = reinterpret_cast<float*>(sStage) + wave * 32 * GB_EP_STRIDE;
 #pragma unroll
-      for (int i = 0; i < FI; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < FJ; ++j)
+      for (int jp = 0; jp < 2; ++jp) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            __builtin_nontemporal_store(acc[i][j][e] * ys,
-                                        y + (rw + i * 16 + e) * p.ldy + cw + j * 16);
-    } else {
+        for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-      for (int i = 0; i < FI; ++i)
+          for (int e = 0; e < 16; ++e)
+            ep[(8 * (e >> 2) + 4 * hi + (e & 3)) * GB_EP_STRIDE + 32 * jj + l31] =
+                acc[i][2 * jp + jj][e] * tw;
+        const int64_t row0 = rw + 32 * i, col0 = cw + 64 * jp;
+        if (!p.y_bf16) {
+          float* y = reinterpret_cast<float*>(p.y);
 #pragma unroll
-        for (int j = 0; j < FJ; ++j)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int64_t row = rw + i * 16 + e, col = cw + j * 16;
-            if (row < p.M && col < p.N)
-              __builtin_nontemporal_store(acc[i][j][e] * ys, y + row * p.ldy + col);
+          for (int k = 0; k < 8; ++k) {
+            const int rr = 4 * k + (lane >> 4), cc = 4 * (lane & 15);
+            const f32x4b v = *reinterpret_cast<const f32x4b*>(ep + rr * GB_EP_STRIDE + cc);
+            __builtin_nontemporal_store(
+                v, reinterpret_cast<f32x4b*>(y + (row0 + rr) * p.ldy + col0 + cc));
           }
-    }
-  } else {
-    uint16_t* y = reinterpret_cast<uint16_t*>(p.y);
+        } else {
+          uint16_t* y = reinterpret_cast<uint16_t*>(p.y);
 #pragma unroll
-    for (int i = 0; i < FI; ++i)
-#pragma unroll
-      for (int j = 0; j < FJ; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int64_t row = rw + i * 16 + e, col = cw + j * 16;
-          if (interior || (row < p.M && col < p.N))
-            y[row * p.ldy + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][e] * ys);
+          for (int k = 0; k < 4; ++k) {
+            const int rr = 8 * k + (lane >> 3), cc = 8 * (lane & 7);
+            const f32x4b v0 = *reinterpret_cast<const f32x4b*>(ep + rr * GB_EP_STRIDE + cc);
+            const f32x4b v1 = *reinterpret_cast<const f32x4b*>(ep + rr * GB_EP_STRIDE + cc + 4);
+            const u32x4 w = {f32_to_bf16_rne(v0.x) | (f32_to_bf16_rne(v0.y) << 16),
+                             f32_to_bf16_rne(v0.z) | (f32_to_bf16_rne(v0.w) << 16),
+                             f32_to_bf16_rne(v1.x) | (f32_to_bf16_rne(v1.y) << 16),
+                             f32_to_bf16_rne(v1.z) | (f32_to_bf16_rne(v1.w) << 16)};
+            __builtin_nontemporal_store(
+                w, reinterpret_cast<u32x4*>(y + (row0 + rr) * p.ldy + col0 + cc));
+          }
         }
+      }
+    return;
   }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t row = rw + 32 * i + 8 * (e >> 2) + 4 * hi + (e & 3);
+        const int64_t col = cw + 32 * j + l31;
+        if (row < p.M && col < p.N) {
+          const float v = acc[i][j][e] * tw;
+          if (p.y_bf16)
+            reinterpret_cast<uint16_t*>(p.y)[row * p.ldy + col] = (uint16_t)f32_to_bf16_rne(v);
+          else
+            reinterpret_cast<float*>(p.y)[row * p.ldy + col] = v;
+        }
+      }
 }
 
-bool big_gemm_eligible(int64_t M, int64_t N, int64_t K, int nS, const void* resid) {
+// ---- B_S gather ---------------------------------------------------------------
+// bsel holds B_S[n, j] (bf16 bits of e2m1 * block scale, tensor scale
+// excluded; exact) for n < ceil16(N), j < ceil32(|S|), zero past N or |S|,
+// as 1 KB blocks per (16-row group G, 32-channel chunk C) at (G nc + C) * 1024,
+// inside which channels 8c .. 8c+7 of row 16G + r are the 16 bytes at
+// (16c + r) * 16.  One wave writes one block; lane l = 16c + r.
+template <int FMT, bool TL>
+__global__ void __launch_bounds__(256) k_gather_bsel(const uint8_t* __restrict__ bq,
+                                                     const uint8_t* __restrict__ bs, int64_t N,
+                                                     int64_t K, const int32_t* __restrict__ chan,
+                                                     int nS, int nc, int64_t nblocks,
+                                                     uint8_t* __restrict__ bsel) {
+  constexpr int BLK = (FMT == FP4Q_NVFP4) ? 16 : 32;
+  const int lane = threadIdx.x & 63;
+  const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (blk >= nblocks) return;
+  const int64_t G = blk / nc;
+  const int C = (int)(blk - G * nc);
+  const int64_t n = 16 * G + (lane & 15);
+  const int j0 = GB_CS * C + 8 * (lane >> 4);
+  uint32_t h[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int j = j0 + e;
+    h[e] = 0u;
+    if (j < nS && n < N) {
+      const int c = chan[j];
+      const uint32_t byte = bq[code_off(TL, n, c >> 1, K)];
+      const uint32_t code = (c & 1) ? (byte >> 4) : (byte & 15u);
+      const uint32_t sc = bs[scale_off<FMT>(TL, n, c / BLK, K)];
+      const float s = (FMT == FP4Q_NVFP4)
+                          ? e4m3_value(sc)
+                          : (sc ? __uint_as_float(sc << 23) : __uint_as_float(0x00400000u));
+      const float v = e2m1_mag_value(code) * s;
+      h[e] = (__float_as_uint(v) >> 16) | ((code & 8u) << 12);
+    }
+  }
+  const u32x4 w = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                   h[6] | (h[7] << 16)};
+  *reinterpret_cast<u32x4*>(bsel + (blk << 10) + lane * 16) = w;
+}
+
+// ---- host side ---------------------------------------------------------------
+
+bool big_gemm_eligible(int64_t M, int64_t N, int64_t K, int nS) {
   // residual rows are brought in as 16-byte pieces of 8 channels
-  const bool resid_ok = nS == 0 || (reinterpret_cast<uintptr_t>(resid) & 15) == 0;
-  return M >= 256 && N >= 256 && K % 128 == 0 && K / 128 <= GB_MAX_NK && nS <= GB_MAX_NS &&
-         nS % GB_CG == 0 && resid_ok;
+  return M >= GB_TILE && N >= GB_TILE && K % 128 == 0 && nS % 8 == 0;
 }
 
-// Configuration per format: wave count and fragment double buffering.
-template <int FMT> struct BigConfig;
-template <> struct BigConfig<FP4Q_MXFP4> { static constexpr int W = 8; static constexpr bool DB = false; };
-template <> struct BigConfig<FP4Q_NVFP4> { static constexpr int W = 8; static constexpr bool DB = false; };
+size_t big_gemm_workspace_bytes(int64_t N, int nS) {
+  if (nS <= 0) return 0;
+  const int64_t nc = (nS + GB_CS - 1) / GB_CS;
+  return (size_t)(((N + 15) / 16) * nc * 1024);
+}
 
 template <int FMT>
 static void launch_big(const BigArgs& a, bool tiled, hipStream_t stream) {
-  using C = BigConfig<FMT>;
   dim3 grid((unsigned)(a.mt * a.nt));
   if (tiled)
-    hipLaunchKernelGGL((k_gemm_big<FMT, C::W, C::DB, true>), grid, dim3(64 * C::W), 0, stream, a);
+    hipLaunchKernelGGL((k_gemm_big<FMT, true>), grid, dim3(GB_T), 0, stream, a);
   else
-    hipLaunchKernelGGL((k_gemm_big<FMT, C::W, C::DB, false>), grid, dim3(64 * C::W), 0, stream, a);
+    hipLaunchKernelGGL((k_gemm_big<FMT, false>), grid, dim3(GB_T), 0, stream, a);
+}
+
+template <int FMT>
+static void launch_gather(bool tiled, const uint8_t* bq, const uint8_t* bs, int64_t N, int64_t K,
+                          const int32_t* chan, int nS, int nc, uint8_t* bsel,
+                          hipStream_t stream) {
+  const int64_t nblocks = ((N + 15) / 16) * nc;
+  dim3 grid((unsigned)((nblocks + 3) / 4));
+  if (tiled)
+    hipLaunchKernelGGL((k_gather_bsel<FMT, true>), grid, dim3(256), 0, stream, bq, bs, N, K, chan,
+                       nS, nc, nblocks, bsel);
+  else
+    hipLaunchKernelGGL((k_gather_bsel<FMT, false>), grid, dim3(256), 0, stream, bq, bs, N, K,
+                       chan, nS, nc, nblocks, bsel);
 }
 
 int launch_gemm_big(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const uint8_t* aq,
                     const uint8_t* as, const float* ats, const uint8_t* bq, const uint8_t* bs,
                     const float* bts, const int32_t* chan, int nS, const uint16_t* resid,
-                    void* y, int y_bf16, int64_t ldy, hipStream_t stream) {
-  BigArgs a{M, N, K, aq, as, ats, bq, bs, bts, chan, nS, resid, y, y_bf16, ldy,
-            (int)((M + GB_TILE - 1) / GB_TILE), (int)((N + GB_TILE - 1) / GB_TILE)};
-  if (fmt == FP4Q_NVFP4) launch_big<FP4Q_NVFP4>(a, tiled, stream);
-  else launch_big<FP4Q_MXFP4>(a, tiled, stream);
+                    void* y, int y_bf16, int64_t ldy, void* ws, hipStream_t stream) {
+  const int nc = nS > 0 ? (nS + GB_CS - 1) / GB_CS : 0;
+  uint8_t* bsel = static_cast<uint8_t*>(ws);
+  BigArgs a{M, N, K, aq, as, ats, bq, bs, bts, nS, resid, bsel, y, y_bf16, ldy,
+            (int)((M + GB_TILE - 1) / GB_TILE), (int)((N + GB_TILE - 1) / GB_TILE),
+            (int)(K / 128), nc};
+  if (fmt == FP4Q_NVFP4) {
+    if (nc) launch_gather<FP4Q_NVFP4>(tiled, bq, bs, N, K, chan, nS, nc, bsel, stream);
+    launch_big<FP4Q_NVFP4>(a, tiled, stream);
+  } else {
+    if (nc) launch_gather<FP4Q_MXFP4>(tiled, bq, bs, N, K, chan, nS, nc, bsel, stream);
+    launch_big<FP4Q_MXFP4>(a, tiled, stream);
+  }
   return 0;
 }
 

@@ -400,11 +400,10 @@ __global__ void __launch_bounds__(SK_T, 1) k_gemm_skinny(SkinnyArgs p) {
   }
 }
 
-bool skinny_gemm_eligible(int64_t M, int64_t N, int64_t K, int nS, const void* resid) {
-  // the residual rows are read as 16-byte pieces of 8 entries
-  const bool resid_ok =
-      nS == 0 || ((reinterpret_cast<uintptr_t>(resid) & 15) == 0 && (M * nS) % 8 == 0);
-  return M >= 1 && M <= SK_M && N >= 1 && K % 128 == 0 && nS <= SK_MAXS && resid_ok;
+bool skinny_gemm_eligible(int64_t M, int64_t N, int64_t K, int nS) {
+  // the residual rows are read as 16-byte pieces of 8 entries (R itself is
+  // 16-byte aligned)
+  return M >= 1 && M <= SK_M && N >= 1 && K % 128 == 0 && nS <= SK_MAXS && (M * nS) % 8 == 0;
 }
 
 int launch_gemm_skinny(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const uint8_t* aq,

@@ -157,16 +157,24 @@ int fp4q_quantize(fp4q_format_t fmt, fp4q_layout_t layout, const uint16_t* x, in
  *   a_ts       device f32 [1] tensor scale (NVFP4), NULL for MXFP4
  *   b_q, b_s   packed W^T, [N, K/2], [N, K/blk] when row-major (same alignment)
  *   b_ts       device f32 [1] (NVFP4), NULL for MXFP4
- *   chan_idx   device int32 [n_chan] ascending, < K; resid bf16 [M, n_chan]
- *              (both NULL iff n_chan == 0)
+ *   chan_idx   device int32 [n_chan] ascending, < K; resid bf16 [M, n_chan],
+ *              16-byte aligned (both NULL iff n_chan == 0)
  *   y          out [M, ldy] f32 or bf16 (nearest-even), ldy >= N
+ *   workspace  device scratch of fp4q_gemm_workspace_bytes() bytes, 16-byte
+ *              aligned (may be NULL when that is 0); it receives the gathered
+ *              compensation weights B[n, S_j] as BF16 and is left undefined
  *
  * K must be a multiple of 128 (FP4Q_ERR_UNSUPPORTED otherwise).
+ * FP4Q_ERR_WORKSPACE if a needed workspace is missing, small or misaligned.
  * ------------------------------------------------------------------------ */
+size_t fp4q_gemm_workspace_bytes(fp4q_format_t fmt, fp4q_layout_t layout, int64_t M, int64_t N,
+                                 int64_t K, int32_t n_chan);
+
 int fp4q_gemm(fp4q_format_t fmt, fp4q_layout_t layout, int64_t M, int64_t N, int64_t K,
               const uint8_t* a_q, const uint8_t* a_s, const float* a_ts, const uint8_t* b_q,
               const uint8_t* b_s, const float* b_ts, const int32_t* chan_idx, int32_t n_chan,
-              const uint16_t* resid, void* y, fp4q_dtype_t y_dtype, int64_t ldy, void* stream);
+              const uint16_t* resid, void* y, fp4q_dtype_t y_dtype, int64_t ldy, void* workspace,
+              size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Expert-grouped compensated GEMM (MoE layer; QUADS abstract: NVFP4 rollout

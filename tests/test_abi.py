@@ -83,9 +83,9 @@ def test_quantize_rejects(L):
 
 
 def g(L, fmt=0, M=4, N=8, K=256, aq=A, as_=A, ats=B, bq=B, bs=B, bts=B, chan=None, nS=0, R=None,
-      y=A, dt=0, ldy=8, layout=0):
+      y=A, dt=0, ldy=8, layout=0, ws=None, wsb=0):
     return L.fp4q_gemm(fmt, layout, M, N, K, aq, as_, ats, bq, bs, bts, chan, nS, R, y, dt, ldy,
-                       None)
+                       ws, wsb, None)
 
 
 def test_gemm_rejects(L):
@@ -102,6 +102,19 @@ def test_gemm_rejects(L):
     assert g(L, y=None) == INVALID
     assert g(L, layout=5) == INVALID
     assert g(L, layout=1, K=144) == UNSUPPORTED
+    assert g(L, nS=8, chan=A, R=ctypes.c_void_p(0x20008)) == INVALID   # resid 16-byte aligned
+    # the 256x256-tile path gathers the compensation weights into a workspace
+    need = L.fp4q_gemm_workspace_bytes(0, 1, 512, 512, 256, 32)
+    assert need == (512 // 16) * 1 * 1024
+    assert L.fp4q_gemm_workspace_bytes(0, 1, 512, 512, 256, 64) == (512 // 16) * 2 * 1024
+    assert L.fp4q_gemm_workspace_bytes(0, 1, 512, 500, 256, 40) == (512 // 16) * 2 * 1024
+    assert L.fp4q_gemm_workspace_bytes(0, 1, 512, 512, 256, 0) == 0
+    assert L.fp4q_gemm_workspace_bytes(0, 1, 64, 11008, 2048, 64) == 0    # decode shape
+    assert L.fp4q_gemm_workspace_bytes(0, 1, 512, 512, 256, 12) == 0      # |S| % 8: other path
+    big = dict(M=512, N=512, K=256, nS=32, chan=A, R=B, ldy=512)
+    assert g(L, **big) == WORKSPACE
+    assert g(L, **big, ws=A, wsb=need - 1) == WORKSPACE
+    assert g(L, **big, ws=ctypes.c_void_p(0x10008), wsb=need) == WORKSPACE
 
 
 def _packed(L, fmt, layout, rows, cols):

@@ -122,6 +122,52 @@ def test_large_tiles_ragged(orc, fmt, M, N, K, nS):
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("M,N,K,nS", [(256, 256, 128, 8), (512, 272, 384, 40), (300, 520, 640, 640),
+                                      (768, 256, 256, 256), (257, 1000, 512, 96)])
+def test_large_tiles_compensation_stages(orc, fmt, M, N, K, nS):
+    """256x256-tile path with |S| % 32 != 0 (a partial compensation stage),
+    N off the 16-row padding, |S| = K (every channel compensated)."""
+    need_gpu()
+    say(f"gemm large-tile comp stages fmt {fmt} M{M} N{N} K{K} nS{nS}")
+    d = dense_case(M, K, N, n_out=max(1, K // 100), seed=M + 5 * N + K + nS)
+    chan = np.sort(np.random.default_rng(N + nS).choice(K, nS, replace=False)).astype(np.int32)
+    qa, qb = _prep(orc, fmt, d, chan)
+    yo, ya = _oracle_full(orc, fmt, qa, qb, chan)
+    for layout in (fq.ROWMAJOR, fq.TILED):
+        y = to_host(_gpu_gemm(fmt, qa, qb, chan, layout=layout))
+        assert_gemm_close(y, yo, ya)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_large_tiles_bf16_and_ldy(orc, fmt):
+    """256x256-tile path: vector epilogue (FP32, BF16) and the element-wise
+    one (row stride not a multiple of 8)."""
+    dev = need_gpu()
+    say(f"gemm large-tile bf16 + ldy fmt {fmt}")
+    M, N, K, nS = 512, 384, 256, 64
+    d = dense_case(M, K, N, n_out=3, seed=91)
+    chan = np.sort(np.random.default_rng(3).choice(K, nS, replace=False)).astype(np.int32)
+    qa, qb = _prep(orc, fmt, d, chan)
+    yo, ya = _oracle_full(orc, fmt, qa, qb, chan)
+    a = dev_quant(qa, layout=fq.TILED, fmt=fmt)
+    b = dev_quant(qb, layout=fq.TILED, fmt=fmt)
+    ws = torch.empty(fq.gemm_workspace_bytes(fmt, fq.TILED, M, N, K, nS), dtype=torch.uint8,
+                     device=dev)
+    for ldy in (400, 389):
+        ybig = torch.full((M, ldy), 7.0, dtype=torch.float32, device=dev)
+        fq.gemm_into(fmt, fq.TILED, M, N, K, a["q"], a["scales"], a["tscale"], b["q"],
+                     b["scales"], b["tscale"], to_dev(chan), nS, a["resid"], ybig, 0, ldy, ws)
+        torch.cuda.synchronize()
+        yf = to_host(ybig)
+        assert np.all(yf[:, N:] == 7.0)
+        assert_gemm_close(yf[:, :N], yo, ya)
+    yb = fq.gemm(fmt, a, b, chan_idx=to_dev(chan), y_dtype=1)
+    torch.cuda.synchronize()
+    ybf = bf16_to_f32(to_host(yb.view(torch.int16))).astype(np.float64)
+    assert np.all(np.abs(ybf - yo) <= 1e-3 * ya + 2.0 ** -8 * np.abs(yo))
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
 def test_bf16_output_and_ldy(orc, fmt):
     need_gpu()
     say(f"gemm bf16 out + ldy fmt {fmt}")
