@@ -115,6 +115,22 @@ __device__ __forceinline__ void lds_load4(const void* g, void* lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
                :: "s"(lds_addr(lds)), "v"(g) : "memory");
 }
+// The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
+// byte offset (the tiled layout's loads: block base + 16 l or 4 l).
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ void lds_load16s(const void* base, uint32_t voff, void* lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds_addr(lds)), "v"(voff), "s"(uniform_ptr(base)) : "memory");
+}
+__device__ __forceinline__ void lds_load4s(const void* base, uint32_t voff, void* lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+               :: "s"(lds_addr(lds)), "v"(voff), "s"(uniform_ptr(base)) : "memory");
+}
 
 __device__ __forceinline__ h16x8 nv_decode8(uint32_t w, h16x2 s) {
   h16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s;
@@ -181,7 +197,7 @@ __device__ __forceinline__ void issue_stage(const BigArgs& p, int s, int wave, i
       int64_t gb = (c0 >> 4) + g;
       gb = gb < gN ? gb : gN;
       lds_load16(p.resid + row * p.nS + ch, st + SL::A + g * GB_GRP);
-      lds_load16(p.bsel + ((gb * p.nc + cs) << 10) + lane * 16, st + SL::B + g * GB_GRP);
+      lds_load16s(p.bsel + ((gb * p.nc + cs) << 10), lane * 16, st + SL::B + g * GB_GRP);
     }
 #pragma unroll
     for (int i = 0; i < SL::SPW; ++i)  // placeholders keeping the per-stage load count
@@ -200,8 +216,8 @@ __device__ __forceinline__ void issue_stage(const BigArgs& p, int s, int wave, i
       int64_t ga = (r0 >> 4) + g, gb = (c0 >> 4) + g;
       ga = ga < gM ? ga : gM;
       gb = gb < gN ? gb : gN;
-      lds_load16(p.aq + ((ga * KB + kt) << 10) + lane * 16, st + SL::A + g * GB_GRP);
-      lds_load16(p.bq + ((gb * KB + kt) << 10) + lane * 16, st + SL::B + g * GB_GRP);
+      lds_load16s(p.aq + ((ga * KB + kt) << 10), lane * 16, st + SL::A + g * GB_GRP);
+      lds_load16s(p.bq + ((gb * KB + kt) << 10), lane * 16, st + SL::B + g * GB_GRP);
     }
     const int64_t hM = ((p.M + 63) >> 6) - 1, hN = ((p.N + 63) >> 6) - 1;
 #pragma unroll
@@ -212,13 +228,13 @@ __device__ __forceinline__ void issue_stage(const BigArgs& p, int s, int wave, i
       int64_t h = ((isb ? c0 : r0) >> 6) + c;
       const int64_t hl = isb ? hN : hM;
       h = h < hl ? h : hl;
-      const uint8_t* src = (isb ? p.bs : p.as) + (h * KB + kt) * (SPS * 64) + lane * 4;
+      const uint8_t* src = (isb ? p.bs : p.as) + (h * KB + kt) * (SPS * 64);
       uint8_t* dst = st + (isb ? SL::SB : SL::SA);
       if (FMT == FP4Q_NVFP4) {
         const int d = (n >> 2) & 1;
-        lds_load4(src + d * 256, dst + (d * 256 + 64 * c) * 4);
+        lds_load4s(src + d * 256, lane * 4, dst + (d * 256 + 64 * c) * 4);
       } else {
-        lds_load4(src, dst + 64 * c * 4);
+        lds_load4s(src, lane * 4, dst + 64 * c * 4);
       }
     }
     return;
@@ -431,6 +447,13 @@ __global__ void __launch_bounds__(GB_T, 1) k_gemm_big(BigArgs args) {
     Frag f;
     read_frags<FMT, true>(stage(s), wm, wn, lane, f);
     compute_fp4<FMT>(acc, f, lane);
+    if (FMT == FP4Q_MXFP4) {
+      // every LDS read of the stage is issued before its first MFMA, so the
+      // wave waits for LDS once per stage, not once per fragment (NVFP4's
+      // decode temporaries leave no registers for that)
+      __builtin_amdgcn_sched_group_barrier(0x100, 18, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    }
   }
   if (FMT == FP4Q_NVFP4) {
     // y = t_w (t_x main + comp): scale the main sum once, before R B_S
@@ -444,6 +467,8 @@ __global__ void __launch_bounds__(GB_T, 1) k_gemm_big(BigArgs args) {
     Frag f;
     read_frags<FMT, false>(stage(s), wm, wn, lane, f);
     compute_comp(acc, f);
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
   }
 
   // ---- epilogue.  acc[i][j][e] is row 64 wm + 32 i + 8 (e / 4) + 4 (l / 32)
