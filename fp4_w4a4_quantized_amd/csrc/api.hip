@@ -98,7 +98,8 @@ int fp4q_quantize(fp4q_format_t fmt, fp4q_layout_t layout, const uint16_t* x, in
   if (rows > 0 && (!x || !q || !scales)) return FP4Q_ERR_INVALID;
   if (rows > 0 && (!aligned(x, 16) || !aligned(q, 16) || !aligned(scales, 4)))
     return FP4Q_ERR_INVALID;
-  if (rows * (cols / 8) >= ((int64_t)1 << 31)) return FP4Q_ERR_UNSUPPORTED;  // 32-bit chunk index
+  const int64_t prow = layout == FP4Q_LAYOUT_TILED ? (rows + 15) / 16 * 16 : rows;
+  if (prow * (cols / 8) >= ((int64_t)1 << 31)) return FP4Q_ERR_UNSUPPORTED;  // 32-bit chunk index
   const size_t need = fp4q_quantize_workspace_bytes(fmt, rows, cols, num_groups);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 4)))
     return FP4Q_ERR_WORKSPACE;

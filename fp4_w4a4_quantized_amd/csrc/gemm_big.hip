@@ -557,23 +557,29 @@ __global__ void __launch_bounds__(256) k_gather_bsel(const uint8_t* __restrict__
   const int64_t G = blk / nc;
   const int C = (int)(blk - G * nc);
   const int64_t n = 16 * G + (lane & 15);
+  const int64_t nn = n < N ? n : N - 1;
   const int j0 = GB_CS * C + 8 * (lane >> 4);
+  // every load is unconditional (clamped row and channel), so all of a
+  // lane's loads are in flight together; out-of-range entries become 0
+  int c[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) c[e] = chan[j0 + e < nS ? j0 + e : nS - 1];
+  uint32_t byte[8], sc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    byte[e] = bq[code_off(TL, nn, c[e] >> 1, K)];
+    sc[e] = bs[scale_off<FMT>(TL, nn, c[e] / BLK, K)];
+  }
   uint32_t h[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const int j = j0 + e;
-    h[e] = 0u;
-    if (j < nS && n < N) {
-      const int c = chan[j];
-      const uint32_t byte = bq[code_off(TL, n, c >> 1, K)];
-      const uint32_t code = (c & 1) ? (byte >> 4) : (byte & 15u);
-      const uint32_t sc = bs[scale_off<FMT>(TL, n, c / BLK, K)];
-      const float s = (FMT == FP4Q_NVFP4)
-                          ? e4m3_value(sc)
-                          : (sc ? __uint_as_float(sc << 23) : __uint_as_float(0x00400000u));
-      const float v = e2m1_mag_value(code) * s;
-      h[e] = (__float_as_uint(v) >> 16) | ((code & 8u) << 12);
-    }
+    const uint32_t code = (c[e] & 1) ? (byte[e] >> 4) : (byte[e] & 15u);
+    const float s = (FMT == FP4Q_NVFP4)
+                        ? e4m3_value(sc[e])
+                        : (sc[e] ? __uint_as_float(sc[e] << 23) : __uint_as_float(0x00400000u));
+    const float v = e2m1_mag_value(code) * s;
+    const uint32_t bits = (__float_as_uint(v) >> 16) | ((code & 8u) << 12);
+    h[e] = (j0 + e < nS && n < N) ? bits : 0u;
   }
   const u32x4 w = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
                    h[6] | (h[7] << 16)};

@@ -318,7 +318,12 @@ __device__ __forceinline__ void quantize_chunk(u32x4 v, bool active, bool tiled,
 // How NVFP4 finds its tensor scale.
 enum { AMAX_NONE = 0, AMAX_GROUP_WORDS = 1, AMAX_PARTIALS = 2, AMAX_FUSED = 3 };
 
-template <int FMT, int MODE, int NT, int U>
+// TO (tiled order, for the tiled packed layout): chunk c covers block
+// c / 256 of 16 rows x 16 chunks (one 1 KB block of codes), row-group major,
+// row (c % 256) / 16 and chunk c % 16 inside it, so a wave's stores fill
+// contiguous 64-byte runs of the tiled blocks while its loads still read
+// 256-byte row segments.  Otherwise chunks run in row-major order.
+template <int FMT, int MODE, int NT, int U, bool TO>
 __global__ void __launch_bounds__(NT) k_quantize(
     ChunkGrid gr, int64_t rows, int64_t cols, bool tiled, const int32_t* __restrict__ off, int G,
     const int32_t* __restrict__ chan, int nS, uint8_t* __restrict__ q,
@@ -326,9 +331,20 @@ __global__ void __launch_bounds__(NT) k_quantize(
     const uint32_t* __restrict__ amax_words, int nparts) {
   __shared__ uint32_t red[NT / 64];
   __shared__ uint32_t tab[TAB_MAX];
-  const uint32_t cpr = gr.cpr, total = (uint32_t)(rows * cpr);
+  const uint32_t cpr = gr.cpr, total_rm = (uint32_t)(rows * cpr);
+  const uint32_t nbk = cpr >> 4;  // (TO) 16-chunk blocks per row group
+  const uint32_t total = TO ? (uint32_t)(((rows + 15) >> 4) * 16 * cpr) : total_rm;
   const uint32_t base = blockIdx.x * (uint32_t)(NT * U);
   const bool grouped = (G > 1);
+  auto rc_of = [&](uint32_t c, uint32_t& row, uint32_t& cc) __attribute__((always_inline)) {
+    if (TO) {
+      const uint32_t blk = c >> 8, w = c & 255u, rg = blk / nbk;
+      row = rg * 16 + (w >> 4);
+      cc = (blk - rg * nbk) * 16 + (w & 15u);
+    } else {
+      chunk_rc(gr, c, row, cc);
+    }
+  };
 
   // this thread's chunks go out first (a clamped in-range address past the
   // end, so no branch separates the loads)
@@ -336,7 +352,15 @@ __global__ void __launch_bounds__(NT) k_quantize(
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const uint32_t c = base + u * NT + threadIdx.x;
-    v[u] = load_chunk(gr, c < total ? c : total - 1);
+    if (TO) {
+      uint32_t row, cc;
+      rc_of(c < total ? c : total - 1, row, cc);
+      row = row < (uint32_t)rows ? row : (uint32_t)rows - 1;
+      v[u] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(gr.x + (int64_t)row * gr.ldx + (int64_t)cc * 8));
+    } else {
+      v[u] = load_chunk(gr, c < total ? c : total - 1);
+    }
   }
 
   // tensor scale of the dense paths (one group)
@@ -347,7 +371,7 @@ __global__ void __launch_bounds__(NT) k_quantize(
     tdense = nv_tensor_scale(bf16_to_f32(wg_max<NT>(m, red)));
   } else if (MODE == AMAX_FUSED) {
     // the whole (small) tensor, read by every workgroup from L2
-    const uint32_t m = strided_amax(gr, threadIdx.x, total, NT);
+    const uint32_t m = strided_amax(gr, threadIdx.x, total_rm, NT);
     tdense = nv_tensor_scale(bf16_to_f32(wg_max<NT>(m, red)));
   }
   if ((MODE == AMAX_PARTIALS || MODE == AMAX_FUSED) && blockIdx.x == 0 && threadIdx.x == 0)
@@ -355,7 +379,7 @@ __global__ void __launch_bounds__(NT) k_quantize(
 
   // group of the workgroup's first row; its channel table
   uint32_t row_first, cc_first;
-  chunk_rc(gr, base, row_first, cc_first);
+  rc_of(base, row_first, cc_first);
   const int gA = grouped ? group_of_row(off, G, row_first) : 0;
   const int64_t gA_end = grouped ? (int64_t)off[gA + 1] : rows;
   const bool use_tab = nS > 0 && cpr <= TAB_MAX;
@@ -364,9 +388,10 @@ __global__ void __launch_bounds__(NT) k_quantize(
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const uint32_t c = base + u * NT + threadIdx.x;
-    const bool active = c < total;
     uint32_t row, cc;
-    chunk_rc(gr, active ? c : 0u, row, cc);
+    rc_of(c < total ? c : 0u, row, cc);
+    const bool active = c < total && row < (uint32_t)rows;
+    if (!active) row = cc = 0;
     int g = gA;
     if (grouped && active && row >= gA_end) g = group_of_row(off, G, row);
     float t = tdense;
@@ -383,14 +408,18 @@ __global__ void __launch_bounds__(NT) k_quantize(
 
 template <int FMT, int MODE, int NT, int U>
 static void launch_q(const ChunkGrid& gr, int64_t rows, int64_t cols, bool tiled,
-                     hipStream_t stream,
-                     const int32_t* off, int G, const int32_t* chan, int nS, uint8_t* q,
-                     uint8_t* scales, float* tscale, uint16_t* resid, const uint32_t* words,
-                     int nparts) {
-  const int64_t per = (int64_t)NT * U, total = rows * (int64_t)gr.cpr;
+                     hipStream_t stream, const int32_t* off, int G, const int32_t* chan, int nS,
+                     uint8_t* q, uint8_t* scales, float* tscale, uint16_t* resid,
+                     const uint32_t* words, int nparts) {
+  const int64_t per = (int64_t)NT * U;
+  const int64_t total = (tiled ? (rows + 15) / 16 * 16 : rows) * (int64_t)gr.cpr;
   dim3 grid((unsigned)((total + per - 1) / per));
-  hipLaunchKernelGGL((k_quantize<FMT, MODE, NT, U>), grid, dim3(NT), 0, stream, gr, rows, cols,
-                     tiled, off, G, chan, nS, q, scales, tscale, resid, words, nparts);
+  if (tiled)
+    hipLaunchKernelGGL((k_quantize<FMT, MODE, NT, U, true>), grid, dim3(NT), 0, stream, gr, rows,
+                       cols, true, off, G, chan, nS, q, scales, tscale, resid, words, nparts);
+  else
+    hipLaunchKernelGGL((k_quantize<FMT, MODE, NT, U, false>), grid, dim3(NT), 0, stream, gr, rows,
+                       cols, false, off, G, chan, nS, q, scales, tscale, resid, words, nparts);
 }
 
 int launch_quantize(int fmt, bool tiled, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
