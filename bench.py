@@ -156,7 +156,7 @@ def main():
         gwsb = fq.gemm_workspace_bytes(fmt, layout, M, N, K, nS)
         gws = torch.empty(gwsb, dtype=torch.uint8, device=dev) if gwsb else None
         G = 1
-        qws = torch.empty(max(fq.quantize_workspace_bytes(fmt, M, K, 1), 16), dtype=torch.uint8,
+        qws = torch.zeros(max(fq.quantize_workspace_bytes(fmt, M, K, 1), 16), dtype=torch.uint8,
                           device=dev)
         cb, sb = fq.packed_bytes(fmt, layout, M, K)
         aq = torch.empty(cb, dtype=torch.uint8, device=dev)
@@ -206,7 +206,7 @@ def main():
                 s=torch.empty((r, k // blk), dtype=torch.uint8, device=dev),
                 t=torch.empty(G, dtype=torch.float32, device=dev),
                 r=torch.empty((r, nS), dtype=torch.int16, device=dev),
-                ws=torch.empty(max(fq.quantize_workspace_bytes(fmt, r, k, G), 16),
+                ws=torch.zeros(max(fq.quantize_workspace_bytes(fmt, r, k, G), 16),
                                dtype=torch.uint8, device=dev))
         ygu = torch.empty((rows, I2), dtype=torch.float32, device=dev)
         ydn = torch.empty((rows, H), dtype=torch.float32, device=dev)

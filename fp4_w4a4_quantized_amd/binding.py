@@ -187,7 +187,7 @@ def quantize(fmt, x, group_offsets=None, chan_idx=None, layout=ROWMAJOR, stream=
     ts = torch.empty(G, dtype=torch.float32, device=dev) if fmt == NVFP4 else None
     R = torch.empty((rows, nS), dtype=torch.int16, device=dev) if nS else None
     wsb = quantize_workspace_bytes(fmt, rows, cols, G)
-    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev) if wsb else None
+    ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device=dev) if wsb else None
     quantize_into(fmt, layout, x, group_offsets, G, chan_idx, nS, q, sc, ts, R, ws, stream)
     return {"q": q, "scales": sc, "tscale": ts, "resid": R, "layout": layout, "rows": rows,
             "cols": cols}

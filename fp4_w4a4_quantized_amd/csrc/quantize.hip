@@ -363,6 +363,15 @@ __global__ void __launch_bounds__(NT) k_quantize(
     }
   }
 
+  // group of the workgroup's first row; its channel table (built while the
+  // chunk loads are in flight)
+  uint32_t row_first, cc_first;
+  rc_of(base, row_first, cc_first);
+  const int gA = grouped ? group_of_row(off, G, row_first) : 0;
+  const int64_t gA_end = grouped ? (int64_t)off[gA + 1] : rows;
+  const bool use_tab = nS > 0 && cpr <= TAB_MAX;
+  if (use_tab) build_chan_table(chan + (int64_t)gA * nS, nS, cpr, tab, NT);
+
   // tensor scale of the dense paths (one group)
   float tdense = 1.0f;
   if (MODE == AMAX_PARTIALS) {
@@ -376,14 +385,6 @@ __global__ void __launch_bounds__(NT) k_quantize(
   }
   if ((MODE == AMAX_PARTIALS || MODE == AMAX_FUSED) && blockIdx.x == 0 && threadIdx.x == 0)
     tscale[0] = tdense;
-
-  // group of the workgroup's first row; its channel table
-  uint32_t row_first, cc_first;
-  rc_of(base, row_first, cc_first);
-  const int gA = grouped ? group_of_row(off, G, row_first) : 0;
-  const int64_t gA_end = grouped ? (int64_t)off[gA + 1] : rows;
-  const bool use_tab = nS > 0 && cpr <= TAB_MAX;
-  if (use_tab) build_chan_table(chan + (int64_t)gA * nS, nS, cpr, tab, NT);
 
 #pragma unroll
   for (int u = 0; u < U; ++u) {

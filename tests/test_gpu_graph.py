@@ -23,7 +23,7 @@ def _bufs(fmt, rows, K, nS, G, dev, layout=fq.ROWMAJOR):
         s=torch.empty(sb, dtype=torch.uint8, device=dev),
         t=torch.empty(G, dtype=torch.float32, device=dev) if fmt == fq.NVFP4 else None,
         r=torch.empty((rows, nS), dtype=torch.int16, device=dev) if nS else None,
-        ws=torch.empty(max(fq.quantize_workspace_bytes(fmt, rows, K, G), 16), dtype=torch.uint8,
+        ws=torch.zeros(max(fq.quantize_workspace_bytes(fmt, rows, K, G), 16), dtype=torch.uint8,
                        device=dev))
 
 

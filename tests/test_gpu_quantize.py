@@ -80,7 +80,7 @@ def test_tiled_ragged(orc, fmt, rows, cols, nS):
     ts = torch.empty(1, dtype=torch.float32, device=dev) if fmt == 0 else None
     R = torch.empty((rows, nS), dtype=torch.int16, device=dev) if nS else None
     wsb = fq.quantize_workspace_bytes(fmt, rows, cols, 1)
-    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)
     fq.quantize_into(fmt, fq.TILED, to_dev(d["x"]), None, 1, to_dev(chan) if nS else None, nS,
                      q, sc, ts, R, ws)
     torch.cuda.synchronize(dev)
@@ -89,6 +89,30 @@ def test_tiled_ragged(orc, fmt, rows, cols, nS):
     got = {"q": q[:cb], "scales": sc[:sb], "tscale": ts, "resid": R, "layout": fq.TILED,
            "rows": rows, "cols": cols}
     assert_quant_equal(got, ref, fmt)
+
+
+def test_workspace_reuse_across_paths(orc):
+    """One NVFP4 workspace through the single-launch small-tensor path, the
+    two-pass large path, the grouped path and the small path again: every
+    result exact whatever the previous call left in the workspace."""
+    dev = need_gpu()
+    say("quantize workspace reuse across paths")
+    wsb = max(fq.quantize_workspace_bytes(0, 4096, 4096, 1), fq.quantize_workspace_bytes(0, 600, 512, 5))
+    ws = torch.full((wsb,), 0xA7, dtype=torch.uint8, device=dev)
+    cases = [(64, 2048, None), (1, 256, None), (600, 4096, None),
+             (333, 512, np.array([0, 40, 40, 41, 200, 333], np.int32)), (64, 2048, None),
+             (300, 4096, None)]
+    for i, (rows, cols, off) in enumerate(cases):
+        d = dense_case(rows, cols, 8, n_out=3, seed=500 + i)
+        G = 1 if off is None else off.size - 1
+        ref = orc.quantize(0, d["x"], offsets=off)
+        q = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+        sc = torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev)
+        ts = torch.empty(G, dtype=torch.float32, device=dev)
+        fq.quantize_into(0, fq.ROWMAJOR, to_dev(d["x"]), None if off is None else to_dev(off), G,
+                         None, 0, q, sc, ts, None, ws)
+        torch.cuda.synchronize(dev)
+        assert_quant_equal({"q": q, "scales": sc, "tscale": ts, "resid": None}, ref, 0)
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
