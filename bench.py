@@ -217,11 +217,15 @@ def main():
                 fq.quantize_into(fmt, fq.ROWMAJOR, xin, off, G, ch, nS, b["q"], b["s"], b["t"], b["r"],
                                  b["ws"])
 
+        gws_bytes = max(fq.grouped_gemm_workspace_bytes(fmt, rows, I2, H, G, nS),
+                        fq.grouped_gemm_workspace_bytes(fmt, rows, H, I, G, nS))
+        gws = torch.empty(gws_bytes, dtype=torch.uint8, device=dev) if gws_bytes else None
+
         def gemm(i):
             for tag, w, y, n, k, ch in (("gu", wgu, ygu, I2, H, cg), ("dn", wdn, ydn, H, I, cd)):
                 b = bufs[tag]
                 fq.grouped_gemm_into(fmt, rows, n, k, off, G, b["q"], b["s"], b["t"], w[0], w[1],
-                                     w[2], ch, nS, b["r"], y, 0)
+                                     w[2], ch, nS, b["r"], y, 0, gws)
 
         loads = data["loads"]
         active = int((loads > 0).sum())

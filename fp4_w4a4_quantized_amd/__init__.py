@@ -22,6 +22,7 @@ from .binding import (  # noqa: F401
     gemm_workspace_bytes,
     grouped_gemm,
     grouped_gemm_into,
+    grouped_gemm_workspace_bytes,
     lib,
     packed_bytes,
     quantize,

@@ -79,9 +79,11 @@ def lib():
         L.fp4q_gemm.restype = ctypes.c_int
         L.fp4q_gemm.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, P, P, P, P, P, P, P,
                                 i32, P, P, ctypes.c_int, i64, P, sz, P]
+        L.fp4q_grouped_gemm_workspace_bytes.restype = sz
+        L.fp4q_grouped_gemm_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i64, i32, i32]
         L.fp4q_grouped_gemm.restype = ctypes.c_int
         L.fp4q_grouped_gemm.argtypes = [ctypes.c_int, i64, i64, i64, P, i32, P, P, P, P, P, P, P,
-                                        i32, P, P, ctypes.c_int, P]
+                                        i32, P, P, ctypes.c_int, P, sz, P]
         L.fp4q_error_decompose_workspace_bytes.restype = sz
         L.fp4q_error_decompose_workspace_bytes.argtypes = [i64, i64]
         L.fp4q_error_decompose.restype = ctypes.c_int
@@ -123,6 +125,10 @@ def gemm_workspace_bytes(fmt, layout, M, N, K, n_chan) -> int:
     return lib().fp4q_gemm_workspace_bytes(fmt, layout, M, N, K, n_chan)
 
 
+def grouped_gemm_workspace_bytes(fmt, total_rows, N, K, num_groups, n_chan) -> int:
+    return lib().fp4q_grouped_gemm_workspace_bytes(fmt, total_rows, N, K, num_groups, n_chan)
+
+
 def error_decompose_workspace_bytes(rows, cols) -> int:
     return lib().fp4q_error_decompose_workspace_bytes(rows, cols)
 
@@ -148,11 +154,13 @@ def gemm_into(fmt, layout, M, N, K, a_q, a_s, a_ts, b_q, b_s, b_ts, chan_idx, n_
 
 
 def grouped_gemm_into(fmt, total_rows, N, K, group_offsets, num_groups, a_q, a_s, a_ts, b_q,
-                      b_s, b_ts, chan_idx, n_chan, resid, y, y_dtype=OUT_F32, stream=None):
+                      b_s, b_ts, chan_idx, n_chan, resid, y, y_dtype=OUT_F32, workspace=None,
+                      stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = lib().fp4q_grouped_gemm(fmt, total_rows, N, K, _ptr(group_offsets), num_groups,
                                  _ptr(a_q), _ptr(a_s), _ptr(a_ts), _ptr(b_q), _ptr(b_s),
                                  _ptr(b_ts), _ptr(chan_idx), n_chan, _ptr(resid), _ptr(y),
-                                 y_dtype, _stream(stream))
+                                 y_dtype, _ptr(workspace), ws_bytes, _stream(stream))
     _check("fp4q_grouped_gemm", rc)
 
 
@@ -226,10 +234,13 @@ def grouped_gemm(fmt, group_offsets, a, bq, bs, bts, chan_idx=None, y_dtype=OUT_
     G = group_offsets.numel() - 1
     N = bq.shape[1]
     nS = 0 if chan_idx is None else chan_idx.numel() // G
+    dev = a["q"].device
     y = torch.empty((total, N), dtype=torch.float32 if y_dtype == OUT_F32 else torch.bfloat16,
-                    device=a["q"].device)
+                    device=dev)
+    wsb = grouped_gemm_workspace_bytes(fmt, total, N, K, G, nS)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
     grouped_gemm_into(fmt, total, N, K, group_offsets, G, a["q"], a["scales"], a["tscale"], bq,
-                      bs, bts, chan_idx, nS, a["resid"] if nS else None, y, y_dtype, stream)
+                      bs, bts, chan_idx, nS, a["resid"] if nS else None, y, y_dtype, ws, stream)
     return y
 
 

@@ -162,22 +162,33 @@ int fp4q_gemm(fp4q_format_t fmt, fp4q_layout_t layout, int64_t M, int64_t N, int
   return check_launch();
 }
 
+size_t fp4q_grouped_gemm_workspace_bytes(fp4q_format_t fmt, int64_t total_rows, int64_t N,
+                                         int64_t K, int32_t num_groups, int32_t n_chan) {
+  (void)fmt;
+  if (total_rows <= 0 || N <= 0 || K <= 0 || n_chan <= 0 || num_groups < 1) return 0;
+  return fp4q::grouped_workspace_bytes(N, K, num_groups, n_chan);
+}
+
 int fp4q_grouped_gemm(fp4q_format_t fmt, int64_t total_rows, int64_t N, int64_t K,
                       const int32_t* group_offsets, int32_t num_groups, const uint8_t* a_q,
                       const uint8_t* a_s, const float* a_ts, const uint8_t* b_q,
                       const uint8_t* b_s, const float* b_ts, const int32_t* chan_idx,
                       int32_t n_chan, const uint16_t* resid, void* y, fp4q_dtype_t y_dtype,
-                      void* stream) {
+                      void* workspace, size_t workspace_bytes, void* stream) {
   int rc = validate_gemm_common(fmt, N, K, a_q, a_s, a_ts, b_q, b_s, b_ts, chan_idx, n_chan,
                                 resid, y, y_dtype, total_rows);
   if (rc != FP4Q_OK) return rc;
   if (num_groups < 1 || !group_offsets) return FP4Q_ERR_INVALID;
   if (num_groups > MAX_GROUPS) return FP4Q_ERR_UNSUPPORTED;
   if ((N + 127) / 128 > 65535) return FP4Q_ERR_UNSUPPORTED;
+  const size_t need =
+      fp4q_grouped_gemm_workspace_bytes(fmt, total_rows, N, K, num_groups, n_chan);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
+    return FP4Q_ERR_WORKSPACE;
   clear_error();
   fp4q::launch_gemm(fmt, false, total_rows, N, K, group_offsets, num_groups, a_q, a_s, a_ts, b_q,
-                    b_s, b_ts, chan_idx, n_chan, resid, y, y_dtype == FP4Q_OUT_BF16, N, nullptr,
-                    static_cast<hipStream_t>(stream));
+                    b_s, b_ts, chan_idx, n_chan, resid, y, y_dtype == FP4Q_OUT_BF16, N,
+                    workspace, static_cast<hipStream_t>(stream));
   return check_launch();
 }
 

@@ -30,7 +30,15 @@ int launch_gemm(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const int3
                 hipStream_t stream);
 
 bool big_gemm_eligible(int64_t M, int64_t N, int64_t K, int nS);
+bool big_grouped_eligible(int64_t N, int64_t K, int nS);
 size_t big_gemm_workspace_bytes(int64_t N, int nS);
+size_t grouped_workspace_bytes(int64_t N, int64_t K, int G, int nS);
+int launch_gemm_big_grouped(int fmt, int64_t total_rows, int64_t N, int64_t K,
+                            const int32_t* off, int G, const uint8_t* aq, const uint8_t* as,
+                            const float* ats, const uint8_t* bq, const uint8_t* bs,
+                            const float* bts, const int32_t* chan, int nS,
+                            const uint16_t* resid, void* y, int y_bf16, void* ws,
+                            hipStream_t stream);
 int launch_gemm_big(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const uint8_t* aq,
                     const uint8_t* as, const float* ats, const uint8_t* bq, const uint8_t* bs,
                     const float* bts, const int32_t* chan, int nS, const uint16_t* resid,

@@ -387,6 +387,10 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int nS) {
   return gemm_path(M, N, K, nS) == PATH_BIG ? big_gemm_workspace_bytes(N, nS) : 0;
 }
 
+size_t grouped_workspace_bytes(int64_t N, int64_t K, int G, int nS) {
+  return big_grouped_eligible(N, K, nS) ? (size_t)G * big_gemm_workspace_bytes(N, nS) : 0;
+}
+
 int launch_gemm(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const int32_t* off, int G,
                 const uint8_t* aq, const uint8_t* as, const float* ats, const uint8_t* bq,
                 const uint8_t* bs, const float* bts, const int32_t* chan, int nS,
@@ -394,6 +398,11 @@ int launch_gemm(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const int3
                 hipStream_t stream) {
   GemmArgs a{M, N, K, off, G, aq, as, ats, bq, bs, bts, chan, nS, resid, y, y_bf16, ldy, tiled};
   if (M == 0 || N == 0) return 0;
+  if (off != nullptr && big_grouped_eligible(N, K, nS)) {
+    launch_gemm_big_grouped(fmt, M, N, K, off, G, aq, as, ats, bq, bs, bts, chan, nS, resid, y,
+                            y_bf16, ws, stream);
+    return 0;
+  }
   if (off != nullptr) {
     constexpr int BM = 64;
     unsigned mt = (unsigned)((M + BM - 1) / BM + G);  // each group adds at most one partial tile

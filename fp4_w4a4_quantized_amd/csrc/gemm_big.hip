@@ -61,6 +61,9 @@ constexpr int GB_DATA = 16 * GB_GRP;     // 16 KB per operand per stage
 constexpr int GB_CS = 32;                // channels per compensation stage
 constexpr int GB_GROUP_M = 4;            // tile rows per L2 group
 constexpr int GB_EP_STRIDE = 68;         // epilogue LDS row stride (floats)
+constexpr int GB_XS_MAX = 96;            // channels extracted in-kernel (3 stages of 32)
+constexpr int GB_XS_BYTES = 3 * GB_DATA; // their B_S, laid out as 3 compensation B tiles
+constexpr int GB_XS_MAX_NK = 256;        // K <= 32768 for the per-stage channel table
 
 struct BigArgs {
   int64_t M, N, K;
@@ -73,11 +76,24 @@ struct BigArgs {
   int nS;
   const uint16_t* resid;
   const uint8_t* bsel;  // gathered B_S, tiled BF16 (see k_gather_bsel)
+  const int32_t* chan;  // channel lists (in-kernel extraction)
   void* y;
   int y_bf16;
   int64_t ldy;
   int mt, nt;  // tile counts
   int nk, nc;  // FP4 stages, compensation stages
+  // grouped (expert) form: row ranges [off[g], off[g+1]) use operand set g
+  const int32_t* off;
+  int G;
+};
+
+// The operands and row range of one output tile.  Grouped: B, its scales,
+// B_S and the tensor scales of the tile's group.
+struct TileCtx {
+  int64_t r0, c0, rend;
+  const uint8_t* bq;
+  const uint8_t* bs;
+  const uint8_t* bsel;
 };
 
 // Byte offsets inside one LDS stage and the direct-to-LDS loads a wave
@@ -179,11 +195,12 @@ __device__ __forceinline__ void lds_barrier() {
 // Compensation stage cs: per 16-row group, R rows (channels 32cs + 8(l/16)
 // .. +7 of row 16g + l%16; a piece past |S| is re-read from the last valid
 // one and meets zero weights) and the matching 1 KB block of B_S.
-template <int FMT, bool TL>
+template <int FMT, bool TL, bool XS>
 __device__ __forceinline__ void issue_stage(const BigArgs& p, int s, int wave, int lane,
-                                            int64_t r0, int64_t c0, uint8_t* st) {
+                                            const TileCtx& tc, uint8_t* st) {
   using SL = StageLayout<FMT>;
   constexpr int SPS = (FMT == FP4Q_NVFP4) ? 8 : 4;  // scale bytes per row per step
+  const int64_t r0 = tc.r0, c0 = tc.c0, rend = tc.rend;
   if (s >= p.nk) {
     const int cs = s - p.nk;
     const int64_t gN = ((p.N + 15) >> 4) - 1;
@@ -193,11 +210,14 @@ __device__ __forceinline__ void issue_stage(const BigArgs& p, int s, int wave, i
     for (int i = 0; i < 2; ++i) {
       const int g = wave * 2 + i;
       int64_t row = r0 + 16 * g + (lane & 15);
-      row = row < p.M ? row : p.M - 1;
+      row = row < rend ? row : rend - 1;
       int64_t gb = (c0 >> 4) + g;
       gb = gb < gN ? gb : gN;
       lds_load16(p.resid + row * p.nS + ch, st + SL::A + g * GB_GRP);
-      lds_load16s(p.bsel + ((gb * p.nc + cs) << 10), lane * 16, st + SL::B + g * GB_GRP);
+      if (XS)  // B_S is already in LDS; a placeholder keeps the load count
+        lds_load4(p.resid, st + SL::B + g * GB_GRP);
+      else
+        lds_load16s(tc.bsel + ((gb * p.nc + cs) << 10), lane * 16, st + SL::B + g * GB_GRP);
     }
 #pragma unroll
     for (int i = 0; i < SL::SPW; ++i)  // placeholders keeping the per-stage load count
@@ -217,7 +237,7 @@ __device__ __forceinline__ void issue_stage(const BigArgs& p, int s, int wave, i
       ga = ga < gM ? ga : gM;
       gb = gb < gN ? gb : gN;
       lds_load16s(p.aq + ((ga * KB + kt) << 10), lane * 16, st + SL::A + g * GB_GRP);
-      lds_load16s(p.bq + ((gb * KB + kt) << 10), lane * 16, st + SL::B + g * GB_GRP);
+      lds_load16s(tc.bq + ((gb * KB + kt) << 10), lane * 16, st + SL::B + g * GB_GRP);
     }
     const int64_t hM = ((p.M + 63) >> 6) - 1, hN = ((p.N + 63) >> 6) - 1;
 #pragma unroll
@@ -228,7 +248,7 @@ __device__ __forceinline__ void issue_stage(const BigArgs& p, int s, int wave, i
       int64_t h = ((isb ? c0 : r0) >> 6) + c;
       const int64_t hl = isb ? hN : hM;
       h = h < hl ? h : hl;
-      const uint8_t* src = (isb ? p.bs : p.as) + (h * KB + kt) * (SPS * 64);
+      const uint8_t* src = (isb ? tc.bs : p.as) + (h * KB + kt) * (SPS * 64);
       uint8_t* dst = st + (isb ? SL::SB : SL::SA);
       if (FMT == FP4Q_NVFP4) {
         const int d = (n >> 2) & 1;
@@ -245,10 +265,10 @@ __device__ __forceinline__ void issue_stage(const BigArgs& p, int s, int wave, i
   for (int i = 0; i < 2; ++i) {
     const int g = wave * 2 + i;
     int64_t ra = r0 + 16 * g + (lane & 15), rb = c0 + 16 * g + (lane & 15);
-    ra = ra < p.M ? ra : p.M - 1;
+    ra = ra < rend ? ra : rend - 1;
     rb = rb < p.N ? rb : p.N - 1;
     lds_load16(p.aq + ra * K2 + off, st + SL::A + g * GB_GRP);
-    lds_load16(p.bq + rb * K2 + off, st + SL::B + g * GB_GRP);
+    lds_load16(tc.bq + rb * K2 + off, st + SL::B + g * GB_GRP);
   }
 #pragma unroll
   for (int i = 0; i < SL::SPW; ++i) {
@@ -256,9 +276,9 @@ __device__ __forceinline__ void issue_stage(const BigArgs& p, int s, int wave, i
     const int c = n & 3;
     const bool isb = n >= SL::SCALE_INSTR / 2;
     int64_t row = (isb ? c0 : r0) + 64 * c + lane;
-    const int64_t lim = isb ? p.N : p.M;
+    const int64_t lim = isb ? p.N : rend;
     row = row < lim ? row : lim - 1;
-    const uint8_t* src = isb ? p.bs : p.as;
+    const uint8_t* src = isb ? tc.bs : p.as;
     uint8_t* dst = st + (isb ? SL::SB : SL::SA);
     if (FMT == FP4Q_NVFP4) {
       const int d = (n >> 2) & 1;
@@ -285,7 +305,8 @@ struct Frag {
 };
 
 template <int FMT, bool SCALES>
-__device__ __forceinline__ void read_frags(const uint8_t* st, int wm, int wn, int lane, Frag& f) {
+__device__ __forceinline__ void read_frags(const uint8_t* st, const uint8_t* bsrc, int wm, int wn,
+                                           int lane, Frag& f) {
   using SL = StageLayout<FMT>;
   const uint32_t l32 =
       (uint32_t)((((lane >> 4) & 1) * GB_GRP) + ((lane >> 5) * 16 + (lane & 15)) * 16);
@@ -299,8 +320,7 @@ __device__ __forceinline__ void read_frags(const uint8_t* st, int wm, int wn, in
   for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-      f.b[j][h] = *reinterpret_cast<const u32x4*>(st + SL::B + (wn * 8 + 2 * j) * GB_GRP + l32 +
-                                                  h * 512);
+      f.b[j][h] = *reinterpret_cast<const u32x4*>(bsrc + (wn * 8 + 2 * j) * GB_GRP + l32 + h * 512);
   if (!SCALES) return;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -388,38 +408,124 @@ __device__ __forceinline__ void compute_comp(f32x16 (&acc)[2][4], const Frag& f)
     }
 }
 
-template <int FMT, bool TL>
+// XS: the compensation weights of up to GB_XS_MAX channels are taken from
+// the B tiles as the FP4 stages pass through LDS (no gather kernel).
+template <int FMT, bool TL, bool GR, bool XS>
 __global__ void __launch_bounds__(GB_T, 1) k_gemm_big(BigArgs args) {
   using SL = StageLayout<FMT>;
   constexpr int L = SL::LOADS;
   __shared__ __attribute__((aligned(16))) uint8_t sStage[3 * SL::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t sBS[XS ? GB_XS_BYTES : 16];
+  __shared__ int sChan[XS ? GB_XS_MAX : 1];
+  __shared__ int sFirst[XS ? GB_XS_MAX_NK + 1 : 1];
   static_assert(GB_W * 32 * GB_EP_STRIDE * 4 <= 3 * SL::BYTES, "epilogue staging");
 
   const BigArgs& p = args;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // ---- tile id: XCD-aware, then grouped along M for L2 reuse
-  const int T = p.mt * p.nt;
-  int tile = blockIdx.x;
-  if ((T & 7) == 0) tile = (blockIdx.x & 7) * (T >> 3) + (blockIdx.x >> 3);
-  const int gsize = GB_GROUP_M * p.nt;
-  const int gid = tile / gsize, first_m = gid * GB_GROUP_M;
-  const int gm = min(p.mt - first_m, GB_GROUP_M);
-  const int pid_m = first_m + (tile % gsize) % gm;
-  const int pid_n = (tile % gsize) / gm;
-  const int64_t r0 = (int64_t)pid_m * GB_TILE, c0 = (int64_t)pid_n * GB_TILE;
+  TileCtx tc;
+  int grp = 0;
+  if (GR) {
+    // Tiles in group order, then M, then N (the N tiles of one 256-row
+    // block of A run together): group g has ceil(rows_g / 256) * nt tiles.
+    // Find this workgroup's group by a block-wide scan over per-thread runs
+    // of 4 groups (G <= 2048).
+    __shared__ int s_wsum[GB_W];
+    __shared__ int s_tile[2];
+    const int G = p.G;
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int gg = t * 4 + i;
+      if (gg < G) cnt += (p.off[gg + 1] - p.off[gg] + GB_TILE - 1) / GB_TILE * p.nt;
+    }
+    int incl = cnt;
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl, d);
+      if (lane >= d) incl += v;
+    }
+    if (lane == 63) s_wsum[wave] = incl;
+    if (t == 0) s_tile[0] = -1;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += s_wsum[w];
+    const int excl = before + incl - cnt;
+    const int tile = blockIdx.x;
+    if (tile >= excl && tile < excl + cnt) {
+      int acc0 = excl;
+      for (int i = 0; i < 4; ++i) {
+        const int gg = t * 4 + i;
+        const int c = (gg < G) ? (p.off[gg + 1] - p.off[gg] + GB_TILE - 1) / GB_TILE * p.nt : 0;
+        if (tile < acc0 + c) {
+          s_tile[0] = gg;
+          s_tile[1] = tile - acc0;
+          break;
+        }
+        acc0 += c;
+      }
+    }
+    __syncthreads();
+    if (s_tile[0] < 0) return;  // past the last tile: uniform exit
+    grp = s_tile[0];
+    const int local = s_tile[1];
+    tc.r0 = (int64_t)p.off[grp] + (int64_t)(local / p.nt) * GB_TILE;
+    tc.c0 = (int64_t)(local % p.nt) * GB_TILE;
+    tc.rend = p.off[grp + 1];
+    const int blk = (FMT == FP4Q_NVFP4) ? 16 : 32;
+    tc.bq = p.bq + (int64_t)grp * p.N * (p.K >> 1);
+    tc.bs = p.bs + (int64_t)grp * p.N * (p.K / blk);
+    tc.bsel = p.bsel + (int64_t)grp * ((p.N + 15) / 16) * p.nc * 1024;
+  } else {
+    // XCD-aware, then grouped along M for L2 reuse
+    const int T = p.mt * p.nt;
+    int tile = blockIdx.x;
+    if ((T & 7) == 0) tile = (blockIdx.x & 7) * (T >> 3) + (blockIdx.x >> 3);
+    const int gsize = GB_GROUP_M * p.nt;
+    const int gid = tile / gsize, first_m = gid * GB_GROUP_M;
+    const int gm = min(p.mt - first_m, GB_GROUP_M);
+    const int pid_m = first_m + (tile % gsize) % gm;
+    const int pid_n = (tile % gsize) / gm;
+    tc.r0 = (int64_t)pid_m * GB_TILE;
+    tc.c0 = (int64_t)pid_n * GB_TILE;
+    tc.rend = p.M;
+    tc.bq = p.bq;
+    tc.bs = p.bs;
+    tc.bsel = p.bsel;
+  }
+  const int64_t r0 = tc.r0, c0 = tc.c0;
 
   const int nk = p.nk, ns = p.nk + p.nc;
   float tx = 1.0f, tw = 1.0f;
   if (FMT == FP4Q_NVFP4) {
-    tx = *p.ats;
-    tw = *p.bts;
+    tx = p.ats[grp];
+    tw = p.bts[grp];
   }
   auto stage = [&](int s) __attribute__((always_inline)) { return sStage + (s % 3) * SL::BYTES; };
 
-  issue_stage<FMT, TL>(p, 0, wave, lane, r0, c0, stage(0));
-  if (ns > 1) issue_stage<FMT, TL>(p, 1, wave, lane, r0, c0, stage(1));
+  const int nS = p.nS;
+  if (XS) {
+    // channel list and, per FP4 stage kt, the first list entry at or past
+    // 128 kt (the list is ascending); B_S starts zeroed (entries past |S|
+    // stay zero).  Before any stage is in flight, so the fences cost nothing.
+    const int32_t* chg = p.chan + (GR ? (int64_t)grp * nS : 0);
+    for (int j = t; j < nS; j += GB_T) sChan[j] = chg[j];
+    for (int i = t; i < GB_XS_BYTES / 16; i += GB_T)
+      reinterpret_cast<u32x4*>(sBS)[i] = u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();
+    for (int kt = t; kt <= nk; kt += GB_T) {
+      int lo = 0, hi = nS;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (sChan[mid] < 128 * kt) lo = mid + 1; else hi = mid;
+      }
+      sFirst[kt] = lo;
+    }
+    __syncthreads();
+  }
+
+  issue_stage<FMT, TL, XS>(p, 0, wave, lane, tc, stage(0));
+  if (ns > 1) issue_stage<FMT, TL, XS>(p, 1, wave, lane, tc, stage(1));
 
   f32x16 acc[2][4];
 #pragma unroll
@@ -440,12 +546,12 @@ __global__ void __launch_bounds__(GB_T, 1) k_gemm_big(BigArgs args) {
     else
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
-    if (s + 2 < ns) issue_stage<FMT, TL>(p, s + 2, wave, lane, r0, c0, stage(s + 2));
+    if (s + 2 < ns) issue_stage<FMT, TL, XS>(p, s + 2, wave, lane, tc, stage(s + 2));
   };
   for (int s = 0; s < nk; ++s) {
     pipe(s);
     Frag f;
-    read_frags<FMT, true>(stage(s), wm, wn, lane, f);
+    read_frags<FMT, true>(stage(s), stage(s) + SL::B, wm, wn, lane, f);
     compute_fp4<FMT>(acc, f, lane);
     if (FMT == FP4Q_MXFP4) {
       // every LDS read of the stage is issued before its first MFMA, so the
@@ -453,6 +559,32 @@ __global__ void __launch_bounds__(GB_T, 1) k_gemm_big(BigArgs args) {
       // decode temporaries leave no registers for that)
       __builtin_amdgcn_sched_group_barrier(0x100, 18, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    }
+    if (XS) {
+      // B_S of the stage's channels: thread t takes column t % 256 of every
+      // second channel; code byte and block scale from the stage's B tile,
+      // e2m1 * scale (exact in BF16) into the compensation layout
+      const uint8_t* st = stage(s);
+      const int j1 = __builtin_amdgcn_readfirstlane(sFirst[s + 1]);
+      const int col = t & 255;
+      for (int j = __builtin_amdgcn_readfirstlane(sFirst[s]) + (t >> 8); j < j1; j += 2) {
+        const int pos = sChan[j] & 127;
+        const uint32_t byte =
+            st[SL::B + (col >> 4) * GB_GRP + ((pos >> 5) * 16 + (col & 15)) * 16 + ((pos >> 1) & 15)];
+        const uint32_t code = (pos & 1) ? (byte >> 4) : (byte & 15u);
+        float sv;
+        if (FMT == FP4Q_NVFP4) {
+          sv = e4m3_value(st[SL::SB + ((pos >> 6) * 256 + col) * 4 + ((pos >> 4) & 3)]);
+        } else {
+          const uint32_t c8 = st[SL::SB + col * 4 + (pos >> 5)];
+          sv = c8 ? __uint_as_float(c8 << 23) : __uint_as_float(0x00400000u);
+        }
+        const float v = e2m1_mag_value(code) * sv;
+        const int jj = j & 31;
+        *reinterpret_cast<uint16_t*>(sBS + (j >> 5) * GB_DATA + (col >> 4) * GB_GRP +
+                                     ((jj >> 3) * 16 + (col & 15)) * 16 + (jj & 7) * 2) =
+            (uint16_t)((__float_as_uint(v) >> 16) | ((code & 8u) << 12));
+      }
     }
   }
   if (FMT == FP4Q_NVFP4) {
@@ -465,7 +597,8 @@ __global__ void __launch_bounds__(GB_T, 1) k_gemm_big(BigArgs args) {
   for (int s = nk; s < ns; ++s) {
     pipe(s);
     Frag f;
-    read_frags<FMT, false>(stage(s), wm, wn, lane, f);
+    read_frags<FMT, false>(stage(s), XS ? sBS + (s - nk) * GB_DATA : stage(s) + SL::B, wm, wn,
+                           lane, f);
     compute_comp(acc, f);
     __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
@@ -475,7 +608,8 @@ __global__ void __launch_bounds__(GB_T, 1) k_gemm_big(BigArgs args) {
   // + e % 4, column 128 wn + 32 j + l % 32.
   const int hi = lane >> 5, l31 = lane & 31;
   const int64_t rw = r0 + wm * 64, cw = c0 + wn * 128;
-  const bool interior = (r0 + GB_TILE <= p.M) && (c0 + GB_TILE <= p.N);
+  const int64_t rend = tc.rend;
+  const bool interior = (r0 + GB_TILE <= rend) && (c0 + GB_TILE <= p.N);
   const bool vec = interior && (p.ldy % 8) == 0 && (reinterpret_cast<uintptr_t>(p.y) & 15) == 0;
   if (vec) {
     // Each wave stages 32 x 64 pieces (two blocks) in its own LDS region and
@@ -528,7 +662,7 @@ __global__ void __launch_bounds__(GB_T, 1) k_gemm_big(BigArgs args) {
       for (int e = 0; e < 16; ++e) {
         const int64_t row = rw + 32 * i + 8 * (e >> 2) + 4 * hi + (e & 3);
         const int64_t col = cw + 32 * j + l31;
-        if (row < p.M && col < p.N) {
+        if (row < rend && col < p.N) {
           const float v = acc[i][j][e] * tw;
           if (p.y_bf16)
             reinterpret_cast<uint16_t*>(p.y)[row * p.ldy + col] = (uint16_t)f32_to_bf16_rne(v);
@@ -543,32 +677,38 @@ __global__ void __launch_bounds__(GB_T, 1) k_gemm_big(BigArgs args) {
 // excluded; exact) for n < ceil16(N), j < ceil32(|S|), zero past N or |S|,
 // as 1 KB blocks per (16-row group G, 32-channel chunk C) at (G nc + C) * 1024,
 // inside which channels 8c .. 8c+7 of row 16G + r are the 16 bytes at
-// (16c + r) * 16.  One wave writes one block; lane l = 16c + r.
+// (16c + r) * 16.  Grouped: one such array per group, back to back, from
+// the group's weights and channel list.  One wave writes one block; lane
+// l = 16c + r.
 template <int FMT, bool TL>
 __global__ void __launch_bounds__(256) k_gather_bsel(const uint8_t* __restrict__ bq,
                                                      const uint8_t* __restrict__ bs, int64_t N,
                                                      int64_t K, const int32_t* __restrict__ chan,
-                                                     int nS, int nc, int64_t nblocks,
+                                                     int nS, int nc, int64_t nblocks, int G,
                                                      uint8_t* __restrict__ bsel) {
   constexpr int BLK = (FMT == FP4Q_NVFP4) ? 16 : 32;
   const int lane = threadIdx.x & 63;
   const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (blk >= nblocks) return;
-  const int64_t G = blk / nc;
-  const int C = (int)(blk - G * nc);
-  const int64_t n = 16 * G + (lane & 15);
+  if (blk >= nblocks * G) return;
+  const int64_t grp = blk / nblocks, lb = blk - grp * nblocks;
+  const uint8_t* gq = bq + grp * N * (K >> 1);
+  const uint8_t* gs = bs + grp * N * (K / BLK);
+  const int32_t* gc = chan + grp * nS;
+  const int64_t Gr = lb / nc;
+  const int C = (int)(lb - Gr * nc);
+  const int64_t n = 16 * Gr + (lane & 15);
   const int64_t nn = n < N ? n : N - 1;
   const int j0 = GB_CS * C + 8 * (lane >> 4);
   // every load is unconditional (clamped row and channel), so all of a
   // lane's loads are in flight together; out-of-range entries become 0
   int c[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) c[e] = chan[j0 + e < nS ? j0 + e : nS - 1];
+  for (int e = 0; e < 8; ++e) c[e] = gc[j0 + e < nS ? j0 + e : nS - 1];
   uint32_t byte[8], sc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    byte[e] = bq[code_off(TL, nn, c[e] >> 1, K)];
-    sc[e] = bs[scale_off<FMT>(TL, nn, c[e] / BLK, K)];
+    byte[e] = gq[code_off(TL, nn, c[e] >> 1, K)];
+    sc[e] = gs[scale_off<FMT>(TL, nn, c[e] / BLK, K)];
   }
   uint32_t h[8];
 #pragma unroll
@@ -588,38 +728,57 @@ __global__ void __launch_bounds__(256) k_gather_bsel(const uint8_t* __restrict__
 
 // ---- host side ---------------------------------------------------------------
 
-bool big_gemm_eligible(int64_t M, int64_t N, int64_t K, int nS) {
-  // residual rows are brought in as 16-byte pieces of 8 channels
-  return M >= GB_TILE && N >= GB_TILE && K % 128 == 0 && nS % 8 == 0;
+// Residual rows are brought in as 16-byte pieces of 8 channels; in-kernel
+// extraction of B_S (|S| <= 96) needs the per-stage table (K <= 32768).
+static bool big_ok(int64_t K, int nS) {
+  return K % 128 == 0 && nS % 8 == 0 && (nS > GB_XS_MAX || K / 128 <= GB_XS_MAX_NK);
 }
 
+bool big_gemm_eligible(int64_t M, int64_t N, int64_t K, int nS) {
+  return M >= GB_TILE && N >= GB_TILE && big_ok(K, nS);
+}
+
+bool big_grouped_eligible(int64_t N, int64_t K, int nS) { return N >= GB_TILE && big_ok(K, nS); }
+
+// Only more than GB_XS_MAX channels use the gather kernel and its workspace.
 size_t big_gemm_workspace_bytes(int64_t N, int nS) {
-  if (nS <= 0) return 0;
+  if (nS <= GB_XS_MAX) return 0;
   const int64_t nc = (nS + GB_CS - 1) / GB_CS;
   return (size_t)(((N + 15) / 16) * nc * 1024);
 }
 
-template <int FMT>
-static void launch_big(const BigArgs& a, bool tiled, hipStream_t stream) {
-  dim3 grid((unsigned)(a.mt * a.nt));
-  if (tiled)
-    hipLaunchKernelGGL((k_gemm_big<FMT, true>), grid, dim3(GB_T), 0, stream, a);
-  else
-    hipLaunchKernelGGL((k_gemm_big<FMT, false>), grid, dim3(GB_T), 0, stream, a);
+template <int FMT, bool GR>
+static void launch_big(const BigArgs& a, bool tiled, unsigned grid, hipStream_t stream) {
+  const bool xs = a.nS > 0 && a.nS <= GB_XS_MAX;
+  if constexpr (GR) {  // grouped operands are row-major
+    if (xs)
+      hipLaunchKernelGGL((k_gemm_big<FMT, false, true, true>), dim3(grid), dim3(GB_T), 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_gemm_big<FMT, false, true, false>), dim3(grid), dim3(GB_T), 0, stream, a);
+  } else {
+    if (tiled && xs)
+      hipLaunchKernelGGL((k_gemm_big<FMT, true, false, true>), dim3(grid), dim3(GB_T), 0, stream, a);
+    else if (tiled)
+      hipLaunchKernelGGL((k_gemm_big<FMT, true, false, false>), dim3(grid), dim3(GB_T), 0, stream, a);
+    else if (xs)
+      hipLaunchKernelGGL((k_gemm_big<FMT, false, false, true>), dim3(grid), dim3(GB_T), 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_gemm_big<FMT, false, false, false>), dim3(grid), dim3(GB_T), 0, stream, a);
+  }
 }
 
 template <int FMT>
 static void launch_gather(bool tiled, const uint8_t* bq, const uint8_t* bs, int64_t N, int64_t K,
-                          const int32_t* chan, int nS, int nc, uint8_t* bsel,
+                          const int32_t* chan, int nS, int nc, int G, uint8_t* bsel,
                           hipStream_t stream) {
   const int64_t nblocks = ((N + 15) / 16) * nc;
-  dim3 grid((unsigned)((nblocks + 3) / 4));
+  dim3 grid((unsigned)((nblocks * G + 3) / 4));
   if (tiled)
     hipLaunchKernelGGL((k_gather_bsel<FMT, true>), grid, dim3(256), 0, stream, bq, bs, N, K, chan,
-                       nS, nc, nblocks, bsel);
+                       nS, nc, nblocks, G, bsel);
   else
     hipLaunchKernelGGL((k_gather_bsel<FMT, false>), grid, dim3(256), 0, stream, bq, bs, N, K,
-                       chan, nS, nc, nblocks, bsel);
+                       chan, nS, nc, nblocks, G, bsel);
 }
 
 int launch_gemm_big(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const uint8_t* aq,
@@ -628,15 +787,40 @@ int launch_gemm_big(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const 
                     void* y, int y_bf16, int64_t ldy, void* ws, hipStream_t stream) {
   const int nc = nS > 0 ? (nS + GB_CS - 1) / GB_CS : 0;
   uint8_t* bsel = static_cast<uint8_t*>(ws);
-  BigArgs a{M, N, K, aq, as, ats, bq, bs, bts, nS, resid, bsel, y, y_bf16, ldy,
+  BigArgs a{M, N, K, aq, as, ats, bq, bs, bts, nS, resid, bsel, chan, y, y_bf16, ldy,
             (int)((M + GB_TILE - 1) / GB_TILE), (int)((N + GB_TILE - 1) / GB_TILE),
-            (int)(K / 128), nc};
+            (int)(K / 128), nc, nullptr, 1};
+  const bool gather = nS > GB_XS_MAX;
+  const unsigned grid = (unsigned)(a.mt * a.nt);
   if (fmt == FP4Q_NVFP4) {
-    if (nc) launch_gather<FP4Q_NVFP4>(tiled, bq, bs, N, K, chan, nS, nc, bsel, stream);
-    launch_big<FP4Q_NVFP4>(a, tiled, stream);
+    if (gather) launch_gather<FP4Q_NVFP4>(tiled, bq, bs, N, K, chan, nS, nc, 1, bsel, stream);
+    launch_big<FP4Q_NVFP4, false>(a, tiled, grid, stream);
   } else {
-    if (nc) launch_gather<FP4Q_MXFP4>(tiled, bq, bs, N, K, chan, nS, nc, bsel, stream);
-    launch_big<FP4Q_MXFP4>(a, tiled, stream);
+    if (gather) launch_gather<FP4Q_MXFP4>(tiled, bq, bs, N, K, chan, nS, nc, 1, bsel, stream);
+    launch_big<FP4Q_MXFP4, false>(a, tiled, grid, stream);
+  }
+  return 0;
+}
+
+int launch_gemm_big_grouped(int fmt, int64_t total_rows, int64_t N, int64_t K,
+                            const int32_t* off, int G, const uint8_t* aq, const uint8_t* as,
+                            const float* ats, const uint8_t* bq, const uint8_t* bs,
+                            const float* bts, const int32_t* chan, int nS,
+                            const uint16_t* resid, void* y, int y_bf16, void* ws,
+                            hipStream_t stream) {
+  const int nc = nS > 0 ? (nS + GB_CS - 1) / GB_CS : 0;
+  uint8_t* bsel = static_cast<uint8_t*>(ws);
+  BigArgs a{total_rows, N, K, aq, as, ats, bq, bs, bts, nS, resid, bsel, chan, y, y_bf16, N,
+            0, (int)((N + GB_TILE - 1) / GB_TILE), (int)(K / 128), nc, off, G};
+  const bool gather = nS > GB_XS_MAX;
+  // every group adds at most one partial 256-row tile
+  const unsigned grid = (unsigned)(((total_rows + GB_TILE - 1) / GB_TILE + G) * a.nt);
+  if (fmt == FP4Q_NVFP4) {
+    if (gather) launch_gather<FP4Q_NVFP4>(false, bq, bs, N, K, chan, nS, nc, G, bsel, stream);
+    launch_big<FP4Q_NVFP4, true>(a, false, grid, stream);
+  } else {
+    if (gather) launch_gather<FP4Q_MXFP4>(false, bq, bs, N, K, chan, nS, nc, G, bsel, stream);
+    launch_big<FP4Q_MXFP4, true>(a, false, grid, stream);
   }
   return 0;
 }

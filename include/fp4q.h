@@ -186,17 +186,25 @@ int fp4q_gemm(fp4q_format_t fmt, fp4q_layout_t layout, int64_t M, int64_t N, int
  *   a_ts           device f32 [G] (NVFP4), NULL for MXFP4
  *   b_q, b_s       [G, N, K/2], [G, N, K/blk]
  *   b_ts           device f32 [G] (NVFP4), NULL for MXFP4
- *   chan_idx       device int32 [G, n_chan]; resid bf16 [total_rows, n_chan]
+ *   chan_idx       device int32 [G, n_chan]; resid bf16 [total_rows, n_chan],
+ *                  16-byte aligned
  *   y              out [total_rows, N] (row stride N)
+ *   workspace      device scratch of fp4q_grouped_gemm_workspace_bytes()
+ *                  bytes, 16-byte aligned (may be NULL when that is 0): the
+ *                  gathered compensation weights of every group, as BF16
  *
  * Empty groups produce nothing.  K must be a multiple of 128.
+ * FP4Q_ERR_WORKSPACE if a needed workspace is missing, small or misaligned.
  * ------------------------------------------------------------------------ */
+size_t fp4q_grouped_gemm_workspace_bytes(fp4q_format_t fmt, int64_t total_rows, int64_t N,
+                                         int64_t K, int32_t num_groups, int32_t n_chan);
+
 int fp4q_grouped_gemm(fp4q_format_t fmt, int64_t total_rows, int64_t N, int64_t K,
                       const int32_t* group_offsets, int32_t num_groups, const uint8_t* a_q,
                       const uint8_t* a_s, const float* a_ts, const uint8_t* b_q,
                       const uint8_t* b_s, const float* b_ts, const int32_t* chan_idx,
                       int32_t n_chan, const uint16_t* resid, void* y, fp4q_dtype_t y_dtype,
-                      void* stream);
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Exact three-way MXFP4 error decomposition ("Decomposing MXFP4

@@ -103,15 +103,17 @@ def test_gemm_rejects(L):
     assert g(L, layout=5) == INVALID
     assert g(L, layout=1, K=144) == UNSUPPORTED
     assert g(L, nS=8, chan=A, R=ctypes.c_void_p(0x20008)) == INVALID   # resid 16-byte aligned
-    # the 256x256-tile path gathers the compensation weights into a workspace
-    need = L.fp4q_gemm_workspace_bytes(0, 1, 512, 512, 256, 32)
-    assert need == (512 // 16) * 1 * 1024
-    assert L.fp4q_gemm_workspace_bytes(0, 1, 512, 512, 256, 64) == (512 // 16) * 2 * 1024
-    assert L.fp4q_gemm_workspace_bytes(0, 1, 512, 500, 256, 40) == (512 // 16) * 2 * 1024
-    assert L.fp4q_gemm_workspace_bytes(0, 1, 512, 512, 256, 0) == 0
-    assert L.fp4q_gemm_workspace_bytes(0, 1, 64, 11008, 2048, 64) == 0    # decode shape
+    # the 256x256-tile path takes up to 96 compensation channels from its own
+    # B tiles; more are gathered into a workspace first
+    need = L.fp4q_gemm_workspace_bytes(0, 1, 512, 512, 256, 128)
+    assert need == (512 // 16) * 4 * 1024
+    assert L.fp4q_gemm_workspace_bytes(0, 1, 512, 512, 256, 104) == (512 // 16) * 4 * 1024
+    assert L.fp4q_gemm_workspace_bytes(0, 1, 512, 500, 256, 136) == (512 // 16) * 5 * 1024
+    for nS in (0, 8, 32, 40, 96):
+        assert L.fp4q_gemm_workspace_bytes(0, 1, 512, 512, 256, nS) == 0
+    assert L.fp4q_gemm_workspace_bytes(0, 1, 64, 11008, 2048, 128) == 0   # decode shape
     assert L.fp4q_gemm_workspace_bytes(0, 1, 512, 512, 256, 12) == 0      # |S| % 8: other path
-    big = dict(M=512, N=512, K=256, nS=32, chan=A, R=B, ldy=512)
+    big = dict(M=512, N=512, K=256, nS=128, chan=A, R=B, ldy=512)
     assert g(L, **big) == WORKSPACE
     assert g(L, **big, ws=A, wsb=need - 1) == WORKSPACE
     assert g(L, **big, ws=ctypes.c_void_p(0x10008), wsb=need) == WORKSPACE
@@ -141,11 +143,25 @@ def test_packed_bytes(L):
 
 def test_grouped_gemm_rejects(L):
     f = L.fp4q_grouped_gemm
-    assert f(0, 10, 8, 256, None, 2, A, A, B, B, B, B, None, 0, None, A, 0, None) == INVALID
-    assert f(0, 10, 8, 256, A, 0, A, A, B, B, B, B, None, 0, None, A, 0, None) == INVALID
-    assert f(0, 10, 8, 256, A, 5000, A, A, B, B, B, B, None, 0, None, A, 0, None) == UNSUPPORTED
-    # MXFP4 takes no tensor scales
-    assert f(1, 10, 8, 256, A, 2, A, A, B, B, B, None, None, 0, None, A, 0, None) == INVALID
+
+    def gg(fmt=0, rows=10, N=8, K=256, off=A, G=2, ats=B, bts=B, chan=None, nS=0, R=None, ws=None,
+           wsb=0):
+        return f(fmt, rows, N, K, off, G, A, A, ats, B, B, bts, chan, nS, R, A, 0, ws, wsb, None)
+
+    assert gg(off=None) == INVALID
+    assert gg(G=0) == INVALID
+    assert gg(G=5000) == UNSUPPORTED
+    assert gg(fmt=1, bts=None) == INVALID        # MXFP4 takes no tensor scales
+    # the staged 256-column path gathers every group's compensation weights
+    # when there are more than 96 channels
+    need = L.fp4q_grouped_gemm_workspace_bytes(0, 1000, 512, 256, 4, 128)
+    assert need == 4 * (512 // 16) * 4 * 1024
+    assert L.fp4q_grouped_gemm_workspace_bytes(0, 1000, 512, 256, 4, 32) == 0
+    assert L.fp4q_grouped_gemm_workspace_bytes(0, 1000, 128, 256, 4, 128) == 0   # N < 256
+    assert L.fp4q_grouped_gemm_workspace_bytes(0, 1000, 512, 256, 4, 0) == 0
+    big = dict(rows=1000, N=512, K=256, G=4, chan=A, nS=128, R=B)
+    assert gg(**big) == WORKSPACE
+    assert gg(**big, ws=A, wsb=need - 16) == WORKSPACE
 
 
 def test_error_decompose_rejects(L):

@@ -139,6 +139,28 @@ def test_large_tiles_compensation_stages(orc, fmt, M, N, K, nS):
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("chan_kind", ["one_step", "edges"])
+def test_large_tiles_clustered_channels(orc, fmt, chan_kind):
+    """256x256-tile path with the compensated channels bunched into one
+    128-column step (every channel of a compensation stage comes from the
+    same B tile) or at the first and last columns of K."""
+    need_gpu()
+    M, N, K = 512, 512, 512
+    if chan_kind == "one_step":
+        chan = np.arange(256, 352, dtype=np.int32)                 # 96 channels, step 2
+    else:
+        chan = np.array([0, 1, 2, 127, 128, 383, 510, 511], np.int32)
+    nS = len(chan)
+    say(f"gemm large-tile clustered channels fmt {fmt} {chan_kind} nS{nS}")
+    d = dense_case(M, K, N, n_out=4, seed=700 + nS)
+    qa, qb = _prep(orc, fmt, d, chan)
+    yo, ya = _oracle_full(orc, fmt, qa, qb, chan)
+    for layout in (fq.ROWMAJOR, fq.TILED):
+        y = to_host(_gpu_gemm(fmt, qa, qb, chan, layout=layout))
+        assert_gemm_close(y, yo, ya)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
 def test_large_tiles_bf16_and_ldy(orc, fmt):
     """256x256-tile path: vector epilogue (FP32, BF16) and the element-wise
     one (row stride not a multiple of 8)."""

@@ -78,11 +78,14 @@ def test_graph_decode_step(fmt, layout):
     _check_replays(run, outputs, scramble)
 
 
-def test_graph_grouped_layer():
+@pytest.mark.parametrize("N,nS", [(160, 8), (512, 8), (512, 104)])
+def test_graph_grouped_layer(N, nS):
+    """Staged grouped path with the compensation weights taken in-kernel
+    (|S| <= 96) and gathered into the workspace (|S| > 96)."""
     dev = need_gpu()
-    say("graph replay: grouped quantize + grouped gemm (NVFP4)")
+    say(f"graph replay: grouped quantize + grouped gemm (NVFP4), N {N}, |S| {nS}")
     fmt = fq.NVFP4
-    K, N, nS = 256, 160, 8
+    K = 256
     off_h = np.array([0, 40, 40, 41, 200, 333], np.int32)
     G = off_h.size - 1
     rows = int(off_h[-1])
@@ -97,12 +100,15 @@ def test_graph_grouped_layer():
     bt = torch.cat([q["tscale"] for q in ws])
     b = _bufs(fmt, rows, K, nS, G, dev)
     y = torch.empty((rows, N), dtype=torch.float32, device=dev)
+    gwsb = fq.grouped_gemm_workspace_bytes(fmt, rows, N, K, G, nS)
+    gws = torch.empty(gwsb, dtype=torch.uint8, device=dev) if gwsb else None
+    assert (gwsb > 0) == (N >= 256 and nS > 96)
 
     def run():
         fq.quantize_into(fmt, fq.ROWMAJOR, x, off, G, chan, nS, b["q"], b["s"], b["t"], b["r"],
                          b["ws"])
         fq.grouped_gemm_into(fmt, rows, N, K, off, G, b["q"], b["s"], b["t"], bq, bs, bt, chan, nS,
-                             b["r"], y, 0)
+                             b["r"], y, 0, gws)
 
     def outputs():
         return [b["q"], b["s"], b["t"], b["r"], y]

@@ -55,6 +55,25 @@ def test_small_groups(orc, fmt, nS):
     _run(orc, fmt, x, off, chan, wts)
 
 
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("nS", [0, 8, 40, 104])
+def test_groups_large_tiles(orc, fmt, nS):
+    """The staged 256x256-tile grouped path (N >= 256): empty, single-row,
+    sub-tile and multi-tile experts, tiles ending mid-group and a partial
+    last column tile; |S| off the 32-channel stage size."""
+    need_gpu()
+    say(f"grouped large-tile fmt {fmt} nS {nS}")
+    K, N = 384, 300
+    off = np.array([0, 0, 1, 257, 257, 300, 900, 1000], np.int32)
+    G = off.size - 1
+    x = dense_case(int(off[-1]), K, 8, n_out=3, seed=53)["x"]
+    wts = [dense_case(1, K, N, seed=80 + g)["wt"] for g in range(G)]
+    rng = np.random.default_rng(4)
+    chan = (np.sort(np.stack([rng.choice(K, nS, replace=False) for _ in range(G)]), 1)
+            .astype(np.int32) if nS else None)
+    _run(orc, fmt, x, off, chan, wts)
+
+
 def test_all_rows_in_one_group(orc):
     need_gpu()
     off = np.array([0, 0, 0, 150, 150], np.int32)
