@@ -20,9 +20,11 @@
 //    then one v_pk_mul_f16 by the E4M3 block scale: exact in f16) for
 //    v_mfma_f32_16x16x32_f16; MXFP4 feeds the packed codes and E8M0 scales
 //    to v_mfma_scale_f32_16x16x128_f8f6f4 directly;
-//  * the compensation weights B[n, S_j] are taken from the weight registers
-//    of the wave whose K step holds channel S_j (decoded to bf16, exact) and
-//    written to LDS; R[:, S] is staged in LDS at the start (16-byte loads).
+//  * the compensation weights B[n, S_j] come from the wave whose K step holds
+//    channel S_j: it copies the step's weight bytes to a wave-private LDS
+//    slot; then the 64 lanes decode four channels x 16 columns at a time
+//    (to bf16, exact), with no branches; R[:, S] is staged in LDS at the
+//    start (16-byte loads).
 //    After the eight K-partial sums meet in LDS, waves 0-3 (16 rows each)
 //    add R B_S with v_mfma_f32_16x16x16_bf16 and store
 //    y = tw * (tx * main + comp).
@@ -34,6 +36,7 @@
 namespace fp4q {
 
 typedef float v4f32s __attribute__((ext_vector_type(4)));
+typedef float v2f32s __attribute__((ext_vector_type(2)));
 typedef int i32x8s __attribute__((ext_vector_type(8)));
 typedef _Float16 h8s __attribute__((ext_vector_type(8)));
 typedef _Float16 h2s __attribute__((ext_vector_type(2)));
@@ -74,9 +77,10 @@ __device__ __forceinline__ h8s sk_decode8(uint32_t w, h2s s) {
   return r;
 }
 
-__device__ __forceinline__ h2s sk_scale2(uint32_t code) {
-  _Float16 v = (_Float16)e4m3_value(code & 0xFFu);
-  return h2s{v, v};
+// The two E4M3 scale bytes in the low half of `codes`, as f16 (exact: every
+// E4M3 value, subnormals included, is an f16 value).
+__device__ __forceinline__ h2s sk_scales2(uint32_t codes) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(codes, 1.0f, false);
 }
 
 // Registers of one K step for one wave.  Lane (lr = lane % 16, q = lane / 16)
@@ -161,13 +165,6 @@ __device__ __forceinline__ void load_step(const SkinnyArgs& p, int kt, int lane,
   }
 }
 
-// Element e (0..31) of a lane's 16 packed bytes: its 4-bit code.
-__device__ __forceinline__ uint32_t nibble_of(u32x4 v, int e) {
-  const int d = e >> 3;  // wave-uniform
-  const uint32_t word = d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w;
-  return (word >> (4 * (e & 7))) & 15u;
-}
-
 // Bytes of one wave-private scale slot: weight rows then activation rows.
 template <int FMT> struct SlotLayout {
   static constexpr int PER_ROW = (FMT == FP4Q_NVFP4) ? 8 : 4;  // scale bytes per row per step
@@ -178,9 +175,9 @@ template <int FMT> struct SlotLayout {
 // Multiply one K step into the accumulators; take the compensation weights
 // of the channels that fall in it.
 template <int FMT>
-__device__ __forceinline__ void process_step(const Step& st, int kt, uint8_t* slot, int lane,
-                                             int my_ch, int nS, uint16_t* sB,
-                                             v4f32s (&acc)[4][SK_CG]) {
+__device__ __forceinline__ void process_step(const Step& st, int kt, uint8_t* slot,
+                                             uint8_t* cslot, int lane, int my_ch, int nS,
+                                             uint16_t* sB, v4f32s (&acc)[4][SK_CG]) {
   using L = SlotLayout<FMT>;
   const int q = lane >> 4, lr = lane & 15;
   // redistribute the scale bytes: lane (lr, q) needs those of its rows for
@@ -205,15 +202,21 @@ __device__ __forceinline__ void process_step(const Step& st, int kt, uint8_t* sl
                 : (uint32_t)slot[L::X_OFF + (16 * a + lr) * 4 + q];
 
   if (FMT == FP4Q_NVFP4) {
+    // lane (lr, q): scales of blocks 2q (elements 32q .. +15) and 2q + 1
+    h2s wsp[SK_CG], xsp[4];
+#pragma unroll
+    for (int g = 0; g < SK_CG; ++g) wsp[g] = sk_scales2(ws[g]);
+#pragma unroll
+    for (int a = 0; a < 4; ++a) xsp[a] = sk_scales2(xs[a]);
     // sub-step s: lane (lr, q) holds elements 32q + 8s .. +7 of the step
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       h8s db[SK_CG];
 #pragma unroll
-      for (int g = 0; g < SK_CG; ++g) db[g] = sk_decode8(st.w[g][s], sk_scale2(ws[g] >> (8 * (s >> 1))));
+      for (int g = 0; g < SK_CG; ++g) db[g] = sk_decode8(st.w[g][s], (s >> 1) ? wsp[g].yy : wsp[g].xx);
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const h8s da = sk_decode8(st.x[a][s], sk_scale2(xs[a] >> (8 * (s >> 1))));
+        const h8s da = sk_decode8(st.x[a][s], (s >> 1) ? xsp[a].yy : xsp[a].xx);
 #pragma unroll
         for (int g = 0; g < SK_CG; ++g)
           acc[a][g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(da, db[g], acc[a][g], 0, 0, 0);
@@ -233,28 +236,38 @@ __device__ __forceinline__ void process_step(const Step& st, int kt, uint8_t* sl
       }
     }
   }
-  // compensation weights of the channels in this step (S ascending: a run
-  // of the lanes of my_ch); the lanes of group q_t hold the byte
+  // compensation weights of the channels in this step: S is ascending, so
+  // they are the entries [j0, j1) of the lanes of my_ch.  The step's weight
+  // bytes go to the wave-private slot as rows of 64 bytes; lane (r, u) then
+  // takes channel jb + u and the columns 16g + r.  One wave's LDS operations
+  // complete in order, so the slot needs no barrier.  Lanes past j1 write
+  // the unused padding column SK_MAXS of sB.
   if (nS > 0) {
-    uint64_t m = __ballot(my_ch >= 0 && (my_ch >> 7) == kt);
-    while (m) {
-      const int j = __builtin_ctzll(m);
-      m &= m - 1;
-      const int ch = __builtin_amdgcn_readlane(my_ch, j);
-      const int pos = ch & 127, qt = pos >> 5, e = pos & 31;
-      if (q == qt) {
+    const uint64_t m = __ballot(my_ch >= 0 && (my_ch >> 7) == kt);
+    if (m) {
+      const int j0 = __builtin_ctzll(m), j1 = 64 - __builtin_clzll(m);
+#pragma unroll
+      for (int g = 0; g < SK_CG; ++g)
+        *reinterpret_cast<u32x4*>(cslot + (16 * g + lr) * 64 + 16 * q) = st.w[g];
+      for (int jb = j0; jb < j1; jb += 4) {
+        const int j = jb + q;
+        const bool ok = j < j1;
+        const int pos = __builtin_amdgcn_ds_bpermute((ok ? j : j0) << 2, my_ch) & 127;
+        const int jw = ok ? j : SK_MAXS;
 #pragma unroll
         for (int g = 0; g < SK_CG; ++g) {
-          const uint32_t code = nibble_of(st.w[g], e);
+          const int n = 16 * g + lr;
+          const uint32_t byte = cslot[n * 64 + (pos >> 1)];
+          const uint32_t c8 = (FMT == FP4Q_NVFP4) ? slot[n * 8 + (pos >> 4)] : slot[n * 4 + (pos >> 5)];
+          const v2f32s pr = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(byte, 1.0f, 0);
+          const float e = (pos & 1) ? pr[1] : pr[0];  // signed E2M1 value
           float sv;
-          if (FMT == FP4Q_NVFP4) {
-            sv = e4m3_value(ws[g] >> (8 * (e >> 4)));
-          } else {
-            const uint32_t c8 = ws[g] & 0xFFu;
+          if (FMT == FP4Q_NVFP4)
+            sv = e4m3_value(c8);
+          else
             sv = c8 ? __uint_as_float(c8 << 23) : __uint_as_float(0x00400000u);
-          }
-          const float v = e2m1_mag_value(code) * sv;  // exact, and exact in bf16
-          sB[(16 * g + lr) * SK_SRS + j] = (uint16_t)((__float_as_uint(v) >> 16) | ((code & 8u) << 12));
+          // exact, and exact in bf16 (at most 6 significant bits)
+          sB[n * SK_SRS + jw] = (uint16_t)(__float_as_uint(e * sv) >> 16);
         }
       }
     }
@@ -268,6 +281,7 @@ __global__ void __launch_bounds__(SK_T, 1) k_gemm_skinny(SkinnyArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t sScale[SK_WAVES * 2 * L::BYTES];  // 2 slots per wave
   __shared__ __attribute__((aligned(16))) uint16_t sR[SK_M * SK_SRS];              // R[m][j]
   __shared__ __attribute__((aligned(16))) uint16_t sB[SK_COLS * SK_SRS];           // B_S[n][j]
+  __shared__ __attribute__((aligned(16))) uint8_t sCode[SK_WAVES * SK_COLS * 64];    // 24 KB
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int q = lane >> 4, lr = lane & 15;
@@ -275,9 +289,9 @@ __global__ void __launch_bounds__(SK_T, 1) k_gemm_skinny(SkinnyArgs p) {
   const int nk = (int)(p.K / 128);
   const int nS = p.nS;
 
-  // ---- prologue.  No barrier: everything here is per wave, and the
-  // residual rows (held in registers through the main loop) reach LDS just
-  // before the reduction barrier.  Every load is unconditional (clamped
+  // ---- prologue.  No barrier: everything here is per wave (the residual
+  // rows are staged in LDS while the operand stream is in flight, and are
+  // read after the reduction barrier).  Every load is unconditional (clamped
   // indices, or a valid stand-in address when there are no channels) so the
   // compiler can count the loads in flight and wait only for the data used.
   float tx = 1.0f, tw = 1.0f;
@@ -285,10 +299,15 @@ __global__ void __launch_bounds__(SK_T, 1) k_gemm_skinny(SkinnyArgs p) {
     tx = *p.ats;
     tw = *p.bts;
   }
-  // lane j holds channel S_j (valid for j < nS); issued first, so waiting
-  // for it never waits for the operand stream
+  // lane j holds channel S_j (valid for j < nS); this and the residual
+  // load are issued first, so waiting for them never waits for the operand
+  // stream.  R [M][nS] bf16, contiguous, 16-byte aligned, M nS a multiple of
+  // 8: thread t takes elements 8t .. 8t+7 (of at most 4096).
   const int my_ch_raw = *(nS > 0 ? p.chan + (lane < nS ? lane : nS - 1)
                                  : reinterpret_cast<const int32_t*>(p.aq));
+  const int rtot = (int)p.M * nS, e0 = 8 * t;
+  const u32x4 rv = *reinterpret_cast<const u32x4*>(
+      nS > 0 ? p.resid + (e0 < rtot ? e0 : rtot - 8) : reinterpret_cast<const uint16_t*>(p.aq));
   // tiled layout: this lane's weight-row scale offset within a step (rows
   // exist up to the 64-row padding)
   int64_t wso = 0;
@@ -302,11 +321,15 @@ __global__ void __launch_bounds__(SK_T, 1) k_gemm_skinny(SkinnyArgs p) {
   Step s0, s1;
   load_step<FMT, TL>(p, wave < nk ? wave : nk - 1, lane, col0, wso, s0);
   load_step<FMT, TL>(p, wave + SK_WAVES < nk ? wave + SK_WAVES : nk - 1, lane, col0, wso, s1);
-  // R [M][nS] bf16, contiguous, 16-byte aligned, M nS a multiple of 8:
-  // elements 8t .. 8t+7 of the (at most 4096)
-  const int rtot = (int)p.M * nS, e0 = 8 * t;
-  const u32x4 rv = *reinterpret_cast<const u32x4*>(
-      nS > 0 ? p.resid + (e0 < rtot ? e0 : rtot - 8) : reinterpret_cast<const uint16_t*>(p.aq));
+  if (nS > 0 && e0 < rtot) {
+    const uint32_t w4[4] = {rv.x, rv.y, rv.z, rv.w};
+    int row = e0 / nS, j = e0 - row * nS;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      sR[row * SK_SRS + j] = (uint16_t)(w4[k >> 1] >> (16 * (k & 1)));
+      if (++j == nS) { j = 0; ++row; }
+    }
+  }
 
   v4f32s acc[4][SK_CG];
 #pragma unroll
@@ -317,34 +340,23 @@ __global__ void __launch_bounds__(SK_T, 1) k_gemm_skinny(SkinnyArgs p) {
   // ---- K steps wave, wave + 8, wave + 16, ...: two steps in flight
   uint8_t* slot0 = sScale + (wave * 2 + 0) * L::BYTES;
   uint8_t* slot1 = sScale + (wave * 2 + 1) * L::BYTES;
+  uint8_t* cslot = sCode + wave * (SK_COLS * 64);
   const int my_ch = (nS > 0 && lane < nS) ? my_ch_raw : -1;
   if (nk <= 2 * SK_WAVES) {
     // K <= 2048: both steps are already in flight
-    if (wave < nk) process_step<FMT>(s0, wave, slot0, lane, my_ch, nS, sB, acc);
-    if (wave + SK_WAVES < nk) process_step<FMT>(s1, wave + SK_WAVES, slot1, lane, my_ch, nS, sB, acc);
+    if (wave < nk) process_step<FMT>(s0, wave, slot0, cslot, lane, my_ch, nS, sB, acc);
+    if (wave + SK_WAVES < nk) process_step<FMT>(s1, wave + SK_WAVES, slot1, cslot, lane, my_ch, nS, sB, acc);
   } else {
     for (int kt = wave; kt < nk; kt += 2 * SK_WAVES) {
-      process_step<FMT>(s0, kt, slot0, lane, my_ch, nS, sB, acc);
+      process_step<FMT>(s0, kt, slot0, cslot, lane, my_ch, nS, sB, acc);
       if (kt + 2 * SK_WAVES < nk) load_step<FMT, TL>(p, kt + 2 * SK_WAVES, lane, col0, wso, s0);
       if (kt + SK_WAVES < nk) {
-        process_step<FMT>(s1, kt + SK_WAVES, slot1, lane, my_ch, nS, sB, acc);
+        process_step<FMT>(s1, kt + SK_WAVES, slot1, cslot, lane, my_ch, nS, sB, acc);
         if (kt + 3 * SK_WAVES < nk) load_step<FMT, TL>(p, kt + 3 * SK_WAVES, lane, col0, wso, s1);
       }
     }
   }
 
-  // (keep the staging below the main loop: it waits for the residual load,
-  // the last one issued)
-  asm volatile("" ::: "memory");
-  if (nS > 0 && e0 < rtot) {
-    const uint32_t w4[4] = {rv.x, rv.y, rv.z, rv.w};
-    int row = e0 / nS, j = e0 - row * nS;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      sR[row * SK_SRS + j] = (uint16_t)(w4[k >> 1] >> (16 * (k & 1)));
-      if (++j == nS) { j = 0; ++row; }
-    }
-  }
 
   // ---- K-partial sums meet in LDS; wave a (< 4) then owns rows 16a .. 16a+15
 #pragma unroll
@@ -361,25 +373,33 @@ __global__ void __launch_bounds__(SK_T, 1) k_gemm_skinny(SkinnyArgs p) {
     for (int w2 = 1; w2 < SK_WAVES; ++w2) out[g] += red[((w2 * 4 + wave) * SK_CG + g) * 64 + lane];
   }
 
-  // ---- compensation: y = tw * (tx * main + comp).  Entries j >= nS of
-  // both operands are masked to zero (the LDS there is not written).
-  if (FMT == FP4Q_NVFP4) {
+  // ---- compensation: y = tw * (tx * main + comp).  All SK_MAXS / 16
+  // chunks run, with entries j >= nS of both operands masked to zero (the
+  // LDS there is not written), so every LDS read is issued up front.
+  if (nS > 0) {
+    v4f32s comp[SK_CG];
+#pragma unroll
+    for (int g = 0; g < SK_CG; ++g) comp[g] = v4f32s{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < SK_MAXS / 16; ++c) {
+      const int jq = 16 * c + 4 * q;
+      const u32x2 m2 = u32x2{(jq + 0 < nS ? 0xFFFFu : 0u) | (jq + 1 < nS ? 0xFFFF0000u : 0u),
+                             (jq + 2 < nS ? 0xFFFFu : 0u) | (jq + 3 < nS ? 0xFFFF0000u : 0u)};
+      // A: R[16 wave + lr][jq .. jq+3]; B: B_S[16 g + lr][jq .. jq+3]
+      const s4s ra = __builtin_bit_cast(
+          s4s, *reinterpret_cast<const u32x2*>(sR + (16 * wave + lr) * SK_SRS + jq) & m2);
+#pragma unroll
+      for (int g = 0; g < SK_CG; ++g) {
+        const s4s rb = __builtin_bit_cast(
+            s4s, *reinterpret_cast<const u32x2*>(sB + (16 * g + lr) * SK_SRS + jq) & m2);
+        comp[g] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ra, rb, comp[g], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < SK_CG; ++g) out[g] = out[g] * tx + comp[g];
+  } else if (FMT == FP4Q_NVFP4) {
 #pragma unroll
     for (int g = 0; g < SK_CG; ++g) out[g] *= tx;
-  }
-  for (int j0 = 0; j0 < nS; j0 += 16) {
-    const int jq = j0 + 4 * q;
-    const u32x2 m2 = u32x2{(jq + 0 < nS ? 0xFFFFu : 0u) | (jq + 1 < nS ? 0xFFFF0000u : 0u),
-                           (jq + 2 < nS ? 0xFFFFu : 0u) | (jq + 3 < nS ? 0xFFFF0000u : 0u)};
-    // A: R[16 wave + lr][jq .. jq+3]; B: B_S[16 g + lr][jq .. jq+3]
-    const s4s ra = __builtin_bit_cast(
-        s4s, *reinterpret_cast<const u32x2*>(sR + (16 * wave + lr) * SK_SRS + jq) & m2);
-#pragma unroll
-    for (int g = 0; g < SK_CG; ++g) {
-      const s4s rb = __builtin_bit_cast(
-          s4s, *reinterpret_cast<const u32x2*>(sB + (16 * g + lr) * SK_SRS + jq) & m2);
-      out[g] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ra, rb, out[g], 0, 0, 0);
-    }
   }
 
   // ---- store: lane holds rows 16 wave + 4q + e, column col0 + 16g + lr
