@@ -421,7 +421,9 @@ __global__ void __launch_bounds__(GB_T, 1) k_gemm_big(BigArgs args) {
   static_assert(GB_W * 32 * GB_EP_STRIDE * 4 <= 3 * SL::BYTES, "epilogue staging");
 
   const BigArgs& p = args;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  // the wave index is made visibly uniform, so block-address arithmetic
+  // stays in scalar registers
+  const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
   TileCtx tc;
@@ -524,8 +526,21 @@ __global__ void __launch_bounds__(GB_T, 1) k_gemm_big(BigArgs args) {
     __syncthreads();
   }
 
-  issue_stage<FMT, TL, XS>(p, 0, wave, lane, tc, stage(0));
-  if (ns > 1) issue_stage<FMT, TL, XS>(p, 1, wave, lane, tc, stage(1));
+  // MXFP4 runs the two waves of each SIMD half a stage apart (below); only
+  // waves 0..3 load, each the share of two waves
+  const bool late = FMT == FP4Q_MXFP4 && wave >= GB_W / 2;
+  auto issue = [&](int s) __attribute__((always_inline)) {
+    if (FMT == FP4Q_MXFP4) {
+      issue_stage<FMT, TL, XS>(p, s, 2 * wave, lane, tc, stage(s));
+      issue_stage<FMT, TL, XS>(p, s, 2 * wave + 1, lane, tc, stage(s));
+    } else {
+      issue_stage<FMT, TL, XS>(p, s, wave, lane, tc, stage(s));
+    }
+  };
+  if (!late) {
+    issue(0);
+    if (ns > 1) issue(1);
+  }
 
   f32x16 acc[2][4];
 #pragma unroll
@@ -548,18 +563,7 @@ __global__ void __launch_bounds__(GB_T, 1) k_gemm_big(BigArgs args) {
     lds_barrier();
     if (s + 2 < ns) issue_stage<FMT, TL, XS>(p, s + 2, wave, lane, tc, stage(s + 2));
   };
-  for (int s = 0; s < nk; ++s) {
-    pipe(s);
-    Frag f;
-    read_frags<FMT, true>(stage(s), stage(s) + SL::B, wm, wn, lane, f);
-    compute_fp4<FMT>(acc, f, lane);
-    if (FMT == FP4Q_MXFP4) {
-      // every LDS read of the stage is issued before its first MFMA, so the
-      // wave waits for LDS once per stage, not once per fragment (NVFP4's
-      // decode temporaries leave no registers for that)
-      __builtin_amdgcn_sched_group_barrier(0x100, 18, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
-    }
+  auto extract = [&](int s) __attribute__((always_inline)) {
     if (XS) {
       // B_S of the stage's channels: thread t takes column t % 256 of every
       // second channel; code byte and block scale from the stage's B tile,
@@ -586,22 +590,69 @@ __global__ void __launch_bounds__(GB_T, 1) k_gemm_big(BigArgs args) {
             (uint16_t)((__float_as_uint(v) >> 16) | ((code & 8u) << 12));
       }
     }
-  }
-  if (FMT == FP4Q_NVFP4) {
+  };
+  auto comp_src = [&](int s) __attribute__((always_inline)) {
+    return XS ? sBS + (s - nk) * GB_DATA : stage(s) + SL::B;
+  };
+  if constexpr (FMT == FP4Q_MXFP4) {
+    // Ping-pong.  Each stage is two barrier intervals: LDS fragment reads,
+    // then MFMAs.  Waves 4..7 (the second wave of each SIMD) pass one extra
+    // barrier first, so they multiply while the first wave of their SIMD
+    // reads, and read while it multiplies: a wave's own LDS reads do not
+    // overlap its MFMAs, but they do overlap the other wave's, so the matrix
+    // pipe stays busy.  Waves 0..3 issue all loads and wait for them before
+    // the barrier that opens a stage's read interval, so the stage has
+    // landed for both groups.  The buffer of stage s - 1 is free once the
+    // late waves have read it, which is before that barrier too.
+    constexpr int L2 = 2 * L;
+    auto open = [&](int s) __attribute__((always_inline)) {
+      if (!late) {
+        if (s + 1 < ns)
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L2) : "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      lds_barrier();
+      if (!late && s + 2 < ns) issue(s + 2);
+    };
+    if (late) lds_barrier();
+    for (int s = 0; s < nk; ++s) {
+      open(s);
+      Frag f;
+      read_frags<FMT, true>(stage(s), stage(s) + SL::B, wm, wn, lane, f);
+      extract(s);
+      lds_barrier();
+      compute_fp4<FMT>(acc, f, lane);
+    }
+    for (int s = nk; s < ns; ++s) {
+      open(s);
+      Frag f;
+      read_frags<FMT, false>(stage(s), comp_src(s), wm, wn, lane, f);
+      lds_barrier();
+      compute_comp(acc, f);
+    }
+    if (!late) lds_barrier();
+  } else {
+    for (int s = 0; s < nk; ++s) {
+      pipe(s);
+      Frag f;
+      read_frags<FMT, true>(stage(s), stage(s) + SL::B, wm, wn, lane, f);
+      compute_fp4<FMT>(acc, f, lane);
+      extract(s);
+    }
     // y = t_w (t_x main + comp): scale the main sum once, before R B_S
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] *= tx;
-  }
-  for (int s = nk; s < ns; ++s) {
-    pipe(s);
-    Frag f;
-    read_frags<FMT, false>(stage(s), XS ? sBS + (s - nk) * GB_DATA : stage(s) + SL::B, wm, wn,
-                           lane, f);
-    compute_comp(acc, f);
-    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    for (int s = nk; s < ns; ++s) {
+      pipe(s);
+      Frag f;
+      read_frags<FMT, false>(stage(s), comp_src(s), wm, wn, lane, f);
+      compute_comp(acc, f);
+      __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    }
   }
 
   // ---- epilogue.  acc[i][j][e] is row 64 wm + 32 i + 8 (e / 4) + 4 (l / 32)
