@@ -230,12 +230,16 @@ __device__ __forceinline__ float div_rn(float x, float d, float y) {
 // nibble), by gfx950's v_cvt_scalef32_pk_fp4_f32 with scale 1: nearest-even
 // on the E2M1 grid, saturating at 6, sign kept (also for -0 and values that
 // round to zero) -- the same decisions as the threshold rule of the grid.
-__device__ __forceinline__ uint32_t e2m1_pack8(const float (&v)[8]) {
+// With an E8M0 scale 2^e (passed as the float whose exponent field is the
+// code, 0.0f for code 0) the instruction divides by 2^e exactly before
+// rounding, for every code 0..254 (checked on the GPU against pre-scaled
+// inputs), which saves the MXFP4 path its eight multiplies.
+__device__ __forceinline__ uint32_t e2m1_pack8(const float (&v)[8], float scale = 1.0f) {
   uint32_t p = 0;
-  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[0], v[1], 1.0f, 0);
-  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[2], v[3], 1.0f, 1);
-  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[4], v[5], 1.0f, 2);
-  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[6], v[7], 1.0f, 3);
+  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[0], v[1], scale, 0);
+  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[2], v[3], scale, 1);
+  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[4], v[5], scale, 2);
+  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[6], v[7], scale, 3);
   return p;
 }
 
@@ -261,7 +265,7 @@ __device__ __forceinline__ void quantize_chunk(u32x4 v, bool active, bool tiled,
   for (int k = 0; k < 8; ++k) xs[k] = __uint_as_float((k & 1) ? (w[k >> 1] & 0xFFFF0000u) : (w[k >> 1] << 16));
 
   float d, sb = 0.0f, qv[8];
-  uint32_t sc;
+  uint32_t sc, packed;
   if (FMT == FP4Q_NVFP4) {
     const float vs = (amax / 6.0f) / t;
     sc = e4m3_encode(vs);
@@ -278,18 +282,16 @@ __device__ __forceinline__ void quantize_chunk(u32x4 v, bool active, bool tiled,
 #pragma unroll
       for (int k = 0; k < 8; ++k) qv[k] = xs[k] * 0.0f;  // signed zero: magnitude code 0
     }
+    packed = e2m1_pack8(qv);
   } else {
     const int e = mx_exponent(amax);
     sc = (uint32_t)(e + 127);
     d = exp2i(e);
-    const float inv_pow2 = exp2i(-e);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) qv[k] = xs[k] * inv_pow2;  // exact
+    packed = e2m1_pack8(xs, __uint_as_float(sc << 23));  // x / 2^e, exact
   }
   if (!active) return;
   if ((cc & (CPB - 1)) == 0) scales[scale_off<FMT>(tiled, row, cc / CPB, cols)] = (uint8_t)sc;
 
-  const uint32_t packed = e2m1_pack8(qv);
   *reinterpret_cast<uint32_t*>(q + code_off(tiled, row, 4 * cc, cols)) = packed;
 
   // residual on the selected channels of this chunk
@@ -346,6 +348,34 @@ __global__ void __launch_bounds__(NT) k_quantize(
     }
   };
 
+  // Row and column chunk of this thread's U chunks: one division for the
+  // first, then steps of NT chunks (a chunk past the end gets a row past the
+  // last one, so it stays inactive).
+  uint32_t rowu[U], ccu[U];
+  rc_of(base + threadIdx.x, rowu[0], ccu[0]);
+  if (TO && NT == 256) {
+    // tiled order: NT = 256 chunks is one 1 KB block further
+    const uint32_t w = threadIdx.x;
+    uint32_t rg = rowu[0] >> 4, bk = ccu[0] >> 4;
+#pragma unroll
+    for (int u = 1; u < U; ++u) {
+      if (++bk == nbk) { bk = 0; ++rg; }
+      rowu[u] = rg * 16 + (w >> 4);
+      ccu[u] = bk * 16 + (w & 15u);
+    }
+  } else if (!TO) {
+    const uint32_t drow = (uint32_t)NT / cpr, dcc = (uint32_t)NT - drow * cpr;
+#pragma unroll
+    for (int u = 1; u < U; ++u) {
+      rowu[u] = rowu[u - 1] + drow;
+      ccu[u] = ccu[u - 1] + dcc;
+      if (ccu[u] >= cpr) { ccu[u] -= cpr; ++rowu[u]; }
+    }
+  } else {
+#pragma unroll
+    for (int u = 1; u < U; ++u) rc_of(base + u * NT + threadIdx.x, rowu[u], ccu[u]);
+  }
+
   // this thread's chunks go out first (a clamped in-range address past the
   // end, so no branch separates the loads)
   u32x4 v[U];
@@ -353,11 +383,9 @@ __global__ void __launch_bounds__(NT) k_quantize(
   for (int u = 0; u < U; ++u) {
     const uint32_t c = base + u * NT + threadIdx.x;
     if (TO) {
-      uint32_t row, cc;
-      rc_of(c < total ? c : total - 1, row, cc);
-      row = row < (uint32_t)rows ? row : (uint32_t)rows - 1;
+      const uint32_t row = rowu[u] < (uint32_t)rows ? rowu[u] : (uint32_t)rows - 1;
       v[u] = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(gr.x + (int64_t)row * gr.ldx + (int64_t)cc * 8));
+          reinterpret_cast<const u32x4*>(gr.x + (int64_t)row * gr.ldx + (int64_t)ccu[u] * 8));
     } else {
       v[u] = load_chunk(gr, c < total ? c : total - 1);
     }
@@ -389,8 +417,7 @@ __global__ void __launch_bounds__(NT) k_quantize(
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const uint32_t c = base + u * NT + threadIdx.x;
-    uint32_t row, cc;
-    rc_of(c < total ? c : 0u, row, cc);
+    uint32_t row = rowu[u], cc = ccu[u];
     const bool active = c < total && row < (uint32_t)rows;
     if (!active) row = cc = 0;
     int g = gA;
