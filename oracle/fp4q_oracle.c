@@ -39,6 +39,12 @@
  *  - Two codes per byte, even element in the low nibble.
  *  - Residual R = bf16(x - deq(code)) on the chosen channels only.
  *  - GEMM: Y = deq(Xq) * deq(Wq)^T + R[:,S] * deq(Wq)[:,S]^T, in FP64.
+ *  - Second-pass residual (the explainer's section 2.2 B: the high-residual
+ *    channels are quantized a second time and the correction term is added
+ *    to the quantized output): R[:,S] itself quantized by the same rule, as
+ *    an M x |S| tensor with blocks along the selected-channel index j and,
+ *    for NVFP4, its own tensor scale; the compensation term is then
+ *    deq(Q(R)) * deq(Wq)[:,S]^T.
  *
  * Every FP32 step of the quantizer is one IEEE binary32 operation with
  * round-to-nearest-even; build with -O2 -ffp-contract=off, no fast-math.
@@ -278,12 +284,27 @@ static double deq(int fmt, const uint8_t* qm, const uint8_t* sm, double ts, int6
     return orc_e2m1_value(code) * s;
 }
 
+/* The residual operand of the compensation term: BF16 values R[m][j], or
+ * (second pass) the FP4 codes rq / block scales rs / tensor scale rts of
+ * R quantized as an M x nS tensor. */
+typedef struct {
+    const uint16_t* R;
+    const uint8_t* rq;
+    const uint8_t* rs;
+    double rts;
+} ResidOperand;
+
+static double resid_value(int fmt, const ResidOperand* ro, int32_t nS, int64_t m, int32_t j) {
+    if (ro->rq) return deq(fmt, ro->rq, ro->rs, ro->rts, nS, m, j);
+    return (double)orc_bf16_value(ro->R[m * nS + j]);
+}
+
 /* One output element: y = sum_k A[m,k] B[n,k] + sum_j R[m,j] B[n,S_j], with
  * yabs the same sum over absolute values of every term. */
-static void gemm_point(int fmt, int64_t K, const uint8_t* aq, const uint8_t* as, double ats,
-                       const uint8_t* bq, const uint8_t* bs, double bts, const int32_t* S,
-                       int32_t nS, const uint16_t* R, int64_t m, int64_t n, double* y,
-                       double* yabs) {
+static void gemm_point_r(int fmt, int64_t K, const uint8_t* aq, const uint8_t* as, double ats,
+                         const uint8_t* bq, const uint8_t* bs, double bts, const int32_t* S,
+                         int32_t nS, const ResidOperand* ro, int64_t m, int64_t n, double* y,
+                         double* yabs) {
     double acc = 0.0, aabs = 0.0;
     for (int64_t k = 0; k < K; ++k) {
         double p = deq(fmt, aq, as, ats, K, m, k) * deq(fmt, bq, bs, bts, K, n, k);
@@ -291,12 +312,20 @@ static void gemm_point(int fmt, int64_t K, const uint8_t* aq, const uint8_t* as,
         aabs += fabs(p);
     }
     for (int32_t j = 0; j < nS; ++j) {
-        double p = (double)orc_bf16_value(R[m * nS + j]) * deq(fmt, bq, bs, bts, K, n, S[j]);
+        double p = resid_value(fmt, ro, nS, m, j) * deq(fmt, bq, bs, bts, K, n, S[j]);
         acc += p;
         aabs += fabs(p);
     }
     *y = acc;
     *yabs = aabs;
+}
+
+static void gemm_point(int fmt, int64_t K, const uint8_t* aq, const uint8_t* as, double ats,
+                       const uint8_t* bq, const uint8_t* bs, double bts, const int32_t* S,
+                       int32_t nS, const uint16_t* R, int64_t m, int64_t n, double* y,
+                       double* yabs) {
+    const ResidOperand ro = {R, NULL, NULL, 0.0};
+    gemm_point_r(fmt, K, aq, as, ats, bq, bs, bts, S, nS, &ro, m, n, y, yabs);
 }
 
 /* Dense GEMM at chosen points (pm[i], pn[i]).  A = activations [M, K]
@@ -327,6 +356,43 @@ int orc_gemm_full(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* aq,
         for (int64_t n = 0; n < N; ++n)
             gemm_point(fmt, K, aq, as, ta, bq, bs, tb, S, nS, R, m, n, &y[m * N + n],
                        &yabs[m * N + n]);
+    return 0;
+}
+
+/* Dense GEMM at points with the second-pass (FP4) residual: rq [M, nS/2]
+ * codes, rs [M, nS/blk] block scales, rts its tensor scale (NVFP4; ignored
+ * for MXFP4). */
+int orc_gemm_points_r4(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* aq,
+                       const uint8_t* as, float ats, const uint8_t* bq, const uint8_t* bs,
+                       float bts, const int32_t* S, int32_t nS, const uint8_t* rq,
+                       const uint8_t* rs, float rts, const int64_t* pm, const int64_t* pn,
+                       int64_t npts, double* y, double* yabs) {
+    (void)M;
+    (void)N;
+    const int blk = (fmt == ORC_NVFP4) ? 16 : 32;
+    if (nS > 0 && (nS % blk != 0 || !rq || !rs)) return -1;
+    double ta = (fmt == ORC_NVFP4) ? ats : 1.0, tb = (fmt == ORC_NVFP4) ? bts : 1.0;
+    const ResidOperand ro = {NULL, rq, rs, (fmt == ORC_NVFP4) ? (double)rts : 1.0};
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t i = 0; i < npts; ++i)
+        gemm_point_r(fmt, K, aq, as, ta, bq, bs, tb, S, nS, &ro, pm[i], pn[i], &y[i], &yabs[i]);
+    return 0;
+}
+
+/* The same, every output: y, yabs [M, N] row-major. */
+int orc_gemm_full_r4(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* aq,
+                     const uint8_t* as, float ats, const uint8_t* bq, const uint8_t* bs, float bts,
+                     const int32_t* S, int32_t nS, const uint8_t* rq, const uint8_t* rs,
+                     float rts, double* y, double* yabs) {
+    const int blk = (fmt == ORC_NVFP4) ? 16 : 32;
+    if (nS > 0 && (nS % blk != 0 || !rq || !rs)) return -1;
+    double ta = (fmt == ORC_NVFP4) ? ats : 1.0, tb = (fmt == ORC_NVFP4) ? bts : 1.0;
+    const ResidOperand ro = {NULL, rq, rs, (fmt == ORC_NVFP4) ? (double)rts : 1.0};
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            gemm_point_r(fmt, K, aq, as, ta, bq, bs, tb, S, nS, &ro, m, n, &y[m * N + n],
+                         &yabs[m * N + n]);
     return 0;
 }
 

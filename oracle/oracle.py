@@ -85,6 +85,12 @@ def lib():
         L.orc_gemm_full.restype = ctypes.c_int
         L.orc_gemm_full.argtypes = [ctypes.c_int, i64, i64, i64, P, P, f32, P, P, f32, P, i32,
                                     P, P, P]
+        L.orc_gemm_points_r4.restype = ctypes.c_int
+        L.orc_gemm_points_r4.argtypes = [ctypes.c_int, i64, i64, i64, P, P, f32, P, P, f32, P, i32,
+                                         P, P, f32, P, P, i64, P, P]
+        L.orc_gemm_full_r4.restype = ctypes.c_int
+        L.orc_gemm_full_r4.argtypes = [ctypes.c_int, i64, i64, i64, P, P, f32, P, P, f32, P, i32,
+                                       P, P, f32, P, P]
         L.orc_grouped_gemm_points.restype = ctypes.c_int
         L.orc_grouped_gemm_points.argtypes = [ctypes.c_int, i64, i64, i64, P, i32, P, P, P, P, P,
                                               P, P, i32, P, P, P, i64, P, P]
@@ -199,6 +205,49 @@ def gemm_full(fmt, aq, as_, ats, bq, bs, bts, chan_idx, resid):
     ya = np.zeros((M, N), np.float64)
     lib().orc_gemm_full(fmt, M, N, 2 * K2, _p(aq), _p(as_), float(ats), _p(bq), _p(bs),
                         float(bts), _p(ci), nS, _p(R), _p(y), _p(ya))
+    return y, ya
+
+
+def quantize_residual(fmt: int, resid: np.ndarray):
+    """Second pass: the BF16 residual R [M, nS] quantized by the same rule as
+    an M x nS tensor (blocks along the selected-channel index; NVFP4 with
+    its own tensor scale).  Returns the quantize() dict of R."""
+    return quantize(fmt, resid)
+
+
+def gemm_points_r4(fmt, aq, as_, ats, bq, bs, bts, chan_idx, rq, rs, rts, pm, pn):
+    """gemm_points with the compensation term deq(Q(R)) B_S^T: rq [M, nS/2],
+    rs [M, nS/blk], rts the residual's tensor scale (NVFP4)."""
+    aq, as_, bq, bs = (_c(a, np.uint8) for a in (aq, as_, bq, bs))
+    M, K2 = aq.shape
+    N = bq.shape[0]
+    ci = _c(chan_idx, np.int32)
+    nS = 0 if ci is None else ci.size
+    rq, rs = _c(rq, np.uint8), _c(rs, np.uint8)
+    pm, pn = _c(pm, np.int64), _c(pn, np.int64)
+    y = np.zeros(pm.size, np.float64)
+    ya = np.zeros(pm.size, np.float64)
+    rc = lib().orc_gemm_points_r4(fmt, M, N, 2 * K2, _p(aq), _p(as_), float(ats), _p(bq), _p(bs),
+                                  float(bts), _p(ci), nS, _p(rq), _p(rs), float(rts), _p(pm),
+                                  _p(pn), pm.size, _p(y), _p(ya))
+    if rc != 0:
+        raise ValueError("oracle: |S| must be a multiple of the block size")
+    return y, ya
+
+
+def gemm_full_r4(fmt, aq, as_, ats, bq, bs, bts, chan_idx, rq, rs, rts):
+    aq, as_, bq, bs = (_c(a, np.uint8) for a in (aq, as_, bq, bs))
+    M, K2 = aq.shape
+    N = bq.shape[0]
+    ci = _c(chan_idx, np.int32)
+    nS = 0 if ci is None else ci.size
+    rq, rs = _c(rq, np.uint8), _c(rs, np.uint8)
+    y = np.zeros((M, N), np.float64)
+    ya = np.zeros((M, N), np.float64)
+    rc = lib().orc_gemm_full_r4(fmt, M, N, 2 * K2, _p(aq), _p(as_), float(ats), _p(bq), _p(bs),
+                                float(bts), _p(ci), nS, _p(rq), _p(rs), float(rts), _p(y), _p(ya))
+    if rc != 0:
+        raise ValueError("oracle: |S| must be a multiple of the block size")
     return y, ya
 
 
