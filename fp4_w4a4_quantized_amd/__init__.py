@@ -19,6 +19,9 @@ from .binding import (  # noqa: F401
     error_decompose_workspace_bytes,
     gemm,
     gemm_into,
+    gemm_residual_fp4,
+    gemm_residual_fp4_into,
+    gemm_residual_fp4_workspace_bytes,
     gemm_workspace_bytes,
     grouped_gemm,
     grouped_gemm_into,

@@ -81,6 +81,13 @@ def lib():
                                 i32, P, P, ctypes.c_int, i64, P, sz, P]
         L.fp4q_grouped_gemm_workspace_bytes.restype = sz
         L.fp4q_grouped_gemm_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i64, i32, i32]
+        L.fp4q_gemm_residual_fp4_workspace_bytes.restype = sz
+        L.fp4q_gemm_residual_fp4_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64,
+                                                             i64, i32]
+        L.fp4q_gemm_residual_fp4.restype = ctypes.c_int
+        L.fp4q_gemm_residual_fp4.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, P, P, P, P,
+                                             P, P, P, i32, P, P, P, P, ctypes.c_int, i64, P, sz,
+                                             P]
         L.fp4q_grouped_gemm.restype = ctypes.c_int
         L.fp4q_grouped_gemm.argtypes = [ctypes.c_int, i64, i64, i64, P, i32, P, P, P, P, P, P, P,
                                         i32, P, P, ctypes.c_int, P, sz, P]
@@ -125,6 +132,10 @@ def gemm_workspace_bytes(fmt, layout, M, N, K, n_chan) -> int:
     return lib().fp4q_gemm_workspace_bytes(fmt, layout, M, N, K, n_chan)
 
 
+def gemm_residual_fp4_workspace_bytes(fmt, layout, M, N, K, n_chan) -> int:
+    return lib().fp4q_gemm_residual_fp4_workspace_bytes(fmt, layout, M, N, K, n_chan)
+
+
 def grouped_gemm_workspace_bytes(fmt, total_rows, N, K, num_groups, n_chan) -> int:
     return lib().fp4q_grouped_gemm_workspace_bytes(fmt, total_rows, N, K, num_groups, n_chan)
 
@@ -151,6 +162,18 @@ def gemm_into(fmt, layout, M, N, K, a_q, a_s, a_ts, b_q, b_s, b_ts, chan_idx, n_
                          _ptr(b_ts), _ptr(chan_idx), n_chan, _ptr(resid), _ptr(y), y_dtype,
                          N if ldy is None else ldy, _ptr(workspace), ws_bytes, _stream(stream))
     _check("fp4q_gemm", rc)
+
+
+def gemm_residual_fp4_into(fmt, layout, M, N, K, a_q, a_s, a_ts, b_q, b_s, b_ts, chan_idx, n_chan,
+                           r_q, r_s, r_ts, y, y_dtype=OUT_F32, ldy=None, workspace=None,
+                           stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().fp4q_gemm_residual_fp4(fmt, layout, M, N, K, _ptr(a_q), _ptr(a_s), _ptr(a_ts),
+                                      _ptr(b_q), _ptr(b_s), _ptr(b_ts), _ptr(chan_idx), n_chan,
+                                      _ptr(r_q), _ptr(r_s), _ptr(r_ts), _ptr(y), y_dtype,
+                                      N if ldy is None else ldy, _ptr(workspace), ws_bytes,
+                                      _stream(stream))
+    _check("fp4q_gemm_residual_fp4", rc)
 
 
 def grouped_gemm_into(fmt, total_rows, N, K, group_offsets, num_groups, a_q, a_s, a_ts, b_q,
@@ -224,6 +247,26 @@ def gemm(fmt, a, b, chan_idx=None, y_dtype=OUT_F32, stream=None):
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
     gemm_into(fmt, layout, M, N, K, a["q"], a["scales"], a["tscale"], b["q"], b["scales"],
               b["tscale"], chan_idx, nS, a["resid"] if nS else None, y, y_dtype, N, ws, stream)
+    return y
+
+
+def gemm_residual_fp4(fmt, a, b, chan_idx, r, y_dtype=OUT_F32, stream=None):
+    """The compensated GEMM with the second-pass residual: a, b as for gemm();
+    r = quantize(fmt, a["resid"]) (row-major, the residual as an M x n_chan
+    tensor).  Returns Y [M, N]."""
+    M, K, layout = _shape(a)
+    N, Kb, layout_b = _shape(b)
+    if Kb != K or layout_b != layout:
+        raise ValueError("operands differ in K or layout")
+    nS = chan_idx.numel()
+    dev = a["q"].device
+    y = torch.empty((M, N), dtype=torch.float32 if y_dtype == OUT_F32 else torch.bfloat16,
+                    device=dev)
+    wsb = gemm_residual_fp4_workspace_bytes(fmt, layout, M, N, K, nS)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
+    gemm_residual_fp4_into(fmt, layout, M, N, K, a["q"], a["scales"], a["tscale"], b["q"],
+                           b["scales"], b["tscale"], chan_idx, nS, r["q"], r["scales"],
+                           r["tscale"], y, y_dtype, N, ws, stream)
     return y
 
 

@@ -157,8 +157,57 @@ int fp4q_gemm(fp4q_format_t fmt, fp4q_layout_t layout, int64_t M, int64_t N, int
     return FP4Q_ERR_WORKSPACE;
   clear_error();
   fp4q::launch_gemm(fmt, layout == FP4Q_LAYOUT_TILED, M, N, K, nullptr, 1, a_q, a_s, a_ts, b_q,
-                    b_s, b_ts, chan_idx, n_chan, resid, y, y_dtype == FP4Q_OUT_BF16, ldy,
+                    b_s, b_ts, chan_idx, n_chan, resid, nullptr, y, y_dtype == FP4Q_OUT_BF16, ldy,
                     workspace, static_cast<hipStream_t>(stream));
+  return check_launch();
+}
+
+static size_t deq_resid_bytes(int64_t M, int32_t n_chan) {
+  return (size_t)((M * n_chan * 2 + 255) / 256 * 256);
+}
+
+size_t fp4q_gemm_residual_fp4_workspace_bytes(fp4q_format_t fmt, fp4q_layout_t layout, int64_t M,
+                                              int64_t N, int64_t K, int32_t n_chan) {
+  if (M <= 0 || N <= 0 || K <= 0 || n_chan <= 0) return 0;
+  return deq_resid_bytes(M, n_chan) + fp4q_gemm_workspace_bytes(fmt, layout, M, N, K, n_chan);
+}
+
+int fp4q_gemm_residual_fp4(fp4q_format_t fmt, fp4q_layout_t layout, int64_t M, int64_t N,
+                           int64_t K, const uint8_t* a_q, const uint8_t* a_s, const float* a_ts,
+                           const uint8_t* b_q, const uint8_t* b_s, const float* b_ts,
+                           const int32_t* chan_idx, int32_t n_chan, const uint8_t* r_q,
+                           const uint8_t* r_s, const float* r_ts, void* y, fp4q_dtype_t y_dtype,
+                           int64_t ldy, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!layout_ok(layout) || !fmt_ok(fmt)) return FP4Q_ERR_INVALID;
+  if (n_chan < 0 || (n_chan > 0) != (r_q != nullptr) || (n_chan > 0) != (r_s != nullptr))
+    return FP4Q_ERR_INVALID;
+  if (n_chan % blk_of(fmt) != 0) return FP4Q_ERR_INVALID;
+  if (fmt == FP4Q_NVFP4 && (n_chan > 0) != (r_ts != nullptr)) return FP4Q_ERR_INVALID;
+  if (fmt == FP4Q_MXFP4 && r_ts) return FP4Q_ERR_INVALID;
+  const bool work = M > 0 && N > 0 && n_chan > 0;
+  const size_t need = work ? fp4q_gemm_residual_fp4_workspace_bytes(fmt, layout, M, N, K, n_chan)
+                           : 0;
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
+    return FP4Q_ERR_WORKSPACE;
+  // the decoded residual goes to the front of the workspace; it stands in
+  // for fp4q_gemm's resid in the shared validation (an empty product only
+  // needs a non-null stand-in, never read)
+  alignas(16) static const uint16_t kNoRows[8] = {};
+  uint16_t* rdeq = work ? static_cast<uint16_t*>(workspace) : nullptr;
+  const uint16_t* rval = work ? rdeq : (n_chan > 0 ? kNoRows : nullptr);
+  int rc = validate_gemm_common(fmt, N, K, a_q, a_s, a_ts, b_q, b_s, b_ts, chan_idx, n_chan,
+                                rval, y, y_dtype, M);
+  if (rc != FP4Q_OK) return rc;
+  if (ldy < N) return FP4Q_ERR_INVALID;
+  if ((M + 127) / 128 > (int64_t)UINT32_MAX || (N + 31) / 32 > 65535) return FP4Q_ERR_UNSUPPORTED;
+  if (M * (int64_t)n_chan / 8 >= ((int64_t)1 << 31)) return FP4Q_ERR_UNSUPPORTED;
+  clear_error();
+  void* gws = work ? static_cast<uint8_t*>(workspace) + deq_resid_bytes(M, n_chan) : nullptr;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (work) fp4q::launch_deq_resid(fmt, M, n_chan, r_q, r_s, rdeq, st);
+  fp4q::launch_gemm(fmt, layout == FP4Q_LAYOUT_TILED, M, N, K, nullptr, 1, a_q, a_s, a_ts, b_q,
+                    b_s, b_ts, chan_idx, n_chan, rval, r_ts, y, y_dtype == FP4Q_OUT_BF16, ldy, gws,
+                    st);
   return check_launch();
 }
 
@@ -187,7 +236,7 @@ int fp4q_grouped_gemm(fp4q_format_t fmt, int64_t total_rows, int64_t N, int64_t 
     return FP4Q_ERR_WORKSPACE;
   clear_error();
   fp4q::launch_gemm(fmt, false, total_rows, N, K, group_offsets, num_groups, a_q, a_s, a_ts, b_q,
-                    b_s, b_ts, chan_idx, n_chan, resid, y, y_dtype == FP4Q_OUT_BF16, N,
+                    b_s, b_ts, chan_idx, n_chan, resid, nullptr, y, y_dtype == FP4Q_OUT_BF16, N,
                     workspace, static_cast<hipStream_t>(stream));
   return check_launch();
 }

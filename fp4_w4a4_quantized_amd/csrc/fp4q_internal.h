@@ -23,11 +23,18 @@ enum GemmPath { PATH_GENERIC = 0, PATH_SKINNY = 1, PATH_BIG = 2 };
 GemmPath gemm_path(int64_t M, int64_t N, int64_t K, int nS);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int nS);
 
+// cts: device tensor scale of the compensation term (NVFP4 second-pass
+// residual), or null for 1: y = t_w (t_x main + cts comp).
 int launch_gemm(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const int32_t* off, int G,
                 const uint8_t* aq, const uint8_t* as, const float* ats, const uint8_t* bq,
                 const uint8_t* bs, const float* bts, const int32_t* chan, int nS,
-                const uint16_t* resid, void* y, int y_bf16, int64_t ldy, void* ws,
-                hipStream_t stream);
+                const uint16_t* resid, const float* cts, void* y, int y_bf16, int64_t ldy,
+                void* ws, hipStream_t stream);
+
+// Second-pass residual: BF16 e2m1 * block scale (exact; tensor scale
+// excluded) of the row-major FP4 residual rq [M, nS/2], rs [M, nS/blk].
+void launch_deq_resid(int fmt, int64_t M, int nS, const uint8_t* rq, const uint8_t* rs,
+                      uint16_t* out, hipStream_t stream);
 
 bool big_gemm_eligible(int64_t M, int64_t N, int64_t K, int nS);
 bool big_grouped_eligible(int64_t N, int64_t K, int nS);
@@ -42,13 +49,14 @@ int launch_gemm_big_grouped(int fmt, int64_t total_rows, int64_t N, int64_t K,
 int launch_gemm_big(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const uint8_t* aq,
                     const uint8_t* as, const float* ats, const uint8_t* bq, const uint8_t* bs,
                     const float* bts, const int32_t* chan, int nS, const uint16_t* resid,
-                    void* y, int y_bf16, int64_t ldy, void* ws, hipStream_t stream);
+                    const float* cts, void* y, int y_bf16, int64_t ldy, void* ws,
+                    hipStream_t stream);
 
 bool skinny_gemm_eligible(int64_t M, int64_t N, int64_t K, int nS);
 int launch_gemm_skinny(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const uint8_t* aq,
                        const uint8_t* as, const float* ats, const uint8_t* bq, const uint8_t* bs,
                        const float* bts, const int32_t* chan, int nS, const uint16_t* resid,
-                       void* y, int y_bf16, int64_t ldy, hipStream_t stream);
+                       const float* cts, void* y, int y_bf16, int64_t ldy, hipStream_t stream);
 
 size_t decompose_workspace_bytes(int64_t rows, int64_t cols);
 int launch_decompose(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,

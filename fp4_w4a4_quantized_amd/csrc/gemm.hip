@@ -54,6 +54,7 @@ struct GemmArgs {
   const int32_t* chan;
   int nS;
   const uint16_t* resid;
+  const float* cts;  // tensor scale of the compensation term, or null (1)
   void* y;
   int y_bf16;
   int64_t ldy;
@@ -299,11 +300,13 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs p) {
     __syncthreads();
   }
 
-  // ---- tensor scales (NVFP4): acc = tw * (tx * main + comp)
+  // ---- tensor scales (NVFP4): y = tw (tx main + c comp), run as
+  // (tw c) ((tx / c) main + comp); with c = 1 the factors are tw and tx exactly
   float tx = 1.0f, tw = 1.0f;
   if (FMT == FP4Q_NVFP4) {
-    tx = p.ats[GROUPED ? g : 0];
-    tw = p.bts[GROUPED ? g : 0];
+    const float c = p.cts ? *p.cts : 1.0f;
+    tx = p.ats[GROUPED ? g : 0] / c;
+    tw = p.bts[GROUPED ? g : 0] * c;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -391,12 +394,55 @@ size_t grouped_workspace_bytes(int64_t N, int64_t K, int G, int nS) {
   return big_grouped_eligible(N, K, nS) ? (size_t)G * big_gemm_workspace_bytes(N, nS) : 0;
 }
 
+// Second-pass residual decode: thread i takes elements 8i .. 8i+7 of the
+// row-major [M, nS] residual (one 32-bit code word, one block scale) and
+// writes e2m1 * block scale as BF16, exact (at most 6 significant bits; the
+// tensor scale is applied by the GEMM).
+template <int FMT>
+__global__ void __launch_bounds__(256) k_deq_resid(const uint8_t* __restrict__ rq,
+                                                   const uint8_t* __restrict__ rs, int64_t M,
+                                                   int nS, uint16_t* __restrict__ out) {
+  constexpr int BLK = (FMT == FP4Q_NVFP4) ? 16 : 32;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int per_row = nS >> 3;
+  if (i >= M * per_row) return;
+  const int64_t m = i / per_row;
+  const int j0 = (int)(i - m * per_row) * 8;
+  const uint8_t* cw = rq + m * (nS >> 1) + (j0 >> 1);
+  const uint32_t w = (uint32_t)cw[0] | ((uint32_t)cw[1] << 8) | ((uint32_t)cw[2] << 16) |
+                     ((uint32_t)cw[3] << 24);
+  const uint32_t c8 = rs[m * (nS / BLK) + j0 / BLK];
+  const float sv = (FMT == FP4Q_NVFP4)
+                       ? e4m3_value(c8)
+                       : (c8 ? __uint_as_float(c8 << 23) : __uint_as_float(0x00400000u));
+  uint32_t h[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t code = (w >> (4 * e)) & 15u;
+    h[e] = (__float_as_uint(e2m1_mag_value(code) * sv) >> 16) | ((code & 8u) << 12);
+  }
+  *reinterpret_cast<u32x4*>(out + m * nS + j0) =
+      u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+}
+
+void launch_deq_resid(int fmt, int64_t M, int nS, const uint8_t* rq, const uint8_t* rs,
+                      uint16_t* out, hipStream_t stream) {
+  const int64_t n = M * (nS >> 3);
+  if (n <= 0) return;
+  dim3 grid((unsigned)((n + 255) / 256));
+  if (fmt == FP4Q_NVFP4)
+    hipLaunchKernelGGL((k_deq_resid<FP4Q_NVFP4>), grid, dim3(256), 0, stream, rq, rs, M, nS, out);
+  else
+    hipLaunchKernelGGL((k_deq_resid<FP4Q_MXFP4>), grid, dim3(256), 0, stream, rq, rs, M, nS, out);
+}
+
 int launch_gemm(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const int32_t* off, int G,
                 const uint8_t* aq, const uint8_t* as, const float* ats, const uint8_t* bq,
                 const uint8_t* bs, const float* bts, const int32_t* chan, int nS,
-                const uint16_t* resid, void* y, int y_bf16, int64_t ldy, void* ws,
-                hipStream_t stream) {
-  GemmArgs a{M, N, K, off, G, aq, as, ats, bq, bs, bts, chan, nS, resid, y, y_bf16, ldy, tiled};
+                const uint16_t* resid, const float* cts, void* y, int y_bf16, int64_t ldy,
+                void* ws, hipStream_t stream) {
+  GemmArgs a{M, N, K, off, G, aq, as, ats, bq, bs, bts, chan, nS, resid, cts, y, y_bf16, ldy,
+             tiled};
   if (M == 0 || N == 0) return 0;
   if (off != nullptr && big_grouped_eligible(N, K, nS)) {
     launch_gemm_big_grouped(fmt, M, N, K, off, G, aq, as, ats, bq, bs, bts, chan, nS, resid, y,
@@ -412,12 +458,12 @@ int launch_gemm(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const int3
   }
   switch (gemm_path(M, N, K, nS)) {
     case PATH_SKINNY:
-      launch_gemm_skinny(fmt, tiled, M, N, K, aq, as, ats, bq, bs, bts, chan, nS, resid, y, y_bf16,
-                         ldy, stream);
+      launch_gemm_skinny(fmt, tiled, M, N, K, aq, as, ats, bq, bs, bts, chan, nS, resid, cts, y,
+                         y_bf16, ldy, stream);
       break;
     case PATH_BIG:
-      launch_gemm_big(fmt, tiled, M, N, K, aq, as, ats, bq, bs, bts, chan, nS, resid, y, y_bf16,
-                      ldy, ws, stream);
+      launch_gemm_big(fmt, tiled, M, N, K, aq, as, ats, bq, bs, bts, chan, nS, resid, cts, y,
+                      y_bf16, ldy, ws, stream);
       break;
     default:
       if (M <= 64) {

@@ -77,6 +77,7 @@ struct BigArgs {
   const uint16_t* resid;
   const uint8_t* bsel;  // gathered B_S, tiled BF16 (see k_gather_bsel)
   const int32_t* chan;  // channel lists (in-kernel extraction)
+  const float* cts;     // tensor scale of the compensation term, or null (1)
   void* y;
   int y_bf16;
   int64_t ldy;
@@ -498,10 +499,13 @@ __global__ void __launch_bounds__(GB_T, 1) k_gemm_big(BigArgs args) {
   const int64_t r0 = tc.r0, c0 = tc.c0;
 
   const int nk = p.nk, ns = p.nk + p.nc;
+  // y = t_w (t_x main + c comp), run as (t_w c) ((t_x / c) main + comp):
+  // with c = 1 both factors are exactly t_w and t_x
   float tx = 1.0f, tw = 1.0f;
   if (FMT == FP4Q_NVFP4) {
-    tx = p.ats[grp];
-    tw = p.bts[grp];
+    const float c = p.cts ? *p.cts : 1.0f;
+    tx = p.ats[grp] / c;
+    tw = p.bts[grp] * c;
   }
   auto stage = [&](int s) __attribute__((always_inline)) { return sStage + (s % 3) * SL::BYTES; };
 
@@ -835,10 +839,11 @@ static void launch_gather(bool tiled, const uint8_t* bq, const uint8_t* bs, int6
 int launch_gemm_big(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const uint8_t* aq,
                     const uint8_t* as, const float* ats, const uint8_t* bq, const uint8_t* bs,
                     const float* bts, const int32_t* chan, int nS, const uint16_t* resid,
-                    void* y, int y_bf16, int64_t ldy, void* ws, hipStream_t stream) {
+                    const float* cts, void* y, int y_bf16, int64_t ldy, void* ws,
+                    hipStream_t stream) {
   const int nc = nS > 0 ? (nS + GB_CS - 1) / GB_CS : 0;
   uint8_t* bsel = static_cast<uint8_t*>(ws);
-  BigArgs a{M, N, K, aq, as, ats, bq, bs, bts, nS, resid, bsel, chan, y, y_bf16, ldy,
+  BigArgs a{M, N, K, aq, as, ats, bq, bs, bts, nS, resid, bsel, chan, cts, y, y_bf16, ldy,
             (int)((M + GB_TILE - 1) / GB_TILE), (int)((N + GB_TILE - 1) / GB_TILE),
             (int)(K / 128), nc, nullptr, 1};
   const bool gather = nS > GB_XS_MAX;
@@ -861,7 +866,7 @@ int launch_gemm_big_grouped(int fmt, int64_t total_rows, int64_t N, int64_t K,
                             hipStream_t stream) {
   const int nc = nS > 0 ? (nS + GB_CS - 1) / GB_CS : 0;
   uint8_t* bsel = static_cast<uint8_t*>(ws);
-  BigArgs a{total_rows, N, K, aq, as, ats, bq, bs, bts, nS, resid, bsel, chan, y, y_bf16, N,
+  BigArgs a{total_rows, N, K, aq, as, ats, bq, bs, bts, nS, resid, bsel, chan, nullptr, y, y_bf16, N,
             0, (int)((N + GB_TILE - 1) / GB_TILE), (int)(K / 128), nc, off, G};
   const bool gather = nS > GB_XS_MAX;
   // every group adds at most one partial 256-row tile

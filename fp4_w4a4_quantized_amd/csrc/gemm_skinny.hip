@@ -61,6 +61,7 @@ struct SkinnyArgs {
   const int32_t* chan;
   int nS;
   const uint16_t* resid;
+  const float* cts;  // tensor scale of the compensation term, or null (1)
   void* y;
   int y_bf16;
   int64_t ldy;
@@ -395,8 +396,9 @@ __global__ void __launch_bounds__(SK_T, 1) k_gemm_skinny(SkinnyArgs p) {
         comp[g] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ra, rb, comp[g], 0, 0, 0);
       }
     }
+    const float cs = p.cts ? *p.cts : 1.0f;
 #pragma unroll
-    for (int g = 0; g < SK_CG; ++g) out[g] = out[g] * tx + comp[g];
+    for (int g = 0; g < SK_CG; ++g) out[g] = out[g] * tx + comp[g] * cs;
   } else if (FMT == FP4Q_NVFP4) {
 #pragma unroll
     for (int g = 0; g < SK_CG; ++g) out[g] *= tx;
@@ -429,8 +431,8 @@ bool skinny_gemm_eligible(int64_t M, int64_t N, int64_t K, int nS) {
 int launch_gemm_skinny(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const uint8_t* aq,
                        const uint8_t* as, const float* ats, const uint8_t* bq, const uint8_t* bs,
                        const float* bts, const int32_t* chan, int nS, const uint16_t* resid,
-                       void* y, int y_bf16, int64_t ldy, hipStream_t stream) {
-  SkinnyArgs a{M, N, K, aq, as, ats, bq, bs, bts, chan, nS, resid, y, y_bf16, ldy};
+                       const float* cts, void* y, int y_bf16, int64_t ldy, hipStream_t stream) {
+  SkinnyArgs a{M, N, K, aq, as, ats, bq, bs, bts, chan, nS, resid, cts, y, y_bf16, ldy};
   dim3 grid((unsigned)((N + SK_COLS - 1) / SK_COLS));
   if (fmt == FP4Q_NVFP4 && tiled)
     hipLaunchKernelGGL((k_gemm_skinny<FP4Q_NVFP4, true>), grid, dim3(SK_T), 0, stream, a);

@@ -177,6 +177,41 @@ int fp4q_gemm(fp4q_format_t fmt, fp4q_layout_t layout, int64_t M, int64_t N, int
               size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Compensated W4A4 GEMM with a second-pass FP4 residual.  Explainer of the
+ * QUADS paper, section 2.2 B: the high-residual channels are quantized a
+ * second time and that correction term is added to the quantized output.
+ * The residual R [M, n_chan] of the selected channels is itself quantized
+ * by fp4q_quantize (same format, row-major layout, blocks along the channel
+ * index j, NVFP4 with its own tensor scale), and
+ *
+ *   Y[m, n] = sum_k A[m, k] * B[n, k] + sum_j deq(R_q)[m, j] * B[n, S_j]
+ *
+ * Arguments as fp4q_gemm, except the residual:
+ *   r_q, r_s   FP4 residual from fp4q_quantize(ROWMAJOR) of R: [M, n_chan/2]
+ *              codes, [M, n_chan/blk] block scales (NULL iff n_chan == 0)
+ *   r_ts       device f32 [1] its tensor scale (NVFP4), NULL for MXFP4
+ *   workspace  device scratch of fp4q_gemm_residual_fp4_workspace_bytes()
+ *              bytes, 16-byte aligned: it receives deq(R_q) / r_ts as BF16
+ *              (exact: e2m1 times a block scale has at most 6 significant
+ *              bits) and then serves the GEMM as fp4q_gemm's workspace
+ *
+ * n_chan must be a multiple of the block size (16 NVFP4, 32 MXFP4), else
+ * FP4Q_ERR_INVALID.  Residual values must stay below 2^125 in magnitude (the
+ * largest MXFP4 block scale times 6 is outside BF16).  The tensor scale
+ * enters as y = t_w ((t_x / r_ts) main + comp) * r_ts, which differs from
+ * the exact sum by a few FP32 roundings of the main term.
+ * ------------------------------------------------------------------------ */
+size_t fp4q_gemm_residual_fp4_workspace_bytes(fp4q_format_t fmt, fp4q_layout_t layout, int64_t M,
+                                              int64_t N, int64_t K, int32_t n_chan);
+
+int fp4q_gemm_residual_fp4(fp4q_format_t fmt, fp4q_layout_t layout, int64_t M, int64_t N,
+                           int64_t K, const uint8_t* a_q, const uint8_t* a_s, const float* a_ts,
+                           const uint8_t* b_q, const uint8_t* b_s, const float* b_ts,
+                           const int32_t* chan_idx, int32_t n_chan, const uint8_t* r_q,
+                           const uint8_t* r_s, const float* r_ts, void* y, fp4q_dtype_t y_dtype,
+                           int64_t ldy, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Expert-grouped compensated GEMM (MoE layer; QUADS abstract: NVFP4 rollout
  * for Mixture-of-Experts).  Rows [off[g], off[g+1]) of the permuted
  * activations use expert g's weights, tensor scales and channel list:

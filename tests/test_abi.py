@@ -171,3 +171,28 @@ def test_error_decompose_rejects(L):
     assert f(0, A, 4, 64, 64, B, A, 1 << 20, None) == UNSUPPORTED  # NVFP4 split is not offered
     assert f(1, A, 4, 64, 64, B, None, 0, None) == WORKSPACE
     assert f(1, A, 4, 64, 64, B, A, 8, None) == WORKSPACE
+
+
+def g4(L, fmt=0, M=4, N=8, K=256, aq=A, as_=A, ats=B, bq=B, bs=B, bts=B, chan=A, nS=16, rq=B,
+       rs=B, rts=B, y=A, dt=0, ldy=8, layout=0, ws=A, wsb=1 << 20):
+    return L.fp4q_gemm_residual_fp4(fmt, layout, M, N, K, aq, as_, ats, bq, bs, bts, chan, nS, rq,
+                                    rs, rts, y, dt, ldy, ws, wsb, None)
+
+
+def test_gemm_residual_fp4_rejects(L):
+    assert g4(L, nS=8) == INVALID                 # not a whole NVFP4 block of channels
+    assert g4(L, fmt=1, ats=None, bts=None, rts=None, nS=16) == INVALID   # MXFP4 blocks are 32
+    assert g4(L, rts=None) == INVALID             # NVFP4 residual needs its tensor scale
+    assert g4(L, fmt=1, ats=None, bts=None, nS=32) == INVALID             # MXFP4 takes none
+    assert g4(L, rq=None) == INVALID
+    assert g4(L, rs=None) == INVALID
+    assert g4(L, ws=None) == WORKSPACE
+    assert g4(L, wsb=64) == WORKSPACE
+    assert g4(L, ws=ctypes.c_void_p(0x10008)) == WORKSPACE                 # misaligned
+    assert g4(L, layout=3) == INVALID
+    assert g4(L, chan=None) == INVALID
+    # workspace: the decoded residual (256-byte rounded) then the GEMM's own
+    assert L.fp4q_gemm_residual_fp4_workspace_bytes(0, 0, 4, 8, 256, 16) == 256
+    assert (L.fp4q_gemm_residual_fp4_workspace_bytes(1, 1, 512, 512, 256, 128)
+            == 512 * 128 * 2 + L.fp4q_gemm_workspace_bytes(1, 1, 512, 512, 256, 128))
+    assert L.fp4q_gemm_residual_fp4_workspace_bytes(0, 0, 4, 8, 256, 0) == 0
