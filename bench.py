@@ -47,6 +47,9 @@ def parse():
                    help="packed operand layout of the dense workloads (MoE is row-major)")
     p.add_argument("--out-dtype", choices=("f32", "bf16"), default="f32",
                    help="GEMM output type of the dense workloads")
+    p.add_argument("--residual", choices=("bf16", "fp4"), default="bf16",
+                   help="compensation residual of the dense workloads: BF16, or quantized a "
+                        "second time to the workload's FP4 format (fp4q_gemm_residual_fp4)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle baseline sample")
@@ -164,21 +167,45 @@ def main():
         ats = torch.empty(1, dtype=torch.float32, device=dev) if fmt == fq.NVFP4 else None
         ar = torch.empty((M, nS), dtype=torch.int16, device=dev) if nS else None
 
+        r4 = args.residual == "fp4"
+        if r4:
+            if nS == 0 or nS % blk:
+                sys.exit(f"--residual fp4 needs |S| a multiple of {blk} (this workload: {nS})")
+            # second pass: R [M, nS] quantized row-major, then the FP4-residual GEMM
+            rq = torch.empty((M, nS // 2), dtype=torch.uint8, device=dev)
+            rsc = torch.empty((M, nS // blk), dtype=torch.uint8, device=dev)
+            rts = torch.empty(1, dtype=torch.float32, device=dev) if fmt == fq.NVFP4 else None
+            rqws = torch.zeros(max(fq.quantize_workspace_bytes(fmt, M, nS, 1), 16),
+                               dtype=torch.uint8, device=dev)
+            gwsb = fq.gemm_residual_fp4_workspace_bytes(fmt, layout, M, N, K, nS)
+            gws = torch.empty(gwsb, dtype=torch.uint8, device=dev)
+
         def quant():
             fq.quantize_into(fmt, layout, x, None, 1, chan, nS, aq, asc, ats, ar, qws)
+            if r4:
+                fq.quantize_into(fmt, fq.ROWMAJOR, ar, None, 1, None, 0, rq, rsc, rts, None, rqws)
 
         def gemm(i):
             w = wcopies[i % n_rot]
-            fq.gemm_into(fmt, layout, M, N, K, aq, asc, ats, w["q"], w["scales"], w["tscale"],
-                         chan, nS, ar, ys[i % n_rot], ydt, N, gws)
+            if r4:
+                fq.gemm_residual_fp4_into(fmt, layout, M, N, K, aq, asc, ats, w["q"], w["scales"],
+                                          w["tscale"], chan, nS, rq, rsc, rts, ys[i % n_rot], ydt,
+                                          N, gws)
+            else:
+                fq.gemm_into(fmt, layout, M, N, K, aq, asc, ats, w["q"], w["scales"],
+                             w["tscale"], chan, nS, ar, ys[i % n_rot], ydt, N, gws)
 
         flops = 2.0 * M * N * K
-        gemm_bytes = (M * K // 2 + M * K // blk + M * nS * 2 + nS * 4 + w_bytes + y_bytes +
+        r_bytes = (M * nS // 2 + M * nS // blk + (4 if fmt == fq.NVFP4 else 0)) if r4 else M * nS * 2
+        gemm_bytes = (M * K // 2 + M * K // blk + r_bytes + nS * 4 + w_bytes + y_bytes +
                       (8 if fmt == fq.NVFP4 else 0))
         quant_bytes = M * K * 2 + M * K // 2 + M * K // blk + M * nS * 2 + (4 if fmt == fq.NVFP4
                                                                              else 0)
+        if r4:
+            quant_bytes += M * nS * 2 + r_bytes
         wl = {"workload": name, "format": cfg["fmt"], "M": M, "K": K, "N": N, "n_s": nS,
-              "layout": args.layout, "out_dtype": args.out_dtype, "weight_copies_rotated": n_rot}
+              "layout": args.layout, "out_dtype": args.out_dtype, "weight_copies_rotated": n_rot,
+              "residual": args.residual}
     else:
         # MoE layer: gate_up then down, per-expert NVFP4, grouped GEMMs
         off = up(data["offsets"])
@@ -311,7 +338,8 @@ def main():
     # ---- CPU baseline: the oracle on this host --------------------------------
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(name, cfg, data, fmt, args.cpu_seconds)
+        cpu = cpu_baseline(name, cfg, data, fmt, args.cpu_seconds,
+                           r4=name != "moe_nvfp4" and args.residual == "fp4")
 
     value = flops / (step_ms * 1e-3) / 1e12
     out = {
@@ -340,9 +368,10 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(name, cfg, data, fmt, target_s):
-    """Time the oracle (as it is) on the host: quantize the activations, then
-    the FP64 GEMM on a bounded sample of outputs, scaled to TFLOP/s."""
+def cpu_baseline(name, cfg, data, fmt, target_s, r4=False):
+    """Time the oracle (as it is) on the host: quantize the activations (and,
+    with the FP4 residual, the residual a second time), then the FP64 GEMM on
+    a bounded sample of outputs, scaled to TFLOP/s."""
     import numpy as np
 
     from oracle import oracle as orc
@@ -371,11 +400,20 @@ def cpu_baseline(name, cfg, data, fmt, target_s):
     ta = float(qa["tscale"][0]) if fmt == 0 else 1.0
     tb = float(qb["tscale"][0]) if fmt == 0 else 1.0
     R = qa["resid"][:M] if qa["resid"] is not None else None
+    if r4:
+        t0 = time.perf_counter()
+        qr = orc.quantize_residual(fmt, R)
+        t_q += time.perf_counter() - t0
+        tr = float(qr["tscale"][0]) if fmt == 0 else 1.0
     while True:
         pm, pn = rng.integers(0, M, npts), rng.integers(0, n_cols, npts)
         t0 = time.perf_counter()
-        orc.gemm_points(fmt, qa["q"][:M], qa["scales"][:M], ta, qb["q"], qb["scales"], tb,
-                        ch0 if ch0.size else None, R, pm, pn)
+        if r4:
+            orc.gemm_points_r4(fmt, qa["q"][:M], qa["scales"][:M], ta, qb["q"], qb["scales"], tb,
+                               ch0, qr["q"], qr["scales"], tr, pm, pn)
+        else:
+            orc.gemm_points(fmt, qa["q"][:M], qa["scales"][:M], ta, qb["q"], qb["scales"], tb,
+                            ch0 if ch0.size else None, R, pm, pn)
         t_g = time.perf_counter() - t0
         if t_g > 0.2 * target_s or npts >= 1 << 24:
             break
