@@ -39,6 +39,11 @@
  *  - Two codes per byte, even element in the low nibble.
  *  - Residual R = bf16(x - deq(code)) on the chosen channels only.
  *  - GEMM: Y = deq(Xq) * deq(Wq)^T + R[:,S] * deq(Wq)[:,S]^T, in FP64.
+ *  - Online channel selection (the explainer's section 2.2 B: a binary mask
+ *    keeps the top-k% channels by residual magnitude): the magnitude of
+ *    channel c is max over rows of |R(m, c)|, R the BF16 residual the
+ *    quantizer would emit for c; the k largest win, ties to the lower index;
+ *    the list is returned ascending.
  *  - Second-pass residual (the explainer's section 2.2 B: the high-residual
  *    channels are quantized a second time and the correction term is added
  *    to the quantized output): R[:,S] itself quantized by the same rule, as
@@ -265,6 +270,76 @@ int orc_quantize(int fmt, const uint16_t* x, int64_t rows, int64_t cols, int64_t
         }
         free(jmap);
     }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Online channel selection                                                  */
+/* ------------------------------------------------------------------------ */
+
+/* The BF16 residual of element (r, c) from X and its quantized form, with
+ * the same FP32 steps as the quantizer's residual output. */
+static uint16_t residual_at(int fmt, const uint16_t* x, int64_t ldx, const uint8_t* q,
+                            const uint8_t* scales, float t, int64_t cols, int64_t r, int64_t c) {
+    const int blk = (fmt == ORC_NVFP4) ? 16 : 32;
+    const uint8_t byte = q[r * (cols / 2) + c / 2];
+    const uint8_t code = (c & 1) ? (byte >> 4) : (byte & 15);
+    const uint8_t sc = scales[r * (cols / blk) + c / blk];
+    float p;
+    if (fmt == ORC_NVFP4)
+        p = ((float)E2M1_GRID[code & 7] * (float)orc_e4m3_value(sc)) * t;
+    else
+        p = (float)E2M1_GRID[code & 7] * (float)orc_e8m0_value(sc);
+    if (code & 8) p = -p;
+    return orc_bf16_from_f32(orc_bf16_value(x[r * ldx + c]) - p);
+}
+
+typedef struct {
+    float score;
+    int64_t c;
+} ChanScore;
+
+/* larger score first, then the lower channel index */
+static int by_score(const void* a, const void* b) {
+    const ChanScore* u = (const ChanScore*)a;
+    const ChanScore* v = (const ChanScore*)b;
+    if (u->score != v->score) return u->score > v->score ? -1 : 1;
+    return u->c < v->c ? -1 : (u->c > v->c ? 1 : 0);
+}
+
+static int by_index(const void* a, const void* b) {
+    const int32_t u = *(const int32_t*)a, v = *(const int32_t*)b;
+    return u < v ? -1 : (u > v ? 1 : 0);
+}
+
+/* Select the k channels of largest residual magnitude from X [rows, cols]
+ * and its quantized form (q, scales, tensor scale t; row-major).  Writes
+ * chan_out [k] ascending and resid_out [rows, k] (BF16 residual on them).
+ * Returns 0, or -1 for k outside [0, cols]. */
+int orc_select_channels(int fmt, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                        const uint8_t* q, const uint8_t* scales, float t, int32_t k,
+                        int32_t* chan_out, uint16_t* resid_out) {
+    if (k < 0 || k > cols) return -1;
+    ChanScore* sc = (ChanScore*)malloc(sizeof(ChanScore) * (size_t)(cols > 0 ? cols : 1));
+    if (!sc) return -1;
+    const float tt = (fmt == ORC_NVFP4) ? t : 1.0f;
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < cols; ++c) {
+        float m = 0.0f;
+        for (int64_t r = 0; r < rows; ++r) {
+            const float a = fabsf(orc_bf16_value(residual_at(fmt, x, ldx, q, scales, tt, cols, r, c)));
+            if (a > m) m = a;
+        }
+        sc[c].score = m;
+        sc[c].c = c;
+    }
+    qsort(sc, (size_t)cols, sizeof(ChanScore), by_score);
+    for (int32_t j = 0; j < k; ++j) chan_out[j] = (int32_t)sc[j].c;
+    free(sc);
+    qsort(chan_out, (size_t)k, sizeof(int32_t), by_index);
+    for (int64_t r = 0; r < rows; ++r)
+        for (int32_t j = 0; j < k; ++j)
+            resid_out[r * k + j] = residual_at(fmt, x, ldx, q, scales, tt, cols, r, chan_out[j]);
     return 0;
 }
 

@@ -85,6 +85,8 @@ def lib():
         L.orc_gemm_full.restype = ctypes.c_int
         L.orc_gemm_full.argtypes = [ctypes.c_int, i64, i64, i64, P, P, f32, P, P, f32, P, i32,
                                     P, P, P]
+        L.orc_select_channels.restype = ctypes.c_int
+        L.orc_select_channels.argtypes = [ctypes.c_int, P, i64, i64, i64, P, P, f32, i32, P, P]
         L.orc_gemm_points_r4.restype = ctypes.c_int
         L.orc_gemm_points_r4.argtypes = [ctypes.c_int, i64, i64, i64, P, P, f32, P, P, f32, P, i32,
                                          P, P, f32, P, P, i64, P, P]
@@ -206,6 +208,22 @@ def gemm_full(fmt, aq, as_, ats, bq, bs, bts, chan_idx, resid):
     lib().orc_gemm_full(fmt, M, N, 2 * K2, _p(aq), _p(as_), float(ats), _p(bq), _p(bs),
                         float(bts), _p(ci), nS, _p(R), _p(y), _p(ya))
     return y, ya
+
+
+def select_channels(fmt: int, x: np.ndarray, qx: dict, k: int):
+    """The k channels of largest residual magnitude (max over rows of the BF16
+    residual) of x given its quantize() result qx (one group); ties to the
+    lower index.  Returns (chan int32 [k] ascending, resid uint16 [rows, k])."""
+    x = _c(x, np.uint16)
+    rows, cols = x.shape
+    t = float(qx["tscale"][0]) if fmt == NVFP4 else 1.0
+    chan = np.zeros(k, np.int32)
+    R = np.zeros((rows, k), np.uint16)
+    rc = lib().orc_select_channels(fmt, _p(x), rows, cols, cols, _p(_c(qx["q"], np.uint8)),
+                                   _p(_c(qx["scales"], np.uint8)), t, k, _p(chan), _p(R))
+    if rc != 0:
+        raise ValueError("oracle select_channels: k must lie in [0, cols]")
+    return chan, R
 
 
 def quantize_residual(fmt: int, resid: np.ndarray):
