@@ -50,6 +50,10 @@ def parse():
     p.add_argument("--residual", choices=("bf16", "fp4"), default="bf16",
                    help="compensation residual of the dense workloads: BF16, or quantized a "
                         "second time to the workload's FP4 format (fp4q_gemm_residual_fp4)")
+    p.add_argument("--channels", choices=("fixed", "online"), default="fixed",
+                   help="compensated channels of the dense workloads: the workload's fixed "
+                        "list, or chosen each step by residual magnitude "
+                        "(fp4q_select_channels, k = the workload's channel count)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle baseline sample")
@@ -167,6 +171,17 @@ def main():
         ats = torch.empty(1, dtype=torch.float32, device=dev) if fmt == fq.NVFP4 else None
         ar = torch.empty((M, nS), dtype=torch.int16, device=dev) if nS else None
 
+        online = args.channels == "online"
+        if online:
+            if nS == 0:
+                sys.exit("--channels online needs a workload with compensated channels")
+            chan = torch.empty(nS, dtype=torch.int32, device=dev)
+            sws = torch.empty(fq.select_channels_workspace_bytes(M, K), dtype=torch.uint8,
+                              device=dev)
+
+            def select():
+                fq.select_channels_into(fmt, layout, x, aq, asc, ats, nS, chan, ar, sws)
+
         r4 = args.residual == "fp4"
         if r4:
             if nS == 0 or nS % blk:
@@ -181,7 +196,11 @@ def main():
             gws = torch.empty(gwsb, dtype=torch.uint8, device=dev)
 
         def quant():
-            fq.quantize_into(fmt, layout, x, None, 1, chan, nS, aq, asc, ats, ar, qws)
+            if online:
+                fq.quantize_into(fmt, layout, x, None, 1, None, 0, aq, asc, ats, None, qws)
+                select()
+            else:
+                fq.quantize_into(fmt, layout, x, None, 1, chan, nS, aq, asc, ats, ar, qws)
             if r4:
                 fq.quantize_into(fmt, fq.ROWMAJOR, ar, None, 1, None, 0, rq, rsc, rts, None, rqws)
 
@@ -203,10 +222,18 @@ def main():
                                                                              else 0)
         if r4:
             quant_bytes += M * nS * 2 + r_bytes
+        if online:
+            # the selection reads x, codes and scales again, writes R and S
+            select_bytes = (M * K * 2 + M * K // 2 + M * K // blk + M * nS * 2 + nS * 4 +
+                            (4 if fmt == fq.NVFP4 else 0))
+            quant_bytes += select_bytes
         wl = {"workload": name, "format": cfg["fmt"], "M": M, "K": K, "N": N, "n_s": nS,
               "layout": args.layout, "out_dtype": args.out_dtype, "weight_copies_rotated": n_rot,
-              "residual": args.residual}
+              "residual": args.residual, "channels": args.channels}
     else:
+        if args.channels != "fixed" or args.residual != "bf16":
+            sys.exit("moe_nvfp4 takes the fixed per-expert channel lists and the BF16 residual")
+        online = False
         # MoE layer: gate_up then down, per-expert NVFP4, grouped GEMMs
         off = up(data["offsets"])
         G = int(data["offsets"].size - 1)
@@ -319,6 +346,10 @@ def main():
     t_quant = timed(lambda i: quant(), reps)
     print(f"[bench] gemm {t_gemm * 1e6:.2f} us, quantize {t_quant * 1e6:.2f} us per launch",
           file=sys.stderr, flush=True)
+    t_sel = timed(lambda i: select(), reps) if online else None
+    if online:
+        print(f"[bench] channel selection {t_sel * 1e6:.2f} us per call", file=sys.stderr,
+              flush=True)
 
     kh = src_hash()
     if name in ("prefill_nvfp4", "prefill_mxfp4"):
@@ -339,7 +370,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(name, cfg, data, fmt, args.cpu_seconds,
-                           r4=name != "moe_nvfp4" and args.residual == "fp4")
+                           r4=name != "moe_nvfp4" and args.residual == "fp4", online=online)
 
     value = flops / (step_ms * 1e-3) / 1e12
     out = {
@@ -365,12 +396,16 @@ def main():
         "cpu_baseline": cpu,
         "kernel_src_hash": kh,
     }
+    if online:
+        out["select_us"] = round(t_sel * 1e6, 3)
+        out["select_gbps"] = round(select_bytes / t_sel / 1e9, 1)
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(name, cfg, data, fmt, target_s, r4=False):
-    """Time the oracle (as it is) on the host: quantize the activations (and,
-    with the FP4 residual, the residual a second time), then the FP64 GEMM on
+def cpu_baseline(name, cfg, data, fmt, target_s, r4=False, online=False):
+    """Time the oracle (as it is) on the host: quantize the activations (with
+    online channels, then choose them; with the FP4 residual, quantize the
+    residual a second time), then the FP64 GEMM on
     a bounded sample of outputs, scaled to TFLOP/s."""
     import numpy as np
 
@@ -384,7 +419,11 @@ def cpu_baseline(name, cfg, data, fmt, target_s, r4=False):
         x, chan, off = data["x"], data["chan_idx"], None
         K = cfg["K"]
     t0 = time.perf_counter()
-    qa = orc.quantize(fmt, x, offsets=off, chan_idx=chan if chan.size else None)
+    if online:
+        qa = orc.quantize(fmt, x)
+        chan, qa["resid"] = orc.select_channels(fmt, x, qa, int(chan.size))
+    else:
+        qa = orc.quantize(fmt, x, offsets=off, chan_idx=chan if chan.size else None)
     t_q = time.perf_counter() - t0
     # weights for the sample: the first rows of W^T (first expert for MoE)
     wt = data["wt_gate_up"][0] if name == "moe_nvfp4" else data["wt"]
@@ -423,7 +462,8 @@ def cpu_baseline(name, cfg, data, fmt, target_s, r4=False):
     return {"value": round(gflops_rate / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle",
             "sample": f"oracle FP64 GEMM on {npts} sampled outputs of the {name} workload "
-                      f"(K={K}, {t_g:.1f}s) after oracle quantization of the full activation "
+                      f"(K={K}, {t_g:.1f}s) after oracle quantization"
+                      f"{' and channel selection' if online else ''} of the full activation "
                       f"tensor ({t_q:.2f}s)",
             "quantize_s": round(t_q, 4)}
 

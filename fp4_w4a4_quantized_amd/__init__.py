@@ -31,4 +31,7 @@ from .binding import (  # noqa: F401
     quantize,
     quantize_into,
     quantize_workspace_bytes,
+    select_channels,
+    select_channels_into,
+    select_channels_workspace_bytes,
 )

@@ -91,6 +91,11 @@ def lib():
         L.fp4q_grouped_gemm.restype = ctypes.c_int
         L.fp4q_grouped_gemm.argtypes = [ctypes.c_int, i64, i64, i64, P, i32, P, P, P, P, P, P, P,
                                         i32, P, P, ctypes.c_int, P, sz, P]
+        L.fp4q_select_channels_workspace_bytes.restype = sz
+        L.fp4q_select_channels_workspace_bytes.argtypes = [i64, i64]
+        L.fp4q_select_channels.restype = ctypes.c_int
+        L.fp4q_select_channels.argtypes = [ctypes.c_int, ctypes.c_int, P, i64, i64, i64, P, P, P,
+                                           i32, P, P, P, sz, P]
         L.fp4q_error_decompose_workspace_bytes.restype = sz
         L.fp4q_error_decompose_workspace_bytes.argtypes = [i64, i64]
         L.fp4q_error_decompose.restype = ctypes.c_int
@@ -140,6 +145,10 @@ def grouped_gemm_workspace_bytes(fmt, total_rows, N, K, num_groups, n_chan) -> i
     return lib().fp4q_grouped_gemm_workspace_bytes(fmt, total_rows, N, K, num_groups, n_chan)
 
 
+def select_channels_workspace_bytes(rows, cols) -> int:
+    return lib().fp4q_select_channels_workspace_bytes(rows, cols)
+
+
 def error_decompose_workspace_bytes(rows, cols) -> int:
     return lib().fp4q_error_decompose_workspace_bytes(rows, cols)
 
@@ -185,6 +194,16 @@ def grouped_gemm_into(fmt, total_rows, N, K, group_offsets, num_groups, a_q, a_s
                                  _ptr(b_ts), _ptr(chan_idx), n_chan, _ptr(resid), _ptr(y),
                                  y_dtype, _ptr(workspace), ws_bytes, _stream(stream))
     _check("fp4q_grouped_gemm", rc)
+
+
+def select_channels_into(fmt, layout, x, q, scales, tensor_scale, k, chan_out, resid_out,
+                         workspace, stream=None):
+    rows, cols = x.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().fp4q_select_channels(fmt, layout, _ptr(x), rows, cols, x.stride(0), _ptr(q),
+                                    _ptr(scales), _ptr(tensor_scale), k, _ptr(chan_out),
+                                    _ptr(resid_out), _ptr(workspace), ws_bytes, _stream(stream))
+    _check("fp4q_select_channels", rc)
 
 
 def error_decompose_into(fmt, x, out, workspace, stream=None):
@@ -268,6 +287,21 @@ def gemm_residual_fp4(fmt, a, b, chan_idx, r, y_dtype=OUT_F32, stream=None):
                            b["scales"], b["tscale"], chan_idx, nS, r["q"], r["scales"],
                            r["tscale"], y, y_dtype, N, ws, stream)
     return y
+
+
+def select_channels(fmt, x, a, k, stream=None):
+    """a = quantize(fmt, x) (one group, any layout).  Returns (chan int32
+    [k] ascending, resid bf16 bits as int16 [rows, k]): the k channels of
+    largest residual magnitude and the residual on them."""
+    rows, cols = x.shape
+    dev = x.device
+    chan = torch.empty(k, dtype=torch.int32, device=dev)
+    R = torch.empty((rows, k), dtype=torch.int16, device=dev)
+    wsb = select_channels_workspace_bytes(rows, cols)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
+    select_channels_into(fmt, a["layout"], x, a["q"], a["scales"], a["tscale"], k, chan, R, ws,
+                         stream)
+    return chan, R
 
 
 def grouped_gemm(fmt, group_offsets, a, bq, bs, bts, chan_idx=None, y_dtype=OUT_F32,

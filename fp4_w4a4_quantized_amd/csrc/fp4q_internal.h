@@ -58,6 +58,12 @@ int launch_gemm_skinny(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, con
                        const float* bts, const int32_t* chan, int nS, const uint16_t* resid,
                        const float* cts, void* y, int y_bf16, int64_t ldy, hipStream_t stream);
 
+// Online channel selection: scores, top-k pick, residual emission.
+size_t select_workspace_bytes(int64_t rows, int64_t cols);
+void launch_select(int fmt, bool tiled, const uint16_t* x, int64_t rows, int64_t cols,
+                   int64_t ldx, const uint8_t* q, const uint8_t* scales, const float* tscale,
+                   int k, int32_t* chan, uint16_t* resid, void* ws, hipStream_t stream);
+
 size_t decompose_workspace_bytes(int64_t rows, int64_t cols);
 int launch_decompose(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                      fp4q_err_stats_t* out, void* ws, hipStream_t stream);

@@ -212,6 +212,37 @@ int fp4q_gemm_residual_fp4(fp4q_format_t fmt, fp4q_layout_t layout, int64_t M, i
                            int64_t ldy, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Online channel selection.  Explainer of the QUADS paper, section 2.2 B:
+ * a binary mask keeps the top-k channels by residual magnitude.  With R the
+ * residual fp4q_quantize would emit for a channel,
+ * R[m, c] = bf16_rne(x[m, c] - deq(code[m, c])), the magnitude of channel c
+ * is max over rows m of |R[m, c]|; the k channels of largest magnitude are
+ * chosen (equal magnitudes: the lower index first) and returned ascending,
+ * with R on them, ready for fp4q_gemm.
+ *
+ *   x             bf16 [rows, cols] as quantized (ldx as for fp4q_quantize)
+ *   q, scales     fp4q_quantize's codes and block scales of x, in `layout`
+ *                 (one quantization group; q 4-byte aligned)
+ *   tensor_scale  device f32 [1] from that call (NVFP4), NULL for MXFP4
+ *   k             channels to keep, 0 <= k <= cols (k == 0 launches nothing)
+ *   chan_out      out device int32 [k], ascending
+ *   resid_out     out bf16 [rows, k]: R[m, chan_out[j]] (may be NULL when
+ *                 rows == 0)
+ *   workspace     device scratch of fp4q_select_channels_workspace_bytes()
+ *                 bytes, 16-byte aligned; needs no initialisation and is
+ *                 left undefined
+ *
+ * rows * k must be below 2^31 and cols below 2^31 (FP4Q_ERR_UNSUPPORTED).
+ * ------------------------------------------------------------------------ */
+size_t fp4q_select_channels_workspace_bytes(int64_t rows, int64_t cols);
+
+int fp4q_select_channels(fp4q_format_t fmt, fp4q_layout_t layout, const uint16_t* x,
+                         int64_t rows, int64_t cols, int64_t ldx, const uint8_t* q,
+                         const uint8_t* scales, const float* tensor_scale, int32_t k,
+                         int32_t* chan_out, uint16_t* resid_out, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Expert-grouped compensated GEMM (MoE layer; QUADS abstract: NVFP4 rollout
  * for Mixture-of-Experts).  Rows [off[g], off[g+1]) of the permuted
  * activations use expert g's weights, tensor scales and channel list:

@@ -196,3 +196,45 @@ def test_gemm_residual_fp4_rejects(L):
     assert (L.fp4q_gemm_residual_fp4_workspace_bytes(1, 1, 512, 512, 256, 128)
             == 512 * 128 * 2 + L.fp4q_gemm_workspace_bytes(1, 1, 512, 512, 256, 128))
     assert L.fp4q_gemm_residual_fp4_workspace_bytes(0, 0, 4, 8, 256, 0) == 0
+
+
+def sel(L, fmt=0, layout=0, x=A, rows=4, cols=64, ldx=64, qq=B, sc=B, ts=B, k=8, chan=A, R=B,
+        ws=A, wsb=1 << 20):
+    return L.fp4q_select_channels(fmt, layout, x, rows, cols, ldx, qq, sc, ts, k, chan, R, ws,
+                                  wsb, None)
+
+
+def test_select_channels_rejects(L):
+    assert sel(L, fmt=2) == INVALID
+    assert sel(L, layout=3) == INVALID
+    assert sel(L, cols=40, ldx=40) == INVALID           # not whole NVFP4 blocks
+    assert sel(L, fmt=1, ts=None, cols=48, ldx=48) == INVALID  # nor MXFP4 blocks
+    assert sel(L, layout=1) == INVALID                  # tiled needs cols % 128 == 0
+    assert sel(L, ldx=60) == INVALID
+    assert sel(L, ldx=68) == INVALID                    # ldx % 8
+    assert sel(L, k=-1) == INVALID
+    assert sel(L, k=65) == INVALID                      # more channels than columns
+    assert sel(L, ts=None) == INVALID                   # NVFP4 needs its tensor scale
+    assert sel(L, fmt=1) == INVALID                     # MXFP4 takes none
+    assert sel(L, chan=None) == INVALID
+    assert sel(L, R=None) == INVALID
+    assert sel(L, qq=None) == INVALID
+    assert sel(L, sc=None) == INVALID
+    assert sel(L, x=ctypes.c_void_p(0x10008)) == INVALID   # x 16-byte aligned
+    assert sel(L, qq=ctypes.c_void_p(0x20002)) == INVALID  # codes 4-byte aligned
+    assert sel(L, ws=None) == WORKSPACE
+    assert sel(L, wsb=16) == WORKSPACE
+    assert sel(L, ws=ctypes.c_void_p(0x10008)) == WORKSPACE
+    assert sel(L, rows=1 << 27, cols=64, k=32) == UNSUPPORTED   # rows * k >= 2^31
+    # nothing to choose: accepted without launching anything
+    assert sel(L, k=0, chan=None, R=None, ws=None, wsb=0) == 0
+    assert sel(L, rows=0, x=None, qq=None, sc=None, R=None, k=0, chan=None) == 0
+
+
+def test_select_channels_workspace(L):
+    f = L.fp4q_select_channels_workspace_bytes
+    assert f(4, 64) == 256                     # one row block: its partial maxima
+    # many row blocks: partial maxima of every block plus the reduced scores
+    big = f(8192, 7168)
+    assert big > 7168 * 2 * 2 and big % 256 == 0
+    assert f(-1, 64) == 0 and f(4, 0) == 0
