@@ -44,6 +44,12 @@
  *    channel c is max over rows of |R(m, c)|, R the BF16 residual the
  *    quantizer would emit for c; the k largest win, ties to the lower index;
  *    the list is returned ascending.
+ *  - Quantize-before-permute for the expert-grouped layer (the QUADS
+ *    abstract's NVFP4 rollout for MoE; the pages do not say where in the
+ *    routing the activations are quantized): the token matrix is quantized
+ *    once, one tensor scale for all tokens, and row m of the expert-ordered
+ *    operand is a copy of the codes and block scales of its token; the
+ *    residual of expert g's channels is R(token, S_g[j]) by the rule above.
  *  - Second-pass residual (the explainer's section 2.2 B: the high-residual
  *    channels are quantized a second time and the correction term is added
  *    to the quantized output): R[:,S] itself quantized by the same rule, as
@@ -340,6 +346,37 @@ int orc_select_channels(int fmt, const uint16_t* x, int64_t rows, int64_t cols, 
     for (int64_t r = 0; r < rows; ++r)
         for (int32_t j = 0; j < k; ++j)
             resid_out[r * k + j] = residual_at(fmt, x, ldx, q, scales, tt, cols, r, chan_out[j]);
+    return 0;
+}
+
+/* Quantize-before-permute: q, scales (row-major, one group, tensor scale t)
+ * are the quantization of the token matrix x [tokens, cols].  Row m of the
+ * expert-ordered output is token row_src[m]: its codes and block scales are
+ * copied, and for the group g holding m (offsets[g] <= m < offsets[g+1]) the
+ * residual on chan[g][j] is the quantizer's residual at that token.  Returns
+ * -1 for a token index or offsets out of range. */
+int orc_permute_quantized(int fmt, const uint16_t* x, int64_t tokens, int64_t cols, int64_t ldx,
+                          const uint8_t* q, const uint8_t* scales, float t,
+                          const int32_t* row_src, int64_t rows, const int32_t* offsets,
+                          int32_t G, const int32_t* chan, int32_t nS, uint8_t* q_out,
+                          uint8_t* s_out, uint16_t* r_out) {
+    const int blk = (fmt == ORC_NVFP4) ? 16 : 32;
+    const float tt = (fmt == ORC_NVFP4) ? t : 1.0f;
+    if (G < 1 || offsets[0] != 0 || offsets[G] != rows) return -1;
+    for (int32_t g = 0; g < G; ++g)
+        if (offsets[g + 1] < offsets[g]) return -1;
+    for (int64_t m = 0; m < rows; ++m)
+        if (row_src[m] < 0 || row_src[m] >= tokens) return -1;
+    for (int64_t m = 0; m < rows; ++m) {
+        const int64_t tok = row_src[m];
+        memcpy(q_out + m * (cols / 2), q + tok * (cols / 2), (size_t)(cols / 2));
+        memcpy(s_out + m * (cols / blk), scales + tok * (cols / blk), (size_t)(cols / blk));
+    }
+    for (int32_t g = 0; g < G; ++g)
+        for (int64_t m = offsets[g]; m < offsets[g + 1]; ++m)
+            for (int32_t j = 0; j < nS; ++j)
+                r_out[m * nS + j] = residual_at(fmt, x, ldx, q, scales, tt, cols, row_src[m],
+                                                chan[(int64_t)g * nS + j]);
     return 0;
 }
 

@@ -87,6 +87,8 @@ def lib():
                                     P, P, P]
         L.orc_select_channels.restype = ctypes.c_int
         L.orc_select_channels.argtypes = [ctypes.c_int, P, i64, i64, i64, P, P, f32, i32, P, P]
+        L.orc_permute_quantized.argtypes = [ctypes.c_int, P, i64, i64, i64, P, P, f32, P, i64, P,
+                                            i32, P, i32, P, P, P]
         L.orc_gemm_points_r4.restype = ctypes.c_int
         L.orc_gemm_points_r4.argtypes = [ctypes.c_int, i64, i64, i64, P, P, f32, P, P, f32, P, i32,
                                          P, P, f32, P, P, i64, P, P]
@@ -224,6 +226,35 @@ def select_channels(fmt: int, x: np.ndarray, qx: dict, k: int):
     if rc != 0:
         raise ValueError("oracle select_channels: k must lie in [0, cols]")
     return chan, R
+
+
+def permute_quantized(fmt: int, x_tok: np.ndarray, qx: dict, row_src, offsets, chan_idx=None):
+    """Quantize-before-permute: qx = quantize(fmt, x_tok) (one group).  Row m
+    of the expert-ordered result is token row_src[m]; group g holds rows
+    offsets[g] .. offsets[g+1]-1 and has channels chan_idx[g] ([G, nS]).
+    Returns dict(q, scales, tscale [G] (all the token tensor scale; NVFP4),
+    resid [rows, nS] or None)."""
+    x_tok = _c(x_tok, np.uint16)
+    tokens, cols = x_tok.shape
+    blk = 16 if fmt == NVFP4 else 32
+    src = _c(row_src, np.int32)
+    off = _c(offsets, np.int32)
+    G = off.size - 1
+    rows = src.size
+    ci = None if chan_idx is None else _c(np.asarray(chan_idx).reshape(G, -1), np.int32)
+    nS = 0 if ci is None else ci.shape[1]
+    q = np.zeros((rows, cols // 2), np.uint8)
+    sc = np.zeros((rows, cols // blk), np.uint8)
+    R = np.zeros((rows, nS), np.uint16) if nS else None
+    t = float(qx["tscale"][0]) if fmt == NVFP4 else 1.0
+    rc = lib().orc_permute_quantized(fmt, _p(x_tok), tokens, cols, cols,
+                                     _p(_c(qx["q"], np.uint8)), _p(_c(qx["scales"], np.uint8)),
+                                     t, _p(src), rows, _p(off), G, _p(ci), nS, _p(q), _p(sc),
+                                     _p(R))
+    if rc != 0:
+        raise ValueError("oracle permute_quantized: token index or offsets out of range")
+    ts = np.full(G, qx["tscale"][0], np.float32) if fmt == NVFP4 else None
+    return {"q": q, "scales": sc, "tscale": ts, "resid": R}
 
 
 def quantize_residual(fmt: int, resid: np.ndarray):

@@ -111,6 +111,8 @@ def moe_case(tokens=4096, hidden=2048, experts=128, top_k=8, inter=768, zipf=1.1
 
     Returns dict with
       offsets [E+1] i32, loads [E],
+      token_of_row [rows] (the token of each expert-ordered row),
+      x_tok [tokens, hidden] u16 (the token activations),
       x_perm [rows, hidden] u16 (routed token copies in expert order),
       h_perm [rows, inter] u16 (independent down-projection input),
       wt_gate_up [E, 2*inter, hidden] u16, wt_down [E, hidden, inter] u16,
@@ -129,7 +131,7 @@ def moe_case(tokens=4096, hidden=2048, experts=128, top_k=8, inter=768, zipf=1.1
     x_perm = bf16_bits(x_tok[perm])
     h_perm = bf16_bits(_activations(rng, rows, inter, "t4", h_out, out_mult))
     out = {"offsets": offsets.astype(np.int32), "loads": loads, "token_of_row": perm,
-           "x_perm": x_perm, "h_perm": h_perm}
+           "x_tok": bf16_bits(x_tok), "x_perm": x_perm, "h_perm": h_perm}
     chan_gu = np.zeros((experts, n_s), np.int32)
     chan_dn = np.zeros((experts, n_s), np.int32)
     for e in range(experts):
