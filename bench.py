@@ -54,6 +54,10 @@ def parse():
                    help="compensated channels of the dense workloads: the workload's fixed "
                         "list, or chosen each step by residual magnitude "
                         "(fp4q_select_channels, k = the workload's channel count)")
+    p.add_argument("--moe-quant", choices=("expert", "token"), default="expert",
+                   help="MoE gate_up input: quantize the routed copies per expert, or quantize "
+                        "the token matrix once and permute its FP4 codes "
+                        "(fp4q_permute_quantized, one tensor scale for all tokens)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle baseline sample")
@@ -233,6 +237,7 @@ def main():
     else:
         if args.channels != "fixed" or args.residual != "bf16":
             sys.exit("moe_nvfp4 takes the fixed per-expert channel lists and the BF16 residual")
+        moe_tok = args.moe_quant == "token"
         online = False
         # MoE layer: gate_up then down, per-expert NVFP4, grouped GEMMs
         off = up(data["offsets"])
@@ -265,8 +270,24 @@ def main():
         ygu = torch.empty((rows, I2), dtype=torch.float32, device=dev)
         ydn = torch.empty((rows, H), dtype=torch.float32, device=dev)
 
+        if moe_tok:
+            T = cfg["tokens"]
+            xt = up(data["x_tok"])
+            src = up(data["token_of_row"].astype(np.int32))
+            tq = torch.empty((T, H // 2), dtype=torch.uint8, device=dev)
+            tsc = torch.empty((T, H // blk), dtype=torch.uint8, device=dev)
+            tts = torch.empty(1, dtype=torch.float32, device=dev)
+            tws = torch.zeros(max(fq.quantize_workspace_bytes(fmt, T, H, 1), 16),
+                              dtype=torch.uint8, device=dev)
+
         def quant():
-            for tag, xin, ch in (("gu", xg, cg), ("dn", xd, cd)):
+            if moe_tok:
+                b = bufs["gu"]
+                fq.quantize_into(fmt, fq.ROWMAJOR, xt, None, 1, None, 0, tq, tsc, tts, None, tws)
+                fq.permute_quantized_into(fmt, xt, tq, tsc, tts, src, off, G, cg, nS, b["q"],
+                                          b["s"], b["t"], b["r"])
+            for tag, xin, ch in ((("dn", xd, cd),) if moe_tok else
+                                 (("gu", xg, cg), ("dn", xd, cd))):
                 b = bufs[tag]
                 fq.quantize_into(fmt, fq.ROWMAJOR, xin, off, G, ch, nS, b["q"], b["s"], b["t"], b["r"],
                                  b["ws"])
@@ -287,12 +308,21 @@ def main():
         wb = active * (I2 * H // 2 + I2 * H // blk + H * I // 2 + H * I // blk)
         gemm_bytes = (rows * (H + I) // 2 + rows * (H + I) // blk + 2 * rows * nS * 2 +
                       2 * G * nS * 4 + wb + rows * (I2 + H) * 4 + 2 * (G + 1) * 4 + 4 * G * 4)
-        quant_bytes = rows * (H + I) * 2 + rows * (H + I) // 2 + rows * (H + I) // blk + \
-            2 * rows * nS * 2 + 2 * G * 4
+        dn_bytes = rows * I * 2 + rows * I // 2 + rows * I // blk + rows * nS * 2 + G * 4
+        if moe_tok:
+            # tokens read and quantized once; codes read once and written per routed row;
+            # the residual gathers x and writes R
+            T = cfg["tokens"]
+            gu_bytes = (T * H * 2 + 2 * T * (H // 2 + H // blk) + rows * (H // 2 + H // blk) +
+                        rows * nS * 4 + G * 4 + 4)
+        else:
+            gu_bytes = rows * H * 2 + rows * H // 2 + rows * H // blk + rows * nS * 2 + G * 4
+        quant_bytes = gu_bytes + dn_bytes
         M, K, N = rows, H, I2
         wl = {"workload": name, "format": "nvfp4", "tokens": cfg["tokens"], "experts": G,
               "top_k": cfg["top_k"], "hidden": H, "inter": I, "routed_rows": rows,
               "n_s_per_expert": nS, "max_expert_rows": int(loads.max()),
+              "moe_quant": args.moe_quant,
               "empty_experts": int((loads == 0).sum())}
 
     def step(i):
@@ -370,7 +400,8 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(name, cfg, data, fmt, args.cpu_seconds,
-                           r4=name != "moe_nvfp4" and args.residual == "fp4", online=online)
+                           r4=name != "moe_nvfp4" and args.residual == "fp4", online=online,
+                           moe_tok=name == "moe_nvfp4" and args.moe_quant == "token")
 
     value = flops / (step_ms * 1e-3) / 1e12
     out = {
@@ -402,7 +433,7 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(name, cfg, data, fmt, target_s, r4=False, online=False):
+def cpu_baseline(name, cfg, data, fmt, target_s, r4=False, online=False, moe_tok=False):
     """Time the oracle (as it is) on the host: quantize the activations (with
     online channels, then choose them; with the FP4 residual, quantize the
     residual a second time), then the FP64 GEMM on
@@ -422,6 +453,9 @@ def cpu_baseline(name, cfg, data, fmt, target_s, r4=False, online=False):
     if online:
         qa = orc.quantize(fmt, x)
         chan, qa["resid"] = orc.select_channels(fmt, x, qa, int(chan.size))
+    elif moe_tok:
+        qt = orc.quantize(fmt, data["x_tok"])
+        qa = orc.permute_quantized(fmt, data["x_tok"], qt, data["token_of_row"], off, chan)
     else:
         qa = orc.quantize(fmt, x, offsets=off, chan_idx=chan if chan.size else None)
     t_q = time.perf_counter() - t0
@@ -457,14 +491,18 @@ def cpu_baseline(name, cfg, data, fmt, target_s, r4=False, online=False):
         if t_g > 0.2 * target_s or npts >= 1 << 24:
             break
         npts *= 4
+    if moe_tok:
+        prep = "oracle quantization of the token matrix and the permutation of its codes"
+    elif online:
+        prep = "oracle quantization and channel selection of the full activation tensor"
+    else:
+        prep = "oracle quantization of the full activation tensor"
     sample_flops = 2.0 * npts * K
     gflops_rate = sample_flops / t_g
     return {"value": round(gflops_rate / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle",
             "sample": f"oracle FP64 GEMM on {npts} sampled outputs of the {name} workload "
-                      f"(K={K}, {t_g:.1f}s) after oracle quantization"
-                      f"{' and channel selection' if online else ''} of the full activation "
-                      f"tensor ({t_q:.2f}s)",
+                      f"(K={K}, {t_g:.1f}s) after {prep} ({t_q:.2f}s)",
             "quantize_s": round(t_q, 4)}
 
 

@@ -28,6 +28,8 @@ from .binding import (  # noqa: F401
     grouped_gemm_workspace_bytes,
     lib,
     packed_bytes,
+    permute_quantized,
+    permute_quantized_into,
     quantize,
     quantize_into,
     quantize_workspace_bytes,

@@ -96,6 +96,9 @@ def lib():
         L.fp4q_select_channels.restype = ctypes.c_int
         L.fp4q_select_channels.argtypes = [ctypes.c_int, ctypes.c_int, P, i64, i64, i64, P, P, P,
                                            i32, P, P, P, sz, P]
+        L.fp4q_permute_quantized.restype = ctypes.c_int
+        L.fp4q_permute_quantized.argtypes = [ctypes.c_int, P, i64, i64, i64, P, P, P, P, i64, P,
+                                             i32, P, i32, P, P, P, P, P]
         L.fp4q_error_decompose_workspace_bytes.restype = sz
         L.fp4q_error_decompose_workspace_bytes.argtypes = [i64, i64]
         L.fp4q_error_decompose.restype = ctypes.c_int
@@ -206,6 +209,20 @@ def select_channels_into(fmt, layout, x, q, scales, tensor_scale, k, chan_out, r
     _check("fp4q_select_channels", rc)
 
 
+def permute_quantized_into(fmt, x, q, scales, tensor_scale, row_src, group_offsets, num_groups,
+                           chan_idx, n_chan, q_out, scales_out, tensor_scale_out, resid_out,
+                           stream=None):
+    tokens, cols = (x.shape if x is not None else (q.shape[0], q.shape[1] * 2))
+    ldx = x.stride(0) if x is not None else cols
+    rows = row_src.numel()
+    rc = lib().fp4q_permute_quantized(fmt, _ptr(x), tokens, cols, ldx, _ptr(q), _ptr(scales),
+                                      _ptr(tensor_scale), _ptr(row_src), rows,
+                                      _ptr(group_offsets), num_groups, _ptr(chan_idx), n_chan,
+                                      _ptr(q_out), _ptr(scales_out), _ptr(tensor_scale_out),
+                                      _ptr(resid_out), _stream(stream))
+    _check("fp4q_permute_quantized", rc)
+
+
 def error_decompose_into(fmt, x, out, workspace, stream=None):
     rows, cols = x.shape
     ws_bytes = workspace.numel() * workspace.element_size()
@@ -302,6 +319,26 @@ def select_channels(fmt, x, a, k, stream=None):
     select_channels_into(fmt, a["layout"], x, a["q"], a["scales"], a["tscale"], k, chan, R, ws,
                          stream)
     return chan, R
+
+
+def permute_quantized(fmt, x, a, row_src, group_offsets, chan_idx=None, stream=None):
+    """a = quantize(fmt, x) of the token activations (one group, row-major).
+    Returns a grouped quantize()-style dict (q, scales, tscale [G], resid)
+    of the expert-ordered rows row_src, ready for grouped_gemm()."""
+    dev = a["q"].device
+    rows = row_src.numel()
+    cols = a["q"].shape[1] * 2
+    blk = BLOCK[fmt]
+    G = group_offsets.numel() - 1
+    nS = 0 if chan_idx is None else chan_idx.numel() // G
+    q = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    sc = torch.empty((rows, cols // blk), dtype=torch.uint8, device=dev)
+    ts = torch.empty(G, dtype=torch.float32, device=dev) if fmt == NVFP4 else None
+    R = torch.empty((rows, nS), dtype=torch.int16, device=dev) if nS else None
+    permute_quantized_into(fmt, x, a["q"], a["scales"], a["tscale"], row_src, group_offsets, G,
+                           chan_idx, nS, q, sc, ts, R, stream)
+    return {"q": q, "scales": sc, "tscale": ts, "resid": R, "layout": ROWMAJOR, "rows": rows,
+            "cols": cols}
 
 
 def grouped_gemm(fmt, group_offsets, a, bq, bs, bts, chan_idx=None, y_dtype=OUT_F32,

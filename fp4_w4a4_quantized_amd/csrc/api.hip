@@ -272,6 +272,35 @@ int fp4q_select_channels(fp4q_format_t fmt, fp4q_layout_t layout, const uint16_t
   return check_launch();
 }
 
+int fp4q_permute_quantized(fp4q_format_t fmt, const uint16_t* x, int64_t tokens, int64_t cols,
+                           int64_t ldx, const uint8_t* q, const uint8_t* scales,
+                           const float* tensor_scale, const int32_t* row_src, int64_t rows,
+                           const int32_t* group_offsets, int32_t num_groups,
+                           const int32_t* chan_idx, int32_t n_chan, uint8_t* q_out,
+                           uint8_t* scales_out, float* tensor_scale_out, uint16_t* resid_out,
+                           void* stream) {
+  if (!fmt_ok(fmt)) return FP4Q_ERR_INVALID;
+  if (tokens < 0 || rows < 0 || cols <= 0 || cols % blk_of(fmt) != 0) return FP4Q_ERR_INVALID;
+  if (rows > 0 && tokens == 0) return FP4Q_ERR_INVALID;
+  if (num_groups < 1 || !group_offsets) return FP4Q_ERR_INVALID;
+  if (n_chan < 0 || n_chan > cols) return FP4Q_ERR_INVALID;
+  if ((n_chan > 0) != (chan_idx != nullptr) || (n_chan > 0) != (resid_out != nullptr))
+    return FP4Q_ERR_INVALID;
+  if (fmt == FP4Q_NVFP4 && (!tensor_scale || !tensor_scale_out)) return FP4Q_ERR_INVALID;
+  if (fmt == FP4Q_MXFP4 && (tensor_scale || tensor_scale_out)) return FP4Q_ERR_INVALID;
+  if (rows > 0 && (!row_src || !q || !scales || !q_out || !scales_out)) return FP4Q_ERR_INVALID;
+  if (rows > 0 && (!aligned(q, 8) || !aligned(q_out, 8))) return FP4Q_ERR_INVALID;
+  if (rows > 0 && n_chan > 0 && (!x || !aligned(x, 2) || ldx < cols)) return FP4Q_ERR_INVALID;
+  if ((rows + 3) / 4 > (int64_t)UINT32_MAX || cols >= ((int64_t)1 << 30))
+    return FP4Q_ERR_UNSUPPORTED;
+  if (rows == 0 && fmt == FP4Q_MXFP4) return FP4Q_OK;  // no rows and no tensor scales to copy
+  clear_error();
+  fp4q::launch_permute(fmt, x, ldx, tokens, cols, q, scales, tensor_scale, row_src, rows,
+                       group_offsets, num_groups, chan_idx, n_chan, q_out, scales_out,
+                       tensor_scale_out, resid_out, static_cast<hipStream_t>(stream));
+  return check_launch();
+}
+
 size_t fp4q_error_decompose_workspace_bytes(int64_t rows, int64_t cols) {
   if (rows < 0 || cols <= 0) return 0;
   return fp4q::decompose_workspace_bytes(rows, cols);

@@ -64,6 +64,13 @@ void launch_select(int fmt, bool tiled, const uint16_t* x, int64_t rows, int64_t
                    int64_t ldx, const uint8_t* q, const uint8_t* scales, const float* tscale,
                    int k, int32_t* chan, uint16_t* resid, void* ws, hipStream_t stream);
 
+// Quantize-before-permute: token codes to expert order, per-group residual.
+void launch_permute(int fmt, const uint16_t* x, int64_t ldx, int64_t tokens, int64_t cols,
+                    const uint8_t* q, const uint8_t* scales, const float* tscale,
+                    const int32_t* row_src, int64_t rows, const int32_t* off, int G,
+                    const int32_t* chan, int nS, uint8_t* q_out, uint8_t* s_out, float* ts_out,
+                    uint16_t* r_out, hipStream_t stream);
+
 size_t decompose_workspace_bytes(int64_t rows, int64_t cols);
 int launch_decompose(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                      fp4q_err_stats_t* out, void* ws, hipStream_t stream);

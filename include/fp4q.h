@@ -273,6 +273,45 @@ int fp4q_grouped_gemm(fp4q_format_t fmt, int64_t total_rows, int64_t N, int64_t 
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Quantize-before-permute for the expert-grouped layer (QUADS abstract:
+ * NVFP4 rollout for Mixture-of-Experts).  The token activations are
+ * quantized once by fp4q_quantize (one group, row-major, no channels), and
+ * this call builds the expert-ordered operand of fp4q_grouped_gemm from the
+ * FP4 codes instead of quantizing every routed copy:
+ *
+ *   q_out[m] = q[row_src[m]], scales_out[m] = scales[row_src[m]],
+ *   resid_out[m, j] = bf16_rne(x[t, c] - deq(code[t, c])), t = row_src[m],
+ *                     c = chan_idx[g][j] for the group g holding row m,
+ *   tensor_scale_out[g] = tensor_scale[0] for every group (NVFP4)
+ *
+ * with deq as in fp4q_quantize.  Every expert then sees one tensor scale,
+ * that of all the tokens.
+ *
+ *   x              bf16 token activations [tokens, cols], row stride ldx
+ *                  (read only for the residual; may be NULL when n_chan == 0)
+ *   q, scales      fp4q_quantize(fmt, ROWMAJOR) of x: [tokens, cols/2],
+ *                  [tokens, cols/blk] (q 8-byte aligned)
+ *   tensor_scale   device f32 [1] from that call (NVFP4), NULL for MXFP4
+ *   row_src        device int32 [rows]: the token of each expert-ordered row
+ *   group_offsets  device int32 [num_groups + 1], as for fp4q_grouped_gemm
+ *   chan_idx       device int32 [num_groups, n_chan], ascending per group;
+ *                  NULL iff n_chan == 0
+ *   q_out, scales_out   out [rows, cols/2] (8-byte aligned), [rows, cols/blk]
+ *   tensor_scale_out    out device f32 [num_groups] (NVFP4), NULL for MXFP4
+ *   resid_out      out bf16 [rows, n_chan]; NULL iff n_chan == 0
+ *
+ * Preconditions (not checked on the device): row_src[m] < tokens, offsets
+ * as for the grouped GEMM.  Row-major layout only (the grouped GEMM's).
+ * ------------------------------------------------------------------------ */
+int fp4q_permute_quantized(fp4q_format_t fmt, const uint16_t* x, int64_t tokens, int64_t cols,
+                           int64_t ldx, const uint8_t* q, const uint8_t* scales,
+                           const float* tensor_scale, const int32_t* row_src, int64_t rows,
+                           const int32_t* group_offsets, int32_t num_groups,
+                           const int32_t* chan_idx, int32_t n_chan, uint8_t* q_out,
+                           uint8_t* scales_out, float* tensor_scale_out, uint16_t* resid_out,
+                           void* stream);
+
+/* ------------------------------------------------------------------------
  * Exact three-way MXFP4 error decomposition ("Decomposing MXFP4
  * quantization error ...", abstract).  Per 32-block with actual scale
  * s = 2^e and ideal scale s* = amax/6, per element x:

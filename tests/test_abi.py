@@ -238,3 +238,31 @@ def test_select_channels_workspace(L):
     big = f(8192, 7168)
     assert big > 7168 * 2 * 2 and big % 256 == 0
     assert f(-1, 64) == 0 and f(4, 0) == 0
+
+
+def pq(L, fmt=0, x=A, tokens=8, cols=64, ldx=64, qq=B, sc=B, ts=B, src=A, rows=16, off=A, G=2,
+       chan=A, nS=4, qo=B, so=B, tso=B, R=A):
+    return L.fp4q_permute_quantized(fmt, x, tokens, cols, ldx, qq, sc, ts, src, rows, off, G,
+                                    chan, nS, qo, so, tso, R, None)
+
+
+def test_permute_quantized_rejects(L):
+    assert pq(L, fmt=5) == INVALID
+    assert pq(L, cols=40, ldx=40) == INVALID       # not whole NVFP4 blocks
+    assert pq(L, tokens=0) == INVALID              # rows to fill but no tokens
+    assert pq(L, G=0) == INVALID
+    assert pq(L, off=None) == INVALID
+    assert pq(L, nS=65) == INVALID
+    assert pq(L, chan=None) == INVALID
+    assert pq(L, R=None) == INVALID
+    assert pq(L, ts=None) == INVALID               # NVFP4 needs the token tensor scale
+    assert pq(L, tso=None) == INVALID              # ... and somewhere to put the groups' copies
+    assert pq(L, fmt=1) == INVALID                 # MXFP4 takes neither
+    assert pq(L, src=None) == INVALID
+    assert pq(L, qo=None) == INVALID
+    assert pq(L, qq=ctypes.c_void_p(0x20004)) == INVALID   # codes 8-byte aligned
+    assert pq(L, x=None) == INVALID                # the residual reads x
+    assert pq(L, ldx=32) == INVALID
+    # nothing to do: accepted without touching memory
+    assert pq(L, fmt=1, ts=None, tso=None, rows=0, src=None, qq=None, sc=None, qo=None, so=None,
+              chan=None, nS=0, R=None, x=None, tokens=0) == 0
