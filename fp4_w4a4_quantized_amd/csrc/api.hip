@@ -291,7 +291,7 @@ int fp4q_permute_quantized(fp4q_format_t fmt, const uint16_t* x, int64_t tokens,
   if (rows > 0 && (!row_src || !q || !scales || !q_out || !scales_out)) return FP4Q_ERR_INVALID;
   if (rows > 0 && (!aligned(q, 8) || !aligned(q_out, 8))) return FP4Q_ERR_INVALID;
   if (rows > 0 && n_chan > 0 && (!x || !aligned(x, 2) || ldx < cols)) return FP4Q_ERR_INVALID;
-  if ((rows + 3) / 4 > (int64_t)UINT32_MAX || cols >= ((int64_t)1 << 30))
+  if (rows >= ((int64_t)1 << 31) || cols >= ((int64_t)1 << 30) || num_groups > MAX_GROUPS)
     return FP4Q_ERR_UNSUPPORTED;
   if (rows == 0 && fmt == FP4Q_MXFP4) return FP4Q_OK;  // no rows and no tensor scales to copy
   clear_error();

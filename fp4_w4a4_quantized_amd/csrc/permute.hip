@@ -9,12 +9,13 @@
 // residual on the channels of the group holding m is the quantizer's residual
 // at that token (the same FP32 operations as the quantizer).
 //
-// One wave per eight output rows: the code and scale bytes of all eight rows
-// are spread over the lanes in the widest units the row lengths allow (16
-// bytes for the codes at cols % 32 == 0), four units per lane in flight, and
-// one lane per residual channel.
-// The group of the first row comes from a binary search of the offsets
-// (scalar loads); the following rows step forward from it.
+// A workgroup owns one class of tokens (token mod 8) within a chunk of 256
+// output rows; its threads find their rows' tokens and groups (binary search
+// of the offsets in LDS) and compact the rows of the class into a list.
+// Waves then take eight listed rows at a time: the code and scale bytes of
+// the eight rows are spread over the lanes in the widest units the row
+// lengths allow (16 bytes for the codes at cols % 32 == 0), and so are the
+// rows' (row, channel) residual pairs, four per lane in flight.
 #include "fp4q_device.h"
 #include "fp4q_internal.h"
 
@@ -25,18 +26,21 @@ namespace fp4q {
 namespace {
 
 constexpr int PM_THREADS = 256;  // four waves
+constexpr int PM_ROWS = 8;       // output rows per wave and step
+constexpr int PM_CHUNK = 256;    // rows per chunk: one per thread
+constexpr int PM_XCD = 8;        // workgroups per chunk, one per token class
+constexpr int PM_MAX_GROUPS = 2048;
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
-constexpr int PM_ROWS = 8;       // output rows per wave
 
-// Copy the wave's rows (row r of the output from token row tok(r), held by
-// lane r of tk) in units of T: the units of all rows are spread over the
-// lanes, four per lane in flight.
+// Copy rows of the wave's list in units of T: output row mrow(r) from token
+// row tk(r), both held by lane r (r < nr); the units of all rows are spread
+// over the lanes, four per lane in flight.
 template <typename T>
 __device__ __forceinline__ void copy_rows(const uint8_t* __restrict__ src,
                                           uint8_t* __restrict__ dst, int64_t row_bytes, int tk,
-                                          int64_t m0, int nr, int lane) {
+                                          int mrow, int nr, int lane) {
   const uint32_t per = (uint32_t)(row_bytes / (int64_t)sizeof(T));  // < 2^27
   const uint32_t total = per * (uint32_t)nr;
   for (uint32_t u0 = 0; u0 < total; u0 += 4 * 64) {
@@ -48,9 +52,10 @@ __device__ __forceinline__ void copy_rows(const uint8_t* __restrict__ src,
       const bool ok = u < total;
       const int r = ok ? (int)(u / per) : 0;
       const int64_t tok = __shfl(tk, r);
+      const int64_t m = __shfl(mrow, r);
       const int64_t i = ok ? (int64_t)(u - (uint32_t)r * per) : 0;
       v[k] = reinterpret_cast<const T*>(src + tok * row_bytes)[i];
-      d[k] = ok ? (m0 + r) * per + i : -1;
+      d[k] = ok ? m * per + i : -1;
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k)
@@ -58,6 +63,11 @@ __device__ __forceinline__ void copy_rows(const uint8_t* __restrict__ src,
   }
 }
 
+// Workgroup b takes chunk b / 8 of the output rows and, of those, the rows
+// whose token is congruent to b mod 8.  Workgroups are dispatched to the 8
+// XCDs in turn, so each XCD's L2 holds the rows of one eighth of the tokens
+// (their x rows for the residual gathers, their codes for the copies).  Any
+// other dispatch order gives the same result, only with less L2 reuse.
 // CU, SU: bytes per copy unit of the code rows and of the scale rows.
 template <int FMT, int CU, int SU>
 __global__ __launch_bounds__(PM_THREADS) void k_permute_rows(
@@ -68,66 +78,97 @@ __global__ __launch_bounds__(PM_THREADS) void k_permute_rows(
     uint8_t* __restrict__ q_out, uint8_t* __restrict__ s_out, float* __restrict__ ts_out,
     uint16_t* __restrict__ r_out) {
   constexpr int BLK = (FMT == FP4Q_NVFP4) ? 16 : 32;
-  const int lane = threadIdx.x & 63;
+  __shared__ int s_off[PM_MAX_GROUPS + 1];
+  __shared__ int s_m[PM_CHUNK], s_tok[PM_CHUNK], s_g[PM_CHUNK];
+  __shared__ int s_cnt[PM_THREADS / 64];
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   if (FMT == FP4Q_NVFP4 && blockIdx.x == 0)
-    for (int g = threadIdx.x; g < G; g += PM_THREADS) ts_out[g] = tscale[0];
-  const int64_t m0 = ((int64_t)blockIdx.x * (PM_THREADS / 64) +
-                      __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * PM_ROWS;
-  if (m0 >= rows) return;
-  const int nr = (int)min((int64_t)PM_ROWS, rows - m0);
+    for (int g = t; g < G; g += PM_THREADS) ts_out[g] = tscale[0];
+  const int cls = (int)(blockIdx.x % PM_XCD);
+  const int64_t base = (int64_t)(blockIdx.x / PM_XCD) * PM_CHUNK;
+  if (base >= rows) return;
+  if (nS > 0)
+    for (int g = t; g <= G; g += PM_THREADS) s_off[g] = off[g];
+
+  // this thread's row of the chunk: its token (clamped into range; in range
+  // by precondition) and whether it belongs to this workgroup's class
+  const int64_t m = base + t;
+  const bool valid = m < rows;
+  const int tok = valid ? (int)min(max((int64_t)row_src[m], (int64_t)0), tokens - 1) : 0;
+  const bool mine = valid && (tok % PM_XCD) == cls;
+  const uint64_t bal = __ballot(mine);
+  if (lane == 0) s_cnt[wave] = __popcll(bal);
+  __syncthreads();
+  int before = 0, n = 0;
+#pragma unroll
+  for (int w = 0; w < PM_THREADS / 64; ++w) {
+    before += w < wave ? s_cnt[w] : 0;
+    n += s_cnt[w];
+  }
+  if (mine) {
+    const int pos = before + (int)__popcll(bal & ((1ull << lane) - 1ull));
+    int g = 0;
+    if (nS > 0) {  // the last group g with off[g] <= m (skips empty groups)
+      int lo = 0, hi = G;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_off[mid] <= m) lo = mid;
+        else hi = mid;
+      }
+      g = lo;
+    }
+    s_m[pos] = (int)m;
+    s_tok[pos] = tok;
+    s_g[pos] = g;
+  }
+  __syncthreads();
+
   const int64_t cb = cols / 2, sb = cols / BLK;
-
-  // the wave's tokens: lane r loads row m0 + r; a row past the end repeats
-  // the last one (its copies are not stored).  The clamp keeps every load
-  // inside the tokens; row_src is in range by precondition.
-  const int tk = (int)min(max((int64_t)row_src[m0 + min(lane, nr - 1)], (int64_t)0), tokens - 1);
-
   typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
   typedef typename std::conditional<CU == 16, u32x4v, uint64_t>::type CodeUnit;
   typedef typename std::conditional<SU == 16, u32x4v,
                                     typename std::conditional<SU == 4, uint32_t, uint8_t>::type>::type
       ScaleUnit;
-  copy_rows<CodeUnit>(q, q_out, cb, tk, m0, nr, lane);
-  copy_rows<ScaleUnit>(scales, s_out, sb, tk, m0, nr, lane);
+  const float tt = (FMT == FP4Q_NVFP4) ? tscale[0] : 1.0f;
+  for (int i0 = wave * PM_ROWS; i0 < n; i0 += PM_THREADS / 64 * PM_ROWS) {
+    const int nr = min(PM_ROWS, n - i0);
+    const int li = i0 + min(lane, nr - 1);  // lanes past the list repeat its last row
+    const int mrow = s_m[li], tk = s_tok[li], gl = s_g[li];
+    copy_rows<CodeUnit>(q, q_out, cb, tk, mrow, nr, lane);
+    copy_rows<ScaleUnit>(scales, s_out, sb, tk, mrow, nr, lane);
 
-  if (nS > 0) {
-    // group of the first row: the last g with off[g] <= m0 (empty groups
-    // before it are skipped); later rows step forward from it
-    int lo = 0, hi = G;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (off[mid] <= m0) lo = mid;
-      else hi = mid;
-    }
-    int grp[PM_ROWS];
+    // residual: the (row, channel) pairs of the eight rows spread over the
+    // lanes, four per lane in flight
+    const uint32_t pairs = (uint32_t)nr * (uint32_t)nS;
+    for (uint32_t p0 = 0; p0 < pairs; p0 += 4 * 64) {
+      int64_t c[4], tok_k[4], dst[4];
 #pragma unroll
-    for (int r = 0; r < PM_ROWS; ++r) {
-      while (lo + 1 < G && off[lo + 1] <= m0 + r) ++lo;
-      grp[r] = lo;
-    }
-    const float t = (FMT == FP4Q_NVFP4) ? tscale[0] : 1.0f;
-    for (int j = lane; j < nS; j += 64) {
-      uint32_t xv[PM_ROWS], cbt[PM_ROWS], sc[PM_ROWS];
-      int64_t c[PM_ROWS];
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t pr = p0 + lane + 64 * k;
+        const bool ok = pr < pairs;
+        const int r = ok ? (int)(pr / (uint32_t)nS) : 0;
+        const int j = ok ? (int)(pr - (uint32_t)r * (uint32_t)nS) : 0;
+        const int64_t g = __shfl(gl, r);
+        tok_k[k] = __shfl(tk, r);
+        dst[k] = ok ? (int64_t)__shfl(mrow, r) * nS + j : -1;
+        c[k] = min(max((int64_t)chan[g * nS + j], (int64_t)0), cols - 1);
+      }
+      uint32_t xv[4], cbt[4], sc[4];
 #pragma unroll
-      for (int r = 0; r < PM_ROWS; ++r)
-        c[r] = min(max((int64_t)chan[(int64_t)grp[r] * nS + j], (int64_t)0), cols - 1);
-#pragma unroll
-      for (int r = 0; r < PM_ROWS; ++r) {
-        const int64_t tok = __builtin_amdgcn_readlane(tk, r);
-        xv[r] = x[tok * ldx + c[r]];
-        cbt[r] = q[tok * cb + (c[r] >> 1)];
-        sc[r] = scales[tok * sb + c[r] / BLK];
+      for (int k = 0; k < 4; ++k) {
+        xv[k] = x[tok_k[k] * ldx + c[k]];
+        cbt[k] = q[tok_k[k] * cb + (c[k] >> 1)];
+        sc[k] = scales[tok_k[k] * sb + c[k] / BLK];
       }
 #pragma unroll
-      for (int r = 0; r < PM_ROWS; ++r) {
-        if (r < nr) {
-          const uint32_t code = (c[r] & 1) ? (cbt[r] >> 4) : (cbt[r] & 15u);
-          float p = (FMT == FP4Q_NVFP4) ? (e2m1_mag_value(code) * e4m3_value(sc[r])) * t
-                                        : e2m1_mag_value(code) * exp2i((int)sc[r] - 127);
+      for (int k = 0; k < 4; ++k) {
+        if (dst[k] >= 0) {
+          const uint32_t code = (c[k] & 1) ? (cbt[k] >> 4) : (cbt[k] & 15u);
+          float p = (FMT == FP4Q_NVFP4) ? (e2m1_mag_value(code) * e4m3_value(sc[k])) * tt
+                                        : e2m1_mag_value(code) * exp2i((int)sc[k] - 127);
           if (code & 8u) p = -p;
-          r_out[(m0 + r) * nS + j] =
-              (uint16_t)f32_to_bf16_rne(bf16_to_f32(xv[r]) - p);
+          r_out[dst[k]] = (uint16_t)f32_to_bf16_rne(bf16_to_f32(xv[k]) - p);
         }
       }
     }
@@ -141,9 +182,8 @@ void launch_permute(int fmt, const uint16_t* x, int64_t ldx, int64_t tokens, int
                     const int32_t* row_src, int64_t rows, const int32_t* off, int G,
                     const int32_t* chan, int nS, uint8_t* q_out, uint8_t* s_out, float* ts_out,
                     uint16_t* r_out, hipStream_t stream) {
-  const int64_t per_wg = (PM_THREADS / 64) * PM_ROWS;
-  const int64_t wgs = (rows + per_wg - 1) / per_wg;
-  const dim3 grid((unsigned)(wgs > 0 ? wgs : 1));
+  const int64_t chunks = (rows + PM_CHUNK - 1) / PM_CHUNK;
+  const dim3 grid((unsigned)(chunks > 0 ? chunks * PM_XCD : 1));
   // widest units that divide the rows (buffers are at least 8-byte aligned
   // for the codes; 16-byte units need 16-byte aligned buffers)
   const int64_t cb = cols / 2, sb = cols / (fmt == FP4Q_NVFP4 ? 16 : 32);

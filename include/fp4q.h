@@ -302,6 +302,7 @@ int fp4q_grouped_gemm(fp4q_format_t fmt, int64_t total_rows, int64_t N, int64_t 
  *
  * Preconditions (not checked on the device): row_src[m] < tokens, offsets
  * as for the grouped GEMM.  Row-major layout only (the grouped GEMM's).
+ * num_groups <= 2048, rows < 2^31, cols < 2^30 (FP4Q_ERR_UNSUPPORTED).
  * ------------------------------------------------------------------------ */
 int fp4q_permute_quantized(fp4q_format_t fmt, const uint16_t* x, int64_t tokens, int64_t cols,
                            int64_t ldx, const uint8_t* q, const uint8_t* scales,
