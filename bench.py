@@ -81,25 +81,29 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}), flush=True)
 
 
-def src_hash() -> str:
+def src_hash(files=None) -> str:
+    """Hash of the named kernel sources (all of csrc/ when None)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "fp4_w4a4_quantized_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in (sorted(os.listdir(csrc)) if files is None else files):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str, kernel_hash: str):
-    """HBM traffic per launch measured with rocprofv3 --pmc (FETCH_SIZE and
-    WRITE_SIZE, scaled by a copy-kernel calibration); used only if it was
-    taken on the current kernel sources."""
+def load_traffic(workload: str, default_variant: bool):
+    """HBM traffic per launch of the workload's dominant kernel, measured with
+    rocprofv3 --pmc (FETCH_SIZE and WRITE_SIZE, scaled by a copy-kernel
+    calibration) on the default variant of the workload; used only if the
+    sources that define that kernel are unchanged since."""
+    if not default_variant:
+        return None
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
             t = json.load(f)
         ent = t.get(workload)
-        if ent and ent.get("src_hash") == kernel_hash:
+        if ent and ent.get("src_hash") == src_hash(ent.get("sources")):
             return ent["bytes_per_launch"]
     except (OSError, ValueError):
         pass
@@ -382,17 +386,19 @@ def main():
               flush=True)
 
     kh = src_hash()
+    default_variant = (args.layout == "tiled" and args.out_dtype == "f32" and
+                       args.residual == "bf16" and args.channels == "fixed")
     if name in ("prefill_nvfp4", "prefill_mxfp4"):
         mfma_dtype = "f16" if fmt == fq.NVFP4 else "fp4"
         peak = MFMA_PEAK_TFLOPS[mfma_dtype]
         ach = flops / t_gemm / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(ach / peak, 4), "traffic": load_traffic(name, kh),
+                "frac": round(ach / peak, 4), "traffic": load_traffic(name, default_variant),
                 "mfma_dtype": mfma_dtype}
     else:
         ach = gemm_bytes / t_gemm / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": load_traffic(name, kh),
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": load_traffic(name, default_variant),
                 "algorithmic_bytes": gemm_bytes}
     quant_gbs = quant_bytes / t_quant / 1e9
 
