@@ -92,9 +92,12 @@ __device__ __forceinline__ u32x4 load_chunk(const ChunkGrid& gr, uint32_t c) {
 }
 
 // Max |x| (BF16 magnitude pattern) over the chunks first, first + stride, ...
-// below `end`, AMAX_BATCH independent loads in flight per thread.
+// below `end`, AMAX_BATCH independent loads in flight per thread; the rest
+// in batches of four, where a chunk past the end re-reads `first` (which
+// leaves the maximum alone) instead of waiting for one load at a time.
 __device__ __forceinline__ uint32_t strided_amax(const ChunkGrid& gr, uint32_t first, uint32_t end,
                                                  uint32_t stride) {
+  constexpr int TAIL = 4;
   uint32_t m = 0;
   int64_t i = first;
   for (; i + (int64_t)(AMAX_BATCH - 1) * stride < end; i += (int64_t)AMAX_BATCH * stride) {
@@ -104,7 +107,16 @@ __device__ __forceinline__ uint32_t strided_amax(const ChunkGrid& gr, uint32_t f
 #pragma unroll
     for (int u = 0; u < AMAX_BATCH; ++u) m = max(m, absmax8(v[u]));
   }
-  for (; i < end; i += stride) m = max(m, absmax8(load_chunk(gr, (uint32_t)i)));
+  for (; i < end; i += (int64_t)TAIL * stride) {
+    u32x4 v[TAIL];
+#pragma unroll
+    for (int u = 0; u < TAIL; ++u) {
+      const int64_t c = i + (int64_t)u * stride;
+      v[u] = load_chunk(gr, (uint32_t)(c < end ? c : first));
+    }
+#pragma unroll
+    for (int u = 0; u < TAIL; ++u) m = max(m, absmax8(v[u]));
+  }
   return m;
 }
 
