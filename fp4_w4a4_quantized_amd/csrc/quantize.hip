@@ -18,9 +18,11 @@
 // list.
 //
 // NVFP4 needs the tensor (or per-expert group) amax before any block scale:
-//  * small dense tensors (the decode regime): one launch; every workgroup
-//    first reduces the whole tensor's amax itself (it sits in L2), then
-//    quantizes its chunks -- no second launch and no workspace;
+//  * small dense tensors (the decode regime): one launch; each workgroup
+//    takes the maximum of the chunks it holds, the workgroups combine them
+//    through a grid-wide maximum made of agent-scope atomics (grid_max
+//    below), then quantize their chunks -- no second launch and no
+//    workspace;
 //  * large dense tensors: a partial-amax pass writes one maximum per
 //    workgroup to the workspace; each quantize workgroup reduces those
 //    first;
@@ -93,11 +95,11 @@ __device__ __forceinline__ u32x4 load_chunk(const ChunkGrid& gr, uint32_t c) {
 
 // Max |x| (BF16 magnitude pattern) over the chunks first, first + stride, ...
 // below `end`, AMAX_BATCH independent loads in flight per thread; the rest
-// in batches of four, where a chunk past the end re-reads `first` (which
+// in batches of eight, where a chunk past the end re-reads `first` (which
 // leaves the maximum alone) instead of waiting for one load at a time.
 __device__ __forceinline__ uint32_t strided_amax(const ChunkGrid& gr, uint32_t first, uint32_t end,
                                                  uint32_t stride) {
-  constexpr int TAIL = 4;
+  constexpr int TAIL = 8;
   uint32_t m = 0;
   int64_t i = first;
   for (; i + (int64_t)(AMAX_BATCH - 1) * stride < end; i += (int64_t)AMAX_BATCH * stride) {
@@ -146,32 +148,117 @@ __global__ void k_quant_init(uint32_t* __restrict__ amax_bits, float* __restrict
   }
 }
 
-// Per-group amax.  Each workgroup owns a run of rows.  When the run lies in
-// one group the workgroup scans it as one flat range and issues one atomic;
-// otherwise each wave takes rows in turn and issues one atomic per row.
-constexpr int AMAX_ROWS_PER_WG = 16;
+// Per-group amax.  Each workgroup owns a flat run of AMAX_WG_CHUNKS chunks
+// (one batch of AMAX_BATCH loads per thread, all in flight together), which
+// may start and end inside rows.  A run inside one group (most runs) is
+// reduced across the workgroup and issues one atomic.  A run that crosses
+// group boundaries keeps per-row maxima in LDS, and each row's maximum then
+// goes to its group.
+constexpr int AMAX_WG_CHUNKS = QT * AMAX_BATCH;
+constexpr int AMAX_WG_ROWS = AMAX_WG_CHUNKS / 2 + 2;  // rows a run can touch (cpr >= 2)
 
 __global__ void __launch_bounds__(QT) k_group_amax(ChunkGrid gr, int64_t rows,
                                                    const int32_t* __restrict__ off, int G,
                                                    uint32_t* __restrict__ amax_bits) {
   __shared__ uint32_t red[QT / 64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t r0 = (int64_t)blockIdx.x * AMAX_ROWS_PER_WG;
-  const int64_t r1 = r0 + AMAX_ROWS_PER_WG < rows ? r0 + AMAX_ROWS_PER_WG : rows;
+  __shared__ uint32_t rmax[AMAX_WG_ROWS];
+  const uint32_t cpr = gr.cpr, total = (uint32_t)(rows * cpr);
+  const uint32_t c0 = blockIdx.x * (uint32_t)AMAX_WG_CHUNKS;
+  const uint32_t c1 = c0 + AMAX_WG_CHUNKS < total ? c0 + AMAX_WG_CHUNKS : total;
+  uint32_t r0, cc0, rl, ccl;
+  chunk_rc(gr, c0, r0, cc0);
+  chunk_rc(gr, c1 - 1, rl, ccl);
   const int g0 = group_of_row(off, G, r0);
-  const int g1 = group_of_row(off, G, r1 - 1);
-  const uint32_t cpr = gr.cpr;
+  const int g1 = group_of_row(off, G, rl);
   if (g0 == g1) {
-    uint32_t m = strided_amax(gr, (uint32_t)(r0 * cpr) + threadIdx.x, (uint32_t)(r1 * cpr), QT);
+    uint32_t m = strided_amax(gr, c0 + threadIdx.x, c1, QT);
     m = wg_max<QT>(m, red);
     if (threadIdx.x == 0 && m) atomicMax(&amax_bits[g0], m << 16);
     return;
   }
-  for (int64_t r = r0 + wave; r < r1; r += QT / 64) {
-    uint32_t m = strided_amax(gr, (uint32_t)(r * cpr) + lane, (uint32_t)((r + 1) * cpr), 64);
-    for (int s = 32; s > 0; s >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, s));
-    if (lane == 0 && m) atomicMax(&amax_bits[group_of_row(off, G, r)], m << 16);
+  const uint32_t nrows = rl - r0 + 1;
+  for (uint32_t i = threadIdx.x; i < nrows; i += QT) rmax[i] = 0u;
+  __syncthreads();
+  // chunk c0 + t + QT u: its row relative to r0 steps by QT / cpr rows and
+  // QT % cpr chunks per u
+  const uint32_t drow = (uint32_t)QT / cpr, dcc = (uint32_t)QT - drow * cpr;
+  uint32_t rr, cc;
+  chunk_rc(gr, c0 + threadIdx.x, rr, cc);
+  rr -= r0;
+  u32x4 v[AMAX_BATCH];
+  uint32_t row[AMAX_BATCH];
+#pragma unroll
+  for (int u = 0; u < AMAX_BATCH; ++u) {
+    const uint32_t cu = c0 + threadIdx.x + u * QT;
+    v[u] = load_chunk(gr, cu < c1 ? cu : c0);
+    row[u] = cu < c1 ? rr : (uint32_t)AMAX_WG_ROWS;
+    rr += drow;
+    cc += dcc;
+    if (cc >= cpr) { cc -= cpr; ++rr; }
   }
+#pragma unroll
+  for (int u = 0; u < AMAX_BATCH; ++u)
+    if (row[u] < nrows) atomicMax(&rmax[row[u]], absmax8(v[u]));
+  __syncthreads();
+  for (uint32_t i = threadIdx.x; i < nrows; i += QT) {
+    const uint32_t m = rmax[i];
+    if (m) atomicMax(&amax_bits[group_of_row(off, G, r0 + i)], m << 16);
+  }
+}
+
+// Tensor maximum across the workgroups of one launch (the small-tensor NVFP4
+// path), through per-device state that is zero at module load: one word
+// holding a generation (high 16 bits) and an arrival count, and, per
+// generation parity, a maximum slot and a final slot.  Every access is an
+// atomic at agent scope, performed where all XCDs see it.  A workgroup adds
+// its maximum, then counts its arrival; the arrival takes an input from the
+// maximum's returned value, so it is issued after the maximum has been
+// performed, with no release fence (which would write back the per-XCD L2).
+// The last to arrive reads the slot, publishes it with a flag in the final
+// slot, clears the other parity's slots for the next launch and advances
+// the generation (resetting the count); the others spin, bounded, on the
+// final slot.  Every workgroup of the launch is resident at once (at most 32
+// workgroups of 1024 threads), and one such launch runs at a time on a
+// device.
+constexpr uint32_t GRID_SPIN_LIMIT = 1u << 22;
+constexpr uint32_t GRID_FLAG = 0x80000000u;
+static __device__ uint32_t g_fused_bar[5];  // word, max[2], final[2]
+
+// Opaque copy of `v` that can only be formed once `dep` is available.
+__device__ __forceinline__ uint32_t after(uint32_t v, uint32_t dep) {
+  asm volatile("" : "+v"(v) : "v"(dep));
+  return v;
+}
+
+// The launch's generation; read early, before the chunk loads are used.
+__device__ __forceinline__ uint32_t grid_gen() {
+  return __hip_atomic_load(&g_fused_bar[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 16;
+}
+
+// Called by one thread of each workgroup with the workgroup's maximum (a
+// BF16 magnitude pattern, below the flag bit).
+__device__ __forceinline__ uint32_t grid_max(uint32_t m, uint32_t nwg, uint32_t gen) {
+  uint32_t* bar = g_fused_bar;
+  const uint32_t p = gen & 1u;
+  const uint32_t old = __hip_atomic_fetch_max(&bar[1 + p], m, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t arrive = __hip_atomic_fetch_add(&bar[0], after(1u, old), __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+  if ((arrive & 0xFFFFu) == nwg - 1u) {
+    const uint32_t fin = __hip_atomic_fetch_max(&bar[1 + p], after(0u, arrive), __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&bar[3 + p], fin | GRID_FLAG, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&bar[1 + (p ^ 1u)], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&bar[3 + (p ^ 1u)], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(&bar[0], 0x10000u - nwg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return fin;
+  }
+  uint32_t f = 0;
+  for (uint32_t i = 0; i < GRID_SPIN_LIMIT; ++i) {
+    f = __hip_atomic_load(&bar[3 + p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (f & GRID_FLAG) break;
+  }
+  return f & ~GRID_FLAG;
 }
 
 // Dense, large: one partial maximum per workgroup.
@@ -419,9 +506,20 @@ __global__ void __launch_bounds__(NT) k_quantize(
     for (int i = threadIdx.x; i < nparts; i += NT) m = max(m, amax_words[i]);
     tdense = nv_tensor_scale(bf16_to_f32(wg_max<NT>(m, red)));
   } else if (MODE == AMAX_FUSED) {
-    // the whole (small) tensor, read by every workgroup from L2
-    const uint32_t m = strided_amax(gr, threadIdx.x, total_rm, NT);
-    tdense = nv_tensor_scale(bf16_to_f32(wg_max<NT>(m, red)));
+    // the maximum of this workgroup's own chunks (already loaded), then
+    // across the launch
+    __shared__ uint32_t s_amax;
+    const uint32_t gen = threadIdx.x == 0 ? grid_gen() : 0u;
+    uint32_t m = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t c = base + u * NT + threadIdx.x;
+      if (c < total && rowu[u] < (uint32_t)rows) m = max(m, absmax8(v[u]));
+    }
+    m = wg_max<NT>(m, red);
+    if (threadIdx.x == 0) s_amax = grid_max(m, gridDim.x, gen);
+    __syncthreads();
+    tdense = nv_tensor_scale(bf16_to_f32(s_amax));
   }
   if ((MODE == AMAX_PARTIALS || MODE == AMAX_FUSED) && blockIdx.x == 0 && threadIdx.x == 0)
     tscale[0] = tdense;
@@ -480,7 +578,7 @@ int launch_quantize(int fmt, bool tiled, const uint16_t* x, int64_t rows, int64_
   if (grouped) {
     hipLaunchKernelGGL(k_quant_init, dim3((G + QT - 1) / QT), dim3(QT), 0, stream, words, tscale, G);
     if (rows > 0) {
-      const int64_t nwg = (rows + AMAX_ROWS_PER_WG - 1) / AMAX_ROWS_PER_WG;
+      const int64_t nwg = (chunks + AMAX_WG_CHUNKS - 1) / AMAX_WG_CHUNKS;
       hipLaunchKernelGGL(k_group_amax, dim3((unsigned)nwg), dim3(QT), 0, stream, gr, rows, off, G,
                          words);
       launch_q<FP4Q_NVFP4, AMAX_GROUP_WORDS, QT, QU>(gr, rows, cols, tiled, stream, off, G, chan, nS, q,
