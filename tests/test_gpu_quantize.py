@@ -193,3 +193,55 @@ def test_deterministic(orc):
     b = fq.quantize(0, x)
     torch.cuda.synchronize(dev)
     assert torch.equal(a["q"], b["q"]) and torch.equal(a["scales"], b["scales"])
+
+
+def test_small_nvfp4_many_launches_in_a_row(orc):
+    """The one-launch NVFP4 path combines its workgroups' maxima through
+    per-device state that alternates between launches.  Forty back-to-back
+    launches of tensors whose maxima rise and fall (and one of 1, 16 and 32
+    workgroups' size), with no synchronisation between them, each match the
+    oracle; then the same sequence replayed three times from a HIP graph."""
+    dev = need_gpu()
+    say("small NVFP4 quantize, 40 launches in a row")
+    rng = np.random.default_rng(17)
+    shapes = [(64, 2048), (16, 256), (128, 2048), (7, 512)]   # 16, 1, 32, 1 workgroups
+    xs, refs = [], []
+    for i in range(40):
+        r, c = shapes[i % len(shapes)]
+        x = rng.standard_normal((r, c)).astype(np.float32) * np.float32(4.0 ** ((i * 7) % 5 - 2))
+        xb = bf16_bits(x)
+        xs.append(to_dev(xb))
+        refs.append(orc.quantize(0, xb))
+    outs = [fq.quantize(0, x) for x in xs]
+    torch.cuda.synchronize(dev)
+    for got, ref in zip(outs, refs):
+        assert_quant_equal(got, ref, 0)
+
+    bufs = []
+    for x in xs:
+        r, c = x.shape
+        bufs.append(dict(q=torch.empty((r, c // 2), dtype=torch.uint8, device=dev),
+                         s=torch.empty((r, c // 16), dtype=torch.uint8, device=dev),
+                         t=torch.empty(1, dtype=torch.float32, device=dev)))
+    ws = torch.zeros(max(fq.quantize_workspace_bytes(0, 128, 2048, 1), 16), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.Stream(dev)
+    with torch.cuda.stream(stream):
+        fq.quantize_into(0, fq.ROWMAJOR, xs[0], None, 1, None, 0, bufs[0]["q"], bufs[0]["s"],
+                         bufs[0]["t"], None, ws)
+        torch.cuda.synchronize(dev)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for x, b in zip(xs, bufs):
+                fq.quantize_into(0, fq.ROWMAJOR, x, None, 1, None, 0, b["q"], b["s"], b["t"],
+                                 None, ws)
+    for _ in range(3):
+        for b in bufs:
+            b["q"].zero_()
+            b["t"].zero_()
+        torch.cuda.synchronize(dev)
+        g.replay()
+        torch.cuda.synchronize(dev)
+        for b, ref in zip(bufs, refs):
+            got = {"q": b["q"], "scales": b["s"], "tscale": b["t"], "resid": None}
+            assert_quant_equal(got, dict(ref, resid=None), 0)
