@@ -744,3 +744,176 @@ int orc_error_decompose(const uint16_t* x, int64_t rows, int64_t cols, int64_t l
     out->n_elems = rows * cols;
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* The three-way decomposition with the NVFP4 quantizer                      */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The split above, applied to NVFP4 (16-element blocks, E4M3 block scale,
+ * FP32 tensor scale): per block with amax A, the quantizer's own code g of
+ * each element (orc_quantize, one group), its block scale value sb and the
+ * tensor scale t give Q_s(x) = g sb t, the dequantized value (exact real
+ * product); the ideal scale is again s* = A/6, so Q*(x) is the E2M1 point
+ * nearest to 6|x|/A times A/6.  Components as for MXFP4; an element is
+ * clipped when |x| > 6 sb t.  Times 6, the terms 6x, 6 g sb t and g* A are
+ * exact in FP64.  The sums add each term to the fixed point on its own, so
+ * they are exact whenever every term is a multiple of 2^-136, which holds
+ * for a tensor amax of at least 2^-89 (then t >= 2^-101); a smaller tensor
+ * returns -2.
+ */
+static double nv_qstar6(double ax, double A, double sgn) {
+    int best = 0;
+    if (A > 0.0) {
+        double best_d = fabs(6.0 * ax - E2M1_GRID[0] * A);
+        for (int c = 1; c < 8; ++c) {
+            double d = fabs(6.0 * ax - E2M1_GRID[c] * A);
+            if (d < best_d || (d == best_d && (c & 1) == 0 && (best & 1) == 1)) {
+                best = c;
+                best_d = d;
+            }
+        }
+    }
+    return sgn * E2M1_GRID[best] * A;
+}
+
+/* The terms of element (r, c): x6 = 6x, qs6 = 6 Q_s(x), qst6 = 6 Q*(x),
+ * and s6 = 6 sb t, the largest value the block can represent; returns the
+ * code magnitude g (0..7). */
+static int nv_terms(const uint16_t* x, int64_t ldx, const uint8_t* q, const uint8_t* sc, float t,
+                    int64_t cols, int64_t r, int64_t c, double* x6, double* qs6, double* qst6,
+                    double* s6) {
+    const uint16_t* xb = x + r * ldx + (c / 16) * 16;
+    float A = 0.0f;
+    for (int k = 0; k < 16; ++k)
+        if (absf_bf16(xb[k]) > A) A = absf_bf16(xb[k]);
+    const uint16_t h = x[r * ldx + c];
+    const float xv = orc_bf16_value(h);
+    const double sgn = (h & 0x8000u) ? -1.0 : 1.0;
+    const uint8_t byte = q[r * (cols / 2) + c / 2];
+    const int g = ((c & 1) ? (byte >> 4) : (byte & 15)) & 7;
+    const double sb = orc_e4m3_value(sc[r * (cols / 16) + c / 16]);
+    *x6 = 6.0 * (double)xv;
+    *qs6 = sgn * 6.0 * E2M1_GRID[g] * sb * (double)t;
+    *qst6 = nv_qstar6(fabs((double)xv), (double)A, sgn);
+    *s6 = 6.0 * sb * (double)t;
+    return g;
+}
+
+static int nv_quantize_all(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                           uint8_t** q, uint8_t** sc, float* t) {
+    *q = (uint8_t*)malloc((size_t)(rows * cols / 2 + 1));
+    *sc = (uint8_t*)malloc((size_t)(rows * cols / 16 + 1));
+    if (!*q || !*sc) return -1;
+    return orc_quantize(ORC_NVFP4, x, rows, cols, ldx, NULL, 1, NULL, 0, *q, *sc, t, NULL);
+}
+
+/* Per-element components times 6, NVFP4: out[4][rows*cols] (FP64
+ * differences of the exact terms). */
+int orc_error_components_nv(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                            double* out) {
+    if (cols % 16 != 0) return -1;
+    uint8_t *q = NULL, *sc = NULL;
+    float t = 1.0f;
+    int rc = nv_quantize_all(x, rows, cols, ldx, &q, &sc, &t);
+    const int64_t n = rows * cols;
+    for (int64_t r = 0; rc == 0 && r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c) {
+            double x6, qs6, qst6, s6;
+            const int g = nv_terms(x, ldx, q, sc, t, cols, r, c, &x6, &qs6, &qst6, &s6);
+            const int64_t i = r * cols + c;
+            out[0 * n + i] = x6 - qs6;
+            out[1 * n + i] = g ? qst6 - qs6 : 0.0;
+            out[2 * n + i] = g ? 0.0 : x6;
+            out[3 * n + i] = g ? x6 - qst6 : 0.0;
+        }
+    free(q);
+    free(sc);
+    return rc;
+}
+
+/* 1 if v is a multiple of 2^-136 (or zero), so the fixed point holds it. */
+static int fix_exact(double v) {
+    if (v == 0.0) return 1;
+    return ldexp(v, -FIX_LSB_EXP) == floor(ldexp(v, -FIX_LSB_EXP));
+}
+
+static void fix_neg(uint64_t a[FIX_LIMBS]) {
+    unsigned __int128 c = 1;
+    for (int i = 0; i < FIX_LIMBS; ++i) {
+        c += (unsigned __int128)(~a[i]);
+        a[i] = (uint64_t)c;
+        c >>= 64;
+    }
+}
+
+int orc_error_decompose_nv(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                           orc_err_stats* out) {
+    if (cols % 16 != 0) return -1;
+    memset(out, 0, sizeof *out);
+    uint8_t *q = NULL, *sc = NULL;
+    float t = 1.0f;
+    if (nv_quantize_all(x, rows, cols, ldx, &q, &sc, &t) != 0) {
+        free(q);
+        free(sc);
+        return -1;
+    }
+    /* term sums: S[0] = sum of 6x where g == 0, S[1] = sum of 6x where g != 0,
+     * S[2] = sum of 6 Q*(x) where g != 0, S[3] = sum of 6 Q_s(x) */
+    uint64_t S[4][FIX_LIMBS];
+    memset(S, 0, sizeof S);
+    double sq[4] = {0, 0, 0, 0}, cross = 0.0;
+    int64_t ndz = 0, nclip = 0;
+    int ok = 1;
+    for (int64_t r = 0; r < rows && ok; ++r)
+        for (int64_t c = 0; c < cols; ++c) {
+            double x6, qs6, qst6, s6;
+            const int g = nv_terms(x, ldx, q, sc, t, cols, r, c, &x6, &qs6, &qst6, &s6);
+            if (!fix_exact(x6) || !fix_exact(qs6) || !fix_exact(qst6)) {
+                ok = 0;
+                break;
+            }
+            fix_add(S[g ? 1 : 0], x6);
+            if (g) fix_add(S[2], qst6);
+            fix_add(S[3], qs6);
+            const double xv = x6 / 6.0;
+            if (g == 0 && xv != 0.0) ++ndz;
+            if (fabs(xv) > s6) ++nclip;   /* |x| above 6 sb t */
+            const double ct = (x6 - qs6) / 6.0;
+            const double csb = g ? (qst6 - qs6) / 6.0 : 0.0;
+            const double cdz = g ? 0.0 : xv;
+            const double cgn = g ? (x6 - qst6) / 6.0 : 0.0;
+            sq[0] += ct * ct;
+            sq[1] += csb * csb;
+            sq[2] += cdz * cdz;
+            sq[3] += cgn * cgn;
+            cross += csb * cgn;
+        }
+    free(q);
+    free(sc);
+    if (!ok) return -2;
+    /* total = S0 + S1 - S3, scale_bias = S2 - S3, deadzone = S0, grid_noise = S1 - S2 */
+    uint64_t tot[4][FIX_LIMBS], neg3[FIX_LIMBS], neg2[FIX_LIMBS];
+    memcpy(neg3, S[3], sizeof neg3);
+    fix_neg(neg3);
+    memcpy(neg2, S[2], sizeof neg2);
+    fix_neg(neg2);
+    memcpy(tot[0], S[0], sizeof tot[0]);
+    fix_add_fix(tot[0], S[1]);
+    fix_add_fix(tot[0], neg3);
+    memcpy(tot[1], S[2], sizeof tot[1]);
+    fix_add_fix(tot[1], neg3);
+    memcpy(tot[2], S[0], sizeof tot[2]);
+    memcpy(tot[3], S[1], sizeof tot[3]);
+    fix_add_fix(tot[3], neg2);
+    for (int c = 0; c < 4; ++c) {
+        for (int i = 0; i < FIX_LIMBS; ++i) out->exact[c][i] = (int64_t)tot[c][i];
+        out->sum[c] = fix_to_double(tot[c]) / 6.0;
+        out->sumsq[c] = sq[c];
+    }
+    out->cross_sb_gn = cross;
+    out->n_elems = rows * cols;
+    out->n_deadzone = ndz;
+    out->n_clipped = nclip;
+    return 0;
+}

@@ -102,6 +102,10 @@ def lib():
         L.orc_error_components.argtypes = [P, i64, i64, i64, P]
         L.orc_error_decompose.restype = ctypes.c_int
         L.orc_error_decompose.argtypes = [P, i64, i64, i64, ctypes.POINTER(ErrStats)]
+        L.orc_error_components_nv.restype = ctypes.c_int
+        L.orc_error_components_nv.argtypes = [P, i64, i64, i64, P]
+        L.orc_error_decompose_nv.restype = ctypes.c_int
+        L.orc_error_decompose_nv.argtypes = [P, i64, i64, i64, ctypes.POINTER(ErrStats)]
         _lib = L
     return _lib
 
@@ -327,14 +331,16 @@ def grouped_gemm_points(fmt, offsets, aq, as_, ats, bq, bs, bts, chan_idx, resid
 COMPONENTS = ("total", "scale_bias", "deadzone", "grid_noise")
 
 
-def error_components6(x: np.ndarray) -> np.ndarray:
-    """Per-element components times 6: float64 [4, rows, cols]."""
+def error_components6(x: np.ndarray, fmt: int = MXFP4) -> np.ndarray:
+    """Per-element components times 6: float64 [4, rows, cols] (total,
+    scale_bias, deadzone, grid_noise) under the MXFP4 or NVFP4 quantizer."""
     x = _c(x, np.uint16)
     rows, cols = x.shape
     out = np.zeros((4, rows, cols), np.float64)
-    rc = lib().orc_error_components(_p(x), rows, cols, cols, _p(out))
+    f = lib().orc_error_components if fmt == MXFP4 else lib().orc_error_components_nv
+    rc = f(_p(x), rows, cols, cols, _p(out))
     if rc != 0:
-        raise ValueError("cols must be a multiple of 32")
+        raise ValueError("cols must be a multiple of the block size")
     return out
 
 
@@ -348,13 +354,18 @@ def fixed_to_int(limbs) -> int:
     return v
 
 
-def error_decompose(x: np.ndarray) -> dict:
+def error_decompose(x: np.ndarray, fmt: int = MXFP4) -> dict:
+    """Exact component sums (and FP64 statistics) of the three-way split under
+    the MXFP4 or NVFP4 quantizer."""
     x = _c(x, np.uint16)
     rows, cols = x.shape
     st = ErrStats()
-    rc = lib().orc_error_decompose(_p(x), rows, cols, cols, ctypes.byref(st))
+    f = lib().orc_error_decompose if fmt == MXFP4 else lib().orc_error_decompose_nv
+    rc = f(_p(x), rows, cols, cols, ctypes.byref(st))
+    if rc == -2:
+        raise ValueError("NVFP4 decomposition: tensor amax below 2^-89 (terms below 2^-136)")
     if rc != 0:
-        raise ValueError("cols must be a multiple of 32")
+        raise ValueError("cols must be a multiple of the block size")
     return {
         "exact": [[int(st.exact[c][i]) for i in range(5)] for c in range(4)],
         "exact_int": [fixed_to_int(st.exact[c]) for c in range(4)],
