@@ -381,6 +381,16 @@ def main():
     print(f"[bench] gemm {t_gemm * 1e6:.2f} us, quantize {t_quant * 1e6:.2f} us per launch",
           file=sys.stderr, flush=True)
     t_sel = timed(lambda i: select(), reps) if online else None
+    # the exact three-way error decomposition of the activations
+    t_dec = None
+    if name != "moe_nvfp4":
+        dec_out = torch.zeros(fq.binding.ERR_STATS_BYTES, dtype=torch.uint8, device=dev)
+        dec_ws = torch.empty(max(fq.error_decompose_workspace_bytes(M, K), 16), dtype=torch.uint8,
+                             device=dev)
+        t_dec = timed(lambda i: fq.error_decompose_into(fmt, x, dec_out, dec_ws), reps)
+        dec_bytes = M * K * 2
+        print(f"[bench] error decomposition {t_dec * 1e6:.2f} us per call", file=sys.stderr,
+              flush=True)
     if online:
         print(f"[bench] channel selection {t_sel * 1e6:.2f} us per call", file=sys.stderr,
               flush=True)
@@ -433,6 +443,10 @@ def main():
         "cpu_baseline": cpu,
         "kernel_src_hash": kh,
     }
+    if t_dec is not None:
+        out["decompose_us"] = round(t_dec * 1e6, 3)
+        out["decompose_gbps"] = round(dec_bytes / t_dec / 1e9, 1)
+        out["decompose_frac_hbm"] = round(dec_bytes / t_dec / 1e9 / HBM_PEAK_GBS, 4)
     if online:
         out["select_us"] = round(t_sel * 1e6, 3)
         out["select_gbps"] = round(select_bytes / t_sel / 1e9, 1)

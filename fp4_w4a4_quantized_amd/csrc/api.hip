@@ -310,15 +310,15 @@ int fp4q_error_decompose(fp4q_format_t fmt, const uint16_t* x, int64_t rows, int
                          int64_t ldx, fp4q_err_stats_t* out, void* workspace,
                          size_t workspace_bytes, void* stream) {
   if (!fmt_ok(fmt)) return FP4Q_ERR_INVALID;
-  if (rows < 0 || cols <= 0 || cols % 32 != 0 || ldx < cols || ldx % 8 != 0)
+  if (rows < 0 || cols <= 0 || cols % blk_of(fmt) != 0 || ldx < cols || ldx % 8 != 0)
     return FP4Q_ERR_INVALID;
   if (!out || !aligned(out, 8)) return FP4Q_ERR_INVALID;
   if (rows > 0 && (!x || !aligned(x, 16))) return FP4Q_ERR_INVALID;
-  if (fmt != FP4Q_MXFP4) return FP4Q_ERR_UNSUPPORTED;
   const size_t need = fp4q::decompose_workspace_bytes(rows, cols);
   if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return FP4Q_ERR_WORKSPACE;
   clear_error();
-  fp4q::launch_decompose(x, rows, cols, ldx, out, workspace, static_cast<hipStream_t>(stream));
+  fp4q::launch_decompose(fmt, x, rows, cols, ldx, out, workspace,
+                         static_cast<hipStream_t>(stream));
   return check_launch();
 }
 

@@ -77,98 +77,11 @@ __device__ __forceinline__ void fix_add_fix(uint64_t (&a)[5], const uint64_t* b)
   }
 }
 
-// 6x times the components of one element; returns the E2M1 code magnitude.
-__device__ __forceinline__ uint32_t elem_components(uint32_t h, float amax, float inv_s, int e,
-                                                    double (&c6)[4]) {
-  const float x = bf16_to_f32(h);
-  const float ax = bf16_to_f32(h & 0x7FFFu);
-  const double sgn = (h & 0x8000u) ? -1.0 : 1.0;
-  const double x6 = 6.0 * (double)x;
-  const uint32_t mag = e2m1_mag_code(ax * inv_s);
-  const double qs6 = sgn * (6.0 * (double)e2m1_mag_value(mag)) * (double)exp2i(e);
-  // Q*: nearest grid point to 6|x|/amax, decided exactly on 6|x| vs tau*amax
-  const double a6 = 6.0 * (double)ax, A = (double)amax;
-  uint32_t gs = 0;
-  if (amax > 0.0f)
-    gs = (uint32_t)(a6 > 0.25 * A) + (uint32_t)(a6 >= 0.75 * A) + (uint32_t)(a6 > 1.25 * A) +
-         (uint32_t)(a6 >= 1.75 * A) + (uint32_t)(a6 > 2.5 * A) + (uint32_t)(a6 >= 3.5 * A) +
-         (uint32_t)(a6 > 5.0 * A);
-  const double qst6 = sgn * (double)e2m1_mag_value(gs) * A;
-  c6[0] = x6 - qs6;
-  if (mag == 0) {
-    c6[1] = 0.0;
-    c6[2] = x6;
-    c6[3] = 0.0;
-  } else {
-    c6[1] = qst6 - qs6;
-    c6[2] = 0.0;
-    c6[3] = x6 - qst6;
-  }
-  return mag;
-}
-
-__global__ void __launch_bounds__(DEC_THREADS) k_decompose(const uint16_t* __restrict__ x,
-                                                           int64_t rows, int64_t cols,
-                                                           int64_t ldx,
-                                                           DecPartial* __restrict__ part) {
-  uint64_t fix[4][5];
-#pragma unroll
-  for (int c = 0; c < 4; ++c)
-#pragma unroll
-    for (int i = 0; i < 5; ++i) fix[c][i] = 0;
-  double sq[4] = {0.0, 0.0, 0.0, 0.0}, cross = 0.0;
-  int64_t ndz = 0, nclip = 0;
-
-  const int64_t nb = cols >> 5, total = rows * nb;
-  for (int64_t id = (int64_t)blockIdx.x * DEC_THREADS + threadIdx.x; id < total;
-       id += (int64_t)gridDim.x * DEC_THREADS) {
-    const int64_t row = id / nb, b = id - row * nb;
-    uint32_t w[16];
-    const u32x4* src = reinterpret_cast<const u32x4*>(x + row * ldx + b * 32);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      u32x4 tv = __builtin_nontemporal_load(src + v);
-      w[4 * v] = tv.x; w[4 * v + 1] = tv.y; w[4 * v + 2] = tv.z; w[4 * v + 3] = tv.w;
-    }
-    uint32_t am = 0, mn = 0xFFFFu;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      uint32_t lo = w[i] & 0x7FFFu, hi = (w[i] >> 16) & 0x7FFFu;
-      am = max(am, max(lo, hi));
-      mn = min(mn, min(lo ? lo : 0xFFFFu, hi ? hi : 0xFFFFu));
-    }
-    const float amax = bf16_to_f32(am);
-    const int e = mx_exponent(amax);
-    const float inv_s = exp2i(-e);
-    // exponent of the least significant bit of the smallest non-zero element
-    // and of amax; FP64 block sums are exact when the span is small
-    const int ea = (int)(am >> 7) - 127;
-    const int lsb_min = (mn == 0xFFFFu) ? ea : (((mn >> 7) == 0) ? -133 : (int)(mn >> 7) - 134);
-    const bool fast = (am >> 7) == 0 || (ea + 11) - min(lsb_min + 1, ea - 8) <= 52;
-    double bsum[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-    for (int k = 0; k < 32; ++k) {
-      const uint32_t h = (w[k >> 1] >> ((k & 1) * 16)) & 0xFFFFu;
-      double c6[4];
-      const uint32_t mag = elem_components(h, amax, inv_s, e, c6);
-      ndz += (mag == 0 && (h & 0x7FFFu) != 0) ? 1 : 0;
-      nclip += ((double)bf16_to_f32(h & 0x7FFFu) > 6.0 * (double)exp2i(e)) ? 1 : 0;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const double cv = c6[c] / 6.0;
-        sq[c] += cv * cv;
-        if (fast) bsum[c] += c6[c];
-        else fix_add(fix[c], c6[c]);
-      }
-      cross += (c6[1] / 6.0) * (c6[3] / 6.0);
-    }
-    if (fast) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) fix_add(fix[c], bsum[c]);
-    }
-  }
-
-  // workgroup reduction through LDS in a fixed tree order
+// Reduce the per-thread sums over the workgroup through LDS in a fixed tree
+// order and write the workgroup's partial record.
+__device__ __forceinline__ void write_partial(const uint64_t (&fix)[4][5], const double (&sq)[4],
+                                              double cross, int64_t ndz, int64_t nclip,
+                                              DecPartial* __restrict__ part) {
   __shared__ uint64_t sfix[DEC_THREADS][4][5];
   __shared__ double ssq[DEC_THREADS][5];
   __shared__ int64_t scnt[DEC_THREADS][2];
@@ -213,6 +126,266 @@ __global__ void __launch_bounds__(DEC_THREADS) k_decompose(const uint16_t* __res
     o->ndz = scnt[0][0];
     o->nclip = scnt[0][1];
   }
+}
+
+// ---- NVFP4 ------------------------------------------------------------------
+//
+// The same split under the NVFP4 quantizer: per 16-block with amax A, the
+// quantizer's own decisions (scale code of (A / 6) / t, element code of
+// x / (sb t) rounded on the E2M1 grid) give Q_s(x) = g sb t, and the ideal
+// scale is again A / 6.  Terms times 6: x6 = 6x, qs6 = 6 g sb t, qst6 = g* A.
+// One thread per block sums, per block and exactly in FP64,
+//   S0 = x6 where g = 0,  S1 = x6 where g != 0,  S2 = qst6 where g != 0,
+//   S3 = qs6  (= 3 sb t times an integer, S2 = A/2 times an integer),
+// and the components are total = S0 + S1 - S3, scale_bias = S2 - S3,
+// deadzone = S0, grid_noise = S1 - S2.  x6 sums take the fixed point
+// element by element when the block's exponent span would make an FP64 sum
+// inexact.  Exact while every term is a multiple of 2^-136: a tensor amax of
+// at least 2^-89.
+
+// Per-workgroup maximum of |x| (BF16 magnitude pattern).
+__global__ void __launch_bounds__(DEC_THREADS) k_dec_amax(const uint16_t* __restrict__ x,
+                                                          int64_t rows, int64_t cols, int64_t ldx,
+                                                          uint32_t* __restrict__ amax_part) {
+  __shared__ uint32_t red[DEC_THREADS / 64];
+  const int64_t nb = cols >> 4, total = rows * nb;
+  uint32_t m = 0;
+  for (int64_t id = (int64_t)blockIdx.x * DEC_THREADS + threadIdx.x; id < total;
+       id += (int64_t)gridDim.x * DEC_THREADS) {
+    const int64_t row = id / nb, b = id - row * nb;
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + row * ldx + b * 16);
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const u32x4 tv = __builtin_nontemporal_load(src + v);
+      const uint32_t w[4] = {tv.x, tv.y, tv.z, tv.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = max(m, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+    }
+  }
+  for (int s = 32; s > 0; s >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, s));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = 0;
+#pragma unroll
+    for (int i = 0; i < DEC_THREADS / 64; ++i) r = max(r, red[i]);
+    amax_part[blockIdx.x] = r;
+  }
+}
+
+__device__ __forceinline__ void fix_neg(uint64_t (&a)[5]) {
+  uint64_t carry = 1;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const uint64_t v = ~a[i];
+    const uint64_t s = v + carry;
+    carry = (s < v) ? 1ull : 0ull;
+    a[i] = s;
+  }
+}
+
+// One block of NE elements (w: NE/2 packed BF16 pairs) into the thread's
+// sums.  Per block: the quantizer's decisions, then the term sums
+//   S0 = sum of 6x where g = 0,  S1 = sum of 6x where g != 0,
+//   S2 = sum of 6 Q*(x) where g != 0 (A/2 times an integer),
+//   S3 = sum of 6 Q_s(x) (3 s times an integer, s the block's scale),
+// each added to the fixed point once per block (sums of x in FP64 when the
+// block's exponent span keeps them exact, else element by element).  The
+// decisions run in FP32, where every operand is exact: 6|x| and tau * A have
+// at most 11 significant bits, and x scaled by a power of two (MXFP4) or
+// divided by the quantizer's own divisor (NVFP4, the correctly rounded
+// quotient it forms) is what the quantizer rounds.  The squares for the
+// statistics come from component values that are exact (FP32 for MXFP4;
+// FP64 where the NVFP4 tensor scale enters).
+constexpr uint64_t TWICE_E2M1 = 0x0C08060403020100ull;
+
+template <int FMT, int NE>
+__device__ __forceinline__ void block_terms(const uint32_t (&w)[NE / 2], float t,
+                                            uint64_t (&S)[4][5], double (&sq)[4], double& cross,
+                                            int64_t& ndz, int64_t& nclip) {
+  uint32_t am = 0, mn = 0xFFFFu;
+#pragma unroll
+  for (int i = 0; i < NE / 2; ++i) {
+    const uint32_t lo = w[i] & 0x7FFFu, hi = (w[i] >> 16) & 0x7FFFu;
+    am = max(am, max(lo, hi));
+    mn = min(mn, min(lo ? lo : 0xFFFFu, hi ? hi : 0xFFFFu));
+  }
+  const float A = bf16_to_f32(am);
+  // the block's scale s: MXFP4 2^e; NVFP4 sb * t (exact real product)
+  float e8 = 0.0f, sbf = 1.0f, d = 0.0f, y = 0.0f;
+  double s_d;
+  if (FMT == FP4Q_MXFP4) {
+    const int e = mx_exponent(A);
+    e8 = __uint_as_float((uint32_t)(e + 127) << 23);  // the E8M0 scale operand
+    s_d = (double)exp2i(e);
+  } else {
+    sbf = e4m3_value(e4m3_encode((A / 6.0f) / t));
+    d = sbf * t;  // the quantizer's divisor
+    y = 1.0f / d;
+    s_d = (double)sbf * (double)t;
+  }
+  const double s6 = 6.0 * s_d;  // the block's largest representable magnitude
+  // The FP32 work below (6|x|, tau * A, the component values) is taken times
+  // a power of two sc, exact and order-preserving, so that blocks near the
+  // top of the BF16 range do not overflow (6 * 2^127 does); 1/sc undoes it
+  // in FP64.
+  const float sc = (am >> 7) >= 127 + 120 ? 0x1p-16f : 1.0f;
+  const double isc = (double)(1.0f / sc);
+  const float As = A * sc;
+  // tau * A, the Q* decision thresholds on 6|x|
+  const float t0 = 0.25f * As, t1 = 0.75f * As, t2 = 1.25f * As, t3 = 1.75f * As,
+              t4 = 2.5f * As, t5 = 3.5f * As, t6 = 5.0f * As;
+  // FP64 sums of up to 32 values below 2^(ea+1) with least bit 2^lsb_min are
+  // exact when (ea + 6) - lsb_min <= 53
+  const int ea = (int)(am >> 7) - 127;
+  const int lsb_min = (mn == 0xFFFFu) ? ea : (((mn >> 7) == 0) ? -133 : (int)(mn >> 7) - 134);
+  const bool fast = (am >> 7) == 0 || (ea + 6) - lsb_min <= 53;
+  double x0 = 0.0, x1 = 0.0;
+  int i1 = 0, i2 = 0;  // sums of sign * 2 v_g, and of sign * 2 v_g* where g != 0
+  // eight elements (one 16-byte piece) at a time keeps the unrolled body
+  // within the register budget
+#pragma unroll 1
+  for (int v = 0; v < NE / 8; ++v) {
+    uint32_t wv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      wv[j] = NE == 16 ? (v == 0 ? w[j] : w[4 + j])
+                       : (v == 0 ? w[j] : v == 1 ? w[4 + j] : v == 2 ? w[8 + j] : w[12 + j]);
+    // the quantizer's codes of the eight elements, by the same hardware
+    // conversion: x / 2^e (MXFP4), or its correctly rounded quotient by the
+    // divisor sb * t (NVFP4)
+    float xs[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) xs[k] = bf16_to_f32((wv[k >> 1] >> ((k & 1) * 16)) & 0xFFFFu);
+    uint32_t codes;
+    if (FMT == FP4Q_MXFP4) {
+      codes = e2m1_pack8(xs, e8);
+    } else {
+      float qs[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        qs[k] = d >= 0x1p-96f ? div_rn(xs[k], d, y) : (d > 0.0f ? xs[k] / d : xs[k] * 0.0f);
+      codes = e2m1_pack8(qs);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t h = (wv[k >> 1] >> ((k & 1) * 16)) & 0xFFFFu;
+      const float xv = xs[k], ax = bf16_to_f32(h & 0x7FFFu);
+      const bool neg = (h & 0x8000u) != 0;
+      const uint32_t g = (codes >> (4 * k)) & 7u;
+      const float a6 = 6.0f * (ax * sc);
+      const uint32_t gs = A > 0.0f ? (uint32_t)(a6 > t0) + (uint32_t)(a6 >= t1) + (uint32_t)(a6 > t2) +
+                                         (uint32_t)(a6 >= t3) + (uint32_t)(a6 > t4) +
+                                         (uint32_t)(a6 >= t5) + (uint32_t)(a6 > t6)
+                                   : 0u;
+      // twice the E2M1 magnitudes {0, 1, 2, 3, 4, 6, 8, 12}, one byte per code
+      const int tg = (int)((TWICE_E2M1 >> (8 * g)) & 0xFFu);
+      const int tgs = (int)((TWICE_E2M1 >> (8 * gs)) & 0xFFu);
+      i1 += neg ? -tg : tg;
+      if (g) i2 += neg ? -tgs : tgs;
+      if (fast) {
+        if (g) x1 += (double)xv;
+        else x0 += (double)xv;
+      } else {
+        fix_add(S[0], g ? 0.0 : 6.0 * (double)xv);
+        fix_add(S[1], g ? 6.0 * (double)xv : 0.0);
+      }
+      ndz += (g == 0 && ax != 0.0f) ? 1 : 0;
+      nclip += (double)ax > s6 ? 1 : 0;
+      // component values times 6 (times sc in FP32, exact)
+      const float x6 = 6.0f * (xv * sc);
+      const float q6s = (neg ? -0.5f : 0.5f) * (float)tgs * As;  // 6 Q*(x)
+      const float m6 = (neg ? -3.0f : 3.0f) * (float)tg;         // 6 Q_s(x) / s
+      double ct, csb;
+      if (FMT == FP4Q_MXFP4) {
+        const float q6a = m6 * (float)(s_d * (double)sc);  // a power-of-two scale
+        ct = (double)(x6 - q6a) * isc;  // differences within the block's range: exact
+        csb = g ? (double)(q6s - q6a) * isc : 0.0;
+      } else {
+        const double q6a = (double)(m6 * sbf) * (double)t;
+        ct = 6.0 * (double)xv - q6a;
+        csb = g ? (double)q6s * isc - q6a : 0.0;
+      }
+      const double cdz = g ? 0.0 : (double)x6 * isc;
+      const double cgn = g ? (double)(x6 - q6s) * isc : 0.0;
+      sq[0] = __builtin_fma(ct, ct, sq[0]);
+      sq[1] = __builtin_fma(csb, csb, sq[1]);
+      sq[2] = __builtin_fma(cdz, cdz, sq[2]);
+      sq[3] = __builtin_fma(cgn, cgn, sq[3]);
+      cross = __builtin_fma(csb, cgn, cross);
+    }
+  }
+  if (fast) {
+    fix_add(S[0], 6.0 * x0);
+    fix_add(S[1], 6.0 * x1);
+  }
+  fix_add(S[2], (double)i2 * 0.5 * (double)A);
+  fix_add(S[3], (double)i1 * 3.0 * s_d);
+}
+
+// One thread per block (32 elements MXFP4, 16 NVFP4).  NVFP4 first reduces
+// the per-workgroup amax words of k_dec_amax to the tensor scale.
+template <int FMT>
+__global__ void __launch_bounds__(DEC_THREADS) k_decompose(const uint16_t* __restrict__ x,
+                                                           int64_t rows, int64_t cols, int64_t ldx,
+                                                           const uint32_t* __restrict__ amax_part,
+                                                           int nparts,
+                                                           DecPartial* __restrict__ part) {
+  constexpr int NE = (FMT == FP4Q_NVFP4) ? 16 : 32;
+  float t = 1.0f;
+  if (FMT == FP4Q_NVFP4) {
+    __shared__ uint32_t sam;
+    if (threadIdx.x == 0) {
+      uint32_t m = 0;
+      for (int i = 0; i < nparts; ++i) m = max(m, amax_part[i]);
+      sam = m;
+    }
+    __syncthreads();
+    t = nv_tensor_scale(bf16_to_f32(sam));
+  }
+  uint64_t S[4][5];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int i = 0; i < 5; ++i) S[c][i] = 0;
+  double sq[4] = {0.0, 0.0, 0.0, 0.0}, cross = 0.0;
+  int64_t ndz = 0, nclip = 0;
+
+  const int64_t nb = cols / NE, total = rows * nb;
+  for (int64_t id = (int64_t)blockIdx.x * DEC_THREADS + threadIdx.x; id < total;
+       id += (int64_t)gridDim.x * DEC_THREADS) {
+    const int64_t row = id / nb, b = id - row * nb;
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + row * ldx + b * NE);
+    uint32_t w[NE / 2];
+#pragma unroll
+    for (int v = 0; v < NE / 8; ++v) {
+      const u32x4 tv = __builtin_nontemporal_load(src + v);
+      w[4 * v] = tv.x; w[4 * v + 1] = tv.y; w[4 * v + 2] = tv.z; w[4 * v + 3] = tv.w;
+    }
+    block_terms<FMT, NE>(w, t, S, sq, cross, ndz, nclip);
+  }
+
+  // components from the term sums: total = S0 + S1 - S3, scale_bias =
+  // S2 - S3, deadzone = S0, grid_noise = S1 - S2
+  uint64_t fix[4][5], n2[5], n3[5];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    n2[i] = S[2][i];
+    n3[i] = S[3][i];
+    fix[0][i] = S[0][i];
+    fix[1][i] = S[2][i];
+    fix[2][i] = S[0][i];
+    fix[3][i] = S[1][i];
+  }
+  fix_neg(n2);
+  fix_neg(n3);
+  fix_add_fix(fix[0], S[1]);
+  fix_add_fix(fix[0], n3);
+  fix_add_fix(fix[1], n3);
+  fix_add_fix(fix[3], n2);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) sq[c] /= 36.0;  // the squares were taken times 6
+  write_partial(fix, sq, cross / 36.0, ndz, nclip, part);
 }
 
 // Approximate double value of a 320-bit two's complement fixed-point sum.
@@ -301,23 +474,38 @@ __global__ void __launch_bounds__(DEC_THREADS) k_decompose_final(const DecPartia
   }
 }
 
-static int64_t dec_grid(int64_t rows, int64_t cols) {
-  int64_t nb = rows * (cols / 32);
+// Workgroups for `blk`-element blocks, one block per thread.
+static int64_t dec_grid(int64_t rows, int64_t cols, int blk) {
+  int64_t nb = rows * (cols / blk);
   int64_t g = (nb + DEC_THREADS - 1) / DEC_THREADS;
   if (g < 1) g = 1;
   return g < DEC_MAX_WG ? g : DEC_MAX_WG;
 }
 
+// Partial records (for either format: the NVFP4 grid is the larger), then
+// the NVFP4 path's per-workgroup amax words.
 size_t decompose_workspace_bytes(int64_t rows, int64_t cols) {
-  return (size_t)dec_grid(rows, cols) * sizeof(DecPartial);
+  const int64_t g = dec_grid(rows, cols, 16);
+  return (size_t)g * sizeof(DecPartial) + (size_t)((g * 4 + 255) / 256 * 256);
 }
 
-int launch_decompose(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+int launch_decompose(int fmt, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                      fp4q_err_stats_t* out, void* ws, hipStream_t stream) {
-  const int64_t g = dec_grid(rows, cols);
   DecPartial* part = static_cast<DecPartial*>(ws);
-  hipLaunchKernelGGL(k_decompose, dim3((unsigned)g), dim3(DEC_THREADS), 0, stream, x, rows, cols,
-                     ldx, part);
+  if (fmt == FP4Q_NVFP4) {
+    const int64_t g = dec_grid(rows, cols, 16);
+    uint32_t* amax = reinterpret_cast<uint32_t*>(part + g);
+    hipLaunchKernelGGL(k_dec_amax, dim3((unsigned)g), dim3(DEC_THREADS), 0, stream, x, rows, cols,
+                       ldx, amax);
+    hipLaunchKernelGGL(k_decompose<FP4Q_NVFP4>, dim3((unsigned)g), dim3(DEC_THREADS), 0, stream,
+                       x, rows, cols, ldx, amax, (int)g, part);
+    hipLaunchKernelGGL(k_decompose_final, dim3(1), dim3(DEC_THREADS), 0, stream, part, (int)g,
+                       rows * cols, out);
+    return 0;
+  }
+  const int64_t g = dec_grid(rows, cols, 32);
+  hipLaunchKernelGGL(k_decompose<FP4Q_MXFP4>, dim3((unsigned)g), dim3(DEC_THREADS), 0, stream, x,
+                     rows, cols, ldx, nullptr, 0, part);
   hipLaunchKernelGGL(k_decompose_final, dim3(1), dim3(DEC_THREADS), 0, stream, part, (int)g,
                      rows * cols, out);
   return 0;

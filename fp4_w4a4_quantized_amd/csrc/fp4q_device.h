@@ -78,6 +78,40 @@ __device__ __forceinline__ float nv_tensor_scale(float amax) {
   return (amax == 0.0f || t == 0.0f) ? 1.0f : t;
 }
 
+// x / d rounded to nearest FP32, for the quotients the quantizer forms
+// (|x| <= about 7 d).  With y = RN(1/d), q0 = RN(a y), a = |x|, is within two
+// ulps of a/d; one FMA correction brings it within one ulp, and a second
+// yields the correctly rounded quotient by Markstein's theorem (the residual
+// a - q d is exact when nothing underflows).  The sign is x's sign bit: the
+// corrections would turn -0 into +0.  Valid for d >= 2^-96; smaller divisors
+// take the IEEE division instruction sequence.
+__device__ __forceinline__ float div_rn(float x, float d, float y) {
+  const float a = fabsf(x);
+  float q = a * y;
+  float r = __builtin_fmaf(-q, d, a);
+  q = __builtin_fmaf(r, y, q);
+  r = __builtin_fmaf(-q, d, a);
+  q = __builtin_fmaf(r, y, q);
+  return __uint_as_float(__float_as_uint(q) | (__float_as_uint(x) & 0x80000000u));
+}
+
+// E2M1 codes of 8 FP32 values, packed two per byte (even element in the low
+// nibble), by gfx950's v_cvt_scalef32_pk_fp4_f32 with scale 1: nearest-even
+// on the E2M1 grid, saturating at 6, sign kept (also for -0 and values that
+// round to zero) -- the same decisions as the threshold rule of the grid.
+// With an E8M0 scale 2^e (passed as the float whose exponent field is the
+// code, 0.0f for code 0) the instruction divides by 2^e exactly before
+// rounding, for every code 0..254 (checked on the GPU against pre-scaled
+// inputs), which saves the MXFP4 path its eight multiplies.
+__device__ __forceinline__ uint32_t e2m1_pack8(const float (&v)[8], float scale = 1.0f) {
+  uint32_t p = 0;
+  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[0], v[1], scale, 0);
+  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[2], v[3], scale, 1);
+  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[4], v[5], scale, 2);
+  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[6], v[7], scale, 3);
+  return p;
+}
+
 // Byte offsets of packed FP4 operands in the two layouts (include/fp4q.h
 // defines them).  Row-major: codes [rows][K/2], scales [rows][K/blk].
 // Tiled (K % 128 == 0): codes in 1 KB blocks, one per (16-row group,

@@ -72,7 +72,7 @@ void launch_permute(int fmt, const uint16_t* x, int64_t ldx, int64_t tokens, int
                     uint16_t* r_out, hipStream_t stream);
 
 size_t decompose_workspace_bytes(int64_t rows, int64_t cols);
-int launch_decompose(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+int launch_decompose(int fmt, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                      fp4q_err_stats_t* out, void* ws, hipStream_t stream);
 
 }  // namespace fp4q

@@ -328,6 +328,14 @@ int fp4q_permute_quantized(fp4q_format_t fmt, const uint16_t* x, int64_t tokens,
  * Q_s is the MXFP4 quantizer, Q* the same E2M1 rounding with s*.  So
  * total = scale_bias + deadzone + grid_noise element by element, and the
  * exact integer sums below satisfy the identity bit for bit.
+ *
+ * The same split under the NVFP4 quantizer (16-element blocks): the actual
+ * quantization is fp4q_quantize's own (one group): Q_s(x) = g * sb * t with
+ * its code g, E4M3 block scale value sb and tensor scale t (the exact
+ * product); the ideal scale is again s* = amax/6 of the 16-block.  The sums
+ * stay exact while every term (6x, 6 g sb t, g* amax) is a multiple of
+ * 2^-136, which holds for a tensor amax of at least 2^-89 (a precondition,
+ * not checked).
  * ------------------------------------------------------------------------ */
 typedef struct {
     /* 6 * (sum of component c) as a 320-bit two's complement integer in units
@@ -339,11 +347,13 @@ typedef struct {
     double cross_sb_gn;  /* FP64 sum of scale_bias * grid_noise */
     int64_t n_elems;     /* rows * cols */
     int64_t n_deadzone;  /* non-zero inputs quantized to zero */
-    int64_t n_clipped;   /* |x| > 6 * 2^e (0 under the scale rule) */
+    int64_t n_clipped;   /* |x| > 6 * s: 0 for MXFP4 under its scale rule; for
+                            NVFP4 where E4M3 rounded the block scale down */
 } fp4q_err_stats_t;
 
-/*   fmt        must be FP4Q_MXFP4 (NVFP4 gives FP4Q_ERR_UNSUPPORTED)
- *   x          bf16 [rows, cols], ldx as for fp4q_quantize; cols % 32 == 0
+/*   fmt        FP4Q_MXFP4 or FP4Q_NVFP4
+ *   x          bf16 [rows, cols], ldx as for fp4q_quantize; cols a multiple
+ *              of the block size (32 MXFP4, 16 NVFP4)
  *   out        DEVICE pointer to one fp4q_err_stats_t (8-byte aligned)
  *   workspace  device scratch of fp4q_error_decompose_workspace_bytes() */
 size_t fp4q_error_decompose_workspace_bytes(int64_t rows, int64_t cols);

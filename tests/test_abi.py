@@ -168,7 +168,8 @@ def test_error_decompose_rejects(L):
     f = L.fp4q_error_decompose
     assert f(1, A, 4, 48, 48, B, A, 1 << 20, None) == INVALID     # cols % 32
     assert f(1, A, 4, 64, 64, None, A, 1 << 20, None) == INVALID  # no output
-    assert f(0, A, 4, 64, 64, B, A, 1 << 20, None) == UNSUPPORTED  # NVFP4 split is not offered
+    assert f(0, A, 4, 40, 40, B, A, 1 << 20, None) == INVALID  # NVFP4: whole 16-blocks
+    assert f(2, A, 4, 64, 64, B, A, 1 << 20, None) == INVALID  # no such format
     assert f(1, A, 4, 64, 64, B, None, 0, None) == WORKSPACE
     assert f(1, A, 4, 64, 64, B, A, 8, None) == WORKSPACE
 
