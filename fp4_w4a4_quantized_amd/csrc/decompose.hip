@@ -25,7 +25,7 @@
 namespace fp4q {
 
 constexpr int DEC_THREADS = 256;
-constexpr int DEC_MAX_WG = 2048;
+constexpr int DEC_MAX_WG = 512;   // two per CU: one round, and few partial records
 
 struct DecPartial {
   uint64_t fix[4][5];
@@ -334,14 +334,17 @@ __global__ void __launch_bounds__(DEC_THREADS) k_decompose(const uint16_t* __res
   constexpr int NE = (FMT == FP4Q_NVFP4) ? 16 : 32;
   float t = 1.0f;
   if (FMT == FP4Q_NVFP4) {
-    __shared__ uint32_t sam;
-    if (threadIdx.x == 0) {
-      uint32_t m = 0;
-      for (int i = 0; i < nparts; ++i) m = max(m, amax_part[i]);
-      sam = m;
-    }
+    // the tensor amax: the workgroup reduces the per-workgroup words
+    __shared__ uint32_t sred[DEC_THREADS / 64];
+    uint32_t m = 0;
+    for (int i = threadIdx.x; i < nparts; i += DEC_THREADS) m = max(m, amax_part[i]);
+    for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+    if ((threadIdx.x & 63) == 0) sred[threadIdx.x >> 6] = m;
     __syncthreads();
-    t = nv_tensor_scale(bf16_to_f32(sam));
+    m = 0;
+#pragma unroll
+    for (int i = 0; i < DEC_THREADS / 64; ++i) m = max(m, sred[i]);
+    t = nv_tensor_scale(bf16_to_f32(m));
   }
   uint64_t S[4][5];
 #pragma unroll
