@@ -859,36 +859,64 @@ int orc_error_decompose_nv(const uint16_t* x, int64_t rows, int64_t cols, int64_
         return -1;
     }
     /* term sums: S[0] = sum of 6x where g == 0, S[1] = sum of 6x where g != 0,
-     * S[2] = sum of 6 Q*(x) where g != 0, S[3] = sum of 6 Q_s(x) */
+     * S[2] = sum of 6 Q*(x) where g != 0, S[3] = sum of 6 Q_s(x); per row,
+     * then combined in row order (the fixed-point sums are exact in any
+     * order; the FP64 statistics then do not depend on the thread count) */
+    typedef struct {
+        uint64_t S[4][FIX_LIMBS];
+        double sq[4], cross;
+        int64_t ndz, nclip;
+        int bad;
+    } nv_row;
+    nv_row* parts = (nv_row*)calloc((size_t)(rows > 0 ? rows : 1), sizeof(nv_row));
+    if (!parts) {
+        free(q);
+        free(sc);
+        return -1;
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        nv_row* p = &parts[r];
+        for (int64_t c = 0; c < cols; ++c) {
+            double x6, qs6, qst6, s6;
+            const int g = nv_terms(x, ldx, q, sc, t, cols, r, c, &x6, &qs6, &qst6, &s6);
+            if (!fix_exact(x6) || !fix_exact(qs6) || !fix_exact(qst6)) {
+                p->bad = 1;
+                break;
+            }
+            fix_add(p->S[g ? 1 : 0], x6);
+            if (g) fix_add(p->S[2], qst6);
+            fix_add(p->S[3], qs6);
+            const double xv = x6 / 6.0;
+            if (g == 0 && xv != 0.0) ++p->ndz;
+            if (fabs(xv) > s6) ++p->nclip;   /* |x| above 6 sb t */
+            const double ct = (x6 - qs6) / 6.0;
+            const double csb = g ? (qst6 - qs6) / 6.0 : 0.0;
+            const double cdz = g ? 0.0 : xv;
+            const double cgn = g ? (x6 - qst6) / 6.0 : 0.0;
+            p->sq[0] += ct * ct;
+            p->sq[1] += csb * csb;
+            p->sq[2] += cdz * cdz;
+            p->sq[3] += cgn * cgn;
+            p->cross += csb * cgn;
+        }
+    }
     uint64_t S[4][FIX_LIMBS];
     memset(S, 0, sizeof S);
     double sq[4] = {0, 0, 0, 0}, cross = 0.0;
     int64_t ndz = 0, nclip = 0;
     int ok = 1;
-    for (int64_t r = 0; r < rows && ok; ++r)
-        for (int64_t c = 0; c < cols; ++c) {
-            double x6, qs6, qst6, s6;
-            const int g = nv_terms(x, ldx, q, sc, t, cols, r, c, &x6, &qs6, &qst6, &s6);
-            if (!fix_exact(x6) || !fix_exact(qs6) || !fix_exact(qst6)) {
-                ok = 0;
-                break;
-            }
-            fix_add(S[g ? 1 : 0], x6);
-            if (g) fix_add(S[2], qst6);
-            fix_add(S[3], qs6);
-            const double xv = x6 / 6.0;
-            if (g == 0 && xv != 0.0) ++ndz;
-            if (fabs(xv) > s6) ++nclip;   /* |x| above 6 sb t */
-            const double ct = (x6 - qs6) / 6.0;
-            const double csb = g ? (qst6 - qs6) / 6.0 : 0.0;
-            const double cdz = g ? 0.0 : xv;
-            const double cgn = g ? (x6 - qst6) / 6.0 : 0.0;
-            sq[0] += ct * ct;
-            sq[1] += csb * csb;
-            sq[2] += cdz * cdz;
-            sq[3] += cgn * cgn;
-            cross += csb * cgn;
+    for (int64_t r = 0; r < rows; ++r) {
+        if (parts[r].bad) ok = 0;
+        for (int k = 0; k < 4; ++k) {
+            fix_add_fix(S[k], parts[r].S[k]);
+            sq[k] += parts[r].sq[k];
         }
+        cross += parts[r].cross;
+        ndz += parts[r].ndz;
+        nclip += parts[r].nclip;
+    }
+    free(parts);
     free(q);
     free(sc);
     if (!ok) return -2;
