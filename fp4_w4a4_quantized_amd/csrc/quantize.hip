@@ -207,22 +207,25 @@ __global__ void __launch_bounds__(QT) k_group_amax(ChunkGrid gr, int64_t rows,
 }
 
 // Tensor maximum across the workgroups of one launch (the small-tensor NVFP4
-// path), through per-device state that is zero at module load: one word
-// holding a generation (high 16 bits) and an arrival count, and, per
-// generation parity, a maximum slot and a final slot.  Every access is an
-// atomic at agent scope, performed where all XCDs see it.  A workgroup adds
-// its maximum, then counts its arrival; the arrival takes an input from the
-// maximum's returned value, so it is issued after the maximum has been
-// performed, with no release fence (which would write back the per-XCD L2).
-// The last to arrive reads the slot, publishes it with a flag in the final
-// slot, clears the other parity's slots for the next launch and advances
-// the generation (resetting the count); the others spin, bounded, on the
-// final slot.  Every workgroup of the launch is resident at once (at most 32
-// workgroups of 1024 threads), and one such launch runs at a time on a
-// device.
+// path), through per-device state that is zero at module load: a launch
+// counter and one slot per workgroup.  Every access is an atomic at agent
+// scope, performed where all XCDs see it, and no release fence is needed
+// (one would write back the per-XCD L2).  A launch tags its slots with
+// (counter + 1) mod 2^16 in the high half of the word: each workgroup
+// stores its maximum under the tag in its own slot (workgroup 0 also stores
+// the tag with a zero maximum in the slots past the grid, so every slot
+// always carries the previous launch's tag, never the current one, before
+// it is written), then the first wave loads the launch's slots, lane i slot
+// i, until all carry the tag, and takes their maximum: one store and one
+// load on the critical path.  Workgroup 0 then advances the counter; every
+// workgroup has read it by then (their slots carry the tag derived from
+// it).  Spins are bounded.  Every workgroup of the launch is resident at
+// once (at most 32 workgroups of 1024 threads), and one such launch runs at
+// a time on a device.
 constexpr uint32_t GRID_SPIN_LIMIT = 1u << 22;
-constexpr uint32_t GRID_FLAG = 0x80000000u;
-static __device__ uint32_t g_fused_bar[5];  // word, max[2], final[2]
+constexpr uint32_t GRID_SLOTS = 32;
+static __device__ uint32_t g_grid_count;
+static __device__ uint32_t g_grid_slot[GRID_SLOTS];
 
 // Opaque copy of `v` that can only be formed once `dep` is available.
 __device__ __forceinline__ uint32_t after(uint32_t v, uint32_t dep) {
@@ -230,35 +233,35 @@ __device__ __forceinline__ uint32_t after(uint32_t v, uint32_t dep) {
   return v;
 }
 
-// The launch's generation; read early, before the chunk loads are used.
+// The launch counter; read early, before the chunk loads are used.
 __device__ __forceinline__ uint32_t grid_gen() {
-  return __hip_atomic_load(&g_fused_bar[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 16;
+  return __hip_atomic_load(&g_grid_count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Called by one thread of each workgroup with the workgroup's maximum (a
-// BF16 magnitude pattern, below the flag bit).
+// Called by all 64 lanes of the first wave of every workgroup with the
+// workgroup's maximum (a BF16 magnitude pattern, below 2^15) and the
+// counter; returns the launch's maximum in every lane.
 __device__ __forceinline__ uint32_t grid_max(uint32_t m, uint32_t nwg, uint32_t gen) {
-  uint32_t* bar = g_fused_bar;
-  const uint32_t p = gen & 1u;
-  const uint32_t old = __hip_atomic_fetch_max(&bar[1 + p], m, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-  const uint32_t arrive = __hip_atomic_fetch_add(&bar[0], after(1u, old), __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-  if ((arrive & 0xFFFFu) == nwg - 1u) {
-    const uint32_t fin = __hip_atomic_fetch_max(&bar[1 + p], after(0u, arrive), __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&bar[3 + p], fin | GRID_FLAG, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&bar[1 + (p ^ 1u)], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&bar[3 + (p ^ 1u)], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_fetch_add(&bar[0], 0x10000u - nwg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return fin;
+  const int lane = threadIdx.x & 63;
+  const uint32_t tag = ((gen + 1u) & 0xFFFFu) << 16;
+  if (lane == 0)
+    __hip_atomic_store(&g_grid_slot[blockIdx.x], tag | m, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  if (blockIdx.x == 0 && (uint32_t)lane >= nwg && (uint32_t)lane < GRID_SLOTS)
+    __hip_atomic_store(&g_grid_slot[lane], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  uint32_t v = tag;
+  if ((uint32_t)lane < nwg) {
+    for (uint32_t i = 0; i < GRID_SPIN_LIMIT; ++i) {
+      v = __hip_atomic_load(&g_grid_slot[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((v & 0xFFFF0000u) == tag) break;
+    }
   }
-  uint32_t f = 0;
-  for (uint32_t i = 0; i < GRID_SPIN_LIMIT; ++i) {
-    f = __hip_atomic_load(&bar[3 + p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (f & GRID_FLAG) break;
-  }
-  return f & ~GRID_FLAG;
+  uint32_t r = v & 0x7FFFu;
+  for (int s = 32; s > 0; s >>= 1) r = max(r, (uint32_t)__shfl_xor((int)r, s));
+  if (blockIdx.x == 0 && lane == 0)
+    __hip_atomic_store(&g_grid_count, after(gen + 1u, r), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  return r;
 }
 
 // Dense, large: one partial maximum per workgroup.
@@ -475,7 +478,7 @@ __global__ void __launch_bounds__(NT) k_quantize(
     // the maximum of this workgroup's own chunks (already loaded), then
     // across the launch
     __shared__ uint32_t s_amax;
-    const uint32_t gen = threadIdx.x == 0 ? grid_gen() : 0u;
+    const uint32_t gen = threadIdx.x < 64 ? grid_gen() : 0u;
     uint32_t m = 0;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -483,7 +486,10 @@ __global__ void __launch_bounds__(NT) k_quantize(
       if (c < total && rowu[u] < (uint32_t)rows) m = max(m, absmax8(v[u]));
     }
     m = wg_max<NT>(m, red);
-    if (threadIdx.x == 0) s_amax = grid_max(m, gridDim.x, gen);
+    if (threadIdx.x < 64) {
+      const uint32_t g = grid_max(m, gridDim.x, gen);
+      if (threadIdx.x == 0) s_amax = g;
+    }
     __syncthreads();
     tdense = nv_tensor_scale(bf16_to_f32(s_amax));
   }
@@ -556,7 +562,11 @@ int launch_quantize(int fmt, bool tiled, const uint16_t* x, int64_t rows, int64_
     hipLaunchKernelGGL(k_quant_init, dim3(1), dim3(QT), 0, stream, words, tscale, 1);
     return 0;
   }
-  if (chunks <= FUSED_MAX_CHUNKS) {
+  // the fused path's grid (tiled: rows padded to 16) is at most 32
+  // workgroups: one slot each in the grid maximum, all resident at once
+  const int64_t launch_chunks = (tiled ? (rows + 15) / 16 * 16 : rows) * (cols >> 3);
+  if (launch_chunks <= FUSED_MAX_CHUNKS) {
+    static_assert(FUSED_MAX_CHUNKS / FT <= GRID_SLOTS, "one grid slot per workgroup");
     if (SMALL_FUSED) {
       launch_q<FP4Q_NVFP4, AMAX_FUSED, FT, 1>(gr, rows, cols, tiled, stream, off, 1, chan, nS, q, scales,
                                               tscale, resid, words, 0);
