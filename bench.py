@@ -54,6 +54,11 @@ def parse():
                    help="compensated channels of the dense workloads: the workload's fixed "
                         "list, or chosen each step by residual magnitude "
                         "(fp4q_select_channels, k = the workload's channel count)")
+    p.add_argument("--comp-weights", choices=("prepared", "inkernel"), default="prepared",
+                   help="dense workloads with fixed channels and the BF16 residual: stream the "
+                        "compensation weights B[n, S_j] made once per weight copy "
+                        "(fp4q_comp_weights, fp4q_gemm_prepared), or extract them from the "
+                        "packed weights in every call (fp4q_gemm)")
     p.add_argument("--moe-quant", choices=("expert", "token"), default="expert",
                    help="MoE gate_up input: quantize the routed copies per expert, or quantize "
                         "the token matrix once and permute its FP4 codes "
@@ -161,10 +166,16 @@ def main():
         torch.cuda.synchronize()
         w_bytes = N * (K // 2) + N * (K // blk)
         y_bytes = M * N * (2 if args.out_dtype == "bf16" else 4)
-        n_rot = max(1, math.ceil(1.2 * LLC_BYTES / (w_bytes + y_bytes)))
+        prepared = (args.comp_weights == "prepared" and nS > 0 and args.channels == "fixed" and
+                    args.residual == "bf16")
+        cw_bytes = fq.comp_weights_bytes(fmt, layout, N, K, nS) if prepared else 0
+        n_rot = max(1, math.ceil(1.2 * LLC_BYTES / (w_bytes + y_bytes + cw_bytes)))
         n_rot = min(n_rot, 64)
         wcopies = [wq] + [{k: (v.clone() if isinstance(v, torch.Tensor) else v)
                            for k, v in wq.items()} for _ in range(n_rot - 1)]
+        if prepared:  # made once per weight copy, like the weight quantization itself
+            for w in wcopies:
+                w["comp_w"] = fq.comp_weights(fmt, w, chan)
         ydt = fq.OUT_BF16 if args.out_dtype == "bf16" else fq.OUT_F32
         ys = [torch.empty((M, N), dtype=torch.bfloat16 if ydt == fq.OUT_BF16 else torch.float32,
                           device=dev) for _ in range(n_rot)]
@@ -218,6 +229,10 @@ def main():
                 fq.gemm_residual_fp4_into(fmt, layout, M, N, K, aq, asc, ats, w["q"], w["scales"],
                                           w["tscale"], chan, nS, rq, rsc, rts, ys[i % n_rot], ydt,
                                           N, gws)
+            elif prepared:
+                fq.gemm_prepared_into(fmt, layout, M, N, K, aq, asc, ats, w["q"], w["scales"],
+                                      w["tscale"], chan, nS, ar, w["comp_w"], ys[i % n_rot], ydt,
+                                      N)
             else:
                 fq.gemm_into(fmt, layout, M, N, K, aq, asc, ats, w["q"], w["scales"],
                              w["tscale"], chan, nS, ar, ys[i % n_rot], ydt, N, gws)
@@ -225,7 +240,7 @@ def main():
         flops = 2.0 * M * N * K
         r_bytes = (M * nS // 2 + M * nS // blk + (4 if fmt == fq.NVFP4 else 0)) if r4 else M * nS * 2
         gemm_bytes = (M * K // 2 + M * K // blk + r_bytes + nS * 4 + w_bytes + y_bytes +
-                      (8 if fmt == fq.NVFP4 else 0))
+                      cw_bytes + (8 if fmt == fq.NVFP4 else 0))
         quant_bytes = M * K * 2 + M * K // 2 + M * K // blk + M * nS * 2 + (4 if fmt == fq.NVFP4
                                                                              else 0)
         if r4:
@@ -237,7 +252,8 @@ def main():
             quant_bytes += select_bytes
         wl = {"workload": name, "format": cfg["fmt"], "M": M, "K": K, "N": N, "n_s": nS,
               "layout": args.layout, "out_dtype": args.out_dtype, "weight_copies_rotated": n_rot,
-              "residual": args.residual, "channels": args.channels}
+              "residual": args.residual, "channels": args.channels,
+              "comp_weights": "prepared" if prepared else "inkernel"}
     else:
         if args.channels != "fixed" or args.residual != "bf16":
             sys.exit("moe_nvfp4 takes the fixed per-expert channel lists and the BF16 residual")
@@ -397,7 +413,8 @@ def main():
 
     kh = src_hash()
     default_variant = (args.layout == "tiled" and args.out_dtype == "f32" and
-                       args.residual == "bf16" and args.channels == "fixed")
+                       args.residual == "bf16" and args.channels == "fixed" and
+                       args.comp_weights == "prepared")
     if name in ("prefill_nvfp4", "prefill_mxfp4"):
         mfma_dtype = "f16" if fmt == fq.NVFP4 else "fp4"
         peak = MFMA_PEAK_TFLOPS[mfma_dtype]

@@ -14,11 +14,16 @@ from .binding import (  # noqa: F401
     ROWMAJOR,
     TILED,
     Fp4qError,
+    comp_weights,
+    comp_weights_bytes,
+    comp_weights_into,
     error_decompose,
     error_decompose_into,
     error_decompose_workspace_bytes,
     gemm,
     gemm_into,
+    gemm_prepared,
+    gemm_prepared_into,
     gemm_residual_fp4,
     gemm_residual_fp4_into,
     gemm_residual_fp4_workspace_bytes,

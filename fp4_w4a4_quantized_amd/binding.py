@@ -79,6 +79,14 @@ def lib():
         L.fp4q_gemm.restype = ctypes.c_int
         L.fp4q_gemm.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, P, P, P, P, P, P, P,
                                 i32, P, P, ctypes.c_int, i64, P, sz, P]
+        L.fp4q_comp_weights_bytes.restype = sz
+        L.fp4q_comp_weights_bytes.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i32]
+        L.fp4q_comp_weights.restype = ctypes.c_int
+        L.fp4q_comp_weights.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, P, P, P, i32, P, sz,
+                                        P]
+        L.fp4q_gemm_prepared.restype = ctypes.c_int
+        L.fp4q_gemm_prepared.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, P, P, P, P, P,
+                                         P, P, i32, P, P, sz, P, ctypes.c_int, i64, P]
         L.fp4q_grouped_gemm_workspace_bytes.restype = sz
         L.fp4q_grouped_gemm_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i64, i32, i32]
         L.fp4q_gemm_residual_fp4_workspace_bytes.restype = sz
@@ -138,6 +146,27 @@ def quantize_workspace_bytes(fmt, rows, cols, num_groups=1) -> int:
 
 def gemm_workspace_bytes(fmt, layout, M, N, K, n_chan) -> int:
     return lib().fp4q_gemm_workspace_bytes(fmt, layout, M, N, K, n_chan)
+
+
+def comp_weights_bytes(fmt, layout, N, K, n_chan) -> int:
+    return lib().fp4q_comp_weights_bytes(fmt, layout, N, K, n_chan)
+
+
+def comp_weights_into(fmt, layout, N, K, b_q, b_s, chan_idx, n_chan, out, stream=None):
+    nb = 0 if out is None else out.numel() * out.element_size()
+    rc = lib().fp4q_comp_weights(fmt, layout, N, K, _ptr(b_q), _ptr(b_s), _ptr(chan_idx), n_chan,
+                                 _ptr(out), nb, _stream(stream))
+    _check("fp4q_comp_weights", rc)
+
+
+def gemm_prepared_into(fmt, layout, M, N, K, a_q, a_s, a_ts, b_q, b_s, b_ts, chan_idx, n_chan,
+                       resid, comp_w, y, y_dtype=OUT_F32, ldy=None, stream=None):
+    nb = 0 if comp_w is None else comp_w.numel() * comp_w.element_size()
+    rc = lib().fp4q_gemm_prepared(fmt, layout, M, N, K, _ptr(a_q), _ptr(a_s), _ptr(a_ts), _ptr(b_q),
+                                  _ptr(b_s), _ptr(b_ts), _ptr(chan_idx), n_chan, _ptr(resid),
+                                  _ptr(comp_w), nb, _ptr(y), y_dtype, N if ldy is None else ldy,
+                                  _stream(stream))
+    _check("fp4q_gemm_prepared", rc)
 
 
 def gemm_residual_fp4_workspace_bytes(fmt, layout, M, N, K, n_chan) -> int:
@@ -283,6 +312,31 @@ def gemm(fmt, a, b, chan_idx=None, y_dtype=OUT_F32, stream=None):
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
     gemm_into(fmt, layout, M, N, K, a["q"], a["scales"], a["tscale"], b["q"], b["scales"],
               b["tscale"], chan_idx, nS, a["resid"] if nS else None, y, y_dtype, N, ws, stream)
+    return y
+
+
+def comp_weights(fmt, b, chan_idx, stream=None):
+    """The compensation weights B[n, S_j] of a quantize() result b (W^T),
+    in the tiled BF16 layout fp4q_gemm_prepared streams (uint8 tensor)."""
+    N, K, layout = _shape(b)
+    nS = chan_idx.numel()
+    out = torch.empty(max(comp_weights_bytes(fmt, layout, N, K, nS), 16), dtype=torch.uint8,
+                      device=b["q"].device)
+    comp_weights_into(fmt, layout, N, K, b["q"], b["scales"], chan_idx, nS, out, stream)
+    return out
+
+
+def gemm_prepared(fmt, a, b, chan_idx, comp_w, y_dtype=OUT_F32, stream=None):
+    """gemm() with the compensation weights from comp_weights(fmt, b, chan_idx)."""
+    M, K, layout = _shape(a)
+    N, Kb, layout_b = _shape(b)
+    if Kb != K or layout_b != layout:
+        raise ValueError("operands differ in K or layout")
+    nS = chan_idx.numel()
+    y = torch.empty((M, N), dtype=torch.float32 if y_dtype == OUT_F32 else torch.bfloat16,
+                    device=a["q"].device)
+    gemm_prepared_into(fmt, layout, M, N, K, a["q"], a["scales"], a["tscale"], b["q"], b["scales"],
+                       b["tscale"], chan_idx, nS, a["resid"], comp_w, y, y_dtype, N, stream)
     return y
 
 

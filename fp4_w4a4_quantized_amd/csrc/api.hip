@@ -162,6 +162,58 @@ int fp4q_gemm(fp4q_format_t fmt, fp4q_layout_t layout, int64_t M, int64_t N, int
   return check_launch();
 }
 
+size_t fp4q_comp_weights_bytes(fp4q_format_t fmt, fp4q_layout_t layout, int64_t N, int64_t K,
+                               int32_t n_chan) {
+  (void)fmt;
+  (void)layout;
+  (void)K;
+  return fp4q::comp_weights_bytes(N, n_chan);
+}
+
+int fp4q_comp_weights(fp4q_format_t fmt, fp4q_layout_t layout, int64_t N, int64_t K,
+                      const uint8_t* b_q, const uint8_t* b_s, const int32_t* chan_idx,
+                      int32_t n_chan, uint8_t* out, size_t out_bytes, void* stream) {
+  if (!layout_ok(layout) || !fmt_ok(fmt)) return FP4Q_ERR_INVALID;
+  if (N < 0 || K < 0 || n_chan < 0) return FP4Q_ERR_INVALID;
+  if ((n_chan > 0) != (chan_idx != nullptr)) return FP4Q_ERR_INVALID;
+  if (N == 0 || n_chan == 0) return FP4Q_OK;
+  if (!b_q || !b_s || !out || !aligned(out, 16)) return FP4Q_ERR_INVALID;
+  if (K % 128 != 0) return FP4Q_ERR_UNSUPPORTED;
+  if (out_bytes < fp4q_comp_weights_bytes(fmt, layout, N, K, n_chan)) return FP4Q_ERR_WORKSPACE;
+  if (((N + 15) / 16) * ((n_chan + 31) / 32) / 4 >= (int64_t)UINT32_MAX)
+    return FP4Q_ERR_UNSUPPORTED;
+  clear_error();
+  fp4q::launch_comp_weights(fmt, layout == FP4Q_LAYOUT_TILED, b_q, b_s, N, K, chan_idx, n_chan,
+                            out, static_cast<hipStream_t>(stream));
+  return check_launch();
+}
+
+int fp4q_gemm_prepared(fp4q_format_t fmt, fp4q_layout_t layout, int64_t M, int64_t N, int64_t K,
+                       const uint8_t* a_q, const uint8_t* a_s, const float* a_ts,
+                       const uint8_t* b_q, const uint8_t* b_s, const float* b_ts,
+                       const int32_t* chan_idx, int32_t n_chan, const uint16_t* resid,
+                       const uint8_t* comp_w, size_t comp_w_bytes, void* y,
+                       fp4q_dtype_t y_dtype, int64_t ldy, void* stream) {
+  if (!layout_ok(layout)) return FP4Q_ERR_INVALID;
+  int rc = validate_gemm_common(fmt, N, K, a_q, a_s, a_ts, b_q, b_s, b_ts, chan_idx, n_chan,
+                                resid, y, y_dtype, M);
+  if (rc != FP4Q_OK) return rc;
+  if (ldy < N) return FP4Q_ERR_INVALID;
+  if ((M + 127) / 128 > (int64_t)UINT32_MAX || (N + 31) / 32 > 65535) return FP4Q_ERR_UNSUPPORTED;
+  const bool work = M > 0 && N > 0 && n_chan > 0;
+  if (work && (!comp_w || !aligned(comp_w, 16) ||
+               comp_w_bytes < fp4q_comp_weights_bytes(fmt, layout, N, K, n_chan)))
+    return FP4Q_ERR_WORKSPACE;
+  // shapes whose kernels stream no compensation weights take the term from
+  // chan_idx as fp4q_gemm does (they need no workspace)
+  if (fp4q::gemm_path(M, N, K, n_chan) == fp4q::PATH_GENERIC) comp_w = nullptr;
+  clear_error();
+  fp4q::launch_gemm(fmt, layout == FP4Q_LAYOUT_TILED, M, N, K, nullptr, 1, a_q, a_s, a_ts, b_q,
+                    b_s, b_ts, chan_idx, n_chan, resid, nullptr, y, y_dtype == FP4Q_OUT_BF16, ldy,
+                    nullptr, static_cast<hipStream_t>(stream), work ? comp_w : nullptr);
+  return check_launch();
+}
+
 static size_t deq_resid_bytes(int64_t M, int32_t n_chan) {
   return (size_t)((M * n_chan * 2 + 255) / 256 * 256);
 }

@@ -29,7 +29,7 @@ int launch_gemm(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const int3
                 const uint8_t* aq, const uint8_t* as, const float* ats, const uint8_t* bq,
                 const uint8_t* bs, const float* bts, const int32_t* chan, int nS,
                 const uint16_t* resid, const float* cts, void* y, int y_bf16, int64_t ldy,
-                void* ws, hipStream_t stream);
+                void* ws, hipStream_t stream, const uint8_t* bsel_pre = nullptr);
 
 // Second-pass residual: BF16 e2m1 * block scale (exact; tensor scale
 // excluded) of the row-major FP4 residual rq [M, nS/2], rs [M, nS/blk].
@@ -49,14 +49,21 @@ int launch_gemm_big_grouped(int fmt, int64_t total_rows, int64_t N, int64_t K,
 int launch_gemm_big(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const uint8_t* aq,
                     const uint8_t* as, const float* ats, const uint8_t* bq, const uint8_t* bs,
                     const float* bts, const int32_t* chan, int nS, const uint16_t* resid,
-                    const float* cts, void* y, int y_bf16, int64_t ldy, void* ws,
-                    hipStream_t stream);
+                    const float* cts, const uint8_t* bsel_pre, void* y, int y_bf16, int64_t ldy,
+                    void* ws, hipStream_t stream);
+// Compensation weights B[n, S_j] (BF16, tensor scale excluded) in the tiled
+// layout the GEMMs stream: 1 KB per 16 columns and 32 channels.
+size_t comp_weights_bytes(int64_t N, int nS);
+void launch_comp_weights(int fmt, bool tiled, const uint8_t* bq, const uint8_t* bs, int64_t N,
+                         int64_t K, const int32_t* chan, int nS, uint8_t* out,
+                         hipStream_t stream);
 
 bool skinny_gemm_eligible(int64_t M, int64_t N, int64_t K, int nS);
 int launch_gemm_skinny(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const uint8_t* aq,
                        const uint8_t* as, const float* ats, const uint8_t* bq, const uint8_t* bs,
                        const float* bts, const int32_t* chan, int nS, const uint16_t* resid,
-                       const float* cts, void* y, int y_bf16, int64_t ldy, hipStream_t stream);
+                       const float* cts, const uint8_t* bsel, void* y, int y_bf16, int64_t ldy,
+                       hipStream_t stream);
 
 // Online channel selection: scores, top-k pick, residual emission.
 size_t select_workspace_bytes(int64_t rows, int64_t cols);

@@ -440,7 +440,7 @@ int launch_gemm(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const int3
                 const uint8_t* aq, const uint8_t* as, const float* ats, const uint8_t* bq,
                 const uint8_t* bs, const float* bts, const int32_t* chan, int nS,
                 const uint16_t* resid, const float* cts, void* y, int y_bf16, int64_t ldy,
-                void* ws, hipStream_t stream) {
+                void* ws, hipStream_t stream, const uint8_t* bsel_pre) {
   GemmArgs a{M, N, K, off, G, aq, as, ats, bq, bs, bts, chan, nS, resid, cts, y, y_bf16, ldy,
              tiled};
   if (M == 0 || N == 0) return 0;
@@ -458,12 +458,12 @@ int launch_gemm(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const int3
   }
   switch (gemm_path(M, N, K, nS)) {
     case PATH_SKINNY:
-      launch_gemm_skinny(fmt, tiled, M, N, K, aq, as, ats, bq, bs, bts, chan, nS, resid, cts, y,
-                         y_bf16, ldy, stream);
+      launch_gemm_skinny(fmt, tiled, M, N, K, aq, as, ats, bq, bs, bts, chan, nS, resid, cts,
+                         bsel_pre, y, y_bf16, ldy, stream);
       break;
     case PATH_BIG:
-      launch_gemm_big(fmt, tiled, M, N, K, aq, as, ats, bq, bs, bts, chan, nS, resid, cts, y,
-                      y_bf16, ldy, ws, stream);
+      launch_gemm_big(fmt, tiled, M, N, K, aq, as, ats, bq, bs, bts, chan, nS, resid, cts,
+                      bsel_pre, y, y_bf16, ldy, ws, stream);
       break;
     default:
       if (M <= 64) {

@@ -803,8 +803,9 @@ size_t big_gemm_workspace_bytes(int64_t N, int nS) {
 }
 
 template <int FMT, bool GR>
-static void launch_big(const BigArgs& a, bool tiled, unsigned grid, hipStream_t stream) {
-  const bool xs = a.nS > 0 && a.nS <= GB_XS_MAX;
+static void launch_big(const BigArgs& a, bool tiled, unsigned grid, hipStream_t stream,
+                       bool prepared = false) {
+  const bool xs = a.nS > 0 && a.nS <= GB_XS_MAX && !prepared;
   if constexpr (GR) {  // grouped operands are row-major
     if (xs)
       hipLaunchKernelGGL((k_gemm_big<FMT, false, true, true>), dim3(grid), dim3(GB_T), 0, stream, a);
@@ -839,23 +840,41 @@ static void launch_gather(bool tiled, const uint8_t* bq, const uint8_t* bs, int6
 int launch_gemm_big(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const uint8_t* aq,
                     const uint8_t* as, const float* ats, const uint8_t* bq, const uint8_t* bs,
                     const float* bts, const int32_t* chan, int nS, const uint16_t* resid,
-                    const float* cts, void* y, int y_bf16, int64_t ldy, void* ws,
-                    hipStream_t stream) {
+                    const float* cts, const uint8_t* bsel_pre, void* y, int y_bf16, int64_t ldy,
+                    void* ws, hipStream_t stream) {
   const int nc = nS > 0 ? (nS + GB_CS - 1) / GB_CS : 0;
-  uint8_t* bsel = static_cast<uint8_t*>(ws);
+  // prepared compensation weights (the gather kernel's output, made once)
+  // replace both the gather and the in-kernel extraction
+  const bool prepared = bsel_pre != nullptr && nS > 0;
+  uint8_t* bsel = prepared ? const_cast<uint8_t*>(bsel_pre) : static_cast<uint8_t*>(ws);
   BigArgs a{M, N, K, aq, as, ats, bq, bs, bts, nS, resid, bsel, chan, cts, y, y_bf16, ldy,
             (int)((M + GB_TILE - 1) / GB_TILE), (int)((N + GB_TILE - 1) / GB_TILE),
             (int)(K / 128), nc, nullptr, 1};
-  const bool gather = nS > GB_XS_MAX;
+  const bool gather = nS > GB_XS_MAX && !prepared;
   const unsigned grid = (unsigned)(a.mt * a.nt);
   if (fmt == FP4Q_NVFP4) {
     if (gather) launch_gather<FP4Q_NVFP4>(tiled, bq, bs, N, K, chan, nS, nc, 1, bsel, stream);
-    launch_big<FP4Q_NVFP4, false>(a, tiled, grid, stream);
+    launch_big<FP4Q_NVFP4, false>(a, tiled, grid, stream, prepared);
   } else {
     if (gather) launch_gather<FP4Q_MXFP4>(tiled, bq, bs, N, K, chan, nS, nc, 1, bsel, stream);
-    launch_big<FP4Q_MXFP4, false>(a, tiled, grid, stream);
+    launch_big<FP4Q_MXFP4, false>(a, tiled, grid, stream, prepared);
   }
   return 0;
+}
+
+// The compensation weights alone, in the layout the GEMMs stream (one group).
+void launch_comp_weights(int fmt, bool tiled, const uint8_t* bq, const uint8_t* bs, int64_t N,
+                         int64_t K, const int32_t* chan, int nS, uint8_t* out,
+                         hipStream_t stream) {
+  if (N <= 0 || nS <= 0) return;
+  const int nc = (nS + GB_CS - 1) / GB_CS;
+  if (fmt == FP4Q_NVFP4) launch_gather<FP4Q_NVFP4>(tiled, bq, bs, N, K, chan, nS, nc, 1, out, stream);
+  else launch_gather<FP4Q_MXFP4>(tiled, bq, bs, N, K, chan, nS, nc, 1, out, stream);
+}
+
+size_t comp_weights_bytes(int64_t N, int nS) {
+  if (N <= 0 || nS <= 0) return 0;
+  return (size_t)(((N + 15) / 16) * ((nS + GB_CS - 1) / GB_CS) * 1024);
 }
 
 int launch_gemm_big_grouped(int fmt, int64_t total_rows, int64_t N, int64_t K,

@@ -62,6 +62,7 @@ struct SkinnyArgs {
   int nS;
   const uint16_t* resid;
   const float* cts;  // tensor scale of the compensation term, or null (1)
+  const uint8_t* bsel;  // prepared compensation weights (tiled BF16), or null
   void* y;
   int y_bf16;
   int64_t ldy;
@@ -175,7 +176,7 @@ template <int FMT> struct SlotLayout {
 
 // Multiply one K step into the accumulators; take the compensation weights
 // of the channels that fall in it.
-template <int FMT>
+template <int FMT, bool PB>
 __device__ __forceinline__ void process_step(const Step& st, int kt, uint8_t* slot,
                                              uint8_t* cslot, int lane, int my_ch, int nS,
                                              uint16_t* sB, v4f32s (&acc)[4][SK_CG]) {
@@ -237,13 +238,14 @@ __device__ __forceinline__ void process_step(const Step& st, int kt, uint8_t* sl
       }
     }
   }
-  // compensation weights of the channels in this step: S is ascending, so
+  // compensation weights of the channels in this step (unless prepared
+  // ones were staged at the start): S is ascending, so
   // they are the entries [j0, j1) of the lanes of my_ch.  The step's weight
   // bytes go to the wave-private slot as rows of 64 bytes; lane (r, u) then
   // takes channel jb + u and the columns 16g + r.  One wave's LDS operations
   // complete in order, so the slot needs no barrier.  Lanes past j1 write
   // the unused padding column SK_MAXS of sB.
-  if (nS > 0) {
+  if (!PB && nS > 0) {
     const uint64_t m = __ballot(my_ch >= 0 && (my_ch >> 7) == kt);
     if (m) {
       const int j0 = __builtin_ctzll(m), j1 = 64 - __builtin_clzll(m);
@@ -275,7 +277,7 @@ __device__ __forceinline__ void process_step(const Step& st, int kt, uint8_t* sl
   }
 }
 
-template <int FMT, bool TL>
+template <int FMT, bool TL, bool PB>
 __global__ void __launch_bounds__(SK_T, 1) k_gemm_skinny(SkinnyArgs p) {
   using L = SlotLayout<FMT>;
   __shared__ __attribute__((aligned(16))) v4f32s red[SK_WAVES * 4 * SK_CG * 64];   // 96 KB
@@ -309,6 +311,25 @@ __global__ void __launch_bounds__(SK_T, 1) k_gemm_skinny(SkinnyArgs p) {
   const int rtot = (int)p.M * nS, e0 = 8 * t;
   const u32x4 rv = *reinterpret_cast<const u32x4*>(
       nS > 0 ? p.resid + (e0 < rtot ? e0 : rtot - 8) : reinterpret_cast<const uint16_t*>(p.aq));
+  // prepared compensation weights: 1 KB blocks (16-column group, stage of
+  // 32 channels), in each the 16-byte piece (channels 8u .. 8u+7 of the
+  // stage, column r) at (16u + r) * 16; thread t < 3 * 64 nc takes piece
+  // t % 64 of block t / 64 of this workgroup's column groups (clamped to the
+  // last group; those columns are not stored)
+  const int nc = (nS + 31) >> 5;
+  const bool pb_on = PB && t < SK_CG * 64 * nc;
+  int pb_g = 0, pb_c = 0;
+  u32x4 pbv = u32x4{0u, 0u, 0u, 0u};
+  if (PB) {
+    const int blk = pb_on ? t >> 6 : 0;
+    pb_g = blk / (nc > 0 ? nc : 1);
+    pb_c = blk - pb_g * nc;
+    const int64_t glast = ((p.N + 15) >> 4) - 1;
+    int64_t gi = (col0 >> 4) + pb_g;
+    gi = gi < glast ? gi : glast;
+    if (pb_on)
+      pbv = *reinterpret_cast<const u32x4*>(p.bsel + ((gi * nc + pb_c) << 10) + (t & 63) * 16);
+  }
   // tiled layout: this lane's weight-row scale offset within a step (rows
   // exist up to the 64-row padding)
   int64_t wso = 0;
@@ -322,6 +343,12 @@ __global__ void __launch_bounds__(SK_T, 1) k_gemm_skinny(SkinnyArgs p) {
   Step s0, s1;
   load_step<FMT, TL>(p, wave < nk ? wave : nk - 1, lane, col0, wso, s0);
   load_step<FMT, TL>(p, wave + SK_WAVES < nk ? wave + SK_WAVES : nk - 1, lane, col0, wso, s1);
+  if (PB && pb_on) {
+    const int u = (t & 63) >> 4, r = t & 15;
+    uint16_t* dst = sB + (16 * pb_g + r) * SK_SRS + 32 * pb_c + 8 * u;  // 8-byte aligned
+    reinterpret_cast<u32x2*>(dst)[0] = u32x2{pbv.x, pbv.y};
+    reinterpret_cast<u32x2*>(dst)[1] = u32x2{pbv.z, pbv.w};
+  }
   if (nS > 0 && e0 < rtot) {
     const uint32_t w4[4] = {rv.x, rv.y, rv.z, rv.w};
     int row = e0 / nS, j = e0 - row * nS;
@@ -345,14 +372,14 @@ __global__ void __launch_bounds__(SK_T, 1) k_gemm_skinny(SkinnyArgs p) {
   const int my_ch = (nS > 0 && lane < nS) ? my_ch_raw : -1;
   if (nk <= 2 * SK_WAVES) {
     // K <= 2048: both steps are already in flight
-    if (wave < nk) process_step<FMT>(s0, wave, slot0, cslot, lane, my_ch, nS, sB, acc);
-    if (wave + SK_WAVES < nk) process_step<FMT>(s1, wave + SK_WAVES, slot1, cslot, lane, my_ch, nS, sB, acc);
+    if (wave < nk) process_step<FMT, PB>(s0, wave, slot0, cslot, lane, my_ch, nS, sB, acc);
+    if (wave + SK_WAVES < nk) process_step<FMT, PB>(s1, wave + SK_WAVES, slot1, cslot, lane, my_ch, nS, sB, acc);
   } else {
     for (int kt = wave; kt < nk; kt += 2 * SK_WAVES) {
-      process_step<FMT>(s0, kt, slot0, cslot, lane, my_ch, nS, sB, acc);
+      process_step<FMT, PB>(s0, kt, slot0, cslot, lane, my_ch, nS, sB, acc);
       if (kt + 2 * SK_WAVES < nk) load_step<FMT, TL>(p, kt + 2 * SK_WAVES, lane, col0, wso, s0);
       if (kt + SK_WAVES < nk) {
-        process_step<FMT>(s1, kt + SK_WAVES, slot1, cslot, lane, my_ch, nS, sB, acc);
+        process_step<FMT, PB>(s1, kt + SK_WAVES, slot1, cslot, lane, my_ch, nS, sB, acc);
         if (kt + 3 * SK_WAVES < nk) load_step<FMT, TL>(p, kt + 3 * SK_WAVES, lane, col0, wso, s1);
       }
     }
@@ -431,17 +458,20 @@ bool skinny_gemm_eligible(int64_t M, int64_t N, int64_t K, int nS) {
 int launch_gemm_skinny(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const uint8_t* aq,
                        const uint8_t* as, const float* ats, const uint8_t* bq, const uint8_t* bs,
                        const float* bts, const int32_t* chan, int nS, const uint16_t* resid,
-                       const float* cts, void* y, int y_bf16, int64_t ldy, hipStream_t stream) {
-  SkinnyArgs a{M, N, K, aq, as, ats, bq, bs, bts, chan, nS, resid, cts, y, y_bf16, ldy};
+                       const float* cts, const uint8_t* bsel, void* y, int y_bf16, int64_t ldy,
+                       hipStream_t stream) {
+  SkinnyArgs a{M, N, K, aq, as, ats, bq, bs, bts, chan, nS, resid, cts, bsel, y, y_bf16, ldy};
   dim3 grid((unsigned)((N + SK_COLS - 1) / SK_COLS));
-  if (fmt == FP4Q_NVFP4 && tiled)
-    hipLaunchKernelGGL((k_gemm_skinny<FP4Q_NVFP4, true>), grid, dim3(SK_T), 0, stream, a);
-  else if (fmt == FP4Q_NVFP4)
-    hipLaunchKernelGGL((k_gemm_skinny<FP4Q_NVFP4, false>), grid, dim3(SK_T), 0, stream, a);
-  else if (tiled)
-    hipLaunchKernelGGL((k_gemm_skinny<FP4Q_MXFP4, true>), grid, dim3(SK_T), 0, stream, a);
-  else
-    hipLaunchKernelGGL((k_gemm_skinny<FP4Q_MXFP4, false>), grid, dim3(SK_T), 0, stream, a);
+  const bool pb = bsel != nullptr && nS > 0;
+#define FP4Q_SKINNY(F, T, P) hipLaunchKernelGGL((k_gemm_skinny<F, T, P>), grid, dim3(SK_T), 0, stream, a)
+#define FP4Q_SKINNY_P(F, T) \
+  if (pb) FP4Q_SKINNY(F, T, true); else FP4Q_SKINNY(F, T, false)
+  if (fmt == FP4Q_NVFP4 && tiled) { FP4Q_SKINNY_P(FP4Q_NVFP4, true); }
+  else if (fmt == FP4Q_NVFP4) { FP4Q_SKINNY_P(FP4Q_NVFP4, false); }
+  else if (tiled) { FP4Q_SKINNY_P(FP4Q_MXFP4, true); }
+  else { FP4Q_SKINNY_P(FP4Q_MXFP4, false); }
+#undef FP4Q_SKINNY_P
+#undef FP4Q_SKINNY
   return 0;
 }
 

@@ -182,6 +182,50 @@ int fp4q_gemm(fp4q_format_t fmt, fp4q_layout_t layout, int64_t M, int64_t N, int
               size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Prepared compensation weights.  The compensation term of fp4q_gemm
+ * multiplies R by the dequantized weights on the selected channels,
+ * B[n, S_j] (QUADS abstract: Residual Activation Compensation; FourSight
+ * abstract: the selected channels effectively BF16).  With static weights
+ * and a fixed channel list that slice is itself static:
+ * fp4q_comp_weights writes it once, and fp4q_gemm_prepared streams it
+ * instead of extracting it from the packed weights on every call.
+ *
+ * fp4q_comp_weights:
+ *   b_q, b_s   packed W^T and block scales in `layout`, as for fp4q_gemm
+ *   chan_idx   device int32 [n_chan] ascending, < K (NULL iff n_chan == 0)
+ *   out        device buffer of fp4q_comp_weights_bytes() bytes, 16-byte
+ *              aligned, owned by the caller.  Layout: 1 KB blocks, block
+ *              (c, g) at (g * ceil(n_chan/32) + c) * 1024 for columns
+ *              16g .. 16g+15 and channels 32c .. 32c+31; in a block, the 16
+ *              bytes of channels 8u .. 8u+7 of column 16g + r at
+ *              (16u + r) * 16, each the BF16 of e2m1 * block scale (exact,
+ *              tensor scale excluded); entries past n_chan or N are zero.
+ * N == 0 or n_chan == 0 writes nothing.  K % 128 != 0 is
+ * FP4Q_ERR_UNSUPPORTED; out_bytes below the size is FP4Q_ERR_WORKSPACE.
+ *
+ * fp4q_gemm_prepared: fp4q_gemm's product with comp_w =
+ * fp4q_comp_weights(fmt, layout, N, K, b_q, b_s, chan_idx, n_chan) of the
+ * same operands (comp_w is read, not checked against them).  It needs no
+ * workspace.  Shapes served by the general kernel (neither the decode form,
+ * M <= 64 and n_chan <= 64, nor the 256-tile form) take the term from
+ * chan_idx as fp4q_gemm does.  FP4Q_ERR_WORKSPACE if comp_w is missing,
+ * small or misaligned when there is a term.
+ * ------------------------------------------------------------------------ */
+size_t fp4q_comp_weights_bytes(fp4q_format_t fmt, fp4q_layout_t layout, int64_t N, int64_t K,
+                               int32_t n_chan);
+
+int fp4q_comp_weights(fp4q_format_t fmt, fp4q_layout_t layout, int64_t N, int64_t K,
+                      const uint8_t* b_q, const uint8_t* b_s, const int32_t* chan_idx,
+                      int32_t n_chan, uint8_t* out, size_t out_bytes, void* stream);
+
+int fp4q_gemm_prepared(fp4q_format_t fmt, fp4q_layout_t layout, int64_t M, int64_t N, int64_t K,
+                       const uint8_t* a_q, const uint8_t* a_s, const float* a_ts,
+                       const uint8_t* b_q, const uint8_t* b_s, const float* b_ts,
+                       const int32_t* chan_idx, int32_t n_chan, const uint16_t* resid,
+                       const uint8_t* comp_w, size_t comp_w_bytes, void* y,
+                       fp4q_dtype_t y_dtype, int64_t ldy, void* stream);
+
+/* ------------------------------------------------------------------------
  * Compensated W4A4 GEMM with a second-pass FP4 residual.  Explainer of the
  * QUADS paper, section 2.2 B: the high-residual channels are quantized a
  * second time and that correction term is added to the quantized output.

@@ -267,3 +267,36 @@ def test_permute_quantized_rejects(L):
     # nothing to do: accepted without touching memory
     assert pq(L, fmt=1, ts=None, tso=None, rows=0, src=None, qq=None, sc=None, qo=None, so=None,
               chan=None, nS=0, R=None, x=None, tokens=0) == 0
+
+
+def test_comp_weights_rejects(L):
+    def cw(fmt=0, layout=0, N=32, K=256, bq=B, bs=B, chan=A, nS=8, out=A, nb=4096):
+        return L.fp4q_comp_weights(fmt, layout, N, K, bq, bs, chan, nS, out, nb, None)
+    # 1 KB per 16 columns and 32 channels
+    assert L.fp4q_comp_weights_bytes(0, 1, 11008, 2048, 64) == 688 * 2 * 1024
+    assert L.fp4q_comp_weights_bytes(1, 0, 17, 256, 33) == 2 * 2 * 1024
+    assert L.fp4q_comp_weights_bytes(0, 0, 17, 256, 0) == 0
+    assert L.fp4q_comp_weights_bytes(0, 0, 0, 256, 8) == 0
+    assert cw(fmt=2) == INVALID
+    assert cw(layout=3) == INVALID
+    assert cw(chan=None) == INVALID
+    assert cw(out=ctypes.c_void_p(0x10008)) == INVALID          # 16-byte aligned
+    assert cw(K=144) == UNSUPPORTED
+    assert cw(nb=2047) == WORKSPACE
+    assert cw(nS=0, chan=None) == 0                               # nothing to write
+    assert cw(N=0) == 0
+
+
+def test_gemm_prepared_rejects(L):
+    def gp(fmt=0, layout=0, M=4, N=8, K=256, ats=B, bts=B, chan=A, nS=8, R=B, cw=A, nb=1024,
+           y=A, ldy=8):
+        return L.fp4q_gemm_prepared(fmt, layout, M, N, K, A, A, ats, B, B, bts, chan, nS, R, cw,
+                                    nb, y, 0, ldy, None)
+    assert gp(fmt=2) == INVALID
+    assert gp(layout=4) == INVALID
+    assert gp(ldy=4) == INVALID
+    assert gp(R=None) == INVALID
+    assert gp(K=144) == UNSUPPORTED
+    assert gp(cw=None) == WORKSPACE
+    assert gp(nb=1023) == WORKSPACE
+    assert gp(cw=ctypes.c_void_p(0x10008)) == WORKSPACE
