@@ -55,7 +55,7 @@ def parse():
                         "list, or chosen each step by residual magnitude "
                         "(fp4q_select_channels, k = the workload's channel count)")
     p.add_argument("--comp-weights", choices=("prepared", "inkernel"), default="prepared",
-                   help="dense workloads with fixed channels and the BF16 residual: stream the "
+                   help="fixed channels and the BF16 residual (dense and MoE): stream the "
                         "compensation weights B[n, S_j] made once per weight copy "
                         "(fp4q_comp_weights, fp4q_gemm_prepared), or extract them from the "
                         "packed weights in every call (fp4q_gemm)")
@@ -276,6 +276,10 @@ def main():
 
         wgu = qexperts(data["wt_gate_up"])
         wdn = qexperts(data["wt_down"])
+        prepared = args.comp_weights == "prepared" and nS > 0
+        if prepared:  # made once per expert weight set, like its quantization
+            wgu = wgu + (fq.grouped_comp_weights(fmt, wgu[0], wgu[1], cg),)
+            wdn = wdn + (fq.grouped_comp_weights(fmt, wdn[0], wdn[1], cd),)
         torch.cuda.synchronize()
         n_rot = 1   # 128 experts' weights already exceed the last-level cache
         bufs = {}
@@ -319,13 +323,20 @@ def main():
         def gemm(i):
             for tag, w, y, n, k, ch in (("gu", wgu, ygu, I2, H, cg), ("dn", wdn, ydn, H, I, cd)):
                 b = bufs[tag]
-                fq.grouped_gemm_into(fmt, rows, n, k, off, G, b["q"], b["s"], b["t"], w[0], w[1],
-                                     w[2], ch, nS, b["r"], y, 0, gws)
+                if prepared:
+                    fq.grouped_gemm_prepared_into(fmt, rows, n, k, off, G, b["q"], b["s"], b["t"],
+                                                  w[0], w[1], w[2], ch, nS, b["r"], w[3], y, 0)
+                else:
+                    fq.grouped_gemm_into(fmt, rows, n, k, off, G, b["q"], b["s"], b["t"], w[0],
+                                         w[1], w[2], ch, nS, b["r"], y, 0, gws)
 
         loads = data["loads"]
         active = int((loads > 0).sum())
         flops = 2.0 * rows * (H * I2 + I * H)
         wb = active * (I2 * H // 2 + I2 * H // blk + H * I // 2 + H * I // blk)
+        if prepared:  # each active expert's compensation weights, both layers
+            wb += active * (fq.comp_weights_bytes(fmt, fq.ROWMAJOR, I2, H, nS) +
+                            fq.comp_weights_bytes(fmt, fq.ROWMAJOR, H, I, nS))
         gemm_bytes = (rows * (H + I) // 2 + rows * (H + I) // blk + 2 * rows * nS * 2 +
                       2 * G * nS * 4 + wb + rows * (I2 + H) * 4 + 2 * (G + 1) * 4 + 4 * G * 4)
         dn_bytes = rows * I * 2 + rows * I // 2 + rows * I // blk + rows * nS * 2 + G * 4
@@ -343,6 +354,7 @@ def main():
               "top_k": cfg["top_k"], "hidden": H, "inter": I, "routed_rows": rows,
               "n_s_per_expert": nS, "max_expert_rows": int(loads.max()),
               "moe_quant": args.moe_quant,
+              "comp_weights": "prepared" if prepared else "inkernel",
               "empty_experts": int((loads == 0).sum())}
 
     def step(i):
@@ -414,7 +426,7 @@ def main():
     kh = src_hash()
     default_variant = (args.layout == "tiled" and args.out_dtype == "f32" and
                        args.residual == "bf16" and args.channels == "fixed" and
-                       args.comp_weights == "prepared")
+                       args.comp_weights == "prepared" and args.moe_quant == "expert")
     if name in ("prefill_nvfp4", "prefill_mxfp4"):
         mfma_dtype = "f16" if fmt == fq.NVFP4 else "fp4"
         peak = MFMA_PEAK_TFLOPS[mfma_dtype]

@@ -28,7 +28,11 @@ from .binding import (  # noqa: F401
     gemm_residual_fp4_into,
     gemm_residual_fp4_workspace_bytes,
     gemm_workspace_bytes,
+    grouped_comp_weights,
+    grouped_comp_weights_bytes,
     grouped_gemm,
+    grouped_gemm_prepared,
+    grouped_gemm_prepared_into,
     grouped_gemm_into,
     grouped_gemm_workspace_bytes,
     lib,

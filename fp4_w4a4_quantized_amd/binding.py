@@ -87,6 +87,13 @@ def lib():
         L.fp4q_gemm_prepared.restype = ctypes.c_int
         L.fp4q_gemm_prepared.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, P, P, P, P, P,
                                          P, P, i32, P, P, sz, P, ctypes.c_int, i64, P]
+        L.fp4q_grouped_comp_weights_bytes.restype = sz
+        L.fp4q_grouped_comp_weights_bytes.argtypes = [ctypes.c_int, i64, i64, i32, i32]
+        L.fp4q_grouped_comp_weights.restype = ctypes.c_int
+        L.fp4q_grouped_comp_weights.argtypes = [ctypes.c_int, i64, i64, i32, P, P, P, i32, P, sz, P]
+        L.fp4q_grouped_gemm_prepared.restype = ctypes.c_int
+        L.fp4q_grouped_gemm_prepared.argtypes = [ctypes.c_int, i64, i64, i64, P, i32, P, P, P, P, P,
+                                                 P, P, i32, P, P, sz, P, ctypes.c_int, P]
         L.fp4q_grouped_gemm_workspace_bytes.restype = sz
         L.fp4q_grouped_gemm_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i64, i32, i32]
         L.fp4q_gemm_residual_fp4_workspace_bytes.restype = sz
@@ -167,6 +174,34 @@ def gemm_prepared_into(fmt, layout, M, N, K, a_q, a_s, a_ts, b_q, b_s, b_ts, cha
                                   _ptr(comp_w), nb, _ptr(y), y_dtype, N if ldy is None else ldy,
                                   _stream(stream))
     _check("fp4q_gemm_prepared", rc)
+
+
+def grouped_comp_weights_bytes(fmt, N, K, num_groups, n_chan) -> int:
+    return lib().fp4q_grouped_comp_weights_bytes(fmt, N, K, num_groups, n_chan)
+
+
+def grouped_comp_weights(fmt, bq, bs, chan_idx, stream=None):
+    """Every group's compensation weights: bq [G, N, K/2], bs [G, N, K/blk]
+    (row-major), chan_idx [G, n_chan]; a uint8 tensor in the grouped layout."""
+    G, N, K2 = bq.shape
+    nS = chan_idx.numel() // G
+    nb = grouped_comp_weights_bytes(fmt, N, 2 * K2, G, nS)
+    out = torch.empty(max(nb, 16), dtype=torch.uint8, device=bq.device)
+    rc = lib().fp4q_grouped_comp_weights(fmt, N, 2 * K2, G, _ptr(bq), _ptr(bs), _ptr(chan_idx), nS,
+                                         _ptr(out), out.numel(), _stream(stream))
+    _check("fp4q_grouped_comp_weights", rc)
+    return out
+
+
+def grouped_gemm_prepared_into(fmt, total_rows, N, K, group_offsets, num_groups, a_q, a_s, a_ts,
+                               b_q, b_s, b_ts, chan_idx, n_chan, resid, comp_w, y,
+                               y_dtype=OUT_F32, stream=None):
+    nb = 0 if comp_w is None else comp_w.numel() * comp_w.element_size()
+    rc = lib().fp4q_grouped_gemm_prepared(fmt, total_rows, N, K, _ptr(group_offsets), num_groups,
+                                          _ptr(a_q), _ptr(a_s), _ptr(a_ts), _ptr(b_q), _ptr(b_s),
+                                          _ptr(b_ts), _ptr(chan_idx), n_chan, _ptr(resid),
+                                          _ptr(comp_w), nb, _ptr(y), y_dtype, _stream(stream))
+    _check("fp4q_grouped_gemm_prepared", rc)
 
 
 def gemm_residual_fp4_workspace_bytes(fmt, layout, M, N, K, n_chan) -> int:
@@ -409,6 +444,21 @@ def grouped_gemm(fmt, group_offsets, a, bq, bs, bts, chan_idx=None, y_dtype=OUT_
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
     grouped_gemm_into(fmt, total, N, K, group_offsets, G, a["q"], a["scales"], a["tscale"], bq,
                       bs, bts, chan_idx, nS, a["resid"] if nS else None, y, y_dtype, ws, stream)
+    return y
+
+
+def grouped_gemm_prepared(fmt, group_offsets, a, bq, bs, bts, chan_idx, comp_w, y_dtype=OUT_F32,
+                          stream=None):
+    """grouped_gemm() with comp_w = grouped_comp_weights(fmt, bq, bs, chan_idx)."""
+    total, K = a["q"].shape[0], a["q"].shape[1] * 2
+    G = group_offsets.numel() - 1
+    N = bq.shape[1]
+    nS = chan_idx.numel() // G
+    y = torch.empty((total, N), dtype=torch.float32 if y_dtype == OUT_F32 else torch.bfloat16,
+                    device=a["q"].device)
+    grouped_gemm_prepared_into(fmt, total, N, K, group_offsets, G, a["q"], a["scales"],
+                               a["tscale"], bq, bs, bts, chan_idx, nS, a["resid"], comp_w, y,
+                               y_dtype, stream)
     return y
 
 

@@ -183,7 +183,7 @@ int fp4q_comp_weights(fp4q_format_t fmt, fp4q_layout_t layout, int64_t N, int64_
   if (((N + 15) / 16) * ((n_chan + 31) / 32) / 4 >= (int64_t)UINT32_MAX)
     return FP4Q_ERR_UNSUPPORTED;
   clear_error();
-  fp4q::launch_comp_weights(fmt, layout == FP4Q_LAYOUT_TILED, b_q, b_s, N, K, chan_idx, n_chan,
+  fp4q::launch_comp_weights(fmt, layout == FP4Q_LAYOUT_TILED, b_q, b_s, N, K, chan_idx, n_chan, 1,
                             out, static_cast<hipStream_t>(stream));
   return check_launch();
 }
@@ -290,6 +290,60 @@ int fp4q_grouped_gemm(fp4q_format_t fmt, int64_t total_rows, int64_t N, int64_t 
   fp4q::launch_gemm(fmt, false, total_rows, N, K, group_offsets, num_groups, a_q, a_s, a_ts, b_q,
                     b_s, b_ts, chan_idx, n_chan, resid, nullptr, y, y_dtype == FP4Q_OUT_BF16, N,
                     workspace, static_cast<hipStream_t>(stream));
+  return check_launch();
+}
+
+size_t fp4q_grouped_comp_weights_bytes(fp4q_format_t fmt, int64_t N, int64_t K,
+                                       int32_t num_groups, int32_t n_chan) {
+  (void)fmt;
+  (void)K;
+  if (num_groups < 1) return 0;
+  return (size_t)num_groups * fp4q::comp_weights_bytes(N, n_chan);
+}
+
+int fp4q_grouped_comp_weights(fp4q_format_t fmt, int64_t N, int64_t K, int32_t num_groups,
+                              const uint8_t* b_q, const uint8_t* b_s, const int32_t* chan_idx,
+                              int32_t n_chan, uint8_t* out, size_t out_bytes, void* stream) {
+  if (!fmt_ok(fmt)) return FP4Q_ERR_INVALID;
+  if (N < 0 || K < 0 || n_chan < 0 || num_groups < 1) return FP4Q_ERR_INVALID;
+  if (num_groups > MAX_GROUPS) return FP4Q_ERR_UNSUPPORTED;
+  if ((n_chan > 0) != (chan_idx != nullptr)) return FP4Q_ERR_INVALID;
+  if (N == 0 || n_chan == 0) return FP4Q_OK;
+  if (!b_q || !b_s || !out || !aligned(out, 16)) return FP4Q_ERR_INVALID;
+  if (K % 128 != 0) return FP4Q_ERR_UNSUPPORTED;
+  if (out_bytes < fp4q_grouped_comp_weights_bytes(fmt, N, K, num_groups, n_chan))
+    return FP4Q_ERR_WORKSPACE;
+  if ((int64_t)num_groups * ((N + 15) / 16) * ((n_chan + 31) / 32) / 4 >= (int64_t)UINT32_MAX)
+    return FP4Q_ERR_UNSUPPORTED;
+  clear_error();
+  fp4q::launch_comp_weights(fmt, false, b_q, b_s, N, K, chan_idx, n_chan, num_groups, out,
+                            static_cast<hipStream_t>(stream));
+  return check_launch();
+}
+
+int fp4q_grouped_gemm_prepared(fp4q_format_t fmt, int64_t total_rows, int64_t N, int64_t K,
+                               const int32_t* group_offsets, int32_t num_groups,
+                               const uint8_t* a_q, const uint8_t* a_s, const float* a_ts,
+                               const uint8_t* b_q, const uint8_t* b_s, const float* b_ts,
+                               const int32_t* chan_idx, int32_t n_chan, const uint16_t* resid,
+                               const uint8_t* comp_w, size_t comp_w_bytes, void* y,
+                               fp4q_dtype_t y_dtype, void* stream) {
+  int rc = validate_gemm_common(fmt, N, K, a_q, a_s, a_ts, b_q, b_s, b_ts, chan_idx, n_chan,
+                                resid, y, y_dtype, total_rows);
+  if (rc != FP4Q_OK) return rc;
+  if (num_groups < 1 || !group_offsets) return FP4Q_ERR_INVALID;
+  if (num_groups > MAX_GROUPS) return FP4Q_ERR_UNSUPPORTED;
+  if ((N + 127) / 128 > 65535) return FP4Q_ERR_UNSUPPORTED;
+  const bool work = total_rows > 0 && N > 0 && n_chan > 0;
+  if (work && (!comp_w || !aligned(comp_w, 16) ||
+               comp_w_bytes < fp4q_grouped_comp_weights_bytes(fmt, N, K, num_groups, n_chan)))
+    return FP4Q_ERR_WORKSPACE;
+  // shapes served by the general grouped kernel take the term from chan_idx
+  if (!fp4q::big_grouped_eligible(N, K, n_chan)) comp_w = nullptr;
+  clear_error();
+  fp4q::launch_gemm(fmt, false, total_rows, N, K, group_offsets, num_groups, a_q, a_s, a_ts, b_q,
+                    b_s, b_ts, chan_idx, n_chan, resid, nullptr, y, y_dtype == FP4Q_OUT_BF16, N,
+                    nullptr, static_cast<hipStream_t>(stream), work ? comp_w : nullptr);
   return check_launch();
 }
 

@@ -44,8 +44,8 @@ int launch_gemm_big_grouped(int fmt, int64_t total_rows, int64_t N, int64_t K,
                             const int32_t* off, int G, const uint8_t* aq, const uint8_t* as,
                             const float* ats, const uint8_t* bq, const uint8_t* bs,
                             const float* bts, const int32_t* chan, int nS,
-                            const uint16_t* resid, void* y, int y_bf16, void* ws,
-                            hipStream_t stream);
+                            const uint16_t* resid, const uint8_t* bsel_pre, void* y, int y_bf16,
+                            void* ws, hipStream_t stream);
 int launch_gemm_big(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const uint8_t* aq,
                     const uint8_t* as, const float* ats, const uint8_t* bq, const uint8_t* bs,
                     const float* bts, const int32_t* chan, int nS, const uint16_t* resid,
@@ -55,7 +55,7 @@ int launch_gemm_big(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const 
 // layout the GEMMs stream: 1 KB per 16 columns and 32 channels.
 size_t comp_weights_bytes(int64_t N, int nS);
 void launch_comp_weights(int fmt, bool tiled, const uint8_t* bq, const uint8_t* bs, int64_t N,
-                         int64_t K, const int32_t* chan, int nS, uint8_t* out,
+                         int64_t K, const int32_t* chan, int nS, int G, uint8_t* out,
                          hipStream_t stream);
 
 bool skinny_gemm_eligible(int64_t M, int64_t N, int64_t K, int nS);

@@ -445,8 +445,8 @@ int launch_gemm(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const int3
              tiled};
   if (M == 0 || N == 0) return 0;
   if (off != nullptr && big_grouped_eligible(N, K, nS)) {
-    launch_gemm_big_grouped(fmt, M, N, K, off, G, aq, as, ats, bq, bs, bts, chan, nS, resid, y,
-                            y_bf16, ws, stream);
+    launch_gemm_big_grouped(fmt, M, N, K, off, G, aq, as, ats, bq, bs, bts, chan, nS, resid,
+                            bsel_pre, y, y_bf16, ws, stream);
     return 0;
   }
   if (off != nullptr) {

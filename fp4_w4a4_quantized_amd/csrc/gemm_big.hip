@@ -862,14 +862,15 @@ int launch_gemm_big(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const 
   return 0;
 }
 
-// The compensation weights alone, in the layout the GEMMs stream (one group).
+// The compensation weights alone, in the layout the GEMMs stream: the G groups'
+// blocks one after another (group g's weights at bq + g N K/2).
 void launch_comp_weights(int fmt, bool tiled, const uint8_t* bq, const uint8_t* bs, int64_t N,
-                         int64_t K, const int32_t* chan, int nS, uint8_t* out,
+                         int64_t K, const int32_t* chan, int nS, int G, uint8_t* out,
                          hipStream_t stream) {
-  if (N <= 0 || nS <= 0) return;
+  if (N <= 0 || nS <= 0 || G <= 0) return;
   const int nc = (nS + GB_CS - 1) / GB_CS;
-  if (fmt == FP4Q_NVFP4) launch_gather<FP4Q_NVFP4>(tiled, bq, bs, N, K, chan, nS, nc, 1, out, stream);
-  else launch_gather<FP4Q_MXFP4>(tiled, bq, bs, N, K, chan, nS, nc, 1, out, stream);
+  if (fmt == FP4Q_NVFP4) launch_gather<FP4Q_NVFP4>(tiled, bq, bs, N, K, chan, nS, nc, G, out, stream);
+  else launch_gather<FP4Q_MXFP4>(tiled, bq, bs, N, K, chan, nS, nc, G, out, stream);
 }
 
 size_t comp_weights_bytes(int64_t N, int nS) {
@@ -881,21 +882,24 @@ int launch_gemm_big_grouped(int fmt, int64_t total_rows, int64_t N, int64_t K,
                             const int32_t* off, int G, const uint8_t* aq, const uint8_t* as,
                             const float* ats, const uint8_t* bq, const uint8_t* bs,
                             const float* bts, const int32_t* chan, int nS,
-                            const uint16_t* resid, void* y, int y_bf16, void* ws,
-                            hipStream_t stream) {
+                            const uint16_t* resid, const uint8_t* bsel_pre, void* y, int y_bf16,
+                            void* ws, hipStream_t stream) {
   const int nc = nS > 0 ? (nS + GB_CS - 1) / GB_CS : 0;
-  uint8_t* bsel = static_cast<uint8_t*>(ws);
+  // prepared compensation weights (every group's, made once) replace both
+  // the gather and the in-kernel extraction
+  const bool prepared = bsel_pre != nullptr && nS > 0;
+  uint8_t* bsel = prepared ? const_cast<uint8_t*>(bsel_pre) : static_cast<uint8_t*>(ws);
   BigArgs a{total_rows, N, K, aq, as, ats, bq, bs, bts, nS, resid, bsel, chan, nullptr, y, y_bf16, N,
             0, (int)((N + GB_TILE - 1) / GB_TILE), (int)(K / 128), nc, off, G};
-  const bool gather = nS > GB_XS_MAX;
+  const bool gather = nS > GB_XS_MAX && !prepared;
   // every group adds at most one partial 256-row tile
   const unsigned grid = (unsigned)(((total_rows + GB_TILE - 1) / GB_TILE + G) * a.nt);
   if (fmt == FP4Q_NVFP4) {
     if (gather) launch_gather<FP4Q_NVFP4>(false, bq, bs, N, K, chan, nS, nc, G, bsel, stream);
-    launch_big<FP4Q_NVFP4, true>(a, false, grid, stream);
+    launch_big<FP4Q_NVFP4, true>(a, false, grid, stream, prepared);
   } else {
     if (gather) launch_gather<FP4Q_MXFP4>(false, bq, bs, N, K, chan, nS, nc, G, bsel, stream);
-    launch_big<FP4Q_MXFP4, true>(a, false, grid, stream);
+    launch_big<FP4Q_MXFP4, true>(a, false, grid, stream, prepared);
   }
   return 0;
 }

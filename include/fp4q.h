@@ -226,6 +226,29 @@ int fp4q_gemm_prepared(fp4q_format_t fmt, fp4q_layout_t layout, int64_t M, int64
                        const uint8_t* comp_w, size_t comp_w_bytes, void* y,
                        fp4q_dtype_t y_dtype, int64_t ldy, void* stream);
 
+/* Grouped forms, for fp4q_grouped_gemm's operands (row-major, group g's
+ * weights at b_q + g N K/2 and b_s + g N K/blk, its channels at
+ * chan_idx + g n_chan): the groups' blocks one after another, group g's at
+ * g * fp4q_comp_weights_bytes(fmt, ROWMAJOR, N, K, n_chan).
+ * fp4q_grouped_gemm_prepared is fp4q_grouped_gemm streaming them (no
+ * workspace); with N < 256 (the general grouped kernel) the term comes from
+ * chan_idx.  Errors as the dense forms; more than 2048 groups is
+ * FP4Q_ERR_UNSUPPORTED. */
+size_t fp4q_grouped_comp_weights_bytes(fp4q_format_t fmt, int64_t N, int64_t K,
+                                       int32_t num_groups, int32_t n_chan);
+
+int fp4q_grouped_comp_weights(fp4q_format_t fmt, int64_t N, int64_t K, int32_t num_groups,
+                              const uint8_t* b_q, const uint8_t* b_s, const int32_t* chan_idx,
+                              int32_t n_chan, uint8_t* out, size_t out_bytes, void* stream);
+
+int fp4q_grouped_gemm_prepared(fp4q_format_t fmt, int64_t total_rows, int64_t N, int64_t K,
+                               const int32_t* group_offsets, int32_t num_groups,
+                               const uint8_t* a_q, const uint8_t* a_s, const float* a_ts,
+                               const uint8_t* b_q, const uint8_t* b_s, const float* b_ts,
+                               const int32_t* chan_idx, int32_t n_chan, const uint16_t* resid,
+                               const uint8_t* comp_w, size_t comp_w_bytes, void* y,
+                               fp4q_dtype_t y_dtype, void* stream);
+
 /* ------------------------------------------------------------------------
  * Compensated W4A4 GEMM with a second-pass FP4 residual.  Explainer of the
  * QUADS paper, section 2.2 B: the high-residual channels are quantized a

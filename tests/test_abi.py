@@ -300,3 +300,26 @@ def test_gemm_prepared_rejects(L):
     assert gp(cw=None) == WORKSPACE
     assert gp(nb=1023) == WORKSPACE
     assert gp(cw=ctypes.c_void_p(0x10008)) == WORKSPACE
+
+
+def test_grouped_prepared_rejects(L):
+    assert L.fp4q_grouped_comp_weights_bytes(0, 1536, 2048, 128, 32) == 128 * 96 * 1024
+    assert L.fp4q_grouped_comp_weights_bytes(0, 1536, 2048, 0, 32) == 0
+
+    def gcw(fmt=0, N=32, K=256, G=2, chan=A, nS=8, out=A, nb=4096):
+        return L.fp4q_grouped_comp_weights(fmt, N, K, G, B, B, chan, nS, out, nb, None)
+    assert gcw(fmt=3) == INVALID
+    assert gcw(G=0) == INVALID
+    assert gcw(G=5000) == UNSUPPORTED
+    assert gcw(chan=None) == INVALID
+    assert gcw(K=144) == UNSUPPORTED
+    assert gcw(nb=4095) == WORKSPACE
+    assert gcw(out=ctypes.c_void_p(0x10008)) == INVALID
+
+    def ggp(G=2, off=A, cw=A, nb=1 << 20, nS=8, chan=A, R=B):
+        return L.fp4q_grouped_gemm_prepared(0, 64, 256, 256, off, G, A, A, B, B, B, B, chan, nS, R,
+                                            cw, nb, A, 0, None)
+    assert ggp(off=None) == INVALID
+    assert ggp(G=5000) == UNSUPPORTED
+    assert ggp(cw=None) == WORKSPACE
+    assert ggp(nb=100) == WORKSPACE

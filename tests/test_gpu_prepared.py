@@ -99,3 +99,44 @@ def test_prepared_shapes(orc, fmt, M, N, K, nS):
     chan = np.sort(np.random.default_rng(M + N).choice(K, nS, replace=False)).astype(np.int32)
     for layout in (fq.ROWMAJOR, fq.TILED):
         _check_prepared(orc, fmt, layout, d, chan)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("N,nS", [(512, 32), (300, 104), (200, 8)])
+def test_grouped_prepared(orc, fmt, N, nS):
+    """fp4q_grouped_comp_weights bit for bit per group, and
+    fp4q_grouped_gemm_prepared against the oracle's grouped GEMM, with empty,
+    single-row and ragged groups: the 256-tile grouped kernel (|S| taken
+    in-kernel and gathered forms both replaced) and, at N < 256, the general
+    grouped kernel taking the term from chan_idx."""
+    need_gpu()
+    say(f"grouped prepared fmt {fmt} N{N} nS{nS}")
+    K = 384
+    off = np.array([0, 0, 1, 70, 70, 300, 333], np.int32)
+    G = off.size - 1
+    x = dense_case(333, K, 8, n_out=3, seed=71)["x"]
+    wts = [dense_case(1, K, N, seed=80 + g)["wt"] for g in range(G)]
+    rng = np.random.default_rng(N + nS)
+    chan = np.sort(np.stack([rng.choice(K, nS, replace=False) for _ in range(G)]), 1).astype(np.int32)
+    qa = orc.quantize(fmt, x, offsets=off, chan_idx=chan)
+    qbs = [orc.quantize(fmt, w) for w in wts]
+    bq = np.stack([q["q"] for q in qbs])
+    bs = np.stack([q["scales"] for q in qbs])
+    bts = np.array([q["tscale"][0] for q in qbs], np.float32) if fmt == 0 else None
+    cw = fq.grouped_comp_weights(fmt, to_dev(bq), to_dev(bs), to_dev(chan))
+    got = to_host(cw).view(np.uint16)
+    per = fq.comp_weights_bytes(fmt, fq.ROWMAJOR, N, K, nS) // 2
+    for g in range(G):
+        want = _expected_comp_weights(orc, fmt, qbs[g], chan[g])
+        assert want.size == per
+        bad = np.flatnonzero(got[g * per:(g + 1) * per] != want)
+        assert bad.size == 0, f"group {g}: {bad.size} mismatches, first at {bad[:4].tolist()}"
+    a = {"q": to_dev(qa["q"]), "scales": to_dev(qa["scales"]),
+         "tscale": None if fmt else to_dev(qa["tscale"]), "resid": to_dev(qa["resid"])}
+    y = to_host(fq.grouped_gemm_prepared(fmt, to_dev(off), a, to_dev(bq), to_dev(bs),
+                                         None if fmt else to_dev(bts), to_dev(chan), cw))
+    pm = np.repeat(np.arange(x.shape[0]), N)
+    pn = np.tile(np.arange(N), x.shape[0])
+    yo, ya = orc.grouped_gemm_points(fmt, off, qa["q"], qa["scales"], qa["tscale"], bq, bs, bts,
+                                     chan, qa["resid"], pm, pn)
+    assert_gemm_close(y[pm, pn], yo, ya)
