@@ -37,8 +37,8 @@ namespace fp4q {
 
 constexpr int QT = 256;              // threads per workgroup, general path
 constexpr int QU = 4;                // chunks per thread, general path
-constexpr int FT = 1024;             // threads per workgroup, fused small path
-constexpr int64_t FUSED_MAX_CHUNKS = 32 * FT;  // small-tensor path up to 256K elements
+constexpr int FT = 512;              // threads per workgroup, fused small path
+constexpr int64_t FUSED_MAX_CHUNKS = 32 * FT;  // small-tensor path up to 128K elements
 constexpr bool SMALL_FUSED = true;   // small tensors: one launch (else two short passes)
 constexpr int AMAX_PARTS = 1024;     // partial maxima of the dense large path
 constexpr int AMAX_BATCH = 16;       // loads in flight per thread in amax scans
@@ -220,7 +220,7 @@ __global__ void __launch_bounds__(QT) k_group_amax(ChunkGrid gr, int64_t rows,
 // load on the critical path.  Workgroup 0 then advances the counter; every
 // workgroup has read it by then (their slots carry the tag derived from
 // it).  Spins are bounded.  Every workgroup of the launch is resident at
-// once (at most 32 workgroups of 1024 threads), and one such launch runs at
+// once (at most 32 workgroups of 512 threads), and one such launch runs at
 // a time on a device.
 constexpr uint32_t GRID_SPIN_LIMIT = 1u << 22;
 constexpr uint32_t GRID_SLOTS = 32;

@@ -130,7 +130,7 @@ int fp4q_packed_bytes(fp4q_format_t fmt, fp4q_layout_t layout, int64_t rows, int
  * rows * cols / 8 must be below 2^31 (FP4Q_ERR_UNSUPPORTED otherwise: 32 GiB
  * of BF16 per call).
  *
- * Small NVFP4 tensors (one group, at most 262,144 elements, the tiled
+ * Small NVFP4 tensors (one group, at most 131,072 elements, the tiled
  * layout counting its rows padded to 16) take one launch
  * whose workgroups exchange the tensor maximum through per-device state of
  * the library: two such calls must not run at the same time on one GPU
