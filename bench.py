@@ -9,16 +9,21 @@ re-quantized only at weight sync).  Enough distinct weight and output copies
 rotate to defeat the 256 MB last-level cache on the memory-bound workloads.
 
 The timed steps run as one captured HIP graph (host launch cost out of the
-measurement); per-kernel times come from HIP events around a graph of
-repeated launches of that kernel on the same stream.
+measurement); per-kernel times come from HIP events on the launch stream
+around a graph of repeated launches of that kernel.
 
-Default workload: dense decode NVFP4, X [64 x 2048], W [2048 x 11008],
-|S| = 64.  Prints ONE JSON line.  --workload selects another configuration
-(prefill_nvfp4, prefill_mxfp4, moe_nvfp4, tiny_nvfp4) for profiling.
+Default line: the largest single-GPU workload, dense prefill NVFP4
+(X [8192 x 4096], W [4096 x 14336], |S| = 128).  The same line carries the
+other workloads (prefill MXFP4 on the same tensors, dense decode NVFP4, the
+MoE layer) under "extra_workloads", and the chip's attainable matrix-core
+and HBM peaks measured by microbenchmarks under "attainable".  Prints ONE
+JSON line.  --workload alone measures one workload (with its variants) for
+profiling.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -33,16 +38,19 @@ METRIC = "compensated W4A4 GEMM effective TFLOP/s + quantize GB/s, % of roofline
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "fp4": 10100.0}
 LLC_BYTES = 256 << 20
+HEADLINE = "prefill_nvfp4"
+EXTRAS = ("prefill_mxfp4", "decode_nvfp4", "moe_nvfp4")
+WORKLOADS = ("prefill_nvfp4", "prefill_mxfp4", "decode_nvfp4", "moe_nvfp4", "tiny_nvfp4")
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="decode_nvfp4",
-                   choices=["decode_nvfp4", "prefill_nvfp4", "prefill_mxfp4", "moe_nvfp4",
-                            "tiny_nvfp4"])
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default=None, choices=WORKLOADS,
+                   help="measure this workload only (default: the prefill NVFP4 line with the "
+                        "other workloads as extra keys)")
     p.add_argument("--layout", choices=("tiled", "rowmajor"), default="tiled",
                    help="packed operand layout of the dense workloads (MoE is row-major)")
     p.add_argument("--out-dtype", choices=("f32", "bf16"), default="f32",
@@ -63,13 +71,26 @@ def parse():
                    help="MoE gate_up input: quantize the routed copies per expert, or quantize "
                         "the token matrix once and permute its FP4 codes "
                         "(fp4q_permute_quantized, one tensor scale for all tokens)")
+    p.add_argument("--no-extras", action="store_true",
+                   help="default line without the extra workloads")
+    p.add_argument("--no-peaks", action="store_true",
+                   help="skip the attainable-peak microbenchmarks")
+    p.add_argument("--peaks-only", action="store_true",
+                   help="run only the attainable-peak microbenchmarks and print them")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a device-to-device copy of 256 MiB, 5 times (the known-size "
                         "reference for the FETCH_SIZE / WRITE_SIZE counter scale)")
+    p.add_argument("--decompose-only", default=None, choices=("nvfp4", "mxfp4"),
+                   help="run only the error decomposition of the prefill activations, 5 calls "
+                        "(the command behind its counter profile)")
     return p.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def copy_calibration():
@@ -115,31 +136,111 @@ def load_traffic(workload: str, default_variant: bool):
     return None
 
 
-def main():
-    args = parse()
-    if args.copy_calibration:
-        copy_calibration()
-        return
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is "
-              "single-GPU by design and multi-GPU sharding is not built.", file=sys.stderr)
-        sys.exit(2)
+# ---- attainable peaks ---------------------------------------------------------
 
+def measure_peaks(stream):
+    """Matrix-core and HBM throughput the chip delivers to simple kernels
+    (libfp4q_peaks.so): f16 and FP4 MFMA chains with no memory traffic, a
+    streaming read and a streaming copy of 4 GiB (far above the 256 MB
+    last-level cache).  Best of a few launches each."""
+    import torch
+    path = os.path.join(ROOT, "fp4_w4a4_quantized_amd", "libfp4q_peaks.so")
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m fp4_w4a4_quantized_amd.build`")
+    L = ctypes.CDLL(path)
+    P, i32, u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64
+    L.fp4q_peak_mfma.argtypes = [i32, i32, i32, P, ctypes.POINTER(ctypes.c_double), P]
+    L.fp4q_peak_mfma_out_floats.restype = ctypes.c_int64
+    L.fp4q_peak_mfma_out_floats.argtypes = [i32]
+    L.fp4q_peak_read.argtypes = [P, u64, i32, P, P]
+    L.fp4q_peak_copy.argtypes = [P, P, u64, i32, P]
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def best_time(launch, reps=5):
+        best = None
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            launch()
+            b.record(stream)
+            torch.cuda.synchronize()
+            t = a.elapsed_time(b) * 1e-3
+            best = t if best is None else min(best, t)
+        return best
+
+    out = {}
+    blocks = 256 * 2                     # two 4-wave workgroups per CU: 2 waves per SIMD
+    buf = torch.empty(L.fp4q_peak_mfma_out_floats(blocks), dtype=torch.float32,
+                      device=stream.device)
+    for kind, key, iters in ((0, "mfma_f16_tflops", 20000), (1, "mfma_fp4_tflops", 10000)):
+        fl = ctypes.c_double(0.0)
+
+        def run():
+            rc = L.fp4q_peak_mfma(kind, blocks, iters, ctypes.c_void_p(buf.data_ptr()),
+                                  ctypes.byref(fl), sp)
+            assert rc == 0, f"fp4q_peak_mfma rc {rc}"
+        t = best_time(run)
+        out[key] = round(fl.value / t / 1e12, 1)
+    nbytes = 4 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device=stream.device)
+    src.fill_(3)
+    sink = torch.empty(2048 * 256, dtype=torch.int32, device=stream.device)
+
+    def read():
+        assert L.fp4q_peak_read(ctypes.c_void_p(src.data_ptr()), nbytes, 2048,
+                                ctypes.c_void_p(sink.data_ptr()), sp) == 0
+    out["hbm_read_gbs"] = round(nbytes / best_time(read) / 1e9, 1)
+    half = nbytes // 2
+
+    def copy():
+        assert L.fp4q_peak_copy(ctypes.c_void_p(src.data_ptr()),
+                                ctypes.c_void_p(src.data_ptr() + half), half, 2048, sp) == 0
+    out["hbm_copy_gbs"] = round(2 * half / best_time(copy) / 1e9, 1)
+    del src, sink, buf
+    torch.cuda.empty_cache()
+    out["about"] = ("best of 5 launches: 512 workgroups x 4 waves of 8 independent MFMA chains "
+                    "(f16 32x32x16; FP4 32x32x64 scaled, random codes); streaming read and "
+                    "copy over 4 GiB, 16 B per lane per load (copy counts read + write bytes)")
+    return out
+
+
+# ---- workloads ----------------------------------------------------------------
+
+_DATA = {}
+
+
+def workload_data(name, cfg):
+    """Seeded inputs; the two prefill workloads share their tensors."""
+    from workloads import dense_case, moe_case
+    key = tuple(sorted((k, v) for k, v in cfg.items() if k != "fmt"))
+    if key not in _DATA:
+        t0 = time.time()
+        log(f"generating {name} inputs")
+        _DATA[key] = moe_case(**cfg) if name == "moe_nvfp4" else dense_case(**cfg)
+        log(f"inputs ready in {time.time() - t0:.1f}s")
+    return _DATA[key]
+
+
+def input_sha256(name, data) -> str:
+    h = hashlib.sha256()
+    keys = (("x_perm", "h_perm", "offsets", "chan_gate_up", "chan_down") if name == "moe_nvfp4"
+            else ("x", "wt", "chan_idx"))
+    for k in keys:
+        h.update(memoryview(data[k]).cast("B"))
+    return h.hexdigest()
+
+
+class Step:
+    """The pieces of one workload's step: quant(), gemm(i), optional select(),
+    the algorithmic work and the configuration record."""
+
+
+def build_dense(name, cfg, data, args, dev):
     import numpy as np
     import torch
 
     import fp4_w4a4_quantized_amd as fq
-    from workloads import CONFIGS, dense_case, moe_case
-
-    assert torch.cuda.is_available(), "bench.py needs the GPU"
-    dev = torch.device("cuda:0")
-    # an explicit stream (default priority) for all work and for the timing
-    # events.  Library calls take the current stream (no explicit argument):
-    # under graph capture that is the capture stream.
-    stream = torch.cuda.Stream(dev)
-    torch.cuda.set_stream(stream)
-    name = args.workload
-    cfg = CONFIGS[name]
+    s = Step()
     fmt = fq.NVFP4 if cfg["fmt"] == "nvfp4" else fq.MXFP4
     blk = fq.BLOCK[fmt]
 
@@ -147,224 +248,254 @@ def main():
         a = np.ascontiguousarray(a)
         return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
 
-    t0 = time.time()
-    print(f"[bench] generating {name} inputs", file=sys.stderr, flush=True)
-    if name == "moe_nvfp4":
-        data = moe_case(**cfg)
-    else:
-        data = dense_case(**cfg)
-    print(f"[bench] inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    M, K, N = cfg["M"], cfg["K"], cfg["N"]
+    nS = int(data["chan_idx"].size)
+    x = up(data["x"])
+    chan = up(data["chan_idx"]) if nS else None
+    layout = fq.TILED if args.layout == "tiled" else fq.ROWMAJOR
+    wq = fq.quantize(fmt, up(data["wt"]), layout=layout)  # offline weight quantization
+    torch.cuda.synchronize()
+    w_bytes = N * (K // 2) + N * (K // blk)
+    y_bytes = M * N * (2 if args.out_dtype == "bf16" else 4)
+    prepared = (args.comp_weights == "prepared" and nS > 0 and args.channels == "fixed" and
+                args.residual == "bf16")
+    cw_bytes = fq.comp_weights_bytes(fmt, layout, N, K, nS) if prepared else 0
+    n_rot = max(1, math.ceil(1.2 * LLC_BYTES / (w_bytes + y_bytes + cw_bytes)))
+    n_rot = min(n_rot, 64)
+    wcopies = [wq] + [{k: (v.clone() if isinstance(v, torch.Tensor) else v)
+                       for k, v in wq.items()} for _ in range(n_rot - 1)]
+    if prepared:  # made once per weight copy, like the weight quantization itself
+        for w in wcopies:
+            w["comp_w"] = fq.comp_weights(fmt, w, chan)
+    ydt = fq.OUT_BF16 if args.out_dtype == "bf16" else fq.OUT_F32
+    ys = [torch.empty((M, N), dtype=torch.bfloat16 if ydt == fq.OUT_BF16 else torch.float32,
+                      device=dev) for _ in range(n_rot)]
+    gwsb = fq.gemm_workspace_bytes(fmt, layout, M, N, K, nS)
+    gws = torch.empty(gwsb, dtype=torch.uint8, device=dev) if gwsb else None
+    qws = torch.zeros(max(fq.quantize_workspace_bytes(fmt, M, K, 1), 16), dtype=torch.uint8,
+                      device=dev)
+    cb, sb = fq.packed_bytes(fmt, layout, M, K)
+    aq = torch.empty(cb, dtype=torch.uint8, device=dev)
+    asc = torch.empty(sb, dtype=torch.uint8, device=dev)
+    ats = torch.empty(1, dtype=torch.float32, device=dev) if fmt == fq.NVFP4 else None
+    ar = torch.empty((M, nS), dtype=torch.int16, device=dev) if nS else None
 
-    # ---- build the step ------------------------------------------------------
-    if name != "moe_nvfp4":
-        M, K, N = cfg["M"], cfg["K"], cfg["N"]
-        nS = int(data["chan_idx"].size)
-        x = up(data["x"])
-        chan = up(data["chan_idx"]) if nS else None
-        layout = fq.TILED if args.layout == "tiled" else fq.ROWMAJOR
-        wq = fq.quantize(fmt, up(data["wt"]), layout=layout)  # offline weight quantization
-        torch.cuda.synchronize()
-        w_bytes = N * (K // 2) + N * (K // blk)
-        y_bytes = M * N * (2 if args.out_dtype == "bf16" else 4)
-        prepared = (args.comp_weights == "prepared" and nS > 0 and args.channels == "fixed" and
-                    args.residual == "bf16")
-        cw_bytes = fq.comp_weights_bytes(fmt, layout, N, K, nS) if prepared else 0
-        n_rot = max(1, math.ceil(1.2 * LLC_BYTES / (w_bytes + y_bytes + cw_bytes)))
-        n_rot = min(n_rot, 64)
-        wcopies = [wq] + [{k: (v.clone() if isinstance(v, torch.Tensor) else v)
-                           for k, v in wq.items()} for _ in range(n_rot - 1)]
-        if prepared:  # made once per weight copy, like the weight quantization itself
-            for w in wcopies:
-                w["comp_w"] = fq.comp_weights(fmt, w, chan)
-        ydt = fq.OUT_BF16 if args.out_dtype == "bf16" else fq.OUT_F32
-        ys = [torch.empty((M, N), dtype=torch.bfloat16 if ydt == fq.OUT_BF16 else torch.float32,
-                          device=dev) for _ in range(n_rot)]
-        gwsb = fq.gemm_workspace_bytes(fmt, layout, M, N, K, nS)
-        gws = torch.empty(gwsb, dtype=torch.uint8, device=dev) if gwsb else None
-        G = 1
-        qws = torch.zeros(max(fq.quantize_workspace_bytes(fmt, M, K, 1), 16), dtype=torch.uint8,
+    online = args.channels == "online"
+    s.select = None
+    if online:
+        if nS == 0:
+            sys.exit("--channels online needs a workload with compensated channels")
+        chan = torch.empty(nS, dtype=torch.int32, device=dev)
+        sws = torch.empty(fq.select_channels_workspace_bytes(M, K), dtype=torch.uint8,
                           device=dev)
-        cb, sb = fq.packed_bytes(fmt, layout, M, K)
-        aq = torch.empty(cb, dtype=torch.uint8, device=dev)
-        asc = torch.empty(sb, dtype=torch.uint8, device=dev)
-        ats = torch.empty(1, dtype=torch.float32, device=dev) if fmt == fq.NVFP4 else None
-        ar = torch.empty((M, nS), dtype=torch.int16, device=dev) if nS else None
 
-        online = args.channels == "online"
+        def select():
+            fq.select_channels_into(fmt, layout, x, aq, asc, ats, nS, chan, ar, sws)
+        s.select = select
+
+    r4 = args.residual == "fp4"
+    if r4:
+        if nS == 0 or nS % blk:
+            sys.exit(f"--residual fp4 needs |S| a multiple of {blk} (this workload: {nS})")
+        # second pass: R [M, nS] quantized row-major, then the FP4-residual GEMM
+        rq = torch.empty((M, nS // 2), dtype=torch.uint8, device=dev)
+        rsc = torch.empty((M, nS // blk), dtype=torch.uint8, device=dev)
+        rts = torch.empty(1, dtype=torch.float32, device=dev) if fmt == fq.NVFP4 else None
+        rqws = torch.zeros(max(fq.quantize_workspace_bytes(fmt, M, nS, 1), 16),
+                           dtype=torch.uint8, device=dev)
+        gwsb = fq.gemm_residual_fp4_workspace_bytes(fmt, layout, M, N, K, nS)
+        gws = torch.empty(gwsb, dtype=torch.uint8, device=dev)
+
+    def quant():
         if online:
-            if nS == 0:
-                sys.exit("--channels online needs a workload with compensated channels")
-            chan = torch.empty(nS, dtype=torch.int32, device=dev)
-            sws = torch.empty(fq.select_channels_workspace_bytes(M, K), dtype=torch.uint8,
-                              device=dev)
-
-            def select():
-                fq.select_channels_into(fmt, layout, x, aq, asc, ats, nS, chan, ar, sws)
-
-        r4 = args.residual == "fp4"
-        if r4:
-            if nS == 0 or nS % blk:
-                sys.exit(f"--residual fp4 needs |S| a multiple of {blk} (this workload: {nS})")
-            # second pass: R [M, nS] quantized row-major, then the FP4-residual GEMM
-            rq = torch.empty((M, nS // 2), dtype=torch.uint8, device=dev)
-            rsc = torch.empty((M, nS // blk), dtype=torch.uint8, device=dev)
-            rts = torch.empty(1, dtype=torch.float32, device=dev) if fmt == fq.NVFP4 else None
-            rqws = torch.zeros(max(fq.quantize_workspace_bytes(fmt, M, nS, 1), 16),
-                               dtype=torch.uint8, device=dev)
-            gwsb = fq.gemm_residual_fp4_workspace_bytes(fmt, layout, M, N, K, nS)
-            gws = torch.empty(gwsb, dtype=torch.uint8, device=dev)
-
-        def quant():
-            if online:
-                fq.quantize_into(fmt, layout, x, None, 1, None, 0, aq, asc, ats, None, qws)
-                select()
-            else:
-                fq.quantize_into(fmt, layout, x, None, 1, chan, nS, aq, asc, ats, ar, qws)
-            if r4:
-                fq.quantize_into(fmt, fq.ROWMAJOR, ar, None, 1, None, 0, rq, rsc, rts, None, rqws)
-
-        def gemm(i):
-            w = wcopies[i % n_rot]
-            if r4:
-                fq.gemm_residual_fp4_into(fmt, layout, M, N, K, aq, asc, ats, w["q"], w["scales"],
-                                          w["tscale"], chan, nS, rq, rsc, rts, ys[i % n_rot], ydt,
-                                          N, gws)
-            elif prepared:
-                fq.gemm_prepared_into(fmt, layout, M, N, K, aq, asc, ats, w["q"], w["scales"],
-                                      w["tscale"], chan, nS, ar, w["comp_w"], ys[i % n_rot], ydt,
-                                      N)
-            else:
-                fq.gemm_into(fmt, layout, M, N, K, aq, asc, ats, w["q"], w["scales"],
-                             w["tscale"], chan, nS, ar, ys[i % n_rot], ydt, N, gws)
-
-        flops = 2.0 * M * N * K
-        r_bytes = (M * nS // 2 + M * nS // blk + (4 if fmt == fq.NVFP4 else 0)) if r4 else M * nS * 2
-        gemm_bytes = (M * K // 2 + M * K // blk + r_bytes + nS * 4 + w_bytes + y_bytes +
-                      cw_bytes + (8 if fmt == fq.NVFP4 else 0))
-        quant_bytes = M * K * 2 + M * K // 2 + M * K // blk + M * nS * 2 + (4 if fmt == fq.NVFP4
-                                                                             else 0)
-        if r4:
-            quant_bytes += M * nS * 2 + r_bytes
-        if online:
-            # the selection reads x, codes and scales again, writes R and S
-            select_bytes = (M * K * 2 + M * K // 2 + M * K // blk + M * nS * 2 + nS * 4 +
-                            (4 if fmt == fq.NVFP4 else 0))
-            quant_bytes += select_bytes
-        wl = {"workload": name, "format": cfg["fmt"], "M": M, "K": K, "N": N, "n_s": nS,
-              "layout": args.layout, "out_dtype": args.out_dtype, "weight_copies_rotated": n_rot,
-              "residual": args.residual, "channels": args.channels,
-              "comp_weights": "prepared" if prepared else "inkernel"}
-    else:
-        if args.channels != "fixed" or args.residual != "bf16":
-            sys.exit("moe_nvfp4 takes the fixed per-expert channel lists and the BF16 residual")
-        moe_tok = args.moe_quant == "token"
-        online = False
-        # MoE layer: gate_up then down, per-expert NVFP4, grouped GEMMs
-        off = up(data["offsets"])
-        G = int(data["offsets"].size - 1)
-        rows = int(data["offsets"][-1])
-        H, I2 = cfg["hidden"], 2 * cfg["inter"]
-        I = cfg["inter"]
-        nS = cfg["n_s"]
-        xg, xd = up(data["x_perm"]), up(data["h_perm"])
-        cg, cd = up(data["chan_gate_up"]), up(data["chan_down"])
-
-        def qexperts(wt):
-            qs = [fq.quantize(fmt, up(wt[e])) for e in range(G)]
-            return (torch.stack([q["q"] for q in qs]), torch.stack([q["scales"] for q in qs]),
-                    torch.cat([q["tscale"] for q in qs]))
-
-        wgu = qexperts(data["wt_gate_up"])
-        wdn = qexperts(data["wt_down"])
-        prepared = args.comp_weights == "prepared" and nS > 0
-        if prepared:  # made once per expert weight set, like its quantization
-            wgu = wgu + (fq.grouped_comp_weights(fmt, wgu[0], wgu[1], cg),)
-            wdn = wdn + (fq.grouped_comp_weights(fmt, wdn[0], wdn[1], cd),)
-        torch.cuda.synchronize()
-        n_rot = 1   # 128 experts' weights already exceed the last-level cache
-        bufs = {}
-        for tag, (r, k) in {"gu": (rows, H), "dn": (rows, I)}.items():
-            bufs[tag] = dict(
-                q=torch.empty((r, k // 2), dtype=torch.uint8, device=dev),
-                s=torch.empty((r, k // blk), dtype=torch.uint8, device=dev),
-                t=torch.empty(G, dtype=torch.float32, device=dev),
-                r=torch.empty((r, nS), dtype=torch.int16, device=dev),
-                ws=torch.zeros(max(fq.quantize_workspace_bytes(fmt, r, k, G), 16),
-                               dtype=torch.uint8, device=dev))
-        ygu = torch.empty((rows, I2), dtype=torch.float32, device=dev)
-        ydn = torch.empty((rows, H), dtype=torch.float32, device=dev)
-
-        if moe_tok:
-            T = cfg["tokens"]
-            xt = up(data["x_tok"])
-            src = up(data["token_of_row"].astype(np.int32))
-            tq = torch.empty((T, H // 2), dtype=torch.uint8, device=dev)
-            tsc = torch.empty((T, H // blk), dtype=torch.uint8, device=dev)
-            tts = torch.empty(1, dtype=torch.float32, device=dev)
-            tws = torch.zeros(max(fq.quantize_workspace_bytes(fmt, T, H, 1), 16),
-                              dtype=torch.uint8, device=dev)
-
-        def quant():
-            if moe_tok:
-                b = bufs["gu"]
-                fq.quantize_into(fmt, fq.ROWMAJOR, xt, None, 1, None, 0, tq, tsc, tts, None, tws)
-                fq.permute_quantized_into(fmt, xt, tq, tsc, tts, src, off, G, cg, nS, b["q"],
-                                          b["s"], b["t"], b["r"])
-            for tag, xin, ch in ((("dn", xd, cd),) if moe_tok else
-                                 (("gu", xg, cg), ("dn", xd, cd))):
-                b = bufs[tag]
-                fq.quantize_into(fmt, fq.ROWMAJOR, xin, off, G, ch, nS, b["q"], b["s"], b["t"], b["r"],
-                                 b["ws"])
-
-        gws_bytes = max(fq.grouped_gemm_workspace_bytes(fmt, rows, I2, H, G, nS),
-                        fq.grouped_gemm_workspace_bytes(fmt, rows, H, I, G, nS))
-        gws = torch.empty(gws_bytes, dtype=torch.uint8, device=dev) if gws_bytes else None
-
-        def gemm(i):
-            for tag, w, y, n, k, ch in (("gu", wgu, ygu, I2, H, cg), ("dn", wdn, ydn, H, I, cd)):
-                b = bufs[tag]
-                if prepared:
-                    fq.grouped_gemm_prepared_into(fmt, rows, n, k, off, G, b["q"], b["s"], b["t"],
-                                                  w[0], w[1], w[2], ch, nS, b["r"], w[3], y, 0)
-                else:
-                    fq.grouped_gemm_into(fmt, rows, n, k, off, G, b["q"], b["s"], b["t"], w[0],
-                                         w[1], w[2], ch, nS, b["r"], y, 0, gws)
-
-        loads = data["loads"]
-        active = int((loads > 0).sum())
-        flops = 2.0 * rows * (H * I2 + I * H)
-        wb = active * (I2 * H // 2 + I2 * H // blk + H * I // 2 + H * I // blk)
-        if prepared:  # each active expert's compensation weights, both layers
-            wb += active * (fq.comp_weights_bytes(fmt, fq.ROWMAJOR, I2, H, nS) +
-                            fq.comp_weights_bytes(fmt, fq.ROWMAJOR, H, I, nS))
-        gemm_bytes = (rows * (H + I) // 2 + rows * (H + I) // blk + 2 * rows * nS * 2 +
-                      2 * G * nS * 4 + wb + rows * (I2 + H) * 4 + 2 * (G + 1) * 4 + 4 * G * 4)
-        dn_bytes = rows * I * 2 + rows * I // 2 + rows * I // blk + rows * nS * 2 + G * 4
-        if moe_tok:
-            # tokens read and quantized once; codes read once and written per routed row;
-            # the residual gathers x and writes R
-            T = cfg["tokens"]
-            gu_bytes = (T * H * 2 + 2 * T * (H // 2 + H // blk) + rows * (H // 2 + H // blk) +
-                        rows * nS * 4 + G * 4 + 4)
+            fq.quantize_into(fmt, layout, x, None, 1, None, 0, aq, asc, ats, None, qws)
+            select()
         else:
-            gu_bytes = rows * H * 2 + rows * H // 2 + rows * H // blk + rows * nS * 2 + G * 4
-        quant_bytes = gu_bytes + dn_bytes
-        M, K, N = rows, H, I2
-        wl = {"workload": name, "format": "nvfp4", "tokens": cfg["tokens"], "experts": G,
-              "top_k": cfg["top_k"], "hidden": H, "inter": I, "routed_rows": rows,
-              "n_s_per_expert": nS, "max_expert_rows": int(loads.max()),
-              "moe_quant": args.moe_quant,
-              "comp_weights": "prepared" if prepared else "inkernel",
-              "empty_experts": int((loads == 0).sum())}
+            fq.quantize_into(fmt, layout, x, None, 1, chan, nS, aq, asc, ats, ar, qws)
+        if r4:
+            fq.quantize_into(fmt, fq.ROWMAJOR, ar, None, 1, None, 0, rq, rsc, rts, None, rqws)
+
+    def gemm(i):
+        w = wcopies[i % n_rot]
+        if r4:
+            fq.gemm_residual_fp4_into(fmt, layout, M, N, K, aq, asc, ats, w["q"], w["scales"],
+                                      w["tscale"], chan, nS, rq, rsc, rts, ys[i % n_rot], ydt,
+                                      N, gws)
+        elif prepared:
+            fq.gemm_prepared_into(fmt, layout, M, N, K, aq, asc, ats, w["q"], w["scales"],
+                                  w["tscale"], chan, nS, ar, w["comp_w"], ys[i % n_rot], ydt, N)
+        else:
+            fq.gemm_into(fmt, layout, M, N, K, aq, asc, ats, w["q"], w["scales"],
+                         w["tscale"], chan, nS, ar, ys[i % n_rot], ydt, N, gws)
+
+    s.quant, s.gemm = quant, gemm
+    s.fmt, s.M, s.K, s.x = fmt, M, K, x
+    s.flops = 2.0 * M * N * K
+    r_bytes = (M * nS // 2 + M * nS // blk + (4 if fmt == fq.NVFP4 else 0)) if r4 else M * nS * 2
+    # algorithmic bytes of the compensated GEMM: Xq + sx + R + S + Wq + sw + Y
+    # (+ the two tensor scales); the prepared compensation weights are the
+    # implementation's choice and are reported apart as extra bytes
+    s.gemm_bytes = (M * K // 2 + M * K // blk + r_bytes + nS * 4 + w_bytes + y_bytes +
+                    (8 if fmt == fq.NVFP4 else 0))
+    s.extra_bytes = cw_bytes
+    s.quant_bytes = M * K * 2 + M * K // 2 + M * K // blk + M * nS * 2 + (4 if fmt == fq.NVFP4
+                                                                           else 0)
+    if r4:
+        s.quant_bytes += M * nS * 2 + r_bytes
+    s.select_bytes = None
+    if online:
+        # the selection reads x, codes and scales again, writes R and S
+        s.select_bytes = (M * K * 2 + M * K // 2 + M * K // blk + M * nS * 2 + nS * 4 +
+                          (4 if fmt == fq.NVFP4 else 0))
+        s.quant_bytes += s.select_bytes
+    s.mfma = name in ("prefill_nvfp4", "prefill_mxfp4")
+    s.wl = {"workload": name, "format": cfg["fmt"], "M": M, "K": K, "N": N, "n_s": nS,
+            "layout": args.layout, "out_dtype": args.out_dtype, "weight_copies_rotated": n_rot,
+            "residual": args.residual, "channels": args.channels,
+            "comp_weights": "prepared" if prepared else "inkernel"}
+    s.keep = (wcopies, ys, gws, qws, aq, asc, ats, ar, x, chan)
+    return s
+
+
+def build_moe(name, cfg, data, args, dev):
+    import numpy as np
+    import torch
+
+    import fp4_w4a4_quantized_amd as fq
+    if args.channels != "fixed" or args.residual != "bf16":
+        sys.exit("moe_nvfp4 takes the fixed per-expert channel lists and the BF16 residual")
+    s = Step()
+    s.select = None
+    fmt = fq.NVFP4
+    blk = fq.BLOCK[fmt]
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+
+    moe_tok = args.moe_quant == "token"
+    off = up(data["offsets"])
+    G = int(data["offsets"].size - 1)
+    rows = int(data["offsets"][-1])
+    H, I2 = cfg["hidden"], 2 * cfg["inter"]
+    I = cfg["inter"]
+    nS = cfg["n_s"]
+    xg, xd = up(data["x_perm"]), up(data["h_perm"])
+    cg, cd = up(data["chan_gate_up"]), up(data["chan_down"])
+
+    def qexperts(wt):
+        qs = [fq.quantize(fmt, up(wt[e])) for e in range(G)]
+        return (torch.stack([q["q"] for q in qs]), torch.stack([q["scales"] for q in qs]),
+                torch.cat([q["tscale"] for q in qs]))
+
+    wgu = qexperts(data["wt_gate_up"])
+    wdn = qexperts(data["wt_down"])
+    prepared = args.comp_weights == "prepared" and nS > 0
+    if prepared:  # made once per expert weight set, like its quantization
+        wgu = wgu + (fq.grouped_comp_weights(fmt, wgu[0], wgu[1], cg),)
+        wdn = wdn + (fq.grouped_comp_weights(fmt, wdn[0], wdn[1], cd),)
+    torch.cuda.synchronize()
+    bufs = {}
+    for tag, (r, k) in {"gu": (rows, H), "dn": (rows, I)}.items():
+        bufs[tag] = dict(
+            q=torch.empty((r, k // 2), dtype=torch.uint8, device=dev),
+            s=torch.empty((r, k // blk), dtype=torch.uint8, device=dev),
+            t=torch.empty(G, dtype=torch.float32, device=dev),
+            r=torch.empty((r, nS), dtype=torch.int16, device=dev),
+            ws=torch.zeros(max(fq.quantize_workspace_bytes(fmt, r, k, G), 16),
+                           dtype=torch.uint8, device=dev))
+    ygu = torch.empty((rows, I2), dtype=torch.float32, device=dev)
+    ydn = torch.empty((rows, H), dtype=torch.float32, device=dev)
+
+    if moe_tok:
+        T = cfg["tokens"]
+        xt = up(data["x_tok"])
+        src = up(data["token_of_row"].astype(np.int32))
+        tq = torch.empty((T, H // 2), dtype=torch.uint8, device=dev)
+        tsc = torch.empty((T, H // blk), dtype=torch.uint8, device=dev)
+        tts = torch.empty(1, dtype=torch.float32, device=dev)
+        tws = torch.zeros(max(fq.quantize_workspace_bytes(fmt, T, H, 1), 16),
+                          dtype=torch.uint8, device=dev)
+
+    def quant():
+        if moe_tok:
+            b = bufs["gu"]
+            fq.quantize_into(fmt, fq.ROWMAJOR, xt, None, 1, None, 0, tq, tsc, tts, None, tws)
+            fq.permute_quantized_into(fmt, xt, tq, tsc, tts, src, off, G, cg, nS, b["q"],
+                                      b["s"], b["t"], b["r"])
+        for tag, xin, ch in ((("dn", xd, cd),) if moe_tok else
+                             (("gu", xg, cg), ("dn", xd, cd))):
+            b = bufs[tag]
+            fq.quantize_into(fmt, fq.ROWMAJOR, xin, off, G, ch, nS, b["q"], b["s"], b["t"],
+                             b["r"], b["ws"])
+
+    gws_bytes = max(fq.grouped_gemm_workspace_bytes(fmt, rows, I2, H, G, nS),
+                    fq.grouped_gemm_workspace_bytes(fmt, rows, H, I, G, nS))
+    gws = torch.empty(gws_bytes, dtype=torch.uint8, device=dev) if gws_bytes else None
+
+    def gemm(i):
+        for tag, w, y, n, k, ch in (("gu", wgu, ygu, I2, H, cg), ("dn", wdn, ydn, H, I, cd)):
+            b = bufs[tag]
+            if prepared:
+                fq.grouped_gemm_prepared_into(fmt, rows, n, k, off, G, b["q"], b["s"], b["t"],
+                                              w[0], w[1], w[2], ch, nS, b["r"], w[3], y, 0)
+            else:
+                fq.grouped_gemm_into(fmt, rows, n, k, off, G, b["q"], b["s"], b["t"], w[0],
+                                     w[1], w[2], ch, nS, b["r"], y, 0, gws)
+
+    loads = data["loads"]
+    active = int((loads > 0).sum())
+    s.quant, s.gemm = quant, gemm
+    s.fmt, s.x = fmt, None
+    s.flops = 2.0 * rows * (H * I2 + I * H)
+    # algorithmic bytes: activations (codes, scales, residual, channel lists),
+    # the active experts' packed weights, FP32 outputs, offsets and tensor scales
+    wb = active * (I2 * H // 2 + I2 * H // blk + H * I // 2 + H * I // blk)
+    s.gemm_bytes = (rows * (H + I) // 2 + rows * (H + I) // blk + 2 * rows * nS * 2 +
+                    2 * G * nS * 4 + wb + rows * (I2 + H) * 4 + 2 * (G + 1) * 4 + 4 * G * 4)
+    s.extra_bytes = (active * (fq.comp_weights_bytes(fmt, fq.ROWMAJOR, I2, H, nS) +
+                               fq.comp_weights_bytes(fmt, fq.ROWMAJOR, H, I, nS))
+                     if prepared else 0)
+    dn_bytes = rows * I * 2 + rows * I // 2 + rows * I // blk + rows * nS * 2 + G * 4
+    if moe_tok:
+        # tokens read and quantized once; codes read once and written per routed row;
+        # the residual gathers x and writes R
+        T = cfg["tokens"]
+        gu_bytes = (T * H * 2 + 2 * T * (H // 2 + H // blk) + rows * (H // 2 + H // blk) +
+                    rows * nS * 4 + G * 4 + 4)
+    else:
+        gu_bytes = rows * H * 2 + rows * H // 2 + rows * H // blk + rows * nS * 2 + G * 4
+    s.quant_bytes = gu_bytes + dn_bytes
+    s.select_bytes = None
+    s.mfma = False
+    s.wl = {"workload": name, "format": "nvfp4", "tokens": cfg["tokens"], "experts": G,
+            "top_k": cfg["top_k"], "hidden": H, "inter": I, "routed_rows": rows,
+            "n_s_per_expert": nS, "max_expert_rows": int(loads.max()),
+            "moe_quant": args.moe_quant,
+            "comp_weights": "prepared" if prepared else "inkernel",
+            "empty_experts": int((loads == 0).sum())}
+    s.keep = (wgu, wdn, bufs, ygu, ydn, gws, xg, xd, cg, cd, off)
+    return s
+
+
+def measure(name, args, stream, dev, variant_args=None):
+    """Build, warm up and time one workload; returns its record."""
+    import torch
+
+    import fp4_w4a4_quantized_amd as fq
+    from workloads import CONFIGS
+    a = variant_args or args
+    cfg = CONFIGS[name]
+    data = workload_data(name, cfg)
+    s = (build_moe if name == "moe_nvfp4" else build_dense)(name, cfg, data, a, dev)
 
     def step(i):
-        quant()
-        gemm(i)
+        s.quant()
+        s.gemm(i)
 
-    # ---- warmup (eager), then the K timed steps as one HIP graph ----------------
-    # Launching each kernel from Python costs more host time than the decode
-    # kernels take on the GPU, so the timed steps are captured once and
-    # replayed: the GPU then runs them back to back, as a serving loop does.
+    # warmup (eager), then the K timed steps as one HIP graph: launching each
+    # kernel from Python costs more host time than the decode kernels take on
+    # the GPU, so the timed steps are captured once and replayed back to back
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -380,118 +511,235 @@ def main():
         return g
 
     g_steps = capture(step, args.steps)
-    t_start = time.perf_counter()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record(stream)
     g_steps.replay()
     ev1.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
     step_ms = ev0.elapsed_time(ev1) / args.steps
-    print(f"[bench] {args.steps} steps: {step_ms * 1e3:.2f} us/step (wall {wall:.3f}s)",
-          file=sys.stderr, flush=True)
+    log(f"{name}: {args.steps} steps, {step_ms * 1e3:.2f} us/step")
     del g_steps
 
-    # ---- per-kernel averages: HIP events on the launch stream around a graph of
+    # per-kernel averages: HIP events on the launch stream around a graph of
     # `reps` launches of one kernel sequence
     def timed(fn, reps):
         g = capture(fn, reps)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
         g.replay()
-        b.record(stream)
+        e1.record(stream)
         torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps * 1e-3  # seconds
+        return e0.elapsed_time(e1) / reps * 1e-3  # seconds
 
     reps = max(args.steps, 20)
-    t_gemm = timed(gemm, reps)
-    t_quant = timed(lambda i: quant(), reps)
-    print(f"[bench] gemm {t_gemm * 1e6:.2f} us, quantize {t_quant * 1e6:.2f} us per launch",
-          file=sys.stderr, flush=True)
-    t_sel = timed(lambda i: select(), reps) if online else None
-    # the exact three-way error decomposition of the activations
+    t_gemm = timed(s.gemm, reps)
+    t_quant = timed(lambda i: s.quant(), reps)
+    log(f"{name}: gemm {t_gemm * 1e6:.2f} us, quantize {t_quant * 1e6:.2f} us per launch")
+    t_sel = timed(lambda i: s.select(), reps) if s.select else None
     t_dec = None
-    if name != "moe_nvfp4":
+    if s.x is not None:
         dec_out = torch.zeros(fq.binding.ERR_STATS_BYTES, dtype=torch.uint8, device=dev)
-        dec_ws = torch.empty(max(fq.error_decompose_workspace_bytes(M, K), 16), dtype=torch.uint8,
-                             device=dev)
-        t_dec = timed(lambda i: fq.error_decompose_into(fmt, x, dec_out, dec_ws), reps)
-        dec_bytes = M * K * 2
-        print(f"[bench] error decomposition {t_dec * 1e6:.2f} us per call", file=sys.stderr,
-              flush=True)
-    if online:
-        print(f"[bench] channel selection {t_sel * 1e6:.2f} us per call", file=sys.stderr,
-              flush=True)
+        dec_ws = torch.empty(max(fq.error_decompose_workspace_bytes(s.M, s.K), 16),
+                             dtype=torch.uint8, device=dev)
+        t_dec = timed(lambda i: fq.error_decompose_into(s.fmt, s.x, dec_out, dec_ws), reps)
+        log(f"{name}: error decomposition {t_dec * 1e6:.2f} us per call")
 
-    kh = src_hash()
-    default_variant = (args.layout == "tiled" and args.out_dtype == "f32" and
-                       args.residual == "bf16" and args.channels == "fixed" and
-                       args.comp_weights == "prepared" and args.moe_quant == "expert")
-    if name in ("prefill_nvfp4", "prefill_mxfp4"):
-        mfma_dtype = "f16" if fmt == fq.NVFP4 else "fp4"
+    default_variant = (a.layout == "tiled" and a.out_dtype == "f32" and a.residual == "bf16" and
+                       a.channels == "fixed" and a.comp_weights == "prepared" and
+                       a.moe_quant == "expert")
+    traffic = load_traffic(name, default_variant)
+    if s.mfma:
+        mfma_dtype = "f16" if s.fmt == fq.NVFP4 else "fp4"
         peak = MFMA_PEAK_TFLOPS[mfma_dtype]
-        ach = flops / t_gemm / 1e12
+        ach = s.flops / t_gemm / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(ach / peak, 4), "traffic": load_traffic(name, default_variant),
-                "mfma_dtype": mfma_dtype}
+                "frac": round(ach / peak, 4), "traffic": traffic, "mfma_dtype": mfma_dtype,
+                "peak_fp4": MFMA_PEAK_TFLOPS["fp4"],
+                "frac_fp4": round(ach / MFMA_PEAK_TFLOPS["fp4"], 4),
+                "algorithmic_bytes": s.gemm_bytes, "extra_bytes": s.extra_bytes}
     else:
-        ach = gemm_bytes / t_gemm / 1e9
+        ach = s.gemm_bytes / t_gemm / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": load_traffic(name, default_variant),
-                "algorithmic_bytes": gemm_bytes}
-    quant_gbs = quant_bytes / t_quant / 1e9
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "algorithmic_bytes": s.gemm_bytes, "extra_bytes": s.extra_bytes}
+    quant_gbs = s.quant_bytes / t_quant / 1e9
+    rec = {
+        "value": round(s.flops / (step_ms * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "ms_per_step": round(step_ms, 5),
+        "dtype": "f16" if s.fmt == fq.NVFP4 else "fp4",
+        "config": s.wl,
+        "gemm_us": round(t_gemm * 1e6, 3),
+        "gemm_tflops": round(s.flops / t_gemm / 1e12, 2),
+        "quantize_us": round(t_quant * 1e6, 3),
+        "quantize_gbps": round(quant_gbs, 1),
+        "quantize_frac_hbm": round(quant_gbs / HBM_PEAK_GBS, 4),
+        "quantize_bytes": s.quant_bytes,
+        "roofline": roof,
+    }
+    if t_dec is not None:
+        dec_bytes = s.M * s.K * 2
+        rec["decompose_us"] = round(t_dec * 1e6, 3)
+        rec["decompose_gbps"] = round(dec_bytes / t_dec / 1e9, 1)
+        rec["decompose_frac_hbm"] = round(dec_bytes / t_dec / 1e9 / HBM_PEAK_GBS, 4)
+    if t_sel is not None:
+        rec["select_us"] = round(t_sel * 1e6, 3)
+        rec["select_gbps"] = round(s.select_bytes / t_sel / 1e9, 1)
+    rec["_data"] = data
+    rec["_fmt"] = s.fmt
+    del s
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
 
-    # ---- CPU baseline: the oracle on this host --------------------------------
+
+def add_attainable(rec, peaks):
+    """Fractions of the measured attainable peaks next to the published ones."""
+    if not peaks:
+        return
+    r = rec["roofline"]
+    if r["bound"] == "mfma":
+        key = "mfma_f16_tflops" if r["mfma_dtype"] == "f16" else "mfma_fp4_tflops"
+    else:
+        key = "hbm_read_gbs"
+    r["attainable_peak"] = peaks[key]
+    r["frac_attainable"] = round(r["achieved"] / peaks[key], 4)
+    if "quantize_gbps" in rec:
+        rec["quantize_frac_attainable"] = round(rec["quantize_gbps"] / peaks["hbm_copy_gbs"], 4)
+
+
+def main():
+    args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is "
+              "single-GPU by design and multi-GPU sharding is not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import fp4_w4a4_quantized_amd as fq
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    fq.lib()   # fails loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    # an explicit stream (default priority) for all work and for the timing
+    # events.  Library calls take the current stream (no explicit argument):
+    # under graph capture that is the capture stream.
+    stream = torch.cuda.Stream(dev)
+    torch.cuda.set_stream(stream)
+
+    if args.decompose_only:
+        decompose_only(args, stream, dev)
+        return
+    peaks = None
+    if args.peaks_only or not args.no_peaks:
+        peaks = measure_peaks(stream)
+        log(f"attainable: {peaks}")
+        if args.peaks_only:
+            print(json.dumps({"attainable": peaks}), flush=True)
+            return
+
+    name = args.workload or HEADLINE
+    rec = measure(name, args, stream, dev)
+    add_attainable(rec, peaks)
+    extras = {}
+    if args.workload is None and not args.no_extras:
+        dflt = argparse.Namespace(**{**vars(args), "layout": "tiled", "out_dtype": "f32",
+                                     "residual": "bf16", "channels": "fixed",
+                                     "comp_weights": "prepared", "moe_quant": "expert"})
+        for n in EXTRAS:
+            e = measure(n, args, stream, dev, variant_args=dflt)
+            add_attainable(e, peaks)
+            e.pop("_data")
+            e.pop("_fmt")
+            extras[n] = e
+            if n == "moe_nvfp4":
+                _DATA.clear()
+
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(name, cfg, data, fmt, args.cpu_seconds,
-                           r4=name != "moe_nvfp4" and args.residual == "fp4", online=online,
+        cpu = cpu_baseline(name, rec["_data"], rec["_fmt"], args.cpu_seconds,
+                           r4=name != "moe_nvfp4" and args.residual == "fp4",
+                           online=args.channels == "online" and name != "moe_nvfp4",
                            moe_tok=name == "moe_nvfp4" and args.moe_quant == "token")
-
-    value = flops / (step_ms * 1e-3) / 1e12
+    rec.pop("_data")
+    rec.pop("_fmt")
     out = {
         "metric": METRIC,
-        "value": round(value, 3),
-        "unit": "TFLOP/s",
+        "value": rec.pop("value"),
+        "unit": rec.pop("unit"),
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(step_ms, 5),
+        "ms_per_step": rec.pop("ms_per_step"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16" if fmt == fq.NVFP4 else "fp4",
+        "dtype": rec.pop("dtype"),
         "data": "synthetic (seeded; no dataset or trained weights)",
-        "config": wl,
-        "quantize_gbps": round(quant_gbs, 1),
-        "quantize_frac_hbm": round(quant_gbs / HBM_PEAK_GBS, 4),
-        "quantize_bytes": quant_bytes,
-        "gemm_us": round(t_gemm * 1e6, 3),
-        "quantize_us": round(t_quant * 1e6, 3),
-        "roofline": roof,
-        "cpu_baseline": cpu,
-        "kernel_src_hash": kh,
+        "config": rec.pop("config"),
     }
-    if t_dec is not None:
-        out["decompose_us"] = round(t_dec * 1e6, 3)
-        out["decompose_gbps"] = round(dec_bytes / t_dec / 1e9, 1)
-        out["decompose_frac_hbm"] = round(dec_bytes / t_dec / 1e9 / HBM_PEAK_GBS, 4)
-    if online:
-        out["select_us"] = round(t_sel * 1e6, 3)
-        out["select_gbps"] = round(select_bytes / t_sel / 1e9, 1)
+    out.update(rec)
+    out["cpu_baseline"] = cpu
+    if peaks:
+        out["attainable"] = peaks
+    if extras:
+        out["extra_workloads"] = extras
+    out["kernel_src_hash"] = src_hash()
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(name, cfg, data, fmt, target_s, r4=False, online=False, moe_tok=False):
+def decompose_only(args, stream, dev):
+    """Five calls of the error decomposition of the prefill activations
+    (8192 x 4096) in one format: the command the decomposition's counter
+    profile is taken with."""
+    import numpy as np
+    import torch
+
+    import fp4_w4a4_quantized_amd as fq
+    from workloads import CONFIGS
+    name = "prefill_nvfp4" if args.decompose_only == "nvfp4" else "prefill_mxfp4"
+    cfg = CONFIGS[name]
+    data = workload_data(name, cfg)
+    x = torch.from_numpy(np.ascontiguousarray(data["x"]).view(np.int16)).to(dev)
+    fmt = fq.NVFP4 if args.decompose_only == "nvfp4" else fq.MXFP4
+    M, K = x.shape
+    out = torch.zeros(fq.binding.ERR_STATS_BYTES, dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(fq.error_decompose_workspace_bytes(M, K), 16), dtype=torch.uint8,
+                     device=dev)
+    for _ in range(5):
+        fq.error_decompose_into(fmt, x, out, ws)
+    torch.cuda.synchronize()
+    print(json.dumps({"decompose": name, "calls": 5}), flush=True)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(name, data, fmt, target_s, r4=False, online=False, moe_tok=False):
     """Time the oracle (as it is) on the host: quantize the activations (with
     online channels, then choose them; with the FP4 residual, quantize the
-    residual a second time), then the FP64 GEMM on
-    a bounded sample of outputs, scaled to TFLOP/s."""
+    residual a second time), then the FP64 GEMM on a bounded sample of
+    outputs, scaled to TFLOP/s.  Also the quantizer on one thread over the
+    first rows, the CPU model and the inputs' SHA-256."""
     import numpy as np
 
     from oracle import oracle as orc
+    from workloads import CONFIGS
 
-    cores = int(os.environ.get("OMP_NUM_THREADS") or len(os.sched_getaffinity(0)))
+    cfg = CONFIGS[name]
+    cores = orc.max_threads()
     if name == "moe_nvfp4":
         x, chan, off = data["x_perm"], data["chan_gate_up"], data["offsets"]
         K = cfg["hidden"]
@@ -508,6 +756,16 @@ def cpu_baseline(name, cfg, data, fmt, target_s, r4=False, online=False, moe_tok
     else:
         qa = orc.quantize(fmt, x, offsets=off, chan_idx=chan if chan.size else None)
     t_q = time.perf_counter() - t0
+    # the quantizer on one thread, over at most 1024 rows (one group)
+    rows1 = min(x.shape[0], 1024)
+    orc.set_num_threads(1)
+    try:
+        t0 = time.perf_counter()
+        orc.quantize(fmt, x[:rows1],
+                     chan_idx=(chan if off is None else chan[0]) if chan.size else None)
+        t_q1 = time.perf_counter() - t0
+    finally:
+        orc.set_num_threads(cores)
     # weights for the sample: the first rows of W^T (first expert for MoE)
     wt = data["wt_gate_up"][0] if name == "moe_nvfp4" else data["wt"]
     n_cols = min(wt.shape[0], 256)
@@ -547,12 +805,17 @@ def cpu_baseline(name, cfg, data, fmt, target_s, r4=False, online=False, moe_tok
     else:
         prep = "oracle quantization of the full activation tensor"
     sample_flops = 2.0 * npts * K
-    gflops_rate = sample_flops / t_g
-    return {"value": round(gflops_rate / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+    q_bytes = x.shape[0] * x.shape[1] * 2
+    return {"value": round(sample_flops / t_g / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle",
             "sample": f"oracle FP64 GEMM on {npts} sampled outputs of the {name} workload "
                       f"(K={K}, {t_g:.1f}s) after {prep} ({t_q:.2f}s)",
-            "quantize_s": round(t_q, 4)}
+            "quantize_s": round(t_q, 4),
+            "quantize_gbps": round(q_bytes / t_q / 1e9, 3),
+            "quantize_1thread_s": round(t_q1, 4),
+            "quantize_1thread_sample": f"first {rows1} rows x {x.shape[1]} columns, one group",
+            "cpu_model": cpu_model(),
+            "input_sha256": input_sha256(name, data)}
 
 
 if __name__ == "__main__":

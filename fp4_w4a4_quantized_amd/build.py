@@ -13,6 +13,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfp4q.so")
 SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "gemm_big.hip", "gemm_skinny.hip", "decompose.hip", "select.hip", "permute.hip"]
+# the peak microbenchmarks (measurement only) go into a library of their own
+PEAKS_LIB = os.path.join(HERE, "libfp4q_peaks.so")
+PEAKS_SOURCES = ["peaks.hip"]
 ARCH = "gfx950"
 
 
@@ -35,17 +38,23 @@ def flags() -> list[str]:
     ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every kernel source into libfp4q.so; returns its path."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *flags(), "-o", tmp, *[os.path.join(CSRC, s) for s in SOURCES]]
+def _link(out: str, sources: list[str], verbose: bool) -> str:
+    tmp = out + ".tmp"
+    cmd = [hipcc(), *flags(), "-o", tmp, *[os.path.join(CSRC, s) for s in sources]]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
     if verbose and res.stderr:
         print(res.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every kernel source into libfp4q.so (and the peak
+    microbenchmarks into libfp4q_peaks.so); returns libfp4q.so's path."""
+    _link(PEAKS_LIB, PEAKS_SOURCES, verbose)
+    return _link(LIB, SOURCES, verbose)
 
 
 if __name__ == "__main__":

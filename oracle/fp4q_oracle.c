@@ -61,12 +61,18 @@
  * round-to-nearest-even; build with -O2 -ffp-contract=off, no fast-math.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
 #define ORC_NVFP4 0
 #define ORC_MXFP4 1
+
+/* Thread count of the parallel loops (timing of the CPU baseline only; no
+ * result depends on it). */
+void orc_set_num_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+int orc_max_threads(void) { return omp_get_max_threads(); }
 
 /* ------------------------------------------------------------------------ */
 /* Number formats                                                            */

@@ -59,6 +59,10 @@ def lib():
         L = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         i64, i32, f32 = ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+        L.orc_set_num_threads.restype = None
+        L.orc_set_num_threads.argtypes = [ctypes.c_int]
+        L.orc_max_threads.restype = ctypes.c_int
+        L.orc_max_threads.argtypes = []
         L.orc_e2m1_value.restype = ctypes.c_double
         L.orc_e2m1_value.argtypes = [ctypes.c_uint8]
         L.orc_e2m1_encode_mag.restype = ctypes.c_uint8
@@ -116,6 +120,16 @@ def _p(a):
 
 def _c(a, dtype):
     return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+# ---- threads (timing only: no result depends on the count) ----------------
+
+def set_num_threads(n: int) -> None:
+    lib().orc_set_num_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(lib().orc_max_threads())
 
 
 # ---- scalar codecs (exposed for the pins) --------------------------------

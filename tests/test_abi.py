@@ -13,10 +13,10 @@ HEADER = os.path.join(ROOT, "include", "fp4q.h")
 INVALID, UNSUPPORTED, WORKSPACE = -1, -2, -3
 
 
-def declared_functions():
-    src = open(HEADER).read()
+def declared_functions(header=HEADER):
+    src = open(header).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(fp4q_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(fp4q_[a-z_0-9]+)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")
@@ -30,6 +30,32 @@ def test_exports_every_declared_symbol(L):
     assert {"fp4q_quantize", "fp4q_gemm", "fp4q_grouped_gemm", "fp4q_error_decompose"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
+
+
+def test_peaks_library_exports_and_rejects():
+    """libfp4q_peaks.so (the attainable-peak microbenchmarks) exports what
+    include/fp4q_peaks.h declares and rejects bad arguments on the host."""
+    path = os.path.join(ROOT, "fp4_w4a4_quantized_amd", "libfp4q_peaks.so")
+    P = ctypes.CDLL(path)
+    names = declared_functions(os.path.join(ROOT, "include", "fp4q_peaks.h"))
+    assert {"fp4q_peak_mfma", "fp4q_peak_read", "fp4q_peak_copy"} <= set(names)
+    for n in names:
+        assert hasattr(P, n), n
+    P.fp4q_peak_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                 ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
+    P.fp4q_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int32,
+                                 ctypes.c_void_p, ctypes.c_void_p]
+    P.fp4q_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
+                                 ctypes.c_int32, ctypes.c_void_p]
+    P.fp4q_peak_mfma_out_floats.restype = ctypes.c_int64
+    fl = ctypes.c_double()
+    assert P.fp4q_peak_mfma(2, 4, 1, A, ctypes.byref(fl), None) == -1      # bad kind
+    assert P.fp4q_peak_mfma(0, 0, 1, A, ctypes.byref(fl), None) == -1      # no blocks
+    assert P.fp4q_peak_mfma(0, 4, 1, None, ctypes.byref(fl), None) == -1   # no output
+    assert P.fp4q_peak_read(A, 15, 4, B, None) == -1                       # not 16-byte units
+    assert P.fp4q_peak_read(ctypes.c_void_p(0x10008), 64, 4, B, None) == -1  # misaligned
+    assert P.fp4q_peak_copy(A, B, 64, 0, None) == -1
+    assert P.fp4q_peak_mfma_out_floats(4) == 4 * 256
 
 
 def test_status_strings(L):
