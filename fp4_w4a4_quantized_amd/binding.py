@@ -43,6 +43,7 @@ class ErrStats(ctypes.Structure):
         ("n_elems", ctypes.c_int64),
         ("n_deadzone", ctypes.c_int64),
         ("n_clipped", ctypes.c_int64),
+        ("flags", ctypes.c_int64),
     ]
 
 
@@ -114,6 +115,10 @@ def lib():
         L.fp4q_permute_quantized.restype = ctypes.c_int
         L.fp4q_permute_quantized.argtypes = [ctypes.c_int, P, i64, i64, i64, P, P, P, P, i64, P,
                                              i32, P, i32, P, P, P, P, P]
+        L.fp4q_quantize_status.restype = ctypes.c_int
+        L.fp4q_quantize_status.argtypes = [P, sz, ctypes.POINTER(i32), P]
+        L.fp4q_test_hook.restype = ctypes.c_int
+        L.fp4q_test_hook.argtypes = [i32, i64]
         L.fp4q_error_decompose_workspace_bytes.restype = sz
         L.fp4q_error_decompose_workspace_bytes.argtypes = [i64, i64]
         L.fp4q_error_decompose.restype = ctypes.c_int
@@ -293,6 +298,29 @@ def error_decompose_into(fmt, x, out, workspace, stream=None):
     rc = lib().fp4q_error_decompose(fmt, _ptr(x), rows, cols, x.stride(0), _ptr(out),
                                     _ptr(workspace), ws_bytes, _stream(stream))
     _check("fp4q_error_decompose", rc)
+
+
+QSTATUS_GRID_EXPIRED = 1
+HOOK_RESET = 0
+HOOK_FAIL_NEXT_LAUNCH = 1
+HOOK_GRID_SPIN_LIMIT = 2
+HOOK_GRID_SKIP_SLOT = 3
+DEC_INEXACT = 1
+
+
+def quantize_status(workspace, stream=None) -> int:
+    """Status word of an NVFP4 quantize workspace (waits for the stream,
+    then reads and clears it); 0 = every call found its tensor maximum."""
+    st = ctypes.c_int32(0)
+    _check("fp4q_quantize_status",
+           lib().fp4q_quantize_status(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      ctypes.byref(st), _stream(stream)))
+    return st.value
+
+
+def test_hook(hook: int, value: int = 0) -> None:
+    """Failure-injection hooks for tests (fp4q_test_hook)."""
+    _check("fp4q_test_hook", lib().fp4q_test_hook(hook, value))
 
 
 # ---- allocating conveniences ---------------------------------------------
@@ -479,4 +507,5 @@ def error_decompose(fmt, x, stream=None):
         "n_elems": st.n_elems,
         "n_deadzone": st.n_deadzone,
         "n_clipped": st.n_clipped,
+        "flags": st.flags,
     }

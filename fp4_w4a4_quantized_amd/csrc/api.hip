@@ -5,11 +5,25 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "fp4q_internal.h"
 
 namespace {
 
 thread_local int g_last_hip_error = 0;
+
+// FP4Q_HOOK_FAIL_NEXT_LAUNCH: a hipError_t that the next call which would
+// launch reports instead of launching (0: none).
+std::atomic<int> g_fail_next{0};
+
+// True (and the hook consumed) when a test asked the launch path to fail.
+inline bool injected_failure() {
+  const int e = g_fail_next.exchange(0);
+  if (e == 0) return false;
+  g_last_hip_error = e;
+  return true;
+}
 
 inline bool aligned(const void* p, uintptr_t a) {
   return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
@@ -101,13 +115,55 @@ int fp4q_quantize(fp4q_format_t fmt, fp4q_layout_t layout, const uint16_t* x, in
   const int64_t prow = layout == FP4Q_LAYOUT_TILED ? (rows + 15) / 16 * 16 : rows;
   if (prow * (cols / 8) >= ((int64_t)1 << 31)) return FP4Q_ERR_UNSUPPORTED;  // 32-bit chunk index
   const size_t need = fp4q_quantize_workspace_bytes(fmt, rows, cols, num_groups);
-  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 4)))
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 8)))
     return FP4Q_ERR_WORKSPACE;
+  if (injected_failure()) return FP4Q_ERR_HIP;
   clear_error();
   fp4q::launch_quantize(fmt, layout == FP4Q_LAYOUT_TILED, x, rows, cols, ldx, group_offsets,
                         num_groups, chan_idx, n_chan, q, scales, tensor_scale, resid, workspace,
                         static_cast<hipStream_t>(stream));
   return check_launch();
+}
+
+int fp4q_quantize_status(const void* workspace, size_t workspace_bytes, int32_t* status,
+                         void* stream) {
+  if (!status) return FP4Q_ERR_INVALID;
+  if (!workspace || !aligned(workspace, 8) ||
+      workspace_bytes < fp4q_quantize_workspace_bytes(FP4Q_NVFP4, 0, 16, 1))
+    return FP4Q_ERR_WORKSPACE;
+  if (injected_failure()) return FP4Q_ERR_HIP;
+  clear_error();
+  uint32_t v = 0;
+  if (fp4q::quantize_status(workspace, static_cast<hipStream_t>(stream), &v) != 0) {
+    const hipError_t e = hipGetLastError();
+    g_last_hip_error = e != hipSuccess ? (int)e : (int)hipErrorUnknown;
+    return FP4Q_ERR_HIP;
+  }
+  *status = (int32_t)v;
+  return FP4Q_OK;
+}
+
+int fp4q_test_hook(int32_t hook, int64_t value) {
+  switch (hook) {
+    case FP4Q_HOOK_RESET:
+      g_fail_next.store(0);
+      fp4q::set_grid_hooks(0, -1);
+      return FP4Q_OK;
+    case FP4Q_HOOK_FAIL_NEXT_LAUNCH:
+      if (value <= 0 || value > INT32_MAX) return FP4Q_ERR_INVALID;
+      g_fail_next.store((int)value);
+      return FP4Q_OK;
+    case FP4Q_HOOK_GRID_SPIN_LIMIT:
+      if (value < 0 || value > UINT32_MAX) return FP4Q_ERR_INVALID;
+      fp4q::set_grid_hooks((uint32_t)value, fp4q::grid_hook_skip());
+      return FP4Q_OK;
+    case FP4Q_HOOK_GRID_SKIP_SLOT:
+      if (value < -1 || value > 1 << 20) return FP4Q_ERR_INVALID;
+      fp4q::set_grid_hooks(fp4q::grid_hook_spin(), (int)value);
+      return FP4Q_OK;
+    default:
+      return FP4Q_ERR_INVALID;
+  }
 }
 
 static int validate_gemm_common(int fmt, int64_t N, int64_t K, const uint8_t* a_q,
@@ -155,6 +211,7 @@ int fp4q_gemm(fp4q_format_t fmt, fp4q_layout_t layout, int64_t M, int64_t N, int
   const size_t need = fp4q_gemm_workspace_bytes(fmt, layout, M, N, K, n_chan);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
     return FP4Q_ERR_WORKSPACE;
+  if (injected_failure()) return FP4Q_ERR_HIP;
   clear_error();
   fp4q::launch_gemm(fmt, layout == FP4Q_LAYOUT_TILED, M, N, K, nullptr, 1, a_q, a_s, a_ts, b_q,
                     b_s, b_ts, chan_idx, n_chan, resid, nullptr, y, y_dtype == FP4Q_OUT_BF16, ldy,
@@ -182,6 +239,7 @@ int fp4q_comp_weights(fp4q_format_t fmt, fp4q_layout_t layout, int64_t N, int64_
   if (out_bytes < fp4q_comp_weights_bytes(fmt, layout, N, K, n_chan)) return FP4Q_ERR_WORKSPACE;
   if (((N + 15) / 16) * ((n_chan + 31) / 32) / 4 >= (int64_t)UINT32_MAX)
     return FP4Q_ERR_UNSUPPORTED;
+  if (injected_failure()) return FP4Q_ERR_HIP;
   clear_error();
   fp4q::launch_comp_weights(fmt, layout == FP4Q_LAYOUT_TILED, b_q, b_s, N, K, chan_idx, n_chan, 1,
                             out, static_cast<hipStream_t>(stream));
@@ -207,6 +265,7 @@ int fp4q_gemm_prepared(fp4q_format_t fmt, fp4q_layout_t layout, int64_t M, int64
   // shapes whose kernels stream no compensation weights take the term from
   // chan_idx as fp4q_gemm does (they need no workspace)
   if (fp4q::gemm_path(M, N, K, n_chan) == fp4q::PATH_GENERIC) comp_w = nullptr;
+  if (injected_failure()) return FP4Q_ERR_HIP;
   clear_error();
   fp4q::launch_gemm(fmt, layout == FP4Q_LAYOUT_TILED, M, N, K, nullptr, 1, a_q, a_s, a_ts, b_q,
                     b_s, b_ts, chan_idx, n_chan, resid, nullptr, y, y_dtype == FP4Q_OUT_BF16, ldy,
@@ -253,6 +312,7 @@ int fp4q_gemm_residual_fp4(fp4q_format_t fmt, fp4q_layout_t layout, int64_t M, i
   if (ldy < N) return FP4Q_ERR_INVALID;
   if ((M + 127) / 128 > (int64_t)UINT32_MAX || (N + 31) / 32 > 65535) return FP4Q_ERR_UNSUPPORTED;
   if (M * (int64_t)n_chan / 8 >= ((int64_t)1 << 31)) return FP4Q_ERR_UNSUPPORTED;
+  if (injected_failure()) return FP4Q_ERR_HIP;
   clear_error();
   void* gws = work ? static_cast<uint8_t*>(workspace) + deq_resid_bytes(M, n_chan) : nullptr;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -286,6 +346,7 @@ int fp4q_grouped_gemm(fp4q_format_t fmt, int64_t total_rows, int64_t N, int64_t 
       fp4q_grouped_gemm_workspace_bytes(fmt, total_rows, N, K, num_groups, n_chan);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
     return FP4Q_ERR_WORKSPACE;
+  if (injected_failure()) return FP4Q_ERR_HIP;
   clear_error();
   fp4q::launch_gemm(fmt, false, total_rows, N, K, group_offsets, num_groups, a_q, a_s, a_ts, b_q,
                     b_s, b_ts, chan_idx, n_chan, resid, nullptr, y, y_dtype == FP4Q_OUT_BF16, N,
@@ -315,6 +376,7 @@ int fp4q_grouped_comp_weights(fp4q_format_t fmt, int64_t N, int64_t K, int32_t n
     return FP4Q_ERR_WORKSPACE;
   if ((int64_t)num_groups * ((N + 15) / 16) * ((n_chan + 31) / 32) / 4 >= (int64_t)UINT32_MAX)
     return FP4Q_ERR_UNSUPPORTED;
+  if (injected_failure()) return FP4Q_ERR_HIP;
   clear_error();
   fp4q::launch_comp_weights(fmt, false, b_q, b_s, N, K, chan_idx, n_chan, num_groups, out,
                             static_cast<hipStream_t>(stream));
@@ -340,6 +402,7 @@ int fp4q_grouped_gemm_prepared(fp4q_format_t fmt, int64_t total_rows, int64_t N,
     return FP4Q_ERR_WORKSPACE;
   // shapes served by the general grouped kernel take the term from chan_idx
   if (!fp4q::big_grouped_eligible(N, K, n_chan)) comp_w = nullptr;
+  if (injected_failure()) return FP4Q_ERR_HIP;
   clear_error();
   fp4q::launch_gemm(fmt, false, total_rows, N, K, group_offsets, num_groups, a_q, a_s, a_ts, b_q,
                     b_s, b_ts, chan_idx, n_chan, resid, nullptr, y, y_dtype == FP4Q_OUT_BF16, N,
@@ -371,6 +434,7 @@ int fp4q_select_channels(fp4q_format_t fmt, fp4q_layout_t layout, const uint16_t
   if (k == 0) return FP4Q_OK;
   const size_t need = fp4q::select_workspace_bytes(rows, cols);
   if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return FP4Q_ERR_WORKSPACE;
+  if (injected_failure()) return FP4Q_ERR_HIP;
   clear_error();
   fp4q::launch_select(fmt, layout == FP4Q_LAYOUT_TILED, x, rows, cols, ldx, q, scales,
                       tensor_scale, k, chan_out, resid_out, workspace,
@@ -400,6 +464,7 @@ int fp4q_permute_quantized(fp4q_format_t fmt, const uint16_t* x, int64_t tokens,
   if (rows >= ((int64_t)1 << 31) || cols >= ((int64_t)1 << 30) || num_groups > MAX_GROUPS)
     return FP4Q_ERR_UNSUPPORTED;
   if (rows == 0 && fmt == FP4Q_MXFP4) return FP4Q_OK;  // no rows and no tensor scales to copy
+  if (injected_failure()) return FP4Q_ERR_HIP;
   clear_error();
   fp4q::launch_permute(fmt, x, ldx, tokens, cols, q, scales, tensor_scale, row_src, rows,
                        group_offsets, num_groups, chan_idx, n_chan, q_out, scales_out,
@@ -422,6 +487,7 @@ int fp4q_error_decompose(fp4q_format_t fmt, const uint16_t* x, int64_t rows, int
   if (rows > 0 && (!x || !aligned(x, 16))) return FP4Q_ERR_INVALID;
   const size_t need = fp4q::decompose_workspace_bytes(rows, cols);
   if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return FP4Q_ERR_WORKSPACE;
+  if (injected_failure()) return FP4Q_ERR_HIP;
   clear_error();
   fp4q::launch_decompose(fmt, x, rows, cols, ldx, out, workspace,
                          static_cast<hipStream_t>(stream));

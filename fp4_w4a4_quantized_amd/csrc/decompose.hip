@@ -409,13 +409,24 @@ __device__ double fix_to_double(const uint64_t (&a)[5]) {
   return neg ? -r : r;
 }
 
+// amax_part / namax: the NVFP4 path's per-workgroup amax words (BF16
+// magnitude patterns), or null / 0 for MXFP4.  A tensor amax in (0, 2^-89)
+// (patterns below 0x1300) lets terms fall below the fixed point's LSB: the
+// sums are then flagged FP4Q_DEC_INEXACT.
 __global__ void __launch_bounds__(DEC_THREADS) k_decompose_final(const DecPartial* __restrict__ part,
                                                                  int nparts, int64_t n_elems,
+                                                                 const uint32_t* __restrict__ amax_part,
+                                                                 int namax,
                                                                  fp4q_err_stats_t* __restrict__ out) {
   __shared__ uint64_t sfix[DEC_THREADS][4][5];
   __shared__ double ssq[DEC_THREADS][5];
   __shared__ int64_t scnt[DEC_THREADS][2];
+  __shared__ uint32_t samax[DEC_THREADS / 64];
   const int t = threadIdx.x;
+  uint32_t am = 0;
+  for (int p = t; p < namax; p += DEC_THREADS) am = max(am, amax_part[p]);
+  for (int o = 32; o > 0; o >>= 1) am = max(am, (uint32_t)__shfl_xor((int)am, o));
+  if ((t & 63) == 0) samax[t >> 6] = am;
   uint64_t fix[4][5];
   double sq[5] = {0, 0, 0, 0, 0};
   int64_t cnt[2] = {0, 0};
@@ -474,6 +485,9 @@ __global__ void __launch_bounds__(DEC_THREADS) k_decompose_final(const DecPartia
     out->n_elems = n_elems;
     out->n_deadzone = scnt[0][0];
     out->n_clipped = scnt[0][1];
+    uint32_t m = 0;
+    for (int i = 0; i < DEC_THREADS / 64; ++i) m = max(m, samax[i]);
+    out->flags = (m != 0u && m < 0x1300u) ? (int64_t)FP4Q_DEC_INEXACT : 0;
   }
 }
 
@@ -503,14 +517,14 @@ int launch_decompose(int fmt, const uint16_t* x, int64_t rows, int64_t cols, int
     hipLaunchKernelGGL(k_decompose<FP4Q_NVFP4>, dim3((unsigned)g), dim3(DEC_THREADS), 0, stream,
                        x, rows, cols, ldx, amax, (int)g, part);
     hipLaunchKernelGGL(k_decompose_final, dim3(1), dim3(DEC_THREADS), 0, stream, part, (int)g,
-                       rows * cols, out);
+                       rows * cols, amax, (int)g, out);
     return 0;
   }
   const int64_t g = dec_grid(rows, cols, 32);
   hipLaunchKernelGGL(k_decompose<FP4Q_MXFP4>, dim3((unsigned)g), dim3(DEC_THREADS), 0, stream, x,
                      rows, cols, ldx, nullptr, 0, part);
   hipLaunchKernelGGL(k_decompose_final, dim3(1), dim3(DEC_THREADS), 0, stream, part, (int)g,
-                     rows * cols, out);
+                     rows * cols, nullptr, 0, out);
   return 0;
 }
 

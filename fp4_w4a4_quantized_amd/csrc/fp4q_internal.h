@@ -17,6 +17,16 @@ int launch_quantize(int fmt, bool tiled, const uint16_t* x, int64_t rows, int64_
 
 size_t quantize_workspace_bytes(int fmt, int G);
 
+// Status word of a quantize workspace (bit 0: the small-tensor exchange ran
+// out of spins); waits for the stream, then reads and clears it.
+int quantize_status(const void* ws, hipStream_t stream, uint32_t* status);
+
+// Test hooks of the small-tensor exchange: spin limit (0: default) and a
+// workgroup that skips its slot store (-1: none).
+void set_grid_hooks(uint32_t spin, int skip);
+uint32_t grid_hook_spin();
+int grid_hook_skip();
+
 // Dense GEMM kernel choice (a function of the shape only, so that the
 // workspace query and the launch agree).
 enum GemmPath { PATH_GENERIC = 0, PATH_SKINNY = 1, PATH_BIG = 2 };

@@ -30,6 +30,8 @@
 //    order-free for non-negative values) after a fill kernel clears the
 //    words.
 // MXFP4 is a single pass.
+#include <atomic>
+
 #include "fp4q_device.h"
 #include "fp4q_internal.h"
 
@@ -207,25 +209,53 @@ __global__ void __launch_bounds__(QT) k_group_amax(ChunkGrid gr, int64_t rows,
 }
 
 // Tensor maximum across the workgroups of one launch (the small-tensor NVFP4
-// path), through per-device state that is zero at module load: a launch
-// counter and one slot per workgroup.  Every access is an atomic at agent
-// scope, performed where all XCDs see it, and no release fence is needed
-// (one would write back the per-XCD L2).  A launch tags its slots with
-// (counter + 1) mod 2^16 in the high half of the word: each workgroup
-// stores its maximum under the tag in its own slot (workgroup 0 also stores
-// the tag with a zero maximum in the slots past the grid, so every slot
-// always carries the previous launch's tag, never the current one, before
-// it is written), then the first wave loads the launch's slots, lane i slot
-// i, until all carry the tag, and takes their maximum: one store and one
-// load on the critical path.  Workgroup 0 then advances the counter; every
-// workgroup has read it by then (their slots carry the tag derived from
-// it).  Spins are bounded.  Every workgroup of the launch is resident at
-// once (at most 32 workgroups of 512 threads), and one such launch runs at
-// a time on a device.
+// path), through state kept at the front of the caller's workspace (zero
+// before its first use): a launch counter, a status word and one 64-bit
+// slot per workgroup.  Every access is an atomic at agent scope, performed
+// where all XCDs see it, and no release fence is needed (one would write
+// back the per-XCD L2).  A launch tags its slots with counter + 1 in the
+// high 32 bits: each workgroup stores its maximum under the tag in its own
+// slot (workgroup 0 also stores the tag with a zero maximum in the slots
+// past the grid, so every slot always carries an earlier launch's tag,
+// never the current one, before it is written), then the first wave loads
+// the launch's slots, lane i slot i, until all carry the tag, and takes
+// their maximum: one store and one load on the critical path.  Workgroup 0
+// then advances the counter; every workgroup has read it by then (their
+// slots carry the tag derived from it).  Every workgroup of the launch is
+// resident at once (at most 32 workgroups of 512 threads).  Calls with
+// different workspaces are independent; calls that share one must not
+// overlap.
+//
+// The spins are bounded.  A workgroup whose spin runs out has no valid
+// tensor maximum: it sets bit 0 of the status word and poisons what it
+// writes (E4M3 NaN block scales, BF16 NaN residuals, and a NaN tensor scale
+// from workgroup 0), so a GEMM on the result gives NaN instead of a silent
+// wrong value; fp4q_quantize_status() reads and clears the word.
 constexpr uint32_t GRID_SPIN_LIMIT = 1u << 22;
 constexpr uint32_t GRID_SLOTS = 32;
-static __device__ uint32_t g_grid_count;
-static __device__ uint32_t g_grid_slot[GRID_SLOTS];
+constexpr int WS_STATUS = 1;           // u32 index of the status word
+constexpr int WS_SLOT_BYTES = 256;     // byte offset of the slots
+constexpr size_t WS_HEADER = 512;      // bytes before the amax words
+constexpr uint32_t STATUS_GRID_EXPIRED = 1u;
+
+// Test controls of the exchange (kernel arguments): the spin limit, and a
+// workgroup that skips its slot store (-1: none).
+struct GridCtl {
+  uint32_t* state;   // workspace front: [0] counter, [1] status, slots at byte 256
+  uint32_t spin;
+  int skip;
+};
+
+// Host-side test hooks (fp4q_test_hook); zero / -1 in normal operation.
+static std::atomic<uint32_t> g_hook_spin{0};
+static std::atomic<int> g_hook_skip{-1};
+
+void set_grid_hooks(uint32_t spin, int skip) {
+  g_hook_spin.store(spin);
+  g_hook_skip.store(skip);
+}
+uint32_t grid_hook_spin() { return g_hook_spin.load(); }
+int grid_hook_skip() { return g_hook_skip.load(); }
 
 // Opaque copy of `v` that can only be formed once `dep` is available.
 __device__ __forceinline__ uint32_t after(uint32_t v, uint32_t dep) {
@@ -234,33 +264,45 @@ __device__ __forceinline__ uint32_t after(uint32_t v, uint32_t dep) {
 }
 
 // The launch counter; read early, before the chunk loads are used.
-__device__ __forceinline__ uint32_t grid_gen() {
-  return __hip_atomic_load(&g_grid_count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ uint32_t grid_gen(const GridCtl& gc) {
+  return __hip_atomic_load(gc.state, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Called by all 64 lanes of the first wave of every workgroup with the
 // workgroup's maximum (a BF16 magnitude pattern, below 2^15) and the
-// counter; returns the launch's maximum in every lane.
-__device__ __forceinline__ uint32_t grid_max(uint32_t m, uint32_t nwg, uint32_t gen) {
+// counter; returns the launch's maximum in every lane, and in `expired`
+// whether any of this workgroup's spins ran out.
+__device__ __forceinline__ uint32_t grid_max(uint32_t m, uint32_t nwg, uint32_t gen,
+                                             const GridCtl& gc, bool& expired) {
   const int lane = threadIdx.x & 63;
-  const uint32_t tag = ((gen + 1u) & 0xFFFFu) << 16;
-  if (lane == 0)
-    __hip_atomic_store(&g_grid_slot[blockIdx.x], tag | m, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+  uint64_t* slot = reinterpret_cast<uint64_t*>(reinterpret_cast<uint8_t*>(gc.state) +
+                                               WS_SLOT_BYTES);
+  const uint32_t tag = gen + 1u;
+  const uint64_t tagw = (uint64_t)tag << 32;
+  if (lane == 0 && (int)blockIdx.x != gc.skip)
+    __hip_atomic_store(&slot[blockIdx.x], tagw | m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (blockIdx.x == 0 && (uint32_t)lane >= nwg && (uint32_t)lane < GRID_SLOTS)
-    __hip_atomic_store(&g_grid_slot[lane], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  uint32_t v = tag;
+    __hip_atomic_store(&slot[lane], tagw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  uint64_t v = tagw;
+  bool ok = true;
   if ((uint32_t)lane < nwg) {
-    for (uint32_t i = 0; i < GRID_SPIN_LIMIT; ++i) {
-      v = __hip_atomic_load(&g_grid_slot[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if ((v & 0xFFFF0000u) == tag) break;
+    ok = false;
+    for (uint32_t i = 0; i < gc.spin; ++i) {
+      v = __hip_atomic_load(&slot[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((uint32_t)(v >> 32) == tag) {
+        ok = true;
+        break;
+      }
     }
   }
-  uint32_t r = v & 0x7FFFu;
+  uint32_t r = ok ? (uint32_t)v & 0x7FFFu : 0u;
   for (int s = 32; s > 0; s >>= 1) r = max(r, (uint32_t)__shfl_xor((int)r, s));
+  expired = __ballot(!ok) != 0;
+  if (expired && lane == 0)
+    __hip_atomic_fetch_or(gc.state + WS_STATUS, STATUS_GRID_EXPIRED, __ATOMIC_RELAXED,
+                          __HIP_MEMORY_SCOPE_AGENT);
   if (blockIdx.x == 0 && lane == 0)
-    __hip_atomic_store(&g_grid_count, after(gen + 1u, r), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(gc.state, after(gen + 1u, r), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return r;
 }
 
@@ -314,8 +356,8 @@ __device__ __forceinline__ uint32_t chan_entry_search(const int32_t* __restrict_
 // Quantize chunk cc of row `row` held in v.  All lanes of the wave call this
 // (the block max moves between lanes); `active` gates the stores.
 template <int FMT>
-__device__ __forceinline__ void quantize_chunk(u32x4 v, bool active, bool tiled, int64_t row,
-                                               int64_t cc, int64_t cols, float t,
+__device__ __forceinline__ void quantize_chunk(u32x4 v, bool active, bool poison, bool tiled,
+                                               int64_t row, int64_t cc, int64_t cols, float t,
                                                uint32_t chan_ent, int nS,
                                                uint8_t* __restrict__ q, uint8_t* __restrict__ scales,
                                                uint16_t* __restrict__ resid) {
@@ -358,6 +400,7 @@ __device__ __forceinline__ void quantize_chunk(u32x4 v, bool active, bool tiled,
     packed = e2m1_pack8(xs, __uint_as_float(sc << 23));  // x / 2^e, exact
   }
   if (!active) return;
+  if (poison) sc = 0x7Fu;  // E4M3 NaN: no valid tensor scale (see grid_max)
   if ((cc & (CPB - 1)) == 0) scales[scale_off<FMT>(tiled, row, cc / CPB, cols)] = (uint8_t)sc;
 
   *reinterpret_cast<uint32_t*>(q + code_off(tiled, row, 4 * cc, cols)) = packed;
@@ -376,7 +419,7 @@ __device__ __forceinline__ void quantize_chunk(u32x4 v, bool active, bool tiled,
         else
           p = e2m1_mag_value(code) * d;         // exact
         if (code & 8u) p = -p;
-        resid[row * nS + j] = (uint16_t)f32_to_bf16_rne(xs[k] - p);
+        resid[row * nS + j] = poison ? (uint16_t)0x7FC0u : (uint16_t)f32_to_bf16_rne(xs[k] - p);
         ++j;
       }
     }
@@ -398,7 +441,7 @@ __global__ void __launch_bounds__(NT) k_quantize(
     ChunkGrid gr, int64_t rows, int64_t cols, bool tiled, const int32_t* __restrict__ off, int G,
     const int32_t* __restrict__ chan, int nS, uint8_t* __restrict__ q,
     uint8_t* __restrict__ scales, float* __restrict__ tscale, uint16_t* __restrict__ resid,
-    const uint32_t* __restrict__ amax_words, int nparts) {
+    const uint32_t* __restrict__ amax_words, int nparts, GridCtl gc) {
   __shared__ uint32_t red[NT / 64];
   __shared__ uint32_t tab[TAB_MAX];
   const uint32_t cpr = gr.cpr, total_rm = (uint32_t)(rows * cpr);
@@ -470,6 +513,7 @@ __global__ void __launch_bounds__(NT) k_quantize(
 
   // tensor scale of the dense paths (one group)
   float tdense = 1.0f;
+  bool poison = false;
   if (MODE == AMAX_PARTIALS) {
     uint32_t m = 0;
     for (int i = threadIdx.x; i < nparts; i += NT) m = max(m, amax_words[i]);
@@ -477,8 +521,8 @@ __global__ void __launch_bounds__(NT) k_quantize(
   } else if (MODE == AMAX_FUSED) {
     // the maximum of this workgroup's own chunks (already loaded), then
     // across the launch
-    __shared__ uint32_t s_amax;
-    const uint32_t gen = threadIdx.x < 64 ? grid_gen() : 0u;
+    __shared__ uint32_t s_amax, s_bad;
+    const uint32_t gen = threadIdx.x < 64 ? grid_gen(gc) : 0u;
     uint32_t m = 0;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -487,14 +531,19 @@ __global__ void __launch_bounds__(NT) k_quantize(
     }
     m = wg_max<NT>(m, red);
     if (threadIdx.x < 64) {
-      const uint32_t g = grid_max(m, gridDim.x, gen);
-      if (threadIdx.x == 0) s_amax = g;
+      bool expired;
+      const uint32_t g = grid_max(m, gridDim.x, gen, gc, expired);
+      if (threadIdx.x == 0) {
+        s_amax = g;
+        s_bad = expired ? 1u : 0u;
+      }
     }
     __syncthreads();
     tdense = nv_tensor_scale(bf16_to_f32(s_amax));
+    poison = s_bad != 0u;
   }
   if ((MODE == AMAX_PARTIALS || MODE == AMAX_FUSED) && blockIdx.x == 0 && threadIdx.x == 0)
-    tscale[0] = tdense;
+    tscale[0] = poison ? __uint_as_float(0x7FC00000u) : tdense;
 
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -512,7 +561,8 @@ __global__ void __launch_bounds__(NT) k_quantize(
     uint32_t ent = 0;
     if (nS > 0 && active)
       ent = (use_tab && g == gA) ? tab[cc] : chan_entry_search(chan + (int64_t)g * nS, nS, cc);
-    quantize_chunk<FMT>(v[u], active, tiled, row, cc, cols, t, ent, nS, q, scales, resid);
+    quantize_chunk<FMT>(v[u], active, poison, tiled, row, cc, cols, t, ent, nS, q, scales,
+                        resid);
   }
 }
 
@@ -520,16 +570,16 @@ template <int FMT, int MODE, int NT, int U>
 static void launch_q(const ChunkGrid& gr, int64_t rows, int64_t cols, bool tiled,
                      hipStream_t stream, const int32_t* off, int G, const int32_t* chan, int nS,
                      uint8_t* q, uint8_t* scales, float* tscale, uint16_t* resid,
-                     const uint32_t* words, int nparts) {
+                     const uint32_t* words, int nparts, GridCtl gc = GridCtl{nullptr, 0, -1}) {
   const int64_t per = (int64_t)NT * U;
   const int64_t total = (tiled ? (rows + 15) / 16 * 16 : rows) * (int64_t)gr.cpr;
   dim3 grid((unsigned)((total + per - 1) / per));
   if (tiled)
     hipLaunchKernelGGL((k_quantize<FMT, MODE, NT, U, true>), grid, dim3(NT), 0, stream, gr, rows,
-                       cols, true, off, G, chan, nS, q, scales, tscale, resid, words, nparts);
+                       cols, true, off, G, chan, nS, q, scales, tscale, resid, words, nparts, gc);
   else
     hipLaunchKernelGGL((k_quantize<FMT, MODE, NT, U, false>), grid, dim3(NT), 0, stream, gr, rows,
-                       cols, false, off, G, chan, nS, q, scales, tscale, resid, words, nparts);
+                       cols, false, off, G, chan, nS, q, scales, tscale, resid, words, nparts, gc);
 }
 
 int launch_quantize(int fmt, bool tiled, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
@@ -538,7 +588,11 @@ int launch_quantize(int fmt, bool tiled, const uint16_t* x, int64_t rows, int64_
                     hipStream_t stream) {
   const int64_t chunks = rows * (cols >> 3);
   const ChunkGrid gr{x, (uint32_t)(cols >> 3), ldx, 1.0 / (double)(cols >> 3), ldx == cols};
-  uint32_t* words = static_cast<uint32_t*>(ws);
+  // NVFP4 workspace: the exchange state of the small-tensor path, then the
+  // amax words of the other paths
+  uint32_t* state = static_cast<uint32_t*>(ws);
+  uint32_t* words = ws ? reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + WS_HEADER)
+                       : nullptr;
   const bool grouped = (off != nullptr && G > 1);
   const int Gk = grouped ? G : 1;
   if (fmt == FP4Q_MXFP4) {
@@ -568,8 +622,10 @@ int launch_quantize(int fmt, bool tiled, const uint16_t* x, int64_t rows, int64_
   if (launch_chunks <= FUSED_MAX_CHUNKS) {
     static_assert(FUSED_MAX_CHUNKS / FT <= GRID_SLOTS, "one grid slot per workgroup");
     if (SMALL_FUSED) {
+      const uint32_t spin = g_hook_spin.load();
+      const GridCtl gc{state, spin ? spin : GRID_SPIN_LIMIT, g_hook_skip.load()};
       launch_q<FP4Q_NVFP4, AMAX_FUSED, FT, 1>(gr, rows, cols, tiled, stream, off, 1, chan, nS, q, scales,
-                                              tscale, resid, words, 0);
+                                              tscale, resid, words, 0, gc);
     } else {
       // two short passes spread over many workgroups
       const int64_t parts = (chunks + QT - 1) / QT;
@@ -592,7 +648,21 @@ int launch_quantize(int fmt, bool tiled, const uint16_t* x, int64_t rows, int64_
 size_t quantize_workspace_bytes(int fmt, int G) {
   if (fmt != FP4Q_NVFP4) return 0;
   const int n = G > AMAX_PARTS ? G : AMAX_PARTS;
-  return (size_t)n * sizeof(uint32_t);
+  return WS_HEADER + (size_t)n * sizeof(uint32_t);
+}
+
+int quantize_status(const void* ws, hipStream_t stream, uint32_t* status) {
+  uint32_t* word = static_cast<uint32_t*>(const_cast<void*>(ws)) + WS_STATUS;
+  uint32_t v = 0;
+  if (hipStreamSynchronize(stream) != hipSuccess) return -1;
+  if (hipMemcpyAsync(&v, word, sizeof v, hipMemcpyDeviceToHost, stream) != hipSuccess) return -1;
+  if (hipStreamSynchronize(stream) != hipSuccess) return -1;
+  if (v != 0u) {
+    if (hipMemsetAsync(word, 0, sizeof v, stream) != hipSuccess) return -1;
+    if (hipStreamSynchronize(stream) != hipSuccess) return -1;
+  }
+  *status = v;
+  return 0;
 }
 
 }  // namespace fp4q

@@ -52,7 +52,13 @@
  *
  * Conventions for every entry point:
  *  - Tensor pointers are DEVICE pointers owned by the caller.  The library
- *    allocates nothing and keeps no state beyond a thread-local last error.
+ *    allocates nothing.  Its host state is a thread-local last error and
+ *    the test hooks (fp4q_test_hook); it keeps no device state of its own:
+ *    what a kernel carries from one call to the next (the small-tensor
+ *    NVFP4 quantizer's exchange slots, see fp4q_quantize) lives in the
+ *    caller's workspace, so calls with different workspaces are
+ *    independent on any streams, and calls sharing a workspace must not
+ *    overlap (as for any buffer a call writes).
  *  - Every call is asynchronous on the caller's HIP stream (passed as void*,
  *    NULL = default stream); results are ready when that stream is.
  *  - Unpacked tensors are row-major; FP4 blocks run along the contiguous
@@ -122,19 +128,28 @@ int fp4q_packed_bytes(fp4q_format_t fmt, fp4q_layout_t layout, int64_t rows, int
  *   resid         out bf16 [rows, n_chan]: bf16_rne(x - deq(code)) at
  *                 column chan_idx[g][j]; deq = (e2m1 * scale) * t in FP32
  *                 (NVFP4) or e2m1 * 2^e (MXFP4); NULL iff n_chan == 0
- *   workspace     device scratch of fp4q_quantize_workspace_bytes() bytes
- *                 (NVFP4 only; may be NULL when that is 0); contents need
- *                 no initialisation and are left undefined
+ *   workspace     device scratch of fp4q_quantize_workspace_bytes() bytes,
+ *                 8-byte aligned (NVFP4 only; may be NULL when that is 0).
+ *                 Its first 512 bytes hold the small-tensor path's exchange
+ *                 state (below): ZERO-FILL the workspace once before its
+ *                 first use; the library keeps it consistent from then on,
+ *                 so do not write to it between calls.  The rest is scratch
+ *                 left undefined.
  *
  * cols must be a multiple of the block size; 0 <= n_chan <= cols.
  * rows * cols / 8 must be below 2^31 (FP4Q_ERR_UNSUPPORTED otherwise: 32 GiB
  * of BF16 per call).
  *
  * Small NVFP4 tensors (one group, at most 131,072 elements, the tiled
- * layout counting its rows padded to 16) take one launch
- * whose workgroups exchange the tensor maximum through per-device state of
- * the library: two such calls must not run at the same time on one GPU
- * (calls on one stream, or ordered by events, are fine).
+ * layout counting its rows padded to 16) take one launch whose workgroups
+ * exchange the tensor maximum through slots in the workspace, tagged by a
+ * launch counter kept beside them.  The exchange waits a bounded time; a
+ * workgroup whose wait runs out (it cannot happen while every workgroup of
+ * the launch runs; the test hooks force it) poisons what it writes: block
+ * scales 0x7F (E4M3 NaN), residuals BF16 NaN, and a NaN tensor scale when
+ * it is workgroup 0, so a GEMM on the result gives NaN, never a silent
+ * wrong value; it also sets FP4Q_QSTATUS_GRID_EXPIRED in the workspace's
+ * status word, which fp4q_quantize_status() returns.
  * ------------------------------------------------------------------------ */
 size_t fp4q_quantize_workspace_bytes(fp4q_format_t fmt, int64_t rows, int64_t cols,
                                      int32_t num_groups);
@@ -144,6 +159,37 @@ int fp4q_quantize(fp4q_format_t fmt, fp4q_layout_t layout, const uint16_t* x, in
                   const int32_t* chan_idx, int32_t n_chan, uint8_t* q, uint8_t* scales,
                   float* tensor_scale, uint16_t* resid, void* workspace, size_t workspace_bytes,
                   void* stream);
+
+/* Status of the quantize calls that used an NVFP4 workspace since the last
+ * query: waits for `stream` (the caller's stream of those calls), reads the
+ * workspace's status word into *status and clears it.  Bits:
+ * FP4Q_QSTATUS_GRID_EXPIRED (the small-tensor exchange ran out of time; the
+ * outputs of that call are NaN-poisoned).  0 means every such call found
+ * its tensor maximum.  Errors: FP4Q_ERR_INVALID (status NULL),
+ * FP4Q_ERR_WORKSPACE (workspace NULL, misaligned or smaller than an NVFP4
+ * workspace), FP4Q_ERR_HIP. */
+#define FP4Q_QSTATUS_GRID_EXPIRED 1
+int fp4q_quantize_status(const void* workspace, size_t workspace_bytes, int32_t* status,
+                         void* stream);
+
+/* Test hooks (failure injection for the error paths; not for production
+ * use, and not synchronised with calls running on other threads):
+ *   FP4Q_HOOK_RESET              all hooks off (value ignored)
+ *   FP4Q_HOOK_FAIL_NEXT_LAUNCH   the next entry point that passes its
+ *                                argument checks returns FP4Q_ERR_HIP
+ *                                WITHOUT launching anything, with
+ *                                fp4q_last_hip_error() = value (> 0)
+ *   FP4Q_HOOK_GRID_SPIN_LIMIT    spin limit of the small-tensor NVFP4
+ *                                exchange (0 = the default 2^22 loads)
+ *   FP4Q_HOOK_GRID_SKIP_SLOT     that workgroup of the small-tensor NVFP4
+ *                                launches skips its slot store (-1 = none),
+ *                                so the others' waits run out
+ * Returns FP4Q_OK, or FP4Q_ERR_INVALID for an unknown hook or value. */
+#define FP4Q_HOOK_RESET 0
+#define FP4Q_HOOK_FAIL_NEXT_LAUNCH 1
+#define FP4Q_HOOK_GRID_SPIN_LIMIT 2
+#define FP4Q_HOOK_GRID_SKIP_SLOT 3
+int fp4q_test_hook(int32_t hook, int64_t value);
 
 /* ------------------------------------------------------------------------
  * Compensated W4A4 GEMM.  QUADS abstract (native W4A4 FP4 GEMM plus
@@ -402,8 +448,9 @@ int fp4q_permute_quantized(fp4q_format_t fmt, const uint16_t* x, int64_t tokens,
  * its code g, E4M3 block scale value sb and tensor scale t (the exact
  * product); the ideal scale is again s* = amax/6 of the 16-block.  The sums
  * stay exact while every term (6x, 6 g sb t, g* amax) is a multiple of
- * 2^-136, which holds for a tensor amax of at least 2^-89 (a precondition,
- * not checked).
+ * 2^-136, which holds for a tensor amax of at least 2^-89; below that (and
+ * above 0) the kernel sets FP4Q_DEC_INEXACT in `flags`, and the sums may
+ * have lost low-order terms.
  * ------------------------------------------------------------------------ */
 typedef struct {
     /* 6 * (sum of component c) as a 320-bit two's complement integer in units
@@ -417,7 +464,11 @@ typedef struct {
     int64_t n_deadzone;  /* non-zero inputs quantized to zero */
     int64_t n_clipped;   /* |x| > 6 * s: 0 for MXFP4 under its scale rule; for
                             NVFP4 where E4M3 rounded the block scale down */
+    int64_t flags;       /* FP4Q_DEC_INEXACT: NVFP4 tensor amax in (0, 2^-89),
+                            the exact sums are not guaranteed */
 } fp4q_err_stats_t;
+
+#define FP4Q_DEC_INEXACT 1
 
 /*   fmt        FP4Q_MXFP4 or FP4Q_NVFP4
  *   x          bf16 [rows, cols], ldx as for fp4q_quantize; cols a multiple

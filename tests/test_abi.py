@@ -10,7 +10,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fp4q.h")
 
-INVALID, UNSUPPORTED, WORKSPACE = -1, -2, -3
+INVALID, UNSUPPORTED, WORKSPACE, HIP_ERR = -1, -2, -3, -4
 
 
 def declared_functions(header=HEADER):
@@ -106,6 +106,62 @@ def test_quantize_rejects(L):
     assert q(L, layout=1, cols=64) == INVALID    # tiled needs cols % 128
     assert q(L, layout=1, cols=128, ldx=128, sc=ctypes.c_void_p(0x20002)) == INVALID
     assert q(L, sc=ctypes.c_void_p(0x20002)) == INVALID  # scales 4-byte aligned
+
+
+def test_quantize_workspace_alignment(L):
+    """The NVFP4 workspace holds 64-bit exchange slots: 8-byte alignment and
+    the 512-byte state block in front of the amax words."""
+    need = L.fp4q_quantize_workspace_bytes(0, 4, 64, 1)
+    assert need >= 512 + 4 * 1024
+    assert L.fp4q_quantize_workspace_bytes(0, 4, 64, 5000) >= 512 + 4 * 5000
+    assert q(L, ws=ctypes.c_void_p(0x10004), wsb=need) == WORKSPACE
+    assert q(L, wsb=need - 1) == WORKSPACE
+
+
+def test_test_hook_rejects(L):
+    assert L.fp4q_test_hook(99, 0) == INVALID
+    assert L.fp4q_test_hook(1, 0) == INVALID        # no error code to report
+    assert L.fp4q_test_hook(1, -5) == INVALID
+    assert L.fp4q_test_hook(2, -1) == INVALID       # negative spin limit
+    assert L.fp4q_test_hook(3, -2) == INVALID       # skip slot below -1
+    assert L.fp4q_test_hook(0, 0) == 0
+
+
+def test_injected_launch_failure(L):
+    """The test fault hook makes the launch path report FP4Q_ERR_HIP with the
+    given hipError_t, without launching (the pointers here are fake); a call
+    that fails its argument checks first leaves the hook armed, and the hook
+    fires once."""
+    need = L.fp4q_quantize_workspace_bytes(0, 4, 64, 1)
+    try:
+        assert L.fp4q_test_hook(1, 719) == 0
+        assert q(L, fmt=7) == INVALID                 # rejected before the hook
+        assert q(L, wsb=need) == HIP_ERR               # the injected failure
+        assert L.fp4q_last_hip_error() == 719
+        assert L.fp4q_status_str(HIP_ERR) == b"HIP error"
+        # the GEMM, the decomposition and the status query take the same path
+        assert L.fp4q_test_hook(1, 98) == 0
+        assert g(L) == HIP_ERR
+        assert L.fp4q_last_hip_error() == 98
+        assert L.fp4q_test_hook(1, 700) == 0
+        ws = L.fp4q_error_decompose_workspace_bytes(16, 64)
+        assert L.fp4q_error_decompose(1, A, 16, 64, 64, B, A, ws, None) == HIP_ERR
+        assert L.fp4q_last_hip_error() == 700
+        st = ctypes.c_int32(-1)
+        assert L.fp4q_test_hook(1, 4) == 0
+        assert L.fp4q_quantize_status(A, need, ctypes.byref(st), None) == HIP_ERR
+        assert L.fp4q_last_hip_error() == 4 and st.value == -1
+    finally:
+        L.fp4q_test_hook(0, 0)
+
+
+def test_quantize_status_rejects(L):
+    need = L.fp4q_quantize_workspace_bytes(0, 4, 64, 1)
+    st = ctypes.c_int32(0)
+    assert L.fp4q_quantize_status(A, need, None, None) == INVALID
+    assert L.fp4q_quantize_status(None, need, ctypes.byref(st), None) == WORKSPACE
+    assert L.fp4q_quantize_status(ctypes.c_void_p(0x10004), need, ctypes.byref(st), None) == WORKSPACE
+    assert L.fp4q_quantize_status(A, 100, ctypes.byref(st), None) == WORKSPACE
 
 
 def g(L, fmt=0, M=4, N=8, K=256, aq=A, as_=A, ats=B, bq=B, bs=B, bts=B, chan=None, nS=0, R=None,

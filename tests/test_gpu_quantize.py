@@ -92,13 +92,14 @@ def test_tiled_ragged(orc, fmt, rows, cols, nS):
 
 
 def test_workspace_reuse_across_paths(orc):
-    """One NVFP4 workspace through the single-launch small-tensor path, the
-    two-pass large path, the grouped path and the small path again: every
-    result exact whatever the previous call left in the workspace."""
+    """One NVFP4 workspace (zero-filled once, as the header asks) through the
+    single-launch small-tensor path, the two-pass large path, the grouped
+    path and the small path again: every result exact whatever the previous
+    call left in the workspace, and no exchange reported expired."""
     dev = need_gpu()
     say("quantize workspace reuse across paths")
     wsb = max(fq.quantize_workspace_bytes(0, 4096, 4096, 1), fq.quantize_workspace_bytes(0, 600, 512, 5))
-    ws = torch.full((wsb,), 0xA7, dtype=torch.uint8, device=dev)
+    ws = torch.zeros((wsb,), dtype=torch.uint8, device=dev)
     cases = [(64, 2048, None), (1, 256, None), (600, 4096, None),
              (333, 512, np.array([0, 40, 40, 41, 200, 333], np.int32)), (64, 2048, None),
              (300, 4096, None)]
@@ -113,6 +114,7 @@ def test_workspace_reuse_across_paths(orc):
                          None, 0, q, sc, ts, None, ws)
         torch.cuda.synchronize(dev)
         assert_quant_equal({"q": q, "scales": sc, "tscale": ts, "resid": None}, ref, 0)
+    assert fq.quantize_status(ws) == 0
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
