@@ -115,6 +115,9 @@ def lib():
         L.fp4q_permute_quantized.restype = ctypes.c_int
         L.fp4q_permute_quantized.argtypes = [ctypes.c_int, P, i64, i64, i64, P, P, P, P, i64, P,
                                              i32, P, i32, P, P, P, P, P]
+        L.fp4q_quantize_noalloc.restype = ctypes.c_int
+        L.fp4q_quantize_noalloc.argtypes = [ctypes.c_int, ctypes.c_int, P, i64, i64, i64, P, i32,
+                                            P, i32, P, P, P, P, P]
         L.fp4q_quantize_status.restype = ctypes.c_int
         L.fp4q_quantize_status.argtypes = [P, sz, ctypes.POINTER(i32), P]
         L.fp4q_test_hook.restype = ctypes.c_int
@@ -306,6 +309,18 @@ HOOK_FAIL_NEXT_LAUNCH = 1
 HOOK_GRID_SPIN_LIMIT = 2
 HOOK_GRID_SKIP_SLOT = 3
 DEC_INEXACT = 1
+
+
+def quantize_noalloc_into(fmt, layout, x, group_offsets, num_groups, chan_idx, n_chan, q, scales,
+                          tensor_scale, resid, stream=None):
+    """fp4q_quantize_noalloc: quantize_into without a workspace (the library's
+    static per-GPU scratch stands in for it)."""
+    rows, cols = x.shape
+    _check("fp4q_quantize_noalloc",
+           lib().fp4q_quantize_noalloc(fmt, layout, _ptr(x), rows, cols, x.stride(0),
+                                       _ptr(group_offsets), num_groups, _ptr(chan_idx), n_chan,
+                                       _ptr(q), _ptr(scales), _ptr(tensor_scale), _ptr(resid),
+                                       _stream(stream)))
 
 
 def quantize_status(workspace, stream=None) -> int:

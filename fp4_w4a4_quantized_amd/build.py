@@ -12,7 +12,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfp4q.so")
-SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "gemm_big.hip", "gemm_skinny.hip", "decompose.hip", "select.hip", "permute.hip"]
+SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "gemm_big.hip", "gemm_skinny.hip", "decompose.hip", "select.hip", "permute.hip", "noalloc.hip"]
 # the peak microbenchmarks (measurement only) go into a library of their own
 PEAKS_LIB = os.path.join(HERE, "libfp4q_peaks.so")
 PEAKS_SOURCES = ["peaks.hip"]

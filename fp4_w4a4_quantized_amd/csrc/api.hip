@@ -93,11 +93,17 @@ size_t fp4q_quantize_workspace_bytes(fp4q_format_t fmt, int64_t rows, int64_t co
   return fp4q::quantize_workspace_bytes(fmt, num_groups > 0 ? num_groups : 1);
 }
 
-int fp4q_quantize(fp4q_format_t fmt, fp4q_layout_t layout, const uint16_t* x, int64_t rows,
-                  int64_t cols, int64_t ldx, const int32_t* group_offsets, int32_t num_groups,
-                  const int32_t* chan_idx, int32_t n_chan, uint8_t* q, uint8_t* scales,
-                  float* tensor_scale, uint16_t* resid, void* workspace, size_t workspace_bytes,
-                  void* stream) {
+}  // extern "C"
+
+namespace fp4q {
+
+void set_last_hip_error(int e) { g_last_hip_error = e; }
+
+// fp4q_quantize's argument checks other than the workspace (host only).
+int quantize_checks(int fmt, int layout, const uint16_t* x, int64_t rows, int64_t cols,
+                    int64_t ldx, const int32_t* group_offsets, int32_t num_groups,
+                    const int32_t* chan_idx, int32_t n_chan, const uint8_t* q,
+                    const uint8_t* scales, const float* tensor_scale, const uint16_t* resid) {
   if (!fmt_ok(fmt) || !layout_ok(layout)) return FP4Q_ERR_INVALID;
   const int blk = blk_of(fmt);
   if (rows < 0 || cols <= 0 || cols % blk != 0 || ldx < cols || ldx % 8 != 0)
@@ -114,6 +120,21 @@ int fp4q_quantize(fp4q_format_t fmt, fp4q_layout_t layout, const uint16_t* x, in
     return FP4Q_ERR_INVALID;
   const int64_t prow = layout == FP4Q_LAYOUT_TILED ? (rows + 15) / 16 * 16 : rows;
   if (prow * (cols / 8) >= ((int64_t)1 << 31)) return FP4Q_ERR_UNSUPPORTED;  // 32-bit chunk index
+  return FP4Q_OK;
+}
+
+}  // namespace fp4q
+
+extern "C" {
+
+int fp4q_quantize(fp4q_format_t fmt, fp4q_layout_t layout, const uint16_t* x, int64_t rows,
+                  int64_t cols, int64_t ldx, const int32_t* group_offsets, int32_t num_groups,
+                  const int32_t* chan_idx, int32_t n_chan, uint8_t* q, uint8_t* scales,
+                  float* tensor_scale, uint16_t* resid, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  const int rc = fp4q::quantize_checks(fmt, layout, x, rows, cols, ldx, group_offsets, num_groups,
+                                       chan_idx, n_chan, q, scales, tensor_scale, resid);
+  if (rc != FP4Q_OK) return rc;
   const size_t need = fp4q_quantize_workspace_bytes(fmt, rows, cols, num_groups);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 8)))
     return FP4Q_ERR_WORKSPACE;

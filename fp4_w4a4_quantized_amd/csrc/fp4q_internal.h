@@ -17,6 +17,14 @@ int launch_quantize(int fmt, bool tiled, const uint16_t* x, int64_t rows, int64_
 
 size_t quantize_workspace_bytes(int fmt, int G);
 
+// fp4q_quantize's argument checks other than the workspace (host only), and
+// the calling thread's last HIP error (for entry points outside api.hip).
+int quantize_checks(int fmt, int layout, const uint16_t* x, int64_t rows, int64_t cols,
+                    int64_t ldx, const int32_t* group_offsets, int32_t num_groups,
+                    const int32_t* chan_idx, int32_t n_chan, const uint8_t* q,
+                    const uint8_t* scales, const float* tensor_scale, const uint16_t* resid);
+void set_last_hip_error(int e);
+
 // Status word of a quantize workspace (bit 0: the small-tensor exchange ran
 // out of spins); waits for the stream, then reads and clears it.
 int quantize_status(const void* ws, hipStream_t stream, uint32_t* status);

@@ -160,6 +160,21 @@ int fp4q_quantize(fp4q_format_t fmt, fp4q_layout_t layout, const uint16_t* x, in
                   float* tensor_scale, uint16_t* resid, void* workspace, size_t workspace_bytes,
                   void* stream);
 
+/* fp4q_quantize for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments, results and errors without the workspace, which is a
+ * static device array of the library instead (32 KiB per GPU, held until
+ * the process ends, zero at load).  It allocates nothing and calls no
+ * allocating routine.  Limits: NVFP4 with at most 8,064 groups
+ * (FP4Q_ERR_UNSUPPORTED beyond); MXFP4 needs no scratch.  Every call on a
+ * GPU shares that GPU's array, so calls that overlap on one GPU (other
+ * streams, parallel graph branches) race; calls on one stream are fine.
+ * FP4Q_ERR_HIP also when the array's device address cannot be found. */
+int fp4q_quantize_noalloc(fp4q_format_t fmt, fp4q_layout_t layout, const uint16_t* x,
+                          int64_t rows, int64_t cols, int64_t ldx, const int32_t* group_offsets,
+                          int32_t num_groups, const int32_t* chan_idx, int32_t n_chan, uint8_t* q,
+                          uint8_t* scales, float* tensor_scale, uint16_t* resid, void* stream);
+
 /* Status of the quantize calls that used an NVFP4 workspace since the last
  * query: waits for `stream` (the caller's stream of those calls), reads the
  * workspace's status word into *status and clears it.  Bits:
