@@ -951,3 +951,68 @@ int orc_error_decompose_nv(const uint16_t* x, int64_t rows, int64_t cols, int64_
     out->n_clipped = nclip;
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Outlier Fallback ("Decomposing MXFP4 quantization error ...", abstract:   */
+/* the fallback recovers the deadzone entries)                               */
+/* ------------------------------------------------------------------------ */
+
+/* The page names the correction and what it recovers, not its mechanics.
+ * Reading: the entries the quantizer sends to zero -- code magnitude 0, the
+ * deadzone set D of the three-way split -- fall back to their own BF16
+ * value; every other entry is dequantized from its code and block scale
+ * (one quantization group, orc_quantize's codes):
+ *   out = x                  where the code magnitude is 0
+ *   out = e2m1(code) * 2^e   (MXFP4)
+ *   out = (e2m1(code) * sb) * t   (NVFP4: FP32, first product exact; the
+ *                                  same value the quantizer's residual
+ *                                  subtracts)
+ * out is FP32 [rows, cols] (row stride cols); *n_fallback receives the
+ * number of entries with x != 0 that fell back (the deadzone count).
+ * Returns 0, or -1 for a shape the formats do not allow. */
+int orc_qdq_fallback(int fmt, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                     float* out, int64_t* n_fallback) {
+    const int blk = (fmt == ORC_NVFP4) ? 16 : 32;
+    if ((fmt != ORC_NVFP4 && fmt != ORC_MXFP4) || cols % blk != 0 || rows < 0) return -1;
+    uint8_t* q = (uint8_t*)malloc((size_t)(rows > 0 ? rows : 1) * (size_t)(cols / 2));
+    uint8_t* sc = (uint8_t*)malloc((size_t)(rows > 0 ? rows : 1) * (size_t)(cols / blk));
+    if (!q || !sc) {
+        free(q);
+        free(sc);
+        return -1;
+    }
+    float t = 1.0f;
+    if (orc_quantize(fmt, x, rows, cols, ldx, NULL, 1, NULL, 0, q, sc,
+                     fmt == ORC_NVFP4 ? &t : NULL, NULL) != 0) {
+        free(q);
+        free(sc);
+        return -1;
+    }
+    int64_t nfb = 0;
+#pragma omp parallel for schedule(static) reduction(+ : nfb)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t c = 0; c < cols; ++c) {
+            const uint8_t byte = q[r * (cols / 2) + c / 2];
+            const uint8_t code = (c & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15);
+            const uint16_t h = x[r * ldx + c];
+            const float xv = orc_bf16_value(h);
+            float v;
+            if ((code & 7) == 0) {
+                v = xv;                        /* fallback: the entry itself */
+                if (xv != 0.0f) ++nfb;
+            } else {
+                const uint8_t s = sc[r * (cols / blk) + c / blk];
+                const float g = (float)orc_e2m1_value(code);
+                if (fmt == ORC_NVFP4)
+                    v = (g * (float)orc_e4m3_value(s)) * t;
+                else
+                    v = (float)((double)g * orc_e8m0_value(s));
+            }
+            out[r * cols + c] = v;
+        }
+    }
+    free(q);
+    free(sc);
+    if (n_fallback) *n_fallback = nfb;
+    return 0;
+}

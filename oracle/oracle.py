@@ -108,6 +108,9 @@ def lib():
         L.orc_error_decompose.argtypes = [P, i64, i64, i64, ctypes.POINTER(ErrStats)]
         L.orc_error_components_nv.restype = ctypes.c_int
         L.orc_error_components_nv.argtypes = [P, i64, i64, i64, P]
+        L.orc_qdq_fallback.restype = ctypes.c_int
+        L.orc_qdq_fallback.argtypes = [ctypes.c_int, P, i64, i64, i64, P,
+                                       ctypes.POINTER(ctypes.c_int64)]
         L.orc_error_decompose_nv.restype = ctypes.c_int
         L.orc_error_decompose_nv.argtypes = [P, i64, i64, i64, ctypes.POINTER(ErrStats)]
         _lib = L
@@ -390,3 +393,19 @@ def error_decompose(x: np.ndarray, fmt: int = MXFP4) -> dict:
         "n_deadzone": st.n_deadzone,
         "n_clipped": st.n_clipped,
     }
+
+
+# ---- Outlier Fallback ------------------------------------------------------
+
+def qdq_fallback(fmt: int, x: np.ndarray):
+    """Quantize-dequantize with Outlier Fallback: entries whose code magnitude
+    is 0 keep their own value, the rest are dequantized.  Returns
+    (out float32 [rows, cols], number of non-zero entries that fell back)."""
+    x = _c(x, np.uint16)
+    rows, cols = x.shape
+    out = np.zeros((rows, cols), np.float32)
+    n = ctypes.c_int64(0)
+    rc = lib().orc_qdq_fallback(fmt, _p(x), rows, cols, cols, _p(out), ctypes.byref(n))
+    if rc != 0:
+        raise ValueError(f"oracle qdq_fallback rejected the shape (rc={rc})")
+    return out, int(n.value)
