@@ -543,6 +543,16 @@ def measure(name, args, stream, dev, variant_args=None):
                              dtype=torch.uint8, device=dev)
         t_dec = timed(lambda i: fq.error_decompose_into(s.fmt, s.x, dec_out, dec_ws), reps)
         log(f"{name}: error decomposition {t_dec * 1e6:.2f} us per call")
+        # Outlier Fallback: the activations quantized and dequantized with the
+        # deadzone entries kept (FP32 out), and the fallback count
+        fb_y = torch.empty((s.M, s.K), dtype=torch.float32, device=dev)
+        fb_n = torch.empty(1, dtype=torch.int64, device=dev)
+        fb_ws = torch.empty(max(fq.qdq_fallback_workspace_bytes(s.fmt, s.M, s.K), 16),
+                            dtype=torch.uint8, device=dev)
+        t_fb = timed(lambda i: fq.qdq_fallback_into(s.fmt, s.x, fb_y, fb_n, fb_ws), reps)
+        fb_count = int(fb_n.item())
+        del fb_y, fb_ws
+        log(f"{name}: outlier fallback {t_fb * 1e6:.2f} us per call, {fb_count} entries")
 
     default_variant = (a.layout == "tiled" and a.out_dtype == "f32" and a.residual == "bf16" and
                        a.channels == "fixed" and a.comp_weights == "prepared" and
@@ -582,6 +592,11 @@ def measure(name, args, stream, dev, variant_args=None):
         rec["decompose_us"] = round(t_dec * 1e6, 3)
         rec["decompose_gbps"] = round(dec_bytes / t_dec / 1e9, 1)
         rec["decompose_frac_hbm"] = round(dec_bytes / t_dec / 1e9 / HBM_PEAK_GBS, 4)
+        fb_bytes = s.M * s.K * (2 + 4)          # read X (BF16), write the FP32 result
+        rec["fallback_us"] = round(t_fb * 1e6, 3)
+        rec["fallback_gbps"] = round(fb_bytes / t_fb / 1e9, 1)
+        rec["fallback_frac_hbm"] = round(fb_bytes / t_fb / 1e9 / HBM_PEAK_GBS, 4)
+        rec["fallback_entries"] = fb_count
     if t_sel is not None:
         rec["select_us"] = round(t_sel * 1e6, 3)
         rec["select_gbps"] = round(s.select_bytes / t_sel / 1e9, 1)

@@ -115,6 +115,10 @@ def lib():
         L.fp4q_permute_quantized.restype = ctypes.c_int
         L.fp4q_permute_quantized.argtypes = [ctypes.c_int, P, i64, i64, i64, P, P, P, P, i64, P,
                                              i32, P, i32, P, P, P, P, P]
+        L.fp4q_qdq_fallback_workspace_bytes.restype = sz
+        L.fp4q_qdq_fallback_workspace_bytes.argtypes = [ctypes.c_int, i64, i64]
+        L.fp4q_qdq_fallback.restype = ctypes.c_int
+        L.fp4q_qdq_fallback.argtypes = [ctypes.c_int, P, i64, i64, i64, P, i64, P, P, sz, P]
         L.fp4q_quantize_noalloc.restype = ctypes.c_int
         L.fp4q_quantize_noalloc.argtypes = [ctypes.c_int, ctypes.c_int, P, i64, i64, i64, P, i32,
                                             P, i32, P, P, P, P, P]
@@ -309,6 +313,31 @@ HOOK_FAIL_NEXT_LAUNCH = 1
 HOOK_GRID_SPIN_LIMIT = 2
 HOOK_GRID_SKIP_SLOT = 3
 DEC_INEXACT = 1
+
+
+def qdq_fallback_workspace_bytes(fmt, rows, cols) -> int:
+    return lib().fp4q_qdq_fallback_workspace_bytes(fmt, rows, cols)
+
+
+def qdq_fallback_into(fmt, x, y, n_fallback, workspace, stream=None):
+    """fp4q_qdq_fallback: y (f32 [rows, >= cols]) = the dequantized x with the
+    deadzone entries kept; n_fallback: int64 [1] on the GPU or None."""
+    rows, cols = x.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("fp4q_qdq_fallback",
+           lib().fp4q_qdq_fallback(fmt, _ptr(x), rows, cols, x.stride(0), _ptr(y), y.stride(0),
+                                   _ptr(n_fallback), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def qdq_fallback(fmt, x, stream=None):
+    """Returns (y f32 [rows, cols], n_fallback int64 [1]) on the GPU."""
+    rows, cols = x.shape
+    y = torch.empty((rows, cols), dtype=torch.float32, device=x.device)
+    n = torch.empty(1, dtype=torch.int64, device=x.device)
+    wsb = qdq_fallback_workspace_bytes(fmt, rows, cols)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=x.device) if wsb else None
+    qdq_fallback_into(fmt, x, y, n, ws, stream)
+    return y, n
 
 
 def quantize_noalloc_into(fmt, layout, x, group_offsets, num_groups, chan_idx, n_chan, q, scales,

@@ -146,6 +146,33 @@ int fp4q_quantize(fp4q_format_t fmt, fp4q_layout_t layout, const uint16_t* x, in
   return check_launch();
 }
 
+size_t fp4q_qdq_fallback_workspace_bytes(fp4q_format_t fmt, int64_t rows, int64_t cols) {
+  (void)rows;
+  (void)cols;
+  return fp4q::quantize_workspace_bytes(fmt, 1);
+}
+
+int fp4q_qdq_fallback(fp4q_format_t fmt, const uint16_t* x, int64_t rows, int64_t cols,
+                      int64_t ldx, float* y, int64_t ldy, int64_t* n_fallback, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (!fmt_ok(fmt)) return FP4Q_ERR_INVALID;
+  if (rows < 0 || cols <= 0 || cols % blk_of(fmt) != 0 || ldx < cols || ldx % 8 != 0)
+    return FP4Q_ERR_INVALID;
+  if (ldy < cols || ldy % 4 != 0) return FP4Q_ERR_INVALID;
+  if (rows > 0 && (!x || !y || !aligned(x, 16) || !aligned(y, 16))) return FP4Q_ERR_INVALID;
+  if (n_fallback && !aligned(n_fallback, 8)) return FP4Q_ERR_INVALID;
+  if (rows * (cols / 8) >= ((int64_t)1 << 31)) return FP4Q_ERR_UNSUPPORTED;
+  const size_t need = fp4q_qdq_fallback_workspace_bytes(fmt, rows, cols);
+  if (need > 0 && rows > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 8)))
+    return FP4Q_ERR_WORKSPACE;
+  if (rows == 0 && !n_fallback) return FP4Q_OK;
+  if (injected_failure()) return FP4Q_ERR_HIP;
+  clear_error();
+  fp4q::launch_qdq_fallback(fmt, x, rows, cols, ldx, y, ldy, n_fallback, workspace,
+                            static_cast<hipStream_t>(stream));
+  return check_launch();
+}
+
 int fp4q_quantize_status(const void* workspace, size_t workspace_bytes, int32_t* status,
                          void* stream) {
   if (!status) return FP4Q_ERR_INVALID;

@@ -17,6 +17,12 @@ int launch_quantize(int fmt, bool tiled, const uint16_t* x, int64_t rows, int64_
 
 size_t quantize_workspace_bytes(int fmt, int G);
 
+// Outlier Fallback: quantize-dequantize to FP32 with the deadzone entries
+// kept (one group, row-major x); count: device int64 or null.  NVFP4 uses
+// the quantize workspace's amax words.
+int launch_qdq_fallback(int fmt, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                        float* y, int64_t ldy, int64_t* count, void* ws, hipStream_t stream);
+
 // fp4q_quantize's argument checks other than the workspace (host only), and
 // the calling thread's last HIP error (for entry points outside api.hip).
 int quantize_checks(int fmt, int layout, const uint16_t* x, int64_t rows, int64_t cols,

@@ -46,6 +46,8 @@ constexpr int AMAX_PARTS = 1024;     // partial maxima of the dense large path
 constexpr int AMAX_BATCH = 16;       // loads in flight per thread in amax scans
 constexpr int TAB_MAX = 2048;        // column chunks covered by the LDS channel table
 
+typedef float f32x4q __attribute__((ext_vector_type(4)));
+
 // Group of a row: the g with off[g] <= row < off[g+1] (binary search).
 __device__ __forceinline__ int group_of_row(const int32_t* __restrict__ off, int G, int64_t row) {
   int lo = 0, hi = G - 1;
@@ -353,6 +355,73 @@ __device__ __forceinline__ uint32_t chan_entry_search(const int32_t* __restrict_
 
 // ---- one chunk ---------------------------------------------------------------
 
+struct ChunkCodes {
+  float xs[8];     // the chunk's values
+  uint32_t packed; // its 8 codes, low nibble first
+  uint32_t sc;     // block scale code
+  float sb;        // NVFP4 block scale value
+  float d;         // the divisor that maps x onto the grid (sb t, or 2^e)
+};
+
+// Codes and block scale of one 8-element chunk as the quantizer forms them.
+// All lanes of the wave call this (the block max moves between lanes).
+template <int FMT>
+__device__ __forceinline__ ChunkCodes chunk_codes(u32x4 v, float t) {
+  constexpr int CPB = (FMT == FP4Q_NVFP4) ? 2 : 4;  // chunks per scale block
+  // block max over the 2 or 4 lanes of the block: DPP quad permutations
+  // [1,0,3,2] (lane ^ 1) and [2,3,0,1] (lane ^ 2)
+  uint32_t am = absmax8(v);
+  am = max(am, (uint32_t)__builtin_amdgcn_mov_dpp((int)am, 0xB1, 0xF, 0xF, false));
+  if (CPB == 4) am = max(am, (uint32_t)__builtin_amdgcn_mov_dpp((int)am, 0x4E, 0xF, 0xF, false));
+  const float amax = bf16_to_f32(am);
+
+  ChunkCodes r;
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    r.xs[k] = __uint_as_float((k & 1) ? (w[k >> 1] & 0xFFFF0000u) : (w[k >> 1] << 16));
+
+  float qv[8];
+  r.sb = 0.0f;
+  if (FMT == FP4Q_NVFP4) {
+    const float vs = (amax / 6.0f) / t;
+    r.sc = e4m3_encode(vs);
+    r.sb = e4m3_value(r.sc);
+    r.d = r.sb * t;
+    if (r.d >= 0x1p-96f) {
+      const float y = 1.0f / r.d;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) qv[k] = div_rn(r.xs[k], r.d, y);
+    } else if (r.d > 0.0f) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) qv[k] = r.xs[k] / r.d;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) qv[k] = r.xs[k] * 0.0f;  // signed zero: magnitude code 0
+    }
+    r.packed = e2m1_pack8(qv);
+  } else {
+    const int e = mx_exponent(amax);
+    r.sc = (uint32_t)(e + 127);
+    r.d = exp2i(e);
+    r.packed = e2m1_pack8(r.xs, __uint_as_float(r.sc << 23));  // x / 2^e, exact
+  }
+  return r;
+}
+
+// Dequantized value of code `code` of a chunk: (e2m1 * sb) * t (NVFP4; the
+// first product exact) or e2m1 * 2^e (MXFP4, exact) -- the value the
+// residual subtracts.
+template <int FMT>
+__device__ __forceinline__ float chunk_deq(const ChunkCodes& r, uint32_t code, float t) {
+  float p;
+  if (FMT == FP4Q_NVFP4)
+    p = (e2m1_mag_value(code) * r.sb) * t;
+  else
+    p = e2m1_mag_value(code) * r.d;
+  return (code & 8u) ? -p : p;
+}
+
 // Quantize chunk cc of row `row` held in v.  All lanes of the wave call this
 // (the block max moves between lanes); `active` gates the stores.
 template <int FMT>
@@ -362,43 +431,9 @@ __device__ __forceinline__ void quantize_chunk(u32x4 v, bool active, bool poison
                                                uint8_t* __restrict__ q, uint8_t* __restrict__ scales,
                                                uint16_t* __restrict__ resid) {
   constexpr int CPB = (FMT == FP4Q_NVFP4) ? 2 : 4;  // chunks per scale block
-  // block max over the 2 or 4 lanes of the block: DPP quad permutations
-  // [1,0,3,2] (lane ^ 1) and [2,3,0,1] (lane ^ 2)
-  uint32_t am = absmax8(v);
-  am = max(am, (uint32_t)__builtin_amdgcn_mov_dpp((int)am, 0xB1, 0xF, 0xF, false));
-  if (CPB == 4) am = max(am, (uint32_t)__builtin_amdgcn_mov_dpp((int)am, 0x4E, 0xF, 0xF, false));
-  const float amax = bf16_to_f32(am);
-
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  float xs[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) xs[k] = __uint_as_float((k & 1) ? (w[k >> 1] & 0xFFFF0000u) : (w[k >> 1] << 16));
-
-  float d, sb = 0.0f, qv[8];
-  uint32_t sc, packed;
-  if (FMT == FP4Q_NVFP4) {
-    const float vs = (amax / 6.0f) / t;
-    sc = e4m3_encode(vs);
-    sb = e4m3_value(sc);
-    d = sb * t;
-    if (d >= 0x1p-96f) {
-      const float y = 1.0f / d;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) qv[k] = div_rn(xs[k], d, y);
-    } else if (d > 0.0f) {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) qv[k] = xs[k] / d;
-    } else {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) qv[k] = xs[k] * 0.0f;  // signed zero: magnitude code 0
-    }
-    packed = e2m1_pack8(qv);
-  } else {
-    const int e = mx_exponent(amax);
-    sc = (uint32_t)(e + 127);
-    d = exp2i(e);
-    packed = e2m1_pack8(xs, __uint_as_float(sc << 23));  // x / 2^e, exact
-  }
+  const ChunkCodes r = chunk_codes<FMT>(v, t);
+  uint32_t sc = r.sc;
+  const uint32_t packed = r.packed;
   if (!active) return;
   if (poison) sc = 0x7Fu;  // E4M3 NaN: no valid tensor scale (see grid_max)
   if ((cc & (CPB - 1)) == 0) scales[scale_off<FMT>(tiled, row, cc / CPB, cols)] = (uint8_t)sc;
@@ -413,13 +448,8 @@ __device__ __forceinline__ void quantize_chunk(u32x4 v, bool active, bool poison
     for (int k = 0; k < 8; ++k) {
       if (mask & (1u << k)) {
         const uint32_t code = (packed >> (4 * k)) & 15u;
-        float p;
-        if (FMT == FP4Q_NVFP4)
-          p = (e2m1_mag_value(code) * sb) * t;  // first product exact
-        else
-          p = e2m1_mag_value(code) * d;         // exact
-        if (code & 8u) p = -p;
-        resid[row * nS + j] = poison ? (uint16_t)0x7FC0u : (uint16_t)f32_to_bf16_rne(xs[k] - p);
+        const float p = chunk_deq<FMT>(r, code, t);
+        resid[row * nS + j] = poison ? (uint16_t)0x7FC0u : (uint16_t)f32_to_bf16_rne(r.xs[k] - p);
         ++j;
       }
     }
@@ -642,6 +672,96 @@ int launch_quantize(int fmt, bool tiled, const uint16_t* x, int64_t rows, int64_
                      (uint32_t)chunks, words);
   launch_q<FP4Q_NVFP4, AMAX_PARTIALS, QT, QU>(gr, rows, cols, tiled, stream, off, 1, chan, nS, q, scales,
                                                tscale, resid, words, (int)parts);
+  return 0;
+}
+
+// ---- Outlier Fallback: quantize-dequantize with the deadzone entries kept ----
+//
+// Decomposition page, abstract: the fallback recovers the deadzone entries.
+// One lane per 16-byte chunk (row-major, one group), the quantizer's own
+// block scale and codes (chunk_codes); the FP32 output is x itself where the
+// code magnitude is 0 and the dequantized value elsewhere (chunk_deq).  Each
+// workgroup adds its count of non-zero fallback entries to one 64-bit
+// counter, cleared by a fill kernel earlier in the stream.
+__global__ void k_clear_u64(unsigned long long* __restrict__ p) {
+  if (threadIdx.x == 0) *p = 0ull;
+}
+
+template <int FMT>
+__global__ void __launch_bounds__(QT) k_qdq_fallback(ChunkGrid gr, int64_t rows,
+                                                     float* __restrict__ y, int64_t ldy,
+                                                     const uint32_t* __restrict__ amax_words,
+                                                     int nparts,
+                                                     unsigned long long* __restrict__ count) {
+  __shared__ uint32_t red[QT / 64];
+  const uint32_t total = (uint32_t)(rows * gr.cpr);
+  const uint32_t base = blockIdx.x * (uint32_t)(QT * QU);
+  u32x4 v[QU];
+#pragma unroll
+  for (int u = 0; u < QU; ++u) {
+    const uint32_t c = base + u * QT + threadIdx.x;
+    v[u] = load_chunk(gr, c < total ? c : total - 1);
+  }
+  float t = 1.0f;
+  if (FMT == FP4Q_NVFP4) {
+    uint32_t m = 0;
+    for (int i = threadIdx.x; i < nparts; i += QT) m = max(m, amax_words[i]);
+    t = nv_tensor_scale(bf16_to_f32(wg_max<QT>(m, red)));
+  }
+  uint32_t nfb = 0;
+#pragma unroll
+  for (int u = 0; u < QU; ++u) {
+    const uint32_t c = base + u * QT + threadIdx.x;
+    const ChunkCodes r = chunk_codes<FMT>(v[u], t);
+    if (c >= total) continue;
+    uint32_t row, cc;
+    chunk_rc(gr, c, row, cc);
+    float o[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t code = (r.packed >> (4 * k)) & 15u;
+      const bool fb = (code & 7u) == 0u;
+      o[k] = fb ? r.xs[k] : chunk_deq<FMT>(r, code, t);
+      nfb += (fb && r.xs[k] != 0.0f) ? 1u : 0u;
+    }
+    f32x4q* dst = reinterpret_cast<f32x4q*>(y + (int64_t)row * ldy + (int64_t)cc * 8);
+    __builtin_nontemporal_store(f32x4q{o[0], o[1], o[2], o[3]}, dst);
+    __builtin_nontemporal_store(f32x4q{o[4], o[5], o[6], o[7]}, dst + 1);
+  }
+  if (count) {
+    for (int s = 32; s > 0; s >>= 1) nfb += (uint32_t)__shfl_xor((int)nfb, s);
+    __syncthreads();  // red is reused
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = nfb;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t n = 0;
+#pragma unroll
+      for (int i = 0; i < QT / 64; ++i) n += red[i];
+      if (n) atomicAdd(count, (unsigned long long)n);
+    }
+  }
+}
+
+int launch_qdq_fallback(int fmt, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                        float* y, int64_t ldy, int64_t* count, void* ws, hipStream_t stream) {
+  unsigned long long* cnt = reinterpret_cast<unsigned long long*>(count);
+  if (cnt) hipLaunchKernelGGL(k_clear_u64, dim3(1), dim3(64), 0, stream, cnt);
+  if (rows == 0) return 0;
+  const int64_t chunks = rows * (cols >> 3);
+  const ChunkGrid gr{x, (uint32_t)(cols >> 3), ldx, 1.0 / (double)(cols >> 3), ldx == cols};
+  const dim3 grid((unsigned)((chunks + QT * QU - 1) / (QT * QU)));
+  if (fmt == FP4Q_MXFP4) {
+    hipLaunchKernelGGL(k_qdq_fallback<FP4Q_MXFP4>, grid, dim3(QT), 0, stream, gr, rows, y, ldy,
+                       nullptr, 0, cnt);
+    return 0;
+  }
+  uint32_t* words = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + WS_HEADER);
+  int64_t parts = (chunks + (int64_t)QT * AMAX_BATCH - 1) / ((int64_t)QT * AMAX_BATCH);
+  parts = parts < AMAX_PARTS ? parts : AMAX_PARTS;
+  hipLaunchKernelGGL(k_amax_partial, dim3((unsigned)parts), dim3(QT), 0, stream, gr,
+                     (uint32_t)chunks, words);
+  hipLaunchKernelGGL(k_qdq_fallback<FP4Q_NVFP4>, grid, dim3(QT), 0, stream, gr, rows, y, ldy,
+                     words, (int)parts, cnt);
   return 0;
 }
 

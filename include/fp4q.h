@@ -160,6 +160,33 @@ int fp4q_quantize(fp4q_format_t fmt, fp4q_layout_t layout, const uint16_t* x, in
                   float* tensor_scale, uint16_t* resid, void* workspace, size_t workspace_bytes,
                   void* stream);
 
+/* ------------------------------------------------------------------------
+ * Outlier Fallback ("Decomposing MXFP4 quantization error ...", abstract:
+ * the fallback recovers the deadzone entries).  Reading: the entries the
+ * quantizer sends to zero (code magnitude 0: the deadzone set of the
+ * three-way split, and exact zeros) keep their own BF16 value; every other
+ * entry is dequantized from fp4q_quantize's code and block scale (one
+ * group).  The fallback is the element-sparse counterpart of the channel
+ * compensation; this call materialises the dequantized tensor with it:
+ *
+ *   y[r, c] = x[r, c]              where the code magnitude is 0
+ *   y[r, c] = (e2m1 * sb) * t      (NVFP4; FP32, the residual's value)
+ *   y[r, c] = e2m1 * 2^e           (MXFP4; exact)
+ *
+ *   x           bf16 [rows, cols], ldx as for fp4q_quantize
+ *   y           out f32 [rows, ldy] (16-byte aligned, ldy % 4 == 0)
+ *   n_fallback  out device int64 [1] (8-byte aligned) or NULL: the number
+ *               of non-zero entries that fell back (the deadzone count)
+ *   workspace   device scratch of fp4q_qdq_fallback_workspace_bytes()
+ *               bytes (NVFP4 only; 8-byte aligned), left undefined
+ * Errors as fp4q_quantize.
+ * ------------------------------------------------------------------------ */
+size_t fp4q_qdq_fallback_workspace_bytes(fp4q_format_t fmt, int64_t rows, int64_t cols);
+
+int fp4q_qdq_fallback(fp4q_format_t fmt, const uint16_t* x, int64_t rows, int64_t cols,
+                      int64_t ldx, float* y, int64_t ldy, int64_t* n_fallback, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
 /* fp4q_quantize for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
  * the same arguments, results and errors without the workspace, which is a

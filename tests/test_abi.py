@@ -155,6 +155,35 @@ def test_injected_launch_failure(L):
         L.fp4q_test_hook(0, 0)
 
 
+def test_qdq_fallback_rejects(L):
+    P = ctypes.c_void_p
+    L.fp4q_qdq_fallback.argtypes = [ctypes.c_int, P, ctypes.c_int64, ctypes.c_int64,
+                                    ctypes.c_int64, P, ctypes.c_int64, P, P, ctypes.c_size_t, P]
+    need = L.fp4q_qdq_fallback_workspace_bytes(0, 4, 64)
+    assert need > 0 and L.fp4q_qdq_fallback_workspace_bytes(1, 4, 64) == 0
+
+    def f(fmt=0, x=A, rows=4, cols=64, ldx=64, y=B, ldy=64, n=None, ws=A, wsb=need):
+        return L.fp4q_qdq_fallback(fmt, x, rows, cols, ldx, y, ldy, n, ws, wsb, None)
+    assert f(fmt=3) == INVALID
+    assert f(cols=40) == INVALID
+    assert f(fmt=1, cols=48) == INVALID            # MXFP4 blocks of 32
+    assert f(ldx=60) == INVALID
+    assert f(ldy=60) == INVALID
+    assert f(ldy=66) == INVALID                    # rows of float4 stores
+    assert f(y=ctypes.c_void_p(0x20008)) == INVALID
+    assert f(x=None) == INVALID
+    assert f(n=ctypes.c_void_p(0x30004)) == INVALID
+    assert f(ws=None) == WORKSPACE
+    assert f(wsb=need - 1) == WORKSPACE
+    assert f(rows=1 << 28) == UNSUPPORTED
+    assert f(rows=0, n=None) == 0                  # nothing to do, no HIP call
+    try:
+        assert L.fp4q_test_hook(1, 77) == 0
+        assert f() == HIP_ERR and L.fp4q_last_hip_error() == 77
+    finally:
+        L.fp4q_test_hook(0, 0)
+
+
 def test_quantize_status_rejects(L):
     need = L.fp4q_quantize_workspace_bytes(0, 4, 64, 1)
     st = ctypes.c_int32(0)
