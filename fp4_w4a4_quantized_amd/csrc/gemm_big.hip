@@ -39,6 +39,10 @@
 //    writes full 16-byte vectors.
 //  * Workgroup ids are remapped so that the workgroups resident on one XCD
 //    (ids congruent mod 8) share a compact block of tiles in L2.
+//  * Dense NVFP4 with the compensation weights streamed (gathered or
+//    prepared) runs on k_gemm_nv4 below: four waves of 128 x 128, which
+//    decode a third fewer fragments per MFMA and interleave the decode with
+//    their own MFMAs.
 // Rows past M / columns past N load a clamped valid row and are not stored.
 #include "fp4q_device.h"
 #include "fp4q_internal.h"
@@ -305,6 +309,13 @@ struct Frag {
   uint32_t sb[4][2];
 };
 
+struct FragT4 {
+  u32x4 a[4][2];
+  u32x4 b[4][2];
+  uint32_t sa[4][2];
+  uint32_t sb[4][2];
+};
+
 template <int FMT, bool SCALES>
 __device__ __forceinline__ void read_frags(const uint8_t* st, const uint8_t* bsrc, int wm, int wn,
                                            int lane, Frag& f) {
@@ -407,6 +418,78 @@ __device__ __forceinline__ void compute_comp(f32x16 (&acc)[2][4], const Frag& f)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8b, f.a[i][h]),
                                                             bv, acc[i][j], 0, 0, 0);
     }
+}
+
+// Epilogue of a 256 x 256 tile.  acc[i][j][e] is row 32 RI wm + 32 i +
+// 8 (e / 4) + 4 (l / 32) + e % 4, column 128 wn + 32 j + l % 32, scaled by
+// tw on the way out.  Interior tiles are staged through LDS (each wave its
+// own 32 x 64 region) and written as 16-byte vectors: rows of 256 bytes
+// (FP32) or 128 bytes (BF16); edge tiles store element by element.
+template <int RI>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[RI][4], const BigArgs& p,
+                                           int64_t r0, int64_t c0, int64_t rend, int wm, int wn,
+                                           int wave, int lane, float tw, uint8_t* sStage) {
+  const int hi = lane >> 5, l31 = lane & 31;
+  const int64_t rw = r0 + wm * 32 * RI, cw = c0 + wn * 128;
+  const bool interior = (r0 + GB_TILE <= rend) && (c0 + GB_TILE <= p.N);
+  const bool vec = interior && (p.ldy % 8) == 0 && (reinterpret_cast<uintptr_t>(p.y) & 15) == 0;
+  if (vec) {
+    lds_barrier();  // every wave is done with the last stage
+    float* ep = reinterpret_cast<float*>(sStage) + wave * 32 * GB_EP_STRIDE;
+#pragma unroll
+    for (int i = 0; i < RI; ++i)
+#pragma unroll
+      for (int jp = 0; jp < 2; ++jp) {
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            ep[(8 * (e >> 2) + 4 * hi + (e & 3)) * GB_EP_STRIDE + 32 * jj + l31] =
+                acc[i][2 * jp + jj][e] * tw;
+        const int64_t row0 = rw + 32 * i, col0 = cw + 64 * jp;
+        if (!p.y_bf16) {
+          float* y = reinterpret_cast<float*>(p.y);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const int rr = 4 * k + (lane >> 4), cc = 4 * (lane & 15);
+            const f32x4b v = *reinterpret_cast<const f32x4b*>(ep + rr * GB_EP_STRIDE + cc);
+            __builtin_nontemporal_store(
+                v, reinterpret_cast<f32x4b*>(y + (row0 + rr) * p.ldy + col0 + cc));
+          }
+        } else {
+          uint16_t* y = reinterpret_cast<uint16_t*>(p.y);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int rr = 8 * k + (lane >> 3), cc = 8 * (lane & 7);
+            const f32x4b v0 = *reinterpret_cast<const f32x4b*>(ep + rr * GB_EP_STRIDE + cc);
+            const f32x4b v1 = *reinterpret_cast<const f32x4b*>(ep + rr * GB_EP_STRIDE + cc + 4);
+            const u32x4 w = {f32_to_bf16_rne(v0.x) | (f32_to_bf16_rne(v0.y) << 16),
+                             f32_to_bf16_rne(v0.z) | (f32_to_bf16_rne(v0.w) << 16),
+                             f32_to_bf16_rne(v1.x) | (f32_to_bf16_rne(v1.y) << 16),
+                             f32_to_bf16_rne(v1.z) | (f32_to_bf16_rne(v1.w) << 16)};
+            __builtin_nontemporal_store(
+                w, reinterpret_cast<u32x4*>(y + (row0 + rr) * p.ldy + col0 + cc));
+          }
+        }
+      }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < RI; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t row = rw + 32 * i + 8 * (e >> 2) + 4 * hi + (e & 3);
+        const int64_t col = cw + 32 * j + l31;
+        if (row < rend && col < p.N) {
+          const float v = acc[i][j][e] * tw;
+          if (p.y_bf16)
+            reinterpret_cast<uint16_t*>(p.y)[row * p.ldy + col] = (uint16_t)f32_to_bf16_rne(v);
+          else
+            reinterpret_cast<float*>(p.y)[row * p.ldy + col] = v;
+        }
+      }
 }
 
 // XS: the compensation weights of up to GB_XS_MAX channels are taken from
@@ -659,72 +742,199 @@ __global__ void __launch_bounds__(GB_T, 1) k_gemm_big(BigArgs args) {
     }
   }
 
-  // ---- epilogue.  acc[i][j][e] is row 64 wm + 32 i + 8 (e / 4) + 4 (l / 32)
-  // + e % 4, column 128 wn + 32 j + l % 32.
-  const int hi = lane >> 5, l31 = lane & 31;
-  const int64_t rw = r0 + wm * 64, cw = c0 + wn * 128;
-  const int64_t rend = tc.rend;
-  const bool interior = (r0 + GB_TILE <= rend) && (c0 + GB_TILE <= p.N);
-  const bool vec = interior && (p.ldy % 8) == 0 && (reinterpret_cast<uintptr_t>(p.y) & 15) == 0;
-  if (vec) {
-    // Each wave stages 32 x 64 pieces (two blocks) in its own LDS region and
-    // writes 16-byte vectors: rows of 256 bytes (FP32) or 128 bytes (BF16).
-    lds_barrier();  // every wave is done with the last stage
-    float* ep = reinterpret_cast<float*>(sStage) + wave * 32 * GB_EP_STRIDE;
+  // ---- epilogue
+  store_tile<2>(acc, p, r0, c0, tc.rend, wm, wn, wave, lane, tw, sStage);
+}
+
+// ---- dense NVFP4, four waves ----------------------------------------------------
+//
+// The exact NVFP4 decode (v_cvt_scalef32_pk_f16_fp4 then v_pk_mul_f16 by the
+// block scale) costs about 6 clocks per element and wave on gfx950, as much
+// per stage as the f16 MFMAs, so the redundancy of decoding matters: a wave
+// owning 64 x 128 of the tile decodes 6 fragments per 8 MFMAs.  Here four
+// waves, one per SIMD, own 128 x 128 each (4 x 4 blocks of 32 x 32,
+// accumulators in the AGPRs): 8 fragments per 16 MFMAs.  A wave's VALU work
+// overlaps its own MFMAs when the two are interleaved, so the decode of
+// sub-step n + 1 is placed between the 16 MFMAs of sub-step n (scheduling
+// groups of one MFMA and a few VALU instructions).  Stages, direct-to-LDS
+// loads, the compensation stages and the epilogue are those of k_gemm_big.
+struct NvDec4 {
+  h16x8 a[4];
+  h16x8 b[4];
+};
+
+__device__ __forceinline__ void nv4_decode(const FragT4& f, const h16x2 (&sca)[4][2],
+                                           const h16x2 (&scb)[4][2], int n, NvDec4& d) {
+  const int h = n >> 2, st = n & 3, k = st >> 1;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
+    d.a[i] = nv_decode8(f.a[i][h][st], h16x2{sca[i][h][k], sca[i][h][k]});
 #pragma unroll
-      for (int jp = 0; jp < 2; ++jp) {
+  for (int j = 0; j < 4; ++j)
+    d.b[j] = nv_decode8(f.b[j][h][st], h16x2{scb[j][h][k], scb[j][h][k]});
+}
+
+// Half h of a stage's fragments (the 16-byte pieces and scale dwords).
+__device__ __forceinline__ void nv4_read_half(const uint8_t* st, int wm, int wn, int lane, int h,
+                                              FragT4& f) {
+  using SL = StageLayout<FP4Q_NVFP4>;
+  const uint32_t l32 =
+      (uint32_t)((((lane >> 4) & 1) * GB_GRP) + ((lane >> 5) * 16 + (lane & 15)) * 16);
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
+  for (int i = 0; i < 4; ++i)
+    f.a[i][h] = *reinterpret_cast<const u32x4*>(st + SL::A + (wm * 8 + 2 * i) * GB_GRP + l32 +
+                                                h * 512);
 #pragma unroll
-          for (int e = 0; e < 16; ++e)
-            ep[(8 * (e >> 2) + 4 * hi + (e & 3)) * GB_EP_STRIDE + 32 * jj + l31] =
-                acc[i][2 * jp + jj][e] * tw;
-        const int64_t row0 = rw + 32 * i, col0 = cw + 64 * jp;
-        if (!p.y_bf16) {
-          float* y = reinterpret_cast<float*>(p.y);
+  for (int j = 0; j < 4; ++j)
+    f.b[j][h] = *reinterpret_cast<const u32x4*>(st + SL::B + (wn * 8 + 2 * j) * GB_GRP + l32 +
+                                                h * 512);
 #pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            const int rr = 4 * k + (lane >> 4), cc = 4 * (lane & 15);
-            const f32x4b v = *reinterpret_cast<const f32x4b*>(ep + rr * GB_EP_STRIDE + cc);
-            __builtin_nontemporal_store(
-                v, reinterpret_cast<f32x4b*>(y + (row0 + rr) * p.ldy + col0 + cc));
-          }
-        } else {
-          uint16_t* y = reinterpret_cast<uint16_t*>(p.y);
+  for (int i = 0; i < 4; ++i)
+    f.sa[i][h] = *reinterpret_cast<const uint32_t*>(
+        st + SL::SA + (h * 256 + wm * 128 + 32 * i + (lane & 31)) * 4);
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const int rr = 8 * k + (lane >> 3), cc = 8 * (lane & 7);
-            const f32x4b v0 = *reinterpret_cast<const f32x4b*>(ep + rr * GB_EP_STRIDE + cc);
-            const f32x4b v1 = *reinterpret_cast<const f32x4b*>(ep + rr * GB_EP_STRIDE + cc + 4);
-            const u32x4 w = {f32_to_bf16_rne(v0.x) | (f32_to_bf16_rne(v0.y) << 16),
-                             f32_to_bf16_rne(v0.z) | (f32_to_bf16_rne(v0.w) << 16),
-                             f32_to_bf16_rne(v1.x) | (f32_to_bf16_rne(v1.y) << 16),
-                             f32_to_bf16_rne(v1.z) | (f32_to_bf16_rne(v1.w) << 16)};
-            __builtin_nontemporal_store(
-                w, reinterpret_cast<u32x4*>(y + (row0 + rr) * p.ldy + col0 + cc));
-          }
-        }
-      }
-    return;
+  for (int j = 0; j < 4; ++j)
+    f.sb[j][h] = *reinterpret_cast<const uint32_t*>(
+        st + SL::SB + (h * 256 + wn * 128 + 32 * j + (lane & 31)) * 4);
+}
+
+// The lane's two block scales of half h, as f16 (exact for every E4M3 code).
+__device__ __forceinline__ void nv4_scales(const FragT4& f, int h, int lane, h16x2 (&sca)[4][2],
+                                           h16x2 (&scb)[4][2]) {
+  const int hi = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    sca[i][h] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.sa[i][h] >> (16 * hi), 1.0f, false);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    scb[j][h] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.sb[j][h] >> (16 * hi), 1.0f, false);
+}
+
+// The 16 MFMAs of one sub-step, with the VALU instructions placed before
+// them in program order (the next decode) spread between them.
+__device__ __forceinline__ void nv4_mma(f32x16 (&acc)[4][4], const NvDec4& d) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(d.a[i], d.b[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
   }
+}
+
+__device__ __forceinline__ void comp4_stage(f32x16 (&acc)[4][4], const uint8_t* st,
+                                            const uint8_t* bsrc, int wm, int wn, int lane) {
+  using SL = StageLayout<FP4Q_NVFP4>;
+  const uint32_t l32 =
+      (uint32_t)((((lane >> 4) & 1) * GB_GRP) + ((lane >> 5) * 16 + (lane & 15)) * 16);
+  u32x4 a[4][2], b[4][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      a[i][h] = *reinterpret_cast<const u32x4*>(st + SL::A + (wm * 8 + 2 * i) * GB_GRP + l32 +
+                                                h * 512);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      b[j][h] = *reinterpret_cast<const u32x4*>(bsrc + (wn * 8 + 2 * j) * GB_GRP + l32 + h * 512);
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t row = rw + 32 * i + 8 * (e >> 2) + 4 * hi + (e & 3);
-        const int64_t col = cw + 32 * j + l31;
-        if (row < rend && col < p.N) {
-          const float v = acc[i][j][e] * tw;
-          if (p.y_bf16)
-            reinterpret_cast<uint16_t*>(p.y)[row * p.ldy + col] = (uint16_t)f32_to_bf16_rne(v);
-          else
-            reinterpret_cast<float*>(p.y)[row * p.ldy + col] = v;
-        }
-      }
+      for (int i = 0; i < 4; ++i)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8b, a[i][h]), __builtin_bit_cast(bf16x8b, b[j][h]), acc[i][j],
+            0, 0, 0);
+}
+
+template <bool TL>
+__global__ void __launch_bounds__(256, 1) k_gemm_nv4(BigArgs args) {
+  using SL = StageLayout<FP4Q_NVFP4>;
+  constexpr int L = 2 * SL::LOADS;  // each wave issues the share of two
+  __shared__ __attribute__((aligned(16))) uint8_t sStage[3 * SL::BYTES];
+  const BigArgs& p = args;
+  const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // XCD-aware tile order, grouped along M for L2 reuse (as k_gemm_big)
+  TileCtx tc;
+  {
+    const int T = p.mt * p.nt;
+    int tile = blockIdx.x;
+    if ((T & 7) == 0) tile = (blockIdx.x & 7) * (T >> 3) + (blockIdx.x >> 3);
+    const int gsize = GB_GROUP_M * p.nt;
+    const int gid = tile / gsize, first_m = gid * GB_GROUP_M;
+    const int gm = min(p.mt - first_m, GB_GROUP_M);
+    tc.r0 = (int64_t)(first_m + (tile % gsize) % gm) * GB_TILE;
+    tc.c0 = (int64_t)((tile % gsize) / gm) * GB_TILE;
+    tc.rend = p.M;
+    tc.bq = p.bq;
+    tc.bs = p.bs;
+    tc.bsel = p.bsel;
+  }
+  const int nk = p.nk, ns = p.nk + p.nc;
+  const float c = p.cts ? *p.cts : 1.0f;
+  const float tx = p.ats[0] / c, tw = p.bts[0] * c;
+  auto stage = [&](int s) __attribute__((always_inline)) { return sStage + (s % 3) * SL::BYTES; };
+  auto issue = [&](int s) __attribute__((always_inline)) {
+    issue_stage<FP4Q_NVFP4, TL, false>(p, s, 2 * wave, lane, tc, stage(s));
+    issue_stage<FP4Q_NVFP4, TL, false>(p, s, 2 * wave + 1, lane, tc, stage(s));
+  };
+  issue(0);
+  if (ns > 1) issue(1);
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  auto open = [&](int s) __attribute__((always_inline)) {
+    if (s + 1 < ns)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();
+    if (s + 2 < ns) issue(s + 2);
+  };
+  // stage s: wait for its loads, barrier (it landed everywhere; the buffer
+  // of stage s - 1 is free), issue stage s + 2, read it, then decode ahead
+  // of the MFMAs sub-step by sub-step
+  for (int s = 0; s < nk; ++s) {
+    open(s);
+    FragT4 f;
+    nv4_read_half(stage(s), wm, wn, lane, 0, f);
+    nv4_read_half(stage(s), wm, wn, lane, 1, f);
+    h16x2 sca[4][2], scb[4][2];
+    nv4_scales(f, 0, lane, sca, scb);
+    nv4_scales(f, 1, lane, sca, scb);
+    NvDec4 cur, nxt;
+    nv4_decode(f, sca, scb, 0, cur);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (n < 7) nv4_decode(f, sca, scb, n + 1, nxt);
+      nv4_mma(acc, cur);
+      cur = nxt;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // y = t_w (t_x main + comp): scale the main sum once, before R B_S
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] *= tx;
+  for (int s = nk; s < ns; ++s) {
+    open(s);
+    comp4_stage(acc, stage(s), stage(s) + SL::B, wm, wn, lane);
+  }
+  store_tile<4>(acc, p, tc.r0, tc.c0, tc.rend, wm, wn, wave, lane, tw, sStage);
 }
 
 // ---- B_S gather ---------------------------------------------------------------
@@ -811,6 +1021,11 @@ static void launch_big(const BigArgs& a, bool tiled, unsigned grid, hipStream_t 
       hipLaunchKernelGGL((k_gemm_big<FMT, false, true, true>), dim3(grid), dim3(GB_T), 0, stream, a);
     else
       hipLaunchKernelGGL((k_gemm_big<FMT, false, true, false>), dim3(grid), dim3(GB_T), 0, stream, a);
+  } else if (FMT == FP4Q_NVFP4 && !xs) {
+    if (tiled)
+      hipLaunchKernelGGL((k_gemm_nv4<true>), dim3(grid), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_gemm_nv4<false>), dim3(grid), dim3(256), 0, stream, a);
   } else {
     if (tiled && xs)
       hipLaunchKernelGGL((k_gemm_big<FMT, true, false, true>), dim3(grid), dim3(GB_T), 0, stream, a);
