@@ -71,6 +71,10 @@ def parse():
                    help="MoE gate_up input: quantize the routed copies per expert, or quantize "
                         "the token matrix once and permute its FP4 codes "
                         "(fp4q_permute_quantized, one tensor scale for all tokens)")
+    p.add_argument("--decode-datapath", choices=("separate", "fused"), default="separate",
+                   help="decode workload: quantize then GEMM (two launches), or the fused "
+                        "decode datapath (fp4q_gemm_decode_fused: the activations quantized "
+                        "inside the GEMM)")
     p.add_argument("--no-extras", action="store_true",
                    help="default line without the extra workloads")
     p.add_argument("--no-peaks", action="store_true",
@@ -330,6 +334,16 @@ def build_dense(name, cfg, data, args, dev):
 
     s.quant, s.gemm = quant, gemm
     s.fmt, s.M, s.K, s.x = fmt, M, K, x
+    # the fused decode datapath: BF16 activations in, the quantization inside
+    # the GEMM (NVFP4, M <= 64, K <= 2048, prepared compensation weights)
+    s.fused = None
+    if (fmt == fq.NVFP4 and M <= 64 and K <= 2048 and K % 128 == 0 and nS <= 64 and
+            (prepared or nS == 0) and not r4 and not online):
+        def fused(i):
+            w = wcopies[i % n_rot]
+            fq.gemm_decode_fused_into(fmt, layout, x, N, w["q"], w["scales"], w["tscale"], chan,
+                                      nS, w.get("comp_w"), ys[i % n_rot], ydt, N)
+        s.fused = fused
     s.flops = 2.0 * M * N * K
     r_bytes = (M * nS // 2 + M * nS // blk + (4 if fmt == fq.NVFP4 else 0)) if r4 else M * nS * 2
     # algorithmic bytes of the compensated GEMM: Xq + sx + R + S + Wq + sw + Y
@@ -354,6 +368,13 @@ def build_dense(name, cfg, data, args, dev):
             "residual": args.residual, "channels": args.channels,
             "comp_weights": "prepared" if prepared else "inkernel"}
     s.keep = (wcopies, ys, gws, qws, aq, asc, ats, ar, x, chan)
+    if args.decode_datapath == "fused":
+        if s.fused is None:
+            sys.exit("--decode-datapath fused needs an NVFP4 workload with M <= 64, K <= 2048, "
+                     "|S| <= 64 and the default variant")
+        s.quant = lambda: None
+        s.gemm = s.fused
+        s.wl["datapath"] = "fused"
     return s
 
 
@@ -536,6 +557,11 @@ def measure(name, args, stream, dev, variant_args=None):
     t_quant = timed(lambda i: s.quant(), reps)
     log(f"{name}: gemm {t_gemm * 1e6:.2f} us, quantize {t_quant * 1e6:.2f} us per launch")
     t_sel = timed(lambda i: s.select(), reps) if s.select else None
+    t_fused = None
+    if getattr(s, "fused", None) is not None and a.decode_datapath == "separate":
+        t_fused = timed(s.fused, reps)
+        log(f"{name}: fused decode datapath {t_fused * 1e6:.2f} us per launch "
+            f"(quantize + GEMM in one)")
     t_dec = None
     if s.x is not None:
         dec_out = torch.zeros(fq.binding.ERR_STATS_BYTES, dtype=torch.uint8, device=dev)
@@ -597,6 +623,9 @@ def measure(name, args, stream, dev, variant_args=None):
         rec["fallback_gbps"] = round(fb_bytes / t_fb / 1e9, 1)
         rec["fallback_frac_hbm"] = round(fb_bytes / t_fb / 1e9 / HBM_PEAK_GBS, 4)
         rec["fallback_entries"] = fb_count
+    if t_fused is not None:
+        rec["fused_decode_us"] = round(t_fused * 1e6, 3)
+        rec["fused_decode_tflops"] = round(s.flops / t_fused / 1e12, 2)
     if t_sel is not None:
         rec["select_us"] = round(t_sel * 1e6, 3)
         rec["select_gbps"] = round(s.select_bytes / t_sel / 1e9, 1)
@@ -664,7 +693,8 @@ def main():
     if args.workload is None and not args.no_extras:
         dflt = argparse.Namespace(**{**vars(args), "layout": "tiled", "out_dtype": "f32",
                                      "residual": "bf16", "channels": "fixed",
-                                     "comp_weights": "prepared", "moe_quant": "expert"})
+                                     "comp_weights": "prepared", "moe_quant": "expert",
+                                     "decode_datapath": "separate"})
         for n in EXTRAS:
             e = measure(n, args, stream, dev, variant_args=dflt)
             add_attainable(e, peaks)

@@ -119,6 +119,10 @@ def lib():
         L.fp4q_qdq_fallback_workspace_bytes.argtypes = [ctypes.c_int, i64, i64]
         L.fp4q_qdq_fallback.restype = ctypes.c_int
         L.fp4q_qdq_fallback.argtypes = [ctypes.c_int, P, i64, i64, i64, P, i64, P, P, sz, P]
+        L.fp4q_gemm_decode_fused.restype = ctypes.c_int
+        L.fp4q_gemm_decode_fused.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, P, i64,
+                                             P, P, P, P, i32, P, sz, P, ctypes.c_int, i64, P, P,
+                                             P, P, P]
         L.fp4q_quantize_noalloc.restype = ctypes.c_int
         L.fp4q_quantize_noalloc.argtypes = [ctypes.c_int, ctypes.c_int, P, i64, i64, i64, P, i32,
                                             P, i32, P, P, P, P, P]
@@ -338,6 +342,22 @@ def qdq_fallback(fmt, x, stream=None):
     ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=x.device) if wsb else None
     qdq_fallback_into(fmt, x, y, n, ws, stream)
     return y, n
+
+
+def gemm_decode_fused_into(fmt, layout, x, N, b_q, b_s, b_ts, chan_idx, n_chan, comp_w, y,
+                           y_dtype, ldy, a_q_out=None, a_s_out=None, a_ts_out=None,
+                           resid_out=None, stream=None):
+    """fp4q_gemm_decode_fused: Y from BF16 activations x [M, K] (quantized
+    inside the GEMM) and packed weights; optional outputs of the quantized
+    activations."""
+    M, K = x.shape
+    cw_bytes = 0 if comp_w is None else comp_w.numel() * comp_w.element_size()
+    _check("fp4q_gemm_decode_fused",
+           lib().fp4q_gemm_decode_fused(fmt, layout, M, N, K, _ptr(x), x.stride(0), _ptr(b_q),
+                                        _ptr(b_s), _ptr(b_ts), _ptr(chan_idx), n_chan,
+                                        _ptr(comp_w), cw_bytes, _ptr(y), y_dtype, ldy,
+                                        _ptr(a_q_out), _ptr(a_s_out), _ptr(a_ts_out),
+                                        _ptr(resid_out), _stream(stream)))
 
 
 def quantize_noalloc_into(fmt, layout, x, group_offsets, num_groups, chan_idx, n_chan, q, scales,

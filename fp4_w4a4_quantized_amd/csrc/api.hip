@@ -321,6 +321,46 @@ int fp4q_gemm_prepared(fp4q_format_t fmt, fp4q_layout_t layout, int64_t M, int64
   return check_launch();
 }
 
+int fp4q_gemm_decode_fused(fp4q_format_t fmt, fp4q_layout_t layout, int64_t M, int64_t N,
+                           int64_t K, const uint16_t* x, int64_t ldx, const uint8_t* b_q,
+                           const uint8_t* b_s, const float* b_ts, const int32_t* chan_idx,
+                           int32_t n_chan, const uint8_t* comp_w, size_t comp_w_bytes, void* y,
+                           fp4q_dtype_t y_dtype, int64_t ldy, uint8_t* a_q_out,
+                           uint8_t* a_s_out, float* a_ts_out, uint16_t* resid_out,
+                           void* stream) {
+  if (!fmt_ok(fmt) || !layout_ok(layout)) return FP4Q_ERR_INVALID;
+  if (y_dtype != FP4Q_OUT_F32 && y_dtype != FP4Q_OUT_BF16) return FP4Q_ERR_INVALID;
+  if (M < 0 || N < 0 || K <= 0 || K % 16 != 0 || ldx < K || ldx % 8 != 0 || ldy < N)
+    return FP4Q_ERR_INVALID;
+  if (n_chan < 0 || n_chan > K || (n_chan > 0) != (chan_idx != nullptr)) return FP4Q_ERR_INVALID;
+  if (!b_ts) return FP4Q_ERR_INVALID;
+  const bool outs = a_q_out != nullptr;
+  if (outs != (a_s_out != nullptr) || outs != (a_ts_out != nullptr) ||
+      (outs && n_chan > 0) != (resid_out != nullptr))
+    return FP4Q_ERR_INVALID;
+  if (M > 0 && N > 0) {
+    if (!x || !b_q || !b_s || !y) return FP4Q_ERR_INVALID;
+    if (!aligned(x, 16) || !aligned(b_q, 16) || !aligned(b_s, 8)) return FP4Q_ERR_INVALID;
+    if (outs && (!aligned(a_q_out, 16) || !aligned(a_s_out, 2))) return FP4Q_ERR_INVALID;
+  }
+  if (fmt != FP4Q_NVFP4 || K % 128 != 0 || !fp4q::decode_fused_eligible(M > 0 ? M : 1, K, n_chan))
+    return FP4Q_ERR_UNSUPPORTED;
+  if ((N + 47) / 48 > (int64_t)INT32_MAX) return FP4Q_ERR_UNSUPPORTED;
+  const bool work = M > 0 && N > 0;
+  if (work && n_chan > 0 &&
+      (!comp_w || !aligned(comp_w, 16) ||
+       comp_w_bytes < fp4q_comp_weights_bytes(fmt, layout, N, K, n_chan)))
+    return FP4Q_ERR_WORKSPACE;
+  if (!work) return FP4Q_OK;
+  if (injected_failure()) return FP4Q_ERR_HIP;
+  clear_error();
+  fp4q::launch_gemm_decode_fused(layout == FP4Q_LAYOUT_TILED, M, N, K, x, ldx, b_q, b_s, b_ts,
+                                 chan_idx, n_chan, n_chan > 0 ? comp_w : nullptr, y,
+                                 y_dtype == FP4Q_OUT_BF16, ldy, a_q_out, a_s_out, a_ts_out,
+                                 resid_out, static_cast<hipStream_t>(stream));
+  return check_launch();
+}
+
 static size_t deq_resid_bytes(int64_t M, int32_t n_chan) {
   return (size_t)((M * n_chan * 2 + 255) / 256 * 256);
 }

@@ -89,6 +89,16 @@ int launch_gemm_skinny(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, con
                        const float* cts, const uint8_t* bsel, void* y, int y_bf16, int64_t ldy,
                        hipStream_t stream);
 
+// Fused decode datapath: the activations quantized (NVFP4) inside the decode
+// GEMM.  M <= 64, K <= 2048, nS <= 64; bsel = prepared compensation weights
+// (null iff nS == 0); q_out etc. optional (all null or all set).
+bool decode_fused_eligible(int64_t M, int64_t K, int nS);
+int launch_gemm_decode_fused(bool tiled, int64_t M, int64_t N, int64_t K, const uint16_t* x,
+                             int64_t ldx, const uint8_t* bq, const uint8_t* bs, const float* bts,
+                             const int32_t* chan, int nS, const uint8_t* bsel, void* y, int y_bf16,
+                             int64_t ldy, uint8_t* q_out, uint8_t* s_out, float* ts_out,
+                             uint16_t* r_out, hipStream_t stream);
+
 // Online channel selection: scores, top-k pick, residual emission.
 size_t select_workspace_bytes(int64_t rows, int64_t cols);
 void launch_select(int fmt, bool tiled, const uint16_t* x, int64_t rows, int64_t cols,

@@ -449,6 +449,388 @@ __global__ void __launch_bounds__(SK_T, 1) k_gemm_skinny(SkinnyArgs p) {
   }
 }
 
+// ---- the fused decode datapath --------------------------------------------------
+//
+// FourSight abstract: a fused kernel with its own decode datapath.  For
+// decode shapes the activation quantization is a separate launch of about
+// the GEMM's own length, so here it moves into the GEMM: the activations
+// arrive as BF16 and each workgroup quantizes them itself.  With K <= 2048
+// (16 steps of 128) each of the 8 waves owns at most the two K steps it
+// multiplies, wave and wave + 8; it loads their BF16 values (64 rows x 256
+// columns, 32 KB per wave) straight into registers while the weight loads
+// are in flight.  The 8 waves together hold the whole tensor, so the
+// tensor amax is one LDS reduction -- no grid barrier, no second read.
+// Each lane then holds whole 16-element blocks (rows 16a + lr, elements
+// 32q .. 32q + 31 of a step: blocks 2q and 2q + 1), so it forms block
+// scales, quotients and codes with the quantizer's own operations and
+// leaves the codes in exactly the fragment registers the MFMAs take; the
+// residual of the selected channels goes to LDS for the compensation term.
+// Workgroup 0 can also write the quantized activations out (codes, scales,
+// tensor scale, residual; row-major), for checking.  NVFP4, prepared
+// compensation weights (or none).
+struct FusedArgs {
+  int64_t M, N, K;
+  const uint16_t* x;
+  int64_t ldx;
+  const uint8_t* bq;
+  const uint8_t* bs;
+  const float* bts;
+  const int32_t* chan;
+  int nS;
+  const uint8_t* bsel;
+  void* y;
+  int y_bf16;
+  int64_t ldy;
+  uint8_t* q_out;     // optional: [M, K/2] row-major
+  uint8_t* s_out;     // optional: [M, K/16]
+  float* ts_out;      // optional: [1]
+  uint16_t* r_out;    // optional: [M, nS]
+};
+
+// The weights of one K step (load_step without the activations).
+template <bool TL>
+__device__ __forceinline__ void load_w_step(const FusedArgs& p, int kt, int lane, int64_t col0,
+                                            int64_t wso, Step& s) {
+  const int64_t K = p.K;
+  if (TL) {
+    const int64_t KB = K >> 7;
+    const int64_t gN = ((p.N + 15) >> 4) - 1;
+#pragma unroll
+    for (int g = 0; g < SK_CG; ++g) {
+      int64_t grp = (col0 >> 4) + g;
+      grp = grp < gN ? grp : gN;
+      s.w[g] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(p.bq + ((grp * KB + kt) << 10) + lane * 16));
+    }
+    const uint8_t* ws = p.bs + wso + (int64_t)kt * (8 * 64);
+    s.wsc = u32x2{*reinterpret_cast<const uint32_t*>(ws),
+                  *reinterpret_cast<const uint32_t*>(ws + 256)};
+    return;
+  }
+  const int64_t K2 = K >> 1, KS = K / 16;
+  const int q = lane >> 4, lr = lane & 15;
+#pragma unroll
+  for (int g = 0; g < SK_CG; ++g) {
+    int64_t row = col0 + 16 * g + lr;
+    row = row < p.N ? row : p.N - 1;
+    s.w[g] = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(p.bq + row * K2 + (int64_t)kt * 64 + q * 16));
+  }
+  int64_t wrow = col0 + (lane < SK_COLS ? lane : SK_COLS - 1);
+  wrow = wrow < p.N ? wrow : p.N - 1;
+  s.wsc = *reinterpret_cast<const u32x2*>(p.bs + wrow * KS + (int64_t)kt * 8);
+}
+
+// One lane's activations of one K step: rows 16a + lr (a = 0..3, clamped to
+// M - 1), elements 32q .. 32q + 31 of the step, as BF16 pairs.
+struct XSlab {
+  u32x4 v[4][4];  // [a][16-byte piece]
+};
+
+__device__ __forceinline__ void load_x_step(const FusedArgs& p, int kt, int lane, XSlab& x) {
+  const int q = lane >> 4, lr = lane & 15;
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    int64_t row = 16 * a + lr;
+    row = row < p.M ? row : p.M - 1;
+    // plain (cached) loads: every workgroup reads the same activations, and
+    // the four loads of a lane revisit the same cache lines
+    const u32x4* src = reinterpret_cast<const u32x4*>(p.x + row * p.ldx + (int64_t)kt * 128 + 32 * q);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) x.v[a][c] = src[c];
+  }
+}
+
+__device__ __forceinline__ uint32_t slab_absmax(const XSlab& x) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const u32x4 v = x.v[a][c];
+      m = max(m, max(max(v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu), max(v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu)));
+      m = max(m, max(max(v.z & 0x7FFFu, (v.z >> 16) & 0x7FFFu), max(v.w & 0x7FFFu, (v.w >> 16) & 0x7FFFu)));
+    }
+  return m;
+}
+
+// NVFP4 codes of one 16-element block held by one lane (two 16-byte pieces),
+// with the quantizer's operations: block amax, (amax / 6) / t to E4M3
+// (nearest even, saturating), d = sb t, the correctly rounded quotient x / d
+// (reciprocal and two FMA corrections) and the hardware E2M1 conversion.
+__device__ __forceinline__ void nv_block16(u32x4 p0, u32x4 p1, float t, uint32_t& c0,
+                                           uint32_t& c1, uint32_t& sc, float& sb) {
+  const uint32_t w[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+  uint32_t am = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) am = max(am, max(w[k] & 0x7FFFu, (w[k] >> 16) & 0x7FFFu));
+  float xs[16];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    xs[2 * k] = __uint_as_float(w[k] << 16);
+    xs[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+  }
+  const float amax = bf16_to_f32(am);
+  const float vs = (amax / 6.0f) / t;
+  sc = e4m3_encode(vs);
+  sb = e4m3_value(sc);
+  const float d = sb * t;
+  float qv[16];
+  if (d >= 0x1p-96f) {
+    const float yr = 1.0f / d;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) qv[k] = div_rn(xs[k], d, yr);
+  } else if (d > 0.0f) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) qv[k] = xs[k] / d;
+  } else {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) qv[k] = xs[k] * 0.0f;  // signed zero: magnitude code 0
+  }
+  float lo[8], hi[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    lo[k] = qv[k];
+    hi[k] = qv[8 + k];
+  }
+  c0 = e2m1_pack8(lo);
+  c1 = e2m1_pack8(hi);
+}
+
+template <bool TL>
+__global__ void __launch_bounds__(SK_T, 1) k_gemm_decode_fused(FusedArgs p) {
+  using L = SlotLayout<FP4Q_NVFP4>;
+  __shared__ __attribute__((aligned(16))) v4f32s red[SK_WAVES * 4 * SK_CG * 64];   // 96 KB
+  __shared__ __attribute__((aligned(16))) uint8_t sScale[SK_WAVES * 2 * L::BYTES];
+  __shared__ __attribute__((aligned(16))) uint16_t sR[SK_M * SK_SRS];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[SK_COLS * SK_SRS];
+  __shared__ uint32_t sMax[SK_WAVES];
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int q = lane >> 4, lr = lane & 15;
+  const int64_t col0 = (int64_t)blockIdx.x * SK_COLS;
+  const int nk = (int)(p.K / 128);
+  const int nS = p.nS;
+  const float tw = *p.bts;
+  const int my_ch_raw = *(nS > 0 ? p.chan + (lane < nS ? lane : nS - 1)
+                                 : reinterpret_cast<const int32_t*>(p.bts));
+  const int my_ch = (nS > 0 && lane < nS) ? my_ch_raw : -1;
+
+  // prepared compensation weights into sB (as k_gemm_skinny with PB)
+  const int nc = (nS + 31) >> 5;
+  const bool pb_on = nS > 0 && t < SK_CG * 64 * nc;
+  int pb_g = 0, pb_c = 0;
+  u32x4 pbv = u32x4{0u, 0u, 0u, 0u};
+  {
+    const int blk = pb_on ? t >> 6 : 0;
+    pb_g = blk / (nc > 0 ? nc : 1);
+    pb_c = blk - pb_g * nc;
+    const int64_t glast = ((p.N + 15) >> 4) - 1;
+    int64_t gi = (col0 >> 4) + pb_g;
+    gi = gi < glast ? gi : glast;
+    if (pb_on)
+      pbv = *reinterpret_cast<const u32x4*>(p.bsel + ((gi * nc + pb_c) << 10) + (t & 63) * 16);
+  }
+  int64_t wso = 0;
+  if (TL) {
+    int64_t wrow = col0 + (lane < SK_COLS ? lane : SK_COLS - 1);
+    const int64_t wlast = ((p.N + 63) & ~(int64_t)63) - 1;
+    wrow = wrow < wlast ? wrow : wlast;
+    wso = (wrow >> 6) * (p.K >> 7) * (8 * 64) + (wrow & 63) * 4;
+  }
+  // the first step's weights, then this wave's activations (steps wave and
+  // wave + 8); the second step's weights follow once the first step's
+  // activations are quantized (their registers are then free)
+  const int k0 = wave < nk ? wave : nk - 1;
+  const int k1 = wave + SK_WAVES < nk ? wave + SK_WAVES : nk - 1;
+  Step s0, s1;
+  load_w_step<TL>(p, k0, lane, col0, wso, s0);
+  XSlab x0, x1;
+  load_x_step(p, k0, lane, x0);
+  load_x_step(p, k1, lane, x1);
+  if (pb_on) {
+    const int u = (t & 63) >> 4, r = t & 15;
+    uint16_t* dst = sB + (16 * pb_g + r) * SK_SRS + 32 * pb_c + 8 * u;
+    reinterpret_cast<u32x2*>(dst)[0] = u32x2{pbv.x, pbv.y};
+    reinterpret_cast<u32x2*>(dst)[1] = u32x2{pbv.z, pbv.w};
+  }
+
+  // tensor amax: the 8 waves together hold every step of every row
+  uint32_t m = max(slab_absmax(x0), slab_absmax(x1));
+  for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+  if (lane == 0) sMax[wave] = m;
+  __syncthreads();
+  m = 0;
+#pragma unroll
+  for (int w2 = 0; w2 < SK_WAVES; ++w2) m = max(m, sMax[w2]);
+  const float tx = nv_tensor_scale(bf16_to_f32(m));
+  const bool writer = blockIdx.x == 0 && p.q_out != nullptr;
+  if (writer && t == 0) *p.ts_out = tx;
+
+  // quantize this wave's steps into the fragment registers; the residual of
+  // the selected channels (R = bf16(x - (e2m1 sb) t), as the quantizer)
+  // goes to sR, and workgroup 0 may write codes and scales out
+  uint32_t xsc[2][4];
+  auto quant_step = [&](const XSlab& x, int kt, bool valid, Step& s, uint32_t (&xs)[4])
+      __attribute__((always_inline)) {
+    const uint64_t mch = __ballot(my_ch >= 0 && (my_ch >> 7) == kt);
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      uint32_t c[4], sc[2];
+      float sbv[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        nv_block16(x.v[a][2 * b], x.v[a][2 * b + 1], tx, c[2 * b], c[2 * b + 1], sc[b], sbv[b]);
+      s.x[a] = u32x4{c[0], c[1], c[2], c[3]};
+      xs[a] = sc[0] | (sc[1] << 8);
+      const int64_t row = 16 * a + lr;
+      if (writer && valid && row < p.M) {
+        *reinterpret_cast<u32x4*>(p.q_out + row * (p.K >> 1) + (int64_t)kt * 64 + 16 * q) = s.x[a];
+        *reinterpret_cast<uint16_t*>(p.s_out + row * (p.K >> 4) + (int64_t)kt * 8 + 2 * q) =
+            (uint16_t)xs[a];
+      }
+      if (valid && mch) {
+        // channels of this step in the lane's 32 columns
+        for (uint64_t mm = mch; mm; mm &= mm - 1) {
+          const int j = __builtin_ctzll(mm);
+          const int cc = __builtin_amdgcn_ds_bpermute(j << 2, my_ch) & 127;
+          if ((cc >> 5) != q) continue;
+          const int e = cc & 31, b = e >> 4, k = e & 15;
+          const uint32_t code = (c[2 * b + (k >> 3)] >> (4 * (k & 7))) & 15u;
+          float pv = (e2m1_mag_value(code) * sbv[b]) * tx;
+          if (code & 8u) pv = -pv;
+          // element e of the lane's 32: piece e / 8, dword (e % 8) / 2, half e % 2
+          const u32x4 pc = x.v[a][e >> 3];
+          const int wi = (e & 7) >> 1;
+          const uint32_t wd = wi == 0 ? pc.x : wi == 1 ? pc.y : wi == 2 ? pc.z : pc.w;
+          const float xe = __uint_as_float((e & 1) ? (wd & 0xFFFF0000u) : (wd << 16));
+          if (row < p.M) sR[row * SK_SRS + j] = (uint16_t)f32_to_bf16_rne(xe - pv);
+        }
+      }
+    }
+  };
+  quant_step(x0, k0, wave < nk, s0, xsc[0]);
+  load_w_step<TL>(p, k1, lane, col0, wso, s1);
+  quant_step(x1, k1, wave + SK_WAVES < nk, s1, xsc[1]);
+
+  v4f32s acc[4][SK_CG];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int g = 0; g < SK_CG; ++g) acc[a][g] = v4f32s{0.f, 0.f, 0.f, 0.f};
+
+  // multiply: as process_step (NVFP4), the activation scales already in the
+  // lane's own registers
+  uint8_t* slot0 = sScale + (wave * 2 + 0) * L::BYTES;
+  uint8_t* slot1 = sScale + (wave * 2 + 1) * L::BYTES;
+  auto mult = [&](const Step& st, const uint32_t (&xs)[4], uint8_t* slot)
+      __attribute__((always_inline)) {
+    if (lane < SK_COLS) *reinterpret_cast<u32x2*>(slot + lane * 8) = st.wsc;
+    h2s wsp[SK_CG], xsp[4];
+#pragma unroll
+    for (int g = 0; g < SK_CG; ++g)
+      wsp[g] = sk_scales2((uint32_t)*reinterpret_cast<const uint16_t*>(slot + (16 * g + lr) * 8 + 2 * q));
+#pragma unroll
+    for (int a = 0; a < 4; ++a) xsp[a] = sk_scales2(xs[a]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      h8s db[SK_CG];
+#pragma unroll
+      for (int g = 0; g < SK_CG; ++g) db[g] = sk_decode8(st.w[g][s], (s >> 1) ? wsp[g].yy : wsp[g].xx);
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const h8s da = sk_decode8(st.x[a][s], (s >> 1) ? xsp[a].yy : xsp[a].xx);
+#pragma unroll
+        for (int g = 0; g < SK_CG; ++g)
+          acc[a][g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(da, db[g], acc[a][g], 0, 0, 0);
+      }
+    }
+  };
+  if (wave < nk) mult(s0, xsc[0], slot0);
+  if (wave + SK_WAVES < nk) mult(s1, xsc[1], slot1);
+
+  // ---- K-partial sums meet in LDS (sR, sB complete too); wave a (< 4) then
+  // owns rows 16a .. 16a+15
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int g = 0; g < SK_CG; ++g) red[((wave * 4 + a) * SK_CG + g) * 64 + lane] = acc[a][g];
+  __syncthreads();
+  if (writer && nS > 0) {
+    for (int i = t; i < (int)p.M * nS; i += SK_T) {
+      const int row = i / nS, j = i - row * nS;
+      p.r_out[i] = sR[row * SK_SRS + j];
+    }
+  }
+  if (wave >= 4) return;
+  v4f32s out[SK_CG];
+#pragma unroll
+  for (int g = 0; g < SK_CG; ++g) {
+    out[g] = red[((0 * 4 + wave) * SK_CG + g) * 64 + lane];
+#pragma unroll
+    for (int w2 = 1; w2 < SK_WAVES; ++w2) out[g] += red[((w2 * 4 + wave) * SK_CG + g) * 64 + lane];
+  }
+  if (nS > 0) {
+    v4f32s comp[SK_CG];
+#pragma unroll
+    for (int g = 0; g < SK_CG; ++g) comp[g] = v4f32s{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < SK_MAXS / 16; ++c) {
+      const int jq = 16 * c + 4 * q;
+      const u32x2 m2 = u32x2{(jq + 0 < nS ? 0xFFFFu : 0u) | (jq + 1 < nS ? 0xFFFF0000u : 0u),
+                             (jq + 2 < nS ? 0xFFFFu : 0u) | (jq + 3 < nS ? 0xFFFF0000u : 0u)};
+      const s4s ra = __builtin_bit_cast(
+          s4s, *reinterpret_cast<const u32x2*>(sR + (16 * wave + lr) * SK_SRS + jq) & m2);
+#pragma unroll
+      for (int g = 0; g < SK_CG; ++g) {
+        const s4s rb = __builtin_bit_cast(
+            s4s, *reinterpret_cast<const u32x2*>(sB + (16 * g + lr) * SK_SRS + jq) & m2);
+        comp[g] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ra, rb, comp[g], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < SK_CG; ++g) out[g] = out[g] * tx + comp[g];
+  } else {
+#pragma unroll
+    for (int g = 0; g < SK_CG; ++g) out[g] *= tx;
+  }
+#pragma unroll
+  for (int g = 0; g < SK_CG; ++g) {
+    const int64_t col = col0 + 16 * g + lr;
+    if (col >= p.N) continue;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t row = 16 * wave + 4 * q + e;
+      if (row >= p.M) continue;
+      const float v = out[g][e] * tw;
+      if (p.y_bf16)
+        reinterpret_cast<uint16_t*>(p.y)[row * p.ldy + col] = (uint16_t)f32_to_bf16_rne(v);
+      else
+        reinterpret_cast<float*>(p.y)[row * p.ldy + col] = v;
+    }
+  }
+}
+
+bool decode_fused_eligible(int64_t M, int64_t K, int nS) {
+  return M >= 1 && M <= SK_M && K >= 128 && K % 128 == 0 && K <= 128 * 2 * SK_WAVES &&
+         nS >= 0 && nS <= SK_MAXS;
+}
+
+int launch_gemm_decode_fused(bool tiled, int64_t M, int64_t N, int64_t K, const uint16_t* x,
+                             int64_t ldx, const uint8_t* bq, const uint8_t* bs, const float* bts,
+                             const int32_t* chan, int nS, const uint8_t* bsel, void* y, int y_bf16,
+                             int64_t ldy, uint8_t* q_out, uint8_t* s_out, float* ts_out,
+                             uint16_t* r_out, hipStream_t stream) {
+  FusedArgs a{M, N, K, x, ldx, bq, bs, bts, chan, nS, bsel, y, y_bf16, ldy, q_out, s_out, ts_out,
+              r_out};
+  dim3 grid((unsigned)((N + SK_COLS - 1) / SK_COLS));
+  if (tiled)
+    hipLaunchKernelGGL((k_gemm_decode_fused<true>), grid, dim3(SK_T), 0, stream, a);
+  else
+    hipLaunchKernelGGL((k_gemm_decode_fused<false>), grid, dim3(SK_T), 0, stream, a);
+  return 0;
+}
+
 bool skinny_gemm_eligible(int64_t M, int64_t N, int64_t K, int nS) {
   // the residual rows are read as 16-byte pieces of 8 entries (R itself is
   // 16-byte aligned)

@@ -338,6 +338,48 @@ int fp4q_grouped_gemm_prepared(fp4q_format_t fmt, int64_t total_rows, int64_t N,
                                fp4q_dtype_t y_dtype, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Fused decode datapath (FourSight abstract: a fused kernel with separate
+ * prefill and decode datapaths).  For decode shapes the activation
+ * quantization moves into the GEMM: fp4q_gemm_prepared's product, with the
+ * activations given as BF16 and quantized inside the kernel exactly as
+ * fp4q_quantize(NVFP4, one group, channel list chan_idx) would:
+ *
+ *   Y = deq(Q(x)) deq(B)^T + R B_S,  R = the residual of x on chan_idx
+ *
+ *   x          bf16 [M, K], row stride ldx (ldx >= K, ldx % 8 == 0, 16-byte
+ *              aligned)
+ *   b_q, b_s, b_ts, layout   packed W^T as for fp4q_gemm (the layout is the
+ *              weights'; nothing activation-side is packed)
+ *   chan_idx, n_chan, comp_w, comp_w_bytes   as for fp4q_gemm_prepared
+ *              (comp_w from fp4q_comp_weights of the same weights; unused
+ *              when n_chan == 0)
+ *   y, y_dtype, ldy   as for fp4q_gemm
+ *   a_q_out, a_s_out, a_ts_out, resid_out   optional (all NULL, or all set;
+ *              resid_out only with channels): the quantized activations,
+ *              row-major [M, K/2] codes (16-byte aligned), [M, K/16]
+ *              scales, the tensor scale, bf16 [M, n_chan] residual -- the
+ *              values the kernel multiplied, for checking against
+ *              fp4q_quantize
+ *
+ * NVFP4 only; M <= 64, K a multiple of 128 up to 2048, n_chan <= 64
+ * (FP4Q_ERR_UNSUPPORTED otherwise).  Every workgroup reads all of x (at
+ * most 256 KB, from the caches); each of its 8 waves quantizes the two K
+ * steps it multiplies, and the tensor maximum is reduced inside the
+ * workgroup, so no launch or grid-wide exchange precedes the GEMM.  The
+ * price is that every workgroup quantizes all of x: on MI355X at
+ * 64 x 2048 x 11008 this call takes about 56 us against about 16 us for
+ * fp4q_quantize followed by fp4q_gemm_prepared, so the two-launch path is
+ * the faster one there.
+ * ------------------------------------------------------------------------ */
+int fp4q_gemm_decode_fused(fp4q_format_t fmt, fp4q_layout_t layout, int64_t M, int64_t N,
+                           int64_t K, const uint16_t* x, int64_t ldx, const uint8_t* b_q,
+                           const uint8_t* b_s, const float* b_ts, const int32_t* chan_idx,
+                           int32_t n_chan, const uint8_t* comp_w, size_t comp_w_bytes, void* y,
+                           fp4q_dtype_t y_dtype, int64_t ldy, uint8_t* a_q_out,
+                           uint8_t* a_s_out, float* a_ts_out, uint16_t* resid_out,
+                           void* stream);
+
+/* ------------------------------------------------------------------------
  * Compensated W4A4 GEMM with a second-pass FP4 residual.  Explainer of the
  * QUADS paper, section 2.2 B: the high-residual channels are quantized a
  * second time and that correction term is added to the quantized output.

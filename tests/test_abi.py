@@ -184,6 +184,38 @@ def test_qdq_fallback_rejects(L):
         L.fp4q_test_hook(0, 0)
 
 
+def test_gemm_decode_fused_rejects(L):
+    P, i64 = ctypes.c_void_p, ctypes.c_int64
+    L.fp4q_gemm_decode_fused.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, P, i64, P, P,
+                                         P, P, ctypes.c_int32, P, ctypes.c_size_t, P, ctypes.c_int,
+                                         i64, P, P, P, P, P]
+
+    def f(fmt=0, layout=1, M=64, N=256, K=2048, x=A, ldx=2048, bq=B, bs=B, bts=B, chan=None,
+          nS=0, cw=None, cwb=0, y=A, dt=0, ldy=256, qo=None, so=None, tso=None, ro=None):
+        return L.fp4q_gemm_decode_fused(fmt, layout, M, N, K, x, ldx, bq, bs, bts, chan, nS, cw,
+                                        cwb, y, dt, ldy, qo, so, tso, ro, None)
+    assert f(fmt=2) == INVALID
+    assert f(ldx=2000) == INVALID
+    assert f(ldy=100) == INVALID
+    assert f(bts=None) == INVALID
+    assert f(nS=4, chan=None) == INVALID
+    assert f(qo=B) == INVALID                     # optional outputs all or none
+    assert f(x=ctypes.c_void_p(0x10008)) == INVALID
+    assert f(fmt=1) == UNSUPPORTED                # NVFP4 only
+    assert f(M=65) == UNSUPPORTED
+    assert f(K=2176, ldx=2176) == UNSUPPORTED     # at most 16 K steps
+    assert f(K=2000, ldx=2000) == UNSUPPORTED
+    assert f(nS=65, chan=A) == UNSUPPORTED
+    assert f(nS=8, chan=A) == WORKSPACE           # prepared weights missing
+    assert f(nS=8, chan=A, cw=A, cwb=16) == WORKSPACE
+    assert f(M=0) == 0                            # nothing to do, no HIP call
+    try:
+        assert L.fp4q_test_hook(1, 55) == 0
+        assert f() == HIP_ERR and L.fp4q_last_hip_error() == 55
+    finally:
+        L.fp4q_test_hook(0, 0)
+
+
 def test_quantize_status_rejects(L):
     need = L.fp4q_quantize_workspace_bytes(0, 4, 64, 1)
     st = ctypes.c_int32(0)
