@@ -67,10 +67,12 @@ def parse():
                         "compensation weights B[n, S_j] made once per weight copy "
                         "(fp4q_comp_weights, fp4q_gemm_prepared), or extract them from the "
                         "packed weights in every call (fp4q_gemm)")
-    p.add_argument("--moe-quant", choices=("expert", "token"), default="expert",
-                   help="MoE gate_up input: quantize the routed copies per expert, or quantize "
+    p.add_argument("--moe-quant", choices=("expert", "token", "token-gather"), default="expert",
+                   help="MoE gate_up input: quantize the routed copies per expert; or quantize "
                         "the token matrix once and permute its FP4 codes "
-                        "(fp4q_permute_quantized, one tensor scale for all tokens)")
+                        "(fp4q_permute_quantized, one tensor scale for all tokens); or quantize "
+                        "it once and let the grouped GEMM gather each routed row's codes "
+                        "(fp4q_grouped_gemm_gather; the permute writes only the residual)")
     p.add_argument("--decode-datapath", choices=("separate", "fused"), default="separate",
                    help="decode workload: quantize then GEMM (two launches), or the fused "
                         "decode datapath (fp4q_gemm_decode_fused: the activations quantized "
@@ -394,7 +396,10 @@ def build_moe(name, cfg, data, args, dev):
         a = np.ascontiguousarray(a)
         return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
 
-    moe_tok = args.moe_quant == "token"
+    moe_tok = args.moe_quant in ("token", "token-gather")
+    gather = args.moe_quant == "token-gather"
+    if gather and not (args.comp_weights == "prepared" or cfg["n_s"] == 0):
+        sys.exit("--moe-quant token-gather streams the prepared compensation weights")
     off = up(data["offsets"])
     G = int(data["offsets"].size - 1)
     rows = int(data["offsets"][-1])
@@ -442,8 +447,9 @@ def build_moe(name, cfg, data, args, dev):
         if moe_tok:
             b = bufs["gu"]
             fq.quantize_into(fmt, fq.ROWMAJOR, xt, None, 1, None, 0, tq, tsc, tts, None, tws)
-            fq.permute_quantized_into(fmt, xt, tq, tsc, tts, src, off, G, cg, nS, b["q"],
-                                      b["s"], b["t"], b["r"])
+            fq.permute_quantized_into(fmt, xt, tq, tsc, tts, src, off, G, cg, nS,
+                                      None if gather else b["q"], None if gather else b["s"],
+                                      b["t"], b["r"])
         for tag, xin, ch in ((("dn", xd, cd),) if moe_tok else
                              (("gu", xg, cg), ("dn", xd, cd))):
             b = bufs[tag]
@@ -457,7 +463,11 @@ def build_moe(name, cfg, data, args, dev):
     def gemm(i):
         for tag, w, y, n, k, ch in (("gu", wgu, ygu, I2, H, cg), ("dn", wdn, ydn, H, I, cd)):
             b = bufs[tag]
-            if prepared:
+            if gather and tag == "gu":
+                fq.grouped_gemm_gather_into(fmt, rows, n, k, off, G, src, cfg["tokens"], tq, tsc,
+                                            tts, w[0], w[1], w[2], ch, nS, b["r"],
+                                            w[3] if prepared else None, y, 0)
+            elif prepared:
                 fq.grouped_gemm_prepared_into(fmt, rows, n, k, off, G, b["q"], b["s"], b["t"],
                                               w[0], w[1], w[2], ch, nS, b["r"], w[3], y, 0)
             else:
@@ -479,11 +489,11 @@ def build_moe(name, cfg, data, args, dev):
                      if prepared else 0)
     dn_bytes = rows * I * 2 + rows * I // 2 + rows * I // blk + rows * nS * 2 + G * 4
     if moe_tok:
-        # tokens read and quantized once; codes read once and written per routed row;
-        # the residual gathers x and writes R
+        # tokens read and quantized once; codes read once and written per routed row
+        # (not with the gathering GEMM); the residual gathers x and writes R
         T = cfg["tokens"]
-        gu_bytes = (T * H * 2 + 2 * T * (H // 2 + H // blk) + rows * (H // 2 + H // blk) +
-                    rows * nS * 4 + G * 4 + 4)
+        gu_bytes = (T * H * 2 + 2 * T * (H // 2 + H // blk) +
+                    (0 if gather else rows * (H // 2 + H // blk)) + rows * nS * 4 + G * 4 + 4)
     else:
         gu_bytes = rows * H * 2 + rows * H // 2 + rows * H // blk + rows * nS * 2 + G * 4
     s.quant_bytes = gu_bytes + dn_bytes

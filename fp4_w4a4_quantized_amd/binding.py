@@ -119,6 +119,9 @@ def lib():
         L.fp4q_qdq_fallback_workspace_bytes.argtypes = [ctypes.c_int, i64, i64]
         L.fp4q_qdq_fallback.restype = ctypes.c_int
         L.fp4q_qdq_fallback.argtypes = [ctypes.c_int, P, i64, i64, i64, P, i64, P, P, sz, P]
+        L.fp4q_grouped_gemm_gather.restype = ctypes.c_int
+        L.fp4q_grouped_gemm_gather.argtypes = [ctypes.c_int, i64, i64, i64, P, i32, P, i64, P, P,
+                                               P, P, P, P, P, i32, P, P, sz, P, ctypes.c_int, P]
         L.fp4q_gemm_decode_fused.restype = ctypes.c_int
         L.fp4q_gemm_decode_fused.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, P, i64,
                                              P, P, P, P, i32, P, sz, P, ctypes.c_int, i64, P, P,
@@ -342,6 +345,20 @@ def qdq_fallback(fmt, x, stream=None):
     ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=x.device) if wsb else None
     qdq_fallback_into(fmt, x, y, n, ws, stream)
     return y, n
+
+
+def grouped_gemm_gather_into(fmt, total_rows, N, K, group_offsets, num_groups, row_src, tokens,
+                             a_q, a_s, a_ts, b_q, b_s, b_ts, chan_idx, n_chan, resid, comp_w, y,
+                             y_dtype, stream=None):
+    """fp4q_grouped_gemm_gather: the grouped GEMM reading each routed row's
+    codes from the token matrix (row_src)."""
+    cw_bytes = 0 if comp_w is None else comp_w.numel() * comp_w.element_size()
+    _check("fp4q_grouped_gemm_gather",
+           lib().fp4q_grouped_gemm_gather(fmt, total_rows, N, K, _ptr(group_offsets), num_groups,
+                                          _ptr(row_src), tokens, _ptr(a_q), _ptr(a_s),
+                                          _ptr(a_ts), _ptr(b_q), _ptr(b_s), _ptr(b_ts),
+                                          _ptr(chan_idx), n_chan, _ptr(resid), _ptr(comp_w),
+                                          cw_bytes, _ptr(y), y_dtype, _stream(stream)))
 
 
 def gemm_decode_fused_into(fmt, layout, x, N, b_q, b_s, b_ts, chan_idx, n_chan, comp_w, y,

@@ -498,6 +498,36 @@ int fp4q_grouped_gemm_prepared(fp4q_format_t fmt, int64_t total_rows, int64_t N,
   return check_launch();
 }
 
+int fp4q_grouped_gemm_gather(fp4q_format_t fmt, int64_t total_rows, int64_t N, int64_t K,
+                             const int32_t* group_offsets, int32_t num_groups,
+                             const int32_t* row_src, int64_t tokens, const uint8_t* a_q,
+                             const uint8_t* a_s, const float* a_ts, const uint8_t* b_q,
+                             const uint8_t* b_s, const float* b_ts, const int32_t* chan_idx,
+                             int32_t n_chan, const uint16_t* resid, const uint8_t* comp_w,
+                             size_t comp_w_bytes, void* y, fp4q_dtype_t y_dtype, void* stream) {
+  int rc = validate_gemm_common(fmt, N, K, a_q, a_s, a_ts, b_q, b_s, b_ts, chan_idx, n_chan,
+                                resid, y, y_dtype, total_rows);
+  if (rc != FP4Q_OK) return rc;
+  if (num_groups < 1 || !group_offsets) return FP4Q_ERR_INVALID;
+  if (tokens < 0 || (total_rows > 0 && (tokens == 0 || !row_src))) return FP4Q_ERR_INVALID;
+  if (num_groups > MAX_GROUPS) return FP4Q_ERR_UNSUPPORTED;
+  if ((N + 127) / 128 > 65535 || !fp4q::big_grouped_eligible(N, K, n_chan))
+    return FP4Q_ERR_UNSUPPORTED;
+  const bool work = total_rows > 0 && N > 0;
+  if (work && n_chan > 0 &&
+      (!comp_w || !aligned(comp_w, 16) ||
+       comp_w_bytes < fp4q_grouped_comp_weights_bytes(fmt, N, K, num_groups, n_chan)))
+    return FP4Q_ERR_WORKSPACE;
+  if (!work) return FP4Q_OK;
+  if (injected_failure()) return FP4Q_ERR_HIP;
+  clear_error();
+  fp4q::launch_gemm_big_grouped(fmt, total_rows, N, K, group_offsets, num_groups, a_q, a_s, a_ts,
+                                b_q, b_s, b_ts, chan_idx, n_chan, resid,
+                                n_chan > 0 ? comp_w : nullptr, y, y_dtype == FP4Q_OUT_BF16, nullptr,
+                                static_cast<hipStream_t>(stream), row_src);
+  return check_launch();
+}
+
 size_t fp4q_select_channels_workspace_bytes(int64_t rows, int64_t cols) {
   return fp4q::select_workspace_bytes(rows, cols);
 }
@@ -546,7 +576,10 @@ int fp4q_permute_quantized(fp4q_format_t fmt, const uint16_t* x, int64_t tokens,
     return FP4Q_ERR_INVALID;
   if (fmt == FP4Q_NVFP4 && (!tensor_scale || !tensor_scale_out)) return FP4Q_ERR_INVALID;
   if (fmt == FP4Q_MXFP4 && (tensor_scale || tensor_scale_out)) return FP4Q_ERR_INVALID;
-  if (rows > 0 && (!row_src || !q || !scales || !q_out || !scales_out)) return FP4Q_ERR_INVALID;
+  // q_out and scales_out both NULL: the residual (and tensor scales) only,
+  // for a grouped GEMM that gathers the codes itself
+  if ((q_out == nullptr) != (scales_out == nullptr)) return FP4Q_ERR_INVALID;
+  if (rows > 0 && (!row_src || !q || !scales)) return FP4Q_ERR_INVALID;
   if (rows > 0 && (!aligned(q, 8) || !aligned(q_out, 8))) return FP4Q_ERR_INVALID;
   if (rows > 0 && n_chan > 0 && (!x || !aligned(x, 2) || ldx < cols)) return FP4Q_ERR_INVALID;
   if (rows >= ((int64_t)1 << 31) || cols >= ((int64_t)1 << 30) || num_groups > MAX_GROUPS)

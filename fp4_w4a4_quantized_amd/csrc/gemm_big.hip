@@ -90,6 +90,9 @@ struct BigArgs {
   // grouped (expert) form: row ranges [off[g], off[g+1]) use operand set g
   const int32_t* off;
   int G;
+  // grouped, gathering: row m of A is row row_src[m] of the token matrix
+  // (null: row m itself), and every group has the tensor scale ats[0]
+  const int32_t* row_src;
 };
 
 // The operands and row range of one output tile.  Grouped: B, its scales,
@@ -99,6 +102,7 @@ struct TileCtx {
   const uint8_t* bq;
   const uint8_t* bs;
   const uint8_t* bsel;
+  const int* src;  // gathering: the source row of tile row r at src[r] (LDS); else null
 };
 
 // Byte offsets inside one LDS stage and the direct-to-LDS loads a wave
@@ -271,6 +275,7 @@ __device__ __forceinline__ void issue_stage(const BigArgs& p, int s, int wave, i
     const int g = wave * 2 + i;
     int64_t ra = r0 + 16 * g + (lane & 15), rb = c0 + 16 * g + (lane & 15);
     ra = ra < rend ? ra : rend - 1;
+    if (tc.src) ra = tc.src[ra - r0];
     rb = rb < p.N ? rb : p.N - 1;
     lds_load16(p.aq + ra * K2 + off, st + SL::A + g * GB_GRP);
     lds_load16(tc.bq + rb * K2 + off, st + SL::B + g * GB_GRP);
@@ -283,6 +288,7 @@ __device__ __forceinline__ void issue_stage(const BigArgs& p, int s, int wave, i
     int64_t row = (isb ? c0 : r0) + 64 * c + lane;
     const int64_t lim = isb ? p.N : rend;
     row = row < lim ? row : lim - 1;
+    if (!isb && tc.src) row = tc.src[row - r0];
     const uint8_t* src = isb ? tc.bs : p.as;
     uint8_t* dst = st + (isb ? SL::SB : SL::SA);
     if (FMT == FP4Q_NVFP4) {
@@ -562,6 +568,15 @@ __global__ void __launch_bounds__(GB_T, 1) k_gemm_big(BigArgs args) {
     tc.bq = p.bq + (int64_t)grp * p.N * (p.K >> 1);
     tc.bs = p.bs + (int64_t)grp * p.N * (p.K / blk);
     tc.bsel = p.bsel + (int64_t)grp * ((p.N + 15) / 16) * p.nc * 1024;
+    tc.src = nullptr;
+    if (p.row_src) {
+      // the tile's source rows (rows past the group repeat its last row)
+      __shared__ int sSrc[GB_TILE];
+      const int64_t rr = tc.r0 + t;
+      if (t < GB_TILE) sSrc[t] = p.row_src[rr < tc.rend ? rr : tc.rend - 1];
+      __syncthreads();
+      tc.src = sSrc;
+    }
   } else {
     // XCD-aware, then grouped along M for L2 reuse
     const int T = p.mt * p.nt;
@@ -578,6 +593,7 @@ __global__ void __launch_bounds__(GB_T, 1) k_gemm_big(BigArgs args) {
     tc.bq = p.bq;
     tc.bs = p.bs;
     tc.bsel = p.bsel;
+    tc.src = nullptr;
   }
   const int64_t r0 = tc.r0, c0 = tc.c0;
 
@@ -587,7 +603,7 @@ __global__ void __launch_bounds__(GB_T, 1) k_gemm_big(BigArgs args) {
   float tx = 1.0f, tw = 1.0f;
   if (FMT == FP4Q_NVFP4) {
     const float c = p.cts ? *p.cts : 1.0f;
-    tx = p.ats[grp] / c;
+    tx = p.ats[p.row_src ? 0 : grp] / c;
     tw = p.bts[grp] * c;
   }
   auto stage = [&](int s) __attribute__((always_inline)) { return sStage + (s % 3) * SL::BYTES; };
@@ -877,6 +893,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_nv4(BigArgs args) {
     tc.bq = p.bq;
     tc.bs = p.bs;
     tc.bsel = p.bsel;
+    tc.src = nullptr;
   }
   const int nk = p.nk, ns = p.nk + p.nc;
   const float c = p.cts ? *p.cts : 1.0f;
@@ -1064,7 +1081,7 @@ int launch_gemm_big(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const 
   uint8_t* bsel = prepared ? const_cast<uint8_t*>(bsel_pre) : static_cast<uint8_t*>(ws);
   BigArgs a{M, N, K, aq, as, ats, bq, bs, bts, nS, resid, bsel, chan, cts, y, y_bf16, ldy,
             (int)((M + GB_TILE - 1) / GB_TILE), (int)((N + GB_TILE - 1) / GB_TILE),
-            (int)(K / 128), nc, nullptr, 1};
+            (int)(K / 128), nc, nullptr, 1, nullptr};
   const bool gather = nS > GB_XS_MAX && !prepared;
   const unsigned grid = (unsigned)(a.mt * a.nt);
   if (fmt == FP4Q_NVFP4) {
@@ -1098,14 +1115,14 @@ int launch_gemm_big_grouped(int fmt, int64_t total_rows, int64_t N, int64_t K,
                             const float* ats, const uint8_t* bq, const uint8_t* bs,
                             const float* bts, const int32_t* chan, int nS,
                             const uint16_t* resid, const uint8_t* bsel_pre, void* y, int y_bf16,
-                            void* ws, hipStream_t stream) {
+                            void* ws, hipStream_t stream, const int32_t* row_src) {
   const int nc = nS > 0 ? (nS + GB_CS - 1) / GB_CS : 0;
   // prepared compensation weights (every group's, made once) replace both
   // the gather and the in-kernel extraction
   const bool prepared = bsel_pre != nullptr && nS > 0;
   uint8_t* bsel = prepared ? const_cast<uint8_t*>(bsel_pre) : static_cast<uint8_t*>(ws);
   BigArgs a{total_rows, N, K, aq, as, ats, bq, bs, bts, nS, resid, bsel, chan, nullptr, y, y_bf16, N,
-            0, (int)((N + GB_TILE - 1) / GB_TILE), (int)(K / 128), nc, off, G};
+            0, (int)((N + GB_TILE - 1) / GB_TILE), (int)(K / 128), nc, off, G, row_src};
   const bool gather = nS > GB_XS_MAX && !prepared;
   // every group adds at most one partial 256-row tile
   const unsigned grid = (unsigned)(((total_rows + GB_TILE - 1) / GB_TILE + G) * a.nt);

@@ -135,8 +135,10 @@ __global__ __launch_bounds__(PM_THREADS) void k_permute_rows(
     const int nr = min(PM_ROWS, n - i0);
     const int li = i0 + min(lane, nr - 1);  // lanes past the list repeat its last row
     const int mrow = s_m[li], tk = s_tok[li], gl = s_g[li];
-    copy_rows<CodeUnit>(q, q_out, cb, tk, mrow, nr, lane);
-    copy_rows<ScaleUnit>(scales, s_out, sb, tk, mrow, nr, lane);
+    if (q_out != nullptr) {  // null: the grouped GEMM gathers the codes itself
+      copy_rows<CodeUnit>(q, q_out, cb, tk, mrow, nr, lane);
+      copy_rows<ScaleUnit>(scales, s_out, sb, tk, mrow, nr, lane);
+    }
 
     // residual: the (row, channel) pairs of the eight rows spread over the
     // lanes, four per lane in flight
@@ -187,7 +189,7 @@ void launch_permute(int fmt, const uint16_t* x, int64_t ldx, int64_t tokens, int
   // widest units that divide the rows (buffers are at least 8-byte aligned
   // for the codes; 16-byte units need 16-byte aligned buffers)
   const int64_t cb = cols / 2, sb = cols / (fmt == FP4Q_NVFP4 ? 16 : 32);
-  const bool c16 = cb % 16 == 0 && aligned16(q) && aligned16(q_out);
+  const bool c16 = cb % 16 == 0 && aligned16(q) && aligned16(q_out);  // (null is aligned)
   const int su = (sb % 16 == 0 && aligned16(scales) && aligned16(s_out)) ? 16
                  : (sb % 4 == 0 && aligned4(scales) && aligned4(s_out)) ? 4 : 1;
 #define FP4Q_PERMUTE(F, C, S)                                                                 \

@@ -499,7 +499,10 @@ int fp4q_grouped_gemm(fp4q_format_t fmt, int64_t total_rows, int64_t N, int64_t 
  *   group_offsets  device int32 [num_groups + 1], as for fp4q_grouped_gemm
  *   chan_idx       device int32 [num_groups, n_chan], ascending per group;
  *                  NULL iff n_chan == 0
- *   q_out, scales_out   out [rows, cols/2] (8-byte aligned), [rows, cols/blk]
+ *   q_out, scales_out   out [rows, cols/2] (8-byte aligned), [rows, cols/blk];
+ *                  both NULL: only the residual and the tensor scales are
+ *                  written (fp4q_grouped_gemm_gather then reads the codes
+ *                  from the token matrix itself)
  *   tensor_scale_out    out device f32 [num_groups] (NVFP4), NULL for MXFP4
  *   resid_out      out bf16 [rows, n_chan]; NULL iff n_chan == 0
  *
@@ -514,6 +517,43 @@ int fp4q_permute_quantized(fp4q_format_t fmt, const uint16_t* x, int64_t tokens,
                            const int32_t* chan_idx, int32_t n_chan, uint8_t* q_out,
                            uint8_t* scales_out, float* tensor_scale_out, uint16_t* resid_out,
                            void* stream);
+
+/* ------------------------------------------------------------------------
+ * Expert-grouped GEMM gathering the token codes (QUADS abstract: NVFP4
+ * rollout for Mixture-of-Experts; quantize-before-permute).  The tokens
+ * are quantized once (fp4q_quantize, one group, row-major) and every
+ * routed row reads its token's codes and block scales straight from that
+ * matrix -- no expert-ordered copy of them:
+ *
+ *   Y[m, n] = sum_k deq(Xq[row_src[m], k]) B_g[n, k] + sum_j R[m, j] B_g[n, S_gj]
+ *
+ * for m in group g's rows [off[g], off[g+1]).  The residual R [total_rows,
+ * n_chan] is the routed rows' (fp4q_permute_quantized with q_out and
+ * scales_out NULL writes it, and the per-group tensor scales).
+ *
+ *   row_src        device int32 [total_rows]: the token of each routed row
+ *                  (< tokens; a precondition)
+ *   a_q, a_s       the token matrix's codes and scales, row-major
+ *                  [tokens, K/2], [tokens, K/blk]
+ *   a_ts           device f32 [1] its tensor scale (NVFP4), NULL for MXFP4;
+ *                  every group uses it
+ *   b_*, chan_idx, n_chan   as fp4q_grouped_gemm
+ *   resid          bf16 [total_rows, n_chan], 16-byte aligned
+ *   comp_w         fp4q_grouped_comp_weights of the weights (needed when
+ *                  n_chan > 0), comp_w_bytes its size
+ *   y              out [total_rows, N]
+ *
+ * The 256-tile grouped kernel only: N >= 256, K % 128 == 0, n_chan % 8 ==
+ * 0 (FP4Q_ERR_UNSUPPORTED otherwise); more than 2048 groups is
+ * FP4Q_ERR_UNSUPPORTED.
+ * ------------------------------------------------------------------------ */
+int fp4q_grouped_gemm_gather(fp4q_format_t fmt, int64_t total_rows, int64_t N, int64_t K,
+                             const int32_t* group_offsets, int32_t num_groups,
+                             const int32_t* row_src, int64_t tokens, const uint8_t* a_q,
+                             const uint8_t* a_s, const float* a_ts, const uint8_t* b_q,
+                             const uint8_t* b_s, const float* b_ts, const int32_t* chan_idx,
+                             int32_t n_chan, const uint16_t* resid, const uint8_t* comp_w,
+                             size_t comp_w_bytes, void* y, fp4q_dtype_t y_dtype, void* stream);
 
 /* ------------------------------------------------------------------------
  * Exact three-way MXFP4 error decomposition ("Decomposing MXFP4

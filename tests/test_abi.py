@@ -216,6 +216,31 @@ def test_gemm_decode_fused_rejects(L):
         L.fp4q_test_hook(0, 0)
 
 
+def test_grouped_gemm_gather_rejects(L):
+    P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    L.fp4q_grouped_gemm_gather.argtypes = [ctypes.c_int, i64, i64, i64, P, i32, P, i64, P, P, P,
+                                           P, P, P, P, i32, P, P, ctypes.c_size_t, P,
+                                           ctypes.c_int, P]
+
+    def f(fmt=0, rows=64, N=256, K=256, off=A, G=2, src=B, tokens=10, aq=A, as_=A, ats=B, bq=B,
+          bs=B, bts=B, chan=None, nS=0, R=None, cw=None, cwb=0, y=A, dt=0):
+        return L.fp4q_grouped_gemm_gather(fmt, rows, N, K, off, G, src, tokens, aq, as_, ats, bq,
+                                          bs, bts, chan, nS, R, cw, cwb, y, dt, None)
+    assert f(src=None) == INVALID
+    assert f(tokens=0) == INVALID
+    assert f(off=None) == INVALID
+    assert f(N=200) == UNSUPPORTED                 # the 256-tile kernel only
+    assert f(K=200) == INVALID                     # not a multiple of the block
+    assert f(G=3000) == UNSUPPORTED
+    assert f(nS=8, chan=A, R=B) == WORKSPACE       # prepared weights missing
+    assert f(rows=0) == 0
+    try:
+        assert L.fp4q_test_hook(1, 33) == 0
+        assert f() == HIP_ERR and L.fp4q_last_hip_error() == 33
+    finally:
+        L.fp4q_test_hook(0, 0)
+
+
 def test_quantize_status_rejects(L):
     need = L.fp4q_quantize_workspace_bytes(0, 4, 64, 1)
     st = ctypes.c_int32(0)
