@@ -89,6 +89,11 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a device-to-device copy of 256 MiB, 5 times (the known-size "
                         "reference for the FETCH_SIZE / WRITE_SIZE counter scale)")
+    p.add_argument("--record-traffic", default=None, metavar="PMC_DIR",
+                   help="no GPU: read rocprofv3 --pmc CSV output under PMC_DIR "
+                        "(<workload>_FETCH_SIZE, <workload>_WRITE_SIZE, copy_FETCH_SIZE, "
+                        "copy_WRITE_SIZE) and write each workload's entry of "
+                        "profiles/traffic.json")
     p.add_argument("--decompose-only", default=None, choices=("nvfp4", "mxfp4"),
                    help="run only the error decomposition of the prefill activations, 5 calls "
                         "(the command behind its counter profile)")
@@ -121,6 +126,71 @@ def src_hash(files=None) -> str:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+# dominant kernel of each workload's default variant: a substring of its
+# demangled name, the sources that define it, and its dispatches per launch
+DOMINANT = {
+    "prefill_nvfp4": ("k_gemm_nv4<true>", ["gemm_big.hip", "fp4q_device.h"], 1),
+    "prefill_mxfp4": ("k_gemm_big<1, true, false, false>", ["gemm_big.hip", "fp4q_device.h"], 1),
+    "decode_nvfp4": ("k_gemm_skinny<0, true, true>", ["gemm_skinny.hip", "fp4q_device.h"], 1),
+    "moe_nvfp4": ("k_gemm_big<0, false, true, false>", ["gemm_big.hip", "fp4q_device.h"], 2),
+}
+
+
+def _pmc_per_dispatch(run_dir, counter, kernel=None):
+    """Mean value of `counter` per dispatch (and the dispatch count) over the
+    rocprofv3 *counter_collection.csv files under run_dir, for dispatches whose
+    kernel name contains `kernel` (for None: the most frequent kernel)."""
+    import csv
+    import glob
+    per = {}
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(f, newline="") as fh:
+            for row in csv.DictReader(fh):
+                if row.get("Counter_Name") != counter:
+                    continue
+                key = (f, row.get("Dispatch_Id"))
+                name, v = row.get("Kernel_Name", ""), float(row["Counter_Value"])
+                per[key] = (name, per.get(key, (name, 0.0))[1] + v)
+    if kernel is None:
+        names = [n for n, _ in per.values()]
+        if not names:
+            raise SystemExit(f"no {counter} rows under {run_dir}")
+        kernel = max(set(names), key=names.count)
+    vals = [v for n, v in per.values() if kernel in n]
+    if not vals:
+        raise SystemExit(f"no {counter} rows for {kernel} under {run_dir}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def record_traffic(pmc_dir):
+    """Turn FETCH_SIZE / WRITE_SIZE (KiB per dispatch) into HBM bytes per launch
+    with the copy calibration (256 MiB read and written per copy), for every
+    workload whose two counter runs are under pmc_dir."""
+    copy_bytes = 256 << 20
+    cf, _ = _pmc_per_dispatch(os.path.join(pmc_dir, "copy_FETCH_SIZE"), "FETCH_SIZE", "copyBuffer")
+    cw, _ = _pmc_per_dispatch(os.path.join(pmc_dir, "copy_WRITE_SIZE"), "WRITE_SIZE", "copyBuffer")
+    ff, wf = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path) as f:
+        t = json.load(f)
+    for wl, (kern, sources, per_launch) in DOMINANT.items():
+        fd = os.path.join(pmc_dir, f"{wl}_FETCH_SIZE")
+        wd = os.path.join(pmc_dir, f"{wl}_WRITE_SIZE")
+        if not (os.path.isdir(fd) and os.path.isdir(wd)):
+            continue
+        fk, nf = _pmc_per_dispatch(fd, "FETCH_SIZE", kern)
+        wk, nw = _pmc_per_dispatch(wd, "WRITE_SIZE", kern)
+        t[wl] = {"kernel": kern, "sources": sources, "src_hash": src_hash(sources),
+                 "fetch_kib_per_dispatch": round(fk, 1), "write_kib_per_dispatch": round(wk, 1),
+                 "dispatches": [nf, nw], "dispatches_per_launch": per_launch,
+                 "fetch_factor": round(ff, 4), "write_factor": round(wf, 4),
+                 "bytes_per_launch": int(round(per_launch * 1024 * (fk * ff + wk * wf)))}
+        print(f"{wl}: {json.dumps(t[wl])}")
+    with open(path, "w") as f:
+        json.dump(t, f, indent=2)
+        f.write("\n")
 
 
 def load_traffic(workload: str, default_variant: bool):
@@ -666,6 +736,9 @@ def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.record_traffic:
+        record_traffic(args.record_traffic)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is "

@@ -102,7 +102,7 @@ struct TileCtx {
   const uint8_t* bq;
   const uint8_t* bs;
   const uint8_t* bsel;
-  const int* src;  // gathering: the source row of tile row r at src[r] (LDS); else null
+  const int* src;  // gathering (GA): the source row of tile row r at src[r] (LDS)
 };
 
 // Byte offsets inside one LDS stage and the direct-to-LDS loads a wave
@@ -204,7 +204,7 @@ __device__ __forceinline__ void lds_barrier() {
 // Compensation stage cs: per 16-row group, R rows (channels 32cs + 8(l/16)
 // .. +7 of row 16g + l%16; a piece past |S| is re-read from the last valid
 // one and meets zero weights) and the matching 1 KB block of B_S.
-template <int FMT, bool TL, bool XS>
+template <int FMT, bool TL, bool XS, bool GA = false>
 __device__ __forceinline__ void issue_stage(const BigArgs& p, int s, int wave, int lane,
                                             const TileCtx& tc, uint8_t* st) {
   using SL = StageLayout<FMT>;
@@ -275,7 +275,7 @@ __device__ __forceinline__ void issue_stage(const BigArgs& p, int s, int wave, i
     const int g = wave * 2 + i;
     int64_t ra = r0 + 16 * g + (lane & 15), rb = c0 + 16 * g + (lane & 15);
     ra = ra < rend ? ra : rend - 1;
-    if (tc.src) ra = tc.src[ra - r0];
+    if (GA) ra = tc.src[ra - r0];
     rb = rb < p.N ? rb : p.N - 1;
     lds_load16(p.aq + ra * K2 + off, st + SL::A + g * GB_GRP);
     lds_load16(tc.bq + rb * K2 + off, st + SL::B + g * GB_GRP);
@@ -288,7 +288,7 @@ __device__ __forceinline__ void issue_stage(const BigArgs& p, int s, int wave, i
     int64_t row = (isb ? c0 : r0) + 64 * c + lane;
     const int64_t lim = isb ? p.N : rend;
     row = row < lim ? row : lim - 1;
-    if (!isb && tc.src) row = tc.src[row - r0];
+    if (GA && !isb) row = tc.src[row - r0];
     const uint8_t* src = isb ? tc.bs : p.as;
     uint8_t* dst = st + (isb ? SL::SB : SL::SA);
     if (FMT == FP4Q_NVFP4) {
@@ -426,18 +426,18 @@ __device__ __forceinline__ void compute_comp(f32x16 (&acc)[2][4], const Frag& f)
     }
 }
 
-// Epilogue of a 256 x 256 tile.  acc[i][j][e] is row 32 RI wm + 32 i +
+// Epilogue of a TM x TN tile.  acc[i][j][e] is row 32 RI wm + 32 i +
 // 8 (e / 4) + 4 (l / 32) + e % 4, column 128 wn + 32 j + l % 32, scaled by
 // tw on the way out.  Interior tiles are staged through LDS (each wave its
 // own 32 x 64 region) and written as 16-byte vectors: rows of 256 bytes
 // (FP32) or 128 bytes (BF16); edge tiles store element by element.
-template <int RI>
+template <int RI, int TM = GB_TILE, int TN = GB_TILE>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[RI][4], const BigArgs& p,
                                            int64_t r0, int64_t c0, int64_t rend, int wm, int wn,
                                            int wave, int lane, float tw, uint8_t* sStage) {
   const int hi = lane >> 5, l31 = lane & 31;
   const int64_t rw = r0 + wm * 32 * RI, cw = c0 + wn * 128;
-  const bool interior = (r0 + GB_TILE <= rend) && (c0 + GB_TILE <= p.N);
+  const bool interior = (r0 + TM <= rend) && (c0 + TN <= p.N);
   const bool vec = interior && (p.ldy % 8) == 0 && (reinterpret_cast<uintptr_t>(p.y) & 15) == 0;
   if (vec) {
     lds_barrier();  // every wave is done with the last stage
@@ -500,7 +500,9 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[RI][4], const Big
 
 // XS: the compensation weights of up to GB_XS_MAX channels are taken from
 // the B tiles as the FP4 stages pass through LDS (no gather kernel).
-template <int FMT, bool TL, bool GR, bool XS>
+// GR: 0 dense, 1 grouped, 2 grouped with the rows of A gathered by row_src
+// (a separate instance, so the plain grouped kernel keeps its registers).
+template <int FMT, bool TL, int GR, bool XS>
 __global__ void __launch_bounds__(GB_T, 1) k_gemm_big(BigArgs args) {
   using SL = StageLayout<FMT>;
   constexpr int L = SL::LOADS;
@@ -569,7 +571,7 @@ __global__ void __launch_bounds__(GB_T, 1) k_gemm_big(BigArgs args) {
     tc.bs = p.bs + (int64_t)grp * p.N * (p.K / blk);
     tc.bsel = p.bsel + (int64_t)grp * ((p.N + 15) / 16) * p.nc * 1024;
     tc.src = nullptr;
-    if (p.row_src) {
+    if (GR == 2) {
       // the tile's source rows (rows past the group repeat its last row)
       __shared__ int sSrc[GB_TILE];
       const int64_t rr = tc.r0 + t;
@@ -603,7 +605,7 @@ __global__ void __launch_bounds__(GB_T, 1) k_gemm_big(BigArgs args) {
   float tx = 1.0f, tw = 1.0f;
   if (FMT == FP4Q_NVFP4) {
     const float c = p.cts ? *p.cts : 1.0f;
-    tx = p.ats[p.row_src ? 0 : grp] / c;
+    tx = p.ats[GR == 2 ? 0 : grp] / c;
     tw = p.bts[grp] * c;
   }
   auto stage = [&](int s) __attribute__((always_inline)) { return sStage + (s % 3) * SL::BYTES; };
@@ -634,10 +636,10 @@ __global__ void __launch_bounds__(GB_T, 1) k_gemm_big(BigArgs args) {
   const bool late = FMT == FP4Q_MXFP4 && wave >= GB_W / 2;
   auto issue = [&](int s) __attribute__((always_inline)) {
     if (FMT == FP4Q_MXFP4) {
-      issue_stage<FMT, TL, XS>(p, s, 2 * wave, lane, tc, stage(s));
-      issue_stage<FMT, TL, XS>(p, s, 2 * wave + 1, lane, tc, stage(s));
+      issue_stage<FMT, TL, XS, GR == 2>(p, s, 2 * wave, lane, tc, stage(s));
+      issue_stage<FMT, TL, XS, GR == 2>(p, s, 2 * wave + 1, lane, tc, stage(s));
     } else {
-      issue_stage<FMT, TL, XS>(p, s, wave, lane, tc, stage(s));
+      issue_stage<FMT, TL, XS, GR == 2>(p, s, wave, lane, tc, stage(s));
     }
   };
   if (!late) {
@@ -664,7 +666,7 @@ __global__ void __launch_bounds__(GB_T, 1) k_gemm_big(BigArgs args) {
     else
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
-    if (s + 2 < ns) issue_stage<FMT, TL, XS>(p, s + 2, wave, lane, tc, stage(s + 2));
+    if (s + 2 < ns) issue_stage<FMT, TL, XS, GR == 2>(p, s + 2, wave, lane, tc, stage(s + 2));
   };
   auto extract = [&](int s) __attribute__((always_inline)) {
     if (XS) {
@@ -954,6 +956,241 @@ __global__ void __launch_bounds__(256, 1) k_gemm_nv4(BigArgs args) {
   store_tile<4>(acc, p, tc.r0, tc.c0, tc.rend, wm, wn, wave, lane, tw, sStage);
 }
 
+
+// ---- grouped NVFP4: 128 x 512 tiles on four waves ---------------------------
+// The expert-grouped form of k_gemm_nv4 (QUADS abstract: MoE rollout; the
+// same Y = A B^T + R[:, S] B_S^T per group).  The groups of a mixture-of-
+// experts layer are small and uneven, so rows are tiled by 128, not 256
+// (fewer MFMAs on padding rows), and the four waves sit side by side along
+// N, each owning 128 x 128 exactly as in k_gemm_nv4 (same decode work per
+// MFMA).  Grouped operands are row-major: every direct-to-LDS load takes a
+// wave-uniform base (tile origin and K step, in SGPRs) plus a 32-bit lane
+// offset fixed for the whole tile, so the row addressing holds few VGPRs.
+// Tiles run group by group, row tile by row tile, the N tiles of one row
+// tile together, and each XCD (block b runs on XCD b % 8) takes one
+// contiguous run of that order: the weight panels of a group and the code
+// rows of a row tile are shared inside one L2.
+constexpr int G4_TM = 128, G4_TN = 512;
+
+struct G4Layout {
+  static constexpr int A = 0;                        // 8 groups of 16 rows, 1 KB each
+  static constexpr int B = 8 * GB_GRP;               // 32 groups of 16 columns
+  static constexpr int SA = 40 * GB_GRP;             // scale dwords [d][row], 2 x 128
+  static constexpr int SB = SA + 2 * G4_TM * 4;      // scale dwords [d][col], 2 x 512
+  static constexpr int BYTES = SB + 2 * G4_TN * 4;   // 46080
+  static constexpr int LOADS = 2 + 8 + 5;            // per wave and stage
+};
+
+// This wave's loads of stage s: A groups 2w, 2w + 1; B groups 8w .. 8w + 7;
+// scale instructions 5w .. 5w + 4 of 20 (4 for A: dword d, 64-row chunk c;
+// 16 for B).  Compensation stages load R pieces and the prepared B_S blocks
+// into the same places, and placeholders keep the count.
+__device__ __forceinline__ void g4_issue(const BigArgs& p, int s, int wave, int lane,
+                                         const TileCtx& tc, uint8_t* st) {
+  using GL = G4Layout;
+  const int64_t r0 = tc.r0, c0 = tc.c0;
+  const int rlast = (int)(tc.rend - 1 - r0), clast = (int)(p.N - 1 - c0);
+  if (s >= p.nk) {
+    const int cs = s - p.nk;
+    const int64_t gN = ((p.N + 15) >> 4) - 1;
+    int ch = GB_CS * cs + 8 * (lane >> 4);
+    ch = ch < p.nS - 8 ? ch : p.nS - 8;
+    const uint16_t* rb = p.resid + r0 * p.nS;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int g = 2 * wave + i;
+      int r = 16 * g + (lane & 15);
+      r = r < rlast ? r : rlast;
+      lds_load16s(rb, (uint32_t)((r * p.nS + ch) * 2), st + GL::A + g * GB_GRP);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int g = 8 * wave + i;
+      int64_t gb = (c0 >> 4) + g;
+      gb = gb < gN ? gb : gN;
+      lds_load16s(tc.bsel + ((gb * p.nc + cs) << 10), lane * 16, st + GL::B + g * GB_GRP);
+    }
+#pragma unroll
+    for (int i = 0; i < 5; ++i) lds_load4(p.resid, st + GL::SA + (wave * 5 + i) * 256);
+    return;
+  }
+  const int kt = s;
+  const int64_t K2 = p.K >> 1, KS = p.K >> 4;
+  const uint8_t* ab = p.aq + r0 * K2 + kt * 64;
+  const uint8_t* bb = tc.bq + c0 * K2 + kt * 64;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int g = 2 * wave + i;
+    int r = 16 * g + (lane & 15);
+    r = r < rlast ? r : rlast;
+    lds_load16s(ab, (uint32_t)(r * K2 + (lane >> 4) * 16), st + GL::A + g * GB_GRP);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int g = 8 * wave + i;
+    int r = 16 * g + (lane & 15);
+    r = r < clast ? r : clast;
+    lds_load16s(bb, (uint32_t)(r * K2 + (lane >> 4) * 16), st + GL::B + g * GB_GRP);
+  }
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const int n = 5 * wave + i;
+    if (n < 4) {
+      const int d = n >> 1, c = n & 1;
+      int r = 64 * c + lane;
+      r = r < rlast ? r : rlast;
+      lds_load4s(p.as + r0 * KS + kt * 8 + 4 * d, (uint32_t)(r * KS),
+                 st + GL::SA + (d * G4_TM + 64 * c) * 4);
+    } else {
+      const int m = n - 4, d = m >> 3, c = m & 7;
+      int r = 64 * c + lane;
+      r = r < clast ? r : clast;
+      lds_load4s(tc.bs + c0 * KS + kt * 8 + 4 * d, (uint32_t)(r * KS),
+                 st + GL::SB + (d * G4_TN + 64 * c) * 4);
+    }
+  }
+}
+
+// Half h of a stage's fragments for wave w (all 128 rows, columns 128 w ..).
+__device__ __forceinline__ void g4_read_half(const uint8_t* st, int wave, int lane, int h,
+                                             FragT4& f) {
+  using GL = G4Layout;
+  const uint32_t l32 =
+      (uint32_t)((((lane >> 4) & 1) * GB_GRP) + ((lane >> 5) * 16 + (lane & 15)) * 16);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    f.a[i][h] = *reinterpret_cast<const u32x4*>(st + GL::A + (2 * i) * GB_GRP + l32 + h * 512);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    f.b[j][h] = *reinterpret_cast<const u32x4*>(st + GL::B + (wave * 8 + 2 * j) * GB_GRP + l32 +
+                                                h * 512);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    f.sa[i][h] = *reinterpret_cast<const uint32_t*>(
+        st + GL::SA + (h * G4_TM + 32 * i + (lane & 31)) * 4);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    f.sb[j][h] = *reinterpret_cast<const uint32_t*>(
+        st + GL::SB + (h * G4_TN + wave * 128 + 32 * j + (lane & 31)) * 4);
+}
+
+__global__ void __launch_bounds__(256, 1) k_gemm_nv4g(BigArgs args) {
+  using GL = G4Layout;
+  constexpr int L = GL::LOADS;
+  __shared__ __attribute__((aligned(16))) uint8_t sStage[3 * GL::BYTES];
+  __shared__ int s_wsum[4];
+  __shared__ int s_tile[2];
+  const BigArgs& p = args;
+  const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
+
+  // tiles per group: ceil(rows / 128) * nt; thread t counts groups 8t .. 8t + 7
+  // (G <= 2048), a block-wide scan gives every thread its first tile
+  const int G = p.G, nt = p.nt;
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int gg = t * 8 + i;
+    if (gg < G) cnt += (p.off[gg + 1] - p.off[gg] + G4_TM - 1) / G4_TM * nt;
+  }
+  int incl = cnt;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d);
+    if (lane >= d) incl += v;
+  }
+  if (lane == 63) s_wsum[wave] = incl;
+  if (t == 0) s_tile[0] = -1;
+  __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    before += w < wave ? s_wsum[w] : 0;
+    total += s_wsum[w];
+  }
+  const int b = blockIdx.x;
+  if (b >= total) return;  // past the last tile: uniform exit
+  // XCD x (blocks b = 8 idx + x) takes the contiguous run of tiles
+  // [x base + min(x, rem), ...) of length base + (x < rem)
+  const int base = total >> 3, rem = total & 7, x = b & 7;
+  const int tile = x * base + (x < rem ? x : rem) + (b >> 3);
+  const int excl = before + incl - cnt;
+  if (tile >= excl && tile < excl + cnt) {
+    int acc0 = excl;
+    for (int i = 0; i < 8; ++i) {
+      const int gg = t * 8 + i;
+      const int c = (gg < G) ? (p.off[gg + 1] - p.off[gg] + G4_TM - 1) / G4_TM * nt : 0;
+      if (tile < acc0 + c) {
+        s_tile[0] = gg;
+        s_tile[1] = tile - acc0;
+        break;
+      }
+      acc0 += c;
+    }
+  }
+  __syncthreads();
+  const int grp = s_tile[0], local = s_tile[1];
+  TileCtx tc;
+  tc.r0 = (int64_t)p.off[grp] + (int64_t)(local / nt) * G4_TM;
+  tc.c0 = (int64_t)(local % nt) * G4_TN;
+  tc.rend = p.off[grp + 1];
+  tc.bq = p.bq + (int64_t)grp * p.N * (p.K >> 1);
+  tc.bs = p.bs + (int64_t)grp * p.N * (p.K >> 4);
+  tc.bsel = p.bsel + (int64_t)grp * ((p.N + 15) / 16) * p.nc * 1024;
+  tc.src = nullptr;
+
+  const int nk = p.nk, ns = p.nk + p.nc;
+  const float c = p.cts ? *p.cts : 1.0f;
+  const float tx = p.ats[grp] / c, tw = p.bts[grp] * c;
+  auto stage = [&](int s) __attribute__((always_inline)) { return sStage + (s % 3) * GL::BYTES; };
+  auto issue = [&](int s) __attribute__((always_inline)) {
+    g4_issue(p, s, wave, lane, tc, stage(s));
+  };
+  issue(0);
+  if (ns > 1) issue(1);
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  auto open = [&](int s) __attribute__((always_inline)) {
+    if (s + 1 < ns)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();
+    if (s + 2 < ns) issue(s + 2);
+  };
+  for (int s = 0; s < nk; ++s) {
+    open(s);
+    FragT4 f;
+    g4_read_half(stage(s), wave, lane, 0, f);
+    g4_read_half(stage(s), wave, lane, 1, f);
+    h16x2 sca[4][2], scb[4][2];
+    nv4_scales(f, 0, lane, sca, scb);
+    nv4_scales(f, 1, lane, sca, scb);
+    NvDec4 cur, nxt;
+    nv4_decode(f, sca, scb, 0, cur);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (n < 7) nv4_decode(f, sca, scb, n + 1, nxt);
+      nv4_mma(acc, cur);
+      cur = nxt;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] *= tx;
+  for (int s = nk; s < ns; ++s) {
+    open(s);
+    comp4_stage(acc, stage(s), stage(s) + G4Layout::B, 0, wave, lane);
+  }
+  store_tile<4, G4_TM, G4_TN>(acc, p, tc.r0, tc.c0, tc.rend, 0, wave, wave, lane, tw, sStage);
+}
+
 // ---- B_S gather ---------------------------------------------------------------
 // bsel holds B_S[n, j] (bf16 bits of e2m1 * block scale, tensor scale
 // excluded; exact) for n < ceil16(N), j < ceil32(|S|), zero past N or |S|,
@@ -1034,10 +1271,12 @@ static void launch_big(const BigArgs& a, bool tiled, unsigned grid, hipStream_t 
                        bool prepared = false) {
   const bool xs = a.nS > 0 && a.nS <= GB_XS_MAX && !prepared;
   if constexpr (GR) {  // grouped operands are row-major
-    if (xs)
-      hipLaunchKernelGGL((k_gemm_big<FMT, false, true, true>), dim3(grid), dim3(GB_T), 0, stream, a);
+    if (a.row_src)   // the gathering form streams prepared weights (no XS)
+      hipLaunchKernelGGL((k_gemm_big<FMT, false, 2, false>), dim3(grid), dim3(GB_T), 0, stream, a);
+    else if (xs)
+      hipLaunchKernelGGL((k_gemm_big<FMT, false, 1, true>), dim3(grid), dim3(GB_T), 0, stream, a);
     else
-      hipLaunchKernelGGL((k_gemm_big<FMT, false, true, false>), dim3(grid), dim3(GB_T), 0, stream, a);
+      hipLaunchKernelGGL((k_gemm_big<FMT, false, 1, false>), dim3(grid), dim3(GB_T), 0, stream, a);
   } else if (FMT == FP4Q_NVFP4 && !xs) {
     if (tiled)
       hipLaunchKernelGGL((k_gemm_nv4<true>), dim3(grid), dim3(256), 0, stream, a);
@@ -1045,13 +1284,13 @@ static void launch_big(const BigArgs& a, bool tiled, unsigned grid, hipStream_t 
       hipLaunchKernelGGL((k_gemm_nv4<false>), dim3(grid), dim3(256), 0, stream, a);
   } else {
     if (tiled && xs)
-      hipLaunchKernelGGL((k_gemm_big<FMT, true, false, true>), dim3(grid), dim3(GB_T), 0, stream, a);
+      hipLaunchKernelGGL((k_gemm_big<FMT, true, 0, true>), dim3(grid), dim3(GB_T), 0, stream, a);
     else if (tiled)
-      hipLaunchKernelGGL((k_gemm_big<FMT, true, false, false>), dim3(grid), dim3(GB_T), 0, stream, a);
+      hipLaunchKernelGGL((k_gemm_big<FMT, true, 0, false>), dim3(grid), dim3(GB_T), 0, stream, a);
     else if (xs)
-      hipLaunchKernelGGL((k_gemm_big<FMT, false, false, true>), dim3(grid), dim3(GB_T), 0, stream, a);
+      hipLaunchKernelGGL((k_gemm_big<FMT, false, 0, true>), dim3(grid), dim3(GB_T), 0, stream, a);
     else
-      hipLaunchKernelGGL((k_gemm_big<FMT, false, false, false>), dim3(grid), dim3(GB_T), 0, stream, a);
+      hipLaunchKernelGGL((k_gemm_big<FMT, false, 0, false>), dim3(grid), dim3(GB_T), 0, stream, a);
   }
 }
 
@@ -1124,6 +1363,15 @@ int launch_gemm_big_grouped(int fmt, int64_t total_rows, int64_t N, int64_t K,
   BigArgs a{total_rows, N, K, aq, as, ats, bq, bs, bts, nS, resid, bsel, chan, nullptr, y, y_bf16, N,
             0, (int)((N + GB_TILE - 1) / GB_TILE), (int)(K / 128), nc, off, G, row_src};
   const bool gather = nS > GB_XS_MAX && !prepared;
+  const bool xs = nS > 0 && nS <= GB_XS_MAX && !prepared;
+  if (fmt == FP4Q_NVFP4 && !xs && row_src == nullptr) {
+    // 128 x 512 tiles; every group adds at most one partial row tile
+    a.nt = (int)((N + G4_TN - 1) / G4_TN);
+    const unsigned g4 = (unsigned)(((total_rows + G4_TM - 1) / G4_TM + G) * a.nt);
+    if (gather) launch_gather<FP4Q_NVFP4>(false, bq, bs, N, K, chan, nS, nc, G, bsel, stream);
+    hipLaunchKernelGGL(k_gemm_nv4g, dim3(g4), dim3(256), 0, stream, a);
+    return 0;
+  }
   // every group adds at most one partial 256-row tile
   const unsigned grid = (unsigned)(((total_rows + GB_TILE - 1) / GB_TILE + G) * a.nt);
   if (fmt == FP4Q_NVFP4) {

@@ -74,6 +74,26 @@ def test_groups_large_tiles(orc, fmt, nS):
     _run(orc, fmt, x, off, chan, wts)
 
 
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("nS", [0, 104])
+def test_groups_wide_tiles(orc, fmt, nS):
+    """Groups of 127, 128, 129, 300 and 513 rows and N = 1088 (two full
+    512-column tiles and a partial one): interior tiles of the 128 x 512
+    NVFP4 grouped kernel (vector stores) beside edge tiles, with and without
+    the compensation term (104 channels: weights gathered per call)."""
+    need_gpu()
+    say(f"grouped wide-tile fmt {fmt} nS {nS}")
+    K, N = 256, 1088
+    off = np.cumsum([0, 127, 0, 128, 129, 1, 300, 513]).astype(np.int32)
+    G = off.size - 1
+    x = dense_case(int(off[-1]), K, 8, n_out=3, seed=57)["x"]
+    wts = [dense_case(1, K, N, seed=90 + g)["wt"] for g in range(G)]
+    rng = np.random.default_rng(6)
+    chan = (np.sort(np.stack([rng.choice(K, nS, replace=False) for _ in range(G)]), 1)
+            .astype(np.int32) if nS else None)
+    _run(orc, fmt, x, off, chan, wts)
+
+
 def test_all_rows_in_one_group(orc):
     need_gpu()
     off = np.array([0, 0, 0, 150, 150], np.int32)
