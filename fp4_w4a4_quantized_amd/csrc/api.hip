@@ -524,7 +524,7 @@ int fp4q_grouped_gemm_gather(fp4q_format_t fmt, int64_t total_rows, int64_t N, i
   fp4q::launch_gemm_big_grouped(fmt, total_rows, N, K, group_offsets, num_groups, a_q, a_s, a_ts,
                                 b_q, b_s, b_ts, chan_idx, n_chan, resid,
                                 n_chan > 0 ? comp_w : nullptr, y, y_dtype == FP4Q_OUT_BF16, nullptr,
-                                static_cast<hipStream_t>(stream), row_src);
+                                static_cast<hipStream_t>(stream), row_src, tokens);
   return check_launch();
 }
 

@@ -69,7 +69,8 @@ int launch_gemm_big_grouped(int fmt, int64_t total_rows, int64_t N, int64_t K,
                             const float* ats, const uint8_t* bq, const uint8_t* bs,
                             const float* bts, const int32_t* chan, int nS,
                             const uint16_t* resid, const uint8_t* bsel_pre, void* y, int y_bf16,
-                            void* ws, hipStream_t stream, const int32_t* row_src = nullptr);
+                            void* ws, hipStream_t stream, const int32_t* row_src = nullptr,
+                            int64_t src_rows = 0);
 int launch_gemm_big(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const uint8_t* aq,
                     const uint8_t* as, const float* ats, const uint8_t* bq, const uint8_t* bs,
                     const float* bts, const int32_t* chan, int nS, const uint16_t* resid,

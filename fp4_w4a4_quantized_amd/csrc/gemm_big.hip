@@ -984,9 +984,13 @@ struct G4Layout {
 // This wave's loads of stage s: A groups 2w, 2w + 1; B groups 8w .. 8w + 7;
 // scale instructions 5w .. 5w + 4 of 20 (4 for A: dword d, 64-row chunk c;
 // 16 for B).  Compensation stages load R pieces and the prepared B_S blocks
-// into the same places, and placeholders keep the count.
+// into the same places, and placeholders keep the count.  GA (rows of A
+// gathered by row_src): the lane's A code offsets gao[i] (group 2w + i) and
+// scale offsets gso[c] (chunk c) from the token matrix's base, fixed per tile.
+template <bool GA>
 __device__ __forceinline__ void g4_issue(const BigArgs& p, int s, int wave, int lane,
-                                         const TileCtx& tc, uint8_t* st) {
+                                         const TileCtx& tc, uint8_t* st, const uint32_t (&gao)[2],
+                                         const uint32_t (&gso)[2]) {
   using GL = G4Layout;
   const int64_t r0 = tc.r0, c0 = tc.c0;
   const int rlast = (int)(tc.rend - 1 - r0), clast = (int)(p.N - 1 - c0);
@@ -1016,14 +1020,14 @@ __device__ __forceinline__ void g4_issue(const BigArgs& p, int s, int wave, int 
   }
   const int kt = s;
   const int64_t K2 = p.K >> 1, KS = p.K >> 4;
-  const uint8_t* ab = p.aq + r0 * K2 + kt * 64;
+  const uint8_t* ab = p.aq + (GA ? 0 : r0 * K2) + kt * 64;
   const uint8_t* bb = tc.bq + c0 * K2 + kt * 64;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int g = 2 * wave + i;
     int r = 16 * g + (lane & 15);
     r = r < rlast ? r : rlast;
-    lds_load16s(ab, (uint32_t)(r * K2 + (lane >> 4) * 16), st + GL::A + g * GB_GRP);
+    lds_load16s(ab, GA ? gao[i] : (uint32_t)(r * K2 + (lane >> 4) * 16), st + GL::A + g * GB_GRP);
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -1039,7 +1043,7 @@ __device__ __forceinline__ void g4_issue(const BigArgs& p, int s, int wave, int 
       const int d = n >> 1, c = n & 1;
       int r = 64 * c + lane;
       r = r < rlast ? r : rlast;
-      lds_load4s(p.as + r0 * KS + kt * 8 + 4 * d, (uint32_t)(r * KS),
+      lds_load4s(p.as + (GA ? 0 : r0 * KS) + kt * 8 + 4 * d, GA ? gso[c] : (uint32_t)(r * KS),
                  st + GL::SA + (d * G4_TM + 64 * c) * 4);
     } else {
       const int m = n - 4, d = m >> 3, c = m & 7;
@@ -1074,6 +1078,7 @@ __device__ __forceinline__ void g4_read_half(const uint8_t* st, int wave, int la
         st + GL::SB + (h * G4_TN + wave * 128 + 32 * j + (lane & 31)) * 4);
 }
 
+template <bool GA>
 __global__ void __launch_bounds__(256, 1) k_gemm_nv4g(BigArgs args) {
   using GL = G4Layout;
   constexpr int L = GL::LOADS;
@@ -1136,13 +1141,34 @@ __global__ void __launch_bounds__(256, 1) k_gemm_nv4g(BigArgs args) {
   tc.bs = p.bs + (int64_t)grp * p.N * (p.K >> 4);
   tc.bsel = p.bsel + (int64_t)grp * ((p.N + 15) / 16) * p.nc * 1024;
   tc.src = nullptr;
+  // gathering: this lane's source rows of the tile (rows past the group
+  // repeat its last row), as byte offsets into the token matrix's codes and
+  // scales (the host keeps them below 2^32)
+  uint32_t gao[2] = {0, 0}, gso[2] = {0, 0};
+  if (GA) {
+    const int64_t K2 = p.K >> 1, KS = p.K >> 4;
+    const int rlast = (int)(tc.rend - 1 - tc.r0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      int r = 16 * (2 * wave + i) + (lane & 15);
+      r = r < rlast ? r : rlast;
+      gao[i] = (uint32_t)(p.row_src[tc.r0 + r] * K2 + (lane >> 4) * 16);
+    }
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      int r = 64 * cc + lane;
+      r = r < rlast ? r : rlast;
+      gso[cc] = (uint32_t)(p.row_src[tc.r0 + r] * KS);
+    }
+  }
 
   const int nk = p.nk, ns = p.nk + p.nc;
   const float c = p.cts ? *p.cts : 1.0f;
-  const float tx = p.ats[grp] / c, tw = p.bts[grp] * c;
+  // gathered rows share the token matrix's one tensor scale
+  const float tx = p.ats[GA ? 0 : grp] / c, tw = p.bts[grp] * c;
   auto stage = [&](int s) __attribute__((always_inline)) { return sStage + (s % 3) * GL::BYTES; };
   auto issue = [&](int s) __attribute__((always_inline)) {
-    g4_issue(p, s, wave, lane, tc, stage(s));
+    g4_issue<GA>(p, s, wave, lane, tc, stage(s), gao, gso);
   };
   issue(0);
   if (ns > 1) issue(1);
@@ -1354,7 +1380,8 @@ int launch_gemm_big_grouped(int fmt, int64_t total_rows, int64_t N, int64_t K,
                             const float* ats, const uint8_t* bq, const uint8_t* bs,
                             const float* bts, const int32_t* chan, int nS,
                             const uint16_t* resid, const uint8_t* bsel_pre, void* y, int y_bf16,
-                            void* ws, hipStream_t stream, const int32_t* row_src) {
+                            void* ws, hipStream_t stream, const int32_t* row_src,
+                            int64_t src_rows) {
   const int nc = nS > 0 ? (nS + GB_CS - 1) / GB_CS : 0;
   // prepared compensation weights (every group's, made once) replace both
   // the gather and the in-kernel extraction
@@ -1364,12 +1391,17 @@ int launch_gemm_big_grouped(int fmt, int64_t total_rows, int64_t N, int64_t K,
             0, (int)((N + GB_TILE - 1) / GB_TILE), (int)(K / 128), nc, off, G, row_src};
   const bool gather = nS > GB_XS_MAX && !prepared;
   const bool xs = nS > 0 && nS <= GB_XS_MAX && !prepared;
-  if (fmt == FP4Q_NVFP4 && !xs && row_src == nullptr) {
+  // the gathering form keeps 32-bit offsets into the token matrix
+  const bool ga32 = row_src == nullptr || src_rows * (K / 2) <= (int64_t)UINT32_MAX;
+  if (fmt == FP4Q_NVFP4 && !xs && ga32) {
     // 128 x 512 tiles; every group adds at most one partial row tile
     a.nt = (int)((N + G4_TN - 1) / G4_TN);
     const unsigned g4 = (unsigned)(((total_rows + G4_TM - 1) / G4_TM + G) * a.nt);
     if (gather) launch_gather<FP4Q_NVFP4>(false, bq, bs, N, K, chan, nS, nc, G, bsel, stream);
-    hipLaunchKernelGGL(k_gemm_nv4g, dim3(g4), dim3(256), 0, stream, a);
+    if (row_src)
+      hipLaunchKernelGGL(k_gemm_nv4g<true>, dim3(g4), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL(k_gemm_nv4g<false>, dim3(g4), dim3(256), 0, stream, a);
     return 0;
   }
   // every group adds at most one partial 256-row tile
