@@ -455,8 +455,9 @@ def build_moe(name, cfg, data, args, dev):
     import torch
 
     import fp4_w4a4_quantized_amd as fq
-    if args.channels != "fixed" or args.residual != "bf16":
-        sys.exit("moe_nvfp4 takes the fixed per-expert channel lists and the BF16 residual")
+    if args.channels != "fixed":
+        sys.exit("moe_nvfp4 takes the fixed per-expert channel lists")
+    r4 = args.residual == "fp4"   # each expert's residual quantized again, own tensor scale
     s = Step()
     s.select = None
     fmt = fq.NVFP4
@@ -470,6 +471,8 @@ def build_moe(name, cfg, data, args, dev):
     gather = args.moe_quant == "token-gather"
     if gather and not (args.comp_weights == "prepared" or cfg["n_s"] == 0):
         sys.exit("--moe-quant token-gather streams the prepared compensation weights")
+    if r4 and moe_tok:
+        sys.exit("--residual fp4 on moe_nvfp4 takes the per-expert quantization")
     off = up(data["offsets"])
     G = int(data["offsets"].size - 1)
     rows = int(data["offsets"][-1])
@@ -486,7 +489,8 @@ def build_moe(name, cfg, data, args, dev):
 
     wgu = qexperts(data["wt_gate_up"])
     wdn = qexperts(data["wt_down"])
-    prepared = args.comp_weights == "prepared" and nS > 0
+    # the second-pass residual GEMM takes B_S from the packed weights
+    prepared = args.comp_weights == "prepared" and nS > 0 and not r4
     if prepared:  # made once per expert weight set, like its quantization
         wgu = wgu + (fq.grouped_comp_weights(fmt, wgu[0], wgu[1], cg),)
         wdn = wdn + (fq.grouped_comp_weights(fmt, wdn[0], wdn[1], cd),)
@@ -500,6 +504,13 @@ def build_moe(name, cfg, data, args, dev):
             r=torch.empty((r, nS), dtype=torch.int16, device=dev),
             ws=torch.zeros(max(fq.quantize_workspace_bytes(fmt, r, k, G), 16),
                            dtype=torch.uint8, device=dev))
+        if r4:
+            bufs[tag].update(
+                rq=torch.empty((r, nS // 2), dtype=torch.uint8, device=dev),
+                rs=torch.empty((r, nS // blk), dtype=torch.uint8, device=dev),
+                rt=torch.empty(G, dtype=torch.float32, device=dev),
+                rws=torch.zeros(max(fq.quantize_workspace_bytes(fmt, r, nS, G), 16),
+                                dtype=torch.uint8, device=dev))
     ygu = torch.empty((rows, I2), dtype=torch.float32, device=dev)
     ydn = torch.empty((rows, H), dtype=torch.float32, device=dev)
 
@@ -525,15 +536,25 @@ def build_moe(name, cfg, data, args, dev):
             b = bufs[tag]
             fq.quantize_into(fmt, fq.ROWMAJOR, xin, off, G, ch, nS, b["q"], b["s"], b["t"],
                              b["r"], b["ws"])
+            if r4:
+                fq.quantize_into(fmt, fq.ROWMAJOR, b["r"], off, G, None, 0, b["rq"], b["rs"],
+                                 b["rt"], None, b["rws"])
 
     gws_bytes = max(fq.grouped_gemm_workspace_bytes(fmt, rows, I2, H, G, nS),
                     fq.grouped_gemm_workspace_bytes(fmt, rows, H, I, G, nS))
+    if r4:
+        gws_bytes = max(fq.grouped_gemm_residual_fp4_workspace_bytes(fmt, rows, I2, H, G, nS),
+                        fq.grouped_gemm_residual_fp4_workspace_bytes(fmt, rows, H, I, G, nS))
     gws = torch.empty(gws_bytes, dtype=torch.uint8, device=dev) if gws_bytes else None
 
     def gemm(i):
         for tag, w, y, n, k, ch in (("gu", wgu, ygu, I2, H, cg), ("dn", wdn, ydn, H, I, cd)):
             b = bufs[tag]
-            if gather and tag == "gu":
+            if r4:
+                fq.grouped_gemm_residual_fp4_into(fmt, rows, n, k, off, G, b["q"], b["s"], b["t"],
+                                                  w[0], w[1], w[2], ch, nS, b["rq"], b["rs"],
+                                                  b["rt"], y, 0, gws)
+            elif gather and tag == "gu":
                 fq.grouped_gemm_gather_into(fmt, rows, n, k, off, G, src, cfg["tokens"], tq, tsc,
                                             tts, w[0], w[1], w[2], ch, nS, b["r"],
                                             w[3] if prepared else None, y, 0)
@@ -552,7 +573,9 @@ def build_moe(name, cfg, data, args, dev):
     # algorithmic bytes: activations (codes, scales, residual, channel lists),
     # the active experts' packed weights, FP32 outputs, offsets and tensor scales
     wb = active * (I2 * H // 2 + I2 * H // blk + H * I // 2 + H * I // blk)
-    s.gemm_bytes = (rows * (H + I) // 2 + rows * (H + I) // blk + 2 * rows * nS * 2 +
+    # the residual: BF16, or (second pass) its FP4 codes, scales and tensor scales
+    rbytes = (2 * (rows * nS // 2 + rows * nS // blk) + 2 * G * 4) if r4 else 2 * rows * nS * 2
+    s.gemm_bytes = (rows * (H + I) // 2 + rows * (H + I) // blk + rbytes +
                     2 * G * nS * 4 + wb + rows * (I2 + H) * 4 + 2 * (G + 1) * 4 + 4 * G * 4)
     s.extra_bytes = (active * (fq.comp_weights_bytes(fmt, fq.ROWMAJOR, I2, H, nS) +
                                fq.comp_weights_bytes(fmt, fq.ROWMAJOR, H, I, nS))
@@ -567,12 +590,14 @@ def build_moe(name, cfg, data, args, dev):
     else:
         gu_bytes = rows * H * 2 + rows * H // 2 + rows * H // blk + rows * nS * 2 + G * 4
     s.quant_bytes = gu_bytes + dn_bytes
+    if r4:  # the second pass reads R and writes its codes and scales, per layer
+        s.quant_bytes += 2 * (rows * nS * 2 + rows * nS // 2 + rows * nS // blk + G * 4)
     s.select_bytes = None
     s.mfma = False
     s.wl = {"workload": name, "format": "nvfp4", "tokens": cfg["tokens"], "experts": G,
             "top_k": cfg["top_k"], "hidden": H, "inter": I, "routed_rows": rows,
             "n_s_per_expert": nS, "max_expert_rows": int(loads.max()),
-            "moe_quant": args.moe_quant,
+            "moe_quant": args.moe_quant, "residual": args.residual,
             "comp_weights": "prepared" if prepared else "inkernel",
             "empty_experts": int((loads == 0).sum())}
     s.keep = (wgu, wdn, bufs, ygu, ydn, gws, xg, xd, cg, cd, off)

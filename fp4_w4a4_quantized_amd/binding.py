@@ -104,6 +104,13 @@ def lib():
         L.fp4q_gemm_residual_fp4.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, P, P, P, P,
                                              P, P, P, i32, P, P, P, P, ctypes.c_int, i64, P, sz,
                                              P]
+        L.fp4q_grouped_gemm_residual_fp4_workspace_bytes.restype = sz
+        L.fp4q_grouped_gemm_residual_fp4_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i64,
+                                                                     i32, i32]
+        L.fp4q_grouped_gemm_residual_fp4.restype = ctypes.c_int
+        L.fp4q_grouped_gemm_residual_fp4.argtypes = [ctypes.c_int, i64, i64, i64, P, i32, P, P, P,
+                                                     P, P, P, P, i32, P, P, P, P, ctypes.c_int, P,
+                                                     sz, P]
         L.fp4q_grouped_gemm.restype = ctypes.c_int
         L.fp4q_grouped_gemm.argtypes = [ctypes.c_int, i64, i64, i64, P, i32, P, P, P, P, P, P, P,
                                         i32, P, P, ctypes.c_int, P, sz, P]
@@ -227,6 +234,11 @@ def gemm_residual_fp4_workspace_bytes(fmt, layout, M, N, K, n_chan) -> int:
     return lib().fp4q_gemm_residual_fp4_workspace_bytes(fmt, layout, M, N, K, n_chan)
 
 
+def grouped_gemm_residual_fp4_workspace_bytes(fmt, total_rows, N, K, num_groups, n_chan) -> int:
+    return lib().fp4q_grouped_gemm_residual_fp4_workspace_bytes(fmt, total_rows, N, K, num_groups,
+                                                                n_chan)
+
+
 def grouped_gemm_workspace_bytes(fmt, total_rows, N, K, num_groups, n_chan) -> int:
     return lib().fp4q_grouped_gemm_workspace_bytes(fmt, total_rows, N, K, num_groups, n_chan)
 
@@ -269,6 +281,18 @@ def gemm_residual_fp4_into(fmt, layout, M, N, K, a_q, a_s, a_ts, b_q, b_s, b_ts,
                                       N if ldy is None else ldy, _ptr(workspace), ws_bytes,
                                       _stream(stream))
     _check("fp4q_gemm_residual_fp4", rc)
+
+
+def grouped_gemm_residual_fp4_into(fmt, total_rows, N, K, group_offsets, num_groups, a_q, a_s,
+                                   a_ts, b_q, b_s, b_ts, chan_idx, n_chan, r_q, r_s, r_ts, y,
+                                   y_dtype=OUT_F32, workspace=None, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().fp4q_grouped_gemm_residual_fp4(fmt, total_rows, N, K, _ptr(group_offsets),
+                                              num_groups, _ptr(a_q), _ptr(a_s), _ptr(a_ts),
+                                              _ptr(b_q), _ptr(b_s), _ptr(b_ts), _ptr(chan_idx),
+                                              n_chan, _ptr(r_q), _ptr(r_s), _ptr(r_ts), _ptr(y),
+                                              y_dtype, _ptr(workspace), ws_bytes, _stream(stream))
+    _check("fp4q_grouped_gemm_residual_fp4", rc)
 
 
 def grouped_gemm_into(fmt, total_rows, N, K, group_offsets, num_groups, a_q, a_s, a_ts, b_q,
@@ -501,6 +525,25 @@ def gemm_residual_fp4(fmt, a, b, chan_idx, r, y_dtype=OUT_F32, stream=None):
     gemm_residual_fp4_into(fmt, layout, M, N, K, a["q"], a["scales"], a["tscale"], b["q"],
                            b["scales"], b["tscale"], chan_idx, nS, r["q"], r["scales"],
                            r["tscale"], y, y_dtype, N, ws, stream)
+    return y
+
+
+def grouped_gemm_residual_fp4(fmt, group_offsets, a, bq, bs, bts, chan_idx, r, y_dtype=OUT_F32,
+                              stream=None):
+    """grouped_gemm() with the second-pass residual: r = quantize(fmt,
+    a["resid"], group_offsets) (row-major, one tensor scale per group)."""
+    total, K = a["q"].shape[0], a["q"].shape[1] * 2
+    G = group_offsets.numel() - 1
+    N = bq.shape[1]
+    nS = chan_idx.numel() // G
+    dev = a["q"].device
+    y = torch.empty((total, N), dtype=torch.float32 if y_dtype == OUT_F32 else torch.bfloat16,
+                    device=dev)
+    wsb = grouped_gemm_residual_fp4_workspace_bytes(fmt, total, N, K, G, nS)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
+    grouped_gemm_residual_fp4_into(fmt, total, N, K, group_offsets, G, a["q"], a["scales"],
+                                   a["tscale"], bq, bs, bts, chan_idx, nS, r["q"], r["scales"],
+                                   r["tscale"], y, y_dtype, ws, stream)
     return y
 
 

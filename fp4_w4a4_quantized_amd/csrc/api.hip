@@ -442,6 +442,60 @@ int fp4q_grouped_gemm(fp4q_format_t fmt, int64_t total_rows, int64_t N, int64_t 
   return check_launch();
 }
 
+size_t fp4q_grouped_gemm_residual_fp4_workspace_bytes(fp4q_format_t fmt, int64_t total_rows,
+                                                      int64_t N, int64_t K, int32_t num_groups,
+                                                      int32_t n_chan) {
+  if (total_rows <= 0 || N <= 0 || K <= 0 || n_chan <= 0 || num_groups < 1) return 0;
+  return deq_resid_bytes(total_rows, n_chan) +
+         fp4q_grouped_gemm_workspace_bytes(fmt, total_rows, N, K, num_groups, n_chan);
+}
+
+int fp4q_grouped_gemm_residual_fp4(fp4q_format_t fmt, int64_t total_rows, int64_t N, int64_t K,
+                                   const int32_t* group_offsets, int32_t num_groups,
+                                   const uint8_t* a_q, const uint8_t* a_s, const float* a_ts,
+                                   const uint8_t* b_q, const uint8_t* b_s, const float* b_ts,
+                                   const int32_t* chan_idx, int32_t n_chan, const uint8_t* r_q,
+                                   const uint8_t* r_s, const float* r_ts, void* y,
+                                   fp4q_dtype_t y_dtype, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  if (!fmt_ok(fmt)) return FP4Q_ERR_INVALID;
+  if (n_chan < 0 || (n_chan > 0) != (r_q != nullptr) || (n_chan > 0) != (r_s != nullptr))
+    return FP4Q_ERR_INVALID;
+  if (n_chan % blk_of(fmt) != 0) return FP4Q_ERR_INVALID;
+  if (fmt == FP4Q_NVFP4 && (n_chan > 0) != (r_ts != nullptr)) return FP4Q_ERR_INVALID;
+  if (fmt == FP4Q_MXFP4 && r_ts) return FP4Q_ERR_INVALID;
+  if (num_groups < 1 || !group_offsets) return FP4Q_ERR_INVALID;
+  if (num_groups > MAX_GROUPS) return FP4Q_ERR_UNSUPPORTED;
+  const bool work = total_rows > 0 && N > 0 && n_chan > 0;
+  const size_t need = work ? fp4q_grouped_gemm_residual_fp4_workspace_bytes(
+                                 fmt, total_rows, N, K, num_groups, n_chan)
+                           : 0;
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
+    return FP4Q_ERR_WORKSPACE;
+  // the decoded residual goes to the front of the workspace and stands in
+  // for fp4q_grouped_gemm's resid (an empty product only needs a non-null
+  // stand-in, never read)
+  alignas(16) static const uint16_t kNoRows[8] = {};
+  uint16_t* rdeq = work ? static_cast<uint16_t*>(workspace) : nullptr;
+  const uint16_t* rval = work ? rdeq : (n_chan > 0 ? kNoRows : nullptr);
+  int rc = validate_gemm_common(fmt, N, K, a_q, a_s, a_ts, b_q, b_s, b_ts, chan_idx, n_chan,
+                                rval, y, y_dtype, total_rows);
+  if (rc != FP4Q_OK) return rc;
+  if ((N + 127) / 128 > 65535) return FP4Q_ERR_UNSUPPORTED;
+  if (total_rows * (int64_t)n_chan / 8 >= ((int64_t)1 << 31)) return FP4Q_ERR_UNSUPPORTED;
+  if (total_rows == 0 || N == 0) return FP4Q_OK;
+  if (injected_failure()) return FP4Q_ERR_HIP;
+  clear_error();
+  void* gws = work ? static_cast<uint8_t*>(workspace) + deq_resid_bytes(total_rows, n_chan)
+                   : nullptr;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (work) fp4q::launch_deq_resid(fmt, total_rows, n_chan, r_q, r_s, rdeq, st);
+  fp4q::launch_gemm(fmt, false, total_rows, N, K, group_offsets, num_groups, a_q, a_s, a_ts, b_q,
+                    b_s, b_ts, chan_idx, n_chan, rval, r_ts, y, y_dtype == FP4Q_OUT_BF16, N, gws,
+                    st);
+  return check_launch();
+}
+
 size_t fp4q_grouped_comp_weights_bytes(fp4q_format_t fmt, int64_t N, int64_t K,
                                        int32_t num_groups, int32_t n_chan) {
   (void)fmt;
@@ -522,7 +576,7 @@ int fp4q_grouped_gemm_gather(fp4q_format_t fmt, int64_t total_rows, int64_t N, i
   if (injected_failure()) return FP4Q_ERR_HIP;
   clear_error();
   fp4q::launch_gemm_big_grouped(fmt, total_rows, N, K, group_offsets, num_groups, a_q, a_s, a_ts,
-                                b_q, b_s, b_ts, chan_idx, n_chan, resid,
+                                b_q, b_s, b_ts, chan_idx, n_chan, resid, nullptr,
                                 n_chan > 0 ? comp_w : nullptr, y, y_dtype == FP4Q_OUT_BF16, nullptr,
                                 static_cast<hipStream_t>(stream), row_src, tokens);
   return check_launch();

@@ -48,7 +48,8 @@ GemmPath gemm_path(int64_t M, int64_t N, int64_t K, int nS);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int nS);
 
 // cts: device tensor scale of the compensation term (NVFP4 second-pass
-// residual), or null for 1: y = t_w (t_x main + cts comp).
+// residual), or null for 1: y = t_w (t_x main + cts comp); grouped: one per
+// group, cts[g].
 int launch_gemm(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const int32_t* off, int G,
                 const uint8_t* aq, const uint8_t* as, const float* ats, const uint8_t* bq,
                 const uint8_t* bs, const float* bts, const int32_t* chan, int nS,
@@ -68,9 +69,9 @@ int launch_gemm_big_grouped(int fmt, int64_t total_rows, int64_t N, int64_t K,
                             const int32_t* off, int G, const uint8_t* aq, const uint8_t* as,
                             const float* ats, const uint8_t* bq, const uint8_t* bs,
                             const float* bts, const int32_t* chan, int nS,
-                            const uint16_t* resid, const uint8_t* bsel_pre, void* y, int y_bf16,
-                            void* ws, hipStream_t stream, const int32_t* row_src = nullptr,
-                            int64_t src_rows = 0);
+                            const uint16_t* resid, const float* cts, const uint8_t* bsel_pre,
+                            void* y, int y_bf16, void* ws, hipStream_t stream,
+                            const int32_t* row_src = nullptr, int64_t src_rows = 0);
 int launch_gemm_big(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const uint8_t* aq,
                     const uint8_t* as, const float* ats, const uint8_t* bq, const uint8_t* bs,
                     const float* bts, const int32_t* chan, int nS, const uint16_t* resid,

@@ -304,7 +304,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs p) {
   // (tw c) ((tx / c) main + comp); with c = 1 the factors are tw and tx exactly
   float tx = 1.0f, tw = 1.0f;
   if (FMT == FP4Q_NVFP4) {
-    const float c = p.cts ? *p.cts : 1.0f;
+    const float c = p.cts ? p.cts[GROUPED ? g : 0] : 1.0f;
     tx = p.ats[GROUPED ? g : 0] / c;
     tw = p.bts[GROUPED ? g : 0] * c;
 #pragma unroll
@@ -446,7 +446,7 @@ int launch_gemm(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const int3
   if (M == 0 || N == 0) return 0;
   if (off != nullptr && big_grouped_eligible(N, K, nS)) {
     launch_gemm_big_grouped(fmt, M, N, K, off, G, aq, as, ats, bq, bs, bts, chan, nS, resid,
-                            bsel_pre, y, y_bf16, ws, stream);
+                            cts, bsel_pre, y, y_bf16, ws, stream);
     return 0;
   }
   if (off != nullptr) {

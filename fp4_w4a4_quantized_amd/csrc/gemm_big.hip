@@ -604,7 +604,7 @@ __global__ void __launch_bounds__(GB_T, 1) k_gemm_big(BigArgs args) {
   // with c = 1 both factors are exactly t_w and t_x
   float tx = 1.0f, tw = 1.0f;
   if (FMT == FP4Q_NVFP4) {
-    const float c = p.cts ? *p.cts : 1.0f;
+    const float c = p.cts ? p.cts[GR ? grp : 0] : 1.0f;
     tx = p.ats[GR == 2 ? 0 : grp] / c;
     tw = p.bts[grp] * c;
   }
@@ -1163,7 +1163,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_nv4g(BigArgs args) {
   }
 
   const int nk = p.nk, ns = p.nk + p.nc;
-  const float c = p.cts ? *p.cts : 1.0f;
+  const float c = p.cts ? p.cts[grp] : 1.0f;
   // gathered rows share the token matrix's one tensor scale
   const float tx = p.ats[GA ? 0 : grp] / c, tw = p.bts[grp] * c;
   auto stage = [&](int s) __attribute__((always_inline)) { return sStage + (s % 3) * GL::BYTES; };
@@ -1379,15 +1379,15 @@ int launch_gemm_big_grouped(int fmt, int64_t total_rows, int64_t N, int64_t K,
                             const int32_t* off, int G, const uint8_t* aq, const uint8_t* as,
                             const float* ats, const uint8_t* bq, const uint8_t* bs,
                             const float* bts, const int32_t* chan, int nS,
-                            const uint16_t* resid, const uint8_t* bsel_pre, void* y, int y_bf16,
-                            void* ws, hipStream_t stream, const int32_t* row_src,
-                            int64_t src_rows) {
+                            const uint16_t* resid, const float* cts, const uint8_t* bsel_pre,
+                            void* y, int y_bf16, void* ws, hipStream_t stream,
+                            const int32_t* row_src, int64_t src_rows) {
   const int nc = nS > 0 ? (nS + GB_CS - 1) / GB_CS : 0;
   // prepared compensation weights (every group's, made once) replace both
   // the gather and the in-kernel extraction
   const bool prepared = bsel_pre != nullptr && nS > 0;
   uint8_t* bsel = prepared ? const_cast<uint8_t*>(bsel_pre) : static_cast<uint8_t*>(ws);
-  BigArgs a{total_rows, N, K, aq, as, ats, bq, bs, bts, nS, resid, bsel, chan, nullptr, y, y_bf16, N,
+  BigArgs a{total_rows, N, K, aq, as, ats, bq, bs, bts, nS, resid, bsel, chan, cts, y, y_bf16, N,
             0, (int)((N + GB_TILE - 1) / GB_TILE), (int)(K / 128), nc, off, G, row_src};
   const bool gather = nS > GB_XS_MAX && !prepared;
   const bool xs = nS > 0 && nS <= GB_XS_MAX && !prepared;

@@ -415,6 +415,28 @@ int fp4q_gemm_residual_fp4(fp4q_format_t fmt, fp4q_layout_t layout, int64_t M, i
                            const uint8_t* r_s, const float* r_ts, void* y, fp4q_dtype_t y_dtype,
                            int64_t ldy, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Grouped form (QUADS abstract: NVFP4 rollout for MoE; explainer section
+ * 2.2 B): per group g (rows group_offsets[g] .. group_offsets[g+1]) the
+ * dense form above with the group's weights, tensor scales and channel
+ * list, and the group's residual quantized with its own tensor scale:
+ * r_q, r_s from fp4q_quantize(ROWMAJOR) of R [total_rows, n_chan] with the
+ * same group offsets, r_ts device f32 [num_groups] (NVFP4; NULL for MXFP4).
+ * Other arguments as fp4q_grouped_gemm; workspace of
+ * fp4q_grouped_gemm_residual_fp4_workspace_bytes() bytes, 16-byte aligned.
+ * Errors as the dense form and fp4q_grouped_gemm. */
+size_t fp4q_grouped_gemm_residual_fp4_workspace_bytes(fp4q_format_t fmt, int64_t total_rows,
+                                                      int64_t N, int64_t K, int32_t num_groups,
+                                                      int32_t n_chan);
+
+int fp4q_grouped_gemm_residual_fp4(fp4q_format_t fmt, int64_t total_rows, int64_t N, int64_t K,
+                                   const int32_t* group_offsets, int32_t num_groups,
+                                   const uint8_t* a_q, const uint8_t* a_s, const float* a_ts,
+                                   const uint8_t* b_q, const uint8_t* b_s, const float* b_ts,
+                                   const int32_t* chan_idx, int32_t n_chan, const uint8_t* r_q,
+                                   const uint8_t* r_s, const float* r_ts, void* y,
+                                   fp4q_dtype_t y_dtype, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
 /* ------------------------------------------------------------------------
  * Online channel selection.  Explainer of the QUADS paper, section 2.2 B:
  * a binary mask keeps the top-k channels by residual magnitude.  With R the

@@ -321,6 +321,34 @@ def gemm_full_r4(fmt, aq, as_, ats, bq, bs, bts, chan_idx, rq, rs, rts):
     return y, ya
 
 
+def grouped_gemm_points_r4(fmt, offsets, aq, as_, ats, bq, bs, bts, chan_idx, rq, rs, rts, pm,
+                           pn):
+    """Grouped form of gemm_points_r4 (QUADS abstract: MoE rollout; explainer
+    section 2.2 B): each expert g's rows offsets[g] .. offsets[g+1] are the
+    dense second-pass-residual GEMM with its own weights bq[g], bs[g], tensor
+    scales ats[g], bts[g], channel list chan_idx[g] and residual tensor scale
+    rts[g]; rq, rs [rows, ...] are indexed by global row.  Points pm, pn."""
+    off = np.asarray(offsets, np.int64)
+    G = off.size - 1
+    ci = None if chan_idx is None else np.asarray(chan_idx, np.int32).reshape(G, -1)
+    pm, pn = np.asarray(pm, np.int64), np.asarray(pn, np.int64)
+    y = np.zeros(pm.size, np.float64)
+    ya = np.zeros(pm.size, np.float64)
+    grp = np.searchsorted(off, pm, side="right") - 1
+    for g in range(G):
+        sel = np.nonzero(grp == g)[0]
+        if sel.size == 0:
+            continue
+        r0, r1 = int(off[g]), int(off[g + 1])
+        yg, yag = gemm_points_r4(fmt, aq[r0:r1], as_[r0:r1],
+                                 1.0 if ats is None else float(ats[g]), bq[g], bs[g],
+                                 1.0 if bts is None else float(bts[g]),
+                                 None if ci is None else ci[g], rq[r0:r1], rs[r0:r1],
+                                 1.0 if rts is None else float(rts[g]), pm[sel] - r0, pn[sel])
+        y[sel], ya[sel] = yg, yag
+    return y, ya
+
+
 def grouped_gemm_points(fmt, offsets, aq, as_, ats, bq, bs, bts, chan_idx, resid, pm, pn):
     """Grouped GEMM at points; bq [G, N, K/2], bs [G, N, K/blk], ats/bts [G],
     chan_idx [G, nS], resid [rows, nS] indexed by global row."""

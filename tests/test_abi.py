@@ -241,6 +241,33 @@ def test_grouped_gemm_gather_rejects(L):
         L.fp4q_test_hook(0, 0)
 
 
+def test_grouped_gemm_residual_fp4_rejects(L):
+    P, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    L.fp4q_grouped_gemm_residual_fp4.argtypes = [ctypes.c_int, i64, i64, i64, P, i32, P, P, P, P,
+                                                 P, P, P, i32, P, P, P, P, ctypes.c_int, P, sz, P]
+
+    def f(fmt=0, rows=64, N=256, K=256, off=A, G=2, aq=A, as_=A, ats=B, bq=B, bs=B, bts=B,
+          chan=A, nS=16, rq=A, rs=A, rts=B, y=A, dt=0, ws=A, wsb=1 << 30):
+        return L.fp4q_grouped_gemm_residual_fp4(fmt, rows, N, K, off, G, aq, as_, ats, bq, bs, bts,
+                                                chan, nS, rq, rs, rts, y, dt, ws, wsb, None)
+    assert f(nS=8) == INVALID                      # not a multiple of the block
+    assert f(rq=None) == INVALID
+    assert f(rts=None) == INVALID                  # NVFP4: one residual scale per group
+    assert f(fmt=1, ats=None, bts=None, nS=32) == INVALID   # MXFP4 takes none
+    assert f(off=None) == INVALID
+    assert f(G=3000) == UNSUPPORTED
+    assert f(ws=None) == WORKSPACE
+    assert f(wsb=16) == WORKSPACE
+    assert f(rows=0) == 0
+    need = L.fp4q_grouped_gemm_residual_fp4_workspace_bytes(0, 64, 256, 256, 2, 16)
+    assert need >= 64 * 16 * 2                     # the decoded residual at least
+    try:
+        assert L.fp4q_test_hook(1, 34) == 0
+        assert f() == HIP_ERR and L.fp4q_last_hip_error() == 34
+    finally:
+        L.fp4q_test_hook(0, 0)
+
+
 def test_quantize_status_rejects(L):
     need = L.fp4q_quantize_workspace_bytes(0, 4, 64, 1)
     st = ctypes.c_int32(0)

@@ -103,3 +103,88 @@ def test_residual_fp4_reduces_to_bf16_path_for_lossless_residual(orc):
                            qa["resid"])
     assert_gemm_close(y4, yo, ya)
     assert np.allclose(y4, y2, rtol=0, atol=1e-6 * ya.max())
+
+
+# ---- grouped (MoE) form: fp4q_grouped_gemm_residual_fp4 -----------------------
+
+def _grouped_case(orc, fmt, off, K, N, nS, seed):
+    G = off.size - 1
+    x = dense_case(int(off[-1]), K, 8, n_out=3, seed=seed)["x"]
+    wts = [dense_case(1, K, N, seed=seed + 10 + g)["wt"] for g in range(G)]
+    rng = np.random.default_rng(seed)
+    chan = np.sort(np.stack([rng.choice(K, nS, replace=False) for _ in range(G)]), 1)
+    chan = chan.astype(np.int32)
+    qa = orc.quantize(fmt, x, offsets=off, chan_idx=chan)
+    qr = orc.quantize(fmt, qa["resid"], offsets=off)
+    qbs = [orc.quantize(fmt, w) for w in wts]
+    bq = np.stack([q["q"] for q in qbs])
+    bs = np.stack([q["scales"] for q in qbs])
+    bts = np.array([q["tscale"][0] for q in qbs], np.float32) if fmt == 0 else None
+    return x, chan, qa, qr, bq, bs, bts
+
+
+def _grouped_gpu(fmt, off, chan, qa, qr, bq, bs, bts):
+    a = {"q": to_dev(qa["q"]), "scales": to_dev(qa["scales"]),
+         "tscale": None if fmt else to_dev(qa["tscale"])}
+    r = {"q": to_dev(qr["q"]), "scales": to_dev(qr["scales"]),
+         "tscale": None if fmt else to_dev(qr["tscale"])}
+    y = fq.grouped_gemm_residual_fp4(fmt, to_dev(off), a, to_dev(bq), to_dev(bs),
+                                     None if fmt else to_dev(bts), to_dev(chan), r)
+    torch.cuda.synchronize()
+    return to_host(y)
+
+
+@pytest.mark.parametrize("fmt,N,nS", [(0, 300, 32),    # 256-tile kernel, B_S from the tiles
+                                      (0, 560, 128),   # 128x512 NVFP4 kernel, gathered B_S
+                                      (0, 200, 16),    # general grouped kernel
+                                      (1, 300, 32), (1, 560, 128), (1, 200, 64)])
+def test_grouped_residual_fp4_matches_oracle(orc, fmt, N, nS):
+    """Empty, single-row and multi-tile experts; each expert's residual with
+    its own tensor scale (NVFP4)."""
+    need_gpu()
+    say(f"grouped gemm fp4 residual fmt {fmt} N{N} nS{nS}")
+    off = np.array([0, 0, 1, 130, 130, 300, 555], np.int32)
+    K = 384
+    x, chan, qa, qr, bq, bs, bts = _grouped_case(orc, fmt, off, K, N, nS, seed=N + nS + fmt)
+    y = _grouped_gpu(fmt, off, chan, qa, qr, bq, bs, bts)
+    pm = np.repeat(np.arange(int(off[-1])), N)
+    pn = np.tile(np.arange(N), int(off[-1]))
+    yo, ya = orc.grouped_gemm_points_r4(fmt, off, qa["q"], qa["scales"],
+                                        None if fmt else qa["tscale"], bq, bs, bts, chan,
+                                        qr["q"], qr["scales"], None if fmt else qr["tscale"],
+                                        pm, pn)
+    assert_gemm_close(y[pm, pn], yo, ya)
+
+
+def test_grouped_residual_fp4_moe_workload(orc):
+    """The MoE gate_up layer at full size (32,768 routed rows, 128 experts,
+    32 channels each): the GPU's grouped second pass over the GPU residual
+    bit-exact against the oracle's, and the GEMM on 30,000 sampled outputs
+    plus each expert's first and last row."""
+    need_gpu()
+    say("grouped gemm fp4 residual, MoE gate_up workload")
+    from gpu_helpers import workload
+    m = workload("moe_nvfp4")
+    off, x, chan, wts = m["offsets"], m["x_perm"], m["chan_gate_up"], m["wt_gate_up"]
+    fmt, N = 0, wts.shape[1]
+    qa = orc.quantize(fmt, x, offsets=off, chan_idx=chan)
+    qr = orc.quantize(fmt, qa["resid"], offsets=off)
+    doff = to_dev(off)
+    ga = fq.quantize(fmt, to_dev(x), group_offsets=doff, chan_idx=to_dev(chan))
+    gr = fq.quantize(fmt, ga["resid"], group_offsets=doff)
+    torch.cuda.synchronize()
+    assert_quant_equal(gr, qr, fmt)
+    qbs = [fq.quantize(fmt, to_dev(wts[e])) for e in range(off.size - 1)]
+    bq = torch.stack([q["q"] for q in qbs])
+    bs = torch.stack([q["scales"] for q in qbs])
+    bts = torch.cat([q["tscale"] for q in qbs])
+    y = to_host(fq.grouped_gemm_residual_fp4(fmt, doff, ga, bq, bs, bts, to_dev(chan), gr))
+    rng = np.random.default_rng(17)
+    edge = np.concatenate([[off[g], off[g + 1] - 1] for g in range(off.size - 1)
+                           if off[g + 1] > off[g]])
+    pm = np.concatenate([rng.integers(0, x.shape[0], 30000), np.repeat(edge, 4)])
+    pn = np.concatenate([rng.integers(0, N, 30000), rng.integers(0, N, edge.size * 4)])
+    yo, ya = orc.grouped_gemm_points_r4(fmt, off, qa["q"], qa["scales"], qa["tscale"],
+                                        to_host(bq), to_host(bs), to_host(bts), chan, qr["q"],
+                                        qr["scales"], qr["tscale"], pm, pn)
+    assert_gemm_close(y[pm, pn], yo, ya)
