@@ -455,8 +455,7 @@ def build_moe(name, cfg, data, args, dev):
     import torch
 
     import fp4_w4a4_quantized_amd as fq
-    if args.channels != "fixed":
-        sys.exit("moe_nvfp4 takes the fixed per-expert channel lists")
+    online = args.channels == "online"  # each expert chooses its channels every step
     r4 = args.residual == "fp4"   # each expert's residual quantized again, own tensor scale
     s = Step()
     s.select = None
@@ -471,8 +470,9 @@ def build_moe(name, cfg, data, args, dev):
     gather = args.moe_quant == "token-gather"
     if gather and not (args.comp_weights == "prepared" or cfg["n_s"] == 0):
         sys.exit("--moe-quant token-gather streams the prepared compensation weights")
-    if r4 and moe_tok:
-        sys.exit("--residual fp4 on moe_nvfp4 takes the per-expert quantization")
+    if (r4 or online) and moe_tok:
+        sys.exit("--residual fp4 / --channels online on moe_nvfp4 take the per-expert "
+                 "quantization")
     off = up(data["offsets"])
     G = int(data["offsets"].size - 1)
     rows = int(data["offsets"][-1])
@@ -489,8 +489,9 @@ def build_moe(name, cfg, data, args, dev):
 
     wgu = qexperts(data["wt_gate_up"])
     wdn = qexperts(data["wt_down"])
-    # the second-pass residual GEMM takes B_S from the packed weights
-    prepared = args.comp_weights == "prepared" and nS > 0 and not r4
+    # the second-pass residual GEMM and channels chosen per step take B_S from
+    # the packed weights
+    prepared = args.comp_weights == "prepared" and nS > 0 and not r4 and not online
     if prepared:  # made once per expert weight set, like its quantization
         wgu = wgu + (fq.grouped_comp_weights(fmt, wgu[0], wgu[1], cg),)
         wdn = wdn + (fq.grouped_comp_weights(fmt, wdn[0], wdn[1], cd),)
@@ -504,6 +505,11 @@ def build_moe(name, cfg, data, args, dev):
             r=torch.empty((r, nS), dtype=torch.int16, device=dev),
             ws=torch.zeros(max(fq.quantize_workspace_bytes(fmt, r, k, G), 16),
                            dtype=torch.uint8, device=dev))
+        if online:
+            bufs[tag].update(
+                ch=torch.empty((G, nS), dtype=torch.int32, device=dev),
+                sws=torch.empty(max(fq.select_channels_grouped_workspace_bytes(r, k, G), 16),
+                                dtype=torch.uint8, device=dev))
         if r4:
             bufs[tag].update(
                 rq=torch.empty((r, nS // 2), dtype=torch.uint8, device=dev),
@@ -534,6 +540,12 @@ def build_moe(name, cfg, data, args, dev):
         for tag, xin, ch in ((("dn", xd, cd),) if moe_tok else
                              (("gu", xg, cg), ("dn", xd, cd))):
             b = bufs[tag]
+            if online:
+                fq.quantize_into(fmt, fq.ROWMAJOR, xin, off, G, None, 0, b["q"], b["s"], b["t"],
+                                 None, b["ws"])
+                fq.select_channels_grouped_into(fmt, xin, off, G, b["q"], b["s"], b["t"], nS,
+                                                b["ch"], b["r"], b["sws"])
+                continue
             fq.quantize_into(fmt, fq.ROWMAJOR, xin, off, G, ch, nS, b["q"], b["s"], b["t"],
                              b["r"], b["ws"])
             if r4:
@@ -550,6 +562,8 @@ def build_moe(name, cfg, data, args, dev):
     def gemm(i):
         for tag, w, y, n, k, ch in (("gu", wgu, ygu, I2, H, cg), ("dn", wdn, ydn, H, I, cd)):
             b = bufs[tag]
+            if online:
+                ch = b["ch"]
             if r4:
                 fq.grouped_gemm_residual_fp4_into(fmt, rows, n, k, off, G, b["q"], b["s"], b["t"],
                                                   w[0], w[1], w[2], ch, nS, b["rq"], b["rs"],
@@ -590,6 +604,9 @@ def build_moe(name, cfg, data, args, dev):
     else:
         gu_bytes = rows * H * 2 + rows * H // 2 + rows * H // blk + rows * nS * 2 + G * 4
     s.quant_bytes = gu_bytes + dn_bytes
+    if online:  # the selection reads x, codes and scales again, writes R and S
+        s.quant_bytes += sum(rows * k * 2 + rows * k // 2 + rows * k // blk + rows * nS * 2 +
+                             G * nS * 4 + G * 4 for k in (H, I))
     if r4:  # the second pass reads R and writes its codes and scales, per layer
         s.quant_bytes += 2 * (rows * nS * 2 + rows * nS // 2 + rows * nS // blk + G * 4)
     s.select_bytes = None
@@ -597,7 +614,7 @@ def build_moe(name, cfg, data, args, dev):
     s.wl = {"workload": name, "format": "nvfp4", "tokens": cfg["tokens"], "experts": G,
             "top_k": cfg["top_k"], "hidden": H, "inter": I, "routed_rows": rows,
             "n_s_per_expert": nS, "max_expert_rows": int(loads.max()),
-            "moe_quant": args.moe_quant, "residual": args.residual,
+            "moe_quant": args.moe_quant, "residual": args.residual, "channels": args.channels,
             "comp_weights": "prepared" if prepared else "inkernel",
             "empty_experts": int((loads == 0).sum())}
     s.keep = (wgu, wdn, bufs, ygu, ydn, gws, xg, xd, cg, cd, off)

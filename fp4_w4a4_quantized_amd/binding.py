@@ -119,6 +119,11 @@ def lib():
         L.fp4q_select_channels.restype = ctypes.c_int
         L.fp4q_select_channels.argtypes = [ctypes.c_int, ctypes.c_int, P, i64, i64, i64, P, P, P,
                                            i32, P, P, P, sz, P]
+        L.fp4q_select_channels_grouped_workspace_bytes.restype = sz
+        L.fp4q_select_channels_grouped_workspace_bytes.argtypes = [i64, i64, i32]
+        L.fp4q_select_channels_grouped.restype = ctypes.c_int
+        L.fp4q_select_channels_grouped.argtypes = [ctypes.c_int, P, i64, i64, i64, P, i32, P, P, P,
+                                                   i32, P, P, P, sz, P]
         L.fp4q_permute_quantized.restype = ctypes.c_int
         L.fp4q_permute_quantized.argtypes = [ctypes.c_int, P, i64, i64, i64, P, P, P, P, i64, P,
                                              i32, P, i32, P, P, P, P, P]
@@ -545,6 +550,38 @@ def grouped_gemm_residual_fp4(fmt, group_offsets, a, bq, bs, bts, chan_idx, r, y
                                    a["tscale"], bq, bs, bts, chan_idx, nS, r["q"], r["scales"],
                                    r["tscale"], y, y_dtype, ws, stream)
     return y
+
+
+def select_channels_grouped_workspace_bytes(rows, cols, num_groups) -> int:
+    return lib().fp4q_select_channels_grouped_workspace_bytes(rows, cols, num_groups)
+
+
+def select_channels_grouped_into(fmt, x, group_offsets, num_groups, q, scales, tensor_scale, k,
+                                 chan_out, resid_out, workspace, stream=None):
+    rows, cols = x.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().fp4q_select_channels_grouped(fmt, _ptr(x), rows, cols, x.stride(0),
+                                            _ptr(group_offsets), num_groups, _ptr(q),
+                                            _ptr(scales), _ptr(tensor_scale), k, _ptr(chan_out),
+                                            _ptr(resid_out), _ptr(workspace), ws_bytes,
+                                            _stream(stream))
+    _check("fp4q_select_channels_grouped", rc)
+
+
+def select_channels_grouped(fmt, x, group_offsets, a, k, stream=None):
+    """a = quantize(fmt, x, group_offsets) (row-major).  Returns (chan int32
+    [G, k], ascending per group; resid bf16 bits as int16 [rows, k]): each
+    group's k channels of largest residual magnitude and the residual."""
+    rows, cols = x.shape
+    G = group_offsets.numel() - 1
+    dev = x.device
+    chan = torch.empty((G, k), dtype=torch.int32, device=dev)
+    resid = torch.empty((rows, k), dtype=torch.int16, device=dev)
+    wsb = select_channels_grouped_workspace_bytes(rows, cols, G)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    select_channels_grouped_into(fmt, x, group_offsets, G, a["q"], a["scales"], a["tscale"], k,
+                                 chan, resid, ws, stream)
+    return chan, resid
 
 
 def select_channels(fmt, x, a, k, stream=None):

@@ -614,6 +614,42 @@ int fp4q_select_channels(fp4q_format_t fmt, fp4q_layout_t layout, const uint16_t
   return check_launch();
 }
 
+size_t fp4q_select_channels_grouped_workspace_bytes(int64_t rows, int64_t cols,
+                                                    int32_t num_groups) {
+  return fp4q::select_grouped_workspace_bytes(rows, cols, num_groups);
+}
+
+int fp4q_select_channels_grouped(fp4q_format_t fmt, const uint16_t* x, int64_t rows, int64_t cols,
+                                 int64_t ldx, const int32_t* group_offsets, int32_t num_groups,
+                                 const uint8_t* q, const uint8_t* scales,
+                                 const float* tensor_scale, int32_t k, int32_t* chan_out,
+                                 uint16_t* resid_out, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  if (!fmt_ok(fmt)) return FP4Q_ERR_INVALID;
+  if (rows < 0 || cols <= 0 || cols % blk_of(fmt) != 0 || ldx < cols || ldx % 8 != 0)
+    return FP4Q_ERR_INVALID;
+  if (k < 0 || k > cols) return FP4Q_ERR_INVALID;
+  if (num_groups < 1 || !group_offsets) return FP4Q_ERR_INVALID;
+  if (num_groups > MAX_GROUPS) return FP4Q_ERR_UNSUPPORTED;
+  if (fmt == FP4Q_NVFP4 && !tensor_scale) return FP4Q_ERR_INVALID;
+  if (fmt == FP4Q_MXFP4 && tensor_scale) return FP4Q_ERR_INVALID;
+  if (k > 0 && (!chan_out || !aligned(chan_out, 4))) return FP4Q_ERR_INVALID;
+  if (rows > 0 && k > 0 && (!resid_out || !aligned(resid_out, 2))) return FP4Q_ERR_INVALID;
+  if (rows > 0 && (!x || !q || !scales)) return FP4Q_ERR_INVALID;
+  if (rows > 0 && (!aligned(x, 16) || !aligned(q, 4))) return FP4Q_ERR_INVALID;
+  if (!fp4q::select_grouped_cols_ok(cols)) return FP4Q_ERR_UNSUPPORTED;
+  if (rows * (int64_t)k >= ((int64_t)1 << 31)) return FP4Q_ERR_UNSUPPORTED;
+  if (k == 0) return FP4Q_OK;
+  const size_t need = fp4q::select_grouped_workspace_bytes(rows, cols, num_groups);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return FP4Q_ERR_WORKSPACE;
+  if (injected_failure()) return FP4Q_ERR_HIP;
+  clear_error();
+  fp4q::launch_select_grouped(fmt, x, rows, cols, ldx, q, scales, tensor_scale, group_offsets,
+                              num_groups, k, chan_out, resid_out, workspace,
+                              static_cast<hipStream_t>(stream));
+  return check_launch();
+}
+
 int fp4q_permute_quantized(fp4q_format_t fmt, const uint16_t* x, int64_t tokens, int64_t cols,
                            int64_t ldx, const uint8_t* q, const uint8_t* scales,
                            const float* tensor_scale, const int32_t* row_src, int64_t rows,

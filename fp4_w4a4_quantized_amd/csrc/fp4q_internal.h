@@ -106,6 +106,14 @@ size_t select_workspace_bytes(int64_t rows, int64_t cols);
 void launch_select(int fmt, bool tiled, const uint16_t* x, int64_t rows, int64_t cols,
                    int64_t ldx, const uint8_t* q, const uint8_t* scales, const float* tscale,
                    int k, int32_t* chan, uint16_t* resid, void* ws, hipStream_t stream);
+// Grouped selection (row-major operands; cols <= 30720): chan [G, k], each
+// group's residual rows on its own list.
+size_t select_grouped_workspace_bytes(int64_t rows, int64_t cols, int G);
+bool select_grouped_cols_ok(int64_t cols);
+void launch_select_grouped(int fmt, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                           const uint8_t* q, const uint8_t* scales, const float* tscale,
+                           const int32_t* off, int G, int k, int32_t* chan, uint16_t* resid,
+                           void* ws, hipStream_t stream);
 
 // Quantize-before-permute: token codes to expert order, per-group residual.
 void launch_permute(int fmt, const uint16_t* x, int64_t ldx, int64_t tokens, int64_t cols,

@@ -28,6 +28,14 @@
 //  4. k_chan_resid: R on the chosen channels, one thread per (8 rows, j),
 //     with the quantizer's own FP32 operations; the eight rows' gathers are
 //     in flight together.
+//
+// Grouped (the MoE form: each expert's rows choose their own channels, with
+// the expert's tensor scale): the score tiles are (group, row block) in
+// group order, each workgroup finding its tile by a block-wide scan over the
+// groups' block counts; the pick runs one workgroup per group, reducing the
+// group's partial maxima while it loads them into LDS (an empty group scores
+// zero everywhere and takes the first k channels, the tie rule); each
+// residual row takes its group's list and tensor scale.
 #include "fp4q_device.h"
 #include "fp4q_internal.h"
 
@@ -84,19 +92,68 @@ __device__ __forceinline__ float block_scale(uint32_t sc) {
   return (FMT == FP4Q_NVFP4) ? e4m3_value(sc) : exp2i((int)sc - 127);
 }
 
-template <int FMT>
+// Grouped score tiles: group g has ceil(rows_g / rb) row blocks, tiles in
+// group order.  Finds tile `tile`'s group and row range (thread t counts
+// groups 8t .. 8t + 7, G <= 2048); false past the last tile (uniform).
+__device__ bool grouped_tile(const int32_t* __restrict__ off, int G, int64_t rb, int tile,
+                             int* s_wsum, int* s_res, int& g, int64_t& r0, int64_t& r1) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int gg = t * 8 + i;
+    if (gg < G) cnt += (int)((off[gg + 1] - off[gg] + rb - 1) / rb);
+  }
+  int incl = cnt;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d);
+    if (lane >= d) incl += v;
+  }
+  if (lane == 63) s_wsum[wave] = incl;
+  if (t == 0) s_res[0] = -1;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += s_wsum[w];
+  const int excl = before + incl - cnt;
+  if (tile >= excl && tile < excl + cnt) {
+    int acc = excl;
+    for (int i = 0; i < 8; ++i) {
+      const int gg = t * 8 + i;
+      const int c = (gg < G) ? (int)((off[gg + 1] - off[gg] + rb - 1) / rb) : 0;
+      if (tile < acc + c) {
+        s_res[0] = gg;
+        s_res[1] = tile - acc;
+        break;
+      }
+      acc += c;
+    }
+  }
+  __syncthreads();
+  if (s_res[0] < 0) return false;
+  g = s_res[0];
+  r0 = off[g] + (int64_t)s_res[1] * rb;
+  r1 = min((int64_t)off[g + 1], r0 + rb);
+  return true;
+}
+
+template <int FMT, bool GROUPED>
 __global__ __launch_bounds__(SC_THREADS) void k_chan_score(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, bool tiled,
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ scales,
-    const float* __restrict__ tscale, int64_t rb, uint16_t* __restrict__ part) {
+    const float* __restrict__ tscale, int64_t rb, const int32_t* __restrict__ off, int G,
+    uint16_t* __restrict__ part) {
   constexpr int CPB = (FMT == FP4Q_NVFP4) ? 2 : 4;  // chunks per scale block
   __shared__ uint32_t red[4 * SC_CHUNKS * 8];
+  __shared__ int s_wsum[4];
+  __shared__ int s_res[2];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t cc = (int64_t)blockIdx.x * SC_CHUNKS + lane;
-  const int64_t r0 = (int64_t)blockIdx.y * rb;
-  const int64_t r1 = min(rows, r0 + rb);
-  const float t = (FMT == FP4Q_NVFP4) ? tscale[0] : 1.0f;
+  int64_t r0 = (int64_t)blockIdx.y * rb;
+  int64_t r1 = min(rows, r0 + rb);
+  int grp = 0;
+  if (GROUPED && !grouped_tile(off, G, rb, (int)blockIdx.y, s_wsum, s_res, grp, r0, r1)) return;
+  const float t = (FMT == FP4Q_NVFP4) ? tscale[grp] : 1.0f;
 
   float m[8];
 #pragma unroll
@@ -263,16 +320,37 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool vali
 
 // LDS: scores kept in LDS (cols <= PK_LDS_COLS), each the maximum
 // of `parts` partial rows of `part`; otherwise parts == 1 and the scores
-// are read from `part` itself.
-template <bool LDS>
+// are read from `part` itself.  GROUPED (LDS only): workgroup g picks for
+// group g, whose partial rows are its score tiles (ceil(rows_g / rb) of them,
+// after those of the groups before it); chan is [G, k].
+template <bool LDS, bool GROUPED>
 __global__ __launch_bounds__(PK_THREADS) void k_chan_pick(const uint16_t* __restrict__ part,
                                                           int parts, int cols, int k,
-                                                          int32_t* __restrict__ chan) {
+                                                          int32_t* __restrict__ chan,
+                                                          const int32_t* __restrict__ off,
+                                                          int64_t rb) {
   __shared__ uint16_t s_score[LDS ? PK_LDS_COLS : 2];
   __shared__ uint32_t hist[256];
   __shared__ uint32_t sel[4];
   __shared__ int wsum[16];
   const int t = threadIdx.x;
+  if (GROUPED) {
+    // this group's first tile: the sum of the block counts of the groups
+    // before it (a block-wide sum)
+    const int g = blockIdx.x;
+    int sum = 0;
+    for (int gg = t; gg < g; gg += PK_THREADS)
+      sum += (int)((off[gg + 1] - off[gg] + rb - 1) / rb);
+    for (int o = 32; o > 0; o >>= 1) sum += __shfl_down(sum, o);
+    if ((t & 63) == 0) wsum[t >> 6] = sum;
+    __syncthreads();
+    int first = 0;
+    for (int w = 0; w < PK_THREADS / 64; ++w) first += wsum[w];
+    __syncthreads();  // wsum is reused by the scans below
+    parts = (int)((off[g + 1] - off[g] + rb - 1) / rb);
+    part += (int64_t)first * cols;
+    chan += (int64_t)g * k;
+  }
 
   if (t < 256) hist[t] = 0;
   // the scores were written by other workgroups, so every load goes out to
@@ -353,24 +431,47 @@ __global__ __launch_bounds__(PK_THREADS) void k_chan_pick(const uint16_t* __rest
   }
 }
 
-template <int FMT>
+// GROUPED: row r takes the list and tensor scale of its group (chan [G, k]).
+template <int FMT, bool GROUPED>
 __global__ __launch_bounds__(RS_THREADS) void k_chan_resid(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, bool tiled,
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ scales,
     const float* __restrict__ tscale, const int32_t* __restrict__ chan, uint32_t k,
-    uint32_t total, uint16_t* __restrict__ resid) {
+    uint32_t total, uint16_t* __restrict__ resid, const int32_t* __restrict__ off, int G) {
   constexpr int BLK = (FMT == FP4Q_NVFP4) ? 16 : 32;
   const uint32_t i = blockIdx.x * RS_THREADS + threadIdx.x;
   if (i >= total) return;
-  const uint32_t g = i / k, j = i - g * k;
-  const int64_t c = min(max((int64_t)chan[j], (int64_t)0), cols - 1);  // in range by construction
-  const float t = (FMT == FP4Q_NVFP4) ? tscale[0] : 1.0f;
-  const int64_t r0 = (int64_t)g * RS_ROWS;
+  const uint32_t rg = i / k, j = i - rg * k;
+  const int64_t r0 = (int64_t)rg * RS_ROWS;
   const int nr = (int)min((int64_t)RS_ROWS, rows - r0);
+  // the group of each row (GROUPED): the last group starting at or before r0,
+  // then forward over the rows (empty groups skipped)
+  int gr[RS_ROWS];
+  if (GROUPED) {
+    int lo = 0, hi = G - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (off[mid] <= r0) lo = mid; else hi = mid - 1;
+    }
+    int g = lo;
+#pragma unroll
+    for (int u = 0; u < RS_ROWS; ++u) {
+      const int64_t r = r0 + (u < nr ? u : nr - 1);
+      while (g < G - 1 && off[g + 1] <= r) ++g;
+      gr[u] = g;
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < RS_ROWS; ++u) gr[u] = 0;
+  }
   uint32_t xv[RS_ROWS], cb[RS_ROWS], sc[RS_ROWS];
+  int64_t cu[RS_ROWS];
 #pragma unroll
   for (int u = 0; u < RS_ROWS; ++u) {
     const int64_t r = r0 + (u < nr ? u : nr - 1);  // past the end: repeat the last row
+    // in range by construction
+    const int64_t c = min(max((int64_t)chan[(int64_t)gr[u] * k + j], (int64_t)0), cols - 1);
+    cu[u] = c;
     xv[u] = x[r * ldx + c];
     cb[u] = q[code_off(tiled, r, c >> 1, cols)];
     sc[u] = scales[scale_off<FMT>(tiled, r, c / BLK, cols)];
@@ -378,6 +479,8 @@ __global__ __launch_bounds__(RS_THREADS) void k_chan_resid(
 #pragma unroll
   for (int u = 0; u < RS_ROWS; ++u) {
     if (u < nr) {
+      const int64_t c = cu[u];
+      const float t = (FMT == FP4Q_NVFP4) ? tscale[gr[u]] : 1.0f;
       const uint32_t code = (c & 1) ? (cb[u] >> 4) : (cb[u] & 15u);
       const float p = deq_code<FMT>(code, block_scale<FMT>(sc[u]), t);
       resid[(r0 + u) * k + j] = (uint16_t)f32_to_bf16_rne(bf16_to_f32(xv[u]) - p);
@@ -393,8 +496,8 @@ void launch_select_fmt(bool tiled, const uint16_t* x, int64_t rows, int64_t cols
   uint16_t* part = static_cast<uint16_t*>(ws);
   uint16_t* score = part;
   const dim3 sg((unsigned)((cols / 8 + SC_CHUNKS - 1) / SC_CHUNKS), (unsigned)pl.parts);
-  hipLaunchKernelGGL(k_chan_score<FMT>, sg, dim3(SC_THREADS), 0, stream, x, rows, cols, ldx,
-                     tiled, q, scales, tscale, pl.rb, part);
+  hipLaunchKernelGGL((k_chan_score<FMT, false>), sg, dim3(SC_THREADS), 0, stream, x, rows, cols,
+                     ldx, tiled, q, scales, tscale, pl.rb, nullptr, 1, part);
   int parts = (int)pl.parts;
   if (reduce_launch(pl.parts, cols)) {
     score = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) +
@@ -404,17 +507,39 @@ void launch_select_fmt(bool tiled, const uint16_t* x, int64_t rows, int64_t cols
     parts = 1;
   }
   if (cols <= PK_LDS_COLS)
-    hipLaunchKernelGGL(k_chan_pick<true>, dim3(1), dim3(PK_THREADS), 0, stream, score, parts,
-                       (int)cols, k, chan);
+    hipLaunchKernelGGL((k_chan_pick<true, false>), dim3(1), dim3(PK_THREADS), 0, stream, score,
+                       parts, (int)cols, k, chan, nullptr, (int64_t)1);
   else
-    hipLaunchKernelGGL(k_chan_pick<false>, dim3(1), dim3(PK_THREADS), 0, stream, score, 1,
-                       (int)cols, k, chan);
+    hipLaunchKernelGGL((k_chan_pick<false, false>), dim3(1), dim3(PK_THREADS), 0, stream, score,
+                       1, (int)cols, k, chan, nullptr, (int64_t)1);
   const int64_t groups = (rows + RS_ROWS - 1) / RS_ROWS;
   const uint32_t total = (uint32_t)(groups * k);
   if (total > 0)
-    hipLaunchKernelGGL(k_chan_resid<FMT>, dim3((total + RS_THREADS - 1) / RS_THREADS),
+    hipLaunchKernelGGL((k_chan_resid<FMT, false>), dim3((total + RS_THREADS - 1) / RS_THREADS),
                        dim3(RS_THREADS), 0, stream, x, rows, cols, ldx, tiled, q, scales, tscale,
-                       chan, (uint32_t)k, total, resid);
+                       chan, (uint32_t)k, total, resid, nullptr, 1);
+}
+
+// Grouped: score tiles (group, row block) bounded by ceil(rows / rb) + G.
+template <int FMT>
+void launch_select_grouped_fmt(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                               const uint8_t* q, const uint8_t* scales, const float* tscale,
+                               const int32_t* off, int G, int k, int32_t* chan, uint16_t* resid,
+                               void* ws, hipStream_t stream) {
+  const ScorePlan pl = score_plan(rows, cols);
+  const int64_t tiles = (rows + pl.rb - 1) / pl.rb + G;
+  uint16_t* part = static_cast<uint16_t*>(ws);
+  const dim3 sg((unsigned)((cols / 8 + SC_CHUNKS - 1) / SC_CHUNKS), (unsigned)tiles);
+  hipLaunchKernelGGL((k_chan_score<FMT, true>), sg, dim3(SC_THREADS), 0, stream, x, rows, cols,
+                     ldx, false, q, scales, tscale, pl.rb, off, G, part);
+  hipLaunchKernelGGL((k_chan_pick<true, true>), dim3((unsigned)G), dim3(PK_THREADS), 0, stream,
+                     part, 0, (int)cols, k, chan, off, pl.rb);
+  const int64_t groups = (rows + RS_ROWS - 1) / RS_ROWS;
+  const uint32_t total = (uint32_t)(groups * k);
+  if (total > 0)
+    hipLaunchKernelGGL((k_chan_resid<FMT, true>), dim3((total + RS_THREADS - 1) / RS_THREADS),
+                       dim3(RS_THREADS), 0, stream, x, rows, cols, ldx, false, q, scales, tscale,
+                       chan, (uint32_t)k, total, resid, off, G);
 }
 
 }  // namespace
@@ -425,6 +550,27 @@ size_t select_workspace_bytes(int64_t rows, int64_t cols) {
   size_t b = round256((size_t)pl.parts * (size_t)cols * 2);
   if (reduce_launch(pl.parts, cols)) b += round256((size_t)cols * 2);
   return b;
+}
+
+size_t select_grouped_workspace_bytes(int64_t rows, int64_t cols, int G) {
+  if (rows < 0 || cols <= 0 || G < 1) return 0;
+  const ScorePlan pl = score_plan(rows, cols);
+  const int64_t tiles = (rows + pl.rb - 1) / pl.rb + G;
+  return round256((size_t)tiles * (size_t)cols * 2);
+}
+
+bool select_grouped_cols_ok(int64_t cols) { return cols <= PK_LDS_COLS; }
+
+void launch_select_grouped(int fmt, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                           const uint8_t* q, const uint8_t* scales, const float* tscale,
+                           const int32_t* off, int G, int k, int32_t* chan, uint16_t* resid,
+                           void* ws, hipStream_t stream) {
+  if (fmt == FP4Q_NVFP4)
+    launch_select_grouped_fmt<FP4Q_NVFP4>(x, rows, cols, ldx, q, scales, tscale, off, G, k, chan,
+                                          resid, ws, stream);
+  else
+    launch_select_grouped_fmt<FP4Q_MXFP4>(x, rows, cols, ldx, q, scales, tscale, off, G, k, chan,
+                                          resid, ws, stream);
 }
 
 void launch_select(int fmt, bool tiled, const uint16_t* x, int64_t rows, int64_t cols,

@@ -468,6 +468,28 @@ int fp4q_select_channels(fp4q_format_t fmt, fp4q_layout_t layout, const uint16_t
                          int32_t* chan_out, uint16_t* resid_out, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/* Grouped form (the MoE layer: QUADS abstract, NVFP4 rollout for MoE;
+ * explainer section 2.2 B): each group g (rows group_offsets[g] ..
+ * group_offsets[g+1]) chooses its own k channels from its own rows, with
+ * its own tensor scale: chan_out [num_groups, k] (ascending per group) and
+ * resid_out [rows, k], row r on its group's list.  An empty group has all
+ * magnitudes zero and takes channels 0 .. k-1 (the tie rule).
+ *   x, q, scales   row-major (fp4q_quantize(ROWMAJOR) with these offsets)
+ *   tensor_scale   device f32 [num_groups] (NVFP4), NULL for MXFP4
+ *   workspace      fp4q_select_channels_grouped_workspace_bytes() bytes,
+ *                  16-byte aligned
+ * cols above 30,720 or more than 2048 groups is FP4Q_ERR_UNSUPPORTED;
+ * other errors as fp4q_select_channels. */
+size_t fp4q_select_channels_grouped_workspace_bytes(int64_t rows, int64_t cols,
+                                                    int32_t num_groups);
+
+int fp4q_select_channels_grouped(fp4q_format_t fmt, const uint16_t* x, int64_t rows, int64_t cols,
+                                 int64_t ldx, const int32_t* group_offsets, int32_t num_groups,
+                                 const uint8_t* q, const uint8_t* scales,
+                                 const float* tensor_scale, int32_t k, int32_t* chan_out,
+                                 uint16_t* resid_out, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
 /* ------------------------------------------------------------------------
  * Expert-grouped compensated GEMM (MoE layer; QUADS abstract: NVFP4 rollout
  * for Mixture-of-Experts).  Rows [off[g], off[g+1]) of the permuted

@@ -249,6 +249,26 @@ def select_channels(fmt: int, x: np.ndarray, qx: dict, k: int):
     return chan, R
 
 
+def select_channels_grouped(fmt: int, x: np.ndarray, qx: dict, offsets, k: int):
+    """The MoE form of select_channels (QUADS abstract: MoE rollout;
+    explainer section 2.2 B): each group g (rows offsets[g] .. offsets[g+1])
+    chooses its k channels from its own rows with its own tensor scale, by
+    the single-group definition.  qx = quantize(fmt, x, offsets).  Returns
+    (chan int32 [G, k], resid uint16 [rows, k])."""
+    x = _c(x, np.uint16)
+    off = np.asarray(offsets, np.int64)
+    G = off.size - 1
+    rows = x.shape[0]
+    chan = np.zeros((G, k), np.int32)
+    R = np.zeros((rows, k), np.uint16)
+    for g in range(G):
+        r0, r1 = int(off[g]), int(off[g + 1])
+        sub = {"q": qx["q"][r0:r1], "scales": qx["scales"][r0:r1],
+               "tscale": None if fmt == MXFP4 else qx["tscale"][g:g + 1]}
+        chan[g], R[r0:r1] = select_channels(fmt, x[r0:r1], sub, k)
+    return chan, R
+
+
 def permute_quantized(fmt: int, x_tok: np.ndarray, qx: dict, row_src, offsets, chan_idx=None):
     """Quantize-before-permute: qx = quantize(fmt, x_tok) (one group).  Row m
     of the expert-ordered result is token row_src[m]; group g holds rows

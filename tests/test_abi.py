@@ -427,6 +427,30 @@ def test_select_channels_rejects(L):
     assert sel(L, rows=0, x=None, qq=None, sc=None, R=None, k=0, chan=None) == 0
 
 
+def test_select_channels_grouped_rejects(L):
+    P, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    L.fp4q_select_channels_grouped.argtypes = [ctypes.c_int, P, i64, i64, i64, P, i32, P, P, P,
+                                               i32, P, P, P, sz, P]
+
+    def f(fmt=0, x=A, rows=32, cols=64, ldx=64, off=A, G=2, qq=A, sc=A, ts=B, k=8, chan=A, R=A,
+          ws=A, wsb=1 << 20):
+        return L.fp4q_select_channels_grouped(fmt, x, rows, cols, ldx, off, G, qq, sc, ts, k,
+                                              chan, R, ws, wsb, None)
+    assert f(fmt=2) == INVALID
+    assert f(cols=40, ldx=40) == INVALID           # not whole NVFP4 blocks
+    assert f(k=65) == INVALID
+    assert f(off=None) == INVALID
+    assert f(G=0) == INVALID
+    assert f(G=3000) == UNSUPPORTED
+    assert f(ts=None) == INVALID                   # NVFP4: one tensor scale per group
+    assert f(fmt=1) == INVALID                     # MXFP4 takes none
+    assert f(cols=32768, ldx=32768) == UNSUPPORTED  # more columns than the pick keeps in LDS
+    assert f(ws=None) == WORKSPACE
+    assert f(wsb=16) == WORKSPACE
+    assert f(k=0, chan=None, R=None, ws=None, wsb=0) == 0
+    assert L.fp4q_select_channels_grouped_workspace_bytes(32, 64, 2) >= 2 * 64 * 2
+
+
 def test_select_channels_workspace(L):
     f = L.fp4q_select_channels_workspace_bytes
     assert f(4, 64) == 256                     # one row block: its partial maxima

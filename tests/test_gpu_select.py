@@ -134,3 +134,64 @@ def test_select_chained_into_gemm(orc, fmt):
     y = fq.gemm(fmt, dict(ga, resid=gR), b, chan_idx=chan)
     torch.cuda.synchronize()
     assert_gemm_close(to_host(y), yo, ya)
+
+
+# ---- grouped (MoE) form: fp4q_select_channels_grouped ---------------------------
+
+def _check_grouped(orc, fmt, x, off, k):
+    qx = orc.quantize(fmt, x, offsets=off)
+    want_c, want_r = orc.select_channels_grouped(fmt, x, qx, off, k)
+    a = dev_quant(qx)
+    chan, R = fq.select_channels_grouped(fmt, to_dev(x), to_dev(off), a, k)
+    torch.cuda.synchronize()
+    got_c, got_r = to_host(chan), to_host(R)
+    assert np.array_equal(got_c, want_c), [(g, got_c[g][:8], want_c[g][:8])
+                                           for g in range(want_c.shape[0])
+                                           if not np.array_equal(got_c[g], want_c[g])][:3]
+    bad = np.argwhere(got_r.view(np.uint16) != want_r)
+    assert bad.size == 0, f"resid: {len(bad)} mismatches, first {bad[:3].tolist()}"
+    return got_c
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("off,K,k", [([0, 0, 1, 40, 40, 57], 256, 16),      # empty, one row
+                                     ([0, 300, 301, 900], 512, 33),         # several row blocks
+                                     ([0, 5, 2055, 2060, 2061], 1024, 64),  # one big group
+                                     ([0, 0, 0], 256, 8)])                  # no rows at all
+def test_grouped_select_matches_oracle(orc, fmt, off, K, k):
+    need_gpu()
+    off = np.array(off, np.int32)
+    say(f"grouped select fmt {fmt} rows {off[-1]} groups {off.size - 1} K{K} k{k}")
+    d = dense_case(max(int(off[-1]), 1), K, 8, n_out=max(1, K // 64), seed=int(off[-1]) + K + k)
+    _check_grouped(orc, fmt, d["x"][:int(off[-1])], off, k)
+
+
+def test_grouped_select_moe_workload_and_gemm(orc):
+    """The MoE gate_up input at full size (32,768 routed rows, 128 experts,
+    k = 32 per expert): chosen channels and residual bit for bit, then the
+    grouped GEMM on each expert's chosen channels against the oracle on
+    sampled outputs."""
+    need_gpu()
+    say("grouped select, MoE gate_up workload, then the grouped GEMM")
+    from gpu_helpers import workload
+    m = workload("moe_nvfp4")
+    off, x, wts = m["offsets"], m["x_perm"], m["wt_gate_up"]
+    fmt, k = 0, CONFIGS["moe_nvfp4"]["n_s"]
+    chan = _check_grouped(orc, fmt, x, off, k)
+    doff = to_dev(off)
+    ga = fq.quantize(fmt, to_dev(x), group_offsets=doff)
+    dchan, R = fq.select_channels_grouped(fmt, to_dev(x), doff, ga, k)
+    qbs = [fq.quantize(fmt, to_dev(wts[e])) for e in range(off.size - 1)]
+    bq = torch.stack([q["q"] for q in qbs])
+    bs = torch.stack([q["scales"] for q in qbs])
+    bts = torch.cat([q["tscale"] for q in qbs])
+    a = {"q": ga["q"], "scales": ga["scales"], "tscale": ga["tscale"], "resid": R}
+    y = to_host(fq.grouped_gemm(fmt, doff, a, bq, bs, bts, chan_idx=dchan))
+    qx = orc.quantize(fmt, x, offsets=off, chan_idx=chan)
+    N = wts.shape[1]
+    rng = np.random.default_rng(23)
+    pm, pn = rng.integers(0, x.shape[0], 30000), rng.integers(0, N, 30000)
+    yo, ya = orc.grouped_gemm_points(fmt, off, qx["q"], qx["scales"], qx["tscale"],
+                                     to_host(bq), to_host(bs), to_host(bts), chan, qx["resid"],
+                                     pm, pn)
+    assert_gemm_close(y[pm, pn], yo, ya)
