@@ -596,6 +596,396 @@ __global__ void __launch_bounds__(NT) k_quantize(
   }
 }
 
+// ---- the dense tile quantizer ------------------------------------------------
+//
+// One group: the large NVFP4 tensors (after the partial-amax pass) and
+// MXFP4 at every size.  One lane owns a 32-element unit of one row (64
+// bytes of BF16 in, 16 bytes of codes out: two NVFP4 blocks or one MXFP4
+// block), so the per-block work (maximum, scale code, divisor) is done once
+// per block instead of once per lane holding part of it, and the main path
+// moves no data between lanes.  A wave owns a tile of R rows x WC units
+// (R WC = 64); with WC = 4 the tile is 16 rows x 128 columns and its 64 code
+// pieces are one 1 KB block of the tiled layout, written contiguously
+// (lane = piece).  The residual of the selected channels of a tile is
+// formed afterwards by lanes indexed by (row, channel), reading the block
+// scale codes the wave left in LDS, so its cost follows the number of
+// selected entries rather than the tile's width.
+//
+// NVFP4 arithmetic, equal to the IEEE single operations the definitions
+// name:
+//  * amax / 6 is amax * RN(1/6) with one FMA correction; that this equals
+//    the correctly rounded quotient was checked exhaustively over every
+//    non-negative finite BF16 amax;
+//  * (amax / 6) / t and x / d use RN(1/t) and RN(1/d) (a per-workgroup table
+//    over the 127 block-scale codes) with two FMA corrections, which is the
+//    correctly rounded quotient by Markstein's theorem while t >= 2^-87:
+//    then d >= 2^-96 or d = 0, and a dividend too small for the residual
+//    to be exact gives a quotient far below the first rounding threshold
+//    of its format (code 0 either way).  A smaller tensor scale takes the
+//    IEEE division (the same values, slower).  The remainder is formed
+//    negated, which keeps the sign of a zero quotient.
+// MXFP4 converts the BF16 pairs directly (v_cvt_scalef32_pk_fp4_bf16 with
+// the power-of-two block scale: x / 2^e is exact, so this is the
+// nearest-even E2M1 code of x / 2^e as in the FP32 form; checked on the GPU
+// against the FP32 form for every finite BF16 value in both places of a
+// pair and every E8M0 scale).
+constexpr int TT = 256;           // threads per workgroup
+constexpr int TW = TT / 64;       // waves per workgroup
+constexpr int TDU = 2;            // tiles per wave
+constexpr int TILE_PARTS = 256;   // partial maxima of the NVFP4 amax pass
+constexpr uint32_t CTAB_MAX = 2048;  // column tiles covered by the LDS channel table
+constexpr int SCHAN_MAX = 2048;      // channels staged in LDS (longer lists are read from memory)
+
+typedef __bf16 bf16x2t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8t __attribute__((ext_vector_type(8)));
+
+struct TileArgs {
+  const uint16_t* x;
+  int64_t ldx;
+  int64_t cols;
+  uint32_t rows, upr, nct, ntiles;  // units per row, column tiles, tiles
+  const int32_t* chan;
+  int nS;
+  uint8_t* q;
+  uint8_t* scales;
+  float* tscale;
+  uint16_t* resid;
+  const uint32_t* parts;
+  int nparts;
+};
+
+// E2M1 magnitude of a code's 3 low bits, without a branch: 0.5 m for
+// exponent 0, else 2^(e-1) (1 + m/2).
+__device__ __forceinline__ float e2m1_mag_bf(uint32_t c) {
+  const uint32_t e = (c >> 1) & 3u, m = c & 1u;
+  const float nrm = __uint_as_float((126u + e) << 23 | (m << 22));
+  return e ? nrm : (m ? 0.5f : 0.0f);
+}
+
+// x / d rounded to nearest (see above), the sign of a zero x kept.
+__device__ __forceinline__ float quot_rn(float x, float d, float y) {
+  float q = x * y;
+  float r = __builtin_fmaf(q, d, -x);
+  q = __builtin_fmaf(-r, y, q);
+  r = __builtin_fmaf(q, d, -x);
+  return __builtin_fmaf(-r, y, q);
+}
+
+// RN(a / 6) for a non-negative BF16 value a (exhaustively checked).
+__device__ __forceinline__ float div6_rn(float a) {
+  constexpr float c6 = 0x1.555556p-3f;  // RN(1/6)
+  const float q = a * c6;
+  return __builtin_fmaf(__builtin_fmaf(-q, 6.0f, a), c6, q);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t m) {
+  for (int s = 32; s > 0; s >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, s));
+  return m;
+}
+
+// First j with S[j] >= v (S ascending, nS entries).
+__device__ __forceinline__ int chan_lower_bound(const int32_t* __restrict__ S, int nS, int64_t v) {
+  int lo = 0, hi = nS;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if ((int64_t)S[mid] < v) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+// Maximum |x| of 16 unpacked values.
+__device__ __forceinline__ float absmax16(const float* v) {
+  float m = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fabsf(v[2]));
+#pragma unroll
+  for (int k = 3; k < 15; k += 2) m = fmaxf(fmaxf(m, fabsf(v[k])), fabsf(v[k + 1]));
+  return fmaxf(m, fabsf(v[15]));
+}
+
+// Largest BF16 magnitude pattern of 32 packed elements (packed u16 maxima).
+__device__ __forceinline__ uint32_t absmax32_bits(const u32x4 (&w)[4]) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  u16x2 m = __builtin_bit_cast(u16x2, w[0].x & 0x7FFF7FFFu);
+#pragma unroll
+  for (int i = 1; i < 16; ++i)
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[i >> 2][i & 3] & 0x7FFF7FFFu));
+  return max((uint32_t)m.x, (uint32_t)m.y);
+}
+
+// Codes and the two block scale codes (low byte first) of one NVFP4 unit,
+// one 16-element block after the other (unpacked, divided and packed in
+// turn, so few values are live at once).
+template <bool FAST>
+__device__ __forceinline__ void nv_unit(const u32x4 (&w)[4], float t, float yt,
+                                        const float2* dytab, u32x4& codes, uint32_t& scw) {
+  uint32_t cw[4];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    float xs[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t u = w[2 * b + (i >> 2)][i & 3];
+      xs[2 * i] = __uint_as_float(u << 16);
+      xs[2 * i + 1] = __uint_as_float(u & 0xFFFF0000u);
+    }
+    const float a = absmax16(xs);
+    uint32_t sc;
+    float d, y = 0.0f;
+    if (FAST) {
+      sc = e4m3_encode(quot_rn(div6_rn(a), t, yt));
+      const float2 dy = dytab[sc];
+      d = dy.x;
+      y = dy.y;
+    } else {
+      sc = e4m3_encode((a / 6.0f) / t);
+      d = e4m3_value(sc) * t;
+    }
+    scw = b == 0 ? sc : (scw | sc << 8);
+    auto qt = [&](float x) __attribute__((always_inline)) {
+      return FAST ? quot_rn(x, d, y) : (d > 0.0f ? x / d : x * 0.0f);
+    };
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float* xh = xs + 8 * h;
+      uint32_t pk = 0;
+      pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, qt(xh[0]), qt(xh[1]), 1.0f, 0);
+      pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, qt(xh[2]), qt(xh[3]), 1.0f, 1);
+      pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, qt(xh[4]), qt(xh[5]), 1.0f, 2);
+      pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, qt(xh[6]), qt(xh[7]), 1.0f, 3);
+      cw[2 * b + h] = pk;
+    }
+  }
+  codes = u32x4{cw[0], cw[1], cw[2], cw[3]};
+}
+
+// SL: the channel list (nS <= SCHAN_MAX) is staged in LDS.
+template <int FMT, bool TILED, int WC, int DU, bool SL>
+__global__ void __launch_bounds__(TT) k_quant_tile(TileArgs p) {
+  constexpr int R = 64 / WC;
+  constexpr int SPU = (FMT == FP4Q_NVFP4) ? 2 : 1;  // scale blocks per unit
+  static_assert(!TILED || WC == 4, "the tiled layout's code block is 16 rows x 128 columns");
+  __shared__ uint32_t ctab[CTAB_MAX];
+  __shared__ int32_t schan[SL ? SCHAN_MAX : 1];
+  __shared__ float2 dytab[128];
+  __shared__ uint8_t scx[TW][64 * SPU];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane % R, c = lane / R;
+  const uint32_t nct = p.nct;
+
+  // this wave's tiles and their loads, before anything else
+  u32x4 v[DU][4];
+  uint32_t tile[DU];
+#pragma unroll
+  for (int k = 0; k < DU; ++k) {
+    tile[k] = (blockIdx.x * DU + k) * TW + wave;
+    const uint32_t T = tile[k] < p.ntiles ? tile[k] : p.ntiles - 1;
+    const uint32_t rt = T / nct, ct = T - rt * nct;
+    uint32_t row = rt * R + r, uc = ct * WC + c;
+    row = row < p.rows ? row : p.rows - 1;
+    uc = uc < p.upr ? uc : p.upr - 1;
+    const u32x4* src = reinterpret_cast<const u32x4*>(p.x + (int64_t)row * p.ldx + (int64_t)uc * 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[k][i] = src[i];  // plain loads: the amax pass left x in the caches
+  }
+
+  // NVFP4 tensor scale from the partial maxima (every wave), and the
+  // divisor table {d, RN(1/d)} of the block-scale codes
+  float t = 1.0f, yt = 1.0f;
+  bool fast = true;
+  if (FMT == FP4Q_NVFP4) {
+    uint32_t m = 0;
+    for (int i = lane; i < p.nparts; i += 64) m = max(m, p.parts[i]);
+    t = nv_tensor_scale(bf16_to_f32(wave_max_u32(m)));
+    yt = 1.0f / t;
+    fast = t >= 0x1p-87f;
+    if (threadIdx.x < 128) {
+      const float d = e4m3_value(threadIdx.x) * t;
+      dytab[threadIdx.x] = float2{d, d > 0.0f ? 1.0f / d : 0.0f};
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) p.tscale[0] = t;
+  }
+  // channel table: ctab[ct] = first j with S[j] >= 32 WC ct, for ct <= nct;
+  // the first SCHAN_MAX channels staged in LDS
+  const int nS = p.nS;
+  const bool use_ctab = nS > 0 && nct + 1 <= CTAB_MAX;
+  if (nS > 0) {
+    constexpr uint32_t W = 32 * WC;
+    for (int j = threadIdx.x; j <= nS; j += TT) {
+      const int32_t sj = j < nS ? p.chan[j] : 0;
+      if (SL && j < nS) schan[j] = sj;
+      if (use_ctab) {
+        const uint32_t lo = j == 0 ? 0u : (uint32_t)p.chan[j - 1] / W + 1u;
+        const uint32_t hi = j == nS ? nct : (uint32_t)sj / W;
+        for (uint32_t ct = lo; ct <= hi; ++ct) ctab[ct] = (uint32_t)j;
+      }
+    }
+  }
+  __syncthreads();
+  auto chan_at = [&](int j) __attribute__((always_inline)) -> int64_t {
+    return SL ? (int64_t)schan[j] : (int64_t)p.chan[j];
+  };
+
+  // residual entries of the first pass of each tile (lane i: row i % R,
+  // channel jlo + i / R): their x loads go out before the quantization
+  int jlo[DU], nres[DU];
+  uint32_t rcol[DU];
+  uint32_t rx[DU];
+#pragma unroll
+  for (int k = 0; k < DU; ++k) {
+    jlo[k] = 0;
+    nres[k] = 0;
+    rcol[k] = 0;
+    rx[k] = 0;
+    if (nS > 0 && tile[k] < p.ntiles) {
+      const uint32_t rt = tile[k] / nct, ct = tile[k] - rt * nct;
+      const int64_t c0 = (int64_t)ct * (32 * WC);
+      int jhi;
+      if (use_ctab) {
+        jlo[k] = (int)ctab[ct];
+        jhi = (int)ctab[ct + 1];
+      } else {
+        jlo[k] = chan_lower_bound(p.chan, nS, c0);
+        jhi = chan_lower_bound(p.chan, nS, c0 + 32 * WC);
+      }
+      // the same in every lane: keep the range (and the loop over it) scalar
+      jlo[k] = __builtin_amdgcn_readfirstlane(jlo[k]);
+      nres[k] = __builtin_amdgcn_readfirstlane((jhi - jlo[k]) * R);
+      const uint32_t rw = rt * R + (uint32_t)lane % R;
+      if (lane < nres[k] && rw < p.rows) {
+        rcol[k] = (uint32_t)chan_at(jlo[k] + lane / R);
+        rx[k] = p.x[(int64_t)rw * p.ldx + rcol[k]];
+      }
+    }
+  }
+
+#pragma unroll
+  for (int k = 0; k < DU; ++k) {
+    if (tile[k] >= p.ntiles) break;
+    const uint32_t rt = tile[k] / nct, ct = tile[k] - rt * nct;
+    const uint32_t row = rt * R + r, uc = ct * WC + c;
+    const bool active = row < p.rows && uc < p.upr;
+    u32x4 codes;
+    uint32_t scw;  // this unit's block scale codes (NVFP4: two bytes)
+    if (FMT == FP4Q_NVFP4) {
+      if (fast) nv_unit<true>(v[k], t, yt, dytab, codes, scw);
+      else nv_unit<false>(v[k], t, yt, dytab, codes, scw);
+    } else {
+      const int e = mx_exponent(bf16_to_f32(absmax32_bits(v[k])));
+      scw = (uint32_t)(e + 127);
+      const float s = __uint_as_float(scw << 23);
+      // the pairs taken from a bf16x8 view of each 16-byte piece (a bit cast
+      // of one 32-bit element of the u32x4 to a BF16 pair is folded wrongly
+      // by this compiler: it reads element 0 for all four)
+      uint32_t cw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x8t w = __builtin_bit_cast(bf16x8t, v[k][i]);
+        uint32_t pk = 0;
+        pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(pk, bf16x2t{w[0], w[1]}, s, 0);
+        pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(pk, bf16x2t{w[2], w[3]}, s, 1);
+        pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(pk, bf16x2t{w[4], w[5]}, s, 2);
+        pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(pk, bf16x2t{w[6], w[7]}, s, 3);
+        cw[i] = pk;
+      }
+      codes = u32x4{cw[0], cw[1], cw[2], cw[3]};
+    }
+    if (active) {
+      const int64_t K = p.cols;
+      int64_t co, so;
+      if (TILED) {
+        co = ((((int64_t)(row >> 4) * (K >> 7) + (uc >> 2)) << 10) + (int64_t)(lane << 4));
+        const int64_t sb = ((int64_t)(row >> 6) * (K >> 7) + (uc >> 2)) * (SPU * 256);
+        so = (FMT == FP4Q_NVFP4) ? sb + (((((uc & 3) >> 1) << 6) + (row & 63)) << 2) + 2 * (uc & 1)
+                                 : sb + ((row & 63) << 2) + (uc & 3);
+      } else {
+        co = (int64_t)row * (K >> 1) + (int64_t)uc * 16;
+        so = (int64_t)row * (K / (16 * (3 - SPU))) + (int64_t)uc * SPU;
+      }
+      __builtin_nontemporal_store(codes, reinterpret_cast<u32x4*>(p.q + co));
+      if (FMT == FP4Q_NVFP4)
+        *reinterpret_cast<uint16_t*>(p.scales + so) = (uint16_t)scw;
+      else
+        p.scales[so] = (uint8_t)scw;
+    }
+
+    // residual of the selected channels in this tile's columns: lane i of
+    // a pass takes row i % R and channel jlo + i / R
+    if (nS > 0) {
+      if (SPU == 2)
+        *reinterpret_cast<uint16_t*>(&scx[wave][2 * lane]) = (uint16_t)scw;
+      else
+        scx[wave][lane] = (uint8_t)scw;
+      const int64_t c0 = (int64_t)ct * (32 * WC);
+      const int n = nres[k];
+      for (int i0 = 0; i0 < n; i0 += 64) {
+        const int i = i0 + lane;
+        const uint32_t rr = (uint32_t)i % R, jj = (uint32_t)i / R;
+        const uint32_t rw = rt * R + rr;
+        if (i < n && rw < p.rows) {
+          const int j = jlo[k] + (int)jj;
+          const int64_t col = i0 == 0 ? (int64_t)rcol[k] : chan_at(j);
+          const uint32_t cl = (uint32_t)(col - c0);
+          const uint32_t h = i0 == 0 ? rx[k] : (uint32_t)p.x[(int64_t)rw * p.ldx + col];
+          const float xv = bf16_to_f32(h);
+          const uint32_t sc = scx[wave][((cl >> 5) * R + rr) * SPU + (SPU == 2 ? ((cl >> 4) & 1) : 0)];
+          float deq;
+          if (FMT == FP4Q_NVFP4) {
+            const float sb = e4m3_value(sc);
+            float qv;
+            if (fast) {
+              const float2 dy = dytab[sc];
+              qv = quot_rn(xv, dy.x, dy.y);
+            } else {
+              const float d = sb * t;
+              qv = d > 0.0f ? xv / d : xv * 0.0f;
+            }
+            const uint32_t code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, qv, 0.0f, 1.0f, 0) & 15u;
+            deq = (e2m1_mag_bf(code) * sb) * t;
+            if (code & 8u) deq = -deq;
+          } else {
+            const uint32_t code = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(
+                                      0u, __builtin_bit_cast(bf16x2t, h), __uint_as_float(sc << 23), 0) & 15u;
+            deq = e2m1_mag_bf(code) * exp2i((int)sc - 127);
+            if (code & 8u) deq = -deq;
+          }
+          p.resid[(int64_t)rw * nS + j] = (uint16_t)f32_to_bf16_rne(xv - deq);
+        }
+      }
+    }
+  }
+}
+
+template <int FMT, bool TILED, int WC>
+static void launch_tile_wc(const TileArgs& a, hipStream_t stream) {
+  const uint32_t per = TDU * TW;
+  const dim3 grid((a.ntiles + per - 1) / per);
+  if (a.nS <= SCHAN_MAX)
+    hipLaunchKernelGGL((k_quant_tile<FMT, TILED, WC, TDU, true>), grid, dim3(TT), 0, stream, a);
+  else
+    hipLaunchKernelGGL((k_quant_tile<FMT, TILED, WC, TDU, false>), grid, dim3(TT), 0, stream, a);
+}
+
+// The tile quantizer over x [rows, cols] (one group); parts: the NVFP4
+// partial maxima.
+template <int FMT>
+static void launch_tile(bool tiled, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                        const int32_t* chan, int nS, uint8_t* q, uint8_t* scales, float* tscale,
+                        uint16_t* resid, const uint32_t* parts, int nparts, hipStream_t stream) {
+  TileArgs a{};
+  a.x = x; a.ldx = ldx; a.cols = cols;
+  a.rows = (uint32_t)rows;
+  a.upr = (uint32_t)(cols / 32);
+  a.chan = chan; a.nS = nS; a.q = q; a.scales = scales; a.tscale = tscale; a.resid = resid;
+  a.parts = parts; a.nparts = nparts;
+  const int wc = tiled || a.upr >= 3 ? 4 : (int)a.upr;  // 1, 2 or 4 units across a tile
+  const uint32_t R = 64u / (uint32_t)wc;
+  a.nct = (a.upr + wc - 1) / wc;
+  a.ntiles = (uint32_t)((rows + R - 1) / R) * a.nct;
+  if (tiled) launch_tile_wc<FMT, true, 4>(a, stream);
+  else if (wc == 4) launch_tile_wc<FMT, false, 4>(a, stream);
+  else if (wc == 2) launch_tile_wc<FMT, false, 2>(a, stream);
+  else launch_tile_wc<FMT, false, 1>(a, stream);
+}
+
 template <int FMT, int MODE, int NT, int U>
 static void launch_q(const ChunkGrid& gr, int64_t rows, int64_t cols, bool tiled,
                      hipStream_t stream, const int32_t* off, int G, const int32_t* chan, int nS,
@@ -626,9 +1016,13 @@ int launch_quantize(int fmt, bool tiled, const uint16_t* x, int64_t rows, int64_
   const bool grouped = (off != nullptr && G > 1);
   const int Gk = grouped ? G : 1;
   if (fmt == FP4Q_MXFP4) {
-    if (chunks > 0)
-      launch_q<FP4Q_MXFP4, AMAX_NONE, QT, QU>(gr, rows, cols, tiled, stream, off, Gk, chan, nS, q, scales,
-                                               tscale, resid, words, 0);
+    if (chunks == 0) return 0;
+    if (!grouped || nS == 0)  // no tensor scale: groups matter only for their channel lists
+      launch_tile<FP4Q_MXFP4>(tiled, x, rows, cols, ldx, chan, nS, q, scales, tscale, resid,
+                              nullptr, 0, stream);
+    else
+      launch_q<FP4Q_MXFP4, AMAX_NONE, QT, QU>(gr, rows, cols, tiled, stream, off, Gk, chan, nS, q,
+                                               scales, tscale, resid, words, 0);
     return 0;
   }
   if (grouped) {
@@ -666,12 +1060,18 @@ int launch_quantize(int fmt, bool tiled, const uint16_t* x, int64_t rows, int64_
     }
     return 0;
   }
+  const bool tile = cols % 32 == 0;
+  const int64_t pmax = tile ? TILE_PARTS : AMAX_PARTS;
   int64_t parts = (chunks + (int64_t)QT * AMAX_BATCH - 1) / ((int64_t)QT * AMAX_BATCH);
-  parts = parts < AMAX_PARTS ? parts : AMAX_PARTS;
+  parts = parts < pmax ? parts : pmax;
   hipLaunchKernelGGL(k_amax_partial, dim3((unsigned)parts), dim3(QT), 0, stream, gr,
                      (uint32_t)chunks, words);
-  launch_q<FP4Q_NVFP4, AMAX_PARTIALS, QT, QU>(gr, rows, cols, tiled, stream, off, 1, chan, nS, q, scales,
-                                               tscale, resid, words, (int)parts);
+  if (tile)
+    launch_tile<FP4Q_NVFP4>(tiled, x, rows, cols, ldx, chan, nS, q, scales, tscale, resid, words,
+                            (int)parts, stream);
+  else
+    launch_q<FP4Q_NVFP4, AMAX_PARTIALS, QT, QU>(gr, rows, cols, tiled, stream, off, 1, chan, nS, q,
+                                                 scales, tscale, resid, words, (int)parts);
   return 0;
 }
 

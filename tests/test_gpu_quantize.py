@@ -139,6 +139,62 @@ def test_special_values(orc, fmt):
     _run(orc, fmt, x[2:4].copy(), chan)
 
 
+def _special_rows(cols, rng):
+    """Ten rows of the special values of test_special_values, `cols` wide."""
+    x = bf16_bits(rng.standard_normal((10, cols)).astype(np.float32))
+    x[0] = 0
+    x[1, :32] = 0x8000
+    x[2, :] = (np.arange(cols) % 255 + 1).astype(np.uint16)
+    x[3, :] = x[2, :] | 0x8000
+    x[4, :16] = 0x7F7F
+    x[4, 16:32] = 0xFF7F
+    x[5, :] = bf16_bits(np.full(cols, 1e-30, np.float32))
+    x[6, ::2] = bf16_bits(np.float32(2.5))
+    x[7, :] = bf16_bits(np.linspace(-7, 7, cols).astype(np.float32))
+    x[8, ::3] = 0x8000
+    x[9, 1::2] = 0x8000
+    return x
+
+
+@pytest.mark.parametrize("layout", [fq.ROWMAJOR, fq.TILED])
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_special_values_large(orc, fmt, layout):
+    """The special values inside tensors large enough for the two-pass NVFP4
+    path (the tile quantizer): special rows spread through 1,200 x 256
+    random rows, and a tensor of subnormal and tiny values alone, whose
+    NVFP4 tensor scale is far below 2^-87 (the IEEE-division form)."""
+    say(f"quantize special values, large tensors, fmt {fmt} layout {layout}")
+    rng = np.random.default_rng(15)
+    x = bf16_bits(rng.standard_normal((1200, 256)).astype(np.float32))
+    for i in range(0, 1200, 97):
+        x[i:i + 10] = _special_rows(256, rng)
+    chan = np.arange(3, 256, 9, dtype=np.int32)
+    _run(orc, fmt, x, chan, layout=layout)
+    tiny = np.tile(_special_rows(256, rng)[2:4], (600, 1))
+    tiny[::7, 5] = bf16_bits(np.float32(3e-39))
+    _run(orc, fmt, tiny, chan, layout=layout)
+    # tensor scales on both sides of 2^-87: amax 2688 * 2^-87 * (1 +- 1/8)
+    for f in (0.875, 1.125):
+        xs = rng.standard_normal((1100, 128)).astype(np.float32)
+        xs *= np.float32(2688 * 2.0 ** -87 * f) / np.abs(xs).max()
+        _run(orc, fmt, bf16_bits(xs), chan[chan < 128], layout=layout)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("rows,cols,nS", [(5000, 32, 4), (4000, 64, 9), (3000, 96, 5),
+                                          (1100, 160, 0), (70, 4224, 128), (33, 8192, 300),
+                                          (2, 69632, 64), (1, 266240, 64), (130, 4096, 2500)])
+def test_tile_widths(orc, fmt, rows, cols, nS):
+    """Row-major shapes for every tile width of the tile quantizer (1, 2 and
+    4 units across), partial column tiles, channel lists longer than a
+    tile's share, rows wider than its LDS channel table and channel lists
+    longer than it stages in LDS."""
+    say(f"quantize tile widths fmt {fmt} {rows}x{cols} nS {nS}")
+    d = dense_case(rows, cols, 8, n_out=max(1, cols // 100), seed=rows + 3 * cols)
+    chan = np.sort(np.random.default_rng(cols).choice(cols, nS, replace=False)).astype(np.int32)
+    _run(orc, fmt, d["x"], chan if nS else None)
+
+
 @pytest.mark.parametrize("fmt", [0, 1])
 @pytest.mark.parametrize("rows", [20, 600])
 def test_ldx_larger_than_cols(orc, fmt, rows):
