@@ -30,6 +30,7 @@
 //    order-free for non-negative values) after a fill kernel clears the
 //    words.
 // MXFP4 is a single pass.
+#include <algorithm>
 #include <atomic>
 
 #include "fp4q_device.h"
@@ -144,12 +145,11 @@ __device__ __forceinline__ uint32_t wg_max(uint32_t m, uint32_t* red) {
 // Clear the amax words and pre-set every tensor scale to 1 (empty groups
 // keep it).  A fill kernel rather than a memset so the sequence can be
 // captured in a HIP graph.
-__global__ void k_quant_init(uint32_t* __restrict__ amax_bits, float* __restrict__ tscale, int G) {
-  int g = blockIdx.x * blockDim.x + threadIdx.x;
-  if (g < G) {
-    amax_bits[g] = 0u;
-    tscale[g] = 1.0f;
-  }
+__global__ void k_quant_init(uint32_t* __restrict__ amax_bits, float* __restrict__ tscale, int G,
+                             int nwords) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < nwords) amax_bits[i] = 0u;
+  if (i < G) tscale[i] = 1.0f;
 }
 
 // Per-group amax.  Each workgroup owns a flat run of AMAX_WG_CHUNKS chunks
@@ -650,9 +650,20 @@ struct TileArgs {
   uint8_t* scales;
   float* tscale;
   uint16_t* resid;
-  const uint32_t* parts;
+  const uint32_t* parts;   // one group: NVFP4 partial maxima
   int nparts;
+  const int32_t* off;      // groups: row offsets [G + 1]
+  int G;
+  const uint32_t* gwords;  // groups: NVFP4 amax words (FP32 bits of max |x|), gslots per group
+  int gslots;
 };
+
+// NVFP4 tensor scale of group g: the maximum of its amax words.
+__device__ __forceinline__ float group_tscale(const TileArgs& p, int g) {
+  uint32_t m = 0;
+  for (int i = 0; i < p.gslots; ++i) m = max(m, p.gwords[(int64_t)g * p.gslots + i]);
+  return nv_tensor_scale(__uint_as_float(m));
+}
 
 // E2M1 magnitude of a code's 3 low bits, without a branch: 0.5 m for
 // exponent 0, else 2^(e-1) (1 + m/2).
@@ -693,12 +704,14 @@ __device__ __forceinline__ int chan_lower_bound(const int32_t* __restrict__ S, i
   return lo;
 }
 
-// Maximum |x| of 16 unpacked values.
-__device__ __forceinline__ float absmax16(const float* v) {
-  float m = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fabsf(v[2]));
+// Largest BF16 magnitude pattern of 16 packed elements (packed u16 maxima).
+__device__ __forceinline__ uint32_t absmax16_bits(u32x4 a, u32x4 b) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  u16x2 m = __builtin_bit_cast(u16x2, a.x & 0x7FFF7FFFu);
 #pragma unroll
-  for (int k = 3; k < 15; k += 2) m = fmaxf(fmaxf(m, fabsf(v[k])), fabsf(v[k + 1]));
-  return fmaxf(m, fabsf(v[15]));
+  for (int i = 1; i < 8; ++i)
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, (i < 4 ? a[i] : b[i - 4]) & 0x7FFF7FFFu));
+  return max((uint32_t)m.x, (uint32_t)m.y);
 }
 
 // Largest BF16 magnitude pattern of 32 packed elements (packed u16 maxima).
@@ -714,62 +727,135 @@ __device__ __forceinline__ uint32_t absmax32_bits(const u32x4 (&w)[4]) {
 // Codes and the two block scale codes (low byte first) of one NVFP4 unit,
 // one 16-element block after the other (unpacked, divided and packed in
 // turn, so few values are live at once).
-template <bool FAST>
-__device__ __forceinline__ void nv_unit(const u32x4 (&w)[4], float t, float yt,
-                                        const float2* dytab, u32x4& codes, uint32_t& scw) {
+// Codes and the two block scale codes (low byte first) of one NVFP4 unit:
+// both blocks' scale codes and divisors first, from the packed maxima, then
+// each block unpacked, divided and packed (few values live at once).
+// TABLE: {d, RN(1/d)} of the block-scale codes come from the workgroup's
+// table; else RN(1/d) is one IEEE division per block (per-group tensor
+// scales).  sx: 2^64 when the tensor scale is below 2^-87, else 1.
+// Dividends and divisors are multiplied by sx, which is exact for them
+// (then all far below 1) and leaves every quotient unchanged while it
+// brings the operands into the range where the reciprocal-and-FMA
+// division is correctly rounded; d itself is RN(sb t) unscaled, as defined.
+// ts = t sx and yts = RN(1/ts); the table holds {d sx, RN(1/(d sx))}.
+template <bool TABLE>
+__device__ __forceinline__ void nv_unit(const u32x4 (&w)[4], float t, float sx, float ts,
+                                        float yts, const float2* dytab, u32x4& codes,
+                                        uint32_t& scw) {
+  float dr[2], yr[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const float v6 = div6_rn(bf16_to_f32(absmax16_bits(w[2 * b], w[2 * b + 1])));
+    const uint32_t sc = e4m3_encode(quot_rn(v6 * sx, ts, yts));
+    scw = b == 0 ? sc : (scw | sc << 8);
+    if (TABLE) {
+      const float2 dy = dytab[sc];
+      dr[b] = dy.x;
+      yr[b] = dy.y;
+    } else {
+      dr[b] = e4m3_value(sc) * t * sx;
+      yr[b] = dr[b] > 0.0f ? 1.0f / dr[b] : 0.0f;
+    }
+  }
   uint32_t cw[4];
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
-    float xs[16];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t u = w[2 * b + (i >> 2)][i & 3];
-      xs[2 * i] = __uint_as_float(u << 16);
-      xs[2 * i + 1] = __uint_as_float(u & 0xFFFF0000u);
-    }
-    const float a = absmax16(xs);
-    uint32_t sc;
-    float d, y = 0.0f;
-    if (FAST) {
-      sc = e4m3_encode(quot_rn(div6_rn(a), t, yt));
-      const float2 dy = dytab[sc];
-      d = dy.x;
-      y = dy.y;
-    } else {
-      sc = e4m3_encode((a / 6.0f) / t);
-      d = e4m3_value(sc) * t;
-    }
-    scw = b == 0 ? sc : (scw | sc << 8);
-    auto qt = [&](float x) __attribute__((always_inline)) {
-      return FAST ? quot_rn(x, d, y) : (d > 0.0f ? x / d : x * 0.0f);
+    const float d = dr[b], y = yr[b];
+    auto qt = [&](uint32_t bits) __attribute__((always_inline)) {
+      return quot_rn(__uint_as_float(bits) * sx, d, y);
     };
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const float* xh = xs + 8 * h;
+      const u32x4 u = w[2 * b + h];
       uint32_t pk = 0;
-      pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, qt(xh[0]), qt(xh[1]), 1.0f, 0);
-      pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, qt(xh[2]), qt(xh[3]), 1.0f, 1);
-      pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, qt(xh[4]), qt(xh[5]), 1.0f, 2);
-      pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, qt(xh[6]), qt(xh[7]), 1.0f, 3);
+      pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, qt(u.x << 16), qt(u.x & 0xFFFF0000u), 1.0f, 0);
+      pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, qt(u.y << 16), qt(u.y & 0xFFFF0000u), 1.0f, 1);
+      pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, qt(u.z << 16), qt(u.z & 0xFFFF0000u), 1.0f, 2);
+      pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, qt(u.w << 16), qt(u.w & 0xFFFF0000u), 1.0f, 3);
       cw[2 * b + h] = pk;
     }
   }
   codes = u32x4{cw[0], cw[1], cw[2], cw[3]};
 }
 
-// SL: the channel list (nS <= SCHAN_MAX) is staged in LDS.
-template <int FMT, bool TILED, int WC, int DU, bool SL>
+// The operand scale of the division for tensor scale t (see nv_unit).
+__device__ __forceinline__ float div_prescale(float t) { return t >= 0x1p-87f ? 1.0f : 0x1p64f; }
+
+constexpr int RG_MAX = TDU * TW * 64;  // rows the tiles of one workgroup cover at most
+constexpr int SOFF_MAX = 2048;         // group offsets staged in LDS (G + 1 at most)
+
+// rgrp[i] = group of row rbase + i, for the rows of this workgroup's tiles:
+// the offsets are staged in LDS (soff, when G < SOFF_MAX) and searched
+// there, one row per thread.  Contains a barrier; returns rbase.
+template <int R, int DU>
+__device__ __forceinline__ uint32_t build_row_groups(const TileArgs& p, int32_t* rgrp,
+                                                     int32_t* soff) {
+  const uint32_t T0 = blockIdx.x * DU * TW;
+  const uint32_t T1 = (T0 + DU * TW < p.ntiles ? T0 + DU * TW : p.ntiles) - 1;
+  const uint32_t rbase = (T0 / p.nct) * R;
+  const uint32_t rlim0 = (T1 / p.nct + 1) * R, rlim = rlim0 < p.rows ? rlim0 : p.rows;
+  const int G = p.G;
+  if (G < SOFF_MAX) {
+    for (int i = threadIdx.x; i <= G; i += TT) soff[i] = p.off[i];
+    __syncthreads();
+    for (uint32_t i = threadIdx.x; rbase + i < rlim; i += TT) {
+      const int64_t row = rbase + i;
+      int lo = 0, hi = G - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if ((int64_t)soff[mid] <= row) lo = mid; else hi = mid - 1;
+      }
+      rgrp[i] = lo;
+    }
+  } else {
+    for (uint32_t i = threadIdx.x; rbase + i < rlim; i += TT)
+      rgrp[i] = group_of_row(p.off, G, rbase + i);
+  }
+  __syncthreads();
+  return rbase;
+}
+
+// Entries of an ascending channel list S below c0 and below c1: by ballot
+// over one load per lane when nS <= 64 (sl: this lane's entry, or INT_MAX),
+// else by binary search.  Wave-uniform results.
+__device__ __forceinline__ void chan_range(const int32_t* __restrict__ S, int nS, int64_t c0,
+                                           int64_t c1, int& jl, int& jh, int32_t& sl) {
+  const int lane = threadIdx.x & 63;
+  if (nS <= 64) {
+    sl = lane < nS ? S[lane] : 0x7FFFFFFF;
+    jl = __popcll(__ballot((int64_t)sl < c0));
+    jh = __popcll(__ballot((int64_t)sl < c1));
+  } else {
+    sl = 0x7FFFFFFF;
+    jl = chan_lower_bound(S, nS, c0);
+    jh = chan_lower_bound(S, nS, c1);
+  }
+  jl = __builtin_amdgcn_readfirstlane(jl);
+  jh = __builtin_amdgcn_readfirstlane(jh);
+}
+
+// Tiles of R rows x WC units.  GRP: the rows belong to groups (expert
+// ranges off[g] <= row < off[g+1]) with their own NVFP4 tensor scale (from
+// the group amax words) and channel list (chan + g nS); a tile that spans
+// groups takes each lane's group by search and forms the residual group by
+// group.  SL: the one channel list (nS <= SCHAN_MAX) is staged in LDS.
+template <int FMT, bool TILED, int WC, int DU, bool SL, bool GRP>
 __global__ void __launch_bounds__(TT) k_quant_tile(TileArgs p) {
   constexpr int R = 64 / WC;
   constexpr int SPU = (FMT == FP4Q_NVFP4) ? 2 : 1;  // scale blocks per unit
   static_assert(!TILED || WC == 4, "the tiled layout's code block is 16 rows x 128 columns");
-  __shared__ uint32_t ctab[CTAB_MAX];
+  static_assert(!(SL && GRP), "one staged channel list");
+  __shared__ uint32_t ctab[GRP ? 1 : CTAB_MAX];
   __shared__ int32_t schan[SL ? SCHAN_MAX : 1];
-  __shared__ float2 dytab[128];
+  __shared__ float2 dytab[GRP ? 1 : 128];
   __shared__ uint8_t scx[TW][64 * SPU];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ int32_t rgrp[GRP ? RG_MAX : 1];
+  __shared__ int32_t soff[GRP ? SOFF_MAX : 1];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane % R, c = lane / R;
   const uint32_t nct = p.nct;
+  const int nS = p.nS;
 
   // this wave's tiles and their loads, before anything else
   u32x4 v[DU][4];
@@ -787,73 +873,84 @@ __global__ void __launch_bounds__(TT) k_quant_tile(TileArgs p) {
     for (int i = 0; i < 4; ++i) v[k][i] = src[i];  // plain loads: the amax pass left x in the caches
   }
 
-  // NVFP4 tensor scale from the partial maxima (every wave), and the
-  // divisor table {d, RN(1/d)} of the block-scale codes
-  float t = 1.0f, yt = 1.0f;
-  bool fast = true;
-  if (FMT == FP4Q_NVFP4) {
-    uint32_t m = 0;
-    for (int i = lane; i < p.nparts; i += 64) m = max(m, p.parts[i]);
-    t = nv_tensor_scale(bf16_to_f32(wave_max_u32(m)));
-    yt = 1.0f / t;
-    fast = t >= 0x1p-87f;
-    if (threadIdx.x < 128) {
-      const float d = e4m3_value(threadIdx.x) * t;
-      dytab[threadIdx.x] = float2{d, d > 0.0f ? 1.0f / d : 0.0f};
+  // one group: NVFP4 tensor scale from the partial maxima (every wave), the
+  // divisor table {d, RN(1/d)} of the block-scale codes, the channel table
+  // ctab[ct] = first j with S[j] >= 32 WC ct (ct <= nct) and the staged list
+  float t = 1.0f, sx = 1.0f, ts = 1.0f, yts = 1.0f;
+  bool use_ctab = false;
+  if constexpr (!GRP) {
+    if (FMT == FP4Q_NVFP4) {
+      uint32_t m = 0;
+      for (int i = lane; i < p.nparts; i += 64) m = max(m, p.parts[i]);
+      t = nv_tensor_scale(bf16_to_f32(wave_max_u32(m)));
+      sx = div_prescale(t);
+      ts = t * sx;
+      yts = 1.0f / ts;
+      if (threadIdx.x < 128) {
+        const float d = e4m3_value(threadIdx.x) * t * sx;
+        dytab[threadIdx.x] = float2{d, d > 0.0f ? 1.0f / d : 0.0f};
+      }
+      if (blockIdx.x == 0 && threadIdx.x == 0) p.tscale[0] = t;
     }
-    if (blockIdx.x == 0 && threadIdx.x == 0) p.tscale[0] = t;
-  }
-  // channel table: ctab[ct] = first j with S[j] >= 32 WC ct, for ct <= nct;
-  // the first SCHAN_MAX channels staged in LDS
-  const int nS = p.nS;
-  const bool use_ctab = nS > 0 && nct + 1 <= CTAB_MAX;
-  if (nS > 0) {
-    constexpr uint32_t W = 32 * WC;
-    for (int j = threadIdx.x; j <= nS; j += TT) {
-      const int32_t sj = j < nS ? p.chan[j] : 0;
-      if (SL && j < nS) schan[j] = sj;
-      if (use_ctab) {
-        const uint32_t lo = j == 0 ? 0u : (uint32_t)p.chan[j - 1] / W + 1u;
-        const uint32_t hi = j == nS ? nct : (uint32_t)sj / W;
-        for (uint32_t ct = lo; ct <= hi; ++ct) ctab[ct] = (uint32_t)j;
+    use_ctab = nS > 0 && nct + 1 <= CTAB_MAX;
+    if (nS > 0) {
+      constexpr uint32_t W = 32 * WC;
+      for (int j = threadIdx.x; j <= nS; j += TT) {
+        const int32_t sj = j < nS ? p.chan[j] : 0;
+        if (SL && j < nS) schan[j] = sj;
+        if (use_ctab) {
+          const uint32_t lo = j == 0 ? 0u : (uint32_t)p.chan[j - 1] / W + 1u;
+          const uint32_t hi = j == nS ? nct : (uint32_t)sj / W;
+          for (uint32_t ct = lo; ct <= hi; ++ct) ctab[ct] = (uint32_t)j;
+        }
       }
     }
+    __syncthreads();
   }
-  __syncthreads();
-  auto chan_at = [&](int j) __attribute__((always_inline)) -> int64_t {
-    return SL ? (int64_t)schan[j] : (int64_t)p.chan[j];
+  uint32_t rbase = 0;
+  if constexpr (GRP) rbase = build_row_groups<R, DU>(p, rgrp, soff);
+  // entry j of the channel list of group g
+  auto chan_at = [&](int g, int j) __attribute__((always_inline)) -> int64_t {
+    if (SL) return (int64_t)schan[j];
+    return (int64_t)p.chan[(GRP ? (int64_t)g * nS : 0) + j];
   };
 
-  // residual entries of the first pass of each tile (lane i: row i % R,
-  // channel jlo + i / R): their x loads go out before the quantization
-  int jlo[DU], nres[DU];
-  uint32_t rcol[DU];
-  uint32_t rx[DU];
+  // each tile's groups, and the residual entries of its first group's first
+  // pass (lane i: row i % R, channel jlo + i / R), whose x loads go out
+  // before the quantization
+  int g0[DU], g1[DU], jlo[DU], nres[DU];
+  uint32_t rcol[DU], rx[DU];
 #pragma unroll
   for (int k = 0; k < DU; ++k) {
-    jlo[k] = 0;
-    nres[k] = 0;
-    rcol[k] = 0;
-    rx[k] = 0;
-    if (nS > 0 && tile[k] < p.ntiles) {
-      const uint32_t rt = tile[k] / nct, ct = tile[k] - rt * nct;
-      const int64_t c0 = (int64_t)ct * (32 * WC);
-      int jhi;
-      if (use_ctab) {
-        jlo[k] = (int)ctab[ct];
-        jhi = (int)ctab[ct + 1];
-      } else {
-        jlo[k] = chan_lower_bound(p.chan, nS, c0);
-        jhi = chan_lower_bound(p.chan, nS, c0 + 32 * WC);
-      }
-      // the same in every lane: keep the range (and the loop over it) scalar
-      jlo[k] = __builtin_amdgcn_readfirstlane(jlo[k]);
-      nres[k] = __builtin_amdgcn_readfirstlane((jhi - jlo[k]) * R);
-      const uint32_t rw = rt * R + (uint32_t)lane % R;
-      if (lane < nres[k] && rw < p.rows) {
-        rcol[k] = (uint32_t)chan_at(jlo[k] + lane / R);
-        rx[k] = p.x[(int64_t)rw * p.ldx + rcol[k]];
-      }
+    g0[k] = g1[k] = jlo[k] = nres[k] = 0;
+    rcol[k] = rx[k] = 0;
+    if (tile[k] >= p.ntiles) continue;
+    const uint32_t rt = tile[k] / nct, ct = tile[k] - rt * nct;
+    const uint32_t r0 = rt * R, rlast = (r0 + R < p.rows ? r0 + R : p.rows) - 1;
+    if (GRP) {
+      g0[k] = __builtin_amdgcn_readfirstlane(rgrp[r0 - rbase]);
+      g1[k] = __builtin_amdgcn_readfirstlane(rgrp[rlast - rbase]);
+    }
+    if (nS == 0) continue;
+    const int64_t c0 = (int64_t)ct * (32 * WC);
+    int jl, jh;
+    int32_t sl = 0x7FFFFFFF;
+    if (!GRP && use_ctab) {
+      jl = __builtin_amdgcn_readfirstlane((int)ctab[ct]);
+      jh = __builtin_amdgcn_readfirstlane((int)ctab[ct + 1]);
+    } else {
+      chan_range(p.chan + (GRP ? (int64_t)g0[k] * nS : 0), nS, c0, c0 + 32 * WC, jl, jh, sl);
+    }
+    jlo[k] = jl;
+    nres[k] = (jh - jl) * R;
+    const uint32_t rw = r0 + (uint32_t)lane % R;
+    const uint32_t rend = GRP ? (uint32_t)p.off[g0[k] + 1] : p.rows;
+    // the list entry from the lane that loaded it (short group lists)
+    const int src = jl + lane / R;
+    const int32_t sv = __shfl(sl, src < 64 ? src : 63);
+    if (lane < nres[k] && rw < p.rows && rw < rend) {
+      rcol[k] = GRP && nS <= 64 ? (uint32_t)sv : (uint32_t)chan_at(g0[k], jlo[k] + lane / R);
+      rx[k] = p.x[(int64_t)rw * p.ldx + rcol[k]];
     }
   }
 
@@ -861,13 +958,23 @@ __global__ void __launch_bounds__(TT) k_quant_tile(TileArgs p) {
   for (int k = 0; k < DU; ++k) {
     if (tile[k] >= p.ntiles) break;
     const uint32_t rt = tile[k] / nct, ct = tile[k] - rt * nct;
-    const uint32_t row = rt * R + r, uc = ct * WC + c;
+    const uint32_t r0 = rt * R;
+    const uint32_t row = r0 + r, uc = ct * WC + c;
     const bool active = row < p.rows && uc < p.upr;
+    // this lane's group and its NVFP4 tensor scale
+    float tk = t, sxk = sx, tsk = ts, ytsk = yts;
+    if (GRP && FMT == FP4Q_NVFP4) {
+      const int g = g0[k] == g1[k] ? g0[k] : rgrp[(row < p.rows ? row : p.rows - 1) - rbase];
+      tk = group_tscale(p, g);
+      sxk = div_prescale(tk);
+      tsk = tk * sxk;
+      ytsk = 1.0f / tsk;
+      if (active && uc == 0 && row == (uint32_t)p.off[g]) p.tscale[g] = tk;
+    }
     u32x4 codes;
-    uint32_t scw;  // this unit's block scale codes (NVFP4: two bytes)
+    uint32_t scw;  // this unit's block scale codes (NVFP4: two bytes, low first)
     if (FMT == FP4Q_NVFP4) {
-      if (fast) nv_unit<true>(v[k], t, yt, dytab, codes, scw);
-      else nv_unit<false>(v[k], t, yt, dytab, codes, scw);
+      nv_unit<!GRP>(v[k], tk, sxk, tsk, ytsk, dytab, codes, scw);
     } else {
       const int e = mx_exponent(bf16_to_f32(absmax32_bits(v[k])));
       scw = (uint32_t)(e + 127);
@@ -907,83 +1014,202 @@ __global__ void __launch_bounds__(TT) k_quant_tile(TileArgs p) {
         p.scales[so] = (uint8_t)scw;
     }
 
-    // residual of the selected channels in this tile's columns: lane i of
-    // a pass takes row i % R and channel jlo + i / R
+    // residual of the selected channels in this tile's columns, group by
+    // group: lane i of a pass takes row i % R and channel jlo + i / R
     if (nS > 0) {
       if (SPU == 2)
         *reinterpret_cast<uint16_t*>(&scx[wave][2 * lane]) = (uint16_t)scw;
       else
         scx[wave][lane] = (uint8_t)scw;
       const int64_t c0 = (int64_t)ct * (32 * WC);
-      const int n = nres[k];
-      for (int i0 = 0; i0 < n; i0 += 64) {
-        const int i = i0 + lane;
-        const uint32_t rr = (uint32_t)i % R, jj = (uint32_t)i / R;
-        const uint32_t rw = rt * R + rr;
-        if (i < n && rw < p.rows) {
-          const int j = jlo[k] + (int)jj;
-          const int64_t col = i0 == 0 ? (int64_t)rcol[k] : chan_at(j);
-          const uint32_t cl = (uint32_t)(col - c0);
-          const uint32_t h = i0 == 0 ? rx[k] : (uint32_t)p.x[(int64_t)rw * p.ldx + col];
-          const float xv = bf16_to_f32(h);
-          const uint32_t sc = scx[wave][((cl >> 5) * R + rr) * SPU + (SPU == 2 ? ((cl >> 4) & 1) : 0)];
-          float deq;
-          if (FMT == FP4Q_NVFP4) {
-            const float sb = e4m3_value(sc);
-            float qv;
-            if (fast) {
-              const float2 dy = dytab[sc];
-              qv = quot_rn(xv, dy.x, dy.y);
-            } else {
-              const float d = sb * t;
-              qv = d > 0.0f ? xv / d : xv * 0.0f;
-            }
-            const uint32_t code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, qv, 0.0f, 1.0f, 0) & 15u;
-            deq = (e2m1_mag_bf(code) * sb) * t;
-            if (code & 8u) deq = -deq;
-          } else {
-            const uint32_t code = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(
-                                      0u, __builtin_bit_cast(bf16x2t, h), __uint_as_float(sc << 23), 0) & 15u;
-            deq = e2m1_mag_bf(code) * exp2i((int)sc - 127);
-            if (code & 8u) deq = -deq;
+      for (int g = g0[k]; g <= g1[k]; ++g) {
+        const bool first = g == g0[k];
+        int jl = jlo[k], n = nres[k];
+        uint32_t rlo = r0, rhi = p.rows;
+        float tg = t;
+        if (GRP) {
+          rlo = max(r0, (uint32_t)p.off[g]);
+          rhi = min(rhi, (uint32_t)p.off[g + 1]);
+          if (!first) {
+            int jh;
+            int32_t sl;
+            chan_range(p.chan + (int64_t)g * nS, nS, c0, c0 + 32 * WC, jl, jh, sl);
+            n = (jh - jl) * R;
           }
-          p.resid[(int64_t)rw * nS + j] = (uint16_t)f32_to_bf16_rne(xv - deq);
+          if (FMT == FP4Q_NVFP4) tg = group_tscale(p, g);
+        }
+        const float sxg = div_prescale(tg);
+        for (int i0 = 0; i0 < n; i0 += 64) {
+          const int i = i0 + lane;
+          const uint32_t rr = (uint32_t)i % R, jj = (uint32_t)i / R;
+          const uint32_t rw = r0 + rr;
+          if (i < n && rw >= rlo && rw < rhi) {
+            const int j = jl + (int)jj;
+            const bool pre = first && i0 == 0;
+            const int64_t col = pre ? (int64_t)rcol[k] : chan_at(g, j);
+            const uint32_t cl = (uint32_t)(col - c0);
+            const uint32_t h = pre ? rx[k] : (uint32_t)p.x[(int64_t)rw * p.ldx + col];
+            const float xv = bf16_to_f32(h);
+            const uint32_t sc = scx[wave][((cl >> 5) * R + rr) * SPU + (SPU == 2 ? ((cl >> 4) & 1) : 0)];
+            float deq;
+            if (FMT == FP4Q_NVFP4) {
+              const float sb = e4m3_value(sc);
+              float d, y;
+              if (!GRP) {
+                const float2 dy = dytab[sc];
+                d = dy.x;
+                y = dy.y;
+              } else {
+                d = sb * tg * sxg;
+                y = d > 0.0f ? 1.0f / d : 0.0f;
+              }
+              const float qv = quot_rn(xv * sxg, d, y);
+              const uint32_t code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, qv, 0.0f, 1.0f, 0) & 15u;
+              deq = (e2m1_mag_bf(code) * sb) * tg;
+              if (code & 8u) deq = -deq;
+            } else {
+              const uint32_t code = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(
+                                        0u, __builtin_bit_cast(bf16x2t, h), __uint_as_float(sc << 23), 0) & 15u;
+              deq = e2m1_mag_bf(code) * exp2i((int)sc - 127);
+              if (code & 8u) deq = -deq;
+            }
+            p.resid[(int64_t)rw * nS + j] = (uint16_t)f32_to_bf16_rne(xv - deq);
+          }
         }
       }
     }
   }
 }
 
-template <int FMT, bool TILED, int WC>
+// Per-group amax over the tile quantizer's tiles: each lane's unit maximum
+// (packed BF16 magnitudes), then each row's (its WC lanes), then each
+// tile's.  A workgroup combines its single-group tiles in LDS and issues
+// one atomic maximum per run of equal groups; a tile that spans groups
+// issues one per group.  Atomics on one word are serialised, so each group
+// has p.gslots words (as many as the workspace's amax area allows, at most
+// 8) and a workgroup takes word blockIdx % gslots; the group's maximum is
+// the maximum of its words.  The words hold FP32 bit patterns of max |x|
+// (exact and order-free for non-negative values) and are cleared first.
+template <int WC, int DU>
+__global__ void __launch_bounds__(TT) k_group_amax_tile(TileArgs p, uint32_t* __restrict__ words) {
+  constexpr int R = 64 / WC;
+  __shared__ int32_t rgrp[RG_MAX];
+  __shared__ int32_t soff[SOFF_MAX];
+  __shared__ int32_t sg[TW * DU];   // a tile's group, or -1 (none or several)
+  __shared__ uint32_t sm[TW * DU];  // its maximum
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane % R, c = lane / R;
+  const uint32_t nct = p.nct;
+  u32x4 v[DU][4];
+  uint32_t tile[DU];
+#pragma unroll
+  for (int k = 0; k < DU; ++k) {
+    tile[k] = (blockIdx.x * DU + k) * TW + wave;
+    const uint32_t T = tile[k] < p.ntiles ? tile[k] : p.ntiles - 1;
+    const uint32_t rt = T / nct, ct = T - rt * nct;
+    uint32_t row = rt * R + r, uc = ct * WC + c;
+    row = row < p.rows ? row : p.rows - 1;
+    uc = uc < p.upr ? uc : p.upr - 1;
+    const u32x4* src = reinterpret_cast<const u32x4*>(p.x + (int64_t)row * p.ldx + (int64_t)uc * 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[k][i] = src[i];
+  }
+  const uint32_t rbase = build_row_groups<R, DU>(p, rgrp, soff);
+  const int S = p.gslots, slot_w = (int)(blockIdx.x % (uint32_t)S);
+#pragma unroll
+  for (int k = 0; k < DU; ++k) {
+    const int slot = k * TW + wave;  // tile order
+    if (tile[k] >= p.ntiles) {
+      if (lane == 0) sg[slot] = -1;
+      continue;
+    }
+    const uint32_t rt = tile[k] / nct, ct = tile[k] - rt * nct;
+    const uint32_t r0 = rt * R, rlast = (r0 + R < p.rows ? r0 + R : p.rows) - 1;
+    const uint32_t row = r0 + r, uc = ct * WC + c;
+    uint32_t m = (row < p.rows && uc < p.upr) ? absmax32_bits(v[k]) : 0u;
+    if (WC >= 2) m = max(m, (uint32_t)__shfl_xor((int)m, R * (WC / 2)));
+    if (WC == 4) m = max(m, (uint32_t)__shfl_xor((int)m, R));
+    const int g0 = __builtin_amdgcn_readfirstlane(rgrp[r0 - rbase]);
+    const int g1 = __builtin_amdgcn_readfirstlane(rgrp[rlast - rbase]);
+    if (g0 == g1) {
+      m = wave_max_u32(m);
+      if (lane == 0) {
+        sg[slot] = g0;
+        sm[slot] = m;
+      }
+    } else {
+      if (lane == 0) sg[slot] = -1;
+      const int gl = rgrp[(row < p.rows ? row : p.rows - 1) - rbase];
+      for (int g = g0; g <= g1; ++g) {
+        const uint32_t mg = wave_max_u32(gl == g ? m : 0u);
+        if (lane == 0 && mg) atomicMax(&words[g * S + slot_w], mg << 16);
+      }
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int gc = -1;
+    uint32_t mc = 0;
+    for (int i = 0; i < TW * DU; ++i) {
+      if (sg[i] == gc && gc >= 0) {
+        mc = max(mc, sm[i]);
+        continue;
+      }
+      if (gc >= 0 && mc) atomicMax(&words[gc * S + slot_w], mc << 16);
+      gc = sg[i];
+      mc = gc >= 0 ? sm[i] : 0u;
+    }
+    if (gc >= 0 && mc) atomicMax(&words[gc * S + slot_w], mc << 16);
+  }
+}
+
+template <int FMT, bool TILED, int WC, bool GRP>
 static void launch_tile_wc(const TileArgs& a, hipStream_t stream) {
   const uint32_t per = TDU * TW;
   const dim3 grid((a.ntiles + per - 1) / per);
-  if (a.nS <= SCHAN_MAX)
-    hipLaunchKernelGGL((k_quant_tile<FMT, TILED, WC, TDU, true>), grid, dim3(TT), 0, stream, a);
+  if (!GRP && a.nS <= SCHAN_MAX)
+    hipLaunchKernelGGL((k_quant_tile<FMT, TILED, WC, TDU, !GRP, GRP>), grid, dim3(TT), 0, stream, a);
   else
-    hipLaunchKernelGGL((k_quant_tile<FMT, TILED, WC, TDU, false>), grid, dim3(TT), 0, stream, a);
+    hipLaunchKernelGGL((k_quant_tile<FMT, TILED, WC, TDU, false, GRP>), grid, dim3(TT), 0, stream, a);
 }
 
-// The tile quantizer over x [rows, cols] (one group); parts: the NVFP4
-// partial maxima.
+template <int FMT, bool GRP>
+static void launch_tile_g(bool tiled, const TileArgs& a, int wc, hipStream_t stream) {
+  if (tiled) launch_tile_wc<FMT, true, 4, GRP>(a, stream);
+  else if (wc == 4) launch_tile_wc<FMT, false, 4, GRP>(a, stream);
+  else if (wc == 2) launch_tile_wc<FMT, false, 2, GRP>(a, stream);
+  else launch_tile_wc<FMT, false, 1, GRP>(a, stream);
+}
+
+// The tile quantizer over x [rows, cols]; one group (parts: the NVFP4
+// partial maxima) or G groups (off, and gwords: the NVFP4 group amax words).
 template <int FMT>
 static void launch_tile(bool tiled, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
-                        const int32_t* chan, int nS, uint8_t* q, uint8_t* scales, float* tscale,
-                        uint16_t* resid, const uint32_t* parts, int nparts, hipStream_t stream) {
+                        const int32_t* off, int G, const int32_t* chan, int nS, uint8_t* q,
+                        uint8_t* scales, float* tscale, uint16_t* resid, const uint32_t* parts,
+                        int nparts, const uint32_t* gwords, hipStream_t stream,
+                        uint32_t* amax_words = nullptr, int gslots = 1) {
   TileArgs a{};
+  a.gslots = gslots;
   a.x = x; a.ldx = ldx; a.cols = cols;
   a.rows = (uint32_t)rows;
   a.upr = (uint32_t)(cols / 32);
+  a.off = off; a.G = G; a.gwords = gwords;
   a.chan = chan; a.nS = nS; a.q = q; a.scales = scales; a.tscale = tscale; a.resid = resid;
   a.parts = parts; a.nparts = nparts;
   const int wc = tiled || a.upr >= 3 ? 4 : (int)a.upr;  // 1, 2 or 4 units across a tile
   const uint32_t R = 64u / (uint32_t)wc;
   a.nct = (a.upr + wc - 1) / wc;
   a.ntiles = (uint32_t)((rows + R - 1) / R) * a.nct;
-  if (tiled) launch_tile_wc<FMT, true, 4>(a, stream);
-  else if (wc == 4) launch_tile_wc<FMT, false, 4>(a, stream);
-  else if (wc == 2) launch_tile_wc<FMT, false, 2>(a, stream);
-  else launch_tile_wc<FMT, false, 1>(a, stream);
+  if (amax_words != nullptr) {  // the groups' amax pass over the same tiles first
+    const dim3 grid((a.ntiles + TDU * TW - 1) / (TDU * TW));
+    if (wc == 4) hipLaunchKernelGGL((k_group_amax_tile<4, TDU>), grid, dim3(TT), 0, stream, a, amax_words);
+    else if (wc == 2) hipLaunchKernelGGL((k_group_amax_tile<2, TDU>), grid, dim3(TT), 0, stream, a, amax_words);
+    else hipLaunchKernelGGL((k_group_amax_tile<1, TDU>), grid, dim3(TT), 0, stream, a, amax_words);
+  }
+  if (off != nullptr && G > 1) launch_tile_g<FMT, true>(tiled, a, wc, stream);
+  else launch_tile_g<FMT, false>(tiled, a, wc, stream);
 }
 
 template <int FMT, int MODE, int NT, int U>
@@ -1017,27 +1243,35 @@ int launch_quantize(int fmt, bool tiled, const uint16_t* x, int64_t rows, int64_
   const int Gk = grouped ? G : 1;
   if (fmt == FP4Q_MXFP4) {
     if (chunks == 0) return 0;
-    if (!grouped || nS == 0)  // no tensor scale: groups matter only for their channel lists
-      launch_tile<FP4Q_MXFP4>(tiled, x, rows, cols, ldx, chan, nS, q, scales, tscale, resid,
-                              nullptr, 0, stream);
-    else
-      launch_q<FP4Q_MXFP4, AMAX_NONE, QT, QU>(gr, rows, cols, tiled, stream, off, Gk, chan, nS, q,
-                                               scales, tscale, resid, words, 0);
+    // no tensor scale: groups matter only for their channel lists
+    launch_tile<FP4Q_MXFP4>(tiled, x, rows, cols, ldx, grouped && nS > 0 ? off : nullptr, Gk, chan,
+                            nS, q, scales, tscale, resid, nullptr, 0, nullptr, stream);
     return 0;
   }
   if (grouped) {
-    hipLaunchKernelGGL(k_quant_init, dim3((G + QT - 1) / QT), dim3(QT), 0, stream, words, tscale, G);
+    // the tile path spreads each group's amax over gslots words of the
+    // workspace's amax area (AMAX_PARTS words, or G when larger)
+    const bool tile = cols % 32 == 0;
+    const int gslots = tile ? std::max(1, std::min(8, AMAX_PARTS / G)) : 1;
+    const int nwords = G * gslots;
+    hipLaunchKernelGGL(k_quant_init, dim3((nwords + QT - 1) / QT), dim3(QT), 0, stream, words, tscale,
+                       G, nwords);
     if (rows > 0) {
-      const int64_t nwg = (chunks + AMAX_WG_CHUNKS - 1) / AMAX_WG_CHUNKS;
-      hipLaunchKernelGGL(k_group_amax, dim3((unsigned)nwg), dim3(QT), 0, stream, gr, rows, off, G,
-                         words);
-      launch_q<FP4Q_NVFP4, AMAX_GROUP_WORDS, QT, QU>(gr, rows, cols, tiled, stream, off, G, chan, nS, q,
-                                                      scales, tscale, resid, words, 0);
+      if (tile) {  // amax and quantize passes over the same tiles
+        launch_tile<FP4Q_NVFP4>(tiled, x, rows, cols, ldx, off, G, chan, nS, q, scales, tscale,
+                                resid, nullptr, 0, words, stream, words, gslots);
+      } else {
+        const int64_t nwg = (chunks + AMAX_WG_CHUNKS - 1) / AMAX_WG_CHUNKS;
+        hipLaunchKernelGGL(k_group_amax, dim3((unsigned)nwg), dim3(QT), 0, stream, gr, rows, off,
+                           G, words);
+        launch_q<FP4Q_NVFP4, AMAX_GROUP_WORDS, QT, QU>(gr, rows, cols, tiled, stream, off, G, chan,
+                                                        nS, q, scales, tscale, resid, words, 0);
+      }
     }
     return 0;
   }
   if (rows == 0) {  // empty tensor: tensor scale 1
-    hipLaunchKernelGGL(k_quant_init, dim3(1), dim3(QT), 0, stream, words, tscale, 1);
+    hipLaunchKernelGGL(k_quant_init, dim3(1), dim3(QT), 0, stream, words, tscale, 1, 1);
     return 0;
   }
   // the fused path's grid (tiled: rows padded to 16) is at most 32
@@ -1067,8 +1301,8 @@ int launch_quantize(int fmt, bool tiled, const uint16_t* x, int64_t rows, int64_
   hipLaunchKernelGGL(k_amax_partial, dim3((unsigned)parts), dim3(QT), 0, stream, gr,
                      (uint32_t)chunks, words);
   if (tile)
-    launch_tile<FP4Q_NVFP4>(tiled, x, rows, cols, ldx, chan, nS, q, scales, tscale, resid, words,
-                            (int)parts, stream);
+    launch_tile<FP4Q_NVFP4>(tiled, x, rows, cols, ldx, nullptr, 1, chan, nS, q, scales, tscale,
+                            resid, words, (int)parts, nullptr, stream);
   else
     launch_q<FP4Q_NVFP4, AMAX_PARTIALS, QT, QU>(gr, rows, cols, tiled, stream, off, 1, chan, nS, q,
                                                  scales, tscale, resid, words, (int)parts);

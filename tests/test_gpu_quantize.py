@@ -234,6 +234,24 @@ def test_grouped_wide_rows(orc, fmt):
     _run(orc, fmt, x, chan.astype(np.int32), off)
 
 
+@pytest.mark.parametrize("layout", [fq.ROWMAJOR, fq.TILED])
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_grouped_tiles_across_groups(orc, fmt, layout):
+    """Groups whose boundaries fall inside 16-row tiles (empty and one-row
+    groups among them), a group of tiny values (its NVFP4 tensor scale far
+    below 2^-87: the IEEE-division form for its waves), special values, and
+    7 channels per group; both layouts."""
+    say(f"quantize grouped tiles across groups fmt {fmt} layout {layout}")
+    rng = np.random.default_rng(23)
+    x = bf16_bits(rng.standard_normal((700, 384)).astype(np.float32))
+    x[300:513] = bf16_bits((rng.standard_normal((213, 384)) * 1e-30).astype(np.float32))
+    x[22:32] = _special_rows(384, rng)
+    off = np.array([0, 0, 5, 21, 22, 300, 300, 513, 700], np.int32)
+    G = off.size - 1
+    chan = np.sort(np.stack([rng.choice(384, 7, replace=False) for _ in range(G)]), 1)
+    _run(orc, fmt, x, chan.astype(np.int32), off, layout=layout)
+
+
 def test_grouped_moe_workload(orc):
     """MoE layer at full size: 32768 routed rows x 2048, 128 experts with
     per-expert tensor scales and 32 channels each (and the down input)."""
