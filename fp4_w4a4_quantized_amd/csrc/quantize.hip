@@ -633,8 +633,9 @@ constexpr int TT = 256;           // threads per workgroup
 constexpr int TW = TT / 64;       // waves per workgroup
 constexpr int TDU = 2;            // tiles per wave
 constexpr int TILE_PARTS = 256;   // partial maxima of the NVFP4 amax pass
-constexpr uint32_t CTAB_MAX = 2048;  // column tiles covered by the LDS channel table
-constexpr int SCHAN_MAX = 2048;      // channels staged in LDS (longer lists are read from memory)
+constexpr uint32_t CTAB_MAX = 1024;  // column tiles covered by the LDS channel table
+constexpr int SCHAN_MAX = 1024;      // channels staged in LDS (longer lists are read from memory)
+constexpr int RES_W = 128;           // residual entries per row a workgroup collects in LDS
 
 typedef __bf16 bf16x2t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8t __attribute__((ext_vector_type(8)));
@@ -815,6 +816,16 @@ __device__ __forceinline__ uint32_t build_row_groups(const TileArgs& p, int32_t*
   return rbase;
 }
 
+// Dword d (wave-uniform) of a lane's 64-byte unit.
+__device__ __forceinline__ uint32_t unit_dword(const u32x4 (&w)[4], uint32_t d) {
+  switch (d) {
+    case 0: return w[0].x;  case 1: return w[0].y;  case 2: return w[0].z;  case 3: return w[0].w;
+    case 4: return w[1].x;  case 5: return w[1].y;  case 6: return w[1].z;  case 7: return w[1].w;
+    case 8: return w[2].x;  case 9: return w[2].y;  case 10: return w[2].z; case 11: return w[2].w;
+    case 12: return w[3].x; case 13: return w[3].y; case 14: return w[3].z; default: return w[3].w;
+  }
+}
+
 // Entries of an ascending channel list S below c0 and below c1: by ballot
 // over one load per lane when nS <= 64 (sl: this lane's entry, or INT_MAX),
 // else by binary search.  Wave-uniform results.
@@ -851,6 +862,8 @@ __global__ void __launch_bounds__(TT) k_quant_tile(TileArgs p) {
   __shared__ uint8_t scx[TW][64 * SPU];
   __shared__ int32_t rgrp[GRP ? RG_MAX : 1];
   __shared__ int32_t soff[GRP ? SOFF_MAX : 1];
+  __shared__ uint16_t sres[16][RES_W];  // the workgroup's residual rows (see agg)
+  __shared__ uint16_t xres[TW][64 / R][R];  // a residual pass's x values, per wave
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane % R, c = lane / R;
@@ -915,15 +928,48 @@ __global__ void __launch_bounds__(TT) k_quant_tile(TileArgs p) {
     return (int64_t)p.chan[(GRP ? (int64_t)g * nS : 0) + j];
   };
 
-  // each tile's groups, and the residual entries of its first group's first
-  // pass (lane i: row i % R, channel jlo + i / R), whose x loads go out
-  // before the quantization
+  // agg: the workgroup's residual entries are collected in LDS and written
+  // row by row in contiguous runs at the end (scattered 2-byte stores fetch
+  // their lines), when its tiles share one 16-row band and one group and
+  // cover at most RES_W channels of it: rows wr0 .. wr0+15, entries
+  // wjl .. wjl+wn-1 of the group's list
+  bool agg = false;
+  uint32_t wr0 = 0;
+  int wjl = 0, wn = 0;
+  if (R == 16 && nS > 0) {
+    const uint32_t T0 = blockIdx.x * DU * TW;
+    const uint32_t T1 = (T0 + DU * TW < p.ntiles ? T0 + DU * TW : p.ntiles) - 1;
+    const uint32_t rt = T0 / nct;
+    if (T1 / nct == rt) {
+      wr0 = rt * R;
+      const uint32_t wrl = (wr0 + R < p.rows ? wr0 + R : p.rows) - 1;
+      const int g = GRP ? rgrp[wr0 - rbase] : 0;
+      if (!GRP || rgrp[wrl - rbase] == g) {
+        const int64_t C0 = (int64_t)(T0 - rt * nct) * (32 * WC);
+        const int64_t C1 = (int64_t)(T1 - rt * nct + 1) * (32 * WC);
+        int jl, jh;
+        if (!GRP && use_ctab) {
+          jl = (int)ctab[T0 - rt * nct];
+          jh = (int)ctab[T1 - rt * nct + 1];
+        } else {
+          const int32_t* S = p.chan + (GRP ? (int64_t)g * nS : 0);
+          jl = chan_lower_bound(S, nS, C0);
+          jh = chan_lower_bound(S, nS, C1);
+        }
+        jl = __builtin_amdgcn_readfirstlane(jl);
+        jh = __builtin_amdgcn_readfirstlane(jh);
+        agg = jh - jl <= RES_W;
+        wjl = jl;
+        wn = jh - jl;
+      }
+    }
+  }
+
+  // each tile's groups, and the channel range of its first group
   int g0[DU], g1[DU], jlo[DU], nres[DU];
-  uint32_t rcol[DU], rx[DU];
 #pragma unroll
   for (int k = 0; k < DU; ++k) {
     g0[k] = g1[k] = jlo[k] = nres[k] = 0;
-    rcol[k] = rx[k] = 0;
     if (tile[k] >= p.ntiles) continue;
     const uint32_t rt = tile[k] / nct, ct = tile[k] - rt * nct;
     const uint32_t r0 = rt * R, rlast = (r0 + R < p.rows ? r0 + R : p.rows) - 1;
@@ -943,15 +989,6 @@ __global__ void __launch_bounds__(TT) k_quant_tile(TileArgs p) {
     }
     jlo[k] = jl;
     nres[k] = (jh - jl) * R;
-    const uint32_t rw = r0 + (uint32_t)lane % R;
-    const uint32_t rend = GRP ? (uint32_t)p.off[g0[k] + 1] : p.rows;
-    // the list entry from the lane that loaded it (short group lists)
-    const int src = jl + lane / R;
-    const int32_t sv = __shfl(sl, src < 64 ? src : 63);
-    if (lane < nres[k] && rw < p.rows && rw < rend) {
-      rcol[k] = GRP && nS <= 64 ? (uint32_t)sv : (uint32_t)chan_at(g0[k], jlo[k] + lane / R);
-      rx[k] = p.x[(int64_t)rw * p.ldx + rcol[k]];
-    }
   }
 
 #pragma unroll
@@ -1024,7 +1061,7 @@ __global__ void __launch_bounds__(TT) k_quant_tile(TileArgs p) {
       const int64_t c0 = (int64_t)ct * (32 * WC);
       for (int g = g0[k]; g <= g1[k]; ++g) {
         const bool first = g == g0[k];
-        int jl = jlo[k], n = nres[k];
+        int jl = jlo[k], n = nres[k];  // (first group: found before the loop)
         uint32_t rlo = r0, rhi = p.rows;
         float tg = t;
         if (GRP) {
@@ -1040,15 +1077,26 @@ __global__ void __launch_bounds__(TT) k_quant_tile(TileArgs p) {
         }
         const float sxg = div_prescale(tg);
         for (int i0 = 0; i0 < n; i0 += 64) {
+          // the pass's x values come from the registers of the lanes that
+          // own them: channel q of the pass (column col, the same for the
+          // wave) sits in the lanes of unit (col - c0) / 32, at one dword
+          // index; they put it in the wave's LDS slot for the item lanes
+#pragma unroll
+          for (int q = 0; q < 64 / R; ++q) {
+            if (i0 + q * R >= n) break;
+            const uint32_t cq = (uint32_t)__builtin_amdgcn_readfirstlane(
+                                    (int)(chan_at(g, jl + i0 / R + q) - c0));
+            const uint32_t wd = unit_dword(v[k], (cq & 31u) >> 1);
+            if ((uint32_t)c == (cq >> 5)) xres[wave][q][r] = (uint16_t)((cq & 1u) ? (wd >> 16) : wd);
+          }
           const int i = i0 + lane;
           const uint32_t rr = (uint32_t)i % R, jj = (uint32_t)i / R;
           const uint32_t rw = r0 + rr;
           if (i < n && rw >= rlo && rw < rhi) {
             const int j = jl + (int)jj;
-            const bool pre = first && i0 == 0;
-            const int64_t col = pre ? (int64_t)rcol[k] : chan_at(g, j);
+            const int64_t col = chan_at(g, j);
             const uint32_t cl = (uint32_t)(col - c0);
-            const uint32_t h = pre ? rx[k] : (uint32_t)p.x[(int64_t)rw * p.ldx + col];
+            const uint32_t h = xres[wave][lane / R][rr];
             const float xv = bf16_to_f32(h);
             const uint32_t sc = scx[wave][((cl >> 5) * R + rr) * SPU + (SPU == 2 ? ((cl >> 4) & 1) : 0)];
             float deq;
@@ -1073,10 +1121,21 @@ __global__ void __launch_bounds__(TT) k_quant_tile(TileArgs p) {
               deq = e2m1_mag_bf(code) * exp2i((int)sc - 127);
               if (code & 8u) deq = -deq;
             }
-            p.resid[(int64_t)rw * nS + j] = (uint16_t)f32_to_bf16_rne(xv - deq);
+            const uint16_t rv = (uint16_t)f32_to_bf16_rne(xv - deq);
+            if (agg) sres[rw - wr0][j - wjl] = rv;
+            else p.resid[(int64_t)rw * nS + j] = rv;
           }
         }
       }
+    }
+  }
+  if (agg) {  // uniform over the workgroup
+    __syncthreads();
+    const int n = 16 * wn;
+    for (int i = threadIdx.x; i < n; i += TT) {
+      const int rr = i / wn, jj = i - rr * wn;
+      const uint32_t rw = wr0 + (uint32_t)rr;
+      if (rw < p.rows) p.resid[(int64_t)rw * nS + wjl + jj] = sres[rr][jj];
     }
   }
 }
