@@ -1435,6 +1435,150 @@ __global__ void __launch_bounds__(QT) k_qdq_fallback(ChunkGrid gr, int64_t rows,
   }
 }
 
+// Outlier Fallback on the tile quantizer's tiles (one group, row-major,
+// cols % 32 == 0): each lane forms its unit's codes and block scales exactly
+// as the quantizer does, then writes its 32 FP32 outputs: x itself where the
+// code magnitude is 0, else the dequantized value -- the E2M1 value (signed,
+// exact from the hardware conversion) times the block scale, then (NVFP4)
+// times the tensor scale, the residual's rounding.  Workgroups add their
+// count of non-zero fallback entries to one counter, cleared earlier.
+template <int FMT, int WC, int DU>
+__global__ void __launch_bounds__(TT) k_qdq_tile(TileArgs p, float* __restrict__ y, int64_t ldy,
+                                                 unsigned long long* __restrict__ count) {
+  typedef float v2f32t __attribute__((ext_vector_type(2)));
+  constexpr int R = 64 / WC;
+  constexpr int OW = WC * 32 + 4;  // an output row of the tile in LDS (padded)
+  __shared__ float2 dytab[128];
+  __shared__ uint32_t red[TW];
+  __shared__ float ob[TW][R][OW];  // a tile's outputs, for row-contiguous stores
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane % R, c = lane / R;
+  const uint32_t nct = p.nct;
+  u32x4 v[DU][4];
+  uint32_t tile[DU];
+#pragma unroll
+  for (int k = 0; k < DU; ++k) {
+    tile[k] = (blockIdx.x * DU + k) * TW + wave;
+    const uint32_t T = tile[k] < p.ntiles ? tile[k] : p.ntiles - 1;
+    const uint32_t rt = T / nct, ct = T - rt * nct;
+    uint32_t row = rt * R + r, uc = ct * WC + c;
+    row = row < p.rows ? row : p.rows - 1;
+    uc = uc < p.upr ? uc : p.upr - 1;
+    const u32x4* src = reinterpret_cast<const u32x4*>(p.x + (int64_t)row * p.ldx + (int64_t)uc * 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[k][i] = src[i];
+  }
+  float t = 1.0f, sx = 1.0f, ts = 1.0f, yts = 1.0f;
+  if (FMT == FP4Q_NVFP4) {
+    uint32_t m = 0;
+    for (int i = lane; i < p.nparts; i += 64) m = max(m, p.parts[i]);
+    t = nv_tensor_scale(bf16_to_f32(wave_max_u32(m)));
+    sx = div_prescale(t);
+    ts = t * sx;
+    yts = 1.0f / ts;
+    if (threadIdx.x < 128) {
+      const float d = e4m3_value(threadIdx.x) * t * sx;
+      dytab[threadIdx.x] = float2{d, d > 0.0f ? 1.0f / d : 0.0f};
+    }
+    __syncthreads();
+  }
+  uint32_t nfb = 0;
+#pragma unroll
+  for (int k = 0; k < DU; ++k) {
+    if (tile[k] >= p.ntiles) break;
+    const uint32_t rt = tile[k] / nct, ct = tile[k] - rt * nct;
+    const uint32_t row = rt * R + r, uc = ct * WC + c;
+    u32x4 codes;
+    uint32_t scw;
+    if (FMT == FP4Q_NVFP4) {
+      nv_unit<true>(v[k], t, sx, ts, yts, dytab, codes, scw);
+    } else {
+      scw = (uint32_t)(mx_exponent(bf16_to_f32(absmax32_bits(v[k]))) + 127);
+      const float s = __uint_as_float(scw << 23);
+      uint32_t cw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x8t w = __builtin_bit_cast(bf16x8t, v[k][i]);
+        uint32_t pk = 0;
+        pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(pk, bf16x2t{w[0], w[1]}, s, 0);
+        pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(pk, bf16x2t{w[2], w[3]}, s, 1);
+        pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(pk, bf16x2t{w[4], w[5]}, s, 2);
+        pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(pk, bf16x2t{w[6], w[7]}, s, 3);
+        cw[i] = pk;
+      }
+      codes = u32x4{cw[0], cw[1], cw[2], cw[3]};
+    }
+    const bool active = row < p.rows && uc < p.upr;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {  // elements 8i .. 8i+7
+      const float sb = FMT == FP4Q_NVFP4 ? e4m3_value((scw >> (8 * (i >> 1))) & 0xFFu)
+                                         : exp2i((int)scw - 127);
+      const v2f32t e[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes[i], 1.0f, 0),
+                           __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes[i], 1.0f, 1),
+                           __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes[i], 1.0f, 2),
+                           __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes[i], 1.0f, 3)};
+      float o[8];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const uint32_t xw = v[k][i][h];
+        const float x0 = __uint_as_float(xw << 16), x1 = __uint_as_float(xw & 0xFFFF0000u);
+        const float d0 = FMT == FP4Q_NVFP4 ? (e[h].x * sb) * t : e[h].x * sb;
+        const float d1 = FMT == FP4Q_NVFP4 ? (e[h].y * sb) * t : e[h].y * sb;
+        o[2 * h] = e[h].x == 0.0f ? x0 : d0;
+        o[2 * h + 1] = e[h].y == 0.0f ? x1 : d1;
+        nfb += (active && e[h].x == 0.0f && x0 != 0.0f) ? 1u : 0u;
+        nfb += (active && e[h].y == 0.0f && x1 != 0.0f) ? 1u : 0u;
+      }
+      f32x4q* d4 = reinterpret_cast<f32x4q*>(&ob[wave][r][c * 32 + 8 * i]);
+      d4[0] = f32x4q{o[0], o[1], o[2], o[3]};
+      d4[1] = f32x4q{o[4], o[5], o[6], o[7]};
+    }
+    // the tile's rows leave in contiguous runs: 16 bytes per lane, WC * 8
+    // lanes per row (one wave's LDS operations complete in order)
+    const int64_t col0 = (int64_t)ct * (WC * 32);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int idx = m * 64 + lane, rr = idx / (WC * 8), c16 = idx - rr * (WC * 8);
+      const uint32_t orow = rt * R + (uint32_t)rr;
+      if (orow < p.rows && ct * WC + (uint32_t)(c16 >> 3) < p.upr) {
+        const f32x4q val = *reinterpret_cast<const f32x4q*>(&ob[wave][rr][4 * c16]);
+        __builtin_nontemporal_store(val, reinterpret_cast<f32x4q*>(y + (int64_t)orow * ldy + col0 + 4 * c16));
+      }
+    }
+  }
+  if (count) {
+    for (int s2 = 32; s2 > 0; s2 >>= 1) nfb += (uint32_t)__shfl_xor((int)nfb, s2);
+    if (lane == 0) red[wave] = nfb;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t n = 0;
+#pragma unroll
+      for (int i = 0; i < TW; ++i) n += red[i];
+      if (n) atomicAdd(count, (unsigned long long)n);
+    }
+  }
+}
+
+template <int FMT>
+static void launch_qdq_tile(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, float* y,
+                            int64_t ldy, unsigned long long* cnt, const uint32_t* parts, int nparts,
+                            hipStream_t stream) {
+  TileArgs a{};
+  a.x = x; a.ldx = ldx; a.cols = cols;
+  a.rows = (uint32_t)rows;
+  a.upr = (uint32_t)(cols / 32);
+  a.parts = parts; a.nparts = nparts;
+  const int wc = a.upr >= 3 ? 4 : (int)a.upr;
+  const uint32_t R = 64u / (uint32_t)wc;
+  a.nct = (a.upr + wc - 1) / wc;
+  a.ntiles = (uint32_t)((rows + R - 1) / R) * a.nct;
+  const dim3 grid((a.ntiles + TDU * TW - 1) / (TDU * TW));
+  if (wc == 4) hipLaunchKernelGGL((k_qdq_tile<FMT, 4, TDU>), grid, dim3(TT), 0, stream, a, y, ldy, cnt);
+  else if (wc == 2) hipLaunchKernelGGL((k_qdq_tile<FMT, 2, TDU>), grid, dim3(TT), 0, stream, a, y, ldy, cnt);
+  else hipLaunchKernelGGL((k_qdq_tile<FMT, 1, TDU>), grid, dim3(TT), 0, stream, a, y, ldy, cnt);
+}
+
 int launch_qdq_fallback(int fmt, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                         float* y, int64_t ldy, int64_t* count, void* ws, hipStream_t stream) {
   unsigned long long* cnt = reinterpret_cast<unsigned long long*>(count);
@@ -1443,18 +1587,22 @@ int launch_qdq_fallback(int fmt, const uint16_t* x, int64_t rows, int64_t cols, 
   const int64_t chunks = rows * (cols >> 3);
   const ChunkGrid gr{x, (uint32_t)(cols >> 3), ldx, 1.0 / (double)(cols >> 3), ldx == cols};
   const dim3 grid((unsigned)((chunks + QT * QU - 1) / (QT * QU)));
+  const bool tile = cols % 32 == 0;  // the tile form; else one lane per 8-element chunk
   if (fmt == FP4Q_MXFP4) {
-    hipLaunchKernelGGL(k_qdq_fallback<FP4Q_MXFP4>, grid, dim3(QT), 0, stream, gr, rows, y, ldy,
-                       nullptr, 0, cnt);
+    launch_qdq_tile<FP4Q_MXFP4>(x, rows, cols, ldx, y, ldy, cnt, nullptr, 0, stream);
     return 0;
   }
   uint32_t* words = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + WS_HEADER);
+  const int64_t pmax = tile ? TILE_PARTS : AMAX_PARTS;
   int64_t parts = (chunks + (int64_t)QT * AMAX_BATCH - 1) / ((int64_t)QT * AMAX_BATCH);
-  parts = parts < AMAX_PARTS ? parts : AMAX_PARTS;
+  parts = parts < pmax ? parts : pmax;
   hipLaunchKernelGGL(k_amax_partial, dim3((unsigned)parts), dim3(QT), 0, stream, gr,
                      (uint32_t)chunks, words);
-  hipLaunchKernelGGL(k_qdq_fallback<FP4Q_NVFP4>, grid, dim3(QT), 0, stream, gr, rows, y, ldy,
-                     words, (int)parts, cnt);
+  if (tile)
+    launch_qdq_tile<FP4Q_NVFP4>(x, rows, cols, ldx, y, ldy, cnt, words, (int)parts, stream);
+  else
+    hipLaunchKernelGGL(k_qdq_fallback<FP4Q_NVFP4>, grid, dim3(QT), 0, stream, gr, rows, y, ldy,
+                       words, (int)parts, cnt);
   return 0;
 }
 
