@@ -187,22 +187,28 @@ __device__ __forceinline__ void fix_neg(uint64_t (&a)[5]) {
 // One block of NE elements (w: NE/2 packed BF16 pairs) into the thread's
 // sums.  Per block: the quantizer's decisions, then the term sums
 //   S0 = sum of 6x where g = 0,  S1 = sum of 6x where g != 0,
-//   S2 = sum of 6 Q*(x) where g != 0 (A/2 times an integer),
-//   S3 = sum of 6 Q_s(x) (3 s times an integer, s the block's scale),
+//   S2 = sum of 6 Q*(x) where g != 0 (A times a multiple of 1/2),
+//   S3 = sum of 6 Q_s(x) (6 s times a multiple of 1/2, s the block's scale),
 // each added to the fixed point once per block (sums of x in FP64 when the
-// block's exponent span keeps them exact, else element by element).  The
-// decisions run in FP32, where every operand is exact: 6|x| and tau * A have
-// at most 11 significant bits, and x scaled by a power of two (MXFP4) or
-// divided by the quantizer's own divisor (NVFP4, the correctly rounded
-// quotient it forms) is what the quantizer rounds.  The squares for the
-// statistics come from component values that are exact (FP32 for MXFP4;
-// FP64 where the NVFP4 tensor scale enters).
-constexpr uint64_t TWICE_E2M1 = 0x0C08060403020100ull;
-
+// block's exponent span keeps them exact, else element by element).
+// Decisions, as the quantizer takes them, by the hardware conversion to
+// E2M1 (nearest, ties to even, saturating, sign kept):
+//  * g: of x / 2^e (MXFP4, exact: the BF16 pair converted directly), or of
+//    the correctly rounded quotient x / (sb t) (NVFP4, the quantizer's own
+//    reciprocal-and-FMA division with its operand scaling);
+//  * g*: of RN(6x / A), the correctly rounded quotient: 6|x| has at most 10
+//    significant bits and A at most 8, so a quotient within half an ulp of
+//    a rounding threshold of the E2M1 grid equals it, and the rounded
+//    quotient decides exactly as the exact one, ties included.
+// The signed E2M1 values e = v_g and e* = v_g* (with x's sign) come back
+// from the conversion to FP32.  The component values follow as before and
+// are exact (FP32 for MXFP4; FP64 where the NVFP4 tensor scale enters).
 template <int FMT, int NE>
 __device__ __forceinline__ void block_terms(const uint32_t (&w)[NE / 2], float t,
                                             uint64_t (&S)[4][5], double (&sq)[4], double& cross,
-                                            int64_t& ndz, int64_t& nclip) {
+                                            uint32_t& ndz, uint32_t& nclip) {
+  typedef float v2f32t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2d __attribute__((ext_vector_type(2)));
   uint32_t am = 0, mn = 0xFFFFu;
 #pragma unroll
   for (int i = 0; i < NE / 2; ++i) {
@@ -212,7 +218,7 @@ __device__ __forceinline__ void block_terms(const uint32_t (&w)[NE / 2], float t
   }
   const float A = bf16_to_f32(am);
   // the block's scale s: MXFP4 2^e; NVFP4 sb * t (exact real product)
-  float e8 = 0.0f, sbf = 1.0f, d = 0.0f, y = 0.0f;
+  float e8 = 0.0f, sbf = 1.0f, dq = 0.0f, yq = 0.0f, sx = 1.0f;
   double s_d;
   if (FMT == FP4Q_MXFP4) {
     const int e = mx_exponent(A);
@@ -220,94 +226,91 @@ __device__ __forceinline__ void block_terms(const uint32_t (&w)[NE / 2], float t
     s_d = (double)exp2i(e);
   } else {
     sbf = e4m3_value(e4m3_encode((A / 6.0f) / t));
-    d = sbf * t;  // the quantizer's divisor
-    y = 1.0f / d;
+    // the quantizer's divisor sb t, its operand scaling and reciprocal
+    sx = t >= 0x1p-87f ? 1.0f : 0x1p64f;
+    dq = sbf * t * sx;
+    yq = dq > 0.0f ? 1.0f / dq : 0.0f;
     s_d = (double)sbf * (double)t;
   }
   const double s6 = 6.0 * s_d;  // the block's largest representable magnitude
-  // The FP32 work below (6|x|, tau * A, the component values) is taken times
-  // a power of two sc, exact and order-preserving, so that blocks near the
-  // top of the BF16 range do not overflow (6 * 2^127 does); 1/sc undoes it
-  // in FP64.
+  // |x| > s6 exactly when |x| >= s6up, the least FP32 value above s6
+  float s6up = (float)s6;
+  if ((double)s6up <= s6) s6up = __uint_as_float(__float_as_uint(s6up) + 1u);
+  // The FP32 work below (6|x|, the component values) is taken times a power
+  // of two sc, exact and order-preserving, so that blocks near the top of the
+  // BF16 range do not overflow (6 * 2^127 does); 1/sc undoes it in FP64.
   const float sc = (am >> 7) >= 127 + 120 ? 0x1p-16f : 1.0f;
   const double isc = (double)(1.0f / sc);
   const float As = A * sc;
-  // tau * A, the Q* decision thresholds on 6|x|
-  const float t0 = 0.25f * As, t1 = 0.75f * As, t2 = 1.25f * As, t3 = 1.75f * As,
-              t4 = 2.5f * As, t5 = 3.5f * As, t6 = 5.0f * As;
+  // the ideal-scale quotient 6x / A, its operands brought into the range of
+  // the reciprocal-and-FMA division by a power of two sq
+  const float sq6 = As < 0x1p-60f ? 0x1p64f : 1.0f;
+  const float qa = As * sq6, ya = qa > 0.0f ? 1.0f / qa : 0.0f;
+  const float six_sc = 6.0f * sc, six_scq = six_sc * sq6;
+  const float q6u = (float)(s_d * 6.0 * (double)sc);  // MXFP4: 6 s sc, a power of two times 6
+  const float six_sb = 6.0f * sbf;
   // FP64 sums of up to 32 values below 2^(ea+1) with least bit 2^lsb_min are
   // exact when (ea + 6) - lsb_min <= 53
   const int ea = (int)(am >> 7) - 127;
   const int lsb_min = (mn == 0xFFFFu) ? ea : (((mn >> 7) == 0) ? -133 : (int)(mn >> 7) - 134);
   const bool fast = (am >> 7) == 0 || (ea + 6) - lsb_min <= 53;
-  double x0 = 0.0, x1 = 0.0;
-  int i1 = 0, i2 = 0;  // sums of sign * 2 v_g, and of sign * 2 v_g* where g != 0
+  double xa = 0.0, x1 = 0.0;  // sums of x over the block, and where g != 0
+  float i1 = 0.0f, i2 = 0.0f;  // sums of e, and of e* where g != 0 (exact)
   // eight elements (one 16-byte piece) at a time keeps the unrolled body
   // within the register budget
 #pragma unroll 1
   for (int v = 0; v < NE / 8; ++v) {
-    uint32_t wv[4];
+  uint32_t wv[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      wv[j] = NE == 16 ? (v == 0 ? w[j] : w[4 + j])
-                       : (v == 0 ? w[j] : v == 1 ? w[4 + j] : v == 2 ? w[8 + j] : w[12 + j]);
-    // the quantizer's codes of the eight elements, by the same hardware
-    // conversion: x / 2^e (MXFP4), or its correctly rounded quotient by the
-    // divisor sb * t (NVFP4)
-    float xs[8];
+  for (int j = 0; j < 4; ++j)
+    wv[j] = NE == 16 ? (v == 0 ? w[j] : w[4 + j])
+                     : (v == 0 ? w[j] : v == 1 ? w[4 + j] : v == 2 ? w[8 + j] : w[12 + j]);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) xs[k] = bf16_to_f32((wv[k >> 1] >> ((k & 1) * 16)) & 0xFFFFu);
-    uint32_t codes;
+  for (int i = 0; i < 4; ++i) {
+    const float xp[2] = {__uint_as_float(wv[i] << 16), __uint_as_float(wv[i] & 0xFFFF0000u)};
+    uint32_t cg;
     if (FMT == FP4Q_MXFP4) {
-      codes = e2m1_pack8(xs, e8);
+      cg = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, __builtin_bit_cast(bf16x2d, wv[i]), e8, 0);
     } else {
-      float qs[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k)
-        qs[k] = d >= 0x1p-96f ? div_rn(xs[k], d, y) : (d > 0.0f ? xs[k] / d : xs[k] * 0.0f);
-      codes = e2m1_pack8(qs);
+      cg = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, quot_rn(xp[0] * sx, dq, yq),
+                                                    quot_rn(xp[1] * sx, dq, yq), 1.0f, 0);
     }
+    const uint32_t cs = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(
+        0u, quot_rn(xp[0] * six_scq, qa, ya), quot_rn(xp[1] * six_scq, qa, ya), 1.0f, 0);
+    const v2f32t ep = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cg, 1.0f, 0);
+    const v2f32t esp = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cs, 1.0f, 0);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const uint32_t h = (wv[k >> 1] >> ((k & 1) * 16)) & 0xFFFFu;
-      const float xv = xs[k], ax = bf16_to_f32(h & 0x7FFFu);
-      const bool neg = (h & 0x8000u) != 0;
-      const uint32_t g = (codes >> (4 * k)) & 7u;
-      const float a6 = 6.0f * (ax * sc);
-      const uint32_t gs = A > 0.0f ? (uint32_t)(a6 > t0) + (uint32_t)(a6 >= t1) + (uint32_t)(a6 > t2) +
-                                         (uint32_t)(a6 >= t3) + (uint32_t)(a6 > t4) +
-                                         (uint32_t)(a6 >= t5) + (uint32_t)(a6 > t6)
-                                   : 0u;
-      // twice the E2M1 magnitudes {0, 1, 2, 3, 4, 6, 8, 12}, one byte per code
-      const int tg = (int)((TWICE_E2M1 >> (8 * g)) & 0xFFu);
-      const int tgs = (int)((TWICE_E2M1 >> (8 * gs)) & 0xFFu);
-      i1 += neg ? -tg : tg;
-      if (g) i2 += neg ? -tgs : tgs;
+    for (int h = 0; h < 2; ++h) {
+      const float xv = xp[h], ax = fabsf(xv);
+      const float e = ep[h], es = esp[h];
+      const bool gz = e == 0.0f;  // code magnitude 0
+      i1 += e;
+      i2 += gz ? 0.0f : es;
       if (fast) {
-        if (g) x1 += (double)xv;
-        else x0 += (double)xv;
+        const double xd = (double)xv;
+        xa += xd;
+        x1 += gz ? 0.0 : xd;
       } else {
-        fix_add(S[0], g ? 0.0 : 6.0 * (double)xv);
-        fix_add(S[1], g ? 6.0 * (double)xv : 0.0);
+        fix_add(S[0], gz ? 6.0 * (double)xv : 0.0);
+        fix_add(S[1], gz ? 0.0 : 6.0 * (double)xv);
       }
-      ndz += (g == 0 && ax != 0.0f) ? 1 : 0;
-      nclip += (double)ax > s6 ? 1 : 0;
+      ndz += (gz && ax != 0.0f) ? 1u : 0u;
+      nclip += ax >= s6up ? 1u : 0u;
       // component values times 6 (times sc in FP32, exact)
-      const float x6 = 6.0f * (xv * sc);
-      const float q6s = (neg ? -0.5f : 0.5f) * (float)tgs * As;  // 6 Q*(x)
-      const float m6 = (neg ? -3.0f : 3.0f) * (float)tg;         // 6 Q_s(x) / s
+      const float x6 = xv * six_sc;
+      const float q6s = es * As;  // 6 Q*(x)
       double ct, csb;
       if (FMT == FP4Q_MXFP4) {
-        const float q6a = m6 * (float)(s_d * (double)sc);  // a power-of-two scale
+        const float q6a = e * q6u;  // 6 Q_s(x), a power-of-two scale
         ct = (double)(x6 - q6a) * isc;  // differences within the block's range: exact
-        csb = g ? (double)(q6s - q6a) * isc : 0.0;
+        csb = gz ? 0.0 : (double)(q6s - q6a) * isc;
       } else {
-        const double q6a = (double)(m6 * sbf) * (double)t;
+        const double q6a = (double)(e * six_sb) * (double)t;
         ct = 6.0 * (double)xv - q6a;
-        csb = g ? (double)q6s * isc - q6a : 0.0;
+        csb = gz ? 0.0 : (double)q6s * isc - q6a;
       }
-      const double cdz = g ? 0.0 : (double)x6 * isc;
-      const double cgn = g ? (double)(x6 - q6s) * isc : 0.0;
+      const double cdz = gz ? (double)x6 * isc : 0.0;
+      const double cgn = gz ? 0.0 : (double)(x6 - q6s) * isc;
       sq[0] = __builtin_fma(ct, ct, sq[0]);
       sq[1] = __builtin_fma(csb, csb, sq[1]);
       sq[2] = __builtin_fma(cdz, cdz, sq[2]);
@@ -315,12 +318,13 @@ __device__ __forceinline__ void block_terms(const uint32_t (&w)[NE / 2], float t
       cross = __builtin_fma(csb, cgn, cross);
     }
   }
+  }
   if (fast) {
-    fix_add(S[0], 6.0 * x0);
+    fix_add(S[0], 6.0 * (xa - x1));
     fix_add(S[1], 6.0 * x1);
   }
-  fix_add(S[2], (double)i2 * 0.5 * (double)A);
-  fix_add(S[3], (double)i1 * 3.0 * s_d);
+  fix_add(S[2], (double)i2 * (double)A);
+  fix_add(S[3], (double)i1 * 6.0 * s_d);
 }
 
 // One thread per block (32 elements MXFP4, 16 NVFP4).  NVFP4 first reduces
@@ -352,7 +356,7 @@ __global__ void __launch_bounds__(DEC_THREADS) k_decompose(const uint16_t* __res
 #pragma unroll
     for (int i = 0; i < 5; ++i) S[c][i] = 0;
   double sq[4] = {0.0, 0.0, 0.0, 0.0}, cross = 0.0;
-  int64_t ndz = 0, nclip = 0;
+  uint32_t ndz = 0, nclip = 0;
 
   const int64_t nb = cols / NE, total = rows * nb;
   for (int64_t id = (int64_t)blockIdx.x * DEC_THREADS + threadIdx.x; id < total;

@@ -95,6 +95,20 @@ __device__ __forceinline__ float div_rn(float x, float d, float y) {
   return __uint_as_float(__float_as_uint(q) | (__float_as_uint(x) & 0x80000000u));
 }
 
+// x / d rounded to nearest from y = RN(1/d): two FMA corrections of x y
+// (Markstein's theorem, as div_rn), on the signed value with the remainder
+// formed negated, which keeps the sign of a zero quotient (d = 0 with y = 0
+// gives the signed zero).  Correctly rounded while d >= 2^-96 and the
+// remainder does not underflow; callers scale operands by powers of two
+// into that range.
+__device__ __forceinline__ float quot_rn(float x, float d, float y) {
+  float q = x * y;
+  float r = __builtin_fmaf(q, d, -x);
+  q = __builtin_fmaf(-r, y, q);
+  r = __builtin_fmaf(q, d, -x);
+  return __builtin_fmaf(-r, y, q);
+}
+
 // E2M1 codes of 8 FP32 values, packed two per byte (even element in the low
 // nibble), by gfx950's v_cvt_scalef32_pk_fp4_f32 with scale 1: nearest-even
 // on the E2M1 grid, saturating at 6, sign kept (also for -0 and values that

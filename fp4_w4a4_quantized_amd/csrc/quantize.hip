@@ -674,14 +674,6 @@ __device__ __forceinline__ float e2m1_mag_bf(uint32_t c) {
   return e ? nrm : (m ? 0.5f : 0.0f);
 }
 
-// x / d rounded to nearest (see above), the sign of a zero x kept.
-__device__ __forceinline__ float quot_rn(float x, float d, float y) {
-  float q = x * y;
-  float r = __builtin_fmaf(q, d, -x);
-  q = __builtin_fmaf(-r, y, q);
-  r = __builtin_fmaf(q, d, -x);
-  return __builtin_fmaf(-r, y, q);
-}
 
 // RN(a / 6) for a non-negative BF16 value a (exhaustively checked).
 __device__ __forceinline__ float div6_rn(float a) {
