@@ -256,6 +256,10 @@ __device__ __forceinline__ void block_terms(const uint32_t (&w)[NE / 2], float t
   const bool fast = (am >> 7) == 0 || (ea + 6) - lsb_min <= 53;
   double xa = 0.0, x1 = 0.0;  // sums of x over the block, and where g != 0
   float i1 = 0.0f, i2 = 0.0f;  // sums of e, and of e* where g != 0 (exact)
+  // the block's statistics, of components taken times sc (1/sc^2 applied
+  // once at the end; a power of two); NVFP4's t times sc, exact
+  double bq[4] = {0.0, 0.0, 0.0, 0.0}, bx = 0.0;
+  const double tsc = (double)t * (double)sc;
   // eight elements (one 16-byte piece) at a time keeps the unrolled body
   // within the register budget
 #pragma unroll 1
@@ -287,38 +291,43 @@ __device__ __forceinline__ void block_terms(const uint32_t (&w)[NE / 2], float t
       i1 += e;
       i2 += gz ? 0.0f : es;
       if (fast) {
-        const double xd = (double)xv;
-        xa += xd;
-        x1 += gz ? 0.0 : xd;
+        xa += (double)xv;
+        x1 += (double)(gz ? 0.0f : xv);
       } else {
         fix_add(S[0], gz ? 6.0 * (double)xv : 0.0);
         fix_add(S[1], gz ? 0.0 : 6.0 * (double)xv);
       }
       ndz += (gz && ax != 0.0f) ? 1u : 0u;
       nclip += ax >= s6up ? 1u : 0u;
-      // component values times 6 (times sc in FP32, exact)
+      // component values times 6 sc (exact: FP32 values and differences
+      // within the block's range; NVFP4's products with t in FP64).  Q_s is
+      // 0 where g = 0, so the selects act on FP32 operands.
       const float x6 = xv * six_sc;
-      const float q6s = es * As;  // 6 Q*(x)
+      const float q6s = es * As;  // 6 Q*(x) sc
       double ct, csb;
       if (FMT == FP4Q_MXFP4) {
-        const float q6a = e * q6u;  // 6 Q_s(x), a power-of-two scale
-        ct = (double)(x6 - q6a) * isc;  // differences within the block's range: exact
-        csb = gz ? 0.0 : (double)(q6s - q6a) * isc;
+        const float q6a = e * q6u;  // 6 Q_s(x) sc, a power-of-two scale
+        ct = (double)(x6 - q6a);
+        csb = (double)((gz ? 0.0f : q6s) - q6a);
       } else {
-        const double q6a = (double)(e * six_sb) * (double)t;
-        ct = 6.0 * (double)xv - q6a;
-        csb = gz ? 0.0 : (double)q6s * isc - q6a;
+        const double q6a = (double)(e * six_sb) * tsc;
+        ct = (double)x6 - q6a;
+        csb = (double)(gz ? 0.0f : q6s) - q6a;
       }
-      const double cdz = gz ? (double)x6 * isc : 0.0;
-      const double cgn = gz ? 0.0 : (double)(x6 - q6s) * isc;
-      sq[0] = __builtin_fma(ct, ct, sq[0]);
-      sq[1] = __builtin_fma(csb, csb, sq[1]);
-      sq[2] = __builtin_fma(cdz, cdz, sq[2]);
-      sq[3] = __builtin_fma(cgn, cgn, sq[3]);
-      cross = __builtin_fma(csb, cgn, cross);
+      const double cdz = (double)(gz ? x6 : 0.0f);
+      const double cgn = (double)(gz ? 0.0f : x6 - q6s);
+      bq[0] = __builtin_fma(ct, ct, bq[0]);
+      bq[1] = __builtin_fma(csb, csb, bq[1]);
+      bq[2] = __builtin_fma(cdz, cdz, bq[2]);
+      bq[3] = __builtin_fma(cgn, cgn, bq[3]);
+      bx = __builtin_fma(csb, cgn, bx);
     }
   }
   }
+  const double isc2 = isc * isc;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) sq[c] = __builtin_fma(bq[c], isc2, sq[c]);
+  cross = __builtin_fma(bx, isc2, cross);
   if (fast) {
     fix_add(S[0], 6.0 * (xa - x1));
     fix_add(S[1], 6.0 * x1);
