@@ -27,14 +27,13 @@ namespace fp4q {
 constexpr int DEC_THREADS = 256;
 constexpr int DEC_MAX_WG = 512;   // two per CU: one round, and few partial records
 
-struct DecPartial {
-  uint64_t fix[4][5];
-  double sq[4];
-  double cross;
-  int64_t ndz, nclip;
-  int64_t pad[5];
-};
-static_assert(sizeof(DecPartial) == 256, "partial record layout");
+// Partial records, one per workgroup of k_decompose, stored slot-major
+// (word slot * G + record, G records) so that the final kernel's threads,
+// one record each, read consecutive words: slots 0..19 the four 320-bit
+// sums (c * 5 + limb), 20..23 the sums of squares, 24 the cross term (FP64
+// bit patterns), 25 and 26 the counts.
+constexpr int DEC_SLOTS = 32;
+constexpr int DS_SQ = 20, DS_CROSS = 24, DS_NDZ = 25, DS_NCLIP = 26;
 
 // a += v, v an FP64 multiple of 2^-136 below 2^183 in magnitude.
 __device__ __forceinline__ void fix_add(uint64_t (&a)[5], double v) {
@@ -77,54 +76,117 @@ __device__ __forceinline__ void fix_add_fix(uint64_t (&a)[5], const uint64_t* b)
   }
 }
 
-// Reduce the per-thread sums over the workgroup through LDS in a fixed tree
-// order and write the workgroup's partial record.
+// A thread's (or a reduction's) share of the statistics.
+struct DecAcc {
+  uint64_t fix[4][5];
+  double sq[5];  // four sums of squares, then the cross term
+  int64_t cnt[2];
+};
+
+// Sum of the workgroup's DecAcc values into `res` (LDS; valid after the
+// barrier this ends with), in a fixed order.  Every thread's values go to
+// LDS field by field, the 320-bit sums as ten 32-bit digits each (their
+// digit-wise sums, carried once at the end, give the sum modulo 2^320, as
+// the two's complement fixed point needs); then four threads per field add
+// a quarter of the threads each in thread order, one thread per field adds
+// the quarters in order, and the carries are propagated.  The FP64 sums are
+// therefore deterministic, and nothing waits on a chain of wide additions.
+constexpr int DR_DIG = 40, DR_FIELDS = DR_DIG + 7;
+__device__ __forceinline__ void dec_acc_reduce(const DecAcc& a, DecAcc& res) {
+  __shared__ uint32_t sdig[DR_DIG][DEC_THREADS];
+  __shared__ uint64_t sw[7][DEC_THREADS];  // five FP64 sums, two counts
+  __shared__ uint64_t squ[DR_FIELDS][4];
+  __shared__ uint64_t sfin[DR_FIELDS];
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      sdig[10 * c + 2 * i][t] = (uint32_t)a.fix[c][i];
+      sdig[10 * c + 2 * i + 1][t] = (uint32_t)(a.fix[c][i] >> 32);
+    }
+#pragma unroll
+  for (int c = 0; c < 5; ++c) sw[c][t] = (uint64_t)__double_as_longlong(a.sq[c]);
+  sw[5][t] = (uint64_t)a.cnt[0];
+  sw[6][t] = (uint64_t)a.cnt[1];
+  __syncthreads();
+  constexpr int QN = DEC_THREADS / 4;
+  if (t < 4 * DR_FIELDS) {
+    const int f = t >> 2, b = (t & 3) * QN;
+    uint64_t v = 0;
+    if (f < DR_DIG) {
+      for (int k = 0; k < QN; ++k) v += sdig[f][b + k];
+    } else if (f < DR_DIG + 5) {
+      double dv = 0.0;
+      for (int k = 0; k < QN; ++k) dv += __longlong_as_double((long long)sw[f - DR_DIG][b + k]);
+      v = (uint64_t)__double_as_longlong(dv);
+    } else {
+      for (int k = 0; k < QN; ++k) v += sw[f - DR_DIG][b + k];
+    }
+    squ[f][t & 3] = v;
+  }
+  __syncthreads();
+  if (t < DR_FIELDS) {
+    uint64_t v;
+    if (t >= DR_DIG && t < DR_DIG + 5) {
+      double dv = 0.0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dv += __longlong_as_double((long long)squ[t][q]);
+      v = (uint64_t)__double_as_longlong(dv);
+    } else {
+      v = squ[t][0] + squ[t][1] + squ[t][2] + squ[t][3];
+    }
+    sfin[t] = v;
+  }
+  __syncthreads();
+  if (t < 4) {  // component t: carry the digit sums
+    uint64_t carry = 0;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      carry += sfin[10 * t + 2 * i];
+      const uint64_t lo = carry & 0xFFFFFFFFull;
+      carry = (carry >> 32) + sfin[10 * t + 2 * i + 1];
+      res.fix[t][i] = lo | (carry << 32);
+      carry >>= 32;
+    }
+  } else if (t == 4) {
+#pragma unroll
+    for (int c = 0; c < 5; ++c) res.sq[c] = __longlong_as_double((long long)sfin[DR_DIG + c]);
+    res.cnt[0] = (int64_t)sfin[DR_DIG + 5];
+    res.cnt[1] = (int64_t)sfin[DR_DIG + 6];
+  }
+  __syncthreads();
+}
+
+// Reduce the per-thread sums over the workgroup and write the workgroup's
+// partial record.
 __device__ __forceinline__ void write_partial(const uint64_t (&fix)[4][5], const double (&sq)[4],
                                               double cross, int64_t ndz, int64_t nclip,
-                                              DecPartial* __restrict__ part) {
-  __shared__ uint64_t sfix[DEC_THREADS][4][5];
-  __shared__ double ssq[DEC_THREADS][5];
-  __shared__ int64_t scnt[DEC_THREADS][2];
-  const int t = threadIdx.x;
+                                              uint64_t* __restrict__ part) {
+  DecAcc a;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
 #pragma unroll
-    for (int i = 0; i < 5; ++i) sfix[t][c][i] = fix[c][i];
-    ssq[t][c] = sq[c];
+    for (int i = 0; i < 5; ++i) a.fix[c][i] = fix[c][i];
+    a.sq[c] = sq[c];
   }
-  ssq[t][4] = cross;
-  scnt[t][0] = ndz;
-  scnt[t][1] = nclip;
-  __syncthreads();
-  for (int s = DEC_THREADS / 2; s > 0; s >>= 1) {
-    if (t < s) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        uint64_t a[5];
-#pragma unroll
-        for (int i = 0; i < 5; ++i) a[i] = sfix[t][c][i];
-        fix_add_fix(a, &sfix[t + s][c][0]);
-#pragma unroll
-        for (int i = 0; i < 5; ++i) sfix[t][c][i] = a[i];
-      }
-#pragma unroll
-      for (int c = 0; c < 5; ++c) ssq[t][c] += ssq[t + s][c];
-      scnt[t][0] += scnt[t + s][0];
-      scnt[t][1] += scnt[t + s][1];
-    }
-    __syncthreads();
-  }
-  if (t == 0) {
-    DecPartial* o = part + blockIdx.x;
+  a.sq[4] = cross;
+  a.cnt[0] = ndz;
+  a.cnt[1] = nclip;
+  __shared__ DecAcc r;
+  dec_acc_reduce(a, r);
+  if (threadIdx.x == 0) {
+    uint64_t* o = part + blockIdx.x;
+    const int64_t G = gridDim.x;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
 #pragma unroll
-      for (int i = 0; i < 5; ++i) o->fix[c][i] = sfix[0][c][i];
-      o->sq[c] = ssq[0][c];
+      for (int i = 0; i < 5; ++i) o[(c * 5 + i) * G] = r.fix[c][i];
+      o[(DS_SQ + c) * G] = (uint64_t)__double_as_longlong(r.sq[c]);
     }
-    o->cross = ssq[0][4];
-    o->ndz = scnt[0][0];
-    o->nclip = scnt[0][1];
+    o[DS_CROSS * G] = (uint64_t)__double_as_longlong(r.sq[4]);
+    o[DS_NDZ * G] = (uint64_t)r.cnt[0];
+    o[DS_NCLIP * G] = (uint64_t)r.cnt[1];
   }
 }
 
@@ -343,7 +405,7 @@ __global__ void __launch_bounds__(DEC_THREADS) k_decompose(const uint16_t* __res
                                                            int64_t rows, int64_t cols, int64_t ldx,
                                                            const uint32_t* __restrict__ amax_part,
                                                            int nparts,
-                                                           DecPartial* __restrict__ part) {
+                                                           uint64_t* __restrict__ part) {
   constexpr int NE = (FMT == FP4Q_NVFP4) ? 16 : 32;
   float t = 1.0f;
   if (FMT == FP4Q_NVFP4) {
@@ -426,78 +488,64 @@ __device__ double fix_to_double(const uint64_t (&a)[5]) {
 // magnitude patterns), or null / 0 for MXFP4.  A tensor amax in (0, 2^-89)
 // (patterns below 0x1300) lets terms fall below the fixed point's LSB: the
 // sums are then flagged FP4Q_DEC_INEXACT.
-__global__ void __launch_bounds__(DEC_THREADS) k_decompose_final(const DecPartial* __restrict__ part,
+__global__ void __launch_bounds__(DEC_THREADS) k_decompose_final(const uint64_t* __restrict__ part,
                                                                  int nparts, int64_t n_elems,
                                                                  const uint32_t* __restrict__ amax_part,
                                                                  int namax,
                                                                  fp4q_err_stats_t* __restrict__ out) {
-  __shared__ uint64_t sfix[DEC_THREADS][4][5];
-  __shared__ double ssq[DEC_THREADS][5];
-  __shared__ int64_t scnt[DEC_THREADS][2];
   __shared__ uint32_t samax[DEC_THREADS / 64];
   const int t = threadIdx.x;
   uint32_t am = 0;
   for (int p = t; p < namax; p += DEC_THREADS) am = max(am, amax_part[p]);
   for (int o = 32; o > 0; o >>= 1) am = max(am, (uint32_t)__shfl_xor((int)am, o));
   if ((t & 63) == 0) samax[t >> 6] = am;
-  uint64_t fix[4][5];
-  double sq[5] = {0, 0, 0, 0, 0};
-  int64_t cnt[2] = {0, 0};
+  DecAcc acc;
 #pragma unroll
   for (int c = 0; c < 4; ++c)
 #pragma unroll
-    for (int i = 0; i < 5; ++i) fix[c][i] = 0;
-  for (int p = t; p < nparts; p += DEC_THREADS) {
+    for (int i = 0; i < 5; ++i) acc.fix[c][i] = 0;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      fix_add_fix(fix[c], &part[p].fix[c][0]);
-      sq[c] += part[p].sq[c];
-    }
-    sq[4] += part[p].cross;
-    cnt[0] += part[p].ndz;
-    cnt[1] += part[p].nclip;
+  for (int c = 0; c < 5; ++c) acc.sq[c] = 0.0;
+  acc.cnt[0] = acc.cnt[1] = 0;
+  // at most two records per thread: all loads issued before the sums
+  static_assert(DEC_MAX_WG <= 2 * DEC_THREADS, "two partial records per thread");
+  const int64_t G = nparts;
+  uint64_t r[2][DS_NCLIP + 1];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int p = t + h * DEC_THREADS;
+#pragma unroll
+    for (int k = 0; k <= DS_NCLIP; ++k) r[h][k] = p < nparts ? part[k * G + p] : 0ull;
   }
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
+  for (int h = 0; h < 2; ++h) {
 #pragma unroll
-    for (int i = 0; i < 5; ++i) sfix[t][c][i] = fix[c][i];
-#pragma unroll
-  for (int c = 0; c < 5; ++c) ssq[t][c] = sq[c];
-  scnt[t][0] = cnt[0];
-  scnt[t][1] = cnt[1];
-  __syncthreads();
-  for (int s = DEC_THREADS / 2; s > 0; s >>= 1) {
-    if (t < s) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        uint64_t a[5];
-#pragma unroll
-        for (int i = 0; i < 5; ++i) a[i] = sfix[t][c][i];
-        fix_add_fix(a, &sfix[t + s][c][0]);
-#pragma unroll
-        for (int i = 0; i < 5; ++i) sfix[t][c][i] = a[i];
-      }
-#pragma unroll
-      for (int c = 0; c < 5; ++c) ssq[t][c] += ssq[t + s][c];
-      scnt[t][0] += scnt[t + s][0];
-      scnt[t][1] += scnt[t + s][1];
+    for (int c = 0; c < 4; ++c) {
+      fix_add_fix(acc.fix[c], &r[h][c * 5]);
+      acc.sq[c] += __longlong_as_double((long long)r[h][DS_SQ + c]);
     }
-    __syncthreads();
+    acc.sq[4] += __longlong_as_double((long long)r[h][DS_CROSS]);
+    acc.cnt[0] += (int64_t)r[h][DS_NDZ];
+    acc.cnt[1] += (int64_t)r[h][DS_NCLIP];
+  }
+  __shared__ DecAcc sres;
+  dec_acc_reduce(acc, sres);  // its barriers also publish samax
+  // lanes 0..3 convert one component each
+  if (t < 4) {
+    uint64_t a[5];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      a[i] = sres.fix[t][i];
+      out->exact[t][i] = (int64_t)a[i];
+    }
+    out->sum[t] = fix_to_double(a) / 6.0;
+    out->sumsq[t] = sres.sq[t];
   }
   if (t == 0) {
-    for (int c = 0; c < 4; ++c) {
-      uint64_t a[5];
-      for (int i = 0; i < 5; ++i) {
-        a[i] = sfix[0][c][i];
-        out->exact[c][i] = (int64_t)a[i];
-      }
-      out->sum[c] = fix_to_double(a) / 6.0;
-      out->sumsq[c] = ssq[0][c];
-    }
-    out->cross_sb_gn = ssq[0][4];
+    out->cross_sb_gn = sres.sq[4];
     out->n_elems = n_elems;
-    out->n_deadzone = scnt[0][0];
-    out->n_clipped = scnt[0][1];
+    out->n_deadzone = sres.cnt[0];
+    out->n_clipped = sres.cnt[1];
     uint32_t m = 0;
     for (int i = 0; i < DEC_THREADS / 64; ++i) m = max(m, samax[i]);
     out->flags = (m != 0u && m < 0x1300u) ? (int64_t)FP4Q_DEC_INEXACT : 0;
@@ -516,15 +564,15 @@ static int64_t dec_grid(int64_t rows, int64_t cols, int blk) {
 // the NVFP4 path's per-workgroup amax words.
 size_t decompose_workspace_bytes(int64_t rows, int64_t cols) {
   const int64_t g = dec_grid(rows, cols, 16);
-  return (size_t)g * sizeof(DecPartial) + (size_t)((g * 4 + 255) / 256 * 256);
+  return (size_t)g * DEC_SLOTS * 8 + (size_t)((g * 4 + 255) / 256 * 256);
 }
 
 int launch_decompose(int fmt, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                      fp4q_err_stats_t* out, void* ws, hipStream_t stream) {
-  DecPartial* part = static_cast<DecPartial*>(ws);
+  uint64_t* part = static_cast<uint64_t*>(ws);
   if (fmt == FP4Q_NVFP4) {
     const int64_t g = dec_grid(rows, cols, 16);
-    uint32_t* amax = reinterpret_cast<uint32_t*>(part + g);
+    uint32_t* amax = reinterpret_cast<uint32_t*>(part + (size_t)DEC_SLOTS * g);
     hipLaunchKernelGGL(k_dec_amax, dim3((unsigned)g), dim3(DEC_THREADS), 0, stream, x, rows, cols,
                        ldx, amax);
     hipLaunchKernelGGL(k_decompose<FP4Q_NVFP4>, dim3((unsigned)g), dim3(DEC_THREADS), 0, stream,

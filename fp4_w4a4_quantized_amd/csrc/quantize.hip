@@ -607,9 +607,12 @@ __global__ void __launch_bounds__(NT) k_quantize(
 // (R WC = 64); with WC = 4 the tile is 16 rows x 128 columns and its 64 code
 // pieces are one 1 KB block of the tiled layout, written contiguously
 // (lane = piece).  The residual of the selected channels of a tile is
-// formed afterwards by lanes indexed by (row, channel), reading the block
-// scale codes the wave left in LDS, so its cost follows the number of
-// selected entries rather than the tile's width.
+// formed afterwards by lanes indexed by (row, channel): the lane holding a
+// channel's unit passes its BF16 value through a small per-wave LDS slot
+// (x is not read again) and the block scale codes come from the wave's LDS
+// copy, so the cost follows the number of selected entries rather than the
+// tile's width.  A workgroup whose tiles' channels fit RES_W columns
+// collects its residual rows in LDS and writes them as contiguous runs.
 //
 // NVFP4 arithmetic, equal to the IEEE single operations the definitions
 // name:
@@ -621,9 +624,10 @@ __global__ void __launch_bounds__(NT) k_quantize(
 //    correctly rounded quotient by Markstein's theorem while t >= 2^-87:
 //    then d >= 2^-96 or d = 0, and a dividend too small for the residual
 //    to be exact gives a quotient far below the first rounding threshold
-//    of its format (code 0 either way).  A smaller tensor scale takes the
-//    IEEE division (the same values, slower).  The remainder is formed
-//    negated, which keeps the sign of a zero quotient.
+//    of its format (code 0 either way).  Below that tensor scale the
+//    dividends, divisors and t are multiplied by 2^64 first (exact, and no
+//    quotient changes).  The remainder is formed negated, which keeps the
+//    sign of a zero quotient.
 // MXFP4 converts the BF16 pairs directly (v_cvt_scalef32_pk_fp4_bf16 with
 // the power-of-two block scale: x / 2^e is exact, so this is the
 // nearest-even E2M1 code of x / 2^e as in the FP32 form; checked on the GPU
@@ -717,9 +721,6 @@ __device__ __forceinline__ uint32_t absmax32_bits(const u32x4 (&w)[4]) {
   return max((uint32_t)m.x, (uint32_t)m.y);
 }
 
-// Codes and the two block scale codes (low byte first) of one NVFP4 unit,
-// one 16-element block after the other (unpacked, divided and packed in
-// turn, so few values are live at once).
 // Codes and the two block scale codes (low byte first) of one NVFP4 unit:
 // both blocks' scale codes and divisors first, from the packed maxima, then
 // each block unpacked, divided and packed (few values live at once).
