@@ -732,22 +732,25 @@ __device__ __forceinline__ uint32_t absmax32_bits(const u32x4 (&w)[4]) {
 // brings the operands into the range where the reciprocal-and-FMA
 // division is correctly rounded; d itself is RN(sb t) unscaled, as defined.
 // ts = t sx and yts = RN(1/ts); the table holds {d sx, RN(1/(d sx))}.
-template <bool TABLE>
+// PS: sx may differ from 1 (a wave-uniform choice; with PS false sx is 1
+// and the products by it are left out).
+template <bool TABLE, bool PS>
 __device__ __forceinline__ void nv_unit(const u32x4 (&w)[4], float t, float sx, float ts,
                                         float yts, const float2* dytab, u32x4& codes,
                                         uint32_t& scw) {
+  if (!PS) sx = 1.0f;
   float dr[2], yr[2];
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     const float v6 = div6_rn(bf16_to_f32(absmax16_bits(w[2 * b], w[2 * b + 1])));
-    const uint32_t sc = e4m3_encode(quot_rn(v6 * sx, ts, yts));
+    const uint32_t sc = e4m3_encode(quot_rn(PS ? v6 * sx : v6, ts, yts));
     scw = b == 0 ? sc : (scw | sc << 8);
     if (TABLE) {
       const float2 dy = dytab[sc];
       dr[b] = dy.x;
       yr[b] = dy.y;
     } else {
-      dr[b] = e4m3_value(sc) * t * sx;
+      dr[b] = PS ? e4m3_value(sc) * t * sx : e4m3_value(sc) * t;
       yr[b] = dr[b] > 0.0f ? 1.0f / dr[b] : 0.0f;
     }
   }
@@ -756,7 +759,7 @@ __device__ __forceinline__ void nv_unit(const u32x4 (&w)[4], float t, float sx, 
   for (int b = 0; b < 2; ++b) {
     const float d = dr[b], y = yr[b];
     auto qt = [&](uint32_t bits) __attribute__((always_inline)) {
-      return quot_rn(__uint_as_float(bits) * sx, d, y);
+      return quot_rn(PS ? __uint_as_float(bits) * sx : __uint_as_float(bits), d, y);
     };
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -1004,7 +1007,10 @@ __global__ void __launch_bounds__(TT) k_quant_tile(TileArgs p) {
     u32x4 codes;
     uint32_t scw;  // this unit's block scale codes (NVFP4: two bytes, low first)
     if (FMT == FP4Q_NVFP4) {
-      nv_unit<!GRP>(v[k], tk, sxk, tsk, ytsk, dytab, codes, scw);
+      if (__builtin_amdgcn_ballot_w64(sxk != 1.0f) != 0)
+        nv_unit<!GRP, true>(v[k], tk, sxk, tsk, ytsk, dytab, codes, scw);
+      else
+        nv_unit<!GRP, false>(v[k], tk, sxk, tsk, ytsk, dytab, codes, scw);
     } else {
       const int e = mx_exponent(bf16_to_f32(absmax32_bits(v[k])));
       scw = (uint32_t)(e + 127);
@@ -1485,7 +1491,10 @@ __global__ void __launch_bounds__(TT) k_qdq_tile(TileArgs p, float* __restrict__
     u32x4 codes;
     uint32_t scw;
     if (FMT == FP4Q_NVFP4) {
-      nv_unit<true>(v[k], t, sx, ts, yts, dytab, codes, scw);
+      if (sx != 1.0f)  // uniform: one tensor scale
+        nv_unit<true, true>(v[k], t, sx, ts, yts, dytab, codes, scw);
+      else
+        nv_unit<true, false>(v[k], t, sx, ts, yts, dytab, codes, scw);
     } else {
       scw = (uint32_t)(mx_exponent(bf16_to_f32(absmax32_bits(v[k]))) + 127);
       const float s = __uint_as_float(scw << 23);
