@@ -58,10 +58,12 @@ def parse():
     p.add_argument("--residual", choices=("bf16", "fp4"), default="bf16",
                    help="compensation residual of the dense workloads: BF16, or quantized a "
                         "second time to the workload's FP4 format (fp4q_gemm_residual_fp4)")
-    p.add_argument("--channels", choices=("fixed", "online"), default="fixed",
-                   help="compensated channels of the dense workloads: the workload's fixed "
-                        "list, or chosen each step by residual magnitude "
-                        "(fp4q_select_channels, k = the workload's channel count)")
+    p.add_argument("--channels", choices=("fixed", "online", "online-2step"), default="fixed",
+                   help="compensated channels: the workload's fixed list, or chosen each step "
+                        "by residual magnitude, k = the workload's channel count (dense: "
+                        "fp4q_quantize_select, the scores taken in the quantizer's pass; "
+                        "online-2step: fp4q_quantize then fp4q_select_channels; MoE: "
+                        "fp4q_select_channels_grouped either way)")
     p.add_argument("--comp-weights", choices=("prepared", "inkernel"), default="prepared",
                    help="fixed channels and the BF16 residual (dense and MoE): stream the "
                         "compensation weights B[n, S_j] made once per weight copy "
@@ -356,18 +358,23 @@ def build_dense(name, cfg, data, args, dev):
     ats = torch.empty(1, dtype=torch.float32, device=dev) if fmt == fq.NVFP4 else None
     ar = torch.empty((M, nS), dtype=torch.int16, device=dev) if nS else None
 
-    online = args.channels == "online"
+    online = args.channels != "fixed"
+    fused_sel = args.channels == "online"
     s.select = None
     if online:
         if nS == 0:
             sys.exit("--channels online needs a workload with compensated channels")
         chan = torch.empty(nS, dtype=torch.int32, device=dev)
-        sws = torch.empty(fq.select_channels_workspace_bytes(M, K), dtype=torch.uint8,
-                          device=dev)
+        if fused_sel:
+            qsws = torch.zeros(max(fq.quantize_select_workspace_bytes(fmt, layout, M, K), 16),
+                               dtype=torch.uint8, device=dev)
+        else:
+            sws = torch.empty(fq.select_channels_workspace_bytes(M, K), dtype=torch.uint8,
+                              device=dev)
 
-        def select():
-            fq.select_channels_into(fmt, layout, x, aq, asc, ats, nS, chan, ar, sws)
-        s.select = select
+            def select():
+                fq.select_channels_into(fmt, layout, x, aq, asc, ats, nS, chan, ar, sws)
+            s.select = select
 
     r4 = args.residual == "fp4"
     if r4:
@@ -383,7 +390,9 @@ def build_dense(name, cfg, data, args, dev):
         gws = torch.empty(gwsb, dtype=torch.uint8, device=dev)
 
     def quant():
-        if online:
+        if fused_sel:
+            fq.quantize_select_into(fmt, layout, x, nS, aq, asc, ats, chan, ar, qsws)
+        elif online:
             fq.quantize_into(fmt, layout, x, None, 1, None, 0, aq, asc, ats, None, qws)
             select()
         else:
@@ -429,7 +438,9 @@ def build_dense(name, cfg, data, args, dev):
     if r4:
         s.quant_bytes += M * nS * 2 + r_bytes
     s.select_bytes = None
-    if online:
+    if fused_sel:
+        s.quant_bytes += nS * 4  # and S; x is read once for codes and scores
+    elif online:
         # the selection reads x, codes and scales again, writes R and S
         s.select_bytes = (M * K * 2 + M * K // 2 + M * K // blk + M * nS * 2 + nS * 4 +
                           (4 if fmt == fq.NVFP4 else 0))
@@ -455,7 +466,7 @@ def build_moe(name, cfg, data, args, dev):
     import torch
 
     import fp4_w4a4_quantized_amd as fq
-    online = args.channels == "online"  # each expert chooses its channels every step
+    online = args.channels != "fixed"  # each expert chooses its channels every step
     r4 = args.residual == "fp4"   # each expert's residual quantized again, own tensor scale
     s = Step()
     s.select = None
@@ -833,7 +844,7 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(name, rec["_data"], rec["_fmt"], args.cpu_seconds,
                            r4=name != "moe_nvfp4" and args.residual == "fp4",
-                           online=args.channels == "online" and name != "moe_nvfp4",
+                           online=args.channels != "fixed" and name != "moe_nvfp4",
                            moe_tok=name == "moe_nvfp4" and args.moe_quant == "token")
     rec.pop("_data")
     rec.pop("_fmt")

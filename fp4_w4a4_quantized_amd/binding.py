@@ -119,6 +119,11 @@ def lib():
         L.fp4q_select_channels.restype = ctypes.c_int
         L.fp4q_select_channels.argtypes = [ctypes.c_int, ctypes.c_int, P, i64, i64, i64, P, P, P,
                                            i32, P, P, P, sz, P]
+        L.fp4q_quantize_select_workspace_bytes.restype = sz
+        L.fp4q_quantize_select_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64]
+        L.fp4q_quantize_select.restype = ctypes.c_int
+        L.fp4q_quantize_select.argtypes = [ctypes.c_int, ctypes.c_int, P, i64, i64, i64, i32, P, P,
+                                           P, P, P, P, sz, P]
         L.fp4q_select_channels_grouped_workspace_bytes.restype = sz
         L.fp4q_select_channels_grouped_workspace_bytes.argtypes = [i64, i64, i32]
         L.fp4q_select_channels_grouped.restype = ctypes.c_int
@@ -319,6 +324,20 @@ def select_channels_into(fmt, layout, x, q, scales, tensor_scale, k, chan_out, r
                                     _ptr(scales), _ptr(tensor_scale), k, _ptr(chan_out),
                                     _ptr(resid_out), _ptr(workspace), ws_bytes, _stream(stream))
     _check("fp4q_select_channels", rc)
+
+
+def quantize_select_workspace_bytes(fmt, layout, rows, cols) -> int:
+    return lib().fp4q_quantize_select_workspace_bytes(fmt, layout, rows, cols)
+
+
+def quantize_select_into(fmt, layout, x, k, q, scales, tensor_scale, chan_out, resid_out,
+                         workspace, stream=None):
+    rows, cols = x.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().fp4q_quantize_select(fmt, layout, _ptr(x), rows, cols, x.stride(0), k, _ptr(q),
+                                    _ptr(scales), _ptr(tensor_scale), _ptr(chan_out),
+                                    _ptr(resid_out), _ptr(workspace), ws_bytes, _stream(stream))
+    _check("fp4q_quantize_select", rc)
 
 
 def permute_quantized_into(fmt, x, q, scales, tensor_scale, row_src, group_offsets, num_groups,
@@ -597,6 +616,32 @@ def select_channels(fmt, x, a, k, stream=None):
     select_channels_into(fmt, a["layout"], x, a["q"], a["scales"], a["tscale"], k, chan, R, ws,
                          stream)
     return chan, R
+
+
+def quantize_select(fmt, x, k, layout=ROWMAJOR, stream=None):
+    """Quantize x (one group) and choose its k channels of largest residual
+    magnitude in one call.  Returns (a, chan, resid): a as quantize(fmt, x,
+    layout=layout) with a["resid"] the residual on chan (int16 bits
+    [rows, k]), chan int32 [k] ascending."""
+    dev = x.device
+    rows, cols = x.shape
+    blk = BLOCK[fmt]
+    if layout == ROWMAJOR:
+        q = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+        sc = torch.empty((rows, cols // blk), dtype=torch.uint8, device=dev)
+    else:
+        cb, sb = packed_bytes(fmt, layout, rows, cols)
+        q = torch.empty(cb, dtype=torch.uint8, device=dev)
+        sc = torch.empty(sb, dtype=torch.uint8, device=dev)
+    ts = torch.empty(1, dtype=torch.float32, device=dev) if fmt == NVFP4 else None
+    chan = torch.empty(max(k, 1), dtype=torch.int32, device=dev)[:k]
+    R = torch.empty((rows, k), dtype=torch.int16, device=dev)
+    wsb = quantize_select_workspace_bytes(fmt, layout, rows, cols)
+    ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)
+    quantize_select_into(fmt, layout, x, k, q, sc, ts, chan, R, ws, stream)
+    a = {"q": q, "scales": sc, "tscale": ts, "resid": R, "layout": layout, "rows": rows,
+         "cols": cols}
+    return a, chan, R
 
 
 def permute_quantized(fmt, x, a, row_src, group_offsets, chan_idx=None, stream=None):

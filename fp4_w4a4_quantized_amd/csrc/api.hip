@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "fp4q_internal.h"
@@ -611,6 +612,59 @@ int fp4q_select_channels(fp4q_format_t fmt, fp4q_layout_t layout, const uint16_t
   fp4q::launch_select(fmt, layout == FP4Q_LAYOUT_TILED, x, rows, cols, ldx, q, scales,
                       tensor_scale, k, chan_out, resid_out, workspace,
                       static_cast<hipStream_t>(stream));
+  return check_launch();
+}
+
+static size_t round256_sz(size_t b) { return (b + 255) / 256 * 256; }
+
+size_t fp4q_quantize_select_workspace_bytes(fp4q_format_t fmt, fp4q_layout_t layout,
+                                            int64_t rows, int64_t cols) {
+  if (!fmt_ok(fmt) || !layout_ok(layout) || rows < 0 || cols <= 0) return 0;
+  const size_t qb = round256_sz(fp4q_quantize_workspace_bytes(fmt, rows, cols, 1));
+  size_t sb = fp4q::select_workspace_bytes(rows, cols);
+  if (rows > 0 && cols % 32 == 0) {
+    const int64_t bands = fp4q::quantize_score_bands(layout == FP4Q_LAYOUT_TILED, rows, cols);
+    sb = std::max(sb, fp4q::select_scored_workspace_bytes(bands, cols));
+  }
+  return qb + sb;
+}
+
+int fp4q_quantize_select(fp4q_format_t fmt, fp4q_layout_t layout, const uint16_t* x,
+                         int64_t rows, int64_t cols, int64_t ldx, int32_t k, uint8_t* q,
+                         uint8_t* scales, float* tensor_scale, int32_t* chan_out,
+                         uint16_t* resid_out, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  const int rc = fp4q::quantize_checks(fmt, layout, x, rows, cols, ldx, nullptr, 1, nullptr, 0, q,
+                                       scales, tensor_scale, nullptr);
+  if (rc != FP4Q_OK) return rc;
+  if (k < 0 || k > cols || ldx % 8 != 0) return FP4Q_ERR_INVALID;
+  if (k > 0 && (!chan_out || !aligned(chan_out, 4))) return FP4Q_ERR_INVALID;
+  if (rows > 0 && k > 0 && (!resid_out || !aligned(resid_out, 2))) return FP4Q_ERR_INVALID;
+  if (rows > 0 && (!aligned(x, 16) || !aligned(q, 4))) return FP4Q_ERR_INVALID;
+  if (cols > INT32_MAX || rows * (int64_t)k >= ((int64_t)1 << 31)) return FP4Q_ERR_UNSUPPORTED;
+  const size_t need = fp4q_quantize_select_workspace_bytes(fmt, layout, rows, cols);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return FP4Q_ERR_WORKSPACE;
+  if (injected_failure()) return FP4Q_ERR_HIP;
+  clear_error();
+  const bool tiled = layout == FP4Q_LAYOUT_TILED;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  void* wsq = workspace;
+  void* wss = static_cast<char*>(workspace) +
+              round256_sz(fp4q_quantize_workspace_bytes(fmt, rows, cols, 1));
+  if (k > 0 && rows > 0 && cols % 32 == 0) {
+    const int64_t bands = fp4q::launch_quantize_scored(fmt, tiled, x, rows, cols, ldx, q, scales,
+                                                       tensor_scale, wsq,
+                                                       static_cast<uint16_t*>(wss), st);
+    fp4q::launch_select_scored(fmt, tiled, x, rows, cols, ldx, q, scales, tensor_scale, k,
+                               chan_out, resid_out, static_cast<const uint16_t*>(wss), bands, wss,
+                               st);
+  } else {
+    fp4q::launch_quantize(fmt, tiled, x, rows, cols, ldx, nullptr, 1, nullptr, 0, q, scales,
+                          tensor_scale, nullptr, wsq, st);
+    if (k > 0)
+      fp4q::launch_select(fmt, tiled, x, rows, cols, ldx, q, scales, tensor_scale, k, chan_out,
+                          resid_out, wss, st);
+  }
   return check_launch();
 }
 

@@ -106,6 +106,18 @@ size_t select_workspace_bytes(int64_t rows, int64_t cols);
 void launch_select(int fmt, bool tiled, const uint16_t* x, int64_t rows, int64_t cols,
                    int64_t ldx, const uint8_t* q, const uint8_t* scales, const float* tscale,
                    int k, int32_t* chan, uint16_t* resid, void* ws, hipStream_t stream);
+// The fused form: the tile quantizer's scored pass (rows > 0, cols % 32 ==
+// 0; score [bands, cols] BF16 bits; returns bands), then steps 2-4 from its
+// partial maxima (workspace: select_scored_workspace_bytes, part first).
+int64_t launch_quantize_scored(int fmt, bool tiled, const uint16_t* x, int64_t rows, int64_t cols,
+                               int64_t ldx, uint8_t* q, uint8_t* scales, float* tscale, void* ws,
+                               uint16_t* score, hipStream_t stream);
+int64_t quantize_score_bands(bool tiled, int64_t rows, int64_t cols);
+size_t select_scored_workspace_bytes(int64_t bands, int64_t cols);
+void launch_select_scored(int fmt, bool tiled, const uint16_t* x, int64_t rows, int64_t cols,
+                          int64_t ldx, const uint8_t* q, const uint8_t* scales,
+                          const float* tscale, int k, int32_t* chan, uint16_t* resid,
+                          const uint16_t* part, int64_t bands, void* ws, hipStream_t stream);
 // Grouped selection (row-major operands; cols <= 30720): chan [G, k], each
 // group's residual rows on its own list.
 size_t select_grouped_workspace_bytes(int64_t rows, int64_t cols, int G);

@@ -643,6 +643,8 @@ constexpr int RES_W = 128;           // residual entries per row a workgroup col
 
 typedef __bf16 bf16x2t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8t __attribute__((ext_vector_type(8)));
+typedef float f32x2t __attribute__((ext_vector_type(2)));
+typedef float f32x4t __attribute__((ext_vector_type(4)));
 
 struct TileArgs {
   const uint16_t* x;
@@ -661,6 +663,8 @@ struct TileArgs {
   int G;
   const uint32_t* gwords;  // groups: NVFP4 amax words (FP32 bits of max |x|), gslots per group
   int gslots;
+  uint16_t* score;  // score mode: column maxima of |x - p| per band of row tiles, BF16 bits
+  uint32_t nrt;     // score mode: row tiles
 };
 
 // NVFP4 tensor scale of group g: the maximum of its amax words.
@@ -846,20 +850,31 @@ __device__ __forceinline__ void chan_range(const int32_t* __restrict__ S, int nS
 // the group amax words) and channel list (chan + g nS); a tile that spans
 // groups takes each lane's group by search and forms the residual group by
 // group.  SL: the one channel list (nS <= SCHAN_MAX) is staged in LDS.
-template <int FMT, bool TILED, int WC, int DU, bool SL, bool GRP>
+// SCORE (one group, no channels yet): the scores of online channel
+// selection come out of the same pass over x, so that x is read once: a
+// workgroup takes one column tile and a band of DU TW row tiles, and writes
+// for each of its columns the largest |x - p| over the band's rows (p the
+// dequantized code, formed as the selection's residual forms it), rounded
+// once to BF16 (nearest-even rounding is monotone, so this is the largest
+// rounded residual).
+template <int FMT, bool TILED, int WC, int DU, bool SL, bool GRP, bool SCORE = false>
 __global__ void __launch_bounds__(TT) k_quant_tile(TileArgs p) {
   constexpr int R = 64 / WC;
   constexpr int SPU = (FMT == FP4Q_NVFP4) ? 2 : 1;  // scale blocks per unit
+  constexpr int SCW = 8 * WC + 4;                   // score mode: a row of a piece in LDS (padded)
   static_assert(!TILED || WC == 4, "the tiled layout's code block is 16 rows x 128 columns");
   static_assert(!(SL && GRP), "one staged channel list");
-  __shared__ uint32_t ctab[GRP ? 1 : CTAB_MAX];
+  static_assert(!(SCORE && (GRP || SL)), "scores: one group, no channel list");
+  __shared__ uint32_t ctab[GRP || SCORE ? 1 : CTAB_MAX];
   __shared__ int32_t schan[SL ? SCHAN_MAX : 1];
   __shared__ float2 dytab[GRP ? 1 : 128];
   __shared__ uint8_t scx[TW][64 * SPU];
   __shared__ int32_t rgrp[GRP ? RG_MAX : 1];
   __shared__ int32_t soff[GRP ? SOFF_MAX : 1];
-  __shared__ uint16_t sres[16][RES_W];  // the workgroup's residual rows (see agg)
+  __shared__ uint16_t sres[SCORE ? 1 : 16][SCORE ? 1 : RES_W];  // the workgroup's residual rows (see agg)
   __shared__ uint16_t xres[TW][64 / R][R];  // a residual pass's x values, per wave
+  __shared__ __attribute__((aligned(16))) float ssc[SCORE ? TW : 1][SCORE ? R : 1][SCORE ? SCW : 1];  // a piece's x - p, per wave
+  __shared__ float swc[SCORE ? TW : 1][SCORE ? 32 * WC : 1];             // the waves' column maxima
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane % R, c = lane / R;
@@ -869,9 +884,17 @@ __global__ void __launch_bounds__(TT) k_quant_tile(TileArgs p) {
   // this wave's tiles and their loads, before anything else
   u32x4 v[DU][4];
   uint32_t tile[DU];
+  // score mode: column tile bct and row tiles band DU TW .. of it; a tile
+  // past the last row tile is marked ntiles (none)
+  const uint32_t bct = SCORE ? blockIdx.x % nct : 0u, band = SCORE ? blockIdx.x / nct : 0u;
 #pragma unroll
   for (int k = 0; k < DU; ++k) {
-    tile[k] = (blockIdx.x * DU + k) * TW + wave;
+    if (SCORE) {
+      const uint32_t rt = band * (DU * TW) + k * TW + wave;
+      tile[k] = rt < p.nrt ? rt * nct + bct : p.ntiles;
+    } else {
+      tile[k] = (blockIdx.x * DU + k) * TW + wave;
+    }
     const uint32_t T = tile[k] < p.ntiles ? tile[k] : p.ntiles - 1;
     const uint32_t rt = T / nct, ct = T - rt * nct;
     uint32_t row = rt * R + r, uc = ct * WC + c;
@@ -987,6 +1010,10 @@ __global__ void __launch_bounds__(TT) k_quant_tile(TileArgs p) {
     nres[k] = (jh - jl) * R;
   }
 
+  // score mode: lane l reduces column l % (8 WC) of each 8-column piece over
+  // eight rows (row group l / (8 WC)); cm[i] keeps piece i's maximum
+  float cm[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+
 #pragma unroll
   for (int k = 0; k < DU; ++k) {
     if (tile[k] >= p.ntiles) break;
@@ -1050,9 +1077,53 @@ __global__ void __launch_bounds__(TT) k_quant_tile(TileArgs p) {
         p.scales[so] = (uint8_t)scw;
     }
 
+    if (SCORE) {
+      // |x - p| of the unit's elements, one 8-element piece at a time, and
+      // its maximum over the tile's rows (rows past the end repeat the
+      // last row, units past the end a real unit whose columns are not
+      // stored; neither changes a stored maximum)
+      float sv[SPU];
+#pragma unroll
+      for (int b = 0; b < SPU; ++b)
+        sv[b] = FMT == FP4Q_NVFP4 ? e4m3_value((scw >> (8 * b)) & 0xFFu) : exp2i((int)scw - 127);
+      const int cc = lane % (8 * WC), rg = lane / (8 * WC);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float s = sv[FMT == FP4Q_NVFP4 ? (i >> 1) : 0];
+        const uint32_t cw = codes[i];
+        const u32x4 w = v[k][i];
+        const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+        // signed E2M1 values (exact; code 8 gives a zero of either sign,
+        // which |x - p| does not see)
+        const f32x2t ev[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 0),
+                              __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 1),
+                              __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 2),
+                              __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 3)};
+        float dv[8];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const f32x2t e = ev[h];
+          const float p0 = FMT == FP4Q_NVFP4 ? (e.x * s) * tk : e.x * s;
+          const float p1 = FMT == FP4Q_NVFP4 ? (e.y * s) * tk : e.y * s;
+          dv[2 * h] = __uint_as_float(wd[h] << 16) - p0;
+          dv[2 * h + 1] = __uint_as_float(wd[h] & 0xFFFF0000u) - p1;
+        }
+        *reinterpret_cast<f32x4t*>(&ssc[wave][r][8 * c]) = f32x4t{dv[0], dv[1], dv[2], dv[3]};
+        *reinterpret_cast<f32x4t*>(&ssc[wave][r][8 * c + 4]) = f32x4t{dv[4], dv[5], dv[6], dv[7]};
+        __builtin_amdgcn_wave_barrier();
+        float m = cm[i];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(ssc[wave][8 * rg + j][cc]));
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int o = 8 * WC; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+        cm[i] = m;
+      }
+    }
+
     // residual of the selected channels in this tile's columns, group by
     // group: lane i of a pass takes row i % R and channel jlo + i / R
-    if (nS > 0) {
+    if (!SCORE && nS > 0) {
       if (SPU == 2)
         *reinterpret_cast<uint16_t*>(&scx[wave][2 * lane]) = (uint16_t)scw;
       else
@@ -1126,6 +1197,22 @@ __global__ void __launch_bounds__(TT) k_quant_tile(TileArgs p) {
           }
         }
       }
+    }
+  }
+  if (SCORE) {
+    // the waves meet in LDS: lane l < 8 WC holds column (l / 8) 32 + 8 i + l % 8
+    // of the tile for piece i
+    if (lane < 8 * WC) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) swc[wave][(lane >> 3) * 32 + 8 * i + (lane & 7)] = cm[i];
+    }
+    __syncthreads();
+    if (threadIdx.x < 32 * WC) {
+      float m = 0.0f;
+#pragma unroll
+      for (int w = 0; w < TW; ++w) m = fmaxf(m, swc[w][threadIdx.x]);
+      const int64_t col = (int64_t)bct * (32 * WC) + threadIdx.x;
+      if (col < p.cols) p.score[(int64_t)band * p.cols + col] = (uint16_t)f32_to_bf16_rne(m);
     }
   }
   if (agg) {  // uniform over the workgroup
@@ -1270,6 +1357,41 @@ static void launch_tile(bool tiled, const uint16_t* x, int64_t rows, int64_t col
   else launch_tile_g<FMT, false>(tiled, a, wc, stream);
 }
 
+// Score mode of the tile quantizer (one group, no channels): codes, scales
+// and tensor scale as launch_tile, plus score [bands, cols] (BF16 bits),
+// bands = ceil(row tiles / (TDU TW)); returns bands.
+template <int FMT>
+static int64_t launch_tile_score(bool tiled, const uint16_t* x, int64_t rows, int64_t cols,
+                                 int64_t ldx, uint8_t* q, uint8_t* scales, float* tscale,
+                                 const uint32_t* parts, int nparts, uint16_t* score,
+                                 hipStream_t stream) {
+  TileArgs a{};
+  a.gslots = 1;
+  a.x = x; a.ldx = ldx; a.cols = cols;
+  a.rows = (uint32_t)rows;
+  a.upr = (uint32_t)(cols / 32);
+  a.G = 1;
+  a.q = q; a.scales = scales; a.tscale = tscale;
+  a.parts = parts; a.nparts = nparts;
+  a.score = score;
+  const int wc = tiled || a.upr >= 3 ? 4 : (int)a.upr;
+  const uint32_t R = 64u / (uint32_t)wc;
+  a.nct = (a.upr + wc - 1) / wc;
+  a.nrt = (uint32_t)((rows + R - 1) / R);
+  a.ntiles = a.nrt * a.nct;
+  const int64_t bands = ((int64_t)a.nrt + TDU * TW - 1) / (TDU * TW);
+  const dim3 grid((unsigned)(bands * a.nct));
+  if (tiled)
+    hipLaunchKernelGGL((k_quant_tile<FMT, true, 4, TDU, false, false, true>), grid, dim3(TT), 0, stream, a);
+  else if (wc == 4)
+    hipLaunchKernelGGL((k_quant_tile<FMT, false, 4, TDU, false, false, true>), grid, dim3(TT), 0, stream, a);
+  else if (wc == 2)
+    hipLaunchKernelGGL((k_quant_tile<FMT, false, 2, TDU, false, false, true>), grid, dim3(TT), 0, stream, a);
+  else
+    hipLaunchKernelGGL((k_quant_tile<FMT, false, 1, TDU, false, false, true>), grid, dim3(TT), 0, stream, a);
+  return bands;
+}
+
 template <int FMT, int MODE, int NT, int U>
 static void launch_q(const ChunkGrid& gr, int64_t rows, int64_t cols, bool tiled,
                      hipStream_t stream, const int32_t* off, int G, const int32_t* chan, int nS,
@@ -1365,6 +1487,35 @@ int launch_quantize(int fmt, bool tiled, const uint16_t* x, int64_t rows, int64_
     launch_q<FP4Q_NVFP4, AMAX_PARTIALS, QT, QU>(gr, rows, cols, tiled, stream, off, 1, chan, nS, q,
                                                  scales, tscale, resid, words, (int)parts);
   return 0;
+}
+
+// The quantizer's pass that also scores the columns for online channel
+// selection (one group, no channels, rows > 0, cols % 32 == 0): score
+// [bands, cols] BF16 bits; returns bands.  NVFP4 takes the partial-amax pass
+// first, into the workspace's amax words.
+int64_t launch_quantize_scored(int fmt, bool tiled, const uint16_t* x, int64_t rows, int64_t cols,
+                               int64_t ldx, uint8_t* q, uint8_t* scales, float* tscale, void* ws,
+                               uint16_t* score, hipStream_t stream) {
+  if (fmt == FP4Q_MXFP4)
+    return launch_tile_score<FP4Q_MXFP4>(tiled, x, rows, cols, ldx, q, scales, tscale, nullptr, 0,
+                                         score, stream);
+  uint32_t* words = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + WS_HEADER);
+  const int64_t chunks = rows * (cols >> 3);
+  const ChunkGrid gr{x, (uint32_t)(cols >> 3), ldx, 1.0 / (double)(cols >> 3), ldx == cols};
+  int64_t parts = (chunks + (int64_t)QT * AMAX_BATCH - 1) / ((int64_t)QT * AMAX_BATCH);
+  parts = parts < TILE_PARTS ? parts : TILE_PARTS;
+  hipLaunchKernelGGL(k_amax_partial, dim3((unsigned)parts), dim3(QT), 0, stream, gr,
+                     (uint32_t)chunks, words);
+  return launch_tile_score<FP4Q_NVFP4>(tiled, x, rows, cols, ldx, q, scales, tscale, words,
+                                       (int)parts, score, stream);
+}
+
+// Bands of the scored pass (the score buffer holds bands x cols entries).
+int64_t quantize_score_bands(bool tiled, int64_t rows, int64_t cols) {
+  const int64_t upr = cols / 32;
+  const int64_t wc = tiled || upr >= 3 ? 4 : upr;
+  const int64_t nrt = (rows + 64 / wc - 1) / (64 / wc);
+  return (nrt + TDU * TW - 1) / (TDU * TW);
 }
 
 // ---- Outlier Fallback: quantize-dequantize with the deadzone entries kept ----

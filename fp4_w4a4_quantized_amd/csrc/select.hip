@@ -488,22 +488,19 @@ __global__ __launch_bounds__(RS_THREADS) void k_chan_resid(
   }
 }
 
+// Steps 2-4 from the partial maxima part [nparts, cols]; sbuf: cols entries
+// for the reduction's output (used when it gets its own launch).
 template <int FMT>
-void launch_select_fmt(bool tiled, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+void select_from_parts(bool tiled, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                        const uint8_t* q, const uint8_t* scales, const float* tscale, int k,
-                       int32_t* chan, uint16_t* resid, void* ws, hipStream_t stream) {
-  const ScorePlan pl = score_plan(rows, cols);
-  uint16_t* part = static_cast<uint16_t*>(ws);
-  uint16_t* score = part;
-  const dim3 sg((unsigned)((cols / 8 + SC_CHUNKS - 1) / SC_CHUNKS), (unsigned)pl.parts);
-  hipLaunchKernelGGL((k_chan_score<FMT, false>), sg, dim3(SC_THREADS), 0, stream, x, rows, cols,
-                     ldx, tiled, q, scales, tscale, pl.rb, nullptr, 1, part);
-  int parts = (int)pl.parts;
-  if (reduce_launch(pl.parts, cols)) {
-    score = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) +
-                                        round256((size_t)pl.parts * cols * 2));
+                       int32_t* chan, uint16_t* resid, const uint16_t* part, int64_t nparts,
+                       uint16_t* sbuf, hipStream_t stream) {
+  const uint16_t* score = part;
+  int parts = (int)nparts;
+  if (reduce_launch(nparts, cols)) {
     hipLaunchKernelGGL(k_chan_reduce, dim3((unsigned)((cols + 127) / 128)), dim3(RD_THREADS), 0,
-                       stream, part, pl.parts, cols, score);
+                       stream, part, nparts, cols, sbuf);
+    score = sbuf;
     parts = 1;
   }
   if (cols <= PK_LDS_COLS)
@@ -518,6 +515,21 @@ void launch_select_fmt(bool tiled, const uint16_t* x, int64_t rows, int64_t cols
     hipLaunchKernelGGL((k_chan_resid<FMT, false>), dim3((total + RS_THREADS - 1) / RS_THREADS),
                        dim3(RS_THREADS), 0, stream, x, rows, cols, ldx, tiled, q, scales, tscale,
                        chan, (uint32_t)k, total, resid, nullptr, 1);
+}
+
+template <int FMT>
+void launch_select_fmt(bool tiled, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                       const uint8_t* q, const uint8_t* scales, const float* tscale, int k,
+                       int32_t* chan, uint16_t* resid, void* ws, hipStream_t stream) {
+  const ScorePlan pl = score_plan(rows, cols);
+  uint16_t* part = static_cast<uint16_t*>(ws);
+  const dim3 sg((unsigned)((cols / 8 + SC_CHUNKS - 1) / SC_CHUNKS), (unsigned)pl.parts);
+  hipLaunchKernelGGL((k_chan_score<FMT, false>), sg, dim3(SC_THREADS), 0, stream, x, rows, cols,
+                     ldx, tiled, q, scales, tscale, pl.rb, nullptr, 1, part);
+  uint16_t* sbuf =
+      reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + round256((size_t)pl.parts * cols * 2));
+  select_from_parts<FMT>(tiled, x, rows, cols, ldx, q, scales, tscale, k, chan, resid, part,
+                         pl.parts, sbuf, stream);
 }
 
 // Grouped: score tiles (group, row block) bounded by ceil(rows / rb) + G.
@@ -560,6 +572,29 @@ size_t select_grouped_workspace_bytes(int64_t rows, int64_t cols, int G) {
 }
 
 bool select_grouped_cols_ok(int64_t cols) { return cols <= PK_LDS_COLS; }
+
+// The scored quantizer's partial maxima (bands x cols), then the reduction's
+// output when it gets a launch of its own.
+size_t select_scored_workspace_bytes(int64_t bands, int64_t cols) {
+  if (bands < 1 || cols <= 0) return 0;
+  size_t b = round256((size_t)bands * (size_t)cols * 2);
+  if (reduce_launch(bands, cols)) b += round256((size_t)cols * 2);
+  return b;
+}
+
+void launch_select_scored(int fmt, bool tiled, const uint16_t* x, int64_t rows, int64_t cols,
+                          int64_t ldx, const uint8_t* q, const uint8_t* scales,
+                          const float* tscale, int k, int32_t* chan, uint16_t* resid,
+                          const uint16_t* part, int64_t bands, void* ws, hipStream_t stream) {
+  uint16_t* sbuf =
+      reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + round256((size_t)bands * cols * 2));
+  if (fmt == FP4Q_NVFP4)
+    select_from_parts<FP4Q_NVFP4>(tiled, x, rows, cols, ldx, q, scales, tscale, k, chan, resid,
+                                  part, bands, sbuf, stream);
+  else
+    select_from_parts<FP4Q_MXFP4>(tiled, x, rows, cols, ldx, q, scales, tscale, k, chan, resid,
+                                  part, bands, sbuf, stream);
+}
 
 void launch_select_grouped(int fmt, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                            const uint8_t* q, const uint8_t* scales, const float* tscale,

@@ -468,6 +468,37 @@ int fp4q_select_channels(fp4q_format_t fmt, fp4q_layout_t layout, const uint16_t
                          int32_t* chan_out, uint16_t* resid_out, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/* Quantization and online channel selection in one call, the selection's
+ * scores taken in the quantizer's own pass over x (the survey's fused
+ * form of the QUADS top-k channel mask; explainer section 2.2 B): the
+ * results are bit-identical to fp4q_quantize (one group, no channels)
+ * followed by fp4q_select_channels with the same k, and x is read once for
+ * codes and scores (then again only at the k chosen columns, for R).
+ *
+ *   fmt, layout, x, rows, cols, ldx   as fp4q_quantize (x 16-byte aligned,
+ *                                     ldx a multiple of 8)
+ *   k                                 channels to keep, 0 <= k <= cols
+ *   q, scales, tensor_scale           out, as fp4q_quantize (q 4-byte aligned)
+ *   chan_out, resid_out               out, as fp4q_select_channels
+ *   workspace                         device scratch of
+ *                                     fp4q_quantize_select_workspace_bytes()
+ *                                     bytes, 16-byte aligned; for NVFP4 its
+ *                                     first part is the quantize workspace
+ *                                     and carries that workspace's state and
+ *                                     status word (fp4q_quantize_status)
+ *
+ * A column count that is not a multiple of 32 takes the two steps one after
+ * the other (same results).  Errors as the two calls; k == 0 quantizes only.
+ * ------------------------------------------------------------------------ */
+size_t fp4q_quantize_select_workspace_bytes(fp4q_format_t fmt, fp4q_layout_t layout,
+                                            int64_t rows, int64_t cols);
+
+int fp4q_quantize_select(fp4q_format_t fmt, fp4q_layout_t layout, const uint16_t* x,
+                         int64_t rows, int64_t cols, int64_t ldx, int32_t k, uint8_t* q,
+                         uint8_t* scales, float* tensor_scale, int32_t* chan_out,
+                         uint16_t* resid_out, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
 /* Grouped form (the MoE layer: QUADS abstract, NVFP4 rollout for MoE;
  * explainer section 2.2 B): each group g (rows group_offsets[g] ..
  * group_offsets[g+1]) chooses its own k channels from its own rows, with

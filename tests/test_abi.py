@@ -427,6 +427,46 @@ def test_select_channels_rejects(L):
     assert sel(L, rows=0, x=None, qq=None, sc=None, R=None, k=0, chan=None) == 0
 
 
+def qsel(L, fmt=0, layout=0, x=A, rows=4, cols=64, ldx=64, k=8, qq=B, sc=B, ts=B, chan=A, R=B,
+         ws=A, wsb=1 << 20):
+    return L.fp4q_quantize_select(fmt, layout, x, rows, cols, ldx, k, qq, sc, ts, chan, R, ws, wsb,
+                                  None)
+
+
+def test_quantize_select_rejects(L):
+    assert qsel(L, fmt=2) == INVALID
+    assert qsel(L, layout=3) == INVALID
+    assert qsel(L, cols=40, ldx=40) == INVALID           # not whole NVFP4 blocks
+    assert qsel(L, layout=1) == INVALID                  # tiled needs cols % 128 == 0
+    assert qsel(L, ldx=68) == INVALID                    # ldx % 8
+    assert qsel(L, k=-1) == INVALID
+    assert qsel(L, k=65) == INVALID                      # more channels than columns
+    assert qsel(L, ts=None) == INVALID                   # NVFP4 writes its tensor scale
+    assert qsel(L, fmt=1) == INVALID                     # MXFP4 has none
+    assert qsel(L, chan=None) == INVALID
+    assert qsel(L, R=None) == INVALID
+    assert qsel(L, qq=None) == INVALID
+    assert qsel(L, x=ctypes.c_void_p(0x10008)) == INVALID   # x 16-byte aligned
+    assert qsel(L, qq=ctypes.c_void_p(0x20002)) == INVALID  # codes 4-byte aligned
+    assert qsel(L, ws=None) == WORKSPACE
+    assert qsel(L, wsb=16) == WORKSPACE
+    assert qsel(L, ws=ctypes.c_void_p(0x10008)) == WORKSPACE
+    assert qsel(L, rows=1 << 27, cols=64, k=32) == UNSUPPORTED   # rows * k >= 2^31
+
+
+def test_quantize_select_workspace(L):
+    f = L.fp4q_quantize_select_workspace_bytes
+    q = L.fp4q_quantize_workspace_bytes
+    rq = lambda b: (b + 255) // 256 * 256
+    # the quantize workspace, then the larger of the two selection paths'
+    assert f(0, 0, 4, 64) >= rq(q(0, 4, 64, 1)) + L.fp4q_select_channels_workspace_bytes(4, 64)
+    assert f(1, 0, 4, 64) >= L.fp4q_select_channels_workspace_bytes(4, 64)
+    # prefill activations, tiled: 64 bands of 128 rows, scores [64, 4096] BF16
+    big = f(0, 1, 8192, 4096)
+    assert big >= rq(q(0, 8192, 4096, 1)) + 64 * 4096 * 2 and big % 256 == 0
+    assert f(0, 0, -1, 64) == 0 and f(0, 0, 4, 0) == 0 and f(5, 0, 4, 64) == 0
+
+
 def test_select_channels_grouped_rejects(L):
     P, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
     L.fp4q_select_channels_grouped.argtypes = [ctypes.c_int, P, i64, i64, i64, P, i32, P, P, P,
