@@ -183,6 +183,27 @@ __device__ __forceinline__ h16x2 e4m3_h2(uint32_t code) {
 // knows the LDS reads issued before it are complete.  The scheduling
 // barriers keep the compiler from moving any instruction across, so each
 // stage's LDS reads and MFMAs stay in their own interval.
+// a *= s, an accumulator block kept in its AGPRs: eight values at a time
+// are read out, multiplied (the IEEE single product, as a plain multiply
+// would give) and written back through eight scratch VGPRs.  Written out
+// because in the four-wave kernels the compiler's own form of this step,
+// between the main loop and the compensation stages, spilled to scratch
+// memory (about 130 bytes per lane and tile) and cost about 10 us per
+// prefill GEMM; the eight-wave kernel keeps the plain multiply, which does
+// not spill there.
+__device__ __forceinline__ void scale_acc(f32x16& a, float s) {
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    float t[8];
+    asm volatile("v_accvgpr_read_b32 %8, %0\n\tv_accvgpr_read_b32 %9, %1\n\tv_accvgpr_read_b32 %10, %2\n\tv_accvgpr_read_b32 %11, %3\n\tv_accvgpr_read_b32 %12, %4\n\tv_accvgpr_read_b32 %13, %5\n\tv_accvgpr_read_b32 %14, %6\n\tv_accvgpr_read_b32 %15, %7\n\t"
+                 "v_mul_f32 %8, %8, %16\n\tv_mul_f32 %9, %9, %16\n\tv_mul_f32 %10, %10, %16\n\tv_mul_f32 %11, %11, %16\n\tv_mul_f32 %12, %12, %16\n\tv_mul_f32 %13, %13, %16\n\tv_mul_f32 %14, %14, %16\n\tv_mul_f32 %15, %15, %16\n\t"
+                 "v_accvgpr_write_b32 %0, %8\n\tv_accvgpr_write_b32 %1, %9\n\tv_accvgpr_write_b32 %2, %10\n\tv_accvgpr_write_b32 %3, %11\n\tv_accvgpr_write_b32 %4, %12\n\tv_accvgpr_write_b32 %5, %13\n\tv_accvgpr_write_b32 %6, %14\n\tv_accvgpr_write_b32 %7, %15"
+                 : "+a"(a[8 * g + 0]), "+a"(a[8 * g + 1]), "+a"(a[8 * g + 2]), "+a"(a[8 * g + 3]), "+a"(a[8 * g + 4]), "+a"(a[8 * g + 5]), "+a"(a[8 * g + 6]), "+a"(a[8 * g + 7]),
+                   "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]), "=&v"(t[6]), "=&v"(t[7])
+                 : "v"(s));
+  }
+}
+
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("" ::: "memory");
@@ -948,7 +969,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_nv4(BigArgs args) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] *= tx;
+    for (int j = 0; j < 4; ++j) scale_acc(acc[i][j], tx);
   for (int s = nk; s < ns; ++s) {
     open(s);
     comp4_stage(acc, stage(s), stage(s) + SL::B, wm, wn, lane);
@@ -1209,7 +1230,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_nv4g(BigArgs args) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] *= tx;
+    for (int j = 0; j < 4; ++j) scale_acc(acc[i][j], tx);
   for (int s = nk; s < ns; ++s) {
     open(s);
     comp4_stage(acc, stage(s), stage(s) + G4Layout::B, 0, wave, lane);
