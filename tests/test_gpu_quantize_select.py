@@ -139,3 +139,25 @@ def test_quantize_select_equals_two_calls(fmt, layout):
         if fmt == 0:
             assert torch.equal(a1["tscale"].view(torch.int32), a2["tscale"].view(torch.int32))
         assert torch.equal(c1, c2) and torch.equal(r1, r2)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("layout", [fq.ROWMAJOR, fq.TILED])
+def test_quantize_select_strided_rows(orc, fmt, layout):
+    """x as a column slice of a wider tensor (ldx = cols + 64): the scored
+    pass reads rows by ldx; results as for the contiguous tensor."""
+    need_gpu()
+    say(f"quantize_select strided fmt {fmt} layout {layout}")
+    M, K, k = 200, 512, 24
+    d = dense_case(M, K, 8, n_out=8, seed=41 + fmt)
+    wide = np.zeros((M, K + 64), np.uint16)
+    wide[:, :K] = d["x"]
+    wide[:, K:] = bf16_bits(np.full((M, 64), 1e4, np.float32))  # never part of x
+    xw = to_dev(wide)[:, :K]
+    qx = orc.quantize(fmt, d["x"])
+    want_c, want_r = orc.select_channels(fmt, d["x"], qx, k)
+    a, chan, R = fq.quantize_select(fmt, xw, k, layout=layout)
+    torch.cuda.synchronize()
+    assert_quant_equal(dict(a, resid=None), qx, fmt)
+    assert np.array_equal(to_host(chan), want_c)
+    assert np.array_equal(to_host(R), want_r)
