@@ -784,13 +784,14 @@ __device__ __forceinline__ float div_prescale(float t) { return t >= 0x1p-87f ? 
 
 constexpr int RG_MAX = TDU * TW * 64;  // rows the tiles of one workgroup cover at most
 constexpr int SOFF_MAX = 2048;         // group offsets staged in LDS (G + 1 at most)
+constexpr int GT_MAX = 4;              // groups of a workgroup with their divisor tables in LDS
 
 // rgrp[i] = group of row rbase + i, for the rows of this workgroup's tiles:
 // the offsets are staged in LDS (soff, when G < SOFF_MAX) and searched
 // there, one row per thread.  Contains a barrier; returns rbase.
 template <int R, int DU>
 __device__ __forceinline__ uint32_t build_row_groups(const TileArgs& p, int32_t* rgrp,
-                                                     int32_t* soff) {
+                                                     int32_t* soff, uint32_t* nrows = nullptr) {
   const uint32_t T0 = blockIdx.x * DU * TW;
   const uint32_t T1 = (T0 + DU * TW < p.ntiles ? T0 + DU * TW : p.ntiles) - 1;
   const uint32_t rbase = (T0 / p.nct) * R;
@@ -813,6 +814,7 @@ __device__ __forceinline__ uint32_t build_row_groups(const TileArgs& p, int32_t*
       rgrp[i] = group_of_row(p.off, G, rbase + i);
   }
   __syncthreads();
+  if (nrows) *nrows = rlim - rbase;
   return rbase;
 }
 
@@ -875,6 +877,12 @@ __global__ void __launch_bounds__(TT) k_quant_tile(TileArgs p) {
   __shared__ uint16_t xres[TW][64 / R][R];  // a residual pass's x values, per wave
   __shared__ __attribute__((aligned(16))) float ssc[SCORE ? TW : 1][SCORE ? R : 1][SCORE ? SCW : 1];  // a piece's x - p, per wave
   __shared__ float swc[SCORE ? TW : 1][SCORE ? 32 * WC : 1];             // the waves' column maxima
+  // grouped NVFP4: the tensor scales {t, sx, t sx, RN(1/(t sx))} and divisor
+  // tables {d sx, RN(1/(d sx))} of the workgroup's groups, when it spans at
+  // most GT_MAX of them (the usual case: its tiles cover 16 or 32 rows)
+  constexpr bool GTAB = GRP && FMT == FP4Q_NVFP4;
+  __shared__ float4 gts[GTAB ? GT_MAX : 1];
+  __shared__ float2 gdy[GTAB ? GT_MAX : 1][GTAB ? 128 : 1];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane % R, c = lane / R;
@@ -940,7 +948,31 @@ __global__ void __launch_bounds__(TT) k_quant_tile(TileArgs p) {
     __syncthreads();
   }
   uint32_t rbase = 0;
-  if constexpr (GRP) rbase = build_row_groups<R, DU>(p, rgrp, soff);
+  int gA = 0;
+  bool use_gt = false;
+  if constexpr (GRP) {
+    uint32_t nrow = 0;
+    rbase = build_row_groups<R, DU>(p, rgrp, soff, &nrow);
+    if (GTAB && nrow > 0) {
+      gA = rgrp[0];
+      const int ng = rgrp[nrow - 1] - gA + 1;
+      use_gt = ng <= GT_MAX;  // uniform
+      if (use_gt) {
+        if ((int)threadIdx.x < ng) {
+          const float tg = group_tscale(p, gA + (int)threadIdx.x);
+          const float sg = div_prescale(tg);
+          gts[threadIdx.x] = float4{tg, sg, tg * sg, 1.0f / (tg * sg)};
+        }
+        __syncthreads();
+        for (int i = threadIdx.x; i < ng * 128; i += TT) {
+          const float4 T = gts[i >> 7];
+          const float d = e4m3_value((uint32_t)(i & 127)) * T.x * T.y;
+          gdy[i >> 7][i & 127] = float2{d, d > 0.0f ? 1.0f / d : 0.0f};
+        }
+        __syncthreads();
+      }
+    }
+  }
   // entry j of the channel list of group g
   auto chan_at = [&](int g, int j) __attribute__((always_inline)) -> int64_t {
     if (SL) return (int64_t)schan[j];
@@ -1023,21 +1055,35 @@ __global__ void __launch_bounds__(TT) k_quant_tile(TileArgs p) {
     const bool active = row < p.rows && uc < p.upr;
     // this lane's group and its NVFP4 tensor scale
     float tk = t, sxk = sx, tsk = ts, ytsk = yts;
-    if (GRP && FMT == FP4Q_NVFP4) {
+    const float2* dyk = dytab;
+    if (GTAB) {
       const int g = g0[k] == g1[k] ? g0[k] : rgrp[(row < p.rows ? row : p.rows - 1) - rbase];
-      tk = group_tscale(p, g);
-      sxk = div_prescale(tk);
-      tsk = tk * sxk;
-      ytsk = 1.0f / tsk;
+      if (use_gt) {
+        const float4 T = gts[g - gA];
+        tk = T.x;
+        sxk = T.y;
+        tsk = T.z;
+        ytsk = T.w;
+        dyk = gdy[g - gA];
+      } else {
+        tk = group_tscale(p, g);
+        sxk = div_prescale(tk);
+        tsk = tk * sxk;
+        ytsk = 1.0f / tsk;
+      }
       if (active && uc == 0 && row == (uint32_t)p.off[g]) p.tscale[g] = tk;
     }
     u32x4 codes;
     uint32_t scw;  // this unit's block scale codes (NVFP4: two bytes, low first)
     if (FMT == FP4Q_NVFP4) {
-      if (__builtin_amdgcn_ballot_w64(sxk != 1.0f) != 0)
-        nv_unit<!GRP, true>(v[k], tk, sxk, tsk, ytsk, dytab, codes, scw);
-      else
-        nv_unit<!GRP, false>(v[k], tk, sxk, tsk, ytsk, dytab, codes, scw);
+      const bool ps = __builtin_amdgcn_ballot_w64(sxk != 1.0f) != 0;
+      if (!GRP || use_gt) {
+        if (ps) nv_unit<true, true>(v[k], tk, sxk, tsk, ytsk, dyk, codes, scw);
+        else nv_unit<true, false>(v[k], tk, sxk, tsk, ytsk, dyk, codes, scw);
+      } else {
+        if (ps) nv_unit<false, true>(v[k], tk, sxk, tsk, ytsk, dyk, codes, scw);
+        else nv_unit<false, false>(v[k], tk, sxk, tsk, ytsk, dyk, codes, scw);
+      }
     } else {
       const int e = mx_exponent(bf16_to_f32(absmax32_bits(v[k])));
       scw = (uint32_t)(e + 127);
@@ -1143,7 +1189,7 @@ __global__ void __launch_bounds__(TT) k_quant_tile(TileArgs p) {
             chan_range(p.chan + (int64_t)g * nS, nS, c0, c0 + 32 * WC, jl, jh, sl);
             n = (jh - jl) * R;
           }
-          if (FMT == FP4Q_NVFP4) tg = group_tscale(p, g);
+          if (FMT == FP4Q_NVFP4) tg = use_gt ? gts[g - gA].x : group_tscale(p, g);
         }
         const float sxg = div_prescale(tg);
         for (int i0 = 0; i0 < n; i0 += 64) {
@@ -1173,8 +1219,8 @@ __global__ void __launch_bounds__(TT) k_quant_tile(TileArgs p) {
             if (FMT == FP4Q_NVFP4) {
               const float sb = e4m3_value(sc);
               float d, y;
-              if (!GRP) {
-                const float2 dy = dytab[sc];
+              if (!GRP || use_gt) {
+                const float2 dy = GRP ? gdy[g - gA][sc] : dytab[sc];
                 d = dy.x;
                 y = dy.y;
               } else {
