@@ -52,7 +52,8 @@ def parse():
                    help="measure this workload only (default: the prefill NVFP4 line with the "
                         "other workloads as extra keys)")
     p.add_argument("--layout", choices=("tiled", "rowmajor"), default="tiled",
-                   help="packed operand layout of the dense workloads (MoE is row-major)")
+                   help="packed operand layout of the dense workloads, and of the experts' "
+                        "weights in the MoE workload (its routed activations are row-major)")
     p.add_argument("--out-dtype", choices=("f32", "bf16"), default="f32",
                    help="GEMM output type of the dense workloads")
     p.add_argument("--residual", choices=("bf16", "fp4"), default="bf16",
@@ -136,7 +137,7 @@ DOMINANT = {
     "prefill_nvfp4": ("k_gemm_nv4<true>", ["gemm_big.hip", "fp4q_device.h"], 1),
     "prefill_mxfp4": ("k_gemm_big<1, true, 0, false>", ["gemm_big.hip", "fp4q_device.h"], 1),
     "decode_nvfp4": ("k_gemm_skinny<0, true, true>", ["gemm_skinny.hip", "fp4q_device.h"], 1),
-    "moe_nvfp4": ("k_gemm_nv4g<false>", ["gemm_big.hip", "fp4q_device.h"], 2),
+    "moe_nvfp4": ("k_gemm_nv4g<false, true>", ["gemm_big.hip", "fp4q_device.h"], 2),
 }
 
 
@@ -493,8 +494,10 @@ def build_moe(name, cfg, data, args, dev):
     xg, xd = up(data["x_perm"]), up(data["h_perm"])
     cg, cd = up(data["chan_gate_up"]), up(data["chan_down"])
 
+    wl = fq.TILED if args.layout == "tiled" else fq.ROWMAJOR  # the experts' weights
+
     def qexperts(wt):
-        qs = [fq.quantize(fmt, up(wt[e])) for e in range(G)]
+        qs = [fq.quantize(fmt, up(wt[e]), layout=wl) for e in range(G)]
         return (torch.stack([q["q"] for q in qs]), torch.stack([q["scales"] for q in qs]),
                 torch.cat([q["tscale"] for q in qs]))
 
@@ -504,8 +507,8 @@ def build_moe(name, cfg, data, args, dev):
     # the packed weights
     prepared = args.comp_weights == "prepared" and nS > 0 and not r4 and not online
     if prepared:  # made once per expert weight set, like its quantization
-        wgu = wgu + (fq.grouped_comp_weights(fmt, wgu[0], wgu[1], cg),)
-        wdn = wdn + (fq.grouped_comp_weights(fmt, wdn[0], wdn[1], cd),)
+        wgu = wgu + (fq.grouped_comp_weights(fmt, wgu[0], wgu[1], cg, w_layout=wl, N=I2, K=H),)
+        wdn = wdn + (fq.grouped_comp_weights(fmt, wdn[0], wdn[1], cd, w_layout=wl, N=H, K=I),)
     torch.cuda.synchronize()
     bufs = {}
     for tag, (r, k) in {"gu": (rows, H), "dn": (rows, I)}.items():
@@ -563,11 +566,11 @@ def build_moe(name, cfg, data, args, dev):
                 fq.quantize_into(fmt, fq.ROWMAJOR, b["r"], off, G, None, 0, b["rq"], b["rs"],
                                  b["rt"], None, b["rws"])
 
-    gws_bytes = max(fq.grouped_gemm_workspace_bytes(fmt, rows, I2, H, G, nS),
-                    fq.grouped_gemm_workspace_bytes(fmt, rows, H, I, G, nS))
+    gws_bytes = max(fq.grouped_gemm_workspace_bytes(fmt, rows, I2, H, G, nS, wl),
+                    fq.grouped_gemm_workspace_bytes(fmt, rows, H, I, G, nS, wl))
     if r4:
-        gws_bytes = max(fq.grouped_gemm_residual_fp4_workspace_bytes(fmt, rows, I2, H, G, nS),
-                        fq.grouped_gemm_residual_fp4_workspace_bytes(fmt, rows, H, I, G, nS))
+        gws_bytes = max(fq.grouped_gemm_residual_fp4_workspace_bytes(fmt, rows, I2, H, G, nS, wl),
+                        fq.grouped_gemm_residual_fp4_workspace_bytes(fmt, rows, H, I, G, nS, wl))
     gws = torch.empty(gws_bytes, dtype=torch.uint8, device=dev) if gws_bytes else None
 
     def gemm(i):
@@ -578,17 +581,18 @@ def build_moe(name, cfg, data, args, dev):
             if r4:
                 fq.grouped_gemm_residual_fp4_into(fmt, rows, n, k, off, G, b["q"], b["s"], b["t"],
                                                   w[0], w[1], w[2], ch, nS, b["rq"], b["rs"],
-                                                  b["rt"], y, 0, gws)
+                                                  b["rt"], y, 0, gws, w_layout=wl)
             elif gather and tag == "gu":
                 fq.grouped_gemm_gather_into(fmt, rows, n, k, off, G, src, cfg["tokens"], tq, tsc,
                                             tts, w[0], w[1], w[2], ch, nS, b["r"],
-                                            w[3] if prepared else None, y, 0)
+                                            w[3] if prepared else None, y, 0, w_layout=wl)
             elif prepared:
                 fq.grouped_gemm_prepared_into(fmt, rows, n, k, off, G, b["q"], b["s"], b["t"],
-                                              w[0], w[1], w[2], ch, nS, b["r"], w[3], y, 0)
+                                              w[0], w[1], w[2], ch, nS, b["r"], w[3], y, 0,
+                                              w_layout=wl)
             else:
                 fq.grouped_gemm_into(fmt, rows, n, k, off, G, b["q"], b["s"], b["t"], w[0],
-                                     w[1], w[2], ch, nS, b["r"], y, 0, gws)
+                                     w[1], w[2], ch, nS, b["r"], y, 0, gws, w_layout=wl)
 
     loads = data["loads"]
     active = int((loads > 0).sum())
@@ -627,7 +631,7 @@ def build_moe(name, cfg, data, args, dev):
             "n_s_per_expert": nS, "max_expert_rows": int(loads.max()),
             "moe_quant": args.moe_quant, "residual": args.residual, "channels": args.channels,
             "comp_weights": "prepared" if prepared else "inkernel",
-            "empty_experts": int((loads == 0).sum())}
+            "weight_layout": args.layout, "empty_experts": int((loads == 0).sum())}
     s.keep = (wgu, wdn, bufs, ygu, ydn, gws, xg, xd, cg, cd, off)
     return s
 

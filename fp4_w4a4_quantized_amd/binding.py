@@ -91,12 +91,15 @@ def lib():
         L.fp4q_grouped_comp_weights_bytes.restype = sz
         L.fp4q_grouped_comp_weights_bytes.argtypes = [ctypes.c_int, i64, i64, i32, i32]
         L.fp4q_grouped_comp_weights.restype = ctypes.c_int
-        L.fp4q_grouped_comp_weights.argtypes = [ctypes.c_int, i64, i64, i32, P, P, P, i32, P, sz, P]
+        L.fp4q_grouped_comp_weights.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i32, P, P, P,
+                                                i32, P, sz, P]
         L.fp4q_grouped_gemm_prepared.restype = ctypes.c_int
-        L.fp4q_grouped_gemm_prepared.argtypes = [ctypes.c_int, i64, i64, i64, P, i32, P, P, P, P, P,
-                                                 P, P, i32, P, P, sz, P, ctypes.c_int, P]
+        L.fp4q_grouped_gemm_prepared.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, P, i32,
+                                                 P, P, P, P, P, P, P, i32, P, P, sz, P,
+                                                 ctypes.c_int, P]
         L.fp4q_grouped_gemm_workspace_bytes.restype = sz
-        L.fp4q_grouped_gemm_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i64, i32, i32]
+        L.fp4q_grouped_gemm_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64,
+                                                        i32, i32]
         L.fp4q_gemm_residual_fp4_workspace_bytes.restype = sz
         L.fp4q_gemm_residual_fp4_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64,
                                                              i64, i32]
@@ -105,15 +108,15 @@ def lib():
                                              P, P, P, i32, P, P, P, P, ctypes.c_int, i64, P, sz,
                                              P]
         L.fp4q_grouped_gemm_residual_fp4_workspace_bytes.restype = sz
-        L.fp4q_grouped_gemm_residual_fp4_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i64,
-                                                                     i32, i32]
+        L.fp4q_grouped_gemm_residual_fp4_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int,
+                                                                     i64, i64, i64, i32, i32]
         L.fp4q_grouped_gemm_residual_fp4.restype = ctypes.c_int
-        L.fp4q_grouped_gemm_residual_fp4.argtypes = [ctypes.c_int, i64, i64, i64, P, i32, P, P, P,
-                                                     P, P, P, P, i32, P, P, P, P, ctypes.c_int, P,
-                                                     sz, P]
+        L.fp4q_grouped_gemm_residual_fp4.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, P,
+                                                     i32, P, P, P, P, P, P, P, i32, P, P, P, P,
+                                                     ctypes.c_int, P, sz, P]
         L.fp4q_grouped_gemm.restype = ctypes.c_int
-        L.fp4q_grouped_gemm.argtypes = [ctypes.c_int, i64, i64, i64, P, i32, P, P, P, P, P, P, P,
-                                        i32, P, P, ctypes.c_int, P, sz, P]
+        L.fp4q_grouped_gemm.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, P, i32, P, P, P,
+                                        P, P, P, P, i32, P, P, ctypes.c_int, P, sz, P]
         L.fp4q_select_channels_workspace_bytes.restype = sz
         L.fp4q_select_channels_workspace_bytes.argtypes = [i64, i64]
         L.fp4q_select_channels.restype = ctypes.c_int
@@ -137,8 +140,9 @@ def lib():
         L.fp4q_qdq_fallback.restype = ctypes.c_int
         L.fp4q_qdq_fallback.argtypes = [ctypes.c_int, P, i64, i64, i64, P, i64, P, P, sz, P]
         L.fp4q_grouped_gemm_gather.restype = ctypes.c_int
-        L.fp4q_grouped_gemm_gather.argtypes = [ctypes.c_int, i64, i64, i64, P, i32, P, i64, P, P,
-                                               P, P, P, P, P, i32, P, P, sz, P, ctypes.c_int, P]
+        L.fp4q_grouped_gemm_gather.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, P, i32, P,
+                                               i64, P, P, P, P, P, P, P, i32, P, P, sz, P,
+                                               ctypes.c_int, P]
         L.fp4q_gemm_decode_fused.restype = ctypes.c_int
         L.fp4q_gemm_decode_fused.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, P, i64,
                                              P, P, P, P, i32, P, sz, P, ctypes.c_int, i64, P, P,
@@ -216,24 +220,30 @@ def grouped_comp_weights_bytes(fmt, N, K, num_groups, n_chan) -> int:
     return lib().fp4q_grouped_comp_weights_bytes(fmt, N, K, num_groups, n_chan)
 
 
-def grouped_comp_weights(fmt, bq, bs, chan_idx, stream=None):
+def grouped_comp_weights(fmt, bq, bs, chan_idx, stream=None, w_layout=ROWMAJOR, N=None, K=None):
     """Every group's compensation weights: bq [G, N, K/2], bs [G, N, K/blk]
-    (row-major), chan_idx [G, n_chan]; a uint8 tensor in the grouped layout."""
-    G, N, K2 = bq.shape
+    (row-major), or each group's tiled bytes [G, ...] with w_layout=TILED
+    and N, K given; chan_idx [G, n_chan]; a uint8 tensor in the grouped
+    layout."""
+    G = bq.shape[0]
+    if w_layout == ROWMAJOR:
+        N, K = bq.shape[1], 2 * bq.shape[2]
     nS = chan_idx.numel() // G
-    nb = grouped_comp_weights_bytes(fmt, N, 2 * K2, G, nS)
+    nb = grouped_comp_weights_bytes(fmt, N, K, G, nS)
     out = torch.empty(max(nb, 16), dtype=torch.uint8, device=bq.device)
-    rc = lib().fp4q_grouped_comp_weights(fmt, N, 2 * K2, G, _ptr(bq), _ptr(bs), _ptr(chan_idx), nS,
-                                         _ptr(out), out.numel(), _stream(stream))
+    rc = lib().fp4q_grouped_comp_weights(fmt, w_layout, N, K, G, _ptr(bq), _ptr(bs),
+                                         _ptr(chan_idx), nS, _ptr(out), out.numel(),
+                                         _stream(stream))
     _check("fp4q_grouped_comp_weights", rc)
     return out
 
 
 def grouped_gemm_prepared_into(fmt, total_rows, N, K, group_offsets, num_groups, a_q, a_s, a_ts,
                                b_q, b_s, b_ts, chan_idx, n_chan, resid, comp_w, y,
-                               y_dtype=OUT_F32, stream=None):
+                               y_dtype=OUT_F32, stream=None, w_layout=ROWMAJOR):
     nb = 0 if comp_w is None else comp_w.numel() * comp_w.element_size()
-    rc = lib().fp4q_grouped_gemm_prepared(fmt, total_rows, N, K, _ptr(group_offsets), num_groups,
+    rc = lib().fp4q_grouped_gemm_prepared(fmt, w_layout, total_rows, N, K, _ptr(group_offsets),
+                                          num_groups,
                                           _ptr(a_q), _ptr(a_s), _ptr(a_ts), _ptr(b_q), _ptr(b_s),
                                           _ptr(b_ts), _ptr(chan_idx), n_chan, _ptr(resid),
                                           _ptr(comp_w), nb, _ptr(y), y_dtype, _stream(stream))
@@ -244,13 +254,16 @@ def gemm_residual_fp4_workspace_bytes(fmt, layout, M, N, K, n_chan) -> int:
     return lib().fp4q_gemm_residual_fp4_workspace_bytes(fmt, layout, M, N, K, n_chan)
 
 
-def grouped_gemm_residual_fp4_workspace_bytes(fmt, total_rows, N, K, num_groups, n_chan) -> int:
-    return lib().fp4q_grouped_gemm_residual_fp4_workspace_bytes(fmt, total_rows, N, K, num_groups,
-                                                                n_chan)
+def grouped_gemm_residual_fp4_workspace_bytes(fmt, total_rows, N, K, num_groups, n_chan,
+                                              w_layout=ROWMAJOR) -> int:
+    return lib().fp4q_grouped_gemm_residual_fp4_workspace_bytes(fmt, w_layout, total_rows, N, K,
+                                                                num_groups, n_chan)
 
 
-def grouped_gemm_workspace_bytes(fmt, total_rows, N, K, num_groups, n_chan) -> int:
-    return lib().fp4q_grouped_gemm_workspace_bytes(fmt, total_rows, N, K, num_groups, n_chan)
+def grouped_gemm_workspace_bytes(fmt, total_rows, N, K, num_groups, n_chan,
+                                 w_layout=ROWMAJOR) -> int:
+    return lib().fp4q_grouped_gemm_workspace_bytes(fmt, w_layout, total_rows, N, K, num_groups,
+                                                   n_chan)
 
 
 def select_channels_workspace_bytes(rows, cols) -> int:
@@ -295,9 +308,10 @@ def gemm_residual_fp4_into(fmt, layout, M, N, K, a_q, a_s, a_ts, b_q, b_s, b_ts,
 
 def grouped_gemm_residual_fp4_into(fmt, total_rows, N, K, group_offsets, num_groups, a_q, a_s,
                                    a_ts, b_q, b_s, b_ts, chan_idx, n_chan, r_q, r_s, r_ts, y,
-                                   y_dtype=OUT_F32, workspace=None, stream=None):
+                                   y_dtype=OUT_F32, workspace=None, stream=None,
+                                   w_layout=ROWMAJOR):
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = lib().fp4q_grouped_gemm_residual_fp4(fmt, total_rows, N, K, _ptr(group_offsets),
+    rc = lib().fp4q_grouped_gemm_residual_fp4(fmt, w_layout, total_rows, N, K, _ptr(group_offsets),
                                               num_groups, _ptr(a_q), _ptr(a_s), _ptr(a_ts),
                                               _ptr(b_q), _ptr(b_s), _ptr(b_ts), _ptr(chan_idx),
                                               n_chan, _ptr(r_q), _ptr(r_s), _ptr(r_ts), _ptr(y),
@@ -307,9 +321,9 @@ def grouped_gemm_residual_fp4_into(fmt, total_rows, N, K, group_offsets, num_gro
 
 def grouped_gemm_into(fmt, total_rows, N, K, group_offsets, num_groups, a_q, a_s, a_ts, b_q,
                       b_s, b_ts, chan_idx, n_chan, resid, y, y_dtype=OUT_F32, workspace=None,
-                      stream=None):
+                      stream=None, w_layout=ROWMAJOR):
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = lib().fp4q_grouped_gemm(fmt, total_rows, N, K, _ptr(group_offsets), num_groups,
+    rc = lib().fp4q_grouped_gemm(fmt, w_layout, total_rows, N, K, _ptr(group_offsets), num_groups,
                                  _ptr(a_q), _ptr(a_s), _ptr(a_ts), _ptr(b_q), _ptr(b_s),
                                  _ptr(b_ts), _ptr(chan_idx), n_chan, _ptr(resid), _ptr(y),
                                  y_dtype, _ptr(workspace), ws_bytes, _stream(stream))
@@ -397,12 +411,13 @@ def qdq_fallback(fmt, x, stream=None):
 
 def grouped_gemm_gather_into(fmt, total_rows, N, K, group_offsets, num_groups, row_src, tokens,
                              a_q, a_s, a_ts, b_q, b_s, b_ts, chan_idx, n_chan, resid, comp_w, y,
-                             y_dtype, stream=None):
+                             y_dtype, stream=None, w_layout=ROWMAJOR):
     """fp4q_grouped_gemm_gather: the grouped GEMM reading each routed row's
     codes from the token matrix (row_src)."""
     cw_bytes = 0 if comp_w is None else comp_w.numel() * comp_w.element_size()
     _check("fp4q_grouped_gemm_gather",
-           lib().fp4q_grouped_gemm_gather(fmt, total_rows, N, K, _ptr(group_offsets), num_groups,
+           lib().fp4q_grouped_gemm_gather(fmt, w_layout, total_rows, N, K, _ptr(group_offsets),
+                                          num_groups,
                                           _ptr(row_src), tokens, _ptr(a_q), _ptr(a_s),
                                           _ptr(a_ts), _ptr(b_q), _ptr(b_s), _ptr(b_ts),
                                           _ptr(chan_idx), n_chan, _ptr(resid), _ptr(comp_w),
@@ -553,21 +568,22 @@ def gemm_residual_fp4(fmt, a, b, chan_idx, r, y_dtype=OUT_F32, stream=None):
 
 
 def grouped_gemm_residual_fp4(fmt, group_offsets, a, bq, bs, bts, chan_idx, r, y_dtype=OUT_F32,
-                              stream=None):
+                              stream=None, w_layout=ROWMAJOR, N=None):
     """grouped_gemm() with the second-pass residual: r = quantize(fmt,
     a["resid"], group_offsets) (row-major, one tensor scale per group)."""
     total, K = a["q"].shape[0], a["q"].shape[1] * 2
     G = group_offsets.numel() - 1
-    N = bq.shape[1]
+    if w_layout == ROWMAJOR:
+        N = bq.shape[1]
     nS = chan_idx.numel() // G
     dev = a["q"].device
     y = torch.empty((total, N), dtype=torch.float32 if y_dtype == OUT_F32 else torch.bfloat16,
                     device=dev)
-    wsb = grouped_gemm_residual_fp4_workspace_bytes(fmt, total, N, K, G, nS)
+    wsb = grouped_gemm_residual_fp4_workspace_bytes(fmt, total, N, K, G, nS, w_layout)
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
     grouped_gemm_residual_fp4_into(fmt, total, N, K, group_offsets, G, a["q"], a["scales"],
                                    a["tscale"], bq, bs, bts, chan_idx, nS, r["q"], r["scales"],
-                                   r["tscale"], y, y_dtype, ws, stream)
+                                   r["tscale"], y, y_dtype, ws, stream, w_layout)
     return y
 
 
@@ -665,34 +681,38 @@ def permute_quantized(fmt, x, a, row_src, group_offsets, chan_idx=None, stream=N
 
 
 def grouped_gemm(fmt, group_offsets, a, bq, bs, bts, chan_idx=None, y_dtype=OUT_F32,
-                 stream=None):
-    """a: grouped quantize() result; bq [G, N, K/2], bs [G, N, K/blk], bts [G]."""
+                 stream=None, w_layout=ROWMAJOR, N=None):
+    """a: grouped quantize() result; bq [G, N, K/2], bs [G, N, K/blk], bts [G]
+    (w_layout=TILED: each group's tiled bytes [G, ...], N given)."""
     total, K = a["q"].shape[0], a["q"].shape[1] * 2
     G = group_offsets.numel() - 1
-    N = bq.shape[1]
+    if w_layout == ROWMAJOR:
+        N = bq.shape[1]
     nS = 0 if chan_idx is None else chan_idx.numel() // G
     dev = a["q"].device
     y = torch.empty((total, N), dtype=torch.float32 if y_dtype == OUT_F32 else torch.bfloat16,
                     device=dev)
-    wsb = grouped_gemm_workspace_bytes(fmt, total, N, K, G, nS)
+    wsb = grouped_gemm_workspace_bytes(fmt, total, N, K, G, nS, w_layout)
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
     grouped_gemm_into(fmt, total, N, K, group_offsets, G, a["q"], a["scales"], a["tscale"], bq,
-                      bs, bts, chan_idx, nS, a["resid"] if nS else None, y, y_dtype, ws, stream)
+                      bs, bts, chan_idx, nS, a["resid"] if nS else None, y, y_dtype, ws, stream,
+                      w_layout)
     return y
 
 
 def grouped_gemm_prepared(fmt, group_offsets, a, bq, bs, bts, chan_idx, comp_w, y_dtype=OUT_F32,
-                          stream=None):
+                          stream=None, w_layout=ROWMAJOR, N=None):
     """grouped_gemm() with comp_w = grouped_comp_weights(fmt, bq, bs, chan_idx)."""
     total, K = a["q"].shape[0], a["q"].shape[1] * 2
     G = group_offsets.numel() - 1
-    N = bq.shape[1]
+    if w_layout == ROWMAJOR:
+        N = bq.shape[1]
     nS = chan_idx.numel() // G
     y = torch.empty((total, N), dtype=torch.float32 if y_dtype == OUT_F32 else torch.bfloat16,
                     device=a["q"].device)
     grouped_gemm_prepared_into(fmt, total, N, K, group_offsets, G, a["q"], a["scales"],
                                a["tscale"], bq, bs, bts, chan_idx, nS, a["resid"], comp_w, y,
-                               y_dtype, stream)
+                               y_dtype, stream, w_layout)
     return y
 
 

@@ -238,6 +238,19 @@ static int validate_gemm_common(int fmt, int64_t N, int64_t K, const uint8_t* a_
   return FP4Q_OK;
 }
 
+// The experts' weight layout of a grouped GEMM: row-major everywhere; tiled
+// where the 128 x 512 NVFP4 grouped kernel serves the shape (its tokens'
+// codes below 4 GiB when gathered).
+static int validate_w_layout(int fmt, int w_layout, int64_t N, int64_t K, int32_t n_chan,
+                             int64_t gather_bytes = 0) {
+  if (!layout_ok(w_layout)) return FP4Q_ERR_INVALID;
+  if (w_layout != FP4Q_LAYOUT_TILED) return FP4Q_OK;
+  if (K % 128 != 0) return FP4Q_ERR_INVALID;
+  if (!fp4q::grouped_tiled_ok(fmt, N, K, n_chan) || gather_bytes > (int64_t)UINT32_MAX)
+    return FP4Q_ERR_UNSUPPORTED;
+  return FP4Q_OK;
+}
+
 size_t fp4q_gemm_workspace_bytes(fp4q_format_t fmt, fp4q_layout_t layout, int64_t M, int64_t N,
                                  int64_t K, int32_t n_chan) {
   (void)fmt;
@@ -412,15 +425,17 @@ int fp4q_gemm_residual_fp4(fp4q_format_t fmt, fp4q_layout_t layout, int64_t M, i
   return check_launch();
 }
 
-size_t fp4q_grouped_gemm_workspace_bytes(fp4q_format_t fmt, int64_t total_rows, int64_t N,
-                                         int64_t K, int32_t num_groups, int32_t n_chan) {
+size_t fp4q_grouped_gemm_workspace_bytes(fp4q_format_t fmt, fp4q_layout_t w_layout,
+                                         int64_t total_rows, int64_t N, int64_t K,
+                                         int32_t num_groups, int32_t n_chan) {
   (void)fmt;
   if (total_rows <= 0 || N <= 0 || K <= 0 || n_chan <= 0 || num_groups < 1) return 0;
-  return fp4q::grouped_workspace_bytes(N, K, num_groups, n_chan);
+  return fp4q::grouped_workspace_bytes(N, K, num_groups, n_chan, w_layout == FP4Q_LAYOUT_TILED);
 }
 
-int fp4q_grouped_gemm(fp4q_format_t fmt, int64_t total_rows, int64_t N, int64_t K,
-                      const int32_t* group_offsets, int32_t num_groups, const uint8_t* a_q,
+int fp4q_grouped_gemm(fp4q_format_t fmt, fp4q_layout_t w_layout, int64_t total_rows, int64_t N,
+                      int64_t K, const int32_t* group_offsets, int32_t num_groups,
+                      const uint8_t* a_q,
                       const uint8_t* a_s, const float* a_ts, const uint8_t* b_q,
                       const uint8_t* b_s, const float* b_ts, const int32_t* chan_idx,
                       int32_t n_chan, const uint16_t* resid, void* y, fp4q_dtype_t y_dtype,
@@ -428,30 +443,34 @@ int fp4q_grouped_gemm(fp4q_format_t fmt, int64_t total_rows, int64_t N, int64_t 
   int rc = validate_gemm_common(fmt, N, K, a_q, a_s, a_ts, b_q, b_s, b_ts, chan_idx, n_chan,
                                 resid, y, y_dtype, total_rows);
   if (rc != FP4Q_OK) return rc;
+  if ((rc = validate_w_layout(fmt, w_layout, N, K, n_chan)) != FP4Q_OK) return rc;
   if (num_groups < 1 || !group_offsets) return FP4Q_ERR_INVALID;
   if (num_groups > MAX_GROUPS) return FP4Q_ERR_UNSUPPORTED;
   if ((N + 127) / 128 > 65535) return FP4Q_ERR_UNSUPPORTED;
   const size_t need =
-      fp4q_grouped_gemm_workspace_bytes(fmt, total_rows, N, K, num_groups, n_chan);
+      fp4q_grouped_gemm_workspace_bytes(fmt, w_layout, total_rows, N, K, num_groups, n_chan);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
     return FP4Q_ERR_WORKSPACE;
   if (injected_failure()) return FP4Q_ERR_HIP;
   clear_error();
-  fp4q::launch_gemm(fmt, false, total_rows, N, K, group_offsets, num_groups, a_q, a_s, a_ts, b_q,
+  fp4q::launch_gemm(fmt, w_layout == FP4Q_LAYOUT_TILED, total_rows, N, K, group_offsets,
+                    num_groups, a_q, a_s, a_ts, b_q,
                     b_s, b_ts, chan_idx, n_chan, resid, nullptr, y, y_dtype == FP4Q_OUT_BF16, N,
                     workspace, static_cast<hipStream_t>(stream));
   return check_launch();
 }
 
-size_t fp4q_grouped_gemm_residual_fp4_workspace_bytes(fp4q_format_t fmt, int64_t total_rows,
-                                                      int64_t N, int64_t K, int32_t num_groups,
-                                                      int32_t n_chan) {
+size_t fp4q_grouped_gemm_residual_fp4_workspace_bytes(fp4q_format_t fmt,
+                                                      fp4q_layout_t w_layout,
+                                                      int64_t total_rows, int64_t N, int64_t K,
+                                                      int32_t num_groups, int32_t n_chan) {
   if (total_rows <= 0 || N <= 0 || K <= 0 || n_chan <= 0 || num_groups < 1) return 0;
   return deq_resid_bytes(total_rows, n_chan) +
-         fp4q_grouped_gemm_workspace_bytes(fmt, total_rows, N, K, num_groups, n_chan);
+         fp4q_grouped_gemm_workspace_bytes(fmt, w_layout, total_rows, N, K, num_groups, n_chan);
 }
 
-int fp4q_grouped_gemm_residual_fp4(fp4q_format_t fmt, int64_t total_rows, int64_t N, int64_t K,
+int fp4q_grouped_gemm_residual_fp4(fp4q_format_t fmt, fp4q_layout_t w_layout,
+                                   int64_t total_rows, int64_t N, int64_t K,
                                    const int32_t* group_offsets, int32_t num_groups,
                                    const uint8_t* a_q, const uint8_t* a_s, const float* a_ts,
                                    const uint8_t* b_q, const uint8_t* b_s, const float* b_ts,
@@ -469,7 +488,7 @@ int fp4q_grouped_gemm_residual_fp4(fp4q_format_t fmt, int64_t total_rows, int64_
   if (num_groups > MAX_GROUPS) return FP4Q_ERR_UNSUPPORTED;
   const bool work = total_rows > 0 && N > 0 && n_chan > 0;
   const size_t need = work ? fp4q_grouped_gemm_residual_fp4_workspace_bytes(
-                                 fmt, total_rows, N, K, num_groups, n_chan)
+                                 fmt, w_layout, total_rows, N, K, num_groups, n_chan)
                            : 0;
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
     return FP4Q_ERR_WORKSPACE;
@@ -482,6 +501,7 @@ int fp4q_grouped_gemm_residual_fp4(fp4q_format_t fmt, int64_t total_rows, int64_
   int rc = validate_gemm_common(fmt, N, K, a_q, a_s, a_ts, b_q, b_s, b_ts, chan_idx, n_chan,
                                 rval, y, y_dtype, total_rows);
   if (rc != FP4Q_OK) return rc;
+  if ((rc = validate_w_layout(fmt, w_layout, N, K, n_chan)) != FP4Q_OK) return rc;
   if ((N + 127) / 128 > 65535) return FP4Q_ERR_UNSUPPORTED;
   if (total_rows * (int64_t)n_chan / 8 >= ((int64_t)1 << 31)) return FP4Q_ERR_UNSUPPORTED;
   if (total_rows == 0 || N == 0) return FP4Q_OK;
@@ -491,7 +511,8 @@ int fp4q_grouped_gemm_residual_fp4(fp4q_format_t fmt, int64_t total_rows, int64_
                    : nullptr;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (work) fp4q::launch_deq_resid(fmt, total_rows, n_chan, r_q, r_s, rdeq, st);
-  fp4q::launch_gemm(fmt, false, total_rows, N, K, group_offsets, num_groups, a_q, a_s, a_ts, b_q,
+  fp4q::launch_gemm(fmt, w_layout == FP4Q_LAYOUT_TILED, total_rows, N, K, group_offsets,
+                    num_groups, a_q, a_s, a_ts, b_q,
                     b_s, b_ts, chan_idx, n_chan, rval, r_ts, y, y_dtype == FP4Q_OUT_BF16, N, gws,
                     st);
   return check_launch();
@@ -505,10 +526,11 @@ size_t fp4q_grouped_comp_weights_bytes(fp4q_format_t fmt, int64_t N, int64_t K,
   return (size_t)num_groups * fp4q::comp_weights_bytes(N, n_chan);
 }
 
-int fp4q_grouped_comp_weights(fp4q_format_t fmt, int64_t N, int64_t K, int32_t num_groups,
-                              const uint8_t* b_q, const uint8_t* b_s, const int32_t* chan_idx,
-                              int32_t n_chan, uint8_t* out, size_t out_bytes, void* stream) {
-  if (!fmt_ok(fmt)) return FP4Q_ERR_INVALID;
+int fp4q_grouped_comp_weights(fp4q_format_t fmt, fp4q_layout_t w_layout, int64_t N, int64_t K,
+                              int32_t num_groups, const uint8_t* b_q, const uint8_t* b_s,
+                              const int32_t* chan_idx, int32_t n_chan, uint8_t* out,
+                              size_t out_bytes, void* stream) {
+  if (!fmt_ok(fmt) || !layout_ok(w_layout)) return FP4Q_ERR_INVALID;
   if (N < 0 || K < 0 || n_chan < 0 || num_groups < 1) return FP4Q_ERR_INVALID;
   if (num_groups > MAX_GROUPS) return FP4Q_ERR_UNSUPPORTED;
   if ((n_chan > 0) != (chan_idx != nullptr)) return FP4Q_ERR_INVALID;
@@ -521,13 +543,14 @@ int fp4q_grouped_comp_weights(fp4q_format_t fmt, int64_t N, int64_t K, int32_t n
     return FP4Q_ERR_UNSUPPORTED;
   if (injected_failure()) return FP4Q_ERR_HIP;
   clear_error();
-  fp4q::launch_comp_weights(fmt, false, b_q, b_s, N, K, chan_idx, n_chan, num_groups, out,
-                            static_cast<hipStream_t>(stream));
+  fp4q::launch_comp_weights(fmt, w_layout == FP4Q_LAYOUT_TILED, b_q, b_s, N, K, chan_idx,
+                            n_chan, num_groups, out, static_cast<hipStream_t>(stream));
   return check_launch();
 }
 
-int fp4q_grouped_gemm_prepared(fp4q_format_t fmt, int64_t total_rows, int64_t N, int64_t K,
-                               const int32_t* group_offsets, int32_t num_groups,
+int fp4q_grouped_gemm_prepared(fp4q_format_t fmt, fp4q_layout_t w_layout, int64_t total_rows,
+                               int64_t N, int64_t K, const int32_t* group_offsets,
+                               int32_t num_groups,
                                const uint8_t* a_q, const uint8_t* a_s, const float* a_ts,
                                const uint8_t* b_q, const uint8_t* b_s, const float* b_ts,
                                const int32_t* chan_idx, int32_t n_chan, const uint16_t* resid,
@@ -536,6 +559,7 @@ int fp4q_grouped_gemm_prepared(fp4q_format_t fmt, int64_t total_rows, int64_t N,
   int rc = validate_gemm_common(fmt, N, K, a_q, a_s, a_ts, b_q, b_s, b_ts, chan_idx, n_chan,
                                 resid, y, y_dtype, total_rows);
   if (rc != FP4Q_OK) return rc;
+  if ((rc = validate_w_layout(fmt, w_layout, N, K, n_chan)) != FP4Q_OK) return rc;
   if (num_groups < 1 || !group_offsets) return FP4Q_ERR_INVALID;
   if (num_groups > MAX_GROUPS) return FP4Q_ERR_UNSUPPORTED;
   if ((N + 127) / 128 > 65535) return FP4Q_ERR_UNSUPPORTED;
@@ -547,14 +571,16 @@ int fp4q_grouped_gemm_prepared(fp4q_format_t fmt, int64_t total_rows, int64_t N,
   if (!fp4q::big_grouped_eligible(N, K, n_chan)) comp_w = nullptr;
   if (injected_failure()) return FP4Q_ERR_HIP;
   clear_error();
-  fp4q::launch_gemm(fmt, false, total_rows, N, K, group_offsets, num_groups, a_q, a_s, a_ts, b_q,
-                    b_s, b_ts, chan_idx, n_chan, resid, nullptr, y, y_dtype == FP4Q_OUT_BF16, N,
-                    nullptr, static_cast<hipStream_t>(stream), work ? comp_w : nullptr);
+  fp4q::launch_gemm(fmt, w_layout == FP4Q_LAYOUT_TILED, total_rows, N, K, group_offsets,
+                    num_groups, a_q, a_s, a_ts, b_q, b_s, b_ts, chan_idx, n_chan, resid, nullptr,
+                    y, y_dtype == FP4Q_OUT_BF16, N, nullptr, static_cast<hipStream_t>(stream),
+                    work ? comp_w : nullptr);
   return check_launch();
 }
 
-int fp4q_grouped_gemm_gather(fp4q_format_t fmt, int64_t total_rows, int64_t N, int64_t K,
-                             const int32_t* group_offsets, int32_t num_groups,
+int fp4q_grouped_gemm_gather(fp4q_format_t fmt, fp4q_layout_t w_layout, int64_t total_rows,
+                             int64_t N, int64_t K, const int32_t* group_offsets,
+                             int32_t num_groups,
                              const int32_t* row_src, int64_t tokens, const uint8_t* a_q,
                              const uint8_t* a_s, const float* a_ts, const uint8_t* b_q,
                              const uint8_t* b_s, const float* b_ts, const int32_t* chan_idx,
@@ -565,6 +591,8 @@ int fp4q_grouped_gemm_gather(fp4q_format_t fmt, int64_t total_rows, int64_t N, i
   if (rc != FP4Q_OK) return rc;
   if (num_groups < 1 || !group_offsets) return FP4Q_ERR_INVALID;
   if (tokens < 0 || (total_rows > 0 && (tokens == 0 || !row_src))) return FP4Q_ERR_INVALID;
+  if ((rc = validate_w_layout(fmt, w_layout, N, K, n_chan, tokens * (K / 2))) != FP4Q_OK)
+    return rc;
   if (num_groups > MAX_GROUPS) return FP4Q_ERR_UNSUPPORTED;
   if ((N + 127) / 128 > 65535 || !fp4q::big_grouped_eligible(N, K, n_chan))
     return FP4Q_ERR_UNSUPPORTED;
@@ -579,7 +607,8 @@ int fp4q_grouped_gemm_gather(fp4q_format_t fmt, int64_t total_rows, int64_t N, i
   fp4q::launch_gemm_big_grouped(fmt, total_rows, N, K, group_offsets, num_groups, a_q, a_s, a_ts,
                                 b_q, b_s, b_ts, chan_idx, n_chan, resid, nullptr,
                                 n_chan > 0 ? comp_w : nullptr, y, y_dtype == FP4Q_OUT_BF16, nullptr,
-                                static_cast<hipStream_t>(stream), row_src, tokens);
+                                static_cast<hipStream_t>(stream), w_layout == FP4Q_LAYOUT_TILED,
+                                row_src, tokens);
   return check_launch();
 }
 

@@ -64,13 +64,17 @@ void launch_deq_resid(int fmt, int64_t M, int nS, const uint8_t* rq, const uint8
 bool big_gemm_eligible(int64_t M, int64_t N, int64_t K, int nS);
 bool big_grouped_eligible(int64_t N, int64_t K, int nS);
 size_t big_gemm_workspace_bytes(int64_t N, int nS);
-size_t grouped_workspace_bytes(int64_t N, int64_t K, int G, int nS);
+// wtiled: every expert's weights in the tiled layout (NVFP4 only, served by
+// the 128 x 512 grouped kernel; the compensation weights then always come
+// from the workspace or the prepared array, never from in-kernel extraction)
+size_t grouped_workspace_bytes(int64_t N, int64_t K, int G, int nS, bool wtiled);
+bool grouped_tiled_ok(int fmt, int64_t N, int64_t K, int nS);
 int launch_gemm_big_grouped(int fmt, int64_t total_rows, int64_t N, int64_t K,
                             const int32_t* off, int G, const uint8_t* aq, const uint8_t* as,
                             const float* ats, const uint8_t* bq, const uint8_t* bs,
                             const float* bts, const int32_t* chan, int nS,
                             const uint16_t* resid, const float* cts, const uint8_t* bsel_pre,
-                            void* y, int y_bf16, void* ws, hipStream_t stream,
+                            void* y, int y_bf16, void* ws, hipStream_t stream, bool wtiled,
                             const int32_t* row_src = nullptr, int64_t src_rows = 0);
 int launch_gemm_big(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const uint8_t* aq,
                     const uint8_t* as, const float* ats, const uint8_t* bq, const uint8_t* bs,

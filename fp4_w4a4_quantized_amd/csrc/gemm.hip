@@ -390,8 +390,14 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int nS) {
   return gemm_path(M, N, K, nS) == PATH_BIG ? big_gemm_workspace_bytes(N, nS) : 0;
 }
 
-size_t grouped_workspace_bytes(int64_t N, int64_t K, int G, int nS) {
-  return big_grouped_eligible(N, K, nS) ? (size_t)G * big_gemm_workspace_bytes(N, nS) : 0;
+size_t grouped_workspace_bytes(int64_t N, int64_t K, int G, int nS, bool wtiled) {
+  if (!big_grouped_eligible(N, K, nS)) return 0;
+  // tiled weights: B_S is always gathered (no in-kernel extraction)
+  return (size_t)G * (wtiled ? comp_weights_bytes(N, nS) : big_gemm_workspace_bytes(N, nS));
+}
+
+bool grouped_tiled_ok(int fmt, int64_t N, int64_t K, int nS) {
+  return fmt == FP4Q_NVFP4 && big_grouped_eligible(N, K, nS);
 }
 
 // Second-pass residual decode: thread i takes elements 8i .. 8i+7 of the
@@ -446,7 +452,7 @@ int launch_gemm(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const int3
   if (M == 0 || N == 0) return 0;
   if (off != nullptr && big_grouped_eligible(N, K, nS)) {
     launch_gemm_big_grouped(fmt, M, N, K, off, G, aq, as, ats, bq, bs, bts, chan, nS, resid,
-                            cts, bsel_pre, y, y_bf16, ws, stream);
+                            cts, bsel_pre, y, y_bf16, ws, stream, tiled);
     return 0;
   }
   if (off != nullptr) {

@@ -984,9 +984,13 @@ __global__ void __launch_bounds__(256, 1) k_gemm_nv4(BigArgs args) {
 // experts layer are small and uneven, so rows are tiled by 128, not 256
 // (fewer MFMAs on padding rows), and the four waves sit side by side along
 // N, each owning 128 x 128 exactly as in k_gemm_nv4 (same decode work per
-// MFMA).  Grouped operands are row-major: every direct-to-LDS load takes a
-// wave-uniform base (tile origin and K step, in SGPRs) plus a 32-bit lane
-// offset fixed for the whole tile, so the row addressing holds few VGPRs.
+// MFMA).  The expert-ordered activations are row-major: every direct-to-LDS
+// load takes a wave-uniform base (tile origin and K step, in SGPRs) plus a
+// 32-bit lane offset fixed for the whole tile, so the row addressing holds
+// few VGPRs.  The experts' weights are row-major, or (TW) each expert's in
+// the tiled layout, where a stage's 16 columns are one contiguous 1 KB block
+// and 64 columns' scales one 512-byte block; both layouts put the same bytes
+// in LDS.
 // Tiles run group by group, row tile by row tile, the N tiles of one row
 // tile together, and each XCD (block b runs on XCD b % 8) takes one
 // contiguous run of that order: the weight panels of a group and the code
@@ -1008,7 +1012,9 @@ struct G4Layout {
 // into the same places, and placeholders keep the count.  GA (rows of A
 // gathered by row_src): the lane's A code offsets gao[i] (group 2w + i) and
 // scale offsets gso[c] (chunk c) from the token matrix's base, fixed per tile.
-template <bool GA>
+// TW: the expert's weights in the tiled layout (blocks clamped to the last
+// padded 16- or 64-column group, as the dense tiled path does).
+template <bool GA, bool TW>
 __device__ __forceinline__ void g4_issue(const BigArgs& p, int s, int wave, int lane,
                                          const TileCtx& tc, uint8_t* st, const uint32_t (&gao)[2],
                                          const uint32_t (&gso)[2]) {
@@ -1050,12 +1056,20 @@ __device__ __forceinline__ void g4_issue(const BigArgs& p, int s, int wave, int 
     r = r < rlast ? r : rlast;
     lds_load16s(ab, GA ? gao[i] : (uint32_t)(r * K2 + (lane >> 4) * 16), st + GL::A + g * GB_GRP);
   }
+  const int64_t KB = p.K >> 7;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int g = 8 * wave + i;
-    int r = 16 * g + (lane & 15);
-    r = r < clast ? r : clast;
-    lds_load16s(bb, (uint32_t)(r * K2 + (lane >> 4) * 16), st + GL::B + g * GB_GRP);
+    if (TW) {
+      const int64_t gN = ((p.N + 15) >> 4) - 1;
+      int64_t gb = (c0 >> 4) + g;
+      gb = gb < gN ? gb : gN;
+      lds_load16s(tc.bq + ((gb * KB + kt) << 10), lane * 16, st + GL::B + g * GB_GRP);
+    } else {
+      int r = 16 * g + (lane & 15);
+      r = r < clast ? r : clast;
+      lds_load16s(bb, (uint32_t)(r * K2 + (lane >> 4) * 16), st + GL::B + g * GB_GRP);
+    }
   }
 #pragma unroll
   for (int i = 0; i < 5; ++i) {
@@ -1068,10 +1082,18 @@ __device__ __forceinline__ void g4_issue(const BigArgs& p, int s, int wave, int 
                  st + GL::SA + (d * G4_TM + 64 * c) * 4);
     } else {
       const int m = n - 4, d = m >> 3, c = m & 7;
-      int r = 64 * c + lane;
-      r = r < clast ? r : clast;
-      lds_load4s(tc.bs + c0 * KS + kt * 8 + 4 * d, (uint32_t)(r * KS),
-                 st + GL::SB + (d * G4_TN + 64 * c) * 4);
+      if (TW) {
+        const int64_t hN = ((p.N + 63) >> 6) - 1;
+        int64_t h = (c0 >> 6) + c;
+        h = h < hN ? h : hN;
+        lds_load4s(tc.bs + (h * KB + kt) * 512 + d * 256, lane * 4,
+                   st + GL::SB + (d * G4_TN + 64 * c) * 4);
+      } else {
+        int r = 64 * c + lane;
+        r = r < clast ? r : clast;
+        lds_load4s(tc.bs + c0 * KS + kt * 8 + 4 * d, (uint32_t)(r * KS),
+                   st + GL::SB + (d * G4_TN + 64 * c) * 4);
+      }
     }
   }
 }
@@ -1099,7 +1121,7 @@ __device__ __forceinline__ void g4_read_half(const uint8_t* st, int wave, int la
         st + GL::SB + (h * G4_TN + wave * 128 + 32 * j + (lane & 31)) * 4);
 }
 
-template <bool GA>
+template <bool GA, bool TW>
 __global__ void __launch_bounds__(256, 1) k_gemm_nv4g(BigArgs args) {
   using GL = G4Layout;
   constexpr int L = GL::LOADS;
@@ -1158,8 +1180,10 @@ __global__ void __launch_bounds__(256, 1) k_gemm_nv4g(BigArgs args) {
   tc.r0 = (int64_t)p.off[grp] + (int64_t)(local / nt) * G4_TM;
   tc.c0 = (int64_t)(local % nt) * G4_TN;
   tc.rend = p.off[grp + 1];
-  tc.bq = p.bq + (int64_t)grp * p.N * (p.K >> 1);
-  tc.bs = p.bs + (int64_t)grp * p.N * (p.K >> 4);
+  // one expert's weights: N (tiled: N padded to 16 / 64) rows of K/2 code
+  // bytes and K/16 scale bytes
+  tc.bq = p.bq + (int64_t)grp * (TW ? (p.N + 15) & ~(int64_t)15 : p.N) * (p.K >> 1);
+  tc.bs = p.bs + (int64_t)grp * (TW ? (p.N + 63) & ~(int64_t)63 : p.N) * (p.K >> 4);
   tc.bsel = p.bsel + (int64_t)grp * ((p.N + 15) / 16) * p.nc * 1024;
   tc.src = nullptr;
   // gathering: this lane's source rows of the tile (rows past the group
@@ -1189,7 +1213,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_nv4g(BigArgs args) {
   const float tx = p.ats[GA ? 0 : grp] / c, tw = p.bts[grp] * c;
   auto stage = [&](int s) __attribute__((always_inline)) { return sStage + (s % 3) * GL::BYTES; };
   auto issue = [&](int s) __attribute__((always_inline)) {
-    g4_issue<GA>(p, s, wave, lane, tc, stage(s), gao, gso);
+    g4_issue<GA, TW>(p, s, wave, lane, tc, stage(s), gao, gso);
   };
   issue(0);
   if (ns > 1) issue(1);
@@ -1257,8 +1281,9 @@ __global__ void __launch_bounds__(256) k_gather_bsel(const uint8_t* __restrict__
   const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (blk >= nblocks * G) return;
   const int64_t grp = blk / nblocks, lb = blk - grp * nblocks;
-  const uint8_t* gq = bq + grp * N * (K >> 1);
-  const uint8_t* gs = bs + grp * N * (K / BLK);
+  // a group's weights: N rows (tiled: N padded to 16 for codes, 64 for scales)
+  const uint8_t* gq = bq + grp * (TL ? (N + 15) & ~(int64_t)15 : N) * (K >> 1);
+  const uint8_t* gs = bs + grp * (TL ? (N + 63) & ~(int64_t)63 : N) * (K / BLK);
   const int32_t* gc = chan + grp * nS;
   const int64_t Gr = lb / nc;
   const int C = (int)(lb - Gr * nc);
@@ -1401,7 +1426,7 @@ int launch_gemm_big_grouped(int fmt, int64_t total_rows, int64_t N, int64_t K,
                             const float* ats, const uint8_t* bq, const uint8_t* bs,
                             const float* bts, const int32_t* chan, int nS,
                             const uint16_t* resid, const float* cts, const uint8_t* bsel_pre,
-                            void* y, int y_bf16, void* ws, hipStream_t stream,
+                            void* y, int y_bf16, void* ws, hipStream_t stream, bool wtiled,
                             const int32_t* row_src, int64_t src_rows) {
   const int nc = nS > 0 ? (nS + GB_CS - 1) / GB_CS : 0;
   // prepared compensation weights (every group's, made once) replace both
@@ -1410,19 +1435,25 @@ int launch_gemm_big_grouped(int fmt, int64_t total_rows, int64_t N, int64_t K,
   uint8_t* bsel = prepared ? const_cast<uint8_t*>(bsel_pre) : static_cast<uint8_t*>(ws);
   BigArgs a{total_rows, N, K, aq, as, ats, bq, bs, bts, nS, resid, bsel, chan, cts, y, y_bf16, N,
             0, (int)((N + GB_TILE - 1) / GB_TILE), (int)(K / 128), nc, off, G, row_src};
-  const bool gather = nS > GB_XS_MAX && !prepared;
-  const bool xs = nS > 0 && nS <= GB_XS_MAX && !prepared;
+  // tiled weights (NVFP4, 32-bit gather offsets: checked by the caller)
+  // never take the in-kernel extraction
+  const bool xs = nS > 0 && nS <= GB_XS_MAX && !prepared && !wtiled;
+  const bool gather = nS > 0 && !prepared && !xs;
   // the gathering form keeps 32-bit offsets into the token matrix
   const bool ga32 = row_src == nullptr || src_rows * (K / 2) <= (int64_t)UINT32_MAX;
   if (fmt == FP4Q_NVFP4 && !xs && ga32) {
     // 128 x 512 tiles; every group adds at most one partial row tile
     a.nt = (int)((N + G4_TN - 1) / G4_TN);
     const unsigned g4 = (unsigned)(((total_rows + G4_TM - 1) / G4_TM + G) * a.nt);
-    if (gather) launch_gather<FP4Q_NVFP4>(false, bq, bs, N, K, chan, nS, nc, G, bsel, stream);
-    if (row_src)
-      hipLaunchKernelGGL(k_gemm_nv4g<true>, dim3(g4), dim3(256), 0, stream, a);
+    if (gather) launch_gather<FP4Q_NVFP4>(wtiled, bq, bs, N, K, chan, nS, nc, G, bsel, stream);
+    if (row_src && wtiled)
+      hipLaunchKernelGGL((k_gemm_nv4g<true, true>), dim3(g4), dim3(256), 0, stream, a);
+    else if (row_src)
+      hipLaunchKernelGGL((k_gemm_nv4g<true, false>), dim3(g4), dim3(256), 0, stream, a);
+    else if (wtiled)
+      hipLaunchKernelGGL((k_gemm_nv4g<false, true>), dim3(g4), dim3(256), 0, stream, a);
     else
-      hipLaunchKernelGGL(k_gemm_nv4g<false>, dim3(g4), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((k_gemm_nv4g<false, false>), dim3(g4), dim3(256), 0, stream, a);
     return 0;
   }
   // every group adds at most one partial 256-row tile

@@ -315,23 +315,25 @@ int fp4q_gemm_prepared(fp4q_format_t fmt, fp4q_layout_t layout, int64_t M, int64
                        const uint8_t* comp_w, size_t comp_w_bytes, void* y,
                        fp4q_dtype_t y_dtype, int64_t ldy, void* stream);
 
-/* Grouped forms, for fp4q_grouped_gemm's operands (row-major, group g's
- * weights at b_q + g N K/2 and b_s + g N K/blk, its channels at
- * chan_idx + g n_chan): the groups' blocks one after another, group g's at
- * g * fp4q_comp_weights_bytes(fmt, ROWMAJOR, N, K, n_chan).
+/* Grouped forms, for fp4q_grouped_gemm's weights (w_layout as there, its
+ * channels at chan_idx + g n_chan): the groups' blocks one after another,
+ * group g's at g * fp4q_comp_weights_bytes(fmt, ROWMAJOR, N, K, n_chan)
+ * (the same bytes for either weight layout).
  * fp4q_grouped_gemm_prepared is fp4q_grouped_gemm streaming them (no
- * workspace); with N < 256 (the general grouped kernel) the term comes from
- * chan_idx.  Errors as the dense forms; more than 2048 groups is
- * FP4Q_ERR_UNSUPPORTED. */
+ * workspace); with N < 256 (the general grouped kernel, row-major weights
+ * only) the term comes from chan_idx.  Errors as the dense forms and
+ * fp4q_grouped_gemm; more than 2048 groups is FP4Q_ERR_UNSUPPORTED. */
 size_t fp4q_grouped_comp_weights_bytes(fp4q_format_t fmt, int64_t N, int64_t K,
                                        int32_t num_groups, int32_t n_chan);
 
-int fp4q_grouped_comp_weights(fp4q_format_t fmt, int64_t N, int64_t K, int32_t num_groups,
-                              const uint8_t* b_q, const uint8_t* b_s, const int32_t* chan_idx,
-                              int32_t n_chan, uint8_t* out, size_t out_bytes, void* stream);
+int fp4q_grouped_comp_weights(fp4q_format_t fmt, fp4q_layout_t w_layout, int64_t N, int64_t K,
+                              int32_t num_groups, const uint8_t* b_q, const uint8_t* b_s,
+                              const int32_t* chan_idx, int32_t n_chan, uint8_t* out,
+                              size_t out_bytes, void* stream);
 
-int fp4q_grouped_gemm_prepared(fp4q_format_t fmt, int64_t total_rows, int64_t N, int64_t K,
-                               const int32_t* group_offsets, int32_t num_groups,
+int fp4q_grouped_gemm_prepared(fp4q_format_t fmt, fp4q_layout_t w_layout, int64_t total_rows,
+                               int64_t N, int64_t K, const int32_t* group_offsets,
+                               int32_t num_groups,
                                const uint8_t* a_q, const uint8_t* a_s, const float* a_ts,
                                const uint8_t* b_q, const uint8_t* b_s, const float* b_ts,
                                const int32_t* chan_idx, int32_t n_chan, const uint16_t* resid,
@@ -421,14 +423,16 @@ int fp4q_gemm_residual_fp4(fp4q_format_t fmt, fp4q_layout_t layout, int64_t M, i
  * list, and the group's residual quantized with its own tensor scale:
  * r_q, r_s from fp4q_quantize(ROWMAJOR) of R [total_rows, n_chan] with the
  * same group offsets, r_ts device f32 [num_groups] (NVFP4; NULL for MXFP4).
- * Other arguments as fp4q_grouped_gemm; workspace of
+ * Other arguments (w_layout included) as fp4q_grouped_gemm; workspace of
  * fp4q_grouped_gemm_residual_fp4_workspace_bytes() bytes, 16-byte aligned.
  * Errors as the dense form and fp4q_grouped_gemm. */
-size_t fp4q_grouped_gemm_residual_fp4_workspace_bytes(fp4q_format_t fmt, int64_t total_rows,
-                                                      int64_t N, int64_t K, int32_t num_groups,
-                                                      int32_t n_chan);
+size_t fp4q_grouped_gemm_residual_fp4_workspace_bytes(fp4q_format_t fmt,
+                                                      fp4q_layout_t w_layout,
+                                                      int64_t total_rows, int64_t N, int64_t K,
+                                                      int32_t num_groups, int32_t n_chan);
 
-int fp4q_grouped_gemm_residual_fp4(fp4q_format_t fmt, int64_t total_rows, int64_t N, int64_t K,
+int fp4q_grouped_gemm_residual_fp4(fp4q_format_t fmt, fp4q_layout_t w_layout,
+                                   int64_t total_rows, int64_t N, int64_t K,
                                    const int32_t* group_offsets, int32_t num_groups,
                                    const uint8_t* a_q, const uint8_t* a_s, const float* a_ts,
                                    const uint8_t* b_q, const uint8_t* b_s, const float* b_ts,
@@ -526,10 +530,22 @@ int fp4q_select_channels_grouped(fp4q_format_t fmt, const uint16_t* x, int64_t r
  * for Mixture-of-Experts).  Rows [off[g], off[g+1]) of the permuted
  * activations use expert g's weights, tensor scales and channel list:
  *
+ *   w_layout       layout of every expert's weights.  FP4Q_LAYOUT_ROWMAJOR:
+ *                  b_q, b_s are [G, N, K/2], [G, N, K/blk].
+ *                  FP4Q_LAYOUT_TILED: expert g's codes and scales are
+ *                  fp4q_quantize(TILED)'s of its W^T [N, K], at
+ *                  b_q + g * code_bytes and b_s + g * scale_bytes with the
+ *                  sizes of fp4q_packed_bytes(fmt, TILED, N, K).  Tiled
+ *                  weights are served by the 128 x 512 NVFP4 kernel only:
+ *                  MXFP4, N < 256 or n_chan % 8 != 0 is FP4Q_ERR_UNSUPPORTED.
+ *                  On MI355X at the MoE workload (N = 1536 / 2048, K =
+ *                  2048 / 768) tiled weights took the two GEMM calls from
+ *                  about 540 to 490 us (a stage's 512 weight columns are 32
+ *                  contiguous 1 KB blocks instead of 512 rows K/2 apart).
  *   group_offsets  device int32 [G + 1]
  *   a_q, a_s       [total_rows, K/2], [total_rows, K/blk] (row-major)
  *   a_ts           device f32 [G] (NVFP4), NULL for MXFP4
- *   b_q, b_s       [G, N, K/2], [G, N, K/blk]
+ *   b_q, b_s       every expert's W^T, packed in w_layout
  *   b_ts           device f32 [G] (NVFP4), NULL for MXFP4
  *   chan_idx       device int32 [G, n_chan]; resid bf16 [total_rows, n_chan],
  *                  16-byte aligned
@@ -541,11 +557,13 @@ int fp4q_select_channels_grouped(fp4q_format_t fmt, const uint16_t* x, int64_t r
  * Empty groups produce nothing.  K must be a multiple of 128.
  * FP4Q_ERR_WORKSPACE if a needed workspace is missing, small or misaligned.
  * ------------------------------------------------------------------------ */
-size_t fp4q_grouped_gemm_workspace_bytes(fp4q_format_t fmt, int64_t total_rows, int64_t N,
-                                         int64_t K, int32_t num_groups, int32_t n_chan);
+size_t fp4q_grouped_gemm_workspace_bytes(fp4q_format_t fmt, fp4q_layout_t w_layout,
+                                         int64_t total_rows, int64_t N, int64_t K,
+                                         int32_t num_groups, int32_t n_chan);
 
-int fp4q_grouped_gemm(fp4q_format_t fmt, int64_t total_rows, int64_t N, int64_t K,
-                      const int32_t* group_offsets, int32_t num_groups, const uint8_t* a_q,
+int fp4q_grouped_gemm(fp4q_format_t fmt, fp4q_layout_t w_layout, int64_t total_rows, int64_t N,
+                      int64_t K, const int32_t* group_offsets, int32_t num_groups,
+                      const uint8_t* a_q,
                       const uint8_t* a_s, const float* a_ts, const uint8_t* b_q,
                       const uint8_t* b_s, const float* b_ts, const int32_t* chan_idx,
                       int32_t n_chan, const uint16_t* resid, void* y, fp4q_dtype_t y_dtype,
@@ -583,7 +601,8 @@ int fp4q_grouped_gemm(fp4q_format_t fmt, int64_t total_rows, int64_t N, int64_t 
  *   resid_out      out bf16 [rows, n_chan]; NULL iff n_chan == 0
  *
  * Preconditions (not checked on the device): row_src[m] < tokens, offsets
- * as for the grouped GEMM.  Row-major layout only (the grouped GEMM's).
+ * as for the grouped GEMM.  Row-major layout only (the grouped GEMM's
+ * activations').
  * num_groups <= 2048, rows < 2^31, cols < 2^30 (FP4Q_ERR_UNSUPPORTED).
  * ------------------------------------------------------------------------ */
 int fp4q_permute_quantized(fp4q_format_t fmt, const uint16_t* x, int64_t tokens, int64_t cols,
@@ -613,7 +632,8 @@ int fp4q_permute_quantized(fp4q_format_t fmt, const uint16_t* x, int64_t tokens,
  *                  [tokens, K/2], [tokens, K/blk]
  *   a_ts           device f32 [1] its tensor scale (NVFP4), NULL for MXFP4;
  *                  every group uses it
- *   b_*, chan_idx, n_chan   as fp4q_grouped_gemm
+ *   w_layout, b_*, chan_idx, n_chan   as fp4q_grouped_gemm (tiled weights
+ *                  also need tokens * K/2 below 2^32)
  *   resid          bf16 [total_rows, n_chan], 16-byte aligned
  *   comp_w         fp4q_grouped_comp_weights of the weights (needed when
  *                  n_chan > 0), comp_w_bytes its size
@@ -627,8 +647,9 @@ int fp4q_permute_quantized(fp4q_format_t fmt, const uint16_t* x, int64_t tokens,
  * gathering gate_up GEMM took about 25 us more than reading the permuted
  * copy (scattered token rows), against about 10 us saved in the permute.
  * ------------------------------------------------------------------------ */
-int fp4q_grouped_gemm_gather(fp4q_format_t fmt, int64_t total_rows, int64_t N, int64_t K,
-                             const int32_t* group_offsets, int32_t num_groups,
+int fp4q_grouped_gemm_gather(fp4q_format_t fmt, fp4q_layout_t w_layout, int64_t total_rows,
+                             int64_t N, int64_t K, const int32_t* group_offsets,
+                             int32_t num_groups,
                              const int32_t* row_src, int64_t tokens, const uint8_t* a_q,
                              const uint8_t* a_s, const float* a_ts, const uint8_t* b_q,
                              const uint8_t* b_s, const float* b_ts, const int32_t* chan_idx,

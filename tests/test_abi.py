@@ -217,15 +217,10 @@ def test_gemm_decode_fused_rejects(L):
 
 
 def test_grouped_gemm_gather_rejects(L):
-    P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
-    L.fp4q_grouped_gemm_gather.argtypes = [ctypes.c_int, i64, i64, i64, P, i32, P, i64, P, P, P,
-                                           P, P, P, P, i32, P, P, ctypes.c_size_t, P,
-                                           ctypes.c_int, P]
-
-    def f(fmt=0, rows=64, N=256, K=256, off=A, G=2, src=B, tokens=10, aq=A, as_=A, ats=B, bq=B,
-          bs=B, bts=B, chan=None, nS=0, R=None, cw=None, cwb=0, y=A, dt=0):
-        return L.fp4q_grouped_gemm_gather(fmt, rows, N, K, off, G, src, tokens, aq, as_, ats, bq,
-                                          bs, bts, chan, nS, R, cw, cwb, y, dt, None)
+    def f(fmt=0, wl=0, rows=64, N=256, K=256, off=A, G=2, src=B, tokens=10, aq=A, as_=A, ats=B,
+          bq=B, bs=B, bts=B, chan=None, nS=0, R=None, cw=None, cwb=0, y=A, dt=0):
+        return L.fp4q_grouped_gemm_gather(fmt, wl, rows, N, K, off, G, src, tokens, aq, as_, ats,
+                                          bq, bs, bts, chan, nS, R, cw, cwb, y, dt, None)
     assert f(src=None) == INVALID
     assert f(tokens=0) == INVALID
     assert f(off=None) == INVALID
@@ -233,6 +228,11 @@ def test_grouped_gemm_gather_rejects(L):
     assert f(K=200) == INVALID                     # not a multiple of the block
     assert f(G=3000) == UNSUPPORTED
     assert f(nS=8, chan=A, R=B) == WORKSPACE       # prepared weights missing
+    assert f(wl=2) == INVALID                      # no such weight layout
+    assert f(wl=1, fmt=1, ats=None, bts=None) == UNSUPPORTED  # tiled weights: NVFP4 only
+    # tiled weights keep 32-bit offsets into the token matrix's codes
+    assert f(wl=1, K=512, tokens=1 << 24) == UNSUPPORTED
+    assert f(wl=1, rows=0) == 0
     assert f(rows=0) == 0
     try:
         assert L.fp4q_test_hook(1, 33) == 0
@@ -242,14 +242,10 @@ def test_grouped_gemm_gather_rejects(L):
 
 
 def test_grouped_gemm_residual_fp4_rejects(L):
-    P, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
-    L.fp4q_grouped_gemm_residual_fp4.argtypes = [ctypes.c_int, i64, i64, i64, P, i32, P, P, P, P,
-                                                 P, P, P, i32, P, P, P, P, ctypes.c_int, P, sz, P]
-
-    def f(fmt=0, rows=64, N=256, K=256, off=A, G=2, aq=A, as_=A, ats=B, bq=B, bs=B, bts=B,
+    def f(fmt=0, wl=0, rows=64, N=256, K=256, off=A, G=2, aq=A, as_=A, ats=B, bq=B, bs=B, bts=B,
           chan=A, nS=16, rq=A, rs=A, rts=B, y=A, dt=0, ws=A, wsb=1 << 30):
-        return L.fp4q_grouped_gemm_residual_fp4(fmt, rows, N, K, off, G, aq, as_, ats, bq, bs, bts,
-                                                chan, nS, rq, rs, rts, y, dt, ws, wsb, None)
+        return L.fp4q_grouped_gemm_residual_fp4(fmt, wl, rows, N, K, off, G, aq, as_, ats, bq, bs,
+                                                bts, chan, nS, rq, rs, rts, y, dt, ws, wsb, None)
     assert f(nS=8) == INVALID                      # not a multiple of the block
     assert f(rq=None) == INVALID
     assert f(rts=None) == INVALID                  # NVFP4: one residual scale per group
@@ -258,9 +254,15 @@ def test_grouped_gemm_residual_fp4_rejects(L):
     assert f(G=3000) == UNSUPPORTED
     assert f(ws=None) == WORKSPACE
     assert f(wsb=16) == WORKSPACE
+    assert f(wl=2) == INVALID
+    assert f(wl=1, N=128) == UNSUPPORTED           # tiled weights: the 128 x 512 kernel only
+    assert f(wl=1, fmt=1, ats=None, bts=None, nS=32, rts=None) == UNSUPPORTED
     assert f(rows=0) == 0
-    need = L.fp4q_grouped_gemm_residual_fp4_workspace_bytes(0, 64, 256, 256, 2, 16)
+    need = L.fp4q_grouped_gemm_residual_fp4_workspace_bytes(0, 0, 64, 256, 256, 2, 16)
     assert need >= 64 * 16 * 2                     # the decoded residual at least
+    # tiled weights: the compensation weights are always gathered
+    need_t = L.fp4q_grouped_gemm_residual_fp4_workspace_bytes(0, 1, 64, 256, 256, 2, 16)
+    assert need_t == need + 2 * (256 // 16) * 1024
     try:
         assert L.fp4q_test_hook(1, 34) == 0
         assert f() == HIP_ERR and L.fp4q_last_hip_error() == 34
@@ -339,9 +341,10 @@ def test_packed_bytes(L):
 def test_grouped_gemm_rejects(L):
     f = L.fp4q_grouped_gemm
 
-    def gg(fmt=0, rows=10, N=8, K=256, off=A, G=2, ats=B, bts=B, chan=None, nS=0, R=None, ws=None,
-           wsb=0):
-        return f(fmt, rows, N, K, off, G, A, A, ats, B, B, bts, chan, nS, R, A, 0, ws, wsb, None)
+    def gg(fmt=0, wl=0, rows=10, N=8, K=256, off=A, G=2, ats=B, bts=B, chan=None, nS=0, R=None,
+           ws=None, wsb=0):
+        return f(fmt, wl, rows, N, K, off, G, A, A, ats, B, B, bts, chan, nS, R, A, 0, ws, wsb,
+                 None)
 
     assert gg(off=None) == INVALID
     assert gg(G=0) == INVALID
@@ -349,11 +352,17 @@ def test_grouped_gemm_rejects(L):
     assert gg(fmt=1, bts=None) == INVALID        # MXFP4 takes no tensor scales
     # the staged 256-column path gathers every group's compensation weights
     # when there are more than 96 channels
-    need = L.fp4q_grouped_gemm_workspace_bytes(0, 1000, 512, 256, 4, 128)
+    need = L.fp4q_grouped_gemm_workspace_bytes(0, 0, 1000, 512, 256, 4, 128)
     assert need == 4 * (512 // 16) * 4 * 1024
-    assert L.fp4q_grouped_gemm_workspace_bytes(0, 1000, 512, 256, 4, 32) == 0
-    assert L.fp4q_grouped_gemm_workspace_bytes(0, 1000, 128, 256, 4, 128) == 0   # N < 256
-    assert L.fp4q_grouped_gemm_workspace_bytes(0, 1000, 512, 256, 4, 0) == 0
+    assert L.fp4q_grouped_gemm_workspace_bytes(0, 0, 1000, 512, 256, 4, 32) == 0
+    assert L.fp4q_grouped_gemm_workspace_bytes(0, 0, 1000, 128, 256, 4, 128) == 0   # N < 256
+    assert L.fp4q_grouped_gemm_workspace_bytes(0, 0, 1000, 512, 256, 4, 0) == 0
+    # tiled weights gather the compensation weights for any channel count
+    assert L.fp4q_grouped_gemm_workspace_bytes(0, 1, 1000, 512, 256, 4, 32) == 4 * 32 * 1024
+    assert gg(wl=2) == INVALID
+    assert gg(wl=1) == UNSUPPORTED               # N < 256: the general kernel, row-major only
+    assert gg(wl=1, N=512, K=192) == UNSUPPORTED   # K % 128 (checked as for row-major)
+    assert gg(wl=1, N=512, chan=A, nS=32, R=B) == WORKSPACE
     big = dict(rows=1000, N=512, K=256, G=4, chan=A, nS=128, R=B)
     assert gg(**big) == WORKSPACE
     assert gg(**big, ws=A, wsb=need - 16) == WORKSPACE
@@ -565,9 +574,10 @@ def test_grouped_prepared_rejects(L):
     assert L.fp4q_grouped_comp_weights_bytes(0, 1536, 2048, 128, 32) == 128 * 96 * 1024
     assert L.fp4q_grouped_comp_weights_bytes(0, 1536, 2048, 0, 32) == 0
 
-    def gcw(fmt=0, N=32, K=256, G=2, chan=A, nS=8, out=A, nb=4096):
-        return L.fp4q_grouped_comp_weights(fmt, N, K, G, B, B, chan, nS, out, nb, None)
+    def gcw(fmt=0, wl=0, N=32, K=256, G=2, chan=A, nS=8, out=A, nb=4096):
+        return L.fp4q_grouped_comp_weights(fmt, wl, N, K, G, B, B, chan, nS, out, nb, None)
     assert gcw(fmt=3) == INVALID
+    assert gcw(wl=2) == INVALID
     assert gcw(G=0) == INVALID
     assert gcw(G=5000) == UNSUPPORTED
     assert gcw(chan=None) == INVALID
@@ -575,9 +585,12 @@ def test_grouped_prepared_rejects(L):
     assert gcw(nb=4095) == WORKSPACE
     assert gcw(out=ctypes.c_void_p(0x10008)) == INVALID
 
-    def ggp(G=2, off=A, cw=A, nb=1 << 20, nS=8, chan=A, R=B):
-        return L.fp4q_grouped_gemm_prepared(0, 64, 256, 256, off, G, A, A, B, B, B, B, chan, nS, R,
-                                            cw, nb, A, 0, None)
+    def ggp(G=2, off=A, cw=A, nb=1 << 20, nS=8, chan=A, R=B, wl=0, N=256, fmt=0, ts=B):
+        return L.fp4q_grouped_gemm_prepared(fmt, wl, 64, N, 256, off, G, A, A, ts, B, B, ts, chan,
+                                            nS, R, cw, nb, A, 0, None)
+    assert ggp(wl=2) == INVALID
+    assert ggp(wl=1, N=200) == UNSUPPORTED
+    assert ggp(wl=1, fmt=1, ts=None, nS=32) == UNSUPPORTED
     assert ggp(off=None) == INVALID
     assert ggp(G=5000) == UNSUPPORTED
     assert ggp(cw=None) == WORKSPACE

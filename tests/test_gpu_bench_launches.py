@@ -10,7 +10,8 @@ workload sizes, against the oracle:
     gate_up and down: grouped GPU quantization bit for bit, each expert's
     weights quantized on the GPU, the grouped prepared compensation
     weights, fp4q_grouped_gemm_prepared on sampled outputs plus the first
-    and last row of every non-empty expert.
+    and last row of every non-empty expert; then the same with every
+    expert's weights in the tiled layout (as benchmarked), bit for bit.
 """
 import numpy as np
 import pytest
@@ -93,3 +94,16 @@ def test_moe_prepared_chain(orc, layer):
                                      chan, qa["resid"], pm, pn)
     r = assert_gemm_close(y[pm, pn], yo, ya)
     say(f"  worst |dY|/Yabs = {r:.3e}")
+    # the benchmark keeps every expert's weights in the tiled layout: the
+    # same kernel reads the same bytes into LDS, so Y is bit-identical
+    qt = [fq.quantize(0, to_dev(wts[e]), layout=fq.TILED) for e in range(G)]
+    tq = torch.stack([q["q"] for q in qt])
+    ts = torch.stack([q["scales"] for q in qt])
+    cwt = fq.grouped_comp_weights(0, tq, ts, dch, w_layout=fq.TILED, N=N, K=x.shape[1])
+    assert torch.equal(cwt, cw), "grouped compensation weights from tiled weights"
+    yt = fq.grouped_gemm_prepared(0, doff, a, tq, ts, bts, dch, cwt, w_layout=fq.TILED, N=N)
+    torch.cuda.synchronize()
+    yt = to_host(yt)
+    bad = np.flatnonzero(yt.view(np.uint32) != y.view(np.uint32))
+    assert bad.size == 0, f"tiled weights: {bad.size} outputs differ, first {bad[:4].tolist()}"
+    say("  tiled expert weights: Y bit-identical")

@@ -9,7 +9,9 @@ quantize-before-permute) and of the permute's residual-only mode:
     quantize-before-permute product within 1e-3 * Yabs;
   * at the full MoE gate_up layer (32768 routed rows of 4096 tokens, 128
     experts) and on small cases with empty and single-row experts, both
-    formats, with and without channels.
+    formats, with and without channels;
+  * NVFP4 with every expert's weights in the tiled layout equals the
+    row-major result bit for bit.
 """
 import numpy as np
 import pytest
@@ -55,6 +57,20 @@ def _case(orc, fmt, x_tok, row_src, off, chan, wts, pm=None, pn=None):
     if fmt == 0:
         assert torch.equal(ts_only, full["tscale"])
     assert torch.equal(y_gather, y_copy), "gathering GEMM differs from the permuted copy"
+    if fmt == 0 and N >= 256 and nS % 8 == 0:
+        # every expert's weights in the tiled layout: the same bytes reach the
+        # kernel's LDS, so the gathering GEMM's Y is bit-identical
+        qt_ = [fq.quantize(fmt, to_dev(w), layout=fq.TILED) for w in wts]
+        tq = torch.stack([q["q"] for q in qt_])
+        ts = torch.stack([q["scales"] for q in qt_])
+        cwt = (fq.grouped_comp_weights(fmt, tq, ts, dch, w_layout=fq.TILED, N=N, K=K) if nS
+               else None)
+        y_t = torch.empty((rows, N), dtype=torch.float32, device=dev)
+        fq.grouped_gemm_gather_into(fmt, rows, N, K, doff, G, src, T, tok["q"], tok["scales"],
+                                    tok["tscale"], tq, ts, bts, dch, nS, r_only, cwt, y_t, 0,
+                                    w_layout=fq.TILED)
+        torch.cuda.synchronize()
+        assert torch.equal(y_t, y_gather), "tiled expert weights: gathering GEMM differs"
     # the oracle: quantize-before-permute, then the grouped product
     qt = orc.quantize(fmt, x_tok)
     perm = orc.permute_quantized(fmt, x_tok, qt, row_src, off, chan)
