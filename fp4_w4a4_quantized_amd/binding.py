@@ -228,6 +228,8 @@ def grouped_comp_weights(fmt, bq, bs, chan_idx, stream=None, w_layout=ROWMAJOR, 
     G = bq.shape[0]
     if w_layout == ROWMAJOR:
         N, K = bq.shape[1], 2 * bq.shape[2]
+    elif N is None or K is None:
+        raise ValueError("tiled weights: N and K must be given")
     nS = chan_idx.numel() // G
     nb = grouped_comp_weights_bytes(fmt, N, K, G, nS)
     out = torch.empty(max(nb, 16), dtype=torch.uint8, device=bq.device)
@@ -575,6 +577,8 @@ def grouped_gemm_residual_fp4(fmt, group_offsets, a, bq, bs, bts, chan_idx, r, y
     G = group_offsets.numel() - 1
     if w_layout == ROWMAJOR:
         N = bq.shape[1]
+    elif N is None:
+        raise ValueError("tiled weights: N must be given")
     nS = chan_idx.numel() // G
     dev = a["q"].device
     y = torch.empty((total, N), dtype=torch.float32 if y_dtype == OUT_F32 else torch.bfloat16,
@@ -688,6 +692,8 @@ def grouped_gemm(fmt, group_offsets, a, bq, bs, bts, chan_idx=None, y_dtype=OUT_
     G = group_offsets.numel() - 1
     if w_layout == ROWMAJOR:
         N = bq.shape[1]
+    elif N is None:
+        raise ValueError("tiled weights: N must be given")
     nS = 0 if chan_idx is None else chan_idx.numel() // G
     dev = a["q"].device
     y = torch.empty((total, N), dtype=torch.float32 if y_dtype == OUT_F32 else torch.bfloat16,
@@ -707,6 +713,8 @@ def grouped_gemm_prepared(fmt, group_offsets, a, bq, bs, bts, chan_idx, comp_w, 
     G = group_offsets.numel() - 1
     if w_layout == ROWMAJOR:
         N = bq.shape[1]
+    elif N is None:
+        raise ValueError("tiled weights: N must be given")
     nS = chan_idx.numel() // G
     y = torch.empty((total, N), dtype=torch.float32 if y_dtype == OUT_F32 else torch.bfloat16,
                     device=a["q"].device)

@@ -595,3 +595,21 @@ def test_grouped_prepared_rejects(L):
     assert ggp(G=5000) == UNSUPPORTED
     assert ggp(cw=None) == WORKSPACE
     assert ggp(nb=100) == WORKSPACE
+
+
+def test_tiled_weight_wrappers_need_shapes():
+    """The binding cannot read N (and K) from packed tiled weights: it asks
+    for them instead of guessing from padded byte counts."""
+    import torch
+    import fp4_w4a4_quantized_amd as fq
+    bq = torch.zeros((2, 4096), dtype=torch.uint8)
+    chan = torch.zeros((2, 8), dtype=torch.int32)
+    with pytest.raises(ValueError):
+        fq.grouped_comp_weights(0, bq, bq, chan, w_layout=fq.TILED, N=256)
+    a = {"q": torch.zeros((4, 128), dtype=torch.uint8), "scales": None, "tscale": None,
+         "resid": None}
+    off = torch.tensor([0, 2, 4], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        fq.grouped_gemm(0, off, a, bq, bq, None, w_layout=fq.TILED)
+    with pytest.raises(ValueError):
+        fq.grouped_gemm_prepared(0, off, a, bq, bq, None, chan, bq, w_layout=fq.TILED)
