@@ -428,9 +428,9 @@ int fp4q_gemm_residual_fp4(fp4q_format_t fmt, fp4q_layout_t layout, int64_t M, i
 size_t fp4q_grouped_gemm_workspace_bytes(fp4q_format_t fmt, fp4q_layout_t w_layout,
                                          int64_t total_rows, int64_t N, int64_t K,
                                          int32_t num_groups, int32_t n_chan) {
-  (void)fmt;
+  (void)w_layout;
   if (total_rows <= 0 || N <= 0 || K <= 0 || n_chan <= 0 || num_groups < 1) return 0;
-  return fp4q::grouped_workspace_bytes(N, K, num_groups, n_chan, w_layout == FP4Q_LAYOUT_TILED);
+  return fp4q::grouped_workspace_bytes(fmt, N, K, num_groups, n_chan);
 }
 
 int fp4q_grouped_gemm(fp4q_format_t fmt, fp4q_layout_t w_layout, int64_t total_rows, int64_t N,

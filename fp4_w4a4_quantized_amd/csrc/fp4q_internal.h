@@ -64,10 +64,11 @@ void launch_deq_resid(int fmt, int64_t M, int nS, const uint8_t* rq, const uint8
 bool big_gemm_eligible(int64_t M, int64_t N, int64_t K, int nS);
 bool big_grouped_eligible(int64_t N, int64_t K, int nS);
 size_t big_gemm_workspace_bytes(int64_t N, int nS);
-// wtiled: every expert's weights in the tiled layout (NVFP4 only, served by
-// the 128 x 512 grouped kernel; the compensation weights then always come
-// from the workspace or the prepared array, never from in-kernel extraction)
-size_t grouped_workspace_bytes(int64_t N, int64_t K, int G, int nS, bool wtiled);
+// NVFP4 runs on the 128 x 512 grouped kernel, which takes the compensation
+// weights from the workspace (gathered per call) or the prepared array,
+// never by in-kernel extraction.  wtiled: every expert's weights in the
+// tiled layout (NVFP4 only).
+size_t grouped_workspace_bytes(int fmt, int64_t N, int64_t K, int G, int nS);
 bool grouped_tiled_ok(int fmt, int64_t N, int64_t K, int nS);
 int launch_gemm_big_grouped(int fmt, int64_t total_rows, int64_t N, int64_t K,
                             const int32_t* off, int G, const uint8_t* aq, const uint8_t* as,

@@ -390,10 +390,12 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int nS) {
   return gemm_path(M, N, K, nS) == PATH_BIG ? big_gemm_workspace_bytes(N, nS) : 0;
 }
 
-size_t grouped_workspace_bytes(int64_t N, int64_t K, int G, int nS, bool wtiled) {
+size_t grouped_workspace_bytes(int fmt, int64_t N, int64_t K, int G, int nS) {
   if (!big_grouped_eligible(N, K, nS)) return 0;
-  // tiled weights: B_S is always gathered (no in-kernel extraction)
-  return (size_t)G * (wtiled ? comp_weights_bytes(N, nS) : big_gemm_workspace_bytes(N, nS));
+  // NVFP4 (128 x 512 kernel): B_S is always gathered; MXFP4 (256-tile
+  // kernel): only above the in-kernel extraction's channel count
+  return (size_t)G * (fmt == FP4Q_NVFP4 ? comp_weights_bytes(N, nS)
+                                        : big_gemm_workspace_bytes(N, nS));
 }
 
 bool grouped_tiled_ok(int fmt, int64_t N, int64_t K, int nS) {

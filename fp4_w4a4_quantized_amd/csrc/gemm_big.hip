@@ -1435,9 +1435,11 @@ int launch_gemm_big_grouped(int fmt, int64_t total_rows, int64_t N, int64_t K,
   uint8_t* bsel = prepared ? const_cast<uint8_t*>(bsel_pre) : static_cast<uint8_t*>(ws);
   BigArgs a{total_rows, N, K, aq, as, ats, bq, bs, bts, nS, resid, bsel, chan, cts, y, y_bf16, N,
             0, (int)((N + GB_TILE - 1) / GB_TILE), (int)(K / 128), nc, off, G, row_src};
-  // tiled weights (NVFP4, 32-bit gather offsets: checked by the caller)
-  // never take the in-kernel extraction
-  const bool xs = nS > 0 && nS <= GB_XS_MAX && !prepared && !wtiled;
+  // NVFP4 never takes the in-kernel extraction: the 128 x 512 kernel with
+  // B_S gathered once per call beats the 256-tile kernel extracting it from
+  // the tiles (tiled weights: NVFP4 with 32-bit gather offsets, checked by
+  // the caller)
+  const bool xs = nS > 0 && nS <= GB_XS_MAX && !prepared && fmt != FP4Q_NVFP4;
   const bool gather = nS > 0 && !prepared && !xs;
   // the gathering form keeps 32-bit offsets into the token matrix
   const bool ga32 = row_src == nullptr || src_rows * (K / 2) <= (int64_t)UINT32_MAX;

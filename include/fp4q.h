@@ -554,6 +554,9 @@ int fp4q_select_channels_grouped(fp4q_format_t fmt, const uint16_t* x, int64_t r
  *   workspace      device scratch of fp4q_grouped_gemm_workspace_bytes()
  *                  bytes, 16-byte aligned (may be NULL when that is 0): the
  *                  gathered compensation weights of every group, as BF16
+ *                  (NVFP4 with N >= 256: whenever there are channels, the
+ *                  128 x 512 kernel streaming them; MXFP4: above 96
+ *                  channels, fewer being extracted inside the kernel)
  *
  * Empty groups produce nothing.  K must be a multiple of 128.
  * FP4Q_ERR_WORKSPACE if a needed workspace is missing, small or misaligned.

@@ -261,8 +261,9 @@ def test_grouped_gemm_residual_fp4_rejects(L):
     need = L.fp4q_grouped_gemm_residual_fp4_workspace_bytes(0, 0, 64, 256, 256, 2, 16)
     assert need >= 64 * 16 * 2                     # the decoded residual at least
     # tiled weights: the compensation weights are always gathered
+    # NVFP4 gathers the compensation weights for either weight layout
     need_t = L.fp4q_grouped_gemm_residual_fp4_workspace_bytes(0, 1, 64, 256, 256, 2, 16)
-    assert need_t == need + 2 * (256 // 16) * 1024
+    assert need_t == need == 64 * 16 * 2 + 2 * (256 // 16) * 1024
     try:
         assert L.fp4q_test_hook(1, 34) == 0
         assert f() == HIP_ERR and L.fp4q_last_hip_error() == 34
@@ -354,7 +355,10 @@ def test_grouped_gemm_rejects(L):
     # when there are more than 96 channels
     need = L.fp4q_grouped_gemm_workspace_bytes(0, 0, 1000, 512, 256, 4, 128)
     assert need == 4 * (512 // 16) * 4 * 1024
-    assert L.fp4q_grouped_gemm_workspace_bytes(0, 0, 1000, 512, 256, 4, 32) == 0
+    # NVFP4 gathers every group's compensation weights at any channel count;
+    # MXFP4 extracts up to 96 channels in the kernel
+    assert L.fp4q_grouped_gemm_workspace_bytes(0, 0, 1000, 512, 256, 4, 32) == 4 * 32 * 1024
+    assert L.fp4q_grouped_gemm_workspace_bytes(1, 0, 1000, 512, 256, 4, 32) == 0
     assert L.fp4q_grouped_gemm_workspace_bytes(0, 0, 1000, 128, 256, 4, 128) == 0   # N < 256
     assert L.fp4q_grouped_gemm_workspace_bytes(0, 0, 1000, 512, 256, 4, 0) == 0
     # tiled weights gather the compensation weights for any channel count

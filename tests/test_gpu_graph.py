@@ -102,7 +102,8 @@ def test_graph_grouped_layer(N, nS):
     y = torch.empty((rows, N), dtype=torch.float32, device=dev)
     gwsb = fq.grouped_gemm_workspace_bytes(fmt, rows, N, K, G, nS)
     gws = torch.empty(gwsb, dtype=torch.uint8, device=dev) if gwsb else None
-    assert (gwsb > 0) == (N >= 256 and nS > 96)
+    # NVFP4 on the 128 x 512 kernel gathers every group's B_S into the workspace
+    assert (gwsb > 0) == (N >= 256 and nS > 0)
 
     def run():
         fq.quantize_into(fmt, fq.ROWMAJOR, x, off, G, chan, nS, b["q"], b["s"], b["t"], b["r"],

@@ -134,7 +134,7 @@ def _grouped_gpu(fmt, off, chan, qa, qr, bq, bs, bts):
     return to_host(y)
 
 
-@pytest.mark.parametrize("fmt,N,nS", [(0, 300, 32),    # 256-tile kernel, B_S from the tiles
+@pytest.mark.parametrize("fmt,N,nS", [(0, 300, 32),    # 128x512 NVFP4 kernel, gathered B_S
                                       (0, 560, 128),   # 128x512 NVFP4 kernel, gathered B_S
                                       (0, 200, 16),    # general grouped kernel
                                       (1, 300, 32), (1, 560, 128), (1, 200, 64)])
