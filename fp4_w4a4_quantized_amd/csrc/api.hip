@@ -253,10 +253,9 @@ static int validate_w_layout(int fmt, int w_layout, int64_t N, int64_t K, int32_
 
 size_t fp4q_gemm_workspace_bytes(fp4q_format_t fmt, fp4q_layout_t layout, int64_t M, int64_t N,
                                  int64_t K, int32_t n_chan) {
-  (void)fmt;
   (void)layout;
   if (M <= 0 || N <= 0 || K <= 0 || n_chan <= 0) return 0;
-  return fp4q::gemm_workspace_bytes(M, N, K, n_chan);
+  return fp4q::gemm_workspace_bytes(fmt, M, N, K, n_chan);
 }
 
 int fp4q_gemm(fp4q_format_t fmt, fp4q_layout_t layout, int64_t M, int64_t N, int64_t K,

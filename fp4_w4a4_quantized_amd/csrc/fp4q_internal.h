@@ -45,7 +45,7 @@ int grid_hook_skip();
 // workspace query and the launch agree).
 enum GemmPath { PATH_GENERIC = 0, PATH_SKINNY = 1, PATH_BIG = 2 };
 GemmPath gemm_path(int64_t M, int64_t N, int64_t K, int nS);
-size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int nS);
+size_t gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, int nS);
 
 // cts: device tensor scale of the compensation term (NVFP4 second-pass
 // residual), or null for 1: y = t_w (t_x main + cts comp); grouped: one per

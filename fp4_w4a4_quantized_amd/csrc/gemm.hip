@@ -386,8 +386,11 @@ GemmPath gemm_path(int64_t M, int64_t N, int64_t K, int nS) {
   return PATH_GENERIC;
 }
 
-size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int nS) {
-  return gemm_path(M, N, K, nS) == PATH_BIG ? big_gemm_workspace_bytes(N, nS) : 0;
+size_t gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, int nS) {
+  if (gemm_path(M, N, K, nS) != PATH_BIG) return 0;
+  // NVFP4 (four-wave kernel): B_S gathered whenever there are channels;
+  // MXFP4: above the in-kernel extraction's channel count
+  return fmt == FP4Q_NVFP4 ? comp_weights_bytes(N, nS) : big_gemm_workspace_bytes(N, nS);
 }
 
 size_t grouped_workspace_bytes(int fmt, int64_t N, int64_t K, int G, int nS) {

@@ -1341,7 +1341,9 @@ size_t big_gemm_workspace_bytes(int64_t N, int nS) {
 template <int FMT, bool GR>
 static void launch_big(const BigArgs& a, bool tiled, unsigned grid, hipStream_t stream,
                        bool prepared = false) {
-  const bool xs = a.nS > 0 && a.nS <= GB_XS_MAX && !prepared;
+  // NVFP4 runs on the four-wave kernels with B_S gathered or prepared; the
+  // in-kernel extraction (XS) serves MXFP4 up to GB_XS_MAX channels
+  const bool xs = FMT != FP4Q_NVFP4 && a.nS > 0 && a.nS <= GB_XS_MAX && !prepared;
   if constexpr (GR) {  // grouped operands are row-major
     if (a.row_src)   // the gathering form streams prepared weights (no XS)
       hipLaunchKernelGGL((k_gemm_big<FMT, false, 2, false>), dim3(grid), dim3(GB_T), 0, stream, a);
@@ -1393,7 +1395,7 @@ int launch_gemm_big(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const 
   BigArgs a{M, N, K, aq, as, ats, bq, bs, bts, nS, resid, bsel, chan, cts, y, y_bf16, ldy,
             (int)((M + GB_TILE - 1) / GB_TILE), (int)((N + GB_TILE - 1) / GB_TILE),
             (int)(K / 128), nc, nullptr, 1, nullptr};
-  const bool gather = nS > GB_XS_MAX && !prepared;
+  const bool gather = nS > 0 && !prepared && (fmt == FP4Q_NVFP4 || nS > GB_XS_MAX);
   const unsigned grid = (unsigned)(a.mt * a.nt);
   if (fmt == FP4Q_NVFP4) {
     if (gather) launch_gather<FP4Q_NVFP4>(tiled, bq, bs, N, K, chan, nS, nc, 1, bsel, stream);

@@ -301,14 +301,16 @@ def test_gemm_rejects(L):
     assert g(L, layout=5) == INVALID
     assert g(L, layout=1, K=144) == UNSUPPORTED
     assert g(L, nS=8, chan=A, R=ctypes.c_void_p(0x20008)) == INVALID   # resid 16-byte aligned
-    # the 256x256-tile path takes up to 96 compensation channels from its own
-    # B tiles; more are gathered into a workspace first
+    # the large-tile NVFP4 kernel streams B_S gathered into the workspace;
+    # the MXFP4 one takes up to 96 channels from its own B tiles
     need = L.fp4q_gemm_workspace_bytes(0, 1, 512, 512, 256, 128)
     assert need == (512 // 16) * 4 * 1024
     assert L.fp4q_gemm_workspace_bytes(0, 1, 512, 512, 256, 104) == (512 // 16) * 4 * 1024
     assert L.fp4q_gemm_workspace_bytes(0, 1, 512, 500, 256, 136) == (512 // 16) * 5 * 1024
-    for nS in (0, 8, 32, 40, 96):
-        assert L.fp4q_gemm_workspace_bytes(0, 1, 512, 512, 256, nS) == 0
+    assert L.fp4q_gemm_workspace_bytes(0, 1, 512, 512, 256, 0) == 0
+    for nS in (8, 32, 40, 96):
+        assert L.fp4q_gemm_workspace_bytes(0, 1, 512, 512, 256, nS) == (512 // 16) * ((nS + 31) // 32) * 1024
+        assert L.fp4q_gemm_workspace_bytes(1, 1, 512, 512, 256, nS) == 0
     assert L.fp4q_gemm_workspace_bytes(0, 1, 64, 11008, 2048, 128) == 0   # decode shape
     assert L.fp4q_gemm_workspace_bytes(0, 1, 512, 512, 256, 12) == 0      # |S| % 8: other path
     big = dict(M=512, N=512, K=256, nS=128, chan=A, R=B, ldy=512)
