@@ -135,7 +135,7 @@ def src_hash(files=None) -> str:
 # demangled name, the sources that define it, and its dispatches per launch
 DOMINANT = {
     "prefill_nvfp4": ("k_gemm_nv4<true>", ["gemm_big.hip", "fp4q_device.h"], 1),
-    "prefill_mxfp4": ("k_gemm_big<1, true, 0, false>", ["gemm_big.hip", "fp4q_device.h"], 1),
+    "prefill_mxfp4": ("k_gemm_big<1, true, 0>", ["gemm_big.hip", "fp4q_device.h"], 1),
     "decode_nvfp4": ("k_gemm_skinny<0, true, true>", ["gemm_skinny.hip", "fp4q_device.h"], 1),
     "moe_nvfp4": ("k_gemm_nv4g<false, true>", ["gemm_big.hip", "fp4q_device.h"], 2),
 }

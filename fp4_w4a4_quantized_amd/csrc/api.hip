@@ -253,9 +253,10 @@ static int validate_w_layout(int fmt, int w_layout, int64_t N, int64_t K, int32_
 
 size_t fp4q_gemm_workspace_bytes(fp4q_format_t fmt, fp4q_layout_t layout, int64_t M, int64_t N,
                                  int64_t K, int32_t n_chan) {
+  (void)fmt;
   (void)layout;
   if (M <= 0 || N <= 0 || K <= 0 || n_chan <= 0) return 0;
-  return fp4q::gemm_workspace_bytes(fmt, M, N, K, n_chan);
+  return fp4q::gemm_workspace_bytes(M, N, K, n_chan);
 }
 
 int fp4q_gemm(fp4q_format_t fmt, fp4q_layout_t layout, int64_t M, int64_t N, int64_t K,
@@ -427,9 +428,10 @@ int fp4q_gemm_residual_fp4(fp4q_format_t fmt, fp4q_layout_t layout, int64_t M, i
 size_t fp4q_grouped_gemm_workspace_bytes(fp4q_format_t fmt, fp4q_layout_t w_layout,
                                          int64_t total_rows, int64_t N, int64_t K,
                                          int32_t num_groups, int32_t n_chan) {
+  (void)fmt;
   (void)w_layout;
   if (total_rows <= 0 || N <= 0 || K <= 0 || n_chan <= 0 || num_groups < 1) return 0;
-  return fp4q::grouped_workspace_bytes(fmt, N, K, num_groups, n_chan);
+  return fp4q::grouped_workspace_bytes(N, K, num_groups, n_chan);
 }
 
 int fp4q_grouped_gemm(fp4q_format_t fmt, fp4q_layout_t w_layout, int64_t total_rows, int64_t N,

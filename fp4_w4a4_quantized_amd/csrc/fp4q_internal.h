@@ -45,7 +45,7 @@ int grid_hook_skip();
 // workspace query and the launch agree).
 enum GemmPath { PATH_GENERIC = 0, PATH_SKINNY = 1, PATH_BIG = 2 };
 GemmPath gemm_path(int64_t M, int64_t N, int64_t K, int nS);
-size_t gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, int nS);
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int nS);
 
 // cts: device tensor scale of the compensation term (NVFP4 second-pass
 // residual), or null for 1: y = t_w (t_x main + cts comp); grouped: one per
@@ -64,11 +64,10 @@ void launch_deq_resid(int fmt, int64_t M, int nS, const uint8_t* rq, const uint8
 bool big_gemm_eligible(int64_t M, int64_t N, int64_t K, int nS);
 bool big_grouped_eligible(int64_t N, int64_t K, int nS);
 size_t big_gemm_workspace_bytes(int64_t N, int nS);
-// NVFP4 runs on the 128 x 512 grouped kernel, which takes the compensation
-// weights from the workspace (gathered per call) or the prepared array,
-// never by in-kernel extraction.  wtiled: every expert's weights in the
-// tiled layout (NVFP4 only).
-size_t grouped_workspace_bytes(int fmt, int64_t N, int64_t K, int G, int nS);
+// The large-tile grouped kernels take the compensation weights from the
+// prepared array or gather them into the workspace once per call.  wtiled:
+// every expert's weights in the tiled layout (NVFP4 only).
+size_t grouped_workspace_bytes(int64_t N, int64_t K, int G, int nS);
 bool grouped_tiled_ok(int fmt, int64_t N, int64_t K, int nS);
 int launch_gemm_big_grouped(int fmt, int64_t total_rows, int64_t N, int64_t K,
                             const int32_t* off, int G, const uint8_t* aq, const uint8_t* as,

@@ -386,19 +386,14 @@ GemmPath gemm_path(int64_t M, int64_t N, int64_t K, int nS) {
   return PATH_GENERIC;
 }
 
-size_t gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, int nS) {
-  if (gemm_path(M, N, K, nS) != PATH_BIG) return 0;
-  // NVFP4 (four-wave kernel): B_S gathered whenever there are channels;
-  // MXFP4: above the in-kernel extraction's channel count
-  return fmt == FP4Q_NVFP4 ? comp_weights_bytes(N, nS) : big_gemm_workspace_bytes(N, nS);
+// The large-tile kernels stream B_S: without a prepared array it is
+// gathered into the workspace once per call.
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int nS) {
+  return gemm_path(M, N, K, nS) == PATH_BIG ? big_gemm_workspace_bytes(N, nS) : 0;
 }
 
-size_t grouped_workspace_bytes(int fmt, int64_t N, int64_t K, int G, int nS) {
-  if (!big_grouped_eligible(N, K, nS)) return 0;
-  // NVFP4 (128 x 512 kernel): B_S is always gathered; MXFP4 (256-tile
-  // kernel): only above the in-kernel extraction's channel count
-  return (size_t)G * (fmt == FP4Q_NVFP4 ? comp_weights_bytes(N, nS)
-                                        : big_gemm_workspace_bytes(N, nS));
+size_t grouped_workspace_bytes(int64_t N, int64_t K, int G, int nS) {
+  return big_grouped_eligible(N, K, nS) ? (size_t)G * big_gemm_workspace_bytes(N, nS) : 0;
 }
 
 bool grouped_tiled_ok(int fmt, int64_t N, int64_t K, int nS) {

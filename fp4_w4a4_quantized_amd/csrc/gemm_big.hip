@@ -65,9 +65,6 @@ constexpr int GB_DATA = 16 * GB_GRP;     // 16 KB per operand per stage
 constexpr int GB_CS = 32;                // channels per compensation stage
 constexpr int GB_GROUP_M = 4;            // tile rows per L2 group
 constexpr int GB_EP_STRIDE = 68;         // epilogue LDS row stride (floats)
-constexpr int GB_XS_MAX = 96;            // channels extracted in-kernel (3 stages of 32)
-constexpr int GB_XS_BYTES = 3 * GB_DATA; // their B_S, laid out as 3 compensation B tiles
-constexpr int GB_XS_MAX_NK = 256;        // K <= 32768 for the per-stage channel table
 
 struct BigArgs {
   int64_t M, N, K;
@@ -80,7 +77,7 @@ struct BigArgs {
   int nS;
   const uint16_t* resid;
   const uint8_t* bsel;  // gathered B_S, tiled BF16 (see k_gather_bsel)
-  const int32_t* chan;  // channel lists (in-kernel extraction)
+  const int32_t* chan;  // channel lists (not read by the kernels; B_S is gathered)
   const float* cts;     // tensor scale of the compensation term, or null (1)
   void* y;
   int y_bf16;
@@ -225,7 +222,7 @@ __device__ __forceinline__ void lds_barrier() {
 // Compensation stage cs: per 16-row group, R rows (channels 32cs + 8(l/16)
 // .. +7 of row 16g + l%16; a piece past |S| is re-read from the last valid
 // one and meets zero weights) and the matching 1 KB block of B_S.
-template <int FMT, bool TL, bool XS, bool GA = false>
+template <int FMT, bool TL, bool GA = false>
 __device__ __forceinline__ void issue_stage(const BigArgs& p, int s, int wave, int lane,
                                             const TileCtx& tc, uint8_t* st) {
   using SL = StageLayout<FMT>;
@@ -244,10 +241,7 @@ __device__ __forceinline__ void issue_stage(const BigArgs& p, int s, int wave, i
       int64_t gb = (c0 >> 4) + g;
       gb = gb < gN ? gb : gN;
       lds_load16(p.resid + row * p.nS + ch, st + SL::A + g * GB_GRP);
-      if (XS)  // B_S is already in LDS; a placeholder keeps the load count
-        lds_load4(p.resid, st + SL::B + g * GB_GRP);
-      else
-        lds_load16s(tc.bsel + ((gb * p.nc + cs) << 10), lane * 16, st + SL::B + g * GB_GRP);
+      lds_load16s(tc.bsel + ((gb * p.nc + cs) << 10), lane * 16, st + SL::B + g * GB_GRP);
     }
 #pragma unroll
     for (int i = 0; i < SL::SPW; ++i)  // placeholders keeping the per-stage load count
@@ -519,18 +513,15 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[RI][4], const Big
       }
 }
 
-// XS: the compensation weights of up to GB_XS_MAX channels are taken from
-// the B tiles as the FP4 stages pass through LDS (no gather kernel).
+// The compensation weights B_S stream through the compensation stages, from
+// the prepared array or gathered once per call (k_gather_bsel).
 // GR: 0 dense, 1 grouped, 2 grouped with the rows of A gathered by row_src
 // (a separate instance, so the plain grouped kernel keeps its registers).
-template <int FMT, bool TL, int GR, bool XS>
+template <int FMT, bool TL, int GR>
 __global__ void __launch_bounds__(GB_T, 1) k_gemm_big(BigArgs args) {
   using SL = StageLayout<FMT>;
   constexpr int L = SL::LOADS;
   __shared__ __attribute__((aligned(16))) uint8_t sStage[3 * SL::BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t sBS[XS ? GB_XS_BYTES : 16];
-  __shared__ int sChan[XS ? GB_XS_MAX : 1];
-  __shared__ int sFirst[XS ? GB_XS_MAX_NK + 1 : 1];
   static_assert(GB_W * 32 * GB_EP_STRIDE * 4 <= 3 * SL::BYTES, "epilogue staging");
 
   const BigArgs& p = args;
@@ -631,36 +622,15 @@ __global__ void __launch_bounds__(GB_T, 1) k_gemm_big(BigArgs args) {
   }
   auto stage = [&](int s) __attribute__((always_inline)) { return sStage + (s % 3) * SL::BYTES; };
 
-  const int nS = p.nS;
-  if (XS) {
-    // channel list and, per FP4 stage kt, the first list entry at or past
-    // 128 kt (the list is ascending); B_S starts zeroed (entries past |S|
-    // stay zero).  Before any stage is in flight, so the fences cost nothing.
-    const int32_t* chg = p.chan + (GR ? (int64_t)grp * nS : 0);
-    for (int j = t; j < nS; j += GB_T) sChan[j] = chg[j];
-    for (int i = t; i < GB_XS_BYTES / 16; i += GB_T)
-      reinterpret_cast<u32x4*>(sBS)[i] = u32x4{0u, 0u, 0u, 0u};
-    __syncthreads();
-    for (int kt = t; kt <= nk; kt += GB_T) {
-      int lo = 0, hi = nS;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (sChan[mid] < 128 * kt) lo = mid + 1; else hi = mid;
-      }
-      sFirst[kt] = lo;
-    }
-    __syncthreads();
-  }
-
   // MXFP4 runs the two waves of each SIMD half a stage apart (below); only
   // waves 0..3 load, each the share of two waves
   const bool late = FMT == FP4Q_MXFP4 && wave >= GB_W / 2;
   auto issue = [&](int s) __attribute__((always_inline)) {
     if (FMT == FP4Q_MXFP4) {
-      issue_stage<FMT, TL, XS, GR == 2>(p, s, 2 * wave, lane, tc, stage(s));
-      issue_stage<FMT, TL, XS, GR == 2>(p, s, 2 * wave + 1, lane, tc, stage(s));
+      issue_stage<FMT, TL, GR == 2>(p, s, 2 * wave, lane, tc, stage(s));
+      issue_stage<FMT, TL, GR == 2>(p, s, 2 * wave + 1, lane, tc, stage(s));
     } else {
-      issue_stage<FMT, TL, XS, GR == 2>(p, s, wave, lane, tc, stage(s));
+      issue_stage<FMT, TL, GR == 2>(p, s, wave, lane, tc, stage(s));
     }
   };
   if (!late) {
@@ -687,38 +657,7 @@ __global__ void __launch_bounds__(GB_T, 1) k_gemm_big(BigArgs args) {
     else
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
-    if (s + 2 < ns) issue_stage<FMT, TL, XS, GR == 2>(p, s + 2, wave, lane, tc, stage(s + 2));
-  };
-  auto extract = [&](int s) __attribute__((always_inline)) {
-    if (XS) {
-      // B_S of the stage's channels: thread t takes column t % 256 of every
-      // second channel; code byte and block scale from the stage's B tile,
-      // e2m1 * scale (exact in BF16) into the compensation layout
-      const uint8_t* st = stage(s);
-      const int j1 = __builtin_amdgcn_readfirstlane(sFirst[s + 1]);
-      const int col = t & 255;
-      for (int j = __builtin_amdgcn_readfirstlane(sFirst[s]) + (t >> 8); j < j1; j += 2) {
-        const int pos = sChan[j] & 127;
-        const uint32_t byte =
-            st[SL::B + (col >> 4) * GB_GRP + ((pos >> 5) * 16 + (col & 15)) * 16 + ((pos >> 1) & 15)];
-        const uint32_t code = (pos & 1) ? (byte >> 4) : (byte & 15u);
-        float sv;
-        if (FMT == FP4Q_NVFP4) {
-          sv = e4m3_value(st[SL::SB + ((pos >> 6) * 256 + col) * 4 + ((pos >> 4) & 3)]);
-        } else {
-          const uint32_t c8 = st[SL::SB + col * 4 + (pos >> 5)];
-          sv = c8 ? __uint_as_float(c8 << 23) : __uint_as_float(0x00400000u);
-        }
-        const float v = e2m1_mag_value(code) * sv;
-        const int jj = j & 31;
-        *reinterpret_cast<uint16_t*>(sBS + (j >> 5) * GB_DATA + (col >> 4) * GB_GRP +
-                                     ((jj >> 3) * 16 + (col & 15)) * 16 + (jj & 7) * 2) =
-            (uint16_t)((__float_as_uint(v) >> 16) | ((code & 8u) << 12));
-      }
-    }
-  };
-  auto comp_src = [&](int s) __attribute__((always_inline)) {
-    return XS ? sBS + (s - nk) * GB_DATA : stage(s) + SL::B;
+    if (s + 2 < ns) issue_stage<FMT, TL, GR == 2>(p, s + 2, wave, lane, tc, stage(s + 2));
   };
   if constexpr (FMT == FP4Q_MXFP4) {
     // Ping-pong.  Each stage is two barrier intervals: LDS fragment reads,
@@ -746,14 +685,13 @@ __global__ void __launch_bounds__(GB_T, 1) k_gemm_big(BigArgs args) {
       open(s);
       Frag f;
       read_frags<FMT, true>(stage(s), stage(s) + SL::B, wm, wn, lane, f);
-      extract(s);
       lds_barrier();
       compute_fp4<FMT>(acc, f, lane);
     }
     for (int s = nk; s < ns; ++s) {
       open(s);
       Frag f;
-      read_frags<FMT, false>(stage(s), comp_src(s), wm, wn, lane, f);
+      read_frags<FMT, false>(stage(s), stage(s) + SL::B, wm, wn, lane, f);
       lds_barrier();
       compute_comp(acc, f);
     }
@@ -764,7 +702,6 @@ __global__ void __launch_bounds__(GB_T, 1) k_gemm_big(BigArgs args) {
       Frag f;
       read_frags<FMT, true>(stage(s), stage(s) + SL::B, wm, wn, lane, f);
       compute_fp4<FMT>(acc, f, lane);
-      extract(s);
     }
     // y = t_w (t_x main + comp): scale the main sum once, before R B_S
 #pragma unroll
@@ -774,7 +711,7 @@ __global__ void __launch_bounds__(GB_T, 1) k_gemm_big(BigArgs args) {
     for (int s = nk; s < ns; ++s) {
       pipe(s);
       Frag f;
-      read_frags<FMT, false>(stage(s), comp_src(s), wm, wn, lane, f);
+      read_frags<FMT, false>(stage(s), stage(s) + SL::B, wm, wn, lane, f);
       compute_comp(acc, f);
       __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
@@ -1319,11 +1256,8 @@ __global__ void __launch_bounds__(256) k_gather_bsel(const uint8_t* __restrict__
 
 // ---- host side ---------------------------------------------------------------
 
-// Residual rows are brought in as 16-byte pieces of 8 channels; in-kernel
-// extraction of B_S (|S| <= 96) needs the per-stage table (K <= 32768).
-static bool big_ok(int64_t K, int nS) {
-  return K % 128 == 0 && nS % 8 == 0 && (nS > GB_XS_MAX || K / 128 <= GB_XS_MAX_NK);
-}
+// Residual rows are brought in as 16-byte pieces of 8 channels.
+static bool big_ok(int64_t K, int nS) { return K % 128 == 0 && nS % 8 == 0; }
 
 bool big_gemm_eligible(int64_t M, int64_t N, int64_t K, int nS) {
   return M >= GB_TILE && N >= GB_TILE && big_ok(K, nS);
@@ -1331,40 +1265,26 @@ bool big_gemm_eligible(int64_t M, int64_t N, int64_t K, int nS) {
 
 bool big_grouped_eligible(int64_t N, int64_t K, int nS) { return N >= GB_TILE && big_ok(K, nS); }
 
-// Only more than GB_XS_MAX channels use the gather kernel and its workspace.
-size_t big_gemm_workspace_bytes(int64_t N, int nS) {
-  if (nS <= GB_XS_MAX) return 0;
-  const int64_t nc = (nS + GB_CS - 1) / GB_CS;
-  return (size_t)(((N + 15) / 16) * nc * 1024);
-}
+// B_S gathered per call (no prepared array): one array of N columns.
+size_t big_gemm_workspace_bytes(int64_t N, int nS) { return comp_weights_bytes(N, nS); }
 
 template <int FMT, bool GR>
-static void launch_big(const BigArgs& a, bool tiled, unsigned grid, hipStream_t stream,
-                       bool prepared = false) {
-  // NVFP4 runs on the four-wave kernels with B_S gathered or prepared; the
-  // in-kernel extraction (XS) serves MXFP4 up to GB_XS_MAX channels
-  const bool xs = FMT != FP4Q_NVFP4 && a.nS > 0 && a.nS <= GB_XS_MAX && !prepared;
+static void launch_big(const BigArgs& a, bool tiled, unsigned grid, hipStream_t stream) {
   if constexpr (GR) {  // grouped operands are row-major
-    if (a.row_src)   // the gathering form streams prepared weights (no XS)
-      hipLaunchKernelGGL((k_gemm_big<FMT, false, 2, false>), dim3(grid), dim3(GB_T), 0, stream, a);
-    else if (xs)
-      hipLaunchKernelGGL((k_gemm_big<FMT, false, 1, true>), dim3(grid), dim3(GB_T), 0, stream, a);
+    if (a.row_src)
+      hipLaunchKernelGGL((k_gemm_big<FMT, false, 2>), dim3(grid), dim3(GB_T), 0, stream, a);
     else
-      hipLaunchKernelGGL((k_gemm_big<FMT, false, 1, false>), dim3(grid), dim3(GB_T), 0, stream, a);
-  } else if (FMT == FP4Q_NVFP4 && !xs) {
+      hipLaunchKernelGGL((k_gemm_big<FMT, false, 1>), dim3(grid), dim3(GB_T), 0, stream, a);
+  } else if (FMT == FP4Q_NVFP4) {
     if (tiled)
       hipLaunchKernelGGL((k_gemm_nv4<true>), dim3(grid), dim3(256), 0, stream, a);
     else
       hipLaunchKernelGGL((k_gemm_nv4<false>), dim3(grid), dim3(256), 0, stream, a);
   } else {
-    if (tiled && xs)
-      hipLaunchKernelGGL((k_gemm_big<FMT, true, 0, true>), dim3(grid), dim3(GB_T), 0, stream, a);
-    else if (tiled)
-      hipLaunchKernelGGL((k_gemm_big<FMT, true, 0, false>), dim3(grid), dim3(GB_T), 0, stream, a);
-    else if (xs)
-      hipLaunchKernelGGL((k_gemm_big<FMT, false, 0, true>), dim3(grid), dim3(GB_T), 0, stream, a);
+    if (tiled)
+      hipLaunchKernelGGL((k_gemm_big<FMT, true, 0>), dim3(grid), dim3(GB_T), 0, stream, a);
     else
-      hipLaunchKernelGGL((k_gemm_big<FMT, false, 0, false>), dim3(grid), dim3(GB_T), 0, stream, a);
+      hipLaunchKernelGGL((k_gemm_big<FMT, false, 0>), dim3(grid), dim3(GB_T), 0, stream, a);
   }
 }
 
@@ -1389,20 +1309,20 @@ int launch_gemm_big(int fmt, bool tiled, int64_t M, int64_t N, int64_t K, const 
                     void* ws, hipStream_t stream) {
   const int nc = nS > 0 ? (nS + GB_CS - 1) / GB_CS : 0;
   // prepared compensation weights (the gather kernel's output, made once)
-  // replace both the gather and the in-kernel extraction
+  // replace the per-call gather
   const bool prepared = bsel_pre != nullptr && nS > 0;
   uint8_t* bsel = prepared ? const_cast<uint8_t*>(bsel_pre) : static_cast<uint8_t*>(ws);
   BigArgs a{M, N, K, aq, as, ats, bq, bs, bts, nS, resid, bsel, chan, cts, y, y_bf16, ldy,
             (int)((M + GB_TILE - 1) / GB_TILE), (int)((N + GB_TILE - 1) / GB_TILE),
             (int)(K / 128), nc, nullptr, 1, nullptr};
-  const bool gather = nS > 0 && !prepared && (fmt == FP4Q_NVFP4 || nS > GB_XS_MAX);
+  const bool gather = nS > 0 && !prepared;
   const unsigned grid = (unsigned)(a.mt * a.nt);
   if (fmt == FP4Q_NVFP4) {
     if (gather) launch_gather<FP4Q_NVFP4>(tiled, bq, bs, N, K, chan, nS, nc, 1, bsel, stream);
-    launch_big<FP4Q_NVFP4, false>(a, tiled, grid, stream, prepared);
+    launch_big<FP4Q_NVFP4, false>(a, tiled, grid, stream);
   } else {
     if (gather) launch_gather<FP4Q_MXFP4>(tiled, bq, bs, N, K, chan, nS, nc, 1, bsel, stream);
-    launch_big<FP4Q_MXFP4, false>(a, tiled, grid, stream, prepared);
+    launch_big<FP4Q_MXFP4, false>(a, tiled, grid, stream);
   }
   return 0;
 }
@@ -1431,21 +1351,17 @@ int launch_gemm_big_grouped(int fmt, int64_t total_rows, int64_t N, int64_t K,
                             void* y, int y_bf16, void* ws, hipStream_t stream, bool wtiled,
                             const int32_t* row_src, int64_t src_rows) {
   const int nc = nS > 0 ? (nS + GB_CS - 1) / GB_CS : 0;
-  // prepared compensation weights (every group's, made once) replace both
-  // the gather and the in-kernel extraction
+  // prepared compensation weights (every group's, made once) replace the
+  // per-call gather
   const bool prepared = bsel_pre != nullptr && nS > 0;
   uint8_t* bsel = prepared ? const_cast<uint8_t*>(bsel_pre) : static_cast<uint8_t*>(ws);
   BigArgs a{total_rows, N, K, aq, as, ats, bq, bs, bts, nS, resid, bsel, chan, cts, y, y_bf16, N,
             0, (int)((N + GB_TILE - 1) / GB_TILE), (int)(K / 128), nc, off, G, row_src};
-  // NVFP4 never takes the in-kernel extraction: the 128 x 512 kernel with
-  // B_S gathered once per call beats the 256-tile kernel extracting it from
-  // the tiles (tiled weights: NVFP4 with 32-bit gather offsets, checked by
-  // the caller)
-  const bool xs = nS > 0 && nS <= GB_XS_MAX && !prepared && fmt != FP4Q_NVFP4;
-  const bool gather = nS > 0 && !prepared && !xs;
-  // the gathering form keeps 32-bit offsets into the token matrix
+  const bool gather = nS > 0 && !prepared;
+  // the gathering form keeps 32-bit offsets into the token matrix (tiled
+  // weights: NVFP4 with 32-bit offsets, checked by the caller)
   const bool ga32 = row_src == nullptr || src_rows * (K / 2) <= (int64_t)UINT32_MAX;
-  if (fmt == FP4Q_NVFP4 && !xs && ga32) {
+  if (fmt == FP4Q_NVFP4 && ga32) {
     // 128 x 512 tiles; every group adds at most one partial row tile
     a.nt = (int)((N + G4_TN - 1) / G4_TN);
     const unsigned g4 = (unsigned)(((total_rows + G4_TM - 1) / G4_TM + G) * a.nt);
@@ -1464,10 +1380,10 @@ int launch_gemm_big_grouped(int fmt, int64_t total_rows, int64_t N, int64_t K,
   const unsigned grid = (unsigned)(((total_rows + GB_TILE - 1) / GB_TILE + G) * a.nt);
   if (fmt == FP4Q_NVFP4) {
     if (gather) launch_gather<FP4Q_NVFP4>(false, bq, bs, N, K, chan, nS, nc, G, bsel, stream);
-    launch_big<FP4Q_NVFP4, true>(a, false, grid, stream, prepared);
+    launch_big<FP4Q_NVFP4, true>(a, false, grid, stream);
   } else {
     if (gather) launch_gather<FP4Q_MXFP4>(false, bq, bs, N, K, chan, nS, nc, G, bsel, stream);
-    launch_big<FP4Q_MXFP4, true>(a, false, grid, stream, prepared);
+    launch_big<FP4Q_MXFP4, true>(a, false, grid, stream);
   }
   return 0;
 }

@@ -278,7 +278,7 @@ int fp4q_gemm(fp4q_format_t fmt, fp4q_layout_t layout, int64_t M, int64_t N, int
  * abstract: the selected channels effectively BF16).  With static weights
  * and a fixed channel list that slice is itself static:
  * fp4q_comp_weights writes it once, and fp4q_gemm_prepared streams it
- * instead of extracting it from the packed weights on every call.
+ * instead of gathering it from the packed weights on every call.
  *
  * fp4q_comp_weights:
  *   b_q, b_s   packed W^T and block scales in `layout`, as for fp4q_gemm
@@ -554,9 +554,8 @@ int fp4q_select_channels_grouped(fp4q_format_t fmt, const uint16_t* x, int64_t r
  *   workspace      device scratch of fp4q_grouped_gemm_workspace_bytes()
  *                  bytes, 16-byte aligned (may be NULL when that is 0): the
  *                  gathered compensation weights of every group, as BF16
- *                  (NVFP4 with N >= 256: whenever there are channels, the
- *                  128 x 512 kernel streaming them; MXFP4: above 96
- *                  channels, fewer being extracted inside the kernel)
+ *                  (N >= 256: whenever there are channels; the large-tile
+ *                  kernels stream them)
  *
  * Empty groups produce nothing.  K must be a multiple of 128.
  * FP4Q_ERR_WORKSPACE if a needed workspace is missing, small or misaligned.

@@ -261,7 +261,7 @@ def test_grouped_gemm_residual_fp4_rejects(L):
     need = L.fp4q_grouped_gemm_residual_fp4_workspace_bytes(0, 0, 64, 256, 256, 2, 16)
     assert need >= 64 * 16 * 2                     # the decoded residual at least
     # tiled weights: the compensation weights are always gathered
-    # NVFP4 gathers the compensation weights for either weight layout
+    # the compensation weights are gathered for either weight layout
     need_t = L.fp4q_grouped_gemm_residual_fp4_workspace_bytes(0, 1, 64, 256, 256, 2, 16)
     assert need_t == need == 64 * 16 * 2 + 2 * (256 // 16) * 1024
     try:
@@ -301,16 +301,16 @@ def test_gemm_rejects(L):
     assert g(L, layout=5) == INVALID
     assert g(L, layout=1, K=144) == UNSUPPORTED
     assert g(L, nS=8, chan=A, R=ctypes.c_void_p(0x20008)) == INVALID   # resid 16-byte aligned
-    # the large-tile NVFP4 kernel streams B_S gathered into the workspace;
-    # the MXFP4 one takes up to 96 channels from its own B tiles
+    # the large-tile kernels stream B_S, gathered into the workspace first
     need = L.fp4q_gemm_workspace_bytes(0, 1, 512, 512, 256, 128)
     assert need == (512 // 16) * 4 * 1024
     assert L.fp4q_gemm_workspace_bytes(0, 1, 512, 512, 256, 104) == (512 // 16) * 4 * 1024
     assert L.fp4q_gemm_workspace_bytes(0, 1, 512, 500, 256, 136) == (512 // 16) * 5 * 1024
     assert L.fp4q_gemm_workspace_bytes(0, 1, 512, 512, 256, 0) == 0
-    for nS in (8, 32, 40, 96):
-        assert L.fp4q_gemm_workspace_bytes(0, 1, 512, 512, 256, nS) == (512 // 16) * ((nS + 31) // 32) * 1024
-        assert L.fp4q_gemm_workspace_bytes(1, 1, 512, 512, 256, nS) == 0
+    for fmt in (0, 1):
+        for nS in (8, 32, 40, 96):
+            assert (L.fp4q_gemm_workspace_bytes(fmt, 1, 512, 512, 256, nS)
+                    == (512 // 16) * ((nS + 31) // 32) * 1024)
     assert L.fp4q_gemm_workspace_bytes(0, 1, 64, 11008, 2048, 128) == 0   # decode shape
     assert L.fp4q_gemm_workspace_bytes(0, 1, 512, 512, 256, 12) == 0      # |S| % 8: other path
     big = dict(M=512, N=512, K=256, nS=128, chan=A, R=B, ldy=512)
@@ -357,10 +357,9 @@ def test_grouped_gemm_rejects(L):
     # when there are more than 96 channels
     need = L.fp4q_grouped_gemm_workspace_bytes(0, 0, 1000, 512, 256, 4, 128)
     assert need == 4 * (512 // 16) * 4 * 1024
-    # NVFP4 gathers every group's compensation weights at any channel count;
-    # MXFP4 extracts up to 96 channels in the kernel
+    # every group's compensation weights are gathered at any channel count
     assert L.fp4q_grouped_gemm_workspace_bytes(0, 0, 1000, 512, 256, 4, 32) == 4 * 32 * 1024
-    assert L.fp4q_grouped_gemm_workspace_bytes(1, 0, 1000, 512, 256, 4, 32) == 0
+    assert L.fp4q_grouped_gemm_workspace_bytes(1, 0, 1000, 512, 256, 4, 32) == 4 * 32 * 1024
     assert L.fp4q_grouped_gemm_workspace_bytes(0, 0, 1000, 128, 256, 4, 128) == 0   # N < 256
     assert L.fp4q_grouped_gemm_workspace_bytes(0, 0, 1000, 512, 256, 4, 0) == 0
     # tiled weights gather the compensation weights for any channel count

@@ -121,7 +121,7 @@ def test_prefill_term(orc, name, prepared):
                                       (257, 1000, 512, 96), (130, 200, 384, 37)])
 def test_ragged_term(orc, fmt, M, N, K, nS):
     """Channel counts that leave a partial last compensation step, on the
-    decode, 256-tile (gathered, in-kernel and prepared) and general kernels."""
+    decode, large-tile (gathered per call and prepared) and general kernels."""
     need_gpu()
     say(f"compensation term fmt {fmt} M{M} N{N} K{K} nS{nS}")
     d = dense_case(M, K, N, n_out=max(1, K // 100), seed=5 * M + N + K + nS)

@@ -80,8 +80,9 @@ def test_graph_decode_step(fmt, layout):
 
 @pytest.mark.parametrize("N,nS", [(160, 8), (512, 8), (512, 104)])
 def test_graph_grouped_layer(N, nS):
-    """Staged grouped path with the compensation weights taken in-kernel
-    (|S| <= 96) and gathered into the workspace (|S| > 96)."""
+    """Staged grouped path with the compensation weights gathered into the
+    workspace inside the captured graph (N >= 256), and the general grouped
+    kernel (N < 256)."""
     dev = need_gpu()
     say(f"graph replay: grouped quantize + grouped gemm (NVFP4), N {N}, |S| {nS}")
     fmt = fq.NVFP4

@@ -9,8 +9,7 @@ layout is the library's own, fp4q.h), through the C ABI:
     kernel with the same bytes in LDS), and the oracle's grouped GEMM on
     every output within 1e-3 * Yabs;
   * fp4q_grouped_gemm_residual_fp4 with tiled weights against the oracle,
-    and bit for bit against row-major weights where both take the same
-    kernel (more than 96 channels);
+    and bit for bit against row-major weights (same kernel, B_S gathered);
   * empty, single-row, 128-row-crossing and ragged experts; N with padded
     16-row code groups and 64-row scale groups; FP32 and BF16 outputs.
 """
@@ -109,9 +108,8 @@ def test_grouped_residual_fp4_tiled_weights(orc, N, nS):
     a = {"q": to_dev(qa["q"]), "scales": to_dev(qa["scales"]), "tscale": to_dev(qa["tscale"])}
     r = {"q": to_dev(qr["q"]), "scales": to_dev(qr["scales"]), "tscale": to_dev(qr["tscale"])}
     y_t = fq.grouped_gemm_residual_fp4(0, doff, a, tq, ts, dbts, dch, r, w_layout=fq.TILED, N=N)
-    if nS > 96:   # row-major weights take the same kernel and gathered B_S
-        y_r = fq.grouped_gemm_residual_fp4(0, doff, a, rq, rs, dbts, dch, r)
-        _bits_equal(y_t, y_r, "second-pass residual, tiled weights")
+    y_r = fq.grouped_gemm_residual_fp4(0, doff, a, rq, rs, dbts, dch, r)
+    _bits_equal(y_t, y_r, "second-pass residual, tiled weights")
     torch.cuda.synchronize()
     rows = int(off[-1])
     pm = np.repeat(np.arange(rows), N)

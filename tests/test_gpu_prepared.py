@@ -91,8 +91,8 @@ def test_prepared_decode_workload(orc, fmt, layout):
                                       (257, 1000, 512, 96), (100, 200, 256, 12)])
 def test_prepared_shapes(orc, fmt, M, N, K, nS):
     """Ragged decode shapes (columns past N, one or two channel stages), the
-    256-tile kernel with the gather and the in-kernel extraction both
-    replaced, and a general-kernel shape that takes the term from chan_idx."""
+    large-tile kernels with the per-call gather replaced, and a
+    general-kernel shape that takes the term from chan_idx."""
     need_gpu()
     say(f"prepared gemm fmt {fmt} M{M} N{N} K{K} nS{nS}")
     d = dense_case(M, K, N, n_out=max(1, K // 100), seed=3 * M + N + K + nS)
@@ -106,9 +106,9 @@ def test_prepared_shapes(orc, fmt, M, N, K, nS):
 def test_grouped_prepared(orc, fmt, N, nS):
     """fp4q_grouped_comp_weights bit for bit per group, and
     fp4q_grouped_gemm_prepared against the oracle's grouped GEMM, with empty,
-    single-row and ragged groups: the 256-tile grouped kernel (|S| taken
-    in-kernel and gathered forms both replaced) and, at N < 256, the general
-    grouped kernel taking the term from chan_idx."""
+    single-row and ragged groups: the large-tile grouped kernels (the
+    per-call gather replaced) and, at N < 256, the general grouped kernel
+    taking the term from chan_idx."""
     need_gpu()
     say(f"grouped prepared fmt {fmt} N{N} nS{nS}")
     K = 384

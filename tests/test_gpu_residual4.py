@@ -1,7 +1,7 @@
 """GPU parity of the compensated GEMM with the second-pass FP4 residual
 (fp4q_gemm_residual_fp4, through the C ABI) against the oracle, on every
 GEMM path: the general kernel (small shapes), the decode kernel (M <= 64)
-and the 256x256-tile kernel (in-kernel and gathered compensation weights),
+and the large-tile kernels (compensation weights gathered per call),
 both formats and both operand layouts; and the GPU quantizer's second pass
 on R bit-exact against the oracle's."""
 import numpy as np
@@ -44,8 +44,8 @@ def _gpu(fmt, layout, S, qa, qb, qr, y_dtype=fq.OUT_F32):
 @pytest.mark.parametrize("M,K,N,nS", [(16, 256, 256, 32),     # general kernel
                                       (64, 512, 640, 64),     # decode kernel
                                       (33, 384, 200, 32),     # general, ragged
-                                      (300, 512, 520, 64),    # 256-tile, in-kernel B_S
-                                      (257, 512, 300, 128)])  # 256-tile, gathered B_S (|S| > 96)
+                                      (300, 512, 520, 64),    # large-tile, gathered B_S
+                                      (257, 512, 300, 128)])  # large-tile, four stages of B_S
 def test_residual_fp4_matches_oracle(orc, fmt, M, K, N, nS):
     need_gpu()
     say(f"gemm fp4 residual fmt {fmt} M{M} K{K} N{N} nS{nS}")
