@@ -537,8 +537,8 @@ int fp4q_select_channels_grouped(fp4q_format_t fmt, const uint16_t* x, int64_t r
  *                  b_q + g * code_bytes and b_s + g * scale_bytes with the
  *                  sizes of fp4q_packed_bytes(fmt, TILED, N, K).  Tiled
  *                  weights are served by the 128 x 512 NVFP4 kernel only:
- *                  MXFP4, N < 256, n_chan % 8 != 0, or K > 32768 with
- *                  n_chan <= 96 is FP4Q_ERR_UNSUPPORTED.
+ *                  MXFP4, N < 256 or n_chan % 8 != 0 is
+ *                  FP4Q_ERR_UNSUPPORTED.
  *                  On MI355X at the MoE workload (N = 1536 / 2048, K =
  *                  2048 / 768) tiled weights took the two GEMM calls from
  *                  about 540 to 490 us (a stage's 512 weight columns are 32
